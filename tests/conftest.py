@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size parity checks (minutes of CPU oracle work)")
+
+
+@pytest.fixture(scope="session")
+def muse_lib():
+    """The built C-ABI library through its Python binding (GPU tests only)."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from clustered_softmax_attention_amd import binding
+    binding.load()
+    return binding
