@@ -1,0 +1,184 @@
+"""Python binding of the MuSe C-ABI library (libmuse.so): argument marshalling only.
+
+Tensors are torch CUDA tensors of shape [B, H, N, D], contiguous, float32 or
+bfloat16; the library receives their device pointers and the current HIP stream.
+Every computation happens in the library's HIP kernels. Loading fails loudly when
+the library has not been built (``python -m clustered_softmax_attention_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuse.so")
+_lib = None
+
+MUSE_F32, MUSE_BF16 = 0, 1
+MUSE_OK = 0
+STATUS = {0: "MUSE_OK", -1: "MUSE_ERR_INVALID_ARG", -2: "MUSE_ERR_UNSUPPORTED", -3: "MUSE_ERR_HIP",
+          -4: "MUSE_ERR_NO_MEMORY", -5: "MUSE_ERR_WORKSPACE"}
+
+# C entry points declared in include/muse.h
+EXPORTED = ("muse_attn_fwd", "muse_exact_attn_fwd", "muse_attn_fwd_ex", "muse_fwd_params_init",
+            "muse_attn_fwd_workspace_bytes", "muse_last_error", "muse_version")
+
+
+class MuseError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class FwdParams(ctypes.Structure):
+    _fields_ = [
+        ("scale", ctypes.c_float),
+        ("out_dtype", ctypes.c_int),
+        ("dipole", ctypes.c_int),
+        ("topk_clusters", ctypes.c_int),
+        ("topk_blocks", ctypes.c_int),
+        ("labels_q_in", ctypes.c_void_p),
+        ("labels_k_in", ctypes.c_void_p),
+        ("labels_q_trace", ctypes.c_void_p),
+        ("labels_k_trace", ctypes.c_void_p),
+        ("centroids_q_out", ctypes.c_void_p),
+        ("centroids_k_out", ctypes.c_void_p),
+        ("lse_out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def load(path: str = _LIB_PATH) -> ctypes.CDLL:
+    """Load libmuse.so (raises if it is missing: there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m clustered_softmax_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    i, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.muse_attn_fwd.argtypes = [vp, vp, vp, vp] + [i] * 10 + [vp]
+    lib.muse_attn_fwd.restype = i
+    lib.muse_attn_fwd_ex.argtypes = [vp, vp, vp, vp] + [i] * 10 + [vp, ctypes.POINTER(FwdParams)]
+    lib.muse_attn_fwd_ex.restype = i
+    lib.muse_exact_attn_fwd.argtypes = [vp, vp, vp, vp] + [i] * 6 + [vp]
+    lib.muse_exact_attn_fwd.restype = i
+    lib.muse_fwd_params_init.argtypes = [ctypes.POINTER(FwdParams)]
+    lib.muse_fwd_params_init.restype = None
+    lib.muse_attn_fwd_workspace_bytes.argtypes = [i] * 9 + [ctypes.POINTER(FwdParams)]
+    lib.muse_attn_fwd_workspace_bytes.restype = sz
+    lib.muse_last_error.argtypes = []
+    lib.muse_last_error.restype = ctypes.c_char_p
+    lib.muse_version.argtypes = []
+    lib.muse_version.restype = i
+    _lib = lib
+    return lib
+
+
+def _check(code: int):
+    if code != MUSE_OK:
+        raise MuseError(code, _lib.muse_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MUSE_F32
+    if t.dtype == torch.bfloat16:
+        return MUSE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_qkv(q, k, v):
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous() and t.dim() == 4):
+            raise ValueError("q, k, v must be contiguous 4-D [B, H, N, D] device tensors")
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def exact_attn_fwd(q, k, v, causal: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """muse_exact_attn_fwd: exact softmax attention (scale 1/sqrt(D)); out dtype = input dtype."""
+    lib = load()
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.muse_exact_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, D, int(causal),
+                                   _dtype_code(q), _stream()))
+    return out
+
+
+def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False, block: int = 0,
+             out: Optional[torch.Tensor] = None, *, scale: float = 0.0, out_dtype=None, dipole: bool = True,
+             topk_clusters: int = 0, topk_blocks: int = 0, labels_q_in=None, labels_k_in=None,
+             return_trace: bool = False, return_centroids: bool = False, return_lse: bool = False,
+             workspace: Optional[torch.Tensor] = None):
+    """muse_attn_fwd_ex. Returns out, or (out, extras) when any return_* flag is set, where
+    extras holds 'labels_q_trace', 'labels_k_trace' [iters,B,H,N] int32, 'centroids_q',
+    'centroids_k' [B,H,C,D] float32 and 'lse' [B,H,N] float32 as requested."""
+    lib = load()
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    dev = q.device
+    if out_dtype is None:
+        out_dtype = q.dtype
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=out_dtype, device=dev)
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    p.scale = float(scale)
+    p.out_dtype = _dtype_code(out)
+    p.dipole = 1 if dipole else 0
+    p.topk_clusters = int(topk_clusters)
+    p.topk_blocks = int(topk_blocks)
+    extras = {}
+    keep = []
+    for name, lab in (("labels_q_in", labels_q_in), ("labels_k_in", labels_k_in)):
+        if lab is not None:
+            lab = lab.to(device=dev, dtype=torch.int32).contiguous()
+            keep.append(lab)
+            setattr(p, name, lab.data_ptr())
+    if return_trace:
+        for name in ("labels_q_trace", "labels_k_trace"):
+            t = torch.full((kmeans_iters, B, H, N), -1, dtype=torch.int32, device=dev)
+            extras[name] = t
+            setattr(p, name, t.data_ptr())
+    if return_centroids:
+        extras["centroids_q"] = torch.empty((B, H, Cq, D), dtype=torch.float32, device=dev)
+        extras["centroids_k"] = torch.empty((B, H, Ck, D), dtype=torch.float32, device=dev)
+        p.centroids_q_out = extras["centroids_q"].data_ptr()
+        p.centroids_k_out = extras["centroids_k"].data_ptr()
+    if return_lse:
+        extras["lse"] = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        p.lse_out = extras["lse"].data_ptr()
+    if workspace is not None:
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.muse_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, D, Cq, Ck, kmeans_iters,
+                                int(causal), int(block), _dtype_code(q), _stream(), ctypes.byref(p)))
+    del keep
+    return (out, extras) if extras else out
+
+
+def workspace_bytes(B, H, N, D, Cq, Ck, causal=False, block=0, dtype=MUSE_BF16, topk_clusters=0,
+                    topk_blocks=0) -> int:
+    lib = load()
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    p.topk_clusters, p.topk_blocks = topk_clusters, topk_blocks
+    n = lib.muse_attn_fwd_workspace_bytes(B, H, N, D, Cq, Ck, int(causal), int(block), dtype, ctypes.byref(p))
+    if n == 0:
+        raise MuseError(-1, lib.muse_last_error().decode())
+    return n

@@ -1,0 +1,253 @@
+// Lloyd K-means on queries and on keys, each head separately (gfx950, wave64).
+//
+// The method clusters queries and keys separately, each in its own space
+// (gist.science summary of arXiv 2509.10406, Kernmechanismen 1), with a few
+// Euclidean K-means iterations (pith.science review, "Assumptions & free
+// parameters": K-means iterations).
+//
+// Layout: a head's N points are cut into tiles of `tile` consecutive points
+// (one workgroup, one thread per point). Tiles never straddle a causal block,
+// so a (block, cluster) bucket is a concatenation of per-tile segments.
+//
+// Per iteration:
+//   kmeans_assign : label = argmin_j ||x - c_j||^2 (direct form, fp32, ties to the
+//                   lowest j); the tile's points are counting-sorted by label in
+//                   LDS (stable) and the tile's per-cluster sums are written out.
+//   kmeans_update : c_j = (sum over tiles, in tile order) / count, or unchanged
+//                   when the cluster is empty.
+// After the last iteration:
+//   bucket_offsets / bucket_scatter : stable order of the head's points by
+//                   (block, label), i.e. the key (or query) permutation used by
+//                   the summary kernels.
+//
+// Every sum runs in a fixed order, so labels and centroids are bitwise
+// reproducible.
+#include "muse_kernels.hpp"
+
+namespace muse {
+
+template <typename T>
+__global__ void kmeans_init_kernel(KmArgs a) {
+  const KmTensor& t = a.t[blockIdx.z];
+  if (t.labels_in != nullptr) return;
+  const int bh = blockIdx.y;
+  const T* x = static_cast<const T*>(t.x) + static_cast<size_t>(bh) * a.N * a.D;
+  float* c = t.cent + static_cast<size_t>(bh) * t.C * a.D;
+  for (int e = threadIdx.x; e < t.C * a.D; e += blockDim.x) {
+    const int j = e / a.D, d = e % a.D;
+    const long src = (static_cast<long>(j) * a.N) / t.C;
+    c[e] = Elem<T>::load(x, static_cast<size_t>(src) * a.D + d);
+  }
+}
+
+// One workgroup = one tile of `tile` points (blockDim.x == tile, a multiple of 64).
+// Dynamic LDS: centroid chunk [kChunkC][D] f32 | tile labels [tile] | wave histograms
+// [tile/64][C] | tile counts [C] | tile starts [C] | sorted order [tile].
+template <typename T, int D>
+__global__ void __launch_bounds__(kMaxTile) kmeans_assign_kernel(KmArgs a, int iter) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const KmTensor& t = a.t[blockIdx.z];
+  const int C = t.C;
+  const int bh = blockIdx.y;
+  const int tile = blockDim.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int nwaves = tile >> 6;
+  const long n = static_cast<long>(blockIdx.x) * tile + tid;
+  const bool valid = n < a.N;
+  const T* x = static_cast<const T*>(t.x) + static_cast<size_t>(bh) * a.N * D;
+
+  float* sc = reinterpret_cast<float*>(smem);                       // [kChunkC][D]
+  int* s_lab = reinterpret_cast<int*>(sc + kChunkC * D);            // [tile]
+  int* s_whist = s_lab + tile;                                      // [nwaves][C]
+  int* s_cnt = s_whist + nwaves * C;                                // [C]
+  int* s_start = s_cnt + C;                                         // [C]
+  int* s_sorted = s_start + C;                                      // [tile]
+
+  int lab = C;  // sentinel for points past the end of the sequence
+  if (t.labels_in != nullptr) {
+    // caller labels outside [0, C) are clamped so that LDS indexing stays in bounds
+    if (valid) lab = min(max(t.labels_in[static_cast<size_t>(bh) * a.N + n], 0), C - 1);
+  } else {
+    float xr[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) xr[d] = valid ? Elem<T>::load(x, static_cast<size_t>(n) * D + d) : 0.f;
+    const float* cent = t.cent + static_cast<size_t>(bh) * C * D;
+    float best = __builtin_huge_valf();
+    int bj = 0;
+    for (int j0 = 0; j0 < C; j0 += kChunkC) {
+      const int nc = min(kChunkC, C - j0);
+      __syncthreads();
+      for (int e = tid; e < nc * D; e += tile) sc[e] = cent[static_cast<size_t>(j0) * D + e];
+      __syncthreads();
+      for (int jj = 0; jj < nc; ++jj) {
+        const float* cj = sc + jj * D;
+        float dist = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          const float diff = xr[d] - cj[d];
+          dist = fmaf(diff, diff, dist);
+        }
+        if (dist < best) {  // strict: an exact tie keeps the lower index
+          best = dist;
+          bj = j0 + jj;
+        }
+      }
+    }
+    if (valid) lab = bj;
+  }
+  if (valid) {
+    t.labels[static_cast<size_t>(bh) * a.N + n] = lab;
+    if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
+  }
+
+  // ---- stable counting sort of the tile by label ----
+  for (int e = tid; e < nwaves * C; e += tile) s_whist[e] = 0;
+  s_lab[tid] = lab;
+  __syncthreads();
+  // lanes of this wave with the same label (the sentinel C only matches itself)
+  uint64_t peers = __ballot(1);
+  for (int b = 0; (1 << b) <= C; ++b) {
+    const bool bit = (lab >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  const int rank_in_wave = __popcll(peers & lanemask_lt());
+  if (valid && rank_in_wave == 0) s_whist[wave * C + lab] = __popcll(peers);
+  __syncthreads();
+  for (int j = tid; j < C; j += tile) {
+    int run = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      const int h = s_whist[w * C + j];
+      s_whist[w * C + j] = run;  // becomes the wave's base inside the label's segment
+      run += h;
+    }
+    s_cnt[j] = run;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int j = 0; j < C; ++j) {
+      s_start[j] = run;
+      run += s_cnt[j];
+    }
+  }
+  __syncthreads();
+  if (valid) s_sorted[s_start[lab] + s_whist[wave * C + lab] + rank_in_wave] = tid;
+  __syncthreads();
+
+  // ---- outputs: sort info (for bucketing) and this tile's per-cluster sums ----
+  const size_t tix = static_cast<size_t>(bh) * a.ntiles + blockIdx.x;
+  for (int j = tid; j < C; j += tile) {
+    t.tile_cnt[tix * C + j] = s_cnt[j];
+    t.tile_start[tix * C + j] = s_start[j];
+  }
+  t.tile_perm[tix * a.tile + tid] = static_cast<uint16_t>(s_sorted[tid]);
+  float* psum = t.psum + tix * C * D;
+  const long base = static_cast<long>(blockIdx.x) * tile;
+  for (int e = tid; e < C * D; e += tile) {
+    const int j = e / D, d = e % D;
+    const int st = s_start[j], cnt = s_cnt[j];
+    float acc = 0.f;
+    for (int r = 0; r < cnt; ++r) acc += Elem<T>::load(x, static_cast<size_t>(base + s_sorted[st + r]) * D + d);
+    psum[e] = acc;
+  }
+}
+
+// Thread per (cluster j, dim d): sum the tile partials in tile order.
+__global__ void kmeans_update_kernel(KmArgs a) {
+  const KmTensor& t = a.t[blockIdx.z];
+  const int C = t.C, D = a.D, bh = blockIdx.y;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= C * D) return;
+  const int j = e / D;
+  const size_t tbase = static_cast<size_t>(bh) * a.ntiles;
+  float acc = 0.f;
+  int cnt = 0;
+  for (int tt = 0; tt < a.ntiles; ++tt) {
+    acc += t.psum[(tbase + tt) * C * D + e];
+    cnt += t.tile_cnt[(tbase + tt) * C + j];
+  }
+  if (cnt > 0) t.cent[static_cast<size_t>(bh) * C * D + e] = acc / static_cast<float>(cnt);
+  else if (t.labels_in != nullptr) t.cent[static_cast<size_t>(bh) * C * D + e] = 0.f;
+}
+
+// One workgroup per (head, tensor): counts per (block, cluster) and their exclusive
+// scan -> offs[nb*C + 1].
+__global__ void bucket_offsets_kernel(KmArgs a) {
+  const KmTensor& t = a.t[blockIdx.z];
+  if (t.perm == nullptr) return;
+  const int C = t.C, bh = blockIdx.y;
+  const int nbC = a.nb * C;
+  extern __shared__ int s_tot[];  // [nb*C]
+  for (int e = threadIdx.x; e < nbC; e += blockDim.x) {
+    const int b = e / C, j = e % C;
+    int s = 0;
+    for (int tt = b * a.tiles_per_block; tt < min(a.ntiles, (b + 1) * a.tiles_per_block); ++tt)
+      s += t.tile_cnt[(static_cast<size_t>(bh) * a.ntiles + tt) * C + j];
+    s_tot[e] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int* offs = t.offs + static_cast<size_t>(bh) * (nbC + 1);
+    int run = 0;
+    for (int e = 0; e < nbC; ++e) {
+      offs[e] = run;
+      run += s_tot[e];
+    }
+    offs[nbC] = run;
+  }
+}
+
+// One workgroup per tile: scatter the tile's stably sorted points into the head's
+// (block, label) buckets.
+__global__ void bucket_scatter_kernel(KmArgs a) {
+  const KmTensor& t = a.t[blockIdx.z];
+  if (t.perm == nullptr) return;
+  const int C = t.C, bh = blockIdx.y, tt = blockIdx.x;
+  const int b = tt / a.tiles_per_block;
+  const size_t tix = static_cast<size_t>(bh) * a.ntiles + tt;
+  const int* offs = t.offs + static_cast<size_t>(bh) * (a.nb * C + 1);
+  const long tile0 = static_cast<long>(tt) * a.tile;
+  const int npts = static_cast<int>(min(static_cast<long>(a.tile), a.N - tile0));
+  for (int pos = threadIdx.x; pos < npts; pos += blockDim.x) {
+    const int p = t.tile_perm[tix * a.tile + pos];
+    const int j = t.labels[static_cast<size_t>(bh) * a.N + tile0 + p];
+    // members of (b, j) in earlier tiles of the same block come first
+    int before = 0;
+    for (int t2 = b * a.tiles_per_block; t2 < tt; ++t2)
+      before += t.tile_cnt[(static_cast<size_t>(bh) * a.ntiles + t2) * C + j];
+    const int dst = offs[b * C + j] + before + (pos - t.tile_start[tix * C + j]);
+    t.perm[static_cast<size_t>(bh) * a.N + dst] = static_cast<int>(tile0 + p);
+  }
+}
+
+// ------------------------------------------------------------------ host launchers
+
+template <typename T>
+static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
+  const dim3 g_init(1, a.BH, a.ntensors);
+  hipLaunchKernelGGL(kmeans_init_kernel<T>, g_init, dim3(256), 0, s, a);
+  const int Cmax = max(a.t[0].C, a.ntensors > 1 ? a.t[1].C : 0);
+  const size_t lds = static_cast<size_t>(kChunkC) * a.D * sizeof(float) +
+                     sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax);
+  const dim3 g_assign(a.ntiles, a.BH, a.ntensors);
+  const dim3 g_update((Cmax * a.D + 255) / 256, a.BH, a.ntensors);
+  for (int it = 0; it < iters; ++it) {
+    if (a.D == 64)
+      hipLaunchKernelGGL((kmeans_assign_kernel<T, 64>), g_assign, dim3(a.tile), lds, s, a, it);
+    else
+      hipLaunchKernelGGL((kmeans_assign_kernel<T, 128>), g_assign, dim3(a.tile), lds, s, a, it);
+    hipLaunchKernelGGL(kmeans_update_kernel, g_update, dim3(256), 0, s, a);
+  }
+  const size_t lds_off = sizeof(int) * static_cast<size_t>(a.nb) * Cmax;
+  hipLaunchKernelGGL(bucket_offsets_kernel, dim3(1, a.BH, a.ntensors), dim3(256), lds_off, s, a);
+  hipLaunchKernelGGL(bucket_scatter_kernel, dim3(a.ntiles, a.BH, a.ntensors), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans(const KmArgs& a, int iters, int dtype, hipStream_t s) {
+  return dtype == 0 ? launch_kmeans_t<float>(a, iters, s) : launch_kmeans_t<bf16>(a, iters, s);
+}
+
+}  // namespace muse

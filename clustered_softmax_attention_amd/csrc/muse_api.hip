@@ -1,0 +1,387 @@
+// C ABI of the MuSe forward pass: argument validation, workspace plan and the fixed
+// launch sequence on the caller's stream. Declarations and conventions: include/muse.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/muse.h"
+#include "muse_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MUSE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Bump allocator over one device buffer; every region is 256-byte aligned.
+struct Layout {
+  size_t bytes = 0;
+  size_t take(size_t n) {
+    const size_t at = bytes;
+    bytes += (n + 255) & ~static_cast<size_t>(255);
+    return at;
+  }
+};
+
+struct Shape {
+  int B, H, N, D, Cq, Ck, iters, causal, block, dtype;
+  int BH, nb, nbS, tile, ntiles, tiles_per_block;
+};
+
+// Largest multiple of 64 that divides `block` and is at most kMaxTile.
+int tile_for_block(int block) {
+  const int k = block / 64;
+  for (int t = muse::kMaxTile / 64; t >= 1; --t)
+    if (k % t == 0) return 64 * t;
+  return 64;
+}
+
+int validate(Shape& s, const muse_fwd_params* p) {
+  if (s.B < 1 || s.H < 1 || s.N < 1) return fail(MUSE_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", s.B, s.H, s.N);
+  if (s.dtype != MUSE_F32 && s.dtype != MUSE_BF16) return fail(MUSE_ERR_INVALID_ARG, "dtype %d is not MUSE_F32 or MUSE_BF16", s.dtype);
+  if (s.D != 64 && s.D != 128) return fail(MUSE_ERR_UNSUPPORTED, "head dim D=%d unsupported (64 or 128)", s.D);
+  if (static_cast<long>(s.B) * s.H * s.N > (1l << 31) / 256) return fail(MUSE_ERR_UNSUPPORTED, "B*H*N too large");
+  if (s.causal != 0 && s.causal != 1) return fail(MUSE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  s.BH = s.B * s.H;
+  if (s.causal) {
+    if (s.block < 64 || s.block > s.N || s.N % s.block != 0 || s.block % 64 != 0)
+      return fail(MUSE_ERR_INVALID_ARG, "causal block=%d must divide N=%d, be >= 64 and a multiple of 64", s.block, s.N);
+    s.nb = s.N / s.block;
+    s.nbS = s.nb;
+    s.tile = tile_for_block(s.block);
+    s.tiles_per_block = s.block / s.tile;
+  } else {
+    s.block = s.N;
+    s.nb = 1;
+    s.nbS = 1;
+    s.tile = muse::kMaxTile;
+    s.tiles_per_block = (s.N + s.tile - 1) / s.tile;
+  }
+  s.ntiles = (s.N + s.tile - 1) / s.tile;
+  if (p != nullptr) {
+    if (p->out_dtype != -1 && p->out_dtype != MUSE_F32 && p->out_dtype != MUSE_BF16)
+      return fail(MUSE_ERR_INVALID_ARG, "out_dtype %d invalid", p->out_dtype);
+    if (p->dipole != MUSE_DIPOLE_NONE && p->dipole != MUSE_DIPOLE_TILTED)
+      return fail(MUSE_ERR_INVALID_ARG, "dipole mode %d invalid", p->dipole);
+    if (p->topk_clusters < 0 || p->topk_blocks < 0) return fail(MUSE_ERR_INVALID_ARG, "retrieval top-k must be >= 0");
+    if (p->topk_clusters > 0 && !s.causal) return fail(MUSE_ERR_INVALID_ARG, "retrieval requires causal=1");
+    if (p->topk_clusters > 0 && p->topk_blocks < 1) return fail(MUSE_ERR_INVALID_ARG, "retrieval needs topk_blocks >= 1");
+    if (p->topk_clusters > 0) return fail(MUSE_ERR_UNSUPPORTED, "retrieval is not implemented in this build");
+  }
+  return MUSE_OK;
+}
+
+int validate_muse(Shape& s, const muse_fwd_params* p) {
+  const int r = validate(s, p);
+  if (r != MUSE_OK) return r;
+  if (s.Cq < 1 || s.Ck < 1 || s.Cq > s.N || s.Ck > s.N)
+    return fail(MUSE_ERR_INVALID_ARG, "clusters Cq=%d Ck=%d must lie in [1, N=%d]", s.Cq, s.Ck, s.N);
+  if (s.Cq > muse::kMaxClusters || s.Ck > muse::kMaxClusters)
+    return fail(MUSE_ERR_UNSUPPORTED, "at most %d clusters per tensor (Cq=%d Ck=%d)", muse::kMaxClusters, s.Cq, s.Ck);
+  if (s.iters < 1) return fail(MUSE_ERR_INVALID_ARG, "kmeans_iters=%d must be >= 1", s.iters);
+  return MUSE_OK;
+}
+
+struct Plan {
+  size_t cent_q, cent_k, lab_q, lab_k, tperm_q, tperm_k, tcnt_q, tcnt_k, tst_q, tst_k, psum_q, psum_k;
+  size_t perm_k, offs_k;
+  size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom;
+  size_t s_logz, s_k, s_v, s_dipT;
+  size_t o_far, l_far;
+  size_t total;
+};
+
+Plan make_plan(const Shape& s) {
+  Layout L;
+  Plan P{};
+  const size_t BH = s.BH, N = s.N, D = s.D, Cq = s.Cq, Ck = s.Ck, nb = s.nb, nbS = s.nbS;
+  const size_t nt = s.ntiles, tile = s.tile;
+  const size_t f = sizeof(float), i4 = sizeof(int32_t);
+  P.cent_q = L.take(BH * Cq * D * f);
+  P.cent_k = L.take(BH * Ck * D * f);
+  P.lab_q = L.take(BH * N * i4);
+  P.lab_k = L.take(BH * N * i4);
+  P.tperm_q = L.take(BH * nt * tile * sizeof(uint16_t));
+  P.tperm_k = L.take(BH * nt * tile * sizeof(uint16_t));
+  P.tcnt_q = L.take(BH * nt * Cq * i4);
+  P.tcnt_k = L.take(BH * nt * Ck * i4);
+  P.tst_q = L.take(BH * nt * Cq * i4);
+  P.tst_k = L.take(BH * nt * Ck * i4);
+  P.psum_q = L.take(BH * nt * Cq * D * f);
+  P.psum_k = L.take(BH * nt * Ck * D * f);
+  P.perm_k = L.take(BH * N * i4);
+  P.offs_k = L.take(BH * (nb * Ck + 1) * i4);
+  P.at_m = L.take(BH * nb * Cq * Ck * f);
+  P.at_z = L.take(BH * nb * Cq * Ck * f);
+  P.at_k = L.take(BH * nb * Cq * Ck * D * f);
+  P.at_v = L.take(BH * nb * Cq * Ck * D * f);
+  P.blk_lmass = L.take(BH * nb * Cq * f);
+  P.blk_mom = L.take(BH * nb * Cq * D * D * f);
+  P.s_logz = L.take(BH * nbS * Cq * Ck * f);
+  P.s_k = L.take(BH * nbS * Cq * Ck * D * f);
+  P.s_v = L.take(BH * nbS * Cq * Ck * D * f);
+  P.s_dipT = L.take(BH * nbS * Cq * D * D * f);
+  if (s.causal) {
+    P.o_far = L.take(BH * N * D * f);
+    P.l_far = L.take(BH * N * f);
+  }
+  P.total = L.bytes;
+  return P;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+float scale_of(const Shape& s, const muse_fwd_params* p) {
+  return (p != nullptr && p->scale > 0.f) ? p->scale : 1.0f / sqrtf(static_cast<float>(s.D));
+}
+
+int out_is_bf16(const Shape& s, const muse_fwd_params* p) {
+  const int od = (p != nullptr && p->out_dtype != -1) ? p->out_dtype : s.dtype;
+  return od == MUSE_BF16;
+}
+
+int run_muse(const void* q, const void* k, const void* v, void* out, const Shape& s,
+             const muse_fwd_params* p, hipStream_t stream, void* ws) {
+  using namespace muse;
+  const Plan P = make_plan(s);
+  const float scale = scale_of(s, p);
+  const int dipole = p ? p->dipole : MUSE_DIPOLE_TILTED;
+
+  KmArgs km{};
+  km.ntensors = 2;
+  km.BH = s.BH;
+  km.N = s.N;
+  km.D = s.D;
+  km.tile = s.tile;
+  km.ntiles = s.ntiles;
+  km.nb = s.nb;
+  km.tiles_per_block = s.tiles_per_block;
+  KmTensor& tq = km.t[0];
+  tq.x = q;
+  tq.C = s.Cq;
+  tq.cent = at<float>(ws, P.cent_q);
+  tq.labels = at<int32_t>(ws, P.lab_q);
+  tq.trace = p ? p->labels_q_trace : nullptr;
+  tq.labels_in = p ? p->labels_q_in : nullptr;
+  tq.tile_perm = at<uint16_t>(ws, P.tperm_q);
+  tq.tile_cnt = at<int32_t>(ws, P.tcnt_q);
+  tq.tile_start = at<int32_t>(ws, P.tst_q);
+  tq.psum = at<float>(ws, P.psum_q);
+  tq.perm = nullptr;
+  tq.offs = nullptr;
+  KmTensor& tk = km.t[1];
+  tk.x = k;
+  tk.C = s.Ck;
+  tk.cent = at<float>(ws, P.cent_k);
+  tk.labels = at<int32_t>(ws, P.lab_k);
+  tk.trace = p ? p->labels_k_trace : nullptr;
+  tk.labels_in = p ? p->labels_k_in : nullptr;
+  tk.tile_perm = at<uint16_t>(ws, P.tperm_k);
+  tk.tile_cnt = at<int32_t>(ws, P.tcnt_k);
+  tk.tile_start = at<int32_t>(ws, P.tst_k);
+  tk.psum = at<float>(ws, P.psum_k);
+  tk.perm = at<int32_t>(ws, P.perm_k);
+  tk.offs = at<int32_t>(ws, P.offs_k);
+  hipError_t e = launch_kmeans(km, s.iters, s.dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "K-means launch");
+
+  S1Args a1{};
+  a1.k = k;
+  a1.v = v;
+  a1.BH = s.BH;
+  a1.N = s.N;
+  a1.D = s.D;
+  a1.Cq = s.Cq;
+  a1.Ck = s.Ck;
+  a1.nb = s.nb;
+  a1.block = s.block;
+  a1.causal = s.causal;
+  a1.nbS = s.nbS;
+  a1.scale = scale;
+  a1.dipole = dipole;
+  a1.qbar = tq.cent;
+  a1.perm_k = tk.perm;
+  a1.offs_k = tk.offs;
+  a1.at_m = at<float>(ws, P.at_m);
+  a1.at_z = at<float>(ws, P.at_z);
+  a1.at_k = at<float>(ws, P.at_k);
+  a1.at_v = at<float>(ws, P.at_v);
+  a1.blk_lmass = at<float>(ws, P.blk_lmass);
+  a1.blk_mom = at<float>(ws, P.blk_mom);
+  a1.s_logz = at<float>(ws, P.s_logz);
+  a1.s_k = at<float>(ws, P.s_k);
+  a1.s_v = at<float>(ws, P.s_v);
+  a1.s_dipT = at<float>(ws, P.s_dipT);
+  e = launch_stage1(a1, s.dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
+
+  S2Args a2{};
+  a2.q = q;
+  a2.out = out;
+  a2.lse_out = p ? p->lse_out : nullptr;
+  a2.BH = s.BH;
+  a2.N = s.N;
+  a2.D = s.D;
+  a2.Cq = s.Cq;
+  a2.Ck = s.Ck;
+  a2.causal = s.causal;
+  a2.block = s.block;
+  a2.nbS = s.nbS;
+  a2.scale = scale;
+  a2.dipole = dipole;
+  a2.out_bf16 = out_is_bf16(s, p);
+  a2.labels_q = tq.labels;
+  a2.qbar = tq.cent;
+  a2.s_logz = a1.s_logz;
+  a2.s_k = a1.s_k;
+  a2.s_v = a1.s_v;
+  a2.s_dipT = a1.s_dipT;
+  if (s.causal) {
+    a2.o_far = at<float>(ws, P.o_far);
+    a2.l_far = at<float>(ws, P.l_far);
+  }
+  e = launch_stage2(a2, s.dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "stage-2 launch");
+
+  if (s.causal) {
+    ExactArgs ax{};
+    ax.q = q;
+    ax.k = k;
+    ax.v = v;
+    ax.out = out;
+    ax.lse_out = p ? p->lse_out : nullptr;
+    ax.o_far = a2.o_far;
+    ax.l_far = a2.l_far;
+    ax.BH = s.BH;
+    ax.N = s.N;
+    ax.D = s.D;
+    ax.causal = 1;
+    ax.block = s.block;
+    ax.scale = scale;
+    ax.out_bf16 = a2.out_bf16;
+    e = launch_exact(ax, s.dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "local block launch");
+  }
+  if (p != nullptr && p->centroids_q_out != nullptr) {
+    e = hipMemcpyAsync(p->centroids_q_out, tq.cent, sizeof(float) * s.BH * s.Cq * s.D, hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "centroid copy");
+  }
+  if (p != nullptr && p->centroids_k_out != nullptr) {
+    e = hipMemcpyAsync(p->centroids_k_out, tk.cent, sizeof(float) * s.BH * s.Ck * s.D, hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "centroid copy");
+  }
+  return MUSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void muse_fwd_params_init(muse_fwd_params* p) {
+  if (p == nullptr) return;
+  memset(p, 0, sizeof(*p));
+  p->scale = 0.f;
+  p->out_dtype = -1;
+  p->dipole = MUSE_DIPOLE_TILTED;
+}
+
+const char* muse_last_error(void) { return g_last_error.c_str(); }
+
+int muse_version(void) { return 100; }
+
+size_t muse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int Cq, int Ck, int causal, int block,
+                                     int dtype, const muse_fwd_params* p) {
+  Shape s{B, H, N, D, Cq, Ck, 1, causal, block, dtype};
+  if (validate_muse(s, p) != MUSE_OK) return 0;
+  return make_plan(s).total;
+}
+
+int muse_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int D,
+                     int Cq, int Ck, int kmeans_iters, int causal, int block, int dtype, void* hip_stream,
+                     const muse_fwd_params* p) {
+  g_last_error.clear();
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(MUSE_ERR_INVALID_ARG, "q, k, v and out must be non-null device pointers");
+  Shape s{B, H, N, D, Cq, Ck, kmeans_iters, causal, block, dtype};
+  int r = validate_muse(s, p);
+  if (r != MUSE_OK) return r;
+  if (out == q || out == k || out == v) return fail(MUSE_ERR_INVALID_ARG, "out must not alias an input");
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const size_t need = make_plan(s).total;
+  void* ws = p ? p->workspace : nullptr;
+  bool owned = false;
+  if (ws != nullptr) {
+    if (p->workspace_bytes < need)
+      return fail(MUSE_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", p->workspace_bytes, need);
+  } else {
+    const hipError_t e = hipMallocAsync(&ws, need, stream);
+    if (e != hipSuccess) return fail(MUSE_ERR_NO_MEMORY, "hipMallocAsync(%zu): %s", need, hipGetErrorString(e));
+    owned = true;
+  }
+  r = run_muse(q, k, v, out, s, p, stream, ws);
+  if (owned) {
+    const hipError_t e = hipFreeAsync(ws, stream);
+    if (e != hipSuccess && r == MUSE_OK) r = hip_fail(e, "hipFreeAsync");
+  }
+  if (r == MUSE_OK && getenv("MUSE_DEBUG_SYNC") != nullptr) {
+    const hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) r = hip_fail(e, "debug sync");
+  }
+  return r;
+}
+
+int muse_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int D, int Cq,
+                  int Ck, int kmeans_iters, int causal, int block, int dtype, void* hip_stream) {
+  return muse_attn_fwd_ex(q, k, v, out, B, H, N, D, Cq, Ck, kmeans_iters, causal, block, dtype, hip_stream,
+                          nullptr);
+}
+
+int muse_exact_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int D,
+                        int causal, int dtype, void* hip_stream) {
+  g_last_error.clear();
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(MUSE_ERR_INVALID_ARG, "q, k, v and out must be non-null device pointers");
+  Shape s{B, H, N, D, 1, 1, 1, causal, 0, dtype};
+  if (causal != 0 && causal != 1) return fail(MUSE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  s.causal = 0;  // validate the shape without the block checks of causal MuSe
+  const int r = validate(s, nullptr);
+  if (r != MUSE_OK) return r;
+  if (out == q || out == k || out == v) return fail(MUSE_ERR_INVALID_ARG, "out must not alias an input");
+  muse::ExactArgs ax{};
+  ax.q = q;
+  ax.k = k;
+  ax.v = v;
+  ax.out = out;
+  ax.BH = s.BH;
+  ax.N = N;
+  ax.D = D;
+  ax.causal = causal;
+  ax.block = 0;
+  ax.scale = 1.0f / sqrtf(static_cast<float>(D));
+  ax.out_bf16 = dtype == MUSE_BF16;
+  const hipError_t e = muse::launch_exact(ax, dtype, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "exact attention launch");
+  return MUSE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Kernel argument blocks and launcher declarations of the MuSe HIP library.
+#pragma once
+
+#include "muse_common.hpp"
+
+namespace muse {
+
+constexpr int kChunkC = 32;    // centroids staged in LDS at a time by the fp32 assign kernel
+constexpr int kMaxTile = 512;  // K-means tile (points per workgroup) upper bound
+constexpr int kMaxClusters = 128;
+
+// ------------------------------------------------------------------ K-means
+
+struct KmTensor {
+  const void* x;               // [BH, N, D] input (dtype of the call)
+  int C;                       // clusters
+  float* cent;                 // [BH, C, D] current centroids
+  int32_t* labels;             // [BH, N] labels of the latest assign step
+  int32_t* trace;              // [iters, BH, N] or null
+  const int32_t* labels_in;    // [BH, N] caller-fixed labels or null
+  uint16_t* tile_perm;         // [BH, ntiles, tile] tile-local stable order by label
+  int32_t* tile_cnt;           // [BH, ntiles, C]
+  int32_t* tile_start;         // [BH, ntiles, C]
+  float* psum;                 // [BH, ntiles, C, D] per-tile cluster sums
+  int32_t* perm;               // [BH, N] points ordered by (block, label, position), or null
+  int32_t* offs;               // [BH, nb*C + 1] bucket offsets into perm
+};
+
+struct KmArgs {
+  KmTensor t[2];
+  int ntensors;
+  int BH, N, D;
+  int tile, ntiles;            // points per tile, tiles per head
+  int nb, tiles_per_block;     // spatial blocks (1 when acausal) and tiles in one
+};
+
+hipError_t launch_kmeans(const KmArgs& a, int iters, int dtype, hipStream_t s);
+
+// ------------------------------------------------------------------ stage 1
+
+struct S1Args {
+  const void* k;               // [BH, N, D]
+  const void* v;               // [BH, N, D]
+  int BH, N, D, Cq, Ck;
+  int nb, block;               // key blocks (1 and N when acausal)
+  int causal;                  // table entry b holds blocks < b (causal) or all keys (acausal)
+  int nbS;                     // table entries: nb when causal, 1 when acausal
+  float scale;
+  int dipole;
+  const float* qbar;           // [BH, Cq, D] query centroids
+  const int32_t* perm_k;       // [BH, N] keys by (block, label)
+  const int32_t* offs_k;       // [BH, nb*Ck + 1]
+  // atoms: one (query cluster i, key cluster j, key block b') each
+  float* at_m;                 // [BH, nb, Cq, Ck] max logit
+  float* at_z;                 // [BH, nb, Cq, Ck] sum exp(a - m)
+  float* at_k;                 // [BH, nb, Cq, Ck, D] sum exp(a - m) k
+  float* at_v;                 // [BH, nb, Cq, Ck, D] sum exp(a - m) v
+  float* blk_lmass;            // [BH, nb, Cq] log mass of a block seen by centroid i
+  float* blk_mom;              // [BH, nb, Cq, D, D] block-normalised sum w v k^T (v index first)
+  // summary tables
+  float* s_logz;               // [BH, nbS, Cq, Ck]
+  float* s_k;                  // [BH, nbS, Cq, Ck, D] tilted key means
+  float* s_v;                  // [BH, nbS, Cq, Ck, D] tilted value means
+  float* s_dipT;               // [BH, nbS, Cq, D(k), D(v)] aggregated dipole, key index first
+};
+
+hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);
+
+// ------------------------------------------------------------------ stage 2
+
+struct S2Args {
+  const void* q;               // [BH, N, D]
+  void* out;                   // [BH, N, D] (acausal) in out dtype
+  float* o_far;                // [BH, N, D] f32 (causal far field) or null
+  float* l_far;                // [BH, N] (causal) or null
+  float* lse_out;              // [BH, N] (acausal) or null
+  int BH, N, D, Cq, Ck;
+  int causal, block, nbS;
+  float scale;
+  int dipole;
+  int out_bf16;
+  const int32_t* labels_q;     // [BH, N]
+  const float* qbar;           // [BH, Cq, D]
+  const float* s_logz;
+  const float* s_k;
+  const float* s_v;
+  const float* s_dipT;
+};
+
+hipError_t launch_stage2(const S2Args& a, int dtype, hipStream_t s);
+
+// ------------------------------------------------------------------ exact attention
+
+struct ExactArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;                   // [BH, N, D] in out dtype
+  float* lse_out;              // [BH, N] or null
+  const float* o_far;          // far-field partial result to merge, or null
+  const float* l_far;
+  int BH, N, D;
+  int causal;
+  int block;                   // > 0: keys restricted to the query's own block (local)
+  float scale;
+  int out_bf16;
+};
+
+hipError_t launch_exact(const ExactArgs& a, int dtype, hipStream_t s);
+
+}  // namespace muse

@@ -1,0 +1,379 @@
+// Stage 1 of MuSe: coarse query centroids attend to fine key clusters (gfx950).
+//
+// For query centroid qbar_i and the keys m of key cluster j (pith.science review of
+// arXiv 2509.10406, "What carries the argument"; gist.science summary,
+// Kernmechanismen 2, "Exponential Tilting"), with a_m = s qbar_i . k_m:
+//   log Z_ij = logsumexp_m a_m,   K_ij = sum_m w_m k_m,   V_ij = sum_m w_m v_m,
+//   w_m = exp(a_m) / Z_ij,  and the aggregated dipole
+//   D_i = sum_j P_ij C_ij = E_i[v k^T] - sum_j P_ij V_ij K_ij^T,
+// where P_ij = Z_ij / sum_j' Z_ij' and E_i is the expectation under the softmax of
+// a_m over all keys (the two forms are equal because P_ij w_m = exp(a_m) / Z_i).
+//
+// Keys are processed per spatial block b' ("atoms" (i, j, b')): acausal calls have
+// a single block. Causal calls accumulate the atoms of all preceding blocks
+// (gist.science summary, Kernmechanismen 3) by a log-sum-exp fold over blocks.
+//
+// Kernels (all sums in a fixed order; no floating-point atomics):
+//   s1_atoms      one workgroup per (j, b', head): online log-sum-exp over the
+//                 bucket's keys for every centroid i.
+//   s1_moments    one workgroup per (i, b', head): block-normalised sum w v k^T.
+//   s1_prefix     fold of atoms over blocks -> log Z, K, V tables.
+//   s1_mom_prefix fold of block moments over blocks -> E_i[v k^T] per table entry.
+//   s1_dip_final  D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T (stored key index first).
+#include "muse_kernels.hpp"
+
+namespace muse {
+
+// keys staged in LDS per step (fewer for D = 128 to keep LDS under budget)
+template <int D>
+struct S1Keys {
+  static constexpr int value = D == 64 ? 64 : 32;
+};
+
+// LDS: qb [Cq][D] | kc [64][D] | vc [64][D] | sa [Cq][64] | sm, sz, salpha [Cq]
+template <typename T, int D>
+__global__ void __launch_bounds__(256) s1_atoms_kernel(S1Args a) {
+  constexpr int kS1Keys = S1Keys<D>::value;
+  extern __shared__ __align__(16) float sh[];
+  const int j = blockIdx.x, bp = blockIdx.y, bh = blockIdx.z;
+  const int Cq = a.Cq, Ck = a.Ck, tid = threadIdx.x;
+  float* qb = sh;
+  float* kc = qb + Cq * D;
+  float* vc = kc + kS1Keys * D;
+  float* sa = vc + kS1Keys * D;
+  float* sm = sa + Cq * kS1Keys;
+  float* sz = sm + Cq;
+  float* salpha = sz + Cq;
+
+  const int32_t* offs = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
+  const int seg0 = offs[bp * Ck + j], seg1 = offs[bp * Ck + j + 1];
+  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
+  const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+
+  for (int e = tid; e < Cq * D; e += 256) qb[e] = a.qbar[static_cast<size_t>(bh) * Cq * D + e];
+  for (int i = tid; i < Cq; i += 256) {
+    sm[i] = kNegInf;
+    sz[i] = 0.f;
+  }
+  constexpr int kMaxPairs = kMaxClusters * D / 256;
+  const int npairs = (Cq * D + 255) / 256;
+  float accK[kMaxPairs], accV[kMaxPairs];
+#pragma unroll
+  for (int r = 0; r < kMaxPairs; ++r) accK[r] = accV[r] = 0.f;
+
+  for (int c0 = seg0; c0 < seg1; c0 += kS1Keys) {
+    const int nk = min(kS1Keys, seg1 - c0);
+    __syncthreads();
+    for (int e = tid; e < nk * D; e += 256) {
+      const int m = e / D, d = e % D;
+      const size_t row = static_cast<size_t>(perm[c0 + m]) * D;
+      kc[e] = Elem<T>::load(K, row + d);
+      vc[e] = Elem<T>::load(V, row + d);
+    }
+    __syncthreads();
+    for (int e = tid; e < Cq * kS1Keys; e += 256) {
+      const int i = e / kS1Keys, m = e % kS1Keys;
+      float dot = 0.f;
+      if (m < nk) {
+#pragma unroll 16
+        for (int d = 0; d < D; ++d) dot = fmaf(qb[i * D + d], kc[m * D + d], dot);
+      }
+      sa[e] = m < nk ? a.scale * dot : kNegInf;
+    }
+    __syncthreads();
+    for (int i = tid; i < Cq; i += 256) {
+      float cmax = kNegInf;
+      for (int m = 0; m < nk; ++m) cmax = fmaxf(cmax, sa[i * kS1Keys + m]);
+      const float newm = fmaxf(sm[i], cmax);
+      const float alpha = (sm[i] == kNegInf) ? 0.f : __expf(sm[i] - newm);
+      float zc = 0.f;
+      for (int m = 0; m < kS1Keys; ++m) {
+        const float e = (m < nk) ? __expf(sa[i * kS1Keys + m] - newm) : 0.f;
+        sa[i * kS1Keys + m] = e;
+        zc += e;
+      }
+      sz[i] = sz[i] * alpha + zc;
+      sm[i] = newm;
+      salpha[i] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kMaxPairs; ++r) {
+      if (r >= npairs) break;
+      const int p = tid + 256 * r;
+      if (p >= Cq * D) break;
+      const int i = p / D, d = p % D;
+      float sk = 0.f, sv = 0.f;
+      for (int m = 0; m < nk; ++m) {
+        const float w = sa[i * kS1Keys + m];
+        sk = fmaf(w, kc[m * D + d], sk);
+        sv = fmaf(w, vc[m * D + d], sv);
+      }
+      accK[r] = accK[r] * salpha[i] + sk;
+      accV[r] = accV[r] * salpha[i] + sv;
+    }
+  }
+  __syncthreads();
+  const size_t abase = (static_cast<size_t>(bh) * a.nb + bp) * Cq;  // [.., i, j]
+  for (int i = tid; i < Cq; i += 256) {
+    a.at_m[(abase + i) * Ck + j] = sm[i];
+    a.at_z[(abase + i) * Ck + j] = sz[i];
+  }
+#pragma unroll
+  for (int r = 0; r < kMaxPairs; ++r) {
+    if (r >= npairs) break;
+    const int p = tid + 256 * r;
+    if (p >= Cq * D) break;
+    const int i = p / D, d = p % D;
+    a.at_k[((abase + i) * Ck + j) * D + d] = accK[r];
+    a.at_v[((abase + i) * Ck + j) * D + d] = accV[r];
+  }
+}
+
+// Block log-mass R_ib' = logsumexp_j (m_ij + log z_ij) and block-normalised moments
+// sum_m exp(a_m - R) v_m k_m^T over the keys of block b'.
+// Thread layout: 16x16 grid of threads, each owning a (D/16)x(D/16) tile of (dv, dk).
+template <typename T, int D>
+__global__ void __launch_bounds__(256) s1_moments_kernel(S1Args a) {
+  constexpr int TD = D / 16;
+  constexpr int kS1Keys = S1Keys<D>::value;
+  extern __shared__ __align__(16) float sh[];
+  const int i = blockIdx.x, bp = blockIdx.y, bh = blockIdx.z;
+  const int Cq = a.Cq, Ck = a.Ck, tid = threadIdx.x;
+  float* qb = sh;                  // [D]
+  float* kc = qb + D;              // [64][D]
+  float* vc = kc + kS1Keys * D;    // [64][D]
+  float* w = vc + kS1Keys * D;     // [64]
+  float* red = w + kS1Keys;        // [1]
+
+  for (int d = tid; d < D; d += 256) qb[d] = a.qbar[(static_cast<size_t>(bh) * Cq + i) * D + d];
+  const size_t abase = ((static_cast<size_t>(bh) * a.nb + bp) * Cq + i) * Ck;
+  if (tid < 64) {
+    float mx = kNegInf;
+    for (int j = tid; j < Ck; j += 64) {
+      const float z = a.at_z[abase + j];
+      if (z > 0.f) mx = fmaxf(mx, a.at_m[abase + j] + __logf(z));
+    }
+    mx = wave_max(mx);
+    float s = 0.f;
+    for (int j = tid; j < Ck; j += 64) {
+      const float z = a.at_z[abase + j];
+      if (z > 0.f) s += __expf(a.at_m[abase + j] + __logf(z) - mx);
+    }
+    s = wave_sum(s);
+    if (tid == 0) red[0] = (mx == kNegInf) ? kNegInf : mx + __logf(s);
+  }
+  __syncthreads();
+  const float R = red[0];
+  if (tid == 0) a.blk_lmass[(static_cast<size_t>(bh) * a.nb + bp) * Cq + i] = R;
+
+  const int tr = tid / 16, tc = tid % 16;  // rows dv = tr*TD.., cols dk = tc*TD..
+  float acc[TD][TD];
+#pragma unroll
+  for (int x = 0; x < TD; ++x)
+#pragma unroll
+    for (int y = 0; y < TD; ++y) acc[x][y] = 0.f;
+
+  const int key0 = a.causal ? bp * a.block : 0;
+  const int key1 = a.causal ? key0 + a.block : a.N;
+  const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+  if (R != kNegInf) {
+    for (int c0 = key0; c0 < key1; c0 += kS1Keys) {
+      const int nk = min(kS1Keys, key1 - c0);
+      __syncthreads();
+      for (int e = tid; e < nk * D; e += 256) {
+        kc[e] = Elem<T>::load(K, static_cast<size_t>(c0) * D + e);
+        vc[e] = Elem<T>::load(V, static_cast<size_t>(c0) * D + e);
+      }
+      __syncthreads();
+      if (tid < kS1Keys) {
+        float dot = 0.f;
+        if (tid < nk) {
+#pragma unroll 16
+          for (int d = 0; d < D; ++d) dot = fmaf(qb[d], kc[tid * D + d], dot);
+        }
+        w[tid] = (tid < nk) ? __expf(a.scale * dot - R) : 0.f;
+      }
+      __syncthreads();
+      for (int m = 0; m < nk; ++m) {
+        const float wm = w[m];
+        float vr[TD], kr[TD];
+#pragma unroll
+        for (int x = 0; x < TD; ++x) vr[x] = wm * vc[m * D + tr * TD + x];
+#pragma unroll
+        for (int y = 0; y < TD; ++y) kr[y] = kc[m * D + tc * TD + y];
+#pragma unroll
+        for (int x = 0; x < TD; ++x)
+#pragma unroll
+          for (int y = 0; y < TD; ++y) acc[x][y] = fmaf(vr[x], kr[y], acc[x][y]);
+      }
+    }
+  }
+  float* out = a.blk_mom + ((static_cast<size_t>(bh) * a.nb + bp) * Cq + i) * D * D;
+#pragma unroll
+  for (int x = 0; x < TD; ++x)
+#pragma unroll
+    for (int y = 0; y < TD; ++y) out[(tr * TD + x) * D + tc * TD + y] = acc[x][y];
+}
+
+// Fold atoms over blocks: one workgroup per (j, i, head), 2*D threads (K then V dims).
+__global__ void s1_prefix_kernel(S1Args a) {
+  const int j = blockIdx.x, i = blockIdx.y, bh = blockIdx.z;
+  const int D = a.D, Cq = a.Cq, Ck = a.Ck;
+  const int t = threadIdx.x;
+  const bool isK = t < D;
+  const int d = isK ? t : t - D;
+  float rm = kNegInf, rz = 0.f, racc = 0.f;
+  auto emit = [&](int b) {
+    const size_t sidx = ((static_cast<size_t>(bh) * a.nbS + b) * Cq + i) * Ck + j;
+    const bool any = rz > 0.f;
+    if (t == 0) a.s_logz[sidx] = any ? rm + __logf(rz) : kNegInf;
+    float* dst = isK ? a.s_k : a.s_v;
+    dst[sidx * D + d] = any ? racc / rz : 0.f;
+  };
+  for (int b = 0; b < a.nb; ++b) {
+    if (a.causal) emit(b);  // entry b: blocks < b
+    const size_t aidx = ((static_cast<size_t>(bh) * a.nb + b) * Cq + i) * Ck + j;
+    const float m = a.at_m[aidx], z = a.at_z[aidx];
+    if (z > 0.f) {
+      const float x = (isK ? a.at_k : a.at_v)[aidx * D + d];
+      const float nm = fmaxf(rm, m);
+      const float f0 = (rz > 0.f) ? __expf(rm - nm) : 0.f;
+      const float f1 = __expf(m - nm);
+      rz = rz * f0 + z * f1;
+      racc = racc * f0 + x * f1;
+      rm = nm;
+    }
+  }
+  if (!a.causal) emit(0);
+}
+
+// Fold block moments: thread per (dv, dk) element; entry b is normalised by its mass.
+__global__ void s1_mom_prefix_kernel(S1Args a) {
+  const int D = a.D, Cq = a.Cq;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.y, bh = blockIdx.z;
+  if (e >= D * D) return;
+  const int dv = e / D, dk = e % D;
+  float rR = kNegInf, racc = 0.f;
+  auto emit = [&](int b) {
+    // stored key index first: [dk][dv]
+    const size_t sbase = ((static_cast<size_t>(bh) * a.nbS + b) * Cq + i) * D * D;
+    a.s_dipT[sbase + static_cast<size_t>(dk) * D + dv] = (rR == kNegInf) ? 0.f : racc;
+  };
+  for (int b = 0; b < a.nb; ++b) {
+    if (a.causal) emit(b);
+    const size_t bidx = (static_cast<size_t>(bh) * a.nb + b) * Cq + i;
+    const float R = a.blk_lmass[bidx];
+    if (R != kNegInf) {
+      const float x = a.blk_mom[bidx * D * D + e];
+      const float nR = (rR == kNegInf) ? R : fmaxf(rR, R) + __logf(1.f + __expf(-fabsf(rR - R)));
+      const float f0 = (rR == kNegInf) ? 0.f : __expf(rR - nR);
+      const float f1 = __expf(R - nR);
+      racc = racc * f0 + x * f1;
+      rR = nR;
+    }
+  }
+  if (!a.causal) emit(0);
+}
+
+// D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T for one table entry; one workgroup per
+// (i, b, head); thread tiles as in s1_moments.
+template <int D>
+__global__ void __launch_bounds__(256) s1_dip_final_kernel(S1Args a) {
+  constexpr int TD = D / 16;
+  extern __shared__ __align__(16) float sh[];
+  const int i = blockIdx.x, b = blockIdx.y, bh = blockIdx.z;
+  const int Cq = a.Cq, Ck = a.Ck, tid = threadIdx.x;
+  if (a.causal && b == 0) return;  // block 0 has no far field
+  const size_t sidx = ((static_cast<size_t>(bh) * a.nbS + b) * Cq + i);
+  float* P = sh;                    // [Ck]
+  float* kc = P + kMaxClusters;     // [32][D]
+  float* vc = kc + 32 * D;          // [32][D]
+  float* red = vc + 32 * D;
+  if (tid < 64) {
+    float mx = kNegInf;
+    for (int j = tid; j < Ck; j += 64) mx = fmaxf(mx, a.s_logz[sidx * Ck + j]);
+    mx = wave_max(mx);
+    float s = 0.f;
+    for (int j = tid; j < Ck; j += 64) {
+      const float l = a.s_logz[sidx * Ck + j];
+      const float p = (l == kNegInf) ? 0.f : __expf(l - mx);
+      P[j] = p;
+      s += p;
+    }
+    s = wave_sum(s);
+    if (tid == 0) red[0] = s;
+  }
+  __syncthreads();
+  const float inv = red[0] > 0.f ? 1.f / red[0] : 0.f;
+  const int tr = tid / 16, tc = tid % 16;
+  float acc[TD][TD];
+#pragma unroll
+  for (int x = 0; x < TD; ++x)
+#pragma unroll
+    for (int y = 0; y < TD; ++y) acc[x][y] = 0.f;
+  for (int j0 = 0; j0 < Ck; j0 += 32) {
+    const int nj = min(32, Ck - j0);
+    __syncthreads();
+    for (int e = tid; e < nj * D; e += 256) {
+      kc[e] = a.s_k[(sidx * Ck + j0) * D + e];
+      vc[e] = a.s_v[(sidx * Ck + j0) * D + e];
+    }
+    __syncthreads();
+    for (int jj = 0; jj < nj; ++jj) {
+      const float p = P[j0 + jj] * inv;
+      float vr[TD], kr[TD];
+#pragma unroll
+      for (int x = 0; x < TD; ++x) vr[x] = p * vc[jj * D + tr * TD + x];
+#pragma unroll
+      for (int y = 0; y < TD; ++y) kr[y] = kc[jj * D + tc * TD + y];
+#pragma unroll
+      for (int x = 0; x < TD; ++x)
+#pragma unroll
+        for (int y = 0; y < TD; ++y) acc[x][y] = fmaf(vr[x], kr[y], acc[x][y]);
+    }
+  }
+  float* dipT = a.s_dipT + sidx * D * D;
+#pragma unroll
+  for (int x = 0; x < TD; ++x)
+#pragma unroll
+    for (int y = 0; y < TD; ++y) {
+      const size_t o = static_cast<size_t>(tc * TD + y) * D + (tr * TD + x);  // [dk][dv]
+      dipT[o] = dipT[o] - acc[x][y];
+    }
+}
+
+template <typename T, int D>
+static void launch_stage1_t(const S1Args& a, hipStream_t s) {
+  constexpr int kS1Keys = S1Keys<D>::value;
+  const size_t lds_atoms = sizeof(float) * (static_cast<size_t>(a.Cq) * D + 2 * kS1Keys * D +
+                                            static_cast<size_t>(a.Cq) * kS1Keys + 3 * a.Cq);
+  allow_lds((const void*)s1_atoms_kernel<T, D>, lds_atoms);
+  hipLaunchKernelGGL((s1_atoms_kernel<T, D>), dim3(a.Ck, a.nb, a.BH), dim3(256), lds_atoms, s, a);
+  hipLaunchKernelGGL(s1_prefix_kernel, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
+  if (a.dipole) {
+    const size_t lds_mom = sizeof(float) * (D + 2 * kS1Keys * D + kS1Keys + 4);
+    allow_lds((const void*)s1_moments_kernel<T, D>, lds_mom);
+    hipLaunchKernelGGL((s1_moments_kernel<T, D>), dim3(a.Cq, a.nb, a.BH), dim3(256), lds_mom, s, a);
+    hipLaunchKernelGGL(s1_mom_prefix_kernel, dim3((D * D + 255) / 256, a.Cq, a.BH), dim3(256), 0, s, a);
+    const size_t lds_fin = sizeof(float) * (kMaxClusters + 64 * D + 4);
+    allow_lds((const void*)s1_dip_final_kernel<D>, lds_fin);
+    hipLaunchKernelGGL((s1_dip_final_kernel<D>), dim3(a.Cq, a.nbS, a.BH), dim3(256), lds_fin, s, a);
+  }
+}
+
+hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s) {
+  if (dtype == 0) {
+    if (a.D == 64) launch_stage1_t<float, 64>(a, s);
+    else launch_stage1_t<float, 128>(a, s);
+  } else {
+    if (a.D == 64) launch_stage1_t<bf16, 64>(a, s);
+    else launch_stage1_t<bf16, 128>(a, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace muse

@@ -1,0 +1,133 @@
+/*
+ * muse.h - C ABI of the MI355X (gfx950) Multipole Semantic Attention forward pass.
+ *
+ * Method (arXiv 2509.10406, R. Mitchell and K. Kersting, known here from the
+ * pith.science review page, the pith.science verdict record, the gist.science
+ * technical summary and the fugumt.com v2 abstract):
+ *   - queries and keys are clustered separately with K-means (gist.science,
+ *     Kernmechanismen 1; pith.science review, "Core claim");
+ *   - stage 1: coarse query centroids attend to fine key clusters and form
+ *     exponentially tilted key/value means, log-normalisers and a tilted
+ *     value-key covariance (pith.science review, "What carries the argument");
+ *   - stage 2: every query refines its cluster's summaries with its residual:
+ *     monopole plus dipole (gist.science, Kernmechanismen 2);
+ *   - causal: exact attention inside each diagonal block plus summaries of all
+ *     preceding blocks (pith.science review, caption of Figure 2; gist.science,
+ *     Kernmechanismen 3), optionally with retrieval of the top (cluster, block)
+ *     pairs attended exactly (gist.science, Kernmechanismen 4).
+ *
+ * Conventions shared by every entry point
+ *   - q, k, v, out: DEVICE pointers to contiguous [B, H, N, D] tensors, row-major
+ *     with D fastest, 16-byte aligned, owned by the caller. out must not alias an
+ *     input. Every element of out is written; nothing is accumulated into it.
+ *   - dtype: MUSE_F32 or MUSE_BF16 (storage type of q, k, v; bfloat16 as raw
+ *     16-bit patterns). All arithmetic accumulates in fp32.
+ *   - hip_stream: a hipStream_t (NULL = the default stream). Calls only enqueue
+ *     work on it and return; there is no host synchronisation inside. Pointers
+ *     must stay valid until that work completes.
+ *   - Errors: arguments are validated on the host before anything is launched; a
+ *     negative status is returned and muse_last_error() describes it. A launch
+ *     failure returns MUSE_ERR_HIP. Faults during execution surface at the
+ *     caller's next synchronisation. No exception or abort crosses the ABI.
+ *   - Determinism: identical inputs on the same device give bitwise identical
+ *     outputs (no floating-point atomics anywhere).
+ *   - Supported shapes: B, H, N >= 1; D in {64, 128}; 1 <= Cq, Ck <= min(N, 256);
+ *     kmeans_iters >= 1. Causal: 64 <= block <= N, N % block == 0,
+ *     block % 64 == 0.
+ */
+#ifndef MUSE_H_
+#define MUSE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MUSE_F32 = 0, MUSE_BF16 = 1 } muse_dtype_t;
+
+enum {
+  MUSE_OK = 0,
+  MUSE_ERR_INVALID_ARG = -1, /* a pointer, size or flag is out of range         */
+  MUSE_ERR_UNSUPPORTED = -2, /* valid, but not a shape this build implements    */
+  MUSE_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed      */
+  MUSE_ERR_NO_MEMORY = -4,   /* workspace allocation failed                     */
+  MUSE_ERR_WORKSPACE = -5    /* caller workspace too small                      */
+};
+
+enum { MUSE_DIPOLE_NONE = 0, MUSE_DIPOLE_TILTED = 1 };
+
+/*
+ * MuSe forward pass (acausal when causal == 0).
+ *
+ * Cq, Ck       number of query / key clusters per (b, h) head, fitted over the
+ *              whole sequence of that head (also when causal).
+ * kmeans_iters Lloyd iterations: strided init c_j = x[floor(j*N/C)], then
+ *              kmeans_iters x (assign to the nearest centroid in Euclidean
+ *              distance, ties to the lowest index; update to member means, an
+ *              empty cluster keeps its centroid). pith.science review,
+ *              "Assumptions & free parameters": K-means iterations.
+ * causal,block causal = 1: spatial blocks of `block` tokens; exact causal
+ *              attention inside each block, merged by log-sum-exp with the
+ *              two-stage approximation over all keys of earlier blocks.
+ * Softmax scale 1/sqrt(D); output dtype = input dtype; tilted dipole on.
+ */
+int muse_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                  int B, int H, int N, int D, int Cq, int Ck,
+                  int kmeans_iters, int causal, int block,
+                  int dtype, void* hip_stream);
+
+/*
+ * Exact softmax attention softmax(s q k^T) v (causal: key m <= query n), the
+ * quantity MuSe approximates (gist.science, "Probleemstelling"); the in-library
+ * comparator. Same tensor conventions; scale 1/sqrt(D); out dtype = dtype.
+ */
+int muse_exact_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                        int B, int H, int N, int D, int causal,
+                        int dtype, void* hip_stream);
+
+/* Optional controls of muse_attn_fwd_ex. Fill with muse_fwd_params_init(). */
+typedef struct muse_fwd_params {
+  float scale;          /* softmax scale; <= 0 means 1/sqrt(D)                        */
+  int out_dtype;        /* -1: same as input; else MUSE_F32 or MUSE_BF16              */
+  int dipole;           /* MUSE_DIPOLE_TILTED (default) or MUSE_DIPOLE_NONE           */
+  int topk_clusters;    /* retrieval k1 (causal only); 0 = off                        */
+  int topk_blocks;      /* retrieval k2 (>= 1 when k1 > 0)                            */
+  const int32_t* labels_q_in;  /* device [B,H,N]: fixed query clusters, skips Q K-means */
+  const int32_t* labels_k_in;  /* device [B,H,N]: fixed key clusters, skips K K-means   */
+  int32_t* labels_q_trace;     /* device [iters,B,H,N]: labels of every assign step      */
+  int32_t* labels_k_trace;     /* device [iters,B,H,N]                                   */
+  float* centroids_q_out;      /* device [B,H,Cq,D]: final query centroids               */
+  float* centroids_k_out;      /* device [B,H,Ck,D]: final key centroids                 */
+  float* lse_out;              /* device [B,H,N]: log of each row's softmax normaliser   */
+  void* workspace;             /* device scratch; NULL = stream-ordered allocation       */
+  size_t workspace_bytes;      /* size of `workspace`                                     */
+} muse_fwd_params;
+
+/* Defaults: scale 0, out_dtype -1, dipole tilted, retrieval off, all pointers NULL. */
+void muse_fwd_params_init(muse_fwd_params* p);
+
+/* muse_attn_fwd with optional controls; p == NULL means defaults. With fixed
+ * labels (labels_*_in) the centroids are the member means of those labels. */
+int muse_attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
+                     int B, int H, int N, int D, int Cq, int Ck,
+                     int kmeans_iters, int causal, int block,
+                     int dtype, void* hip_stream, const muse_fwd_params* p);
+
+/* Device scratch bytes muse_attn_fwd_ex needs for this shape (0 on invalid
+ * arguments, with muse_last_error() set). */
+size_t muse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int Cq, int Ck,
+                                     int causal, int block, int dtype,
+                                     const muse_fwd_params* p);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* muse_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int muse_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MUSE_H_ */

@@ -1,0 +1,95 @@
+"""The C-ABI library loads and exports every symbol include/muse.h declares; argument
+validation runs on the host before any launch (CPU only: no GPU call is made)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muse.h")
+LIB = os.path.join(ROOT, "clustered_softmax_attention_amd", "libmuse.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muse_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from clustered_softmax_attention_amd import build
+        build.build(verbose=False)
+    from clustered_softmax_attention_amd import binding
+    return binding.load(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("muse_attn_fwd", "muse_exact_attn_fwd", "muse_attn_fwd_ex", "muse_attn_fwd_workspace_bytes",
+              "muse_fwd_params_init", "muse_last_error", "muse_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (muse_\w+)", out))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_binding_covers_the_exports():
+    from clustered_softmax_attention_amd import binding
+    assert sorted(binding.EXPORTED) == declared_functions()
+
+
+def test_params_struct_layout_matches(lib):
+    from clustered_softmax_attention_amd.binding import FwdParams
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    assert p.out_dtype == -1 and p.dipole == 1 and p.scale == 0.0 and p.topk_clusters == 0
+    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8  # 5 ints/floats, pad, 8 pointers, size_t
+
+
+def _call(lib, **kw):
+    args = dict(q=1, k=2, v=3, out=4, B=1, H=1, N=1024, D=64, Cq=8, Ck=32, iters=5, causal=0, block=0, dtype=0)
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return lib.muse_attn_fwd(vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["out"]), args["B"], args["H"],
+                             args["N"], args["D"], args["Cq"], args["Ck"], args["iters"], args["causal"],
+                             args["block"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), -1), (dict(D=96), -2), (dict(N=0), -1), (dict(Cq=0), -1), (dict(Ck=2000), -1),
+    (dict(Cq=200, N=4096), -2), (dict(iters=0), -1), (dict(dtype=7), -1),
+    (dict(causal=1, block=100), -1), (dict(causal=1, block=0), -1), (dict(causal=1, block=2048), -1),
+    (dict(causal=2), -1), (dict(out=1), -1),
+])
+def test_invalid_arguments_are_rejected_before_launch(lib, kw, code):
+    assert _call(lib, **kw) == code
+    assert lib.muse_last_error().decode() != ""
+
+
+def test_workspace_query(lib):
+    from clustered_softmax_attention_amd.binding import FwdParams
+    n_ac = lib.muse_attn_fwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, None)
+    n_c = lib.muse_attn_fwd_workspace_bytes(8, 8, 16384, 64, 16, 64, 1, 1024, 1, None)
+    assert n_ac > 0 and n_c > 0
+    assert lib.muse_attn_fwd_workspace_bytes(1, 1, 1024, 65, 8, 32, 0, 0, 1, None) == 0
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    p.topk_clusters = 2  # acausal retrieval is invalid
+    assert lib.muse_attn_fwd_workspace_bytes(1, 1, 1024, 64, 8, 32, 0, 0, 1, ctypes.byref(p)) == 0
+
+
+def test_exact_rejects_bad_shapes(lib):
+    vp = ctypes.c_void_p
+    assert lib.muse_exact_attn_fwd(vp(1), vp(2), vp(3), vp(4), 1, 1, 64, 80, 0, 1, None) == -2
+    assert lib.muse_exact_attn_fwd(vp(1), vp(2), vp(3), None, 1, 1, 64, 64, 0, 1, None) == -1
+    assert lib.muse_version() >= 100
