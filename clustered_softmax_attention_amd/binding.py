@@ -24,7 +24,9 @@ STATUS = {0: "MUSE_OK", -1: "MUSE_ERR_INVALID_ARG", -2: "MUSE_ERR_UNSUPPORTED", 
 
 # C entry points declared in include/muse.h
 EXPORTED = ("muse_attn_fwd", "muse_exact_attn_fwd", "muse_attn_fwd_ex", "muse_fwd_params_init",
-            "muse_attn_fwd_workspace_bytes", "muse_last_error", "muse_version")
+            "muse_attn_fwd_workspace_bytes", "muse_last_error", "muse_version", "muse_prof_enable",
+            "muse_prof_collect", "muse_prof_name", "muse_prof_total_ms", "muse_prof_launches",
+            "muse_prof_reset")
 
 
 class MuseError(RuntimeError):
@@ -75,6 +77,18 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.muse_last_error.restype = ctypes.c_char_p
     lib.muse_version.argtypes = []
     lib.muse_version.restype = i
+    lib.muse_prof_enable.argtypes = [i]
+    lib.muse_prof_enable.restype = None
+    lib.muse_prof_collect.argtypes = []
+    lib.muse_prof_collect.restype = i
+    lib.muse_prof_name.argtypes = [i]
+    lib.muse_prof_name.restype = ctypes.c_char_p
+    lib.muse_prof_total_ms.argtypes = [i]
+    lib.muse_prof_total_ms.restype = ctypes.c_double
+    lib.muse_prof_launches.argtypes = [i]
+    lib.muse_prof_launches.restype = ctypes.c_long
+    lib.muse_prof_reset.argtypes = []
+    lib.muse_prof_reset.restype = None
     _lib = lib
     return lib
 
@@ -170,6 +184,22 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
                                 int(causal), int(block), _dtype_code(q), _stream(), ctypes.byref(p)))
     del keep
     return (out, extras) if extras else out
+
+
+def prof_enable(on: bool = True):
+    """Bracket every library kernel launch with HIP events (see muse_prof_* in muse.h)."""
+    load().muse_prof_enable(int(on))
+
+
+def prof_reset():
+    load().muse_prof_reset()
+
+
+def prof_collect() -> dict:
+    """{kernel name: (total ms, launches)} accumulated since the last reset (blocks on events)."""
+    lib = load()
+    n = lib.muse_prof_collect()
+    return {lib.muse_prof_name(i).decode(): (lib.muse_prof_total_ms(i), lib.muse_prof_launches(i)) for i in range(n)}
 
 
 def workspace_bytes(B, H, N, D, Cq, Ck, causal=False, block=0, dtype=MUSE_BF16, topk_clusters=0,

@@ -107,6 +107,7 @@ __global__ void __launch_bounds__(kExThreads) exact_valu_kernel(ExactArgs a) {
 
 hipError_t launch_exact(const ExactArgs& a, int dtype, hipStream_t s) {
   const dim3 g((a.N + kExThreads - 1) / kExThreads, a.BH);
+  ProfScope ps_(a.block > 0 ? "local_block_exact" : "exact_valu", s);
   if (dtype == 0) {
     if (a.D == 64) hipLaunchKernelGGL((exact_valu_kernel<float, 64>), g, dim3(kExThreads), 0, s, a);
     else hipLaunchKernelGGL((exact_valu_kernel<float, 128>), g, dim3(kExThreads), 0, s, a);

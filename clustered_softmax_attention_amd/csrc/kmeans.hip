@@ -227,22 +227,37 @@ __global__ void bucket_scatter_kernel(KmArgs a) {
 template <typename T>
 static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
   const dim3 g_init(1, a.BH, a.ntensors);
-  hipLaunchKernelGGL(kmeans_init_kernel<T>, g_init, dim3(256), 0, s, a);
+  {
+    ProfScope ps_("kmeans_init", s);
+    hipLaunchKernelGGL(kmeans_init_kernel<T>, g_init, dim3(256), 0, s, a);
+  }
   const int Cmax = max(a.t[0].C, a.ntensors > 1 ? a.t[1].C : 0);
   const size_t lds = static_cast<size_t>(kChunkC) * a.D * sizeof(float) +
                      sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax);
   const dim3 g_assign(a.ntiles, a.BH, a.ntensors);
   const dim3 g_update((Cmax * a.D + 255) / 256, a.BH, a.ntensors);
   for (int it = 0; it < iters; ++it) {
-    if (a.D == 64)
-      hipLaunchKernelGGL((kmeans_assign_kernel<T, 64>), g_assign, dim3(a.tile), lds, s, a, it);
-    else
-      hipLaunchKernelGGL((kmeans_assign_kernel<T, 128>), g_assign, dim3(a.tile), lds, s, a, it);
-    hipLaunchKernelGGL(kmeans_update_kernel, g_update, dim3(256), 0, s, a);
+    {
+      ProfScope ps_("kmeans_assign", s);
+      if (a.D == 64)
+        hipLaunchKernelGGL((kmeans_assign_kernel<T, 64>), g_assign, dim3(a.tile), lds, s, a, it);
+      else
+        hipLaunchKernelGGL((kmeans_assign_kernel<T, 128>), g_assign, dim3(a.tile), lds, s, a, it);
+    }
+    {
+      ProfScope ps_("kmeans_update", s);
+      hipLaunchKernelGGL(kmeans_update_kernel, g_update, dim3(256), 0, s, a);
+    }
   }
   const size_t lds_off = sizeof(int) * static_cast<size_t>(a.nb) * Cmax;
-  hipLaunchKernelGGL(bucket_offsets_kernel, dim3(1, a.BH, a.ntensors), dim3(256), lds_off, s, a);
-  hipLaunchKernelGGL(bucket_scatter_kernel, dim3(a.ntiles, a.BH, a.ntensors), dim3(256), 0, s, a);
+  {
+    ProfScope ps_("bucket_offsets", s);
+    hipLaunchKernelGGL(bucket_offsets_kernel, dim3(1, a.BH, a.ntensors), dim3(256), lds_off, s, a);
+  }
+  {
+    ProfScope ps_("bucket_scatter", s);
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(a.ntiles, a.BH, a.ntensors), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -6,7 +6,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/muse.h"
 #include "muse_kernels.hpp"
@@ -293,9 +295,116 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   return MUSE_OK;
 }
 
+// ---------------------------------------------------------------- per-kernel timing
+
+struct ProfRec {
+  const char* name;
+  hipEvent_t e0, e1;
+};
+
+struct ProfState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<ProfRec> pending;
+  std::vector<std::string> names;
+  std::vector<double> total_ms;
+  std::vector<long> launches;
+};
+
+ProfState& prof() {
+  static ProfState* p = new ProfState();  // never destroyed: events may outlive static teardown
+  return *p;
+}
+
+hipEvent_t prof_event(ProfState& P) {
+  if (!P.pool.empty()) {
+    hipEvent_t e = P.pool.back();
+    P.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
 }  // namespace
 
+namespace muse {
+
+ProfScope::ProfScope(const char* name, hipStream_t s) : name_(name), s_(s), e0_(nullptr), e1_(nullptr) {
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  if (!P.on) return;
+  e0_ = prof_event(P);
+  e1_ = prof_event(P);
+  if (e0_ != nullptr) (void)hipEventRecord(e0_, s_);
+}
+
+ProfScope::~ProfScope() {
+  if (e0_ == nullptr || e1_ == nullptr) return;
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  (void)hipEventRecord(e1_, s_);
+  P.pending.push_back({name_, e0_, e1_});
+}
+
+}  // namespace muse
+
 extern "C" {
+
+void muse_prof_enable(int on) {
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.on = on != 0;
+}
+
+int muse_prof_collect(void) {
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  for (const ProfRec& r : P.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.e1) == hipSuccess && hipEventElapsedTime(&ms, r.e0, r.e1) == hipSuccess) {
+      size_t i = 0;
+      while (i < P.names.size() && P.names[i] != r.name) ++i;
+      if (i == P.names.size()) {
+        P.names.emplace_back(r.name);
+        P.total_ms.push_back(0.0);
+        P.launches.push_back(0);
+      }
+      P.total_ms[i] += ms;
+      P.launches[i] += 1;
+    }
+    P.pool.push_back(r.e0);
+    P.pool.push_back(r.e1);
+  }
+  P.pending.clear();
+  return static_cast<int>(P.names.size());
+}
+
+const char* muse_prof_name(int i) {
+  ProfState& P = prof();
+  return (i >= 0 && i < static_cast<int>(P.names.size())) ? P.names[i].c_str() : "";
+}
+
+double muse_prof_total_ms(int i) {
+  ProfState& P = prof();
+  return (i >= 0 && i < static_cast<int>(P.total_ms.size())) ? P.total_ms[i] : 0.0;
+}
+
+long muse_prof_launches(int i) {
+  ProfState& P = prof();
+  return (i >= 0 && i < static_cast<int>(P.launches.size())) ? P.launches[i] : 0;
+}
+
+void muse_prof_reset(void) {
+  (void)muse_prof_collect();
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.names.clear();
+  P.total_ms.clear();
+  P.launches.clear();
+}
 
 void muse_fwd_params_init(muse_fwd_params* p) {
   if (p == nullptr) return;

@@ -66,6 +66,20 @@ __device__ __forceinline__ int wave_sum_int(int x) {
   return x;
 }
 
+// Opt-in per-kernel timing: while enabled, every launch is bracketed by a pair of HIP
+// events recorded on its stream (see muse_prof_* in include/muse.h).
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t e0_;
+  hipEvent_t e1_;
+};
+
 // Kernels that use more than 64 KiB of dynamic LDS must opt in (gfx950 has 160 KiB).
 inline void allow_lds(const void* fn, size_t bytes) {
   if (bytes > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));

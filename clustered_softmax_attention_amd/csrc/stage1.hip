@@ -352,16 +352,31 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   const size_t lds_atoms = sizeof(float) * (static_cast<size_t>(a.Cq) * D + 2 * kS1Keys * D +
                                             static_cast<size_t>(a.Cq) * kS1Keys + 3 * a.Cq);
   allow_lds((const void*)s1_atoms_kernel<T, D>, lds_atoms);
-  hipLaunchKernelGGL((s1_atoms_kernel<T, D>), dim3(a.Ck, a.nb, a.BH), dim3(256), lds_atoms, s, a);
-  hipLaunchKernelGGL(s1_prefix_kernel, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
+  {
+    ProfScope ps_("s1_atoms", s);
+    hipLaunchKernelGGL((s1_atoms_kernel<T, D>), dim3(a.Ck, a.nb, a.BH), dim3(256), lds_atoms, s, a);
+  }
+  {
+    ProfScope ps_("s1_prefix", s);
+    hipLaunchKernelGGL(s1_prefix_kernel, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
+  }
   if (a.dipole) {
     const size_t lds_mom = sizeof(float) * (D + 2 * kS1Keys * D + kS1Keys + 4);
     allow_lds((const void*)s1_moments_kernel<T, D>, lds_mom);
-    hipLaunchKernelGGL((s1_moments_kernel<T, D>), dim3(a.Cq, a.nb, a.BH), dim3(256), lds_mom, s, a);
-    hipLaunchKernelGGL(s1_mom_prefix_kernel, dim3((D * D + 255) / 256, a.Cq, a.BH), dim3(256), 0, s, a);
+    {
+      ProfScope ps_("s1_moments", s);
+      hipLaunchKernelGGL((s1_moments_kernel<T, D>), dim3(a.Cq, a.nb, a.BH), dim3(256), lds_mom, s, a);
+    }
+    {
+      ProfScope ps_("s1_mom_prefix", s);
+      hipLaunchKernelGGL(s1_mom_prefix_kernel, dim3((D * D + 255) / 256, a.Cq, a.BH), dim3(256), 0, s, a);
+    }
     const size_t lds_fin = sizeof(float) * (kMaxClusters + 64 * D + 4);
     allow_lds((const void*)s1_dip_final_kernel<D>, lds_fin);
-    hipLaunchKernelGGL((s1_dip_final_kernel<D>), dim3(a.Cq, a.nbS, a.BH), dim3(256), lds_fin, s, a);
+    {
+      ProfScope ps_("s1_dip_final", s);
+      hipLaunchKernelGGL((s1_dip_final_kernel<D>), dim3(a.Cq, a.nbS, a.BH), dim3(256), lds_fin, s, a);
+    }
   }
 }
 

@@ -102,6 +102,7 @@ __global__ void __launch_bounds__(kS2Threads) s2_refine_kernel(S2Args a) {
 
 hipError_t launch_stage2(const S2Args& a, int dtype, hipStream_t s) {
   const dim3 g((a.N + kS2Threads - 1) / kS2Threads, a.BH);
+  ProfScope ps_("s2_refine", s);
   if (dtype == 0) {
     if (a.D == 64) hipLaunchKernelGGL((s2_refine_kernel<float, 64>), g, dim3(kS2Threads), 0, s, a);
     else hipLaunchKernelGGL((s2_refine_kernel<float, 128>), g, dim3(kS2Threads), 0, s, a);

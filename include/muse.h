@@ -31,7 +31,7 @@
  *     caller's next synchronisation. No exception or abort crosses the ABI.
  *   - Determinism: identical inputs on the same device give bitwise identical
  *     outputs (no floating-point atomics anywhere).
- *   - Supported shapes: B, H, N >= 1; D in {64, 128}; 1 <= Cq, Ck <= min(N, 256);
+ *   - Supported shapes: B, H, N >= 1; D in {64, 128}; 1 <= Cq, Ck <= min(N, 128);
  *     kmeans_iters >= 1. Causal: 64 <= block <= N, N % block == 0,
  *     block % 64 == 0.
  */
@@ -123,6 +123,23 @@ size_t muse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int Cq, int Ck,
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* muse_last_error(void);
+
+/*
+ * Per-kernel timing (tracing aid; not part of the method). While enabled, every
+ * kernel the library launches is bracketed by a pair of HIP events recorded on
+ * the caller's stream, which adds a little launch overhead. muse_prof_collect()
+ * waits for the recorded events and folds them into per-kernel totals; it returns
+ * the number of distinct kernel names, which muse_prof_name / muse_prof_total_ms /
+ * muse_prof_launches index (0 .. count-1; out-of-range gives "" / 0). The state is
+ * process-wide and guarded by a mutex; the strings stay valid until the next
+ * muse_prof_collect or muse_prof_reset.
+ */
+void muse_prof_enable(int on);
+int muse_prof_collect(void);
+const char* muse_prof_name(int i);
+double muse_prof_total_ms(int i);
+long muse_prof_launches(int i);
+void muse_prof_reset(void);
 
 /* ABI version: major * 10000 + minor * 100 + patch. */
 int muse_version(void);
