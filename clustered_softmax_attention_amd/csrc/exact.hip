@@ -4,9 +4,15 @@
 // with the far-field approximation by log-sum-exp:
 //   L = log(e^L_loc + e^L_far),  o = e^(L_loc - L) o_loc + e^(L_far - L) o_far.
 //
+// bf16 path (flash_bf16): workgroup of 4 waves = 128 queries; key/value tiles of 64
+// keys staged in LDS (K row-major, V transposed); per wave S^T = K Q^T on the matrix
+// cores (32 keys x 32 queries per tile), online softmax along accumulator rows (one
+// lane and its partner), O^T += V^T P^T with P rounded to bf16. Workgroups are
+// renumbered so that those of one head run on one XCD and share its L2.
 // fp32 path: one thread per query, online softmax over chunks of 32 keys; all lanes
 // of a wave visit the same key at the same time, so key and value rows are read
 // once per wave.
+#include "mfma.hpp"
 #include "muse_kernels.hpp"
 
 namespace muse {
@@ -105,8 +111,189 @@ __global__ void __launch_bounds__(kExThreads) exact_valu_kernel(ExactArgs a) {
   }
 }
 
+// Workgroup id -> (query tile, head) so that consecutive work of a head lands on one XCD
+// (hardware places consecutive ids on XCDs round-robin).
+__device__ __forceinline__ int xcd_swizzle(int id, int total) {
+  constexpr int kXcd = 8;
+  if (total % kXcd != 0) return id;
+  return (id % kXcd) * (total / kXcd) + id / kXcd;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) flash_bf16_kernel(ExactArgs a, int nqt) {
+  constexpr int BQ = 128, BK = 64;
+  constexpr int KST = D + 8;  // bf16 elements per K row in LDS (padded)
+  constexpr int VST = BK + 8; // bf16 elements per V^T row in LDS (padded)
+  constexpr int NKS = D / 16;
+  constexpr int NMT = D / 32;
+  constexpr int CH = D / 8;   // 16-byte chunks per row
+  __shared__ __align__(16) uint16_t sK[BK * KST];
+  __shared__ __align__(16) uint16_t sVt[D * VST];
+
+  const int total = nqt * a.BH;
+  const int id = xcd_swizzle(blockIdx.x, total);
+  int qt = id % nqt;
+  const int bh = id / nqt;
+  if (a.causal) qt = nqt - 1 - qt;  // longest rows first
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int N = a.N;
+  const int q0 = qt * BQ;
+  const int qi = q0 + wave * 32 + c;
+  const bool qvalid = qi < N;
+  const size_t base = static_cast<size_t>(bh) * N;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + base * D;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + base * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + base * D;
+
+  bf16x8_t qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    u16x8_t u = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (qvalid) u = *reinterpret_cast<const u16x8_t*>(Q + static_cast<size_t>(qi) * D + 16 * ks + 8 * h);
+    qf[ks] = as_bf16x8(u);
+  }
+  const int qq = qvalid ? qi : N - 1;
+  const int kbeg = a.block > 0 ? (qq / a.block) * a.block : 0;
+  const int kend = a.causal ? qq + 1 : N;
+  const int wkb_min = wave_min_int(kbeg), wkb_max = wave_max_int(kbeg);
+  const int wke_min = wave_min_int(kend), wke_max = wave_max_int(kend);
+  const int qlast = min(q0 + BQ, N) - 1;
+  const int gkb = a.block > 0 ? (q0 / a.block) * a.block : 0;
+  const int gke = a.causal ? qlast + 1 : N;
+  const float sl2 = a.scale * 1.4426950408889634f;
+
+  float m = -1e30f, l = 0.f;
+  f32x16_t o[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) o[mt] = zero16();
+
+  for (int kt = gkb; kt < gke; kt += BK) {
+    __syncthreads();
+    for (int e = tid; e < BK * CH; e += 256) {
+      const int r = e / CH, cc = e % CH;
+      const int key = kt + r;
+      u16x8_t kv = {0, 0, 0, 0, 0, 0, 0, 0}, vv = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (key < N) {
+        kv = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(key) * D + cc * 8);
+        vv = *reinterpret_cast<const u16x8_t*>(V + static_cast<size_t>(key) * D + cc * 8);
+      }
+      *reinterpret_cast<u16x8_t*>(sK + r * KST + cc * 8) = kv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sVt[(cc * 8 + i) * VST + r] = vv[i];
+    }
+    __syncthreads();
+    if (kt >= wke_max || kt + BK <= wkb_min) continue;  // tile outside every row of this wave
+    const bool full = kt >= wkb_max && kt + BK <= wke_min && kt + BK <= N;
+
+    f32x16_t s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8_t af = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sK + (32 * t + c) * KST + 16 * ks + 8 * h));
+        s[t] = mfma32(af, qf[ks], s[t]);
+      }
+    }
+    float mx = -1e30f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float x = s[t][v] * sl2;
+        if (!full) {
+          const int key = kt + 32 * t + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (key < kbeg || key >= kend) x = kNegInf;
+        }
+        s[t][v] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(s[t][v] - mn);
+        s[t][v] = p;
+        l += p;
+      }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = s[t][8 * ss + i];
+        const bf16x8_t bfr = pack_bf16x8(pv);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          const uint16_t* row = sVt + (32 * mt + c) * VST + 32 * t + 16 * ss + 4 * h;
+          const u16x4_t lo4 = *reinterpret_cast<const u16x4_t*>(row);
+          const u16x4_t hi4 = *reinterpret_cast<const u16x4_t*>(row + 8);
+          const u16x8_t u = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          o[mt] = mfma32(as_bf16x8(u), bfr, o[mt]);
+        }
+      }
+  }
+  const float lt = l + __shfl_xor(l, 32, 64);
+  if (!qvalid) return;
+  const float inv = 1.f / lt;
+  float L = (m + __log2f(lt)) * 0.6931471805599453f;
+  const size_t row = base + qi;
+  float w0 = inv, w1 = 0.f;
+  bool merge = false;
+  if (a.l_far != nullptr) {
+    const float lf = a.l_far[row];
+    if (lf != kNegInf) {
+      const float Lt = fmaxf(L, lf) + __logf(1.f + __expf(-fabsf(L - lf)));
+      w0 = __expf(L - Lt) * inv;
+      w1 = __expf(lf - Lt);
+      L = Lt;
+      merge = true;
+    }
+  }
+  if (a.lse_out != nullptr && h == 0) a.lse_out[row] = L;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * mt + 8 * g + 4 * h;
+      float r4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) r4[r] = o[mt][4 * g + r] * w0;
+      if (merge) {
+        const f32x4_t f = *reinterpret_cast<const f32x4_t*>(a.o_far + row * D + d0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) r4[r] += w1 * f[r];
+      }
+      if (a.out_bf16) {
+        const u16x4_t u = {f32_to_bf16_bits(r4[0]), f32_to_bf16_bits(r4[1]), f32_to_bf16_bits(r4[2]),
+                           f32_to_bf16_bits(r4[3])};
+        *reinterpret_cast<u16x4_t*>(static_cast<uint16_t*>(a.out) + row * D + d0) = u;
+      } else {
+        const f32x4_t f = {r4[0], r4[1], r4[2], r4[3]};
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + row * D + d0) = f;
+      }
+    }
+}
+
 hipError_t launch_exact(const ExactArgs& a, int dtype, hipStream_t s) {
   const dim3 g((a.N + kExThreads - 1) / kExThreads, a.BH);
+  if (dtype == 1) {
+    const int nqt = (a.N + 127) / 128;
+    ProfScope ps_(a.block > 0 ? "local_block_mfma" : "exact_mfma", s);
+    if (a.D == 64) hipLaunchKernelGGL((flash_bf16_kernel<64>), dim3(nqt * a.BH), dim3(256), 0, s, a, nqt);
+    else hipLaunchKernelGGL((flash_bf16_kernel<128>), dim3(nqt * a.BH), dim3(256), 0, s, a, nqt);
+    return hipGetLastError();
+  }
   ProfScope ps_(a.block > 0 ? "local_block_exact" : "exact_valu", s);
   if (dtype == 0) {
     if (a.D == 64) hipLaunchKernelGGL((exact_valu_kernel<float, 64>), g, dim3(kExThreads), 0, s, a);

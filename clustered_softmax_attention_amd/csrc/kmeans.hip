@@ -20,8 +20,17 @@
 //                   (block, label), i.e. the key (or query) permutation used by
 //                   the summary kernels.
 //
+// bf16 inputs (kmeans_assign_mfma): the distance scores ||c_j||^2 - 2 x.c_j come from
+// the matrix cores, with each fp32 centroid split into bf16 hi + lo parts (x is exact
+// in bf16). Their error is bounded by E = 1e-4 ||x|| max||c|| + 2e-5 max||c||^2 (about
+// 2.5x the worst case of the split residual 2^-16 and the fp32 accumulation); when a
+// second centroid scores within 2E of the best, every such candidate is re-scored with
+// the exact fp32 direct form sum_d (x_d - c_jd)^2 of the fp32 path, so labels are the
+// same as the fp32 path's.
+//
 // Every sum runs in a fixed order, so labels and centroids are bitwise
 // reproducible.
+#include "mfma.hpp"
 #include "muse_kernels.hpp"
 
 namespace muse {
@@ -37,6 +46,70 @@ __global__ void kmeans_init_kernel(KmArgs a) {
     const int j = e / a.D, d = e % a.D;
     const long src = (static_cast<long>(j) * a.N) / t.C;
     c[e] = Elem<T>::load(x, static_cast<size_t>(src) * a.D + d);
+  }
+}
+
+// Stable counting sort of the tile's points by label (LDS), then the tile's sort info
+// and per-cluster sums. Called by every thread of the workgroup.
+template <typename T, int D>
+__device__ void tile_sort_and_sums(const KmArgs& a, const KmTensor& t, int lab, bool valid, int* s_lab,
+                                   int* s_whist, int* s_cnt, int* s_start, int* s_sorted) {
+  const int C = t.C;
+  const int bh = blockIdx.y;
+  const int tile = blockDim.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int nwaves = tile >> 6;
+  const T* x = static_cast<const T*>(t.x) + static_cast<size_t>(bh) * a.N * D;
+  for (int e = tid; e < nwaves * C; e += tile) s_whist[e] = 0;
+  s_lab[tid] = lab;
+  __syncthreads();
+  // lanes of this wave with the same label (the sentinel C only matches itself)
+  uint64_t peers = __ballot(1);
+  for (int b = 0; (1 << b) <= C; ++b) {
+    const bool bit = (lab >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  const int rank_in_wave = __popcll(peers & lanemask_lt());
+  if (valid && rank_in_wave == 0) s_whist[wave * C + lab] = __popcll(peers);
+  __syncthreads();
+  for (int j = tid; j < C; j += tile) {
+    int run = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      const int h = s_whist[w * C + j];
+      s_whist[w * C + j] = run;  // becomes the wave's base inside the label's segment
+      run += h;
+    }
+    s_cnt[j] = run;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int j = 0; j < C; ++j) {
+      s_start[j] = run;
+      run += s_cnt[j];
+    }
+  }
+  __syncthreads();
+  if (valid) s_sorted[s_start[lab] + s_whist[wave * C + lab] + rank_in_wave] = tid;
+  __syncthreads();
+
+  // ---- outputs: sort info (for bucketing) and this tile's per-cluster sums ----
+  const size_t tix = static_cast<size_t>(bh) * a.ntiles + blockIdx.x;
+  for (int j = tid; j < C; j += tile) {
+    t.tile_cnt[tix * C + j] = s_cnt[j];
+    t.tile_start[tix * C + j] = s_start[j];
+  }
+  t.tile_perm[tix * a.tile + tid] = static_cast<uint16_t>(s_sorted[tid]);
+  float* psum = t.psum + tix * C * D;
+  const long base = static_cast<long>(blockIdx.x) * tile;
+  for (int e = tid; e < C * D; e += tile) {
+    const int j = e / D, d = e % D;
+    const int st = s_start[j], cnt = s_cnt[j];
+    float acc = 0.f;
+    for (int r = 0; r < cnt; ++r) acc += Elem<T>::load(x, static_cast<size_t>(base + s_sorted[st + r]) * D + d);
+    psum[e] = acc;
   }
 }
 
@@ -101,57 +174,158 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_kernel(KmArgs a, int i
     if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
   }
 
-  // ---- stable counting sort of the tile by label ----
-  for (int e = tid; e < nwaves * C; e += tile) s_whist[e] = 0;
-  s_lab[tid] = lab;
-  __syncthreads();
-  // lanes of this wave with the same label (the sentinel C only matches itself)
-  uint64_t peers = __ballot(1);
-  for (int b = 0; (1 << b) <= C; ++b) {
-    const bool bit = (lab >> b) & 1;
-    const uint64_t m = __ballot(bit);
-    peers &= bit ? m : ~m;
-  }
-  const int rank_in_wave = __popcll(peers & lanemask_lt());
-  if (valid && rank_in_wave == 0) s_whist[wave * C + lab] = __popcll(peers);
-  __syncthreads();
-  for (int j = tid; j < C; j += tile) {
-    int run = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      const int h = s_whist[w * C + j];
-      s_whist[w * C + j] = run;  // becomes the wave's base inside the label's segment
-      run += h;
-    }
-    s_cnt[j] = run;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int j = 0; j < C; ++j) {
-      s_start[j] = run;
-      run += s_cnt[j];
-    }
-  }
-  __syncthreads();
-  if (valid) s_sorted[s_start[lab] + s_whist[wave * C + lab] + rank_in_wave] = tid;
-  __syncthreads();
+  tile_sort_and_sums<T, D>(a, t, lab, valid, s_lab, s_whist, s_cnt, s_start, s_sorted);
+}
 
-  // ---- outputs: sort info (for bucketing) and this tile's per-cluster sums ----
-  const size_t tix = static_cast<size_t>(bh) * a.ntiles + blockIdx.x;
-  for (int j = tid; j < C; j += tile) {
-    t.tile_cnt[tix * C + j] = s_cnt[j];
-    t.tile_start[tix * C + j] = s_start[j];
+// Matrix-core assign for bf16 inputs; blockDim.x == tile (multiple of 64, <= kMaxTile).
+// Wave w scores points w*64 .. w*64+63 in two groups of 32 (lane (c, h) of the product
+// holds 16 centroid rows of point c per 32-row tile). Lane l = 32 h + c of the wave
+// then owns point w*64 + l for the sort. Dynamic LDS: c_hi, c_lo [Cp][D+8] bf16 |
+// ||c||^2 [Cp] | sort buffers.
+template <int D>
+__global__ void __launch_bounds__(kMaxTile) kmeans_assign_mfma_kernel(KmArgs a, int iter) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int CST = D + 8;
+  constexpr int NKS = D / 16;
+  constexpr int MAXJT = kMaxClusters / 32;
+  const KmTensor& t = a.t[blockIdx.z];
+  const int C = t.C, Cp = (C + 31) & ~31, njt = Cp / 32;
+  const int bh = blockIdx.y, tile = blockDim.x, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  uint16_t* chi = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* clo = chi + Cp * CST;
+  float* cn2 = reinterpret_cast<float*>(clo + Cp * CST);
+  int* s_lab = reinterpret_cast<int*>(cn2 + Cp);
+  int* s_whist = s_lab + tile;
+  int* s_cnt = s_whist + (tile >> 6) * C;
+  int* s_start = s_cnt + C;
+  int* s_sorted = s_start + C;
+  const long n = static_cast<long>(blockIdx.x) * tile + tid;
+  const bool valid = n < a.N;
+  const uint16_t* X = static_cast<const uint16_t*>(t.x) + static_cast<size_t>(bh) * a.N * D;
+  const float* cent = t.cent + static_cast<size_t>(bh) * C * D;
+
+  int lab = C;
+  if (t.labels_in != nullptr) {
+    if (valid) lab = min(max(t.labels_in[static_cast<size_t>(bh) * a.N + n], 0), C - 1);
+  } else {
+    for (int e = tid; e < Cp * D; e += tile) {
+      const int j = e / D, d = e % D;
+      const float cv = j < C ? cent[static_cast<size_t>(j) * D + d] : 0.f;
+      const uint16_t hi = f32_to_bf16_bits(cv);
+      chi[j * CST + d] = hi;
+      clo[j * CST + d] = f32_to_bf16_bits(cv - bf16_to_f32(hi));
+    }
+    for (int j = tid; j < Cp; j += tile) {
+      float n2 = 0.f;
+      if (j < C)
+        for (int d = 0; d < D; ++d) n2 = fmaf(cent[static_cast<size_t>(j) * D + d], cent[static_cast<size_t>(j) * D + d], n2);
+      cn2[j] = n2;
+    }
+    __syncthreads();
+    float cmax2 = 0.f;
+    for (int j = 0; j < C; ++j) cmax2 = fmaxf(cmax2, cn2[j]);
+    const float cmax = sqrtf(cmax2);
+    int labs[2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const long p = static_cast<long>(blockIdx.x) * tile + wave * 64 + gi * 32 + c;
+      const bool pv = p < a.N;
+      bf16x8_t xf[NKS];
+      float xx = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        u16x8_t u = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (pv) u = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(p) * D + 16 * ks + 8 * h);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float xv = bf16_to_f32(u[r]);
+          xx = fmaf(xv, xv, xx);
+        }
+        xf[ks] = as_bf16x8(u);
+      }
+      xx += __shfl_xor(xx, 32, 64);
+      float sc[MAXJT][16];
+      float best = __builtin_huge_valf();
+      int bj = C;
+#pragma unroll
+      for (int jt = 0; jt < MAXJT; ++jt) {
+        if (jt >= njt) break;
+        f32x16_t acc = zero16();
+        const int jr = 32 * jt + c;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const u16x8_t*>(chi + jr * CST + 16 * ks + 8 * h));
+          const bf16x8_t al = as_bf16x8(*reinterpret_cast<const u16x8_t*>(clo + jr * CST + 16 * ks + 8 * h));
+          acc = mfma32(ah, xf[ks], acc);
+          acc = mfma32(al, xf[ks], acc);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
+          const float x = j < C ? cn2[j] - 2.f * acc[v] : __builtin_huge_valf();
+          sc[jt][v] = x;
+          if (x < best || (x == best && j < bj)) {
+            best = x;
+            bj = j;
+          }
+        }
+      }
+      {
+        const float ob = __shfl_xor(best, 32, 64);
+        const int oj = __shfl_xor(bj, 32, 64);
+        if (ob < best || (ob == best && oj < bj)) {
+          best = ob;
+          bj = oj;
+        }
+      }
+      const float E = 1e-4f * sqrtf(xx) * cmax + 2e-5f * cmax2;
+      const float thr = best + 2.f * E;
+      uint64_t mask = 0;
+#pragma unroll
+      for (int jt = 0; jt < MAXJT; ++jt) {
+        if (jt >= njt) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (sc[jt][v] <= thr) mask |= 1ull << (16 * jt + v);
+      }
+      const int total = __popcll(mask) + __shfl_xor(__popcll(mask), 32, 64);
+      if (__ballot(pv && total > 1) != 0ull) {
+        if (pv && total > 1) {  // both lanes of the pair take this branch together
+          float fb = __builtin_huge_valf();
+          int fj = C;
+          const uint16_t* xr = X + static_cast<size_t>(p) * D;
+          while (mask != 0ull) {
+            const int idx = __ffsll(static_cast<unsigned long long>(mask)) - 1;
+            mask &= mask - 1;
+            const int jt = idx >> 4, v = idx & 15;
+            const int j = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
+            const float* cr = cent + static_cast<size_t>(j) * D;
+            float dist = 0.f;
+            for (int d = 0; d < D; ++d) {
+              const float diff = bf16_to_f32(xr[d]) - cr[d];
+              dist = fmaf(diff, diff, dist);
+            }
+            if (dist < fb || (dist == fb && j < fj)) {
+              fb = dist;
+              fj = j;
+            }
+          }
+          const float ob = __shfl_xor(fb, 32, 64);
+          const int oj = __shfl_xor(fj, 32, 64);
+          if (ob < fb || (ob == fb && oj < fj)) fj = oj;
+          bj = fj;
+        }
+      }
+      labs[gi] = bj;
+    }
+    if (valid) lab = h == 0 ? labs[0] : labs[1];
   }
-  t.tile_perm[tix * a.tile + tid] = static_cast<uint16_t>(s_sorted[tid]);
-  float* psum = t.psum + tix * C * D;
-  const long base = static_cast<long>(blockIdx.x) * tile;
-  for (int e = tid; e < C * D; e += tile) {
-    const int j = e / D, d = e % D;
-    const int st = s_start[j], cnt = s_cnt[j];
-    float acc = 0.f;
-    for (int r = 0; r < cnt; ++r) acc += Elem<T>::load(x, static_cast<size_t>(base + s_sorted[st + r]) * D + d);
-    psum[e] = acc;
+  if (valid) {
+    t.labels[static_cast<size_t>(bh) * a.N + n] = lab;
+    if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
   }
+  tile_sort_and_sums<bf16, D>(a, t, lab, valid, s_lab, s_whist, s_cnt, s_start, s_sorted);
 }
 
 // Thread per (cluster j, dim d): sum the tile partials in tile order.
@@ -236,8 +410,22 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
                      sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax);
   const dim3 g_assign(a.ntiles, a.BH, a.ntensors);
   const dim3 g_update((Cmax * a.D + 255) / 256, a.BH, a.ntensors);
+  const int Cp = (Cmax + 31) & ~31;
+  const size_t lds_mfma = static_cast<size_t>(Cp) * (a.D + 8) * 2 * sizeof(uint16_t) + Cp * sizeof(float) +
+                          sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax);
+  const bool mf = sizeof(T) == 2;
+  if (mf) {
+    allow_lds((const void*)kmeans_assign_mfma_kernel<64>, lds_mfma);
+    allow_lds((const void*)kmeans_assign_mfma_kernel<128>, lds_mfma);
+  }
   for (int it = 0; it < iters; ++it) {
-    {
+    if (mf) {
+      ProfScope ps_("kmeans_assign_mfma", s);
+      if (a.D == 64)
+        hipLaunchKernelGGL((kmeans_assign_mfma_kernel<64>), g_assign, dim3(a.tile), lds_mfma, s, a, it);
+      else
+        hipLaunchKernelGGL((kmeans_assign_mfma_kernel<128>), g_assign, dim3(a.tile), lds_mfma, s, a, it);
+    } else {
       ProfScope ps_("kmeans_assign", s);
       if (a.D == 64)
         hipLaunchKernelGGL((kmeans_assign_kernel<T, 64>), g_assign, dim3(a.tile), lds, s, a, it);

@@ -45,6 +45,7 @@ struct Layout {
 struct Shape {
   int B, H, N, D, Cq, Ck, iters, causal, block, dtype;
   int BH, nb, nbS, tile, ntiles, tiles_per_block;
+  int nmb, mbk;  // dipole-moment sub-blocks
 };
 
 // Largest multiple of 64 that divides `block` and is at most kMaxTile.
@@ -77,6 +78,13 @@ int validate(Shape& s, const muse_fwd_params* p) {
     s.tiles_per_block = (s.N + s.tile - 1) / s.tile;
   }
   s.ntiles = (s.N + s.tile - 1) / s.tile;
+  // moment sub-blocks: the matrix-core kernel splits long key ranges for parallelism
+  if (s.dtype == MUSE_BF16) {
+    s.mbk = s.causal ? (s.block > 1024 && s.block % 1024 == 0 ? 1024 : s.block) : 1024;
+  } else {
+    s.mbk = s.block;
+  }
+  s.nmb = (s.N + s.mbk - 1) / s.mbk;
   if (p != nullptr) {
     if (p->out_dtype != -1 && p->out_dtype != MUSE_F32 && p->out_dtype != MUSE_BF16)
       return fail(MUSE_ERR_INVALID_ARG, "out_dtype %d invalid", p->out_dtype);
@@ -103,7 +111,9 @@ int validate_muse(Shape& s, const muse_fwd_params* p) {
 
 struct Plan {
   size_t cent_q, cent_k, lab_q, lab_k, tperm_q, tperm_k, tcnt_q, tcnt_k, tst_q, tst_k, psum_q, psum_k;
-  size_t perm_k, offs_k;
+  size_t perm_k, offs_k, perm_q, offs_q;
+  size_t t_khi, t_klo, t_vthi, t_vtlo, t_dip, tiles, ntiles, tile_base;
+  int max_tiles;
   size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom;
   size_t s_logz, s_k, s_v, s_dipT;
   size_t o_far, l_far;
@@ -130,12 +140,14 @@ Plan make_plan(const Shape& s) {
   P.psum_k = L.take(BH * nt * Ck * D * f);
   P.perm_k = L.take(BH * N * i4);
   P.offs_k = L.take(BH * (nb * Ck + 1) * i4);
+  P.perm_q = L.take(BH * N * i4);
+  P.offs_q = L.take(BH * (nb * Cq + 1) * i4);
   P.at_m = L.take(BH * nb * Cq * Ck * f);
   P.at_z = L.take(BH * nb * Cq * Ck * f);
   P.at_k = L.take(BH * nb * Cq * Ck * D * f);
   P.at_v = L.take(BH * nb * Cq * Ck * D * f);
-  P.blk_lmass = L.take(BH * nb * Cq * f);
-  P.blk_mom = L.take(BH * nb * Cq * D * D * f);
+  P.blk_lmass = L.take(BH * static_cast<size_t>(s.nmb) * Cq * f);
+  P.blk_mom = L.take(BH * static_cast<size_t>(s.nmb) * Cq * D * D * f);
   P.s_logz = L.take(BH * nbS * Cq * Ck * f);
   P.s_k = L.take(BH * nbS * Cq * Ck * D * f);
   P.s_v = L.take(BH * nbS * Cq * Ck * D * f);
@@ -143,6 +155,18 @@ Plan make_plan(const Shape& s) {
   if (s.causal) {
     P.o_far = L.take(BH * N * D * f);
     P.l_far = L.take(BH * N * f);
+  }
+  if (s.dtype == MUSE_BF16) {
+    const size_t h2 = sizeof(uint16_t);
+    P.t_khi = L.take(BH * nbS * Cq * Ck * D * h2);
+    P.t_klo = L.take(BH * nbS * Cq * Ck * D * h2);
+    P.t_vthi = L.take(BH * nbS * Cq * Ck * D * h2);
+    P.t_vtlo = L.take(BH * nbS * Cq * Ck * D * h2);
+    P.t_dip = L.take(BH * nbS * Cq * D * D * h2);
+    P.max_tiles = static_cast<int>((N + 31) / 32 + nb * Cq);
+    P.tiles = L.take(BH * P.max_tiles * 2 * i4);
+    P.ntiles = L.take(BH * i4);
+    P.tile_base = L.take(BH * (nb * Cq + 1) * i4);
   }
   P.total = L.bytes;
   return P;
@@ -189,8 +213,9 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   tq.tile_cnt = at<int32_t>(ws, P.tcnt_q);
   tq.tile_start = at<int32_t>(ws, P.tst_q);
   tq.psum = at<float>(ws, P.psum_q);
-  tq.perm = nullptr;
-  tq.offs = nullptr;
+  const bool mf = s.dtype == MUSE_BF16;  // matrix-core stage 2 needs the query buckets
+  tq.perm = mf ? at<int32_t>(ws, P.perm_q) : nullptr;
+  tq.offs = mf ? at<int32_t>(ws, P.offs_q) : nullptr;
   KmTensor& tk = km.t[1];
   tk.x = k;
   tk.C = s.Ck;
@@ -228,12 +253,21 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.at_z = at<float>(ws, P.at_z);
   a1.at_k = at<float>(ws, P.at_k);
   a1.at_v = at<float>(ws, P.at_v);
+  a1.nmb = s.nmb;
+  a1.mbk = s.mbk;
   a1.blk_lmass = at<float>(ws, P.blk_lmass);
   a1.blk_mom = at<float>(ws, P.blk_mom);
   a1.s_logz = at<float>(ws, P.s_logz);
   a1.s_k = at<float>(ws, P.s_k);
   a1.s_v = at<float>(ws, P.s_v);
   a1.s_dipT = at<float>(ws, P.s_dipT);
+  if (mf) {
+    a1.t_khi = at<uint16_t>(ws, P.t_khi);
+    a1.t_klo = at<uint16_t>(ws, P.t_klo);
+    a1.t_vthi = at<uint16_t>(ws, P.t_vthi);
+    a1.t_vtlo = at<uint16_t>(ws, P.t_vtlo);
+    a1.t_dip = at<uint16_t>(ws, P.t_dip);
+  }
   e = launch_stage1(a1, s.dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
 
@@ -258,6 +292,20 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a2.s_k = a1.s_k;
   a2.s_v = a1.s_v;
   a2.s_dipT = a1.s_dipT;
+  a2.t_khi = a1.t_khi;
+  a2.t_klo = a1.t_klo;
+  a2.t_vthi = a1.t_vthi;
+  a2.t_vtlo = a1.t_vtlo;
+  a2.t_dip = a1.t_dip;
+  a2.perm_q = tq.perm;
+  a2.offs_q = tq.offs;
+  a2.nb = s.nb;
+  if (mf) {
+    a2.tiles = at<int2>(ws, P.tiles);
+    a2.ntiles = at<int32_t>(ws, P.ntiles);
+    a2.tile_base = at<int32_t>(ws, P.tile_base);
+    a2.max_tiles = P.max_tiles;
+  }
   if (s.causal) {
     a2.o_far = at<float>(ws, P.o_far);
     a2.l_far = at<float>(ws, P.l_far);

@@ -55,13 +55,20 @@ struct S1Args {
   float* at_z;                 // [BH, nb, Cq, Ck] sum exp(a - m)
   float* at_k;                 // [BH, nb, Cq, Ck, D] sum exp(a - m) k
   float* at_v;                 // [BH, nb, Cq, Ck, D] sum exp(a - m) v
-  float* blk_lmass;            // [BH, nb, Cq] log mass of a block seen by centroid i
-  float* blk_mom;              // [BH, nb, Cq, D, D] block-normalised sum w v k^T (v index first)
+  int nmb, mbk;                // moment sub-blocks: count and keys per sub-block (divides block)
+  float* blk_lmass;            // [BH, nmb, Cq] log mass of a sub-block seen by centroid i
+  float* blk_mom;              // [BH, nmb, Cq, D, D] sub-block-normalised sum w v k^T (v index first)
   // summary tables
   float* s_logz;               // [BH, nbS, Cq, Ck]
   float* s_k;                  // [BH, nbS, Cq, Ck, D] tilted key means
   float* s_v;                  // [BH, nbS, Cq, Ck, D] tilted value means
   float* s_dipT;               // [BH, nbS, Cq, D(k), D(v)] aggregated dipole, key index first
+  // bf16 copies for the matrix-core stage 2 (null on the fp32 path)
+  uint16_t* t_khi;             // [BH, nbS, Cq, Ck, D]  K_ij = hi + lo
+  uint16_t* t_klo;
+  uint16_t* t_vthi;            // [BH, nbS, Cq, D, Ck]  V_ij transposed, = hi + lo
+  uint16_t* t_vtlo;
+  uint16_t* t_dip;             // [BH, nbS, Cq, D(v), D(k)]  s * D_i, value index first
 };
 
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);
@@ -85,6 +92,19 @@ struct S2Args {
   const float* s_k;
   const float* s_v;
   const float* s_dipT;
+  // matrix-core path (bf16 inputs)
+  const uint16_t* t_khi;
+  const uint16_t* t_klo;
+  const uint16_t* t_vthi;
+  const uint16_t* t_vtlo;
+  const uint16_t* t_dip;
+  const int32_t* perm_q;       // [BH, N] queries by (block, label)
+  const int32_t* offs_q;       // [BH, nb*Cq + 1]
+  int nb;                      // query blocks (1 when acausal)
+  int2* tiles;                 // [BH, max_tiles] (bucket, first position) of 32-query tiles
+  int32_t* ntiles;             // [BH]
+  int32_t* tile_base;          // [BH, nb*Cq + 1] scratch: first tile of every bucket
+  int max_tiles;
 };
 
 hipError_t launch_stage2(const S2Args& a, int dtype, hipStream_t s);

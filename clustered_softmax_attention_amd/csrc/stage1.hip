@@ -20,6 +20,7 @@
 //   s1_prefix     fold of atoms over blocks -> log Z, K, V tables.
 //   s1_mom_prefix fold of block moments over blocks -> E_i[v k^T] per table entry.
 //   s1_dip_final  D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T (stored key index first).
+#include "mfma.hpp"
 #include "muse_kernels.hpp"
 
 namespace muse {
@@ -166,7 +167,7 @@ __global__ void __launch_bounds__(256) s1_moments_kernel(S1Args a) {
   }
   __syncthreads();
   const float R = red[0];
-  if (tid == 0) a.blk_lmass[(static_cast<size_t>(bh) * a.nb + bp) * Cq + i] = R;
+  if (tid == 0) a.blk_lmass[(static_cast<size_t>(bh) * a.nmb + bp) * Cq + i] = R;
 
   const int tr = tid / 16, tc = tid % 16;  // rows dv = tr*TD.., cols dk = tc*TD..
   float acc[TD][TD];
@@ -211,11 +212,152 @@ __global__ void __launch_bounds__(256) s1_moments_kernel(S1Args a) {
       }
     }
   }
-  float* out = a.blk_mom + ((static_cast<size_t>(bh) * a.nb + bp) * Cq + i) * D * D;
+  float* out = a.blk_mom + ((static_cast<size_t>(bh) * a.nmb + bp) * Cq + i) * D * D;
 #pragma unroll
   for (int x = 0; x < TD; ++x)
 #pragma unroll
     for (int y = 0; y < TD; ++y) out[(tr * TD + x) * D + tc * TD + y] = acc[x][y];
+}
+
+// Matrix-core sub-block moments (bf16 inputs): M_i = sum_m w_m v_m k_m^T / sum_m w_m over
+// the keys of one sub-block, w_m = exp(s qbar_i . k_m - running max), and the sub-block
+// log mass. Keys are staged 64 at a time in LDS, transposed (K^T, V^T) so that both
+// operands of the product run along keys; the weights are applied to V^T while forming
+// the A operand (rounded to bf16 there). Centroid groups: D = 64, 8 centroids per
+// workgroup (2 per wave, 4 output tiles each); D = 128, 2 centroids per workgroup (each
+// wave owns half of the 16 output tiles of one centroid).
+template <int D>
+__global__ void __launch_bounds__(256) s1_moments_mfma_kernel(S1Args a) {
+  constexpr int KC = 64;          // keys per step
+  constexpr int TST = KC + 8;     // LDS row stride of K^T / V^T (bf16 elements)
+  constexpr int G = D == 64 ? 8 : 2;
+  constexpr int CPW = D == 64 ? 2 : 1;   // centroids per wave
+  constexpr int NMT = D / 32;            // row tiles (dv)
+  constexpr int NNT = D == 64 ? 2 : 2;   // column tiles (dk) per wave
+  __shared__ __align__(16) uint16_t sKt[D * TST];
+  __shared__ __align__(16) uint16_t sVt[D * TST];
+  __shared__ float sq[G * D];
+  __shared__ float sw[G * KC];
+  const int mb = blockIdx.x, ig = blockIdx.y, bh = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int Cq = a.Cq;
+  const int i0 = ig * G;
+  const int ng = min(G, Cq - i0);
+  // this wave's centroids (local index within the group) and dk half
+  const int wc0 = D == 64 ? 2 * wave : wave / 2;
+  const int nt0 = D == 64 ? 0 : 2 * (wave & 1);
+  for (int x = tid; x < G * D; x += 256) {
+    const int g = x / D;
+    sq[x] = g < ng ? a.qbar[(static_cast<size_t>(bh) * Cq + i0 + g) * D + x % D] : 0.f;
+  }
+  const int key0 = mb * a.mbk;
+  const int key1 = min(a.N, key0 + a.mbk);
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+
+  f32x16_t acc[CPW][NMT][NNT];
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NNT; ++nt) acc[cc][mt][nt] = zero16();
+  float runm[CPW], runz[CPW];
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) {
+    runm[cc] = -1e30f;
+    runz[cc] = 0.f;
+  }
+  const float sl2 = a.scale * 1.4426950408889634f;
+
+  for (int c0 = key0; c0 < key1; c0 += KC) {
+    const int nk = min(KC, key1 - c0);
+    __syncthreads();
+    for (int x = tid; x < KC * (D / 8); x += 256) {
+      const int r = x / (D / 8), cc8 = x % (D / 8);
+      u16x8_t kv = {0, 0, 0, 0, 0, 0, 0, 0}, vv = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (r < nk) {
+        kv = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(c0 + r) * D + cc8 * 8);
+        vv = *reinterpret_cast<const u16x8_t*>(V + static_cast<size_t>(c0 + r) * D + cc8 * 8);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sKt[(cc8 * 8 + e) * TST + r] = kv[e];
+        sVt[(cc8 * 8 + e) * TST + r] = vv[e];
+      }
+    }
+    __syncthreads();
+    // weights of this wave's centroids: lane = key
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc) {
+      const int g = wc0 + cc;
+      float dot = 0.f;
+      if (lane < nk) {
+#pragma unroll 16
+        for (int d = 0; d < D; ++d) dot = fmaf(sq[g * D + d], bf16_to_f32(sKt[d * TST + lane]), dot);
+      }
+      const float x = lane < nk ? dot * sl2 : kNegInf;
+      const float cm = wave_max(x);
+      const float nm = fmaxf(runm[cc], cm);
+      const float alpha = fast_exp2(runm[cc] - nm);
+      const float w = fast_exp2(x - nm);
+      runz[cc] = runz[cc] * alpha + wave_sum(w);
+      runm[cc] = nm;
+      sw[g * KC + lane] = w;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[cc][mt][nt][v] *= alpha;
+    }
+    __syncthreads();
+    if (wc0 < ng) {
+#pragma unroll
+      for (int ks = 0; ks < KC / 16; ++ks) {
+        const int kk = 16 * ks + 8 * h;
+        bf16x8_t bk[NNT];
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+          bk[nt] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sKt + (32 * (nt0 + nt) + c) * TST + kk));
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          const u16x8_t vr = *reinterpret_cast<const u16x8_t*>(sVt + (32 * mt + c) * TST + kk);
+#pragma unroll
+          for (int cc = 0; cc < CPW; ++cc) {
+            const float* wr = sw + (wc0 + cc) * KC + kk;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = wr[e] * bf16_to_f32(vr[e]);
+            const bf16x8_t av = pack_bf16x8(x);
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) acc[cc][mt][nt] = mfma32(av, bk[nt], acc[cc][mt][nt]);
+          }
+        }
+      }
+    }
+  }
+  // normalise and store; lane (c, h) holds rows dv = 32 mt + 8 g + 4 h + r, column dk = 32 nt + c
+#pragma unroll
+  for (int cc = 0; cc < CPW; ++cc) {
+    const int g = wc0 + cc;
+    if (g >= ng) continue;
+    const int i = i0 + g;
+    const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
+    const float inv = runz[cc] > 0.f ? 1.f / runz[cc] : 0.f;
+    if (lane == 0 && nt0 == 0)
+      a.blk_lmass[bidx] = runz[cc] > 0.f ? (runm[cc] + __log2f(runz[cc])) * 0.6931471805599453f : kNegInf;
+    float* out = a.blk_mom + bidx * D * D;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int dv = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
+          out[static_cast<size_t>(dv) * D + 32 * (nt0 + nt) + c] = acc[cc][mt][nt][v] * inv;
+        }
+  }
 }
 
 // Fold atoms over blocks: one workgroup per (j, i, head), 2*D threads (K then V dims).
@@ -250,22 +392,24 @@ __global__ void s1_prefix_kernel(S1Args a) {
   if (!a.causal) emit(0);
 }
 
-// Fold block moments: thread per (dv, dk) element; entry b is normalised by its mass.
+// Fold sub-block moments: thread per (dv, dk) element; every table entry is normalised
+// by its mass. Causal entry b holds the sub-blocks of blocks < b.
 __global__ void s1_mom_prefix_kernel(S1Args a) {
   const int D = a.D, Cq = a.Cq;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   const int i = blockIdx.y, bh = blockIdx.z;
   if (e >= D * D) return;
   const int dv = e / D, dk = e % D;
+  const int per_block = a.causal ? a.block / a.mbk : a.nmb;
   float rR = kNegInf, racc = 0.f;
   auto emit = [&](int b) {
     // stored key index first: [dk][dv]
     const size_t sbase = ((static_cast<size_t>(bh) * a.nbS + b) * Cq + i) * D * D;
     a.s_dipT[sbase + static_cast<size_t>(dk) * D + dv] = (rR == kNegInf) ? 0.f : racc;
   };
-  for (int b = 0; b < a.nb; ++b) {
-    if (a.causal) emit(b);
-    const size_t bidx = (static_cast<size_t>(bh) * a.nb + b) * Cq + i;
+  for (int mb = 0; mb < a.nmb; ++mb) {
+    if (a.causal && mb % per_block == 0) emit(mb / per_block);
+    const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
     const float R = a.blk_lmass[bidx];
     if (R != kNegInf) {
       const float x = a.blk_mom[bidx * D * D + e];
@@ -346,6 +490,34 @@ __global__ void __launch_bounds__(256) s1_dip_final_kernel(S1Args a) {
     }
 }
 
+// bf16 hi/lo copies of one table entry (i, e) for the matrix-core stage 2:
+// K_ij (row-major), V_ij transposed to [d][j], and s * D_i with the value index first.
+__global__ void s1_pack_kernel(S1Args a) {
+  const int i = blockIdx.x, e = blockIdx.y, bh = blockIdx.z;
+  const int D = a.D, Ck = a.Ck;
+  const size_t sidx = (static_cast<size_t>(bh) * a.nbS + e) * a.Cq + i;
+  const float* K = a.s_k + sidx * Ck * D;
+  const float* V = a.s_v + sidx * Ck * D;
+  for (int x = threadIdx.x; x < Ck * D; x += blockDim.x) {
+    const float k = K[x];
+    const uint16_t kh = f32_to_bf16_bits(k);
+    a.t_khi[sidx * Ck * D + x] = kh;
+    a.t_klo[sidx * Ck * D + x] = f32_to_bf16_bits(k - bf16_to_f32(kh));
+    const int d = x / Ck, j = x % Ck;  // transposed destination [d][j]
+    const float v = V[static_cast<size_t>(j) * D + d];
+    const uint16_t vh = f32_to_bf16_bits(v);
+    a.t_vthi[sidx * Ck * D + x] = vh;
+    a.t_vtlo[sidx * Ck * D + x] = f32_to_bf16_bits(v - bf16_to_f32(vh));
+  }
+  if (a.dipole) {
+    const float* dipT = a.s_dipT + sidx * D * D;  // [dk][dv]
+    for (int x = threadIdx.x; x < D * D; x += blockDim.x) {
+      const int dv = x / D, dk = x % D;
+      a.t_dip[sidx * D * D + x] = f32_to_bf16_bits(a.scale * dipT[static_cast<size_t>(dk) * D + dv]);
+    }
+  }
+}
+
 template <typename T, int D>
 static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   constexpr int kS1Keys = S1Keys<D>::value;
@@ -361,9 +533,13 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
     hipLaunchKernelGGL(s1_prefix_kernel, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
   }
   if (a.dipole) {
-    const size_t lds_mom = sizeof(float) * (D + 2 * kS1Keys * D + kS1Keys + 4);
-    allow_lds((const void*)s1_moments_kernel<T, D>, lds_mom);
-    {
+    if (sizeof(T) == 2) {
+      constexpr int G = D == 64 ? 8 : 2;
+      ProfScope ps_("s1_moments_mfma", s);
+      hipLaunchKernelGGL((s1_moments_mfma_kernel<D>), dim3(a.nmb, (a.Cq + G - 1) / G, a.BH), dim3(256), 0, s, a);
+    } else {
+      const size_t lds_mom = sizeof(float) * (D + 2 * kS1Keys * D + kS1Keys + 4);
+      allow_lds((const void*)s1_moments_kernel<T, D>, lds_mom);
       ProfScope ps_("s1_moments", s);
       hipLaunchKernelGGL((s1_moments_kernel<T, D>), dim3(a.Cq, a.nb, a.BH), dim3(256), lds_mom, s, a);
     }
@@ -377,6 +553,10 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
       ProfScope ps_("s1_dip_final", s);
       hipLaunchKernelGGL((s1_dip_final_kernel<D>), dim3(a.Cq, a.nbS, a.BH), dim3(256), lds_fin, s, a);
     }
+  }
+  if (a.t_khi != nullptr) {
+    ProfScope ps_("s1_pack", s);
+    hipLaunchKernelGGL(s1_pack_kernel, dim3(a.Cq, a.nbS, a.BH), dim3(256), 0, s, a);
   }
 }
 
