@@ -80,7 +80,13 @@ int validate(Shape& s, const muse_fwd_params* p) {
   s.ntiles = (s.N + s.tile - 1) / s.tile;
   // moment sub-blocks: the matrix-core kernel splits long key ranges for parallelism
   if (s.dtype == MUSE_BF16) {
-    s.mbk = s.causal ? (s.block > 1024 && s.block % 1024 == 0 ? 1024 : s.block) : 1024;
+    s.mbk = 1024;  // largest multiple of 64 that divides the block and is at most 1024
+    if (s.causal)
+      for (int k = 16; k >= 1; --k)
+        if ((s.block / 64) % k == 0) {
+          s.mbk = 64 * k;
+          break;
+        }
   } else {
     s.mbk = s.block;
   }
@@ -114,7 +120,7 @@ struct Plan {
   size_t perm_k, offs_k, perm_q, offs_q;
   size_t t_khi, t_klo, t_vthi, t_vtlo, t_dip, tiles, ntiles, tile_base;
   int max_tiles;
-  size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom;
+  size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores;
   size_t s_logz, s_k, s_v, s_dipT;
   size_t o_far, l_far;
   size_t total;
@@ -146,6 +152,7 @@ Plan make_plan(const Shape& s) {
   P.at_z = L.take(BH * nb * Cq * Ck * f);
   P.at_k = L.take(BH * nb * Cq * Ck * D * f);
   P.at_v = L.take(BH * nb * Cq * Ck * D * f);
+  P.scores = s.dtype == MUSE_BF16 ? L.take(BH * Cq * N * f) : 0;
   P.blk_lmass = L.take(BH * static_cast<size_t>(s.nmb) * Cq * f);
   P.blk_mom = L.take(BH * static_cast<size_t>(s.nmb) * Cq * D * D * f);
   P.s_logz = L.take(BH * nbS * Cq * Ck * f);
@@ -253,6 +260,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.at_z = at<float>(ws, P.at_z);
   a1.at_k = at<float>(ws, P.at_k);
   a1.at_v = at<float>(ws, P.at_v);
+  a1.scores = mf ? at<float>(ws, P.scores) : nullptr;
   a1.nmb = s.nmb;
   a1.mbk = s.mbk;
   a1.blk_lmass = at<float>(ws, P.blk_lmass);

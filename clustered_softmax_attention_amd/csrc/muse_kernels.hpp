@@ -56,6 +56,7 @@ struct S1Args {
   float* at_k;                 // [BH, nb, Cq, Ck, D] sum exp(a - m) k
   float* at_v;                 // [BH, nb, Cq, Ck, D] sum exp(a - m) v
   int nmb, mbk;                // moment sub-blocks: count and keys per sub-block (divides block)
+  float* scores;               // [BH, Cq, N] s qbar_i . k_m (matrix-core path) or null
   float* blk_lmass;            // [BH, nmb, Cq] log mass of a sub-block seen by centroid i
   float* blk_mom;              // [BH, nmb, Cq, D, D] sub-block-normalised sum w v k^T (v index first)
   // summary tables
@@ -72,6 +73,7 @@ struct S1Args {
 };
 
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);
+void launch_stage1_mfma(const S1Args& a, int which, hipStream_t s);  // 0 scores, 1 atoms, 2 moments
 
 // ------------------------------------------------------------------ stage 2
 

@@ -219,147 +219,6 @@ __global__ void __launch_bounds__(256) s1_moments_kernel(S1Args a) {
     for (int y = 0; y < TD; ++y) out[(tr * TD + x) * D + tc * TD + y] = acc[x][y];
 }
 
-// Matrix-core sub-block moments (bf16 inputs): M_i = sum_m w_m v_m k_m^T / sum_m w_m over
-// the keys of one sub-block, w_m = exp(s qbar_i . k_m - running max), and the sub-block
-// log mass. Keys are staged 64 at a time in LDS, transposed (K^T, V^T) so that both
-// operands of the product run along keys; the weights are applied to V^T while forming
-// the A operand (rounded to bf16 there). Centroid groups: D = 64, 8 centroids per
-// workgroup (2 per wave, 4 output tiles each); D = 128, 2 centroids per workgroup (each
-// wave owns half of the 16 output tiles of one centroid).
-template <int D>
-__global__ void __launch_bounds__(256) s1_moments_mfma_kernel(S1Args a) {
-  constexpr int KC = 64;          // keys per step
-  constexpr int TST = KC + 8;     // LDS row stride of K^T / V^T (bf16 elements)
-  constexpr int G = D == 64 ? 8 : 2;
-  constexpr int CPW = D == 64 ? 2 : 1;   // centroids per wave
-  constexpr int NMT = D / 32;            // row tiles (dv)
-  constexpr int NNT = D == 64 ? 2 : 2;   // column tiles (dk) per wave
-  __shared__ __align__(16) uint16_t sKt[D * TST];
-  __shared__ __align__(16) uint16_t sVt[D * TST];
-  __shared__ float sq[G * D];
-  __shared__ float sw[G * KC];
-  const int mb = blockIdx.x, ig = blockIdx.y, bh = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
-  const int Cq = a.Cq;
-  const int i0 = ig * G;
-  const int ng = min(G, Cq - i0);
-  // this wave's centroids (local index within the group) and dk half
-  const int wc0 = D == 64 ? 2 * wave : wave / 2;
-  const int nt0 = D == 64 ? 0 : 2 * (wave & 1);
-  for (int x = tid; x < G * D; x += 256) {
-    const int g = x / D;
-    sq[x] = g < ng ? a.qbar[(static_cast<size_t>(bh) * Cq + i0 + g) * D + x % D] : 0.f;
-  }
-  const int key0 = mb * a.mbk;
-  const int key1 = min(a.N, key0 + a.mbk);
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
-  const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
-
-  f32x16_t acc[CPW][NMT][NNT];
-#pragma unroll
-  for (int cc = 0; cc < CPW; ++cc)
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NNT; ++nt) acc[cc][mt][nt] = zero16();
-  float runm[CPW], runz[CPW];
-#pragma unroll
-  for (int cc = 0; cc < CPW; ++cc) {
-    runm[cc] = -1e30f;
-    runz[cc] = 0.f;
-  }
-  const float sl2 = a.scale * 1.4426950408889634f;
-
-  for (int c0 = key0; c0 < key1; c0 += KC) {
-    const int nk = min(KC, key1 - c0);
-    __syncthreads();
-    for (int x = tid; x < KC * (D / 8); x += 256) {
-      const int r = x / (D / 8), cc8 = x % (D / 8);
-      u16x8_t kv = {0, 0, 0, 0, 0, 0, 0, 0}, vv = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (r < nk) {
-        kv = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(c0 + r) * D + cc8 * 8);
-        vv = *reinterpret_cast<const u16x8_t*>(V + static_cast<size_t>(c0 + r) * D + cc8 * 8);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sKt[(cc8 * 8 + e) * TST + r] = kv[e];
-        sVt[(cc8 * 8 + e) * TST + r] = vv[e];
-      }
-    }
-    __syncthreads();
-    // weights of this wave's centroids: lane = key
-#pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int g = wc0 + cc;
-      float dot = 0.f;
-      if (lane < nk) {
-#pragma unroll 16
-        for (int d = 0; d < D; ++d) dot = fmaf(sq[g * D + d], bf16_to_f32(sKt[d * TST + lane]), dot);
-      }
-      const float x = lane < nk ? dot * sl2 : kNegInf;
-      const float cm = wave_max(x);
-      const float nm = fmaxf(runm[cc], cm);
-      const float alpha = fast_exp2(runm[cc] - nm);
-      const float w = fast_exp2(x - nm);
-      runz[cc] = runz[cc] * alpha + wave_sum(w);
-      runm[cc] = nm;
-      sw[g * KC + lane] = w;
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[cc][mt][nt][v] *= alpha;
-    }
-    __syncthreads();
-    if (wc0 < ng) {
-#pragma unroll
-      for (int ks = 0; ks < KC / 16; ++ks) {
-        const int kk = 16 * ks + 8 * h;
-        bf16x8_t bk[NNT];
-#pragma unroll
-        for (int nt = 0; nt < NNT; ++nt)
-          bk[nt] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sKt + (32 * (nt0 + nt) + c) * TST + kk));
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-          const u16x8_t vr = *reinterpret_cast<const u16x8_t*>(sVt + (32 * mt + c) * TST + kk);
-#pragma unroll
-          for (int cc = 0; cc < CPW; ++cc) {
-            const float* wr = sw + (wc0 + cc) * KC + kk;
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = wr[e] * bf16_to_f32(vr[e]);
-            const bf16x8_t av = pack_bf16x8(x);
-#pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) acc[cc][mt][nt] = mfma32(av, bk[nt], acc[cc][mt][nt]);
-          }
-        }
-      }
-    }
-  }
-  // normalise and store; lane (c, h) holds rows dv = 32 mt + 8 g + 4 h + r, column dk = 32 nt + c
-#pragma unroll
-  for (int cc = 0; cc < CPW; ++cc) {
-    const int g = wc0 + cc;
-    if (g >= ng) continue;
-    const int i = i0 + g;
-    const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
-    const float inv = runz[cc] > 0.f ? 1.f / runz[cc] : 0.f;
-    if (lane == 0 && nt0 == 0)
-      a.blk_lmass[bidx] = runz[cc] > 0.f ? (runm[cc] + __log2f(runz[cc])) * 0.6931471805599453f : kNegInf;
-    float* out = a.blk_mom + bidx * D * D;
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int dv = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
-          out[static_cast<size_t>(dv) * D + 32 * (nt0 + nt) + c] = acc[cc][mt][nt][v] * inv;
-        }
-  }
-}
-
 // Fold atoms over blocks: one workgroup per (j, i, head), 2*D threads (K then V dims).
 __global__ void s1_prefix_kernel(S1Args a) {
   const int j = blockIdx.x, i = blockIdx.y, bh = blockIdx.z;
@@ -521,10 +380,14 @@ __global__ void s1_pack_kernel(S1Args a) {
 template <typename T, int D>
 static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   constexpr int kS1Keys = S1Keys<D>::value;
-  const size_t lds_atoms = sizeof(float) * (static_cast<size_t>(a.Cq) * D + 2 * kS1Keys * D +
-                                            static_cast<size_t>(a.Cq) * kS1Keys + 3 * a.Cq);
-  allow_lds((const void*)s1_atoms_kernel<T, D>, lds_atoms);
-  {
+  const bool mf = sizeof(T) == 2;  // bf16 inputs: matrix-core kernels
+  if (mf) {
+    launch_stage1_mfma(a, 0, s);
+    launch_stage1_mfma(a, 1, s);
+  } else {
+    const size_t lds_atoms = sizeof(float) * (static_cast<size_t>(a.Cq) * D + 2 * kS1Keys * D +
+                                              static_cast<size_t>(a.Cq) * kS1Keys + 3 * a.Cq);
+    allow_lds((const void*)s1_atoms_kernel<T, D>, lds_atoms);
     ProfScope ps_("s1_atoms", s);
     hipLaunchKernelGGL((s1_atoms_kernel<T, D>), dim3(a.Ck, a.nb, a.BH), dim3(256), lds_atoms, s, a);
   }
@@ -533,10 +396,8 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
     hipLaunchKernelGGL(s1_prefix_kernel, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
   }
   if (a.dipole) {
-    if (sizeof(T) == 2) {
-      constexpr int G = D == 64 ? 8 : 2;
-      ProfScope ps_("s1_moments_mfma", s);
-      hipLaunchKernelGGL((s1_moments_mfma_kernel<D>), dim3(a.nmb, (a.Cq + G - 1) / G, a.BH), dim3(256), 0, s, a);
+    if (mf) {
+      launch_stage1_mfma(a, 2, s);
     } else {
       const size_t lds_mom = sizeof(float) * (D + 2 * kS1Keys * D + kS1Keys + 4);
       allow_lds((const void*)s1_moments_kernel<T, D>, lds_mom);
