@@ -35,25 +35,49 @@
 
 namespace muse {
 
-template <typename T>
-__global__ void kmeans_init_kernel(KmArgs a) {
-  const KmTensor& t = a.t[blockIdx.z];
-  if (t.labels_in != nullptr) return;
-  const int bh = blockIdx.y;
-  const T* x = static_cast<const T*>(t.x) + static_cast<size_t>(bh) * a.N * a.D;
-  float* c = t.cent + static_cast<size_t>(bh) * t.C * a.D;
-  for (int e = threadIdx.x; e < t.C * a.D; e += blockDim.x) {
-    const int j = e / a.D, d = e % a.D;
-    const long src = (static_cast<long>(j) * a.N) / t.C;
-    c[e] = Elem<T>::load(x, static_cast<size_t>(src) * a.D + d);
+// Derived forms of centroid j used by the matrix-core assign: bf16 hi/lo split and
+// ||c_j||^2 (fp32, fixed reduction order). Called by one whole wave, lanes over d.
+__device__ __forceinline__ void write_centroid_tables(const KmTensor& t, int D, size_t row, const float* vals,
+                                                      int nper) {
+  float n2 = 0.f;
+  for (int q = 0; q < nper; ++q) {
+    const int d = lane_id() + 64 * q;
+    const float cv = vals[q];
+    n2 = fmaf(cv, cv, n2);
+    if (t.chi != nullptr) {
+      const uint16_t hi = f32_to_bf16_bits(cv);
+      t.chi[row * D + d] = hi;
+      t.clo[row * D + d] = f32_to_bf16_bits(cv - bf16_to_f32(hi));
+    }
   }
+  n2 = wave_sum(n2);
+  if (t.cn2 != nullptr && lane_id() == 0) t.cn2[row] = n2;
+}
+
+// One wave per (centroid j, head, tensor): c_j = x[floor(j*N/C)].
+template <typename T>
+__global__ void __launch_bounds__(64) kmeans_init_kernel(KmArgs a) {
+  const KmTensor& t = a.t[blockIdx.z];
+  const int j = blockIdx.x, bh = blockIdx.y;
+  if (t.labels_in != nullptr || j >= t.C) return;
+  const T* x = static_cast<const T*>(t.x) + static_cast<size_t>(bh) * a.N * a.D;
+  const long src = (static_cast<long>(j) * a.N) / t.C;
+  const size_t row = static_cast<size_t>(bh) * t.C + j;
+  float vals[2];
+  const int nper = a.D / 64;
+  for (int q = 0; q < nper; ++q) {
+    const int d = lane_id() + 64 * q;
+    vals[q] = Elem<T>::load(x, static_cast<size_t>(src) * a.D + d);
+    t.cent[row * a.D + d] = vals[q];
+  }
+  write_centroid_tables(t, a.D, row, vals, nper);
 }
 
 // Stable counting sort of the tile's points by label (LDS), then the tile's sort info
 // and per-cluster sums. Called by every thread of the workgroup.
 template <typename T, int D>
-__device__ void tile_sort_and_sums(const KmArgs& a, const KmTensor& t, int lab, bool valid, int* s_lab,
-                                   int* s_whist, int* s_cnt, int* s_start, int* s_sorted) {
+__device__ void tile_sort(const KmArgs& a, const KmTensor& t, int lab, bool valid, int* s_lab, int* s_whist,
+                          int* s_cnt, int* s_start, int* s_sorted) {
   const int C = t.C;
   const int bh = blockIdx.y;
   const int tile = blockDim.x;
@@ -102,6 +126,18 @@ __device__ void tile_sort_and_sums(const KmArgs& a, const KmTensor& t, int lab, 
     t.tile_start[tix * C + j] = s_start[j];
   }
   t.tile_perm[tix * a.tile + tid] = static_cast<uint16_t>(s_sorted[tid]);
+}
+
+// Per-cluster sums of the tile in sorted order (fp32 path).
+template <typename T, int D>
+__device__ void tile_sums_valu(const KmArgs& a, const KmTensor& t, const int* s_cnt, const int* s_start,
+                               const int* s_sorted) {
+  const int C = t.C;
+  const int bh = blockIdx.y;
+  const int tile = blockDim.x;
+  const int tid = threadIdx.x;
+  const T* x = static_cast<const T*>(t.x) + static_cast<size_t>(bh) * a.N * D;
+  const size_t tix = static_cast<size_t>(bh) * a.ntiles + blockIdx.x;
   float* psum = t.psum + tix * C * D;
   const long base = static_cast<long>(blockIdx.x) * tile;
   for (int e = tid; e < C * D; e += tile) {
@@ -174,16 +210,17 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_kernel(KmArgs a, int i
     if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
   }
 
-  tile_sort_and_sums<T, D>(a, t, lab, valid, s_lab, s_whist, s_cnt, s_start, s_sorted);
+  tile_sort<T, D>(a, t, lab, valid, s_lab, s_whist, s_cnt, s_start, s_sorted);
+  tile_sums_valu<T, D>(a, t, s_cnt, s_start, s_sorted);
 }
 
-// Matrix-core assign for bf16 inputs; blockDim.x == tile (multiple of 64, <= kMaxTile).
+// Matrix-core assign for bf16 inputs; blockDim.x == tile (multiple of 64, <= kMaxTileMfma).
 // Wave w scores points w*64 .. w*64+63 in two groups of 32 (lane (c, h) of the product
 // holds 16 centroid rows of point c per 32-row tile). Lane l = 32 h + c of the wave
 // then owns point w*64 + l for the sort. Dynamic LDS: c_hi, c_lo [Cp][D+8] bf16 |
-// ||c||^2 [Cp] | sort buffers.
-template <int D>
-__global__ void __launch_bounds__(kMaxTile) kmeans_assign_mfma_kernel(KmArgs a, int iter) {
+// ||c||^2 [Cp] | sort buffers | X^T staging [D][64+8] bf16.
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW) kmeans_assign_mfma_kernel(KmArgs a, int iter, int last) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int CST = D + 8;
   constexpr int NKS = D / 16;
@@ -209,22 +246,35 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_mfma_kernel(KmArgs a, 
   if (t.labels_in != nullptr) {
     if (valid) lab = min(max(t.labels_in[static_cast<size_t>(bh) * a.N + n], 0), C - 1);
   } else {
-    for (int e = tid; e < Cp * D; e += tile) {
-      const int j = e / D, d = e % D;
-      const float cv = j < C ? cent[static_cast<size_t>(j) * D + d] : 0.f;
-      const uint16_t hi = f32_to_bf16_bits(cv);
-      chi[j * CST + d] = hi;
-      clo[j * CST + d] = f32_to_bf16_bits(cv - bf16_to_f32(hi));
+    // the first group of this wave's points, loaded before anything waits on memory
+    u16x8_t xraw[NKS];
+    auto load_group = [&](int gi) {
+      const long p = static_cast<long>(blockIdx.x) * tile + wave * 64 + gi * 32 + c;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        xraw[ks] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        if (p < a.N) xraw[ks] = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(p) * D + 16 * ks + 8 * h);
+      }
+    };
+    load_group(0);
+    const uint16_t* ghi = t.chi + static_cast<size_t>(bh) * C * D;
+    const uint16_t* glo = t.clo + static_cast<size_t>(bh) * C * D;
+#pragma unroll 4
+    for (int e = tid; e < Cp * (D / 8); e += tile) {
+      const int j = e / (D / 8), c8 = e % (D / 8);
+      u16x8_t h8 = {0, 0, 0, 0, 0, 0, 0, 0}, l8 = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (j < C) {
+        h8 = *reinterpret_cast<const u16x8_t*>(ghi + static_cast<size_t>(j) * D + c8 * 8);
+        l8 = *reinterpret_cast<const u16x8_t*>(glo + static_cast<size_t>(j) * D + c8 * 8);
+      }
+      *reinterpret_cast<u16x8_t*>(chi + j * CST + c8 * 8) = h8;
+      *reinterpret_cast<u16x8_t*>(clo + j * CST + c8 * 8) = l8;
     }
-    for (int j = tid; j < Cp; j += tile) {
-      float n2 = 0.f;
-      if (j < C)
-        for (int d = 0; d < D; ++d) n2 = fmaf(cent[static_cast<size_t>(j) * D + d], cent[static_cast<size_t>(j) * D + d], n2);
-      cn2[j] = n2;
-    }
+    for (int j = tid; j < Cp; j += tile) cn2[j] = j < C ? t.cn2[static_cast<size_t>(bh) * C + j] : 0.f;
     __syncthreads();
     float cmax2 = 0.f;
-    for (int j = 0; j < C; ++j) cmax2 = fmaxf(cmax2, cn2[j]);
+    for (int j = lane; j < C; j += 64) cmax2 = fmaxf(cmax2, cn2[j]);
+    cmax2 = wave_max(cmax2);
     const float cmax = sqrtf(cmax2);
     int labs[2];
 #pragma unroll
@@ -233,10 +283,10 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_mfma_kernel(KmArgs a, 
       const bool pv = p < a.N;
       bf16x8_t xf[NKS];
       float xx = 0.f;
+      if (gi == 1) load_group(1);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        u16x8_t u = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (pv) u = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(p) * D + 16 * ks + 8 * h);
+        const u16x8_t u = xraw[ks];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const float xv = bf16_to_f32(u[r]);
@@ -245,13 +295,9 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_mfma_kernel(KmArgs a, 
         xf[ks] = as_bf16x8(u);
       }
       xx += __shfl_xor(xx, 32, 64);
-      float sc[MAXJT][16];
-      float best = __builtin_huge_valf();
-      int bj = C;
-#pragma unroll
-      for (int jt = 0; jt < MAXJT; ++jt) {
-        if (jt >= njt) break;
-        f32x16_t acc = zero16();
+      // scores of one 32-centroid tile: lane (c, h) holds centroids 32 jt + 8 g + 4 h + r
+      auto score_tile = [&](int jt, f32x16_t& acc) {
+        acc = zero16();
         const int jr = 32 * jt + c;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -263,59 +309,73 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_mfma_kernel(KmArgs a, 
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
-          const float x = j < C ? cn2[j] - 2.f * acc[v] : __builtin_huge_valf();
-          sc[jt][v] = x;
+          acc[v] = j < C ? cn2[j] - 2.f * acc[v] : __builtin_huge_valf();
+        }
+      };
+      // running best (lowest index on ties) and second-best score
+      float best = __builtin_huge_valf(), second = __builtin_huge_valf();
+      int bj = C;
+      for (int jt = 0; jt < njt; ++jt) {
+        f32x16_t sc;
+        score_tile(jt, sc);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
+          const float x = sc[v];
           if (x < best || (x == best && j < bj)) {
+            second = best;
             best = x;
             bj = j;
+          } else {
+            second = fminf(second, x);
           }
         }
       }
       {
         const float ob = __shfl_xor(best, 32, 64);
+        const float os = __shfl_xor(second, 32, 64);
         const int oj = __shfl_xor(bj, 32, 64);
         if (ob < best || (ob == best && oj < bj)) {
+          second = fminf(best, os);
           best = ob;
           bj = oj;
+        } else {
+          second = fminf(second, ob);
         }
       }
       const float E = 1e-4f * sqrtf(xx) * cmax + 2e-5f * cmax2;
       const float thr = best + 2.f * E;
-      uint64_t mask = 0;
+      // a second centroid within the window: re-score every candidate exactly
+      if (__ballot(pv && second <= thr) != 0ull) {
+        const bool need = pv && second <= thr;  // the same for both lanes of the pair
+        float fb = __builtin_huge_valf();
+        int fj = C;
+        const uint16_t* xr = X + static_cast<size_t>(p) * D;
+        for (int jt = 0; jt < njt; ++jt) {
+          f32x16_t sc;
+          score_tile(jt, sc);
+          if (need) {
 #pragma unroll
-      for (int jt = 0; jt < MAXJT; ++jt) {
-        if (jt >= njt) break;
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (sc[jt][v] <= thr) mask |= 1ull << (16 * jt + v);
-      }
-      const int total = __popcll(mask) + __shfl_xor(__popcll(mask), 32, 64);
-      if (__ballot(pv && total > 1) != 0ull) {
-        if (pv && total > 1) {  // both lanes of the pair take this branch together
-          float fb = __builtin_huge_valf();
-          int fj = C;
-          const uint16_t* xr = X + static_cast<size_t>(p) * D;
-          while (mask != 0ull) {
-            const int idx = __ffsll(static_cast<unsigned long long>(mask)) - 1;
-            mask &= mask - 1;
-            const int jt = idx >> 4, v = idx & 15;
-            const int j = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
-            const float* cr = cent + static_cast<size_t>(j) * D;
-            float dist = 0.f;
-            for (int d = 0; d < D; ++d) {
-              const float diff = bf16_to_f32(xr[d]) - cr[d];
-              dist = fmaf(diff, diff, dist);
-            }
-            if (dist < fb || (dist == fb && j < fj)) {
-              fb = dist;
-              fj = j;
+            for (int v = 0; v < 16; ++v) {
+              if (sc[v] > thr) continue;
+              const int j = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
+              const float* cr = cent + static_cast<size_t>(j) * D;
+              float dist = 0.f;
+              for (int d = 0; d < D; ++d) {
+                const float diff = bf16_to_f32(xr[d]) - cr[d];
+                dist = fmaf(diff, diff, dist);
+              }
+              if (dist < fb || (dist == fb && j < fj)) {
+                fb = dist;
+                fj = j;
+              }
             }
           }
-          const float ob = __shfl_xor(fb, 32, 64);
-          const int oj = __shfl_xor(fj, 32, 64);
-          if (ob < fb || (ob == fb && oj < fj)) fj = oj;
-          bj = fj;
         }
+        const float ob = __shfl_xor(fb, 32, 64);
+        const int oj = __shfl_xor(fj, 32, 64);
+        if (ob < fb || (ob == fb && oj < fj)) fj = oj;
+        if (need) bj = fj;
       }
       labs[gi] = bj;
     }
@@ -325,25 +385,121 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_mfma_kernel(KmArgs a, 
     t.labels[static_cast<size_t>(bh) * a.N + n] = lab;
     if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
   }
-  tile_sort_and_sums<bf16, D>(a, t, lab, valid, s_lab, s_whist, s_cnt, s_start, s_sorted);
+  const size_t tix = static_cast<size_t>(bh) * a.ntiles + blockIdx.x;
+  if (last) {
+    // bucketing after the last iteration needs the stable order
+    tile_sort<bf16, D>(a, t, lab, valid, s_lab, s_whist, s_cnt, s_start, s_sorted);
+  } else {
+    for (int j = tid; j < C; j += tile) s_cnt[j] = 0;
+    s_lab[tid] = lab;
+    __syncthreads();
+    if (valid) atomicAdd(&s_cnt[lab], 1);  // integer counts: order-independent
+    __syncthreads();
+    for (int j = tid; j < C; j += tile) t.tile_cnt[tix * C + j] = s_cnt[j];
+  }
+  // cluster sums psum^T [D x C] = X^T onehot over 64-point sub-chunks; wave w owns output
+  // tiles w, w + nwaves, ... of the (D/32) x (Cp/32) grid
+  constexpr int XST = 64 + 8;
+  constexpr int NDT = D / 32;
+  constexpr int MAXOT = (NDT * (kMaxClusters / 32) + NW - 1) / NW < 4 ? (NDT * (kMaxClusters / 32) + NW - 1) / NW : 4;
+  uint16_t* sXt = reinterpret_cast<uint16_t*>((reinterpret_cast<uintptr_t>(s_sorted + tile) + 15) & ~uintptr_t(15));
+  const int nwaves = tile >> 6;
+  const int not_ = NDT * njt;
+  const uint16_t bf_one = 0x3F80;
+  float* psum = t.psum + tix * C * D;
+  // a sub-chunk of 64 points is 64*D/8 16-byte pieces; each thread carries kPre of them
+  constexpr int kPre = (64 * (D / 8)) / (64 * NW);
+  auto load_chunk = [&](int p0, u16x8_t* buf) {
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) {
+      const int x = tid + tile * q;
+      buf[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      if (x < 64 * (D / 8)) {
+        const int r = x / (D / 8), c8 = x % (D / 8);
+        const long pn = static_cast<long>(blockIdx.x) * tile + p0 + r;
+        if (pn < a.N) buf[q] = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(pn) * D + c8 * 8);
+      }
+    }
+  };
+  for (int ot0 = 0; ot0 < not_; ot0 += nwaves * MAXOT) {
+    f32x16_t acc[MAXOT];
+#pragma unroll
+    for (int r = 0; r < MAXOT; ++r) acc[r] = zero16();
+    u16x8_t pre[kPre];
+    load_chunk(0, pre);
+    for (int p0 = 0; p0 < tile; p0 += 64) {
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kPre; ++q) {
+        const int x = tid + tile * q;
+        if (x < 64 * (D / 8)) {
+          const int r = x / (D / 8), c8 = x % (D / 8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sXt[(c8 * 8 + e) * XST + r] = pre[q][e];
+        }
+      }
+      __syncthreads();
+      if (p0 + 64 < tile) load_chunk(p0 + 64, pre);  // next sub-chunk in flight during this one
+#pragma unroll
+      for (int r = 0; r < MAXOT; ++r) {
+        const int ot = ot0 + wave + nwaves * r;
+        if (ot >= not_) break;
+        const int dt = ot % NDT, ct = ot / NDT;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int kk = 16 * ks + 8 * h;
+          const bf16x8_t ax = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sXt + (32 * dt + c) * XST + kk));
+          u16x8_t oh;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) oh[e] = s_lab[p0 + kk + e] == 32 * ct + c ? bf_one : 0;
+          acc[r] = mfma32(ax, as_bf16x8(oh), acc[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < MAXOT; ++r) {
+      const int ot = ot0 + wave + nwaves * r;
+      if (ot >= not_) break;
+      const int dt = ot % NDT, ct = ot / NDT;
+      const int j = 32 * ct + c;
+      if (j >= C) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4_t f = {acc[r][4 * g], acc[r][4 * g + 1], acc[r][4 * g + 2], acc[r][4 * g + 3]};
+        *reinterpret_cast<f32x4_t*>(psum + static_cast<size_t>(j) * D + 32 * dt + 8 * g + 4 * h) = f;
+      }
+    }
+  }
 }
 
-// Thread per (cluster j, dim d): sum the tile partials in tile order.
-__global__ void kmeans_update_kernel(KmArgs a) {
+// One wave per (centroid j, head, tensor), lanes over d: sum the tile partials in tile
+// order; the mean replaces c_j unless the cluster is empty.
+__global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
-  const int C = t.C, D = a.D, bh = blockIdx.y;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= C * D) return;
-  const int j = e / D;
+  const int C = t.C, D = a.D, j = blockIdx.x, bh = blockIdx.y;
+  if (j >= C) return;
   const size_t tbase = static_cast<size_t>(bh) * a.ntiles;
-  float acc = 0.f;
+  const int nper = D / 64;
+  float acc[2] = {0.f, 0.f};
   int cnt = 0;
+#pragma unroll 8
   for (int tt = 0; tt < a.ntiles; ++tt) {
-    acc += t.psum[(tbase + tt) * C * D + e];
+    const float* ps = t.psum + ((tbase + tt) * C + j) * D;
+    acc[0] += ps[lane_id()];
+    if (nper > 1) acc[1] += ps[lane_id() + 64];
     cnt += t.tile_cnt[(tbase + tt) * C + j];
   }
-  if (cnt > 0) t.cent[static_cast<size_t>(bh) * C * D + e] = acc / static_cast<float>(cnt);
-  else if (t.labels_in != nullptr) t.cent[static_cast<size_t>(bh) * C * D + e] = 0.f;
+  const size_t row = static_cast<size_t>(bh) * C + j;
+  float vals[2];
+  for (int q = 0; q < nper; ++q) {
+    const int d = lane_id() + 64 * q;
+    float v;
+    if (cnt > 0) v = acc[q] / static_cast<float>(cnt);
+    else v = t.labels_in != nullptr ? 0.f : t.cent[row * D + d];  // empty cluster keeps c_j
+    t.cent[row * D + d] = v;
+    vals[q] = v;
+  }
+  write_centroid_tables(t, D, row, vals, nper);
 }
 
 // One workgroup per (head, tensor): counts per (block, cluster) and their exclusive
@@ -400,31 +556,36 @@ __global__ void bucket_scatter_kernel(KmArgs a) {
 
 template <typename T>
 static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
-  const dim3 g_init(1, a.BH, a.ntensors);
+  const int Cmax = max(a.t[0].C, a.ntensors > 1 ? a.t[1].C : 0);
   {
     ProfScope ps_("kmeans_init", s);
-    hipLaunchKernelGGL(kmeans_init_kernel<T>, g_init, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(kmeans_init_kernel<T>, dim3(Cmax, a.BH, a.ntensors), dim3(64), 0, s, a);
   }
-  const int Cmax = max(a.t[0].C, a.ntensors > 1 ? a.t[1].C : 0);
   const size_t lds = static_cast<size_t>(kChunkC) * a.D * sizeof(float) +
                      sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax);
   const dim3 g_assign(a.ntiles, a.BH, a.ntensors);
-  const dim3 g_update((Cmax * a.D + 255) / 256, a.BH, a.ntensors);
+  const dim3 g_update(Cmax, a.BH, a.ntensors);
   const int Cp = (Cmax + 31) & ~31;
   const size_t lds_mfma = static_cast<size_t>(Cp) * (a.D + 8) * 2 * sizeof(uint16_t) + Cp * sizeof(float) +
-                          sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax);
+                          sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax) +
+                          static_cast<size_t>(a.D) * (64 + 8) * sizeof(uint16_t) + 16;
   const bool mf = sizeof(T) == 2;
-  if (mf) {
-    allow_lds((const void*)kmeans_assign_mfma_kernel<64>, lds_mfma);
-    allow_lds((const void*)kmeans_assign_mfma_kernel<128>, lds_mfma);
+  auto launch_mfma = [&](int it) {
+    const int last = it == iters - 1;
+    const int nw = a.tile / 64;
+#define MUSE_KM_CASE(DD, NN)                                                                            \
+  if (a.D == DD && nw == NN) {                                                                          \
+    allow_lds((const void*)kmeans_assign_mfma_kernel<DD, NN>, lds_mfma);                               \
+    hipLaunchKernelGGL((kmeans_assign_mfma_kernel<DD, NN>), g_assign, dim3(a.tile), lds_mfma, s, a, it, last); \
   }
+    MUSE_KM_CASE(64, 1) MUSE_KM_CASE(64, 2) MUSE_KM_CASE(64, 3) MUSE_KM_CASE(64, 4)
+    MUSE_KM_CASE(128, 1) MUSE_KM_CASE(128, 2) MUSE_KM_CASE(128, 3) MUSE_KM_CASE(128, 4)
+#undef MUSE_KM_CASE
+  };
   for (int it = 0; it < iters; ++it) {
     if (mf) {
       ProfScope ps_("kmeans_assign_mfma", s);
-      if (a.D == 64)
-        hipLaunchKernelGGL((kmeans_assign_mfma_kernel<64>), g_assign, dim3(a.tile), lds_mfma, s, a, it);
-      else
-        hipLaunchKernelGGL((kmeans_assign_mfma_kernel<128>), g_assign, dim3(a.tile), lds_mfma, s, a, it);
+      launch_mfma(it);
     } else {
       ProfScope ps_("kmeans_assign", s);
       if (a.D == 64)
@@ -434,7 +595,7 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
     }
     {
       ProfScope ps_("kmeans_update", s);
-      hipLaunchKernelGGL(kmeans_update_kernel, g_update, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(kmeans_update_kernel, g_update, dim3(64), 0, s, a);
     }
   }
   const size_t lds_off = sizeof(int) * static_cast<size_t>(a.nb) * Cmax;

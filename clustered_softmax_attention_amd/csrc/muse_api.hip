@@ -48,10 +48,10 @@ struct Shape {
   int nmb, mbk;  // dipole-moment sub-blocks
 };
 
-// Largest multiple of 64 that divides `block` and is at most kMaxTile.
-int tile_for_block(int block) {
+// Largest multiple of 64 that divides `block` and is at most max_tile.
+int tile_for_block(int block, int max_tile) {
   const int k = block / 64;
-  for (int t = muse::kMaxTile / 64; t >= 1; --t)
+  for (int t = max_tile / 64; t >= 1; --t)
     if (k % t == 0) return 64 * t;
   return 64;
 }
@@ -63,18 +63,19 @@ int validate(Shape& s, const muse_fwd_params* p) {
   if (static_cast<long>(s.B) * s.H * s.N > (1l << 31) / 256) return fail(MUSE_ERR_UNSUPPORTED, "B*H*N too large");
   if (s.causal != 0 && s.causal != 1) return fail(MUSE_ERR_INVALID_ARG, "causal must be 0 or 1");
   s.BH = s.B * s.H;
+  const int max_tile = s.dtype == MUSE_BF16 ? muse::kMaxTileMfma : muse::kMaxTile;
   if (s.causal) {
     if (s.block < 64 || s.block > s.N || s.N % s.block != 0 || s.block % 64 != 0)
       return fail(MUSE_ERR_INVALID_ARG, "causal block=%d must divide N=%d, be >= 64 and a multiple of 64", s.block, s.N);
     s.nb = s.N / s.block;
     s.nbS = s.nb;
-    s.tile = tile_for_block(s.block);
+    s.tile = tile_for_block(s.block, max_tile);
     s.tiles_per_block = s.block / s.tile;
   } else {
     s.block = s.N;
     s.nb = 1;
     s.nbS = 1;
-    s.tile = muse::kMaxTile;
+    s.tile = max_tile;
     s.tiles_per_block = (s.N + s.tile - 1) / s.tile;
   }
   s.ntiles = (s.N + s.tile - 1) / s.tile;
@@ -116,6 +117,7 @@ int validate_muse(Shape& s, const muse_fwd_params* p) {
 }
 
 struct Plan {
+  size_t chi_q, clo_q, cn2_q, chi_k, clo_k, cn2_k;
   size_t cent_q, cent_k, lab_q, lab_k, tperm_q, tperm_k, tcnt_q, tcnt_k, tst_q, tst_k, psum_q, psum_k;
   size_t perm_k, offs_k, perm_q, offs_q;
   size_t t_khi, t_klo, t_vthi, t_vtlo, t_dip, tiles, ntiles, tile_base;
@@ -134,6 +136,14 @@ Plan make_plan(const Shape& s) {
   const size_t f = sizeof(float), i4 = sizeof(int32_t);
   P.cent_q = L.take(BH * Cq * D * f);
   P.cent_k = L.take(BH * Ck * D * f);
+  if (s.dtype == MUSE_BF16) {
+    P.chi_q = L.take(BH * Cq * D * 2);
+    P.clo_q = L.take(BH * Cq * D * 2);
+    P.chi_k = L.take(BH * Ck * D * 2);
+    P.clo_k = L.take(BH * Ck * D * 2);
+  }
+  P.cn2_q = L.take(BH * Cq * f);
+  P.cn2_k = L.take(BH * Ck * f);
   P.lab_q = L.take(BH * N * i4);
   P.lab_k = L.take(BH * N * i4);
   P.tperm_q = L.take(BH * nt * tile * sizeof(uint16_t));
@@ -213,6 +223,9 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   tq.x = q;
   tq.C = s.Cq;
   tq.cent = at<float>(ws, P.cent_q);
+  tq.chi = s.dtype == MUSE_BF16 ? at<uint16_t>(ws, P.chi_q) : nullptr;
+  tq.clo = s.dtype == MUSE_BF16 ? at<uint16_t>(ws, P.clo_q) : nullptr;
+  tq.cn2 = at<float>(ws, P.cn2_q);
   tq.labels = at<int32_t>(ws, P.lab_q);
   tq.trace = p ? p->labels_q_trace : nullptr;
   tq.labels_in = p ? p->labels_q_in : nullptr;
@@ -227,6 +240,9 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   tk.x = k;
   tk.C = s.Ck;
   tk.cent = at<float>(ws, P.cent_k);
+  tk.chi = s.dtype == MUSE_BF16 ? at<uint16_t>(ws, P.chi_k) : nullptr;
+  tk.clo = s.dtype == MUSE_BF16 ? at<uint16_t>(ws, P.clo_k) : nullptr;
+  tk.cn2 = at<float>(ws, P.cn2_k);
   tk.labels = at<int32_t>(ws, P.lab_k);
   tk.trace = p ? p->labels_k_trace : nullptr;
   tk.labels_in = p ? p->labels_k_in : nullptr;

@@ -6,7 +6,8 @@
 namespace muse {
 
 constexpr int kChunkC = 32;    // centroids staged in LDS at a time by the fp32 assign kernel
-constexpr int kMaxTile = 512;  // K-means tile (points per workgroup) upper bound
+constexpr int kMaxTile = 512;  // K-means tile (points per workgroup) upper bound, fp32 path
+constexpr int kMaxTileMfma = 256;  // the same for the matrix-core (bf16) path
 constexpr int kMaxClusters = 128;
 
 // ------------------------------------------------------------------ K-means
@@ -15,6 +16,9 @@ struct KmTensor {
   const void* x;               // [BH, N, D] input (dtype of the call)
   int C;                       // clusters
   float* cent;                 // [BH, C, D] current centroids
+  uint16_t* chi;               // [BH, C, D] bf16 hi part of cent (matrix-core path) or null
+  uint16_t* clo;               // [BH, C, D] bf16 lo part: cent = hi + lo up to 2^-16
+  float* cn2;                  // [BH, C] ||c_j||^2 in fp32
   int32_t* labels;             // [BH, N] labels of the latest assign step
   int32_t* trace;              // [iters, BH, N] or null
   const int32_t* labels_in;    // [BH, N] caller-fixed labels or null

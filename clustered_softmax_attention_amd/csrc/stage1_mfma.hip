@@ -5,11 +5,15 @@
 // a_im = s qbar_i . k_m; per (i, key cluster j, block b') the atom (max, sum exp, sum
 // exp k, sum exp v); per (i, moment sub-block) the normalised sum w v k^T and its log
 // mass. Here:
-//   s1_scores      a_im for every centroid and key, [BH, Cq, N] fp32 (qbar split into
-//                  bf16 hi + lo; keys are exact in bf16).
+// Keys are visited in bucketed order (the key permutation sorted by block, then key
+// cluster), so that a bucket, a block and a moment sub-block are contiguous ranges of
+// positions:
+//   s1_scores      a_i(pos) = s qbar_i . k_perm[pos] for every centroid and position,
+//                  [BH, Cq, N] fp32 (qbar split into bf16 hi + lo; keys are exact).
 //   s1_atoms_mfma  one wave per (block, key cluster) bucket: per-centroid max of a over
-//                  the bucket, then sum_m w_m k_m and sum_m w_m v_m as products
-//                  K_seg^T W^T with the weights split into bf16 hi + lo.
+//                  the bucket, then sum w k and sum w v as products K_seg^T W^T, with the
+//                  bucket's key/value rows gathered into a transposed LDS tile and the
+//                  weights split into bf16 hi + lo.
 //   s1_moments_f16 per (sub-block, centroid group): weights w = exp(a - max) from the
 //                  scores (no running rescale), then sum_m w_m v_m k_m^T with fp16
 //                  operands (the weights are applied to V^T with packed fp16 multiplies)
@@ -44,16 +48,18 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
   }
   __syncthreads();
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
   float* S = a.scores + static_cast<size_t>(bh) * Cq * a.N;
   for (int tt = 0; tt < 2; ++tt) {
-    const int kb = blockIdx.x * 256 + wave * 64 + tt * 32;
+    const int kb = blockIdx.x * 256 + wave * 64 + tt * 32;  // first position of the tile
     if (kb >= a.N) break;
-    const int key = kb + c;
+    const int pos = kb + c;
+    const int key = pos < a.N ? perm[pos] : 0;
     bf16x8_t ak[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       u16x8_t u = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (key < a.N) u = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(key) * D + 16 * ks + 8 * h);
+      if (pos < a.N) u = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(key) * D + 16 * ks + 8 * h);
       ak[ks] = as_bf16x8(u);
     }
     for (int nt = 0; nt < nt_n; ++nt) {
@@ -64,7 +70,7 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
         acc = mfma32(ak[ks], as_bf16x8(*reinterpret_cast<const u16x8_t*>(qhi + o)), acc);
         acc = mfma32(ak[ks], as_bf16x8(*reinterpret_cast<const u16x8_t*>(qlo + o)), acc);
       }
-      // lane (c, h): centroid 32 nt + c, keys kb + 8 g + 4 h + r
+      // lane (c, h): centroid 32 nt + c, positions kb + 8 g + 4 h + r
       const int i = 32 * nt + c;
       if (i >= Cq) continue;
 #pragma unroll
@@ -84,27 +90,38 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
   }
 }
 
-// One wave per (block b', key cluster j) bucket; 4 buckets per workgroup.
+// One wave per (block b', key cluster j) bucket; 4 buckets per workgroup. The bucket's
+// positions are visited kAtomPass at a time: their key and value rows are gathered through
+// the permutation (all loads of a pass in flight together) into a wave-private transposed
+// LDS tile [D][kAtomPass + 8].
+constexpr int kAtomPass = 32;  // bucket positions staged per pass
+
 template <int D>
 __global__ void __launch_bounds__(256) s1_atoms_mfma_kernel(S1Args a) {
   constexpr int NMT = D / 32;
+  constexpr int PST = kAtomPass + 8;
+  __shared__ __align__(16) uint16_t sKt[4][D * PST];
+  __shared__ __align__(16) uint16_t sVt[4][D * PST];
   const int bh = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
   const int Cq = a.Cq, Ck = a.Ck;
   const int u = blockIdx.x * 4 + wave;
-  if (u >= a.nb * Ck) return;
+  if (u >= a.nb * Ck) return;  // no workgroup barrier below: waves are independent
   const int bp = u / Ck, j = u % Ck;
   const int32_t* offs = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
   const int s0 = offs[u], n = offs[u + 1] - s0;
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + s0;
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+  uint16_t* kt = sKt[wave];
+  uint16_t* vt = sVt[wave];
   const size_t abase = (static_cast<size_t>(bh) * a.nb + bp) * Cq;
   for (int nt = 0; nt < (Cq + 31) / 32; ++nt) {
     const int i = 32 * nt + c;
     const bool iv = i < Cq;
-    const float* Si = a.scores + (static_cast<size_t>(bh) * Cq + (iv ? i : 0)) * a.N;
+    const float* Si = a.scores + (static_cast<size_t>(bh) * Cq + (iv ? i : 0)) * a.N + s0;
     float mx = kNegInf;
-    for (int k = h; k < n; k += 2) mx = fmaxf(mx, Si[perm[k]]);
+#pragma unroll 8
+    for (int k = h; k < n; k += 2) mx = fmaxf(mx, Si[k]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     f32x16_t ak[NMT], av[NMT];
 #pragma unroll
@@ -113,32 +130,64 @@ __global__ void __launch_bounds__(256) s1_atoms_mfma_kernel(S1Args a) {
       av[mt] = zero16();
     }
     float z = 0.f;
-    for (int k0 = 0; k0 < n; k0 += 16) {
-      int key[8];
-      float w[8];
+    for (int p0 = 0; p0 < n; p0 += kAtomPass) {
+      // gather up to kAtomPass rows (D/8 16-byte chunks each) and store them transposed
+      constexpr int NCH = kAtomPass * (D / 8) / 64;
+      u16x8_t kv[NCH], vv[NCH];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = k0 + 8 * h + e;
-        key[e] = kk < n ? perm[kk] : -1;
-        w[e] = (key[e] >= 0 && iv) ? __expf(Si[key[e]] - mx) : 0.f;
-        z += w[e];
+      for (int q = 0; q < NCH; ++q) {
+        const int x = lane + 64 * q;
+        const int r = x / (D / 8), c8 = x % (D / 8);
+        kv[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        vv[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        if (p0 + r < n) {
+          const size_t row = static_cast<size_t>(perm[p0 + r]) * D + c8 * 8;
+          kv[q] = *reinterpret_cast<const u16x8_t*>(K + row);
+          vv[q] = *reinterpret_cast<const u16x8_t*>(V + row);
+        }
       }
-      bf16x8_t whi, wlo;
-      split_bf16x8(w, whi, wlo);
+      float w[kAtomPass / 16][8];
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        const int d = 32 * mt + c;
-        u16x8_t kv, vv;
+      for (int ks = 0; ks < kAtomPass / 16; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          kv[e] = key[e] >= 0 ? K[static_cast<size_t>(key[e]) * D + d] : 0;
-          vv[e] = key[e] >= 0 ? V[static_cast<size_t>(key[e]) * D + d] : 0;
+          const int kk = p0 + 16 * ks + 8 * h + e;
+          w[ks][e] = (kk < n && iv) ? __expf(Si[kk] - mx) : 0.f;
         }
-        ak[mt] = mfma32(as_bf16x8(kv), whi, ak[mt]);
-        ak[mt] = mfma32(as_bf16x8(kv), wlo, ak[mt]);
-        av[mt] = mfma32(as_bf16x8(vv), whi, av[mt]);
-        av[mt] = mfma32(as_bf16x8(vv), wlo, av[mt]);
+#pragma unroll
+      for (int q = 0; q < NCH; ++q) {
+        const int x = lane + 64 * q;
+        const int r = x / (D / 8), c8 = x % (D / 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kt[(c8 * 8 + e) * PST + r] = kv[q][e];
+          vt[(c8 * 8 + e) * PST + r] = vv[q][e];
+        }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int ks = 0; ks < kAtomPass / 16; ++ks) {
+        if (p0 + 16 * ks >= n) break;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z += w[ks][e];
+        bf16x8_t whi, wlo;
+        split_bf16x8(w[ks], whi, wlo);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          const int o = (32 * mt + c) * PST + 16 * ks + 8 * h;
+          const bf16x8_t akf = as_bf16x8(*reinterpret_cast<const u16x8_t*>(kt + o));
+          const bf16x8_t avf = as_bf16x8(*reinterpret_cast<const u16x8_t*>(vt + o));
+          ak[mt] = mfma32(akf, whi, ak[mt]);
+          ak[mt] = mfma32(akf, wlo, ak[mt]);
+          av[mt] = mfma32(avf, whi, av[mt]);
+          av[mt] = mfma32(avf, wlo, av[mt]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     z += __shfl_xor(z, 32, 64);
     if (!iv) continue;
@@ -161,7 +210,8 @@ __global__ void __launch_bounds__(256) s1_atoms_mfma_kernel(S1Args a) {
   }
 }
 
-// Sub-block moments with fp16 operands. D = 64: 8 centroids per workgroup, 2 per wave;
+// Sub-block moments with fp16 operands, over consecutive positions of the bucketed order
+// (a causal block is a contiguous range of positions, so sub-blocks never straddle one). D = 64: 8 centroids per workgroup, 2 per wave;
 // D = 128: 2 centroids, each wave half of the 16 output tiles of one centroid.
 // Static LDS: K^T, V^T [D][64+8] fp16 | weights [G][kMaxMbk] fp16 | max, sum [G].
 constexpr int kMaxMbk = 1024;
@@ -178,6 +228,7 @@ __global__ void __launch_bounds__(256) s1_moments_f16_kernel(S1Args a) {
   __shared__ __align__(16) _Float16 sVt[D * TST];
   __shared__ __align__(16) _Float16 sw[G * kMaxMbk];
   __shared__ float smx[G], ssum[G];
+  __shared__ int s_perm[kMaxMbk];
   const int mb = blockIdx.x, ig = blockIdx.y, bh = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int Cq = a.Cq, i0 = ig * G, ng = min(G, Cq - i0);
@@ -187,9 +238,11 @@ __global__ void __launch_bounds__(256) s1_moments_f16_kernel(S1Args a) {
   for (int g = wave; g < G; g += 4) {
     const float* Sg = a.scores + (static_cast<size_t>(bh) * Cq + i0 + (g < ng ? g : 0)) * a.N + key0;
     float mx = kNegInf;
+#pragma unroll 8
     for (int k = lane; k < nkeys; k += 64) mx = fmaxf(mx, Sg[k]);
     mx = wave_max(mx);
     float sum = 0.f;
+#pragma unroll 8
     for (int k = lane; k < kMaxMbk; k += 64) {
       const float w = (k < nkeys && g < ng) ? __expf(Sg[k < nkeys ? k : 0] - mx) : 0.f;
       sw[g * kMaxMbk + k] = static_cast<_Float16>(w);
@@ -205,6 +258,8 @@ __global__ void __launch_bounds__(256) s1_moments_f16_kernel(S1Args a) {
   const int nt0 = D == 64 ? 0 : 2 * (wave & 1);
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + key0;
+  for (int k = tid; k < nkeys; k += 256) s_perm[k] = perm[k];
   f32x16_t acc[CPW][NMT][NNT];
 #pragma unroll
   for (int cc = 0; cc < CPW; ++cc)
@@ -213,23 +268,39 @@ __global__ void __launch_bounds__(256) s1_moments_f16_kernel(S1Args a) {
 #pragma unroll
       for (int nt = 0; nt < NNT; ++nt) acc[cc][mt][nt] = zero16();
 
-  for (int c0 = 0; c0 < nkeys; c0 += KC) {
-    const int nk = min(KC, nkeys - c0);
-    __syncthreads();
-    for (int x = tid; x < KC * (D / 8); x += 256) {
+  // rows of the next 64 positions travel in registers while the current ones are used
+  constexpr int NPRE = KC * (D / 8) / 256;
+  u16x8_t pk[NPRE], pv[NPRE];
+  auto load_rows = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < NPRE; ++q) {
+      const int x = tid + 256 * q;
       const int r = x / (D / 8), cc8 = x % (D / 8);
-      u16x8_t kv = {0, 0, 0, 0, 0, 0, 0, 0}, vv = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (r < nk) {
-        kv = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(key0 + c0 + r) * D + cc8 * 8);
-        vv = *reinterpret_cast<const u16x8_t*>(V + static_cast<size_t>(key0 + c0 + r) * D + cc8 * 8);
+      pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      pv[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      if (c0 + r < nkeys) {
+        const size_t row = static_cast<size_t>(s_perm[c0 + r]) * D + cc8 * 8;
+        pk[q] = *reinterpret_cast<const u16x8_t*>(K + row);
+        pv[q] = *reinterpret_cast<const u16x8_t*>(V + row);
       }
+    }
+  };
+  __syncthreads();  // s_perm, sw complete
+  if (nkeys > 0) load_rows(0);
+  for (int c0 = 0; c0 < nkeys; c0 += KC) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NPRE; ++q) {
+      const int x = tid + 256 * q;
+      const int r = x / (D / 8), cc8 = x % (D / 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        sKt[(cc8 * 8 + e) * TST + r] = static_cast<_Float16>(bf16_to_f32(kv[e]));
-        sVt[(cc8 * 8 + e) * TST + r] = static_cast<_Float16>(bf16_to_f32(vv[e]));
+        sKt[(cc8 * 8 + e) * TST + r] = static_cast<_Float16>(bf16_to_f32(pk[q][e]));
+        sVt[(cc8 * 8 + e) * TST + r] = static_cast<_Float16>(bf16_to_f32(pv[q][e]));
       }
     }
     __syncthreads();
+    if (c0 + KC < nkeys) load_rows(c0 + KC);
     if (wc0 < ng) {
 #pragma unroll
       for (int ks = 0; ks < KC / 16; ++ks) {

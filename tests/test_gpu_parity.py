@@ -45,6 +45,12 @@ def test_causal_bf16_small_blocks(muse_lib):
     check_config(cfg, [(0, 0), (0, 1)])
 
 
+def test_causal_bf16_block64(muse_lib):
+    # one-wave K-means tiles and 64-token diagonal blocks
+    cfg = scaled_config("c3", B=1, H=1, N=512, block=64, Cq=8, Ck=16)
+    check_config(cfg, [(0, 0)])
+
+
 def test_causal_c3_shape_reduced(muse_lib):
     cfg = scaled_config("c3", B=1, H=2, N=4096)
     check_config(cfg, [(0, 0), (0, 1)])
