@@ -51,6 +51,7 @@ class FwdParams(ctypes.Structure):
         ("lse_out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("retrieval_trace", ctypes.c_void_p),
     ]
 
 
@@ -141,7 +142,8 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
              workspace: Optional[torch.Tensor] = None):
     """muse_attn_fwd_ex. Returns out, or (out, extras) when any return_* flag is set, where
     extras holds 'labels_q_trace', 'labels_k_trace' [iters,B,H,N] int32, 'centroids_q',
-    'centroids_k' [B,H,C,D] float32 and 'lse' [B,H,N] float32 as requested."""
+    'centroids_k' [B,H,C,D] float32, 'lse' [B,H,N] float32 and, with retrieval,
+    'retrieval_trace' [B,H,N/block,Cq,k1,1+k2] int32 as requested."""
     lib = load()
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
@@ -169,6 +171,11 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
             t = torch.full((kmeans_iters, B, H, N), -1, dtype=torch.int32, device=dev)
             extras[name] = t
             setattr(p, name, t.data_ptr())
+        if topk_clusters > 0 and causal:
+            t = torch.full((B, H, N // block, Cq, topk_clusters, 1 + topk_blocks), -1, dtype=torch.int32,
+                           device=dev)
+            extras["retrieval_trace"] = t
+            p.retrieval_trace = t.data_ptr()
     if return_centroids:
         extras["centroids_q"] = torch.empty((B, H, Cq, D), dtype=torch.float32, device=dev)
         extras["centroids_k"] = torch.empty((B, H, Ck, D), dtype=torch.float32, device=dev)

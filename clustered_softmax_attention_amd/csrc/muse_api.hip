@@ -100,7 +100,10 @@ int validate(Shape& s, const muse_fwd_params* p) {
     if (p->topk_clusters < 0 || p->topk_blocks < 0) return fail(MUSE_ERR_INVALID_ARG, "retrieval top-k must be >= 0");
     if (p->topk_clusters > 0 && !s.causal) return fail(MUSE_ERR_INVALID_ARG, "retrieval requires causal=1");
     if (p->topk_clusters > 0 && p->topk_blocks < 1) return fail(MUSE_ERR_INVALID_ARG, "retrieval needs topk_blocks >= 1");
-    if (p->topk_clusters > 0) return fail(MUSE_ERR_UNSUPPORTED, "retrieval is not implemented in this build");
+    if (p->topk_clusters > 0 && p->topk_clusters * (1 + p->topk_blocks) > muse::kMaxRetrRow)
+      return fail(MUSE_ERR_UNSUPPORTED, "topk_clusters * (1 + topk_blocks) must be at most %d", muse::kMaxRetrRow);
+    if (p->topk_clusters > 0 && s.nb > muse::kMaxRetrBlocks)
+      return fail(MUSE_ERR_UNSUPPORTED, "retrieval supports at most %d blocks", muse::kMaxRetrBlocks);
   }
   return MUSE_OK;
 }
@@ -124,11 +127,11 @@ struct Plan {
   int max_tiles;
   size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores;
   size_t s_logz, s_k, s_v, s_dipT;
-  size_t o_far, l_far;
+  size_t o_far, l_far, retr_sel;
   size_t total;
 };
 
-Plan make_plan(const Shape& s) {
+Plan make_plan(const Shape& s, const muse_fwd_params* p) {
   Layout L;
   Plan P{};
   const size_t BH = s.BH, N = s.N, D = s.D, Cq = s.Cq, Ck = s.Ck, nb = s.nb, nbS = s.nbS;
@@ -173,6 +176,8 @@ Plan make_plan(const Shape& s) {
     P.o_far = L.take(BH * N * D * f);
     P.l_far = L.take(BH * N * f);
   }
+  if (p != nullptr && p->topk_clusters > 0)
+    P.retr_sel = L.take(BH * nb * Cq * static_cast<size_t>(p->topk_clusters) * (1 + p->topk_blocks) * i4);
   if (s.dtype == MUSE_BF16) {
     const size_t h2 = sizeof(uint16_t);
     P.t_khi = L.take(BH * nbS * Cq * Ck * D * h2);
@@ -206,7 +211,7 @@ int out_is_bf16(const Shape& s, const muse_fwd_params* p) {
 int run_muse(const void* q, const void* k, const void* v, void* out, const Shape& s,
              const muse_fwd_params* p, hipStream_t stream, void* ws) {
   using namespace muse;
-  const Plan P = make_plan(s);
+  const Plan P = make_plan(s, p);
   const float scale = scale_of(s, p);
   const int dipole = p ? p->dipole : MUSE_DIPOLE_TILTED;
 
@@ -233,9 +238,11 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   tq.tile_cnt = at<int32_t>(ws, P.tcnt_q);
   tq.tile_start = at<int32_t>(ws, P.tst_q);
   tq.psum = at<float>(ws, P.psum_q);
-  const bool mf = s.dtype == MUSE_BF16;  // matrix-core stage 2 needs the query buckets
-  tq.perm = mf ? at<int32_t>(ws, P.perm_q) : nullptr;
-  tq.offs = mf ? at<int32_t>(ws, P.offs_q) : nullptr;
+  const bool mf = s.dtype == MUSE_BF16;
+  const bool retr = p != nullptr && p->topk_clusters > 0;
+  // the matrix-core stage 2 and retrieval need the query buckets
+  tq.perm = (mf || retr) ? at<int32_t>(ws, P.perm_q) : nullptr;
+  tq.offs = (mf || retr) ? at<int32_t>(ws, P.offs_q) : nullptr;
   KmTensor& tk = km.t[1];
   tk.x = k;
   tk.C = s.Ck;
@@ -292,6 +299,40 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
     a1.t_vtlo = at<uint16_t>(ws, P.t_vtlo);
     a1.t_dip = at<uint16_t>(ws, P.t_dip);
   }
+  RetrArgs ra{};
+  if (retr) {
+    ra.q = q;
+    ra.k = k;
+    ra.v = v;
+    ra.BH = s.BH;
+    ra.N = s.N;
+    ra.D = s.D;
+    ra.Cq = s.Cq;
+    ra.Ck = s.Ck;
+    ra.nb = s.nb;
+    ra.k1 = p->topk_clusters;
+    ra.k2 = p->topk_blocks;
+    ra.dipole = dipole;
+    ra.scale = scale;
+    ra.qbar = tq.cent;
+    ra.perm_k = tk.perm;
+    ra.offs_k = tk.offs;
+    ra.perm_q = tq.perm;
+    ra.offs_q = tq.offs;
+    ra.at_m = a1.at_m;
+    ra.at_z = a1.at_z;
+    ra.at_k = a1.at_k;
+    ra.at_v = a1.at_v;
+    ra.s_logz = a1.s_logz;
+    ra.s_k = a1.s_k;
+    ra.s_v = a1.s_v;
+    ra.s_dipT = a1.s_dipT;
+    ra.sel = at<int32_t>(ws, P.retr_sel);
+    ra.trace = p->retrieval_trace;
+    ra.o_far = at<float>(ws, P.o_far);
+    ra.l_far = at<float>(ws, P.l_far);
+    a1.retr = &ra;
+  }
   e = launch_stage1(a1, s.dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
 
@@ -336,6 +377,10 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   }
   e = launch_stage2(a2, s.dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "stage-2 launch");
+  if (retr) {
+    e = launch_retrieval(ra, 1, s.dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "retrieval launch");
+  }
 
   if (s.causal) {
     ExactArgs ax{};
@@ -494,7 +539,7 @@ size_t muse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int Cq, int Ck,
                                      int dtype, const muse_fwd_params* p) {
   Shape s{B, H, N, D, Cq, Ck, 1, causal, block, dtype};
   if (validate_muse(s, p) != MUSE_OK) return 0;
-  return make_plan(s).total;
+  return make_plan(s, p).total;
 }
 
 int muse_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int D,
@@ -508,7 +553,7 @@ int muse_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int
   if (r != MUSE_OK) return r;
   if (out == q || out == k || out == v) return fail(MUSE_ERR_INVALID_ARG, "out must not alias an input");
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  const size_t need = make_plan(s).total;
+  const size_t need = make_plan(s, p).total;
   void* ws = p ? p->workspace : nullptr;
   bool owned = false;
   if (ws != nullptr) {

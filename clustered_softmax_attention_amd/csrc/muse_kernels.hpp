@@ -40,6 +40,39 @@ struct KmArgs {
 
 hipError_t launch_kmeans(const KmArgs& a, int iters, int dtype, hipStream_t s);
 
+// ------------------------------------------------------------------ retrieval
+
+constexpr int kMaxRetrBlocks = 4096;  // spatial blocks per head with retrieval on
+constexpr int kMaxRetrRow = 256;      // k1 * (1 + k2)
+
+struct RetrArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int BH, N, D, Cq, Ck, nb;
+  int k1, k2, dipole;
+  float scale;
+  const float* qbar;           // [BH, Cq, D]
+  const int32_t* perm_k;       // [BH, N]
+  const int32_t* offs_k;       // [BH, nb*Ck + 1]
+  const int32_t* perm_q;       // [BH, N]
+  const int32_t* offs_q;       // [BH, nb*Cq + 1]
+  const float* at_m;           // atoms [BH, nb, Cq, Ck(, D)]
+  const float* at_z;
+  const float* at_k;
+  const float* at_v;
+  float* s_logz;               // tables [BH, nb, Cq, ...], entry (b, i) rewritten in place
+  float* s_k;
+  float* s_v;
+  float* s_dipT;               // entry (b, i) holds E[v k^T] before the dipole finalise
+  int32_t* sel;                // [BH, nb, Cq, k1*(1+k2)] selection
+  int32_t* trace;              // copy of sel for the caller, or null
+  float* o_far;                // [BH, N, D] far-field partial result (merged in place)
+  float* l_far;                // [BH, N]
+};
+
+hipError_t launch_retrieval(const RetrArgs& a, int phase, int dtype, hipStream_t s);  // 0 tables, 1 exact
+
 // ------------------------------------------------------------------ stage 1
 
 struct S1Args {
@@ -74,6 +107,7 @@ struct S1Args {
   uint16_t* t_vthi;            // [BH, nbS, Cq, D, Ck]  V_ij transposed, = hi + lo
   uint16_t* t_vtlo;
   uint16_t* t_dip;             // [BH, nbS, Cq, D(v), D(k)]  s * D_i, value index first
+  const RetrArgs* retr;        // retrieval: rewrites table entries before the dipole finalise
 };
 
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);

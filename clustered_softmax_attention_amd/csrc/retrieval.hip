@@ -1,0 +1,351 @@
+// Retrieval for causal MuSe (gist.science summary of arXiv 2509.10406, Kernmechanismen 4):
+// for each query cluster i and block b >= 1,
+//   1. the k1 key clusters j with the largest tilted-summary score log Z^{<b}_ij (the log
+//      mass of cluster j's earlier keys seen from qbar_i),
+//   2. inside each, the k2 earlier blocks b' with the largest atom log mass
+//      m_ij(b') + log z_ij(b'),
+// and the keys of the chosen (cluster, block) atoms are attended exactly; the summaries
+// cover the remaining earlier keys only. Descending order with ties to the lower index;
+// empty candidates are never chosen.
+//
+//   retr_select  one wave per (i, b): the selection, stored as k1 rows of
+//                (j, b'_1 .. b'_k2), -1 padded.
+//   retr_tables  one workgroup per (i, b): table entry (b, i) becomes the far field
+//                without the retrieved atoms: chosen clusters are re-merged from their
+//                unselected atoms (no subtraction of log-sum-exps), and the second
+//                moment becomes (M - sum_R w v k^T) / (1 - sum_R w) with w relative to the
+//                prefix mass.
+//   retr_exact   one workgroup per (i, b): exact softmax over the retrieved keys for the
+//                bucket's queries, merged by log-sum-exp into the far-field partial result.
+#include "muse_kernels.hpp"
+
+namespace muse {
+
+// wave-wide argmax with ties to the lower index; every lane gets the winner
+__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, 64);
+    const int oi = __shfl_xor(idx, o, 64);
+    if (ov > v || (ov == v && oi < idx)) {
+      v = ov;
+      idx = oi;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(64) retr_select_kernel(RetrArgs a) {
+  __shared__ float s_sj[kMaxClusters];
+  __shared__ unsigned char s_used[kMaxClusters];
+  __shared__ unsigned char s_bused[kMaxRetrBlocks];
+  const int i = blockIdx.x, b = blockIdx.y, bh = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int Ck = a.Ck, k1 = a.k1, k2 = a.k2, row = k1 * (1 + k2);
+  int32_t* out = a.sel + ((static_cast<size_t>(bh) * a.nb + b) * a.Cq + i) * row;
+  if (b == 0) {
+    for (int x = lane; x < row; x += 64) out[x] = -1;
+    return;
+  }
+  const size_t sidx = (static_cast<size_t>(bh) * a.nb + b) * a.Cq + i;
+  for (int j = lane; j < Ck; j += 64) {
+    s_sj[j] = a.s_logz[sidx * Ck + j];
+    s_used[j] = 0;
+  }
+  __syncthreads();
+  for (int t = 0; t < k1; ++t) {
+    float v = kNegInf;
+    int idx = 1 << 30;
+    for (int j = lane; j < Ck; j += 64)
+      if (!s_used[j] && s_sj[j] != kNegInf && (s_sj[j] > v || (s_sj[j] == v && j < idx))) {
+        v = s_sj[j];
+        idx = j;
+      }
+    wave_argmax(v, idx);
+    int32_t* o = out + t * (1 + k2);
+    if (v == kNegInf) {
+      for (int x = lane; x < 1 + k2; x += 64) o[x] = -1;
+      continue;
+    }
+    const int j = idx;
+    if (lane == 0) {
+      s_used[j] = 1;
+      o[0] = j;
+    }
+    for (int bb = lane; bb < b; bb += 64) s_bused[bb] = 0;
+    __syncthreads();
+    for (int u = 0; u < k2; ++u) {
+      float bv = kNegInf;
+      int bi = 1 << 30;
+      for (int bb = lane; bb < b; bb += 64) {
+        const size_t aidx = ((static_cast<size_t>(bh) * a.nb + bb) * a.Cq + i) * Ck + j;
+        const float z = a.at_z[aidx];
+        if (s_bused[bb] || !(z > 0.f)) continue;
+        const float sv = a.at_m[aidx] + __logf(z);
+        if (sv > bv || (sv == bv && bb < bi)) {
+          bv = sv;
+          bi = bb;
+        }
+      }
+      wave_argmax(bv, bi);
+      if (lane == 0) o[1 + u] = bv == kNegInf ? -1 : bi;
+      if (bv != kNegInf && lane == 0) s_bused[bi] = 1;
+      __syncthreads();
+    }
+  }
+  if (a.trace != nullptr)
+    for (int x = lane; x < row; x += 64) a.trace[((static_cast<size_t>(bh) * a.nb + b) * a.Cq + i) * row + x] = out[x];
+}
+
+__device__ __forceinline__ bool atom_selected(const int32_t* selrow, int k2, int bb) {
+  for (int u = 0; u < k2; ++u)
+    if (selrow[1 + u] == bb) return true;
+  return false;
+}
+
+// keys staged per step (LDS stays under 64 KiB)
+template <int D>
+struct RetrChunk {
+  static constexpr int value = D == 64 ? 64 : 32;
+};
+
+// 256 threads; LDS: key/value chunk [KCH][D] fp32, weights, reductions.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
+  constexpr int TD = D / 16;
+  constexpr int KCH = RetrChunk<D>::value;
+  __shared__ float s_k[KCH * D];
+  __shared__ float s_v[KCH * D];
+  __shared__ float s_w[64];
+  __shared__ float s_q[D];
+  __shared__ float s_red[2];
+  __shared__ int s_sel[kMaxRetrRow];
+  const int i = blockIdx.x, b = blockIdx.y, bh = blockIdx.z;
+  const int tid = threadIdx.x;
+  if (b == 0) return;
+  const int Ck = a.Ck, k1 = a.k1, k2 = a.k2, row = k1 * (1 + k2);
+  const int32_t* sel = a.sel + ((static_cast<size_t>(bh) * a.nb + b) * a.Cq + i) * row;
+  for (int x = tid; x < row; x += 256) s_sel[x] = sel[x];
+  for (int d = tid; d < D; d += 256) s_q[d] = a.qbar[(static_cast<size_t>(bh) * a.Cq + i) * D + d];
+  const size_t sidx = (static_cast<size_t>(bh) * a.nb + b) * a.Cq + i;
+  // prefix log mass (before any entry is rewritten)
+  if (tid < 64) {
+    float mx = kNegInf;
+    for (int j = tid; j < Ck; j += 64) mx = fmaxf(mx, a.s_logz[sidx * Ck + j]);
+    mx = wave_max(mx);
+    float sm = 0.f;
+    for (int j = tid; j < Ck; j += 64) {
+      const float l = a.s_logz[sidx * Ck + j];
+      if (l != kNegInf) sm += __expf(l - mx);
+    }
+    sm = wave_sum(sm);
+    if (tid == 0) s_red[0] = mx == kNegInf ? kNegInf : mx + __logf(sm);
+  }
+  __syncthreads();
+  const float Rpre = s_red[0];
+
+  // 1. remainder summaries of the chosen clusters (re-merged from unselected atoms)
+  for (int t = 0; t < k1; ++t) {
+    const int* sr = s_sel + t * (1 + k2);
+    const int j = sr[0];
+    if (j < 0) continue;
+    for (int x = tid; x < 2 * D; x += 256) {
+      const bool isK = x < D;
+      const int d = isK ? x : x - D;
+      float rm = kNegInf, rz = 0.f, racc = 0.f;
+      for (int bb = 0; bb < b; ++bb) {
+        if (atom_selected(sr, k2, bb)) continue;
+        const size_t aidx = ((static_cast<size_t>(bh) * a.nb + bb) * a.Cq + i) * Ck + j;
+        const float m = a.at_m[aidx], z = a.at_z[aidx];
+        if (!(z > 0.f)) continue;
+        const float xv = (isK ? a.at_k : a.at_v)[aidx * D + d];
+        const float nm = fmaxf(rm, m);
+        const float f0 = rz > 0.f ? __expf(rm - nm) : 0.f;
+        const float f1 = __expf(m - nm);
+        rz = rz * f0 + z * f1;
+        racc = racc * f0 + xv * f1;
+        rm = nm;
+      }
+      const bool any = rz > 0.f;
+      if (x == 0) a.s_logz[sidx * Ck + j] = any ? rm + __logf(rz) : kNegInf;
+      (isK ? a.s_k : a.s_v)[(sidx * Ck + j) * D + d] = any ? racc / rz : 0.f;
+    }
+  }
+  if (!a.dipole || Rpre == kNegInf) return;
+
+  // 2. second moment without the retrieved keys
+  const int tr = tid / 16, tc = tid % 16;
+  float acc[TD][TD];
+#pragma unroll
+  for (int x = 0; x < TD; ++x)
+#pragma unroll
+    for (int y = 0; y < TD; ++y) acc[x][y] = 0.f;
+  float wsum = 0.f;  // meaningful in thread 0
+  const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
+  const int32_t* offs = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
+  for (int t = 0; t < k1; ++t) {
+    const int j = s_sel[t * (1 + k2)];
+    if (j < 0) continue;
+    for (int u = 0; u < k2; ++u) {
+      const int bb = s_sel[t * (1 + k2) + 1 + u];
+      if (bb < 0) continue;
+      const int p0 = offs[bb * Ck + j], p1 = offs[bb * Ck + j + 1];
+      for (int c0 = p0; c0 < p1; c0 += KCH) {
+        const int nk = min(KCH, p1 - c0);
+        __syncthreads();
+        for (int x = tid; x < nk * D; x += 256) {
+          const int r = x / D, d = x % D;
+          const size_t rowi = static_cast<size_t>(perm[c0 + r]) * D + d;
+          s_k[x] = Elem<T>::load(K, rowi);
+          s_v[x] = Elem<T>::load(V, rowi);
+        }
+        __syncthreads();
+        if (tid < 64) {
+          float w = 0.f;
+          if (tid < nk) {
+            float dot = 0.f;
+            for (int d = 0; d < D; ++d) dot = fmaf(s_q[d], s_k[tid * D + d], dot);
+            w = __expf(a.scale * dot - Rpre);
+          }
+          s_w[tid] = w;
+          const float ws = wave_sum(w);
+          if (tid == 0) wsum += ws;
+        }
+        __syncthreads();
+        for (int m = 0; m < nk; ++m) {
+          const float wm = s_w[m];
+#pragma unroll
+          for (int x = 0; x < TD; ++x)
+#pragma unroll
+            for (int y = 0; y < TD; ++y) acc[x][y] = fmaf(wm * s_v[m * D + tr * TD + x], s_k[m * D + tc * TD + y], acc[x][y]);
+        }
+      }
+    }
+  }
+  if (tid == 0) s_red[1] = wsum;
+  __syncthreads();
+  const float rest = 1.f - s_red[1];
+  const float inv = rest > 1e-30f ? 1.f / rest : 0.f;
+  float* dipT = a.s_dipT + sidx * D * D;  // [dk][dv], holds the prefix E[v k^T]
+#pragma unroll
+  for (int x = 0; x < TD; ++x)
+#pragma unroll
+    for (int y = 0; y < TD; ++y) {
+      const size_t o = static_cast<size_t>(tc * TD + y) * D + (tr * TD + x);
+      dipT[o] = (dipT[o] - acc[x][y]) * inv;
+    }
+}
+
+// Exact softmax over the retrieved keys for the queries of bucket (b, i), merged into
+// the far-field partial result (o_far, l_far). One thread per query, keys staged in LDS.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) retr_exact_kernel(RetrArgs a) {
+  constexpr int KCH = RetrChunk<D>::value;
+  __shared__ float s_k[KCH * D];
+  __shared__ float s_v[KCH * D];
+  __shared__ int s_sel[kMaxRetrRow];
+  const int i = blockIdx.x, b = blockIdx.y, bh = blockIdx.z;
+  const int tid = threadIdx.x;
+  if (b == 0) return;
+  const int Ck = a.Ck, k1 = a.k1, k2 = a.k2, row = k1 * (1 + k2);
+  const int32_t* sel = a.sel + ((static_cast<size_t>(bh) * a.nb + b) * a.Cq + i) * row;
+  for (int x = tid; x < row; x += 256) s_sel[x] = sel[x];
+  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (a.nb * a.Cq + 1);
+  const int q0 = offq[b * a.Cq + i], q1 = offq[b * a.Cq + i + 1];
+  const T* Q = static_cast<const T*>(a.q) + static_cast<size_t>(bh) * a.N * D;
+  const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+  const int32_t* permq = a.perm_q + static_cast<size_t>(bh) * a.N;
+  const int32_t* permk = a.perm_k + static_cast<size_t>(bh) * a.N;
+  const int32_t* offk = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
+  __syncthreads();
+  for (int qb = q0; qb < q1; qb += 256) {
+    const int qp = qb + tid;
+    const bool valid = qp < q1;
+    const int qn = valid ? permq[qp] : 0;
+    float q[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) q[d] = a.scale * Elem<T>::load(Q, static_cast<size_t>(qn) * D + d);
+    float m = kNegInf, l = 0.f;
+    float acc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = 0.f;
+    for (int t = 0; t < k1; ++t) {
+      const int j = s_sel[t * (1 + k2)];
+      if (j < 0) continue;
+      for (int u = 0; u < k2; ++u) {
+        const int bb = s_sel[t * (1 + k2) + 1 + u];
+        if (bb < 0) continue;
+        const int p0 = offk[bb * Ck + j], p1 = offk[bb * Ck + j + 1];
+        for (int c0 = p0; c0 < p1; c0 += KCH) {
+          const int nk = min(KCH, p1 - c0);
+          __syncthreads();
+          for (int x = tid; x < nk * D; x += 256) {
+            const int r = x / D, d = x % D;
+            const size_t rowi = static_cast<size_t>(permk[c0 + r]) * D + d;
+            s_k[x] = Elem<T>::load(K, rowi);
+            s_v[x] = Elem<T>::load(V, rowi);
+          }
+          __syncthreads();
+          for (int r = 0; r < nk; ++r) {
+            float dot = 0.f;
+#pragma unroll
+            for (int d = 0; d < D; ++d) dot = fmaf(q[d], s_k[r * D + d], dot);
+            if (dot > m) {
+              const float f = m == kNegInf ? 0.f : __expf(m - dot);
+              l *= f;
+#pragma unroll
+              for (int d = 0; d < D; ++d) acc[d] *= f;
+              m = dot;
+            }
+            const float p = __expf(dot - m);
+            l += p;
+#pragma unroll
+            for (int d = 0; d < D; ++d) acc[d] = fmaf(p, s_v[r * D + d], acc[d]);
+          }
+        }
+      }
+    }
+    if (!valid || l == 0.f) continue;
+    const size_t rowq = static_cast<size_t>(bh) * a.N + qn;
+    const float LR = m + __logf(l);
+    const float lf = a.l_far[rowq];
+    const float Lt = lf == kNegInf ? LR : fmaxf(LR, lf) + __logf(1.f + __expf(-fabsf(LR - lf)));
+    const float w0 = __expf(LR - Lt) / l;
+    const float w1 = lf == kNegInf ? 0.f : __expf(lf - Lt);
+#pragma unroll
+    for (int d = 0; d < D; ++d) a.o_far[rowq * D + d] = w0 * acc[d] + w1 * a.o_far[rowq * D + d];
+    a.l_far[rowq] = Lt;
+  }
+}
+
+hipError_t launch_retrieval(const RetrArgs& a, int phase, int dtype, hipStream_t s) {
+  const dim3 g(a.Cq, a.nb, a.BH);
+  if (phase == 0) {
+    {
+      ProfScope ps_("retr_select", s);
+      hipLaunchKernelGGL(retr_select_kernel, g, dim3(64), 0, s, a);
+    }
+    ProfScope ps_("retr_tables", s);
+    if (dtype == 0) {
+      if (a.D == 64) hipLaunchKernelGGL((retr_tables_kernel<float, 64>), g, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((retr_tables_kernel<float, 128>), g, dim3(256), 0, s, a);
+    } else {
+      if (a.D == 64) hipLaunchKernelGGL((retr_tables_kernel<bf16, 64>), g, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((retr_tables_kernel<bf16, 128>), g, dim3(256), 0, s, a);
+    }
+  } else {
+    ProfScope ps_("retr_exact", s);
+    if (dtype == 0) {
+      if (a.D == 64) hipLaunchKernelGGL((retr_exact_kernel<float, 64>), g, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((retr_exact_kernel<float, 128>), g, dim3(256), 0, s, a);
+    } else {
+      if (a.D == 64) hipLaunchKernelGGL((retr_exact_kernel<bf16, 64>), g, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((retr_exact_kernel<bf16, 128>), g, dim3(256), 0, s, a);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace muse

@@ -408,6 +408,9 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
       ProfScope ps_("s1_mom_prefix", s);
       hipLaunchKernelGGL(s1_mom_prefix_kernel, dim3((D * D + 255) / 256, a.Cq, a.BH), dim3(256), 0, s, a);
     }
+  }
+  if (a.retr != nullptr) launch_retrieval(*a.retr, 0, sizeof(T) == 2 ? 1 : 0, s);
+  if (a.dipole) {
     const size_t lds_fin = sizeof(float) * (kMaxClusters + 64 * D + 4);
     allow_lds((const void*)s1_dip_final_kernel<D>, lds_fin);
     {

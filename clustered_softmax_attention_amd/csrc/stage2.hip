@@ -77,10 +77,11 @@ __global__ void __launch_bounds__(kS2Threads) s2_refine_kernel(S2Args a) {
 #pragma unroll
     for (int d = 0; d < D; ++d) acc[d] = fmaf(p, Vt[j * D + d], acc[d]);
   }
-  const float inv = 1.f / z;
+  const bool empty = !(z > 0.f);  // no far-field key at all
+  const float inv = empty ? 0.f : 1.f / z;
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] *= inv;
-  if (a.dipole) {
+  if (a.dipole && !empty) {
     const float* dipT = a.s_dipT + sidx * D * D;  // [dk][dv]
     for (int dk = 0; dk < D; ++dk) {
       const float x = a.scale * s_q[dk][tid];
@@ -88,7 +89,7 @@ __global__ void __launch_bounds__(kS2Threads) s2_refine_kernel(S2Args a) {
       for (int dv = 0; dv < D; ++dv) acc[dv] = fmaf(dipT[dk * D + dv], x, acc[dv]);
     }
   }
-  const float L = mx + __logf(z);
+  const float L = empty ? kNegInf : mx + __logf(z);
   if (!valid) return;
   if (a.causal) {
     a.l_far[row] = L;
@@ -225,7 +226,7 @@ __global__ void __launch_bounds__(256) s2_mfma_kernel(S2Args a) {
     }
   }
   z += __shfl_xor(z, 32, 64);
-  const float invz = 1.f / z;
+  const float invz = z > 0.f ? 1.f / z : 0.f;  // z == 0: no far-field key at all
 
   // O^T = V^T P^T (split), then / z, then + (s D_i) qt^T
   const uint16_t* vthi = a.t_vthi + sidx * Ck * D;
@@ -302,7 +303,7 @@ __global__ void __launch_bounds__(256) s2_mfma_kernel(S2Args a) {
   }
   // lanes (c, h) hold rows d = 32 mt + 8 g + 4 h + r of query c
   if (!valid) return;
-  const float L = (mx + __log2f(z)) * 0.6931471805599453f;
+  const float L = z > 0.f ? (mx + __log2f(z)) * 0.6931471805599453f : kNegInf;
   if (a.causal) {
     if (h == 0) a.l_far[row] = L;
 #pragma unroll

@@ -92,8 +92,12 @@ typedef struct muse_fwd_params {
   float scale;          /* softmax scale; <= 0 means 1/sqrt(D)                        */
   int out_dtype;        /* -1: same as input; else MUSE_F32 or MUSE_BF16              */
   int dipole;           /* MUSE_DIPOLE_TILTED (default) or MUSE_DIPOLE_NONE           */
-  int topk_clusters;    /* retrieval k1 (causal only); 0 = off                        */
-  int topk_blocks;      /* retrieval k2 (>= 1 when k1 > 0)                            */
+  int topk_clusters;    /* retrieval k1 (causal only); 0 = off. Per (block b >= 1,
+                           query cluster i): the k1 key clusters of largest log Z^{<b}_ij,
+                           then inside each the k2 earlier blocks of largest atom log
+                           mass; their keys are attended exactly, the summaries cover the
+                           rest (gist.science, Kernmechanismen 4)                       */
+  int topk_blocks;      /* retrieval k2 (>= 1 when k1 > 0); k1*(1+k2) <= 256          */
   const int32_t* labels_q_in;  /* device [B,H,N]: fixed query clusters, skips Q K-means */
   const int32_t* labels_k_in;  /* device [B,H,N]: fixed key clusters, skips K K-means   */
   int32_t* labels_q_trace;     /* device [iters,B,H,N]: labels of every assign step      */
@@ -103,6 +107,9 @@ typedef struct muse_fwd_params {
   float* lse_out;              /* device [B,H,N]: log of each row's softmax normaliser   */
   void* workspace;             /* device scratch; NULL = stream-ordered allocation       */
   size_t workspace_bytes;      /* size of `workspace`                                     */
+  int32_t* retrieval_trace;    /* device [B,H,N/block,Cq,k1*(1+k2)]: per (block, query
+                                  cluster) the k1 chosen key clusters, each followed by
+                                  its k2 chosen earlier blocks; -1 = none (block 0: all -1) */
 } muse_fwd_params;
 
 /* Defaults: scale 0, out_dtype -1, dipole tilted, retrieval off, all pointers NULL. */

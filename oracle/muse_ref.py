@@ -314,6 +314,8 @@ class MuseResult:
     labels_q: np.ndarray
     labels_k: np.ndarray
     qbar: np.ndarray
+    retrieval_near_ties: int = 0
+    retrieval_mismatches: int = 0
 
 
 def _cluster(x, C, iters, labels_in, follow, tie_rel):
@@ -348,18 +350,8 @@ def muse_acausal(q, k, v, Cq: int, Ck: int, iters: int, scale: Optional[float] =
     return MuseResult(o, L, km_q, km_k, lq, lk, qbar)
 
 
-def retrieval_selection(a_prefix: np.ndarray, labels_prefix: np.ndarray,
-                        blocks_prefix: np.ndarray, Ck: int, nblocks: int,
-                        k1: int, k2: int) -> np.ndarray:
-    """Retrieved keys for one (query cluster, block) [R9]; [GIST] Kernmechanismen 4.
-
-    a_prefix: s qbar_i . k_m for the prefix keys; labels/blocks: their key cluster and
-    spatial block. Atom log-mass sigma(j,b') = logsumexp of a over keys of cluster j in
-    block b'; cluster score sigma(j) = logsumexp_b' sigma(j,b').
-      1. J = the k1 clusters of largest sigma(j)   (cluster selection),
-      2. for j in J, the k2 blocks of largest sigma(j,b')  (spatial block selection).
-    Descending order, ties to the lower index, empty (-inf) candidates never chosen,
-    fewer candidates than k -> all of them. Returns a boolean mask over prefix keys."""
+def _atom_log_masses(a_prefix, labels_prefix, blocks_prefix, Ck, nblocks):
+    """sigma(j,b') = logsumexp of a over keys of cluster j in block b' (-inf if none)."""
     sig = np.full((Ck, nblocks), NEG_INF)
     for j in range(Ck):
         for bb in range(nblocks):
@@ -368,28 +360,82 @@ def retrieval_selection(a_prefix: np.ndarray, labels_prefix: np.ndarray,
                 am = a_prefix[m]
                 mx = am.max()
                 sig[j, bb] = mx + np.log(np.exp(am - mx).sum())
+    return sig
+
+
+def _lse_rows(x):
     with np.errstate(invalid="ignore", divide="ignore"):
-        mxj = sig.max(axis=1, keepdims=True)
-        mxj_safe = np.where(np.isfinite(mxj), mxj, 0.0)
-        sj = np.where(np.isfinite(mxj[:, 0]),
-                      mxj_safe[:, 0] + np.log(np.where(np.isfinite(sig), np.exp(sig - mxj_safe), 0.0).sum(axis=1)),
-                      NEG_INF)
-    order = np.argsort(-sj, kind="stable")
-    J = [j for j in order[:k1] if np.isfinite(sj[j])]
-    take = np.zeros(a_prefix.shape[0], bool)
-    for j in J:
-        ob = np.argsort(-sig[j], kind="stable")
-        for bb in ob[:k2]:
-            if np.isfinite(sig[j, bb]):
+        mx = x.max(axis=1, keepdims=True)
+        mx_safe = np.where(np.isfinite(mx), mx, 0.0)
+        return np.where(np.isfinite(mx[:, 0]),
+                        mx_safe[:, 0] + np.log(np.where(np.isfinite(x), np.exp(x - mx_safe), 0.0).sum(axis=1)),
+                        NEG_INF)
+
+
+def _top(values: np.ndarray, k: int) -> list:
+    """Indices of the k largest finite values, descending, ties to the lower index."""
+    order = np.argsort(-values, kind="stable")
+    return [int(x) for x in order[:k] if np.isfinite(values[x])]
+
+
+def _valid_top(values: np.ndarray, chosen: list, k: int, tol: float) -> bool:
+    """Is `chosen` a top-k of `values` once gaps up to `tol` count as ties?"""
+    fin = [int(x) for x in np.nonzero(np.isfinite(values))[0]]
+    if len(chosen) != min(k, len(fin)) or len(set(chosen)) != len(chosen):
+        return False
+    if any(not np.isfinite(values[x]) for x in chosen):
+        return False
+    rest = [x for x in fin if x not in chosen]
+    return not rest or min(values[x] for x in chosen) >= max(values[x] for x in rest) - tol
+
+
+def retrieval_selection(a_prefix: np.ndarray, labels_prefix: np.ndarray,
+                        blocks_prefix: np.ndarray, Ck: int, nblocks: int,
+                        k1: int, k2: int, follow=None, tol: float = 1e-4):
+    """Retrieved keys for one (query cluster, block) [R9]; [GIST] Kernmechanismen 4.
+
+    a_prefix: s qbar_i . k_m for the prefix keys; labels/blocks: their key cluster and
+    spatial block. Atom log-mass sigma(j,b') = logsumexp of a over keys of cluster j in
+    block b'; cluster score sigma(j) = logsumexp_b' sigma(j,b').
+      1. J = the k1 clusters of largest sigma(j)   (cluster selection),
+      2. for j in J, the k2 blocks of largest sigma(j,b')  (spatial block selection).
+    Descending order, ties to the lower index, empty (-inf) candidates never chosen,
+    fewer candidates than k -> all of them. Returns a boolean mask over prefix keys.
+
+    follow: optional selection of another implementation, a list of (j, [b', ...]). It is
+    adopted when it is a valid top-k at both levels once score gaps up to `tol` (natural
+    log units) count as ties; then the return value is (mask, 1 if it differed else 0, 0),
+    otherwise (own mask, 0, 1). Without follow only the mask is returned."""
+    sig = _atom_log_masses(a_prefix, labels_prefix, blocks_prefix, Ck, nblocks)
+    sj = _lse_rows(sig)
+    J = _top(sj, k1)
+    sel = [(j, _top(sig[j], k2)) for j in J]
+
+    def mask_of(selection):
+        take = np.zeros(a_prefix.shape[0], bool)
+        for j, bl in selection:
+            for bb in bl:
                 take |= (labels_prefix == j) & (blocks_prefix == bb)
-    return take
+        return take
+
+    if follow is None:
+        return mask_of(sel)
+    fj = [j for j, _ in follow]
+    same = sorted(fj) == sorted(J) and all(sorted(bl) == sorted(dict(sel)[j]) for j, bl in follow)
+    if same:
+        return mask_of(sel), 0, 0
+    ok = _valid_top(sj, fj, k1, tol) and all(_valid_top(sig[j], list(bl), k2, tol) for j, bl in follow)
+    if ok:
+        return mask_of(follow), 1, 0
+    return mask_of(sel), 0, 1
 
 
 def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
                 scale: Optional[float] = None, dipole: str = "tilted",
                 topk_clusters: int = 0, topk_blocks: int = 0,
                 labels_q=None, labels_k=None, follow_q=None, follow_k=None,
-                tie_rel: float = 1e-5, blocks_to_eval: Optional[Sequence[int]] = None) -> MuseResult:
+                tie_rel: float = 1e-5, blocks_to_eval: Optional[Sequence[int]] = None,
+                retrieval_follow: Optional[np.ndarray] = None) -> MuseResult:
     """Causal MuSe forward of one head [R8].
 
     Clusters are fitted once per head over the whole sequence. For a query n in
@@ -405,7 +451,11 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
     the local block in the exact part, and the far summaries cover the remaining
     prefix keys only.
 
-    blocks_to_eval: optional list of blocks whose rows are computed (others NaN)."""
+    blocks_to_eval: optional list of blocks whose rows are computed (others NaN).
+    retrieval_follow: optional [nblocks, Cq, k1, 1 + k2] selections of another
+    implementation (cluster id then block ids per chosen cluster, -1 padded), adopted
+    where they are valid up to near-ties (see retrieval_selection); the counts are
+    returned in MuseResult.retrieval_near_ties / retrieval_mismatches."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -419,6 +469,7 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
     o = np.full((N, v.shape[1]), np.nan)
     L = np.full(N, np.nan)
     key_block = np.arange(N) // block
+    near = mism = 0
     todo = range(nb) if blocks_to_eval is None else blocks_to_eval
     for b in todo:
         r0, r1 = b * block, (b + 1) * block
@@ -437,7 +488,17 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
         for i in np.unique(lq[r0:r1]):
             qi = rows[lq[r0:r1] == i]
             a = s * (k[pre] @ qbar[i])
-            take = retrieval_selection(a, lk[pre], key_block[pre], Ck, b, topk_clusters, topk_blocks)
+            if retrieval_follow is None:
+                take = retrieval_selection(a, lk[pre], key_block[pre], Ck, b, topk_clusters, topk_blocks)
+            else:
+                fl = []
+                for row in np.asarray(retrieval_follow[b, i]):
+                    if row[0] >= 0:
+                        fl.append((int(row[0]), [int(x) for x in row[1:] if x >= 0]))
+                take, nt, mm = retrieval_selection(a, lk[pre], key_block[pre], Ck, b, topk_clusters,
+                                                   topk_blocks, follow=fl)
+                near += nt
+                mism += mm
             R = np.nonzero(take)[0]
             F = np.nonzero(~take)[0]
             keys = np.concatenate([R, np.arange(r0, r1)])
@@ -451,4 +512,6 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
             else:
                 o_far, L_far = np.zeros_like(o_ex), np.full(qi.size, NEG_INF)
             o[qi], L[qi] = lse_merge(o_far, L_far, o_ex, L_ex)
-    return MuseResult(o, L, km_q, km_k, lq, lk, qbar)
+    res = MuseResult(o, L, km_q, km_k, lq, lk, qbar)
+    res.retrieval_near_ties, res.retrieval_mismatches = near, mism
+    return res

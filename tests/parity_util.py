@@ -45,7 +45,9 @@ class HeadCheck:
 
 
 def run_gpu(cfg: WorkloadConfig, q, k, v, out_dtype=torch.float32, dipole=True, labels_q_in=None,
-            labels_k_in=None, topk=(0, 0)):
+            labels_k_in=None, topk=None):
+    if topk is None:
+        topk = (cfg.topk_clusters, cfg.topk_blocks)
     from clustered_softmax_attention_amd import attn_fwd
     Q, K, V = (to_device(t, cfg.dtype) for t in (q, k, v))
     out, ex = attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=cfg.causal, block=cfg.block,
@@ -57,7 +59,8 @@ def run_gpu(cfg: WorkloadConfig, q, k, v, out_dtype=torch.float32, dipole=True, 
 
 
 def oracle_head(cfg: WorkloadConfig, q, k, v, trace_q, trace_k, dipole="tilted",
-                blocks: Optional[Sequence[int]] = None, rows: Optional[np.ndarray] = None):
+                blocks: Optional[Sequence[int]] = None, rows: Optional[np.ndarray] = None,
+                retrieval_trace: Optional[np.ndarray] = None):
     """Oracle of one head in follow mode (near-tie labels adopted from the GPU traces)."""
     kq = lloyd_kmeans(q, cfg.Cq, cfg.iters, follow_trace=trace_q)
     kk = lloyd_kmeans(k, cfg.Ck, cfg.iters, follow_trace=trace_k)
@@ -66,7 +69,9 @@ def oracle_head(cfg: WorkloadConfig, q, k, v, trace_q, trace_k, dipole="tilted",
     if cfg.causal:
         r = muse_causal(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, cfg.block, dipole=dipole,
                         topk_clusters=cfg.topk_clusters, topk_blocks=cfg.topk_blocks,
-                        labels_q=kq.labels, labels_k=kk.labels, blocks_to_eval=blocks)
+                        labels_q=kq.labels, labels_k=kk.labels, blocks_to_eval=blocks,
+                        retrieval_follow=retrieval_trace)
+        assert r.retrieval_mismatches == 0, "retrieval selections differ beyond near-ties"
     else:
         r = muse_acausal(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, dipole=dipole,
                          labels_q=kq.labels, labels_k=kk.labels, rows=rows)
@@ -84,18 +89,21 @@ def check_config(cfg: WorkloadConfig, heads: List[Tuple[int, int]], tol: Optiona
     tq = ex["labels_q_trace"].cpu().numpy()
     tk = ex["labels_k_trace"].cpu().numpy()
     lse = ex["lse"].cpu().numpy()
+    rtr = ex["retrieval_trace"].cpu().numpy() if "retrieval_trace" in ex else None
     log(f"[{cfg.name}] gpu done in {time.time() - t0:.1f}s; checking heads {heads}")
     res = []
     tol = TOL[cfg.dtype] if tol is None else tol
     for b, h in heads:
         r, kq, kk = oracle_head(cfg, q[b, h], k[b, h], v[b, h], tq[:, b, h], tk[:, b, h],
-                                dipole="tilted" if dipole else "none", blocks=blocks, rows=rows)
+                                dipole="tilted" if dipole else "none", blocks=blocks, rows=rows,
+                                retrieval_trace=None if rtr is None else rtr[b, h])
         assert np.array_equal(kq.labels, tq[-1, b, h]) and np.array_equal(kk.labels, tk[-1, b, h])
         sel = np.isfinite(r.o[:, 0])
         rel = rel_l2(o_gpu[b, h][sel], r.o[sel])
         lse_err = float(np.max(np.abs(lse[b, h][sel] - r.lse[sel])))
         log(f"[{cfg.name}] head ({b},{h}): rel-L2 {rel:.3e} (tol {tol:.0e}), max |dLSE| {lse_err:.2e}, "
-            f"near-ties q={kq.near_ties} k={kk.near_ties}, rows checked {int(sel.sum())}")
+            f"near-ties q={kq.near_ties} k={kk.near_ties} retrieval={r.retrieval_near_ties}, "
+            f"rows checked {int(sel.sum())}")
         assert rel <= tol, f"rel-L2 {rel} > {tol}"
         assert lse_err <= (1e-4 if cfg.dtype == "f32" else 2e-3)
         res.append(HeadCheck(b, h, rel, kq.near_ties, kk.near_ties))

@@ -53,7 +53,7 @@ def test_params_struct_layout_matches(lib):
     p = FwdParams()
     lib.muse_fwd_params_init(ctypes.byref(p))
     assert p.out_dtype == -1 and p.dipole == 1 and p.scale == 0.0 and p.topk_clusters == 0
-    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8  # 5 ints/floats, pad, 8 pointers, size_t
+    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8 + 8  # 5 ints/floats, pad, 8 pointers, size_t, ptr
 
 
 def _call(lib, **kw):

@@ -66,6 +66,28 @@ def test_causal_fp32(muse_lib):
     check_config(cfg, [(0, 0), (0, 1)])
 
 
+def test_retrieval_c5_shape_reduced(muse_lib):
+    cfg = scaled_config("c5", B=1, H=2, N=4096)
+    check_config(cfg, [(0, 0), (0, 1)])
+
+
+def test_retrieval_small_blocks_fp32(muse_lib):
+    cfg = scaled_config("c5", B=1, H=1, N=2048, block=256, dtype="f32", Cq=8, Ck=16, topk_clusters=3,
+                        topk_blocks=2)
+    check_config(cfg, [(0, 0)])
+
+
+def test_retrieval_of_everything_is_exact(muse_lib):
+    # k1 = Ck and k2 = number of blocks: every earlier key is attended exactly
+    cfg = scaled_config("c5", B=1, H=1, N=2048, block=256, Cq=8, Ck=16, topk_clusters=16, topk_blocks=8)
+    q, k, v = make_inputs(cfg)
+    out, _ = run_gpu(cfg, q, k, v)
+    o, _ = exact_attention(q[0, 0], k[0, 0], v[0, 0], causal=True)
+    rel = rel_l2(out.float().cpu().numpy()[0, 0], o)
+    log(f"retrieval of everything vs exact causal: rel-L2 {rel:.3e}")
+    assert rel <= TOL["bf16"]
+
+
 def test_bf16_output_within_tolerance(muse_lib):
     cfg = scaled_config("c2", B=1, H=1, N=2048)
     check_config(cfg, [(0, 0)], out_dtype=torch.bfloat16)
@@ -124,6 +146,11 @@ def test_c2_full_size_sampled_heads(muse_lib):
 def test_c3_full_size_sampled_blocks(muse_lib):
     cfg = CONFIGS["c3"]
     check_config(cfg, [(7, 5)], blocks=[1, 15])
+
+
+def test_c5_full_size_sampled_blocks(muse_lib):
+    cfg = CONFIGS["c5"]
+    check_config(cfg, [(1, 6)], blocks=[1, 15])
 
 
 def test_c4_full_size_sampled_blocks(muse_lib):

@@ -345,3 +345,20 @@ def test_retrieval_finds_planted_outliers():
     a = (k[:7 * blk] @ km_q.centroids[i]) / math.sqrt(D)
     take = retrieval_selection(a, km_k.labels[:7 * blk], np.arange(7 * blk) // blk, 8, 7, 4, 2)
     assert all(take[p] for p in plant)
+
+
+def test_retrieval_follow_mode():
+    labels = np.array([0, 1, 2, 0, 1, 2])
+    blocks = np.array([0, 0, 0, 1, 1, 1])
+    a = np.array([1.0, 1.0 + 1e-6, -3.0, 0.0, 0.0, -3.0])  # clusters 0 and 1 nearly tied
+    base = retrieval_selection(a, labels, blocks, 3, 2, k1=1, k2=1)
+    assert base.tolist() == [False, True, False, False, False, False]
+    # the near-tied alternative is adopted
+    m, near, mism = retrieval_selection(a, labels, blocks, 3, 2, 1, 1, follow=[(0, [0])])
+    assert m.tolist() == [True, False, False, False, False, False] and (near, mism) == (1, 0)
+    # a clearly worse choice is flagged and not adopted
+    m, near, mism = retrieval_selection(a, labels, blocks, 3, 2, 1, 1, follow=[(2, [0])])
+    assert m.tolist() == base.tolist() and (near, mism) == (0, 1)
+    # identical selection: nothing to report
+    m, near, mism = retrieval_selection(a, labels, blocks, 3, 2, 1, 1, follow=[(1, [0])])
+    assert (near, mism) == (0, 0)
