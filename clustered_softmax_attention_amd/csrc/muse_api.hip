@@ -126,7 +126,7 @@ struct Plan {
   size_t t_khi, t_klo, t_vthi, t_vtlo, t_dip, tiles, ntiles, tile_base;
   int max_tiles;
   size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores;
-  size_t s_logz, s_k, s_v, s_dipT;
+  size_t s_logz, s_k, s_v, s_dip;
   size_t o_far, l_far, retr_sel;
   size_t total;
 };
@@ -171,7 +171,7 @@ Plan make_plan(const Shape& s, const muse_fwd_params* p) {
   P.s_logz = L.take(BH * nbS * Cq * Ck * f);
   P.s_k = L.take(BH * nbS * Cq * Ck * D * f);
   P.s_v = L.take(BH * nbS * Cq * Ck * D * f);
-  P.s_dipT = L.take(BH * nbS * Cq * D * D * f);
+  P.s_dip = L.take(BH * nbS * Cq * D * D * f);
   if (s.causal) {
     P.o_far = L.take(BH * N * D * f);
     P.l_far = L.take(BH * N * f);
@@ -291,7 +291,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.s_logz = at<float>(ws, P.s_logz);
   a1.s_k = at<float>(ws, P.s_k);
   a1.s_v = at<float>(ws, P.s_v);
-  a1.s_dipT = at<float>(ws, P.s_dipT);
+  a1.s_dip = at<float>(ws, P.s_dip);
   if (mf) {
     a1.t_khi = at<uint16_t>(ws, P.t_khi);
     a1.t_klo = at<uint16_t>(ws, P.t_klo);
@@ -326,7 +326,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
     ra.s_logz = a1.s_logz;
     ra.s_k = a1.s_k;
     ra.s_v = a1.s_v;
-    ra.s_dipT = a1.s_dipT;
+    ra.s_dip = a1.s_dip;
     ra.sel = at<int32_t>(ws, P.retr_sel);
     ra.trace = p->retrieval_trace;
     ra.o_far = at<float>(ws, P.o_far);
@@ -356,7 +356,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a2.s_logz = a1.s_logz;
   a2.s_k = a1.s_k;
   a2.s_v = a1.s_v;
-  a2.s_dipT = a1.s_dipT;
+  a2.s_dip = a1.s_dip;
   a2.t_khi = a1.t_khi;
   a2.t_klo = a1.t_klo;
   a2.t_vthi = a1.t_vthi;

@@ -64,7 +64,7 @@ struct RetrArgs {
   float* s_logz;               // tables [BH, nb, Cq, ...], entry (b, i) rewritten in place
   float* s_k;
   float* s_v;
-  float* s_dipT;               // entry (b, i) holds E[v k^T] before the dipole finalise
+  float* s_dip;               // entry (b, i) holds E[v k^T] before the dipole finalise
   int32_t* sel;                // [BH, nb, Cq, k1*(1+k2)] selection
   int32_t* trace;              // copy of sel for the caller, or null
   float* o_far;                // [BH, N, D] far-field partial result (merged in place)
@@ -100,7 +100,7 @@ struct S1Args {
   float* s_logz;               // [BH, nbS, Cq, Ck]
   float* s_k;                  // [BH, nbS, Cq, Ck, D] tilted key means
   float* s_v;                  // [BH, nbS, Cq, Ck, D] tilted value means
-  float* s_dipT;               // [BH, nbS, Cq, D(k), D(v)] aggregated dipole, key index first
+  float* s_dip;                // [BH, nbS, Cq, D(v), D(k)] aggregated dipole, value index first
   // bf16 copies for the matrix-core stage 2 (null on the fp32 path)
   uint16_t* t_khi;             // [BH, nbS, Cq, Ck, D]  K_ij = hi + lo
   uint16_t* t_klo;
@@ -131,7 +131,7 @@ struct S2Args {
   const float* s_logz;
   const float* s_k;
   const float* s_v;
-  const float* s_dipT;
+  const float* s_dip;
   // matrix-core path (bf16 inputs)
   const uint16_t* t_khi;
   const uint16_t* t_klo;

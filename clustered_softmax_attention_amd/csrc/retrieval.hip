@@ -227,13 +227,13 @@ __global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
   __syncthreads();
   const float rest = 1.f - s_red[1];
   const float inv = rest > 1e-30f ? 1.f / rest : 0.f;
-  float* dipT = a.s_dipT + sidx * D * D;  // [dk][dv], holds the prefix E[v k^T]
+  float* dip = a.s_dip + sidx * D * D;  // [dv][dk], holds the prefix E[v k^T]
 #pragma unroll
   for (int x = 0; x < TD; ++x)
 #pragma unroll
     for (int y = 0; y < TD; ++y) {
-      const size_t o = static_cast<size_t>(tc * TD + y) * D + (tr * TD + x);
-      dipT[o] = (dipT[o] - acc[x][y]) * inv;
+      const size_t o = static_cast<size_t>(tr * TD + x) * D + (tc * TD + y);
+      dip[o] = (dip[o] - acc[x][y]) * inv;
     }
 }
 

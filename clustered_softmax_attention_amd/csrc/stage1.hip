@@ -19,7 +19,7 @@
 //   s1_moments    one workgroup per (i, b', head): block-normalised sum w v k^T.
 //   s1_prefix     fold of atoms over blocks -> log Z, K, V tables.
 //   s1_mom_prefix fold of block moments over blocks -> E_i[v k^T] per table entry.
-//   s1_dip_final  D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T (stored key index first).
+//   s1_dip_final  D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T (value index first).
 #include "mfma.hpp"
 #include "muse_kernels.hpp"
 
@@ -258,13 +258,11 @@ __global__ void s1_mom_prefix_kernel(S1Args a) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   const int i = blockIdx.y, bh = blockIdx.z;
   if (e >= D * D) return;
-  const int dv = e / D, dk = e % D;
   const int per_block = a.causal ? a.block / a.mbk : a.nmb;
   float rR = kNegInf, racc = 0.f;
   auto emit = [&](int b) {
-    // stored key index first: [dk][dv]
     const size_t sbase = ((static_cast<size_t>(bh) * a.nbS + b) * Cq + i) * D * D;
-    a.s_dipT[sbase + static_cast<size_t>(dk) * D + dv] = (rR == kNegInf) ? 0.f : racc;
+    a.s_dip[sbase + e] = (rR == kNegInf) ? 0.f : racc;  // [dv][dk]
   };
   for (int mb = 0; mb < a.nmb; ++mb) {
     if (a.causal && mb % per_block == 0) emit(mb / per_block);
@@ -339,41 +337,54 @@ __global__ void __launch_bounds__(256) s1_dip_final_kernel(S1Args a) {
         for (int y = 0; y < TD; ++y) acc[x][y] = fmaf(vr[x], kr[y], acc[x][y]);
     }
   }
-  float* dipT = a.s_dipT + sidx * D * D;
+  float* dip = a.s_dip + sidx * D * D;
 #pragma unroll
   for (int x = 0; x < TD; ++x)
 #pragma unroll
     for (int y = 0; y < TD; ++y) {
-      const size_t o = static_cast<size_t>(tc * TD + y) * D + (tr * TD + x);  // [dk][dv]
-      dipT[o] = dipT[o] - acc[x][y];
+      const size_t o = static_cast<size_t>(tr * TD + x) * D + (tc * TD + y);  // [dv][dk]
+      dip[o] = dip[o] - acc[x][y];
     }
 }
 
-// bf16 hi/lo copies of one table entry (i, e) for the matrix-core stage 2:
-// K_ij (row-major), V_ij transposed to [d][j], and s * D_i with the value index first.
-__global__ void s1_pack_kernel(S1Args a) {
+// bf16 hi/lo copies of one table entry (i, e) for the matrix-core stage 2: K_ij
+// (row-major), V_ij transposed to [d][j] through 32 x 32 LDS tiles (reads and writes
+// both coalesced), and s * D_i (value index first, a straight copy).
+__global__ void __launch_bounds__(256) s1_pack_kernel(S1Args a) {
+  __shared__ float tileV[32][33];
   const int i = blockIdx.x, e = blockIdx.y, bh = blockIdx.z;
-  const int D = a.D, Ck = a.Ck;
+  const int D = a.D, Ck = a.Ck, tid = threadIdx.x;
   const size_t sidx = (static_cast<size_t>(bh) * a.nbS + e) * a.Cq + i;
   const float* K = a.s_k + sidx * Ck * D;
   const float* V = a.s_v + sidx * Ck * D;
-  for (int x = threadIdx.x; x < Ck * D; x += blockDim.x) {
+  for (int x = tid; x < Ck * D; x += 256) {
     const float k = K[x];
     const uint16_t kh = f32_to_bf16_bits(k);
     a.t_khi[sidx * Ck * D + x] = kh;
     a.t_klo[sidx * Ck * D + x] = f32_to_bf16_bits(k - bf16_to_f32(kh));
-    const int d = x / Ck, j = x % Ck;  // transposed destination [d][j]
-    const float v = V[static_cast<size_t>(j) * D + d];
-    const uint16_t vh = f32_to_bf16_bits(v);
-    a.t_vthi[sidx * Ck * D + x] = vh;
-    a.t_vtlo[sidx * Ck * D + x] = f32_to_bf16_bits(v - bf16_to_f32(vh));
   }
-  if (a.dipole) {
-    const float* dipT = a.s_dipT + sidx * D * D;  // [dk][dv]
-    for (int x = threadIdx.x; x < D * D; x += blockDim.x) {
-      const int dv = x / D, dk = x % D;
-      a.t_dip[sidx * D * D + x] = f32_to_bf16_bits(a.scale * dipT[static_cast<size_t>(dk) * D + dv]);
+  const int tx = tid & 31, ty = tid >> 5;  // 32 x 8 threads
+  for (int j0 = 0; j0 < Ck; j0 += 32)
+    for (int d0 = 0; d0 < D; d0 += 32) {
+      __syncthreads();
+      for (int r = ty; r < 32; r += 8) {
+        const int j = j0 + r, d = d0 + tx;
+        tileV[r][tx] = j < Ck ? V[static_cast<size_t>(j) * D + d] : 0.f;
+      }
+      __syncthreads();
+      for (int r = ty; r < 32; r += 8) {
+        const int d = d0 + r, j = j0 + tx;
+        if (j >= Ck) continue;
+        const float v = tileV[tx][r];
+        const uint16_t vh = f32_to_bf16_bits(v);
+        const size_t o = sidx * Ck * D + static_cast<size_t>(d) * Ck + j;
+        a.t_vthi[o] = vh;
+        a.t_vtlo[o] = f32_to_bf16_bits(v - bf16_to_f32(vh));
+      }
     }
+  if (a.dipole) {
+    const float* dip = a.s_dip + sidx * D * D;  // [dv][dk]
+    for (int x = tid; x < D * D; x += 256) a.t_dip[sidx * D * D + x] = f32_to_bf16_bits(a.scale * dip[x]);
   }
 }
 

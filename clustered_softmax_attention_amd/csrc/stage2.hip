@@ -82,11 +82,11 @@ __global__ void __launch_bounds__(kS2Threads) s2_refine_kernel(S2Args a) {
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] *= inv;
   if (a.dipole && !empty) {
-    const float* dipT = a.s_dipT + sidx * D * D;  // [dk][dv]
+    const float* dip = a.s_dip + sidx * D * D;  // [dv][dk]
     for (int dk = 0; dk < D; ++dk) {
       const float x = a.scale * s_q[dk][tid];
 #pragma unroll
-      for (int dv = 0; dv < D; ++dv) acc[dv] = fmaf(dipT[dk * D + dv], x, acc[dv]);
+      for (int dv = 0; dv < D; ++dv) acc[dv] = fmaf(dip[dv * D + dk], x, acc[dv]);
     }
   }
   const float L = empty ? kNegInf : mx + __logf(z);
