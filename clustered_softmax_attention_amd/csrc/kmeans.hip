@@ -73,10 +73,9 @@ __global__ void __launch_bounds__(64) kmeans_init_kernel(KmArgs a) {
   write_centroid_tables(t, a.D, row, vals, nper);
 }
 
-// Stable counting sort of the tile's points by label (LDS), then the tile's sort info
-// and per-cluster sums. Called by every thread of the workgroup.
-template <typename T, int D>
-__device__ void tile_sort(const KmArgs& a, const KmTensor& t, int lab, bool valid, int* s_lab, int* s_whist,
+// Stable counting sort of tile tt's points by label (LDS) and the tile's sort info.
+// Called by every thread of the workgroup (one thread per point of the tile).
+__device__ void tile_sort(const KmArgs& a, const KmTensor& t, int lab, bool valid, int tt, int* s_lab, int* s_whist,
                           int* s_cnt, int* s_start, int* s_sorted) {
   const int C = t.C;
   const int bh = blockIdx.y;
@@ -84,7 +83,6 @@ __device__ void tile_sort(const KmArgs& a, const KmTensor& t, int lab, bool vali
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int nwaves = tile >> 6;
-  const T* x = static_cast<const T*>(t.x) + static_cast<size_t>(bh) * a.N * D;
   for (int e = tid; e < nwaves * C; e += tile) s_whist[e] = 0;
   s_lab[tid] = lab;
   __syncthreads();
@@ -119,8 +117,8 @@ __device__ void tile_sort(const KmArgs& a, const KmTensor& t, int lab, bool vali
   if (valid) s_sorted[s_start[lab] + s_whist[wave * C + lab] + rank_in_wave] = tid;
   __syncthreads();
 
-  // ---- outputs: sort info (for bucketing) and this tile's per-cluster sums ----
-  const size_t tix = static_cast<size_t>(bh) * a.ntiles + blockIdx.x;
+  // ---- outputs: sort info for bucketing ----
+  const size_t tix = static_cast<size_t>(bh) * a.ntiles + tt;
   for (int j = tid; j < C; j += tile) {
     t.tile_cnt[tix * C + j] = s_cnt[j];
     t.tile_start[tix * C + j] = s_start[j];
@@ -210,154 +208,243 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_kernel(KmArgs a, int i
     if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
   }
 
-  tile_sort<T, D>(a, t, lab, valid, s_lab, s_whist, s_cnt, s_start, s_sorted);
+  tile_sort(a, t, lab, valid, blockIdx.x, s_lab, s_whist, s_cnt, s_start, s_sorted);
   tile_sums_valu<T, D>(a, t, s_cnt, s_start, s_sorted);
 }
 
-// Matrix-core assign for bf16 inputs; blockDim.x == tile (multiple of 64, <= kMaxTileMfma).
-// Wave w scores points w*64 .. w*64+63 in two groups of 32 (lane (c, h) of the product
-// holds 16 centroid rows of point c per 32-row tile). Lane l = 32 h + c of the wave
-// then owns point w*64 + l for the sort. Dynamic LDS: c_hi, c_lo [Cp][D+8] bf16 |
-// ||c||^2 [Cp] | sort buffers | X^T staging [D][64+8] bf16.
+// Matrix-core assign for bf16 inputs. A workgroup of NW waves takes `tpg` consecutive
+// tiles of 64*NW points of one head and keeps the centroid tables in LDS across them.
+//
+// Scores: with the accumulator preset to -||c_j||^2 / 2, the product C X^T gives
+// x.c_j - ||c_j||^2/2 = (||x||^2 - ||x - c_j||^2) / 2, so the nearest centroid is the
+// largest score. Lane (c, h) of a 32 x 32 tile holds 16 centroid rows of point c; each
+// wave scores its 64 points as two 32-point groups that share every centroid fragment.
+// A running best, second best (med3) and best slot are kept per lane, then merged with
+// the partner lane l^32. An error of E in distance is E/2 in score; a second centroid
+// within E of the best (2E in distance) sends the point to the exact fp32 rescoring.
+//
+// Cluster sums psum^T [D x C] = X^T onehot run on the matrix cores too: the tile's rows
+// sit row-major in LDS and reach the A operand through the transpose read; the one-hot
+// B operand is built from the tile's labels with packed 16-bit compares. Wave w owns a
+// fixed set of output tiles (one cluster tile and all D/32 feature tiles when NW = 4),
+// accumulated over all tiles of the group and written once.
+//
+// Dynamic LDS: c_hi, c_lo [Cp][D] bf16 (16-byte chunks XOR-swizzled by row) | bias [Cp] |
+// X tile [64 NW][XST] bf16 | labels [64 NW] u16 | counts [C] | sort buffers.
+template <int D, int NW>
+struct KmMfmaCfg {
+  static constexpr int NKS = D / 16;
+  static constexpr int XST = D == 64 ? D + 8 : D + 16;
+  static constexpr int NDT = D / 32;
+  static constexpr int TILE = 64 * NW;
+  // cluster tiles per wave and pass (at most 4 accumulator tiles), output tiles per wave
+  static constexpr int CPW = (4 / NDT) < (4 + NW - 1) / NW ? (4 / NDT) : (4 + NW - 1) / NW;
+  static constexpr int OPW = CPW * NDT;
+  static size_t lds_bytes(int Cmax) {
+    const size_t Cp = (Cmax + 31) & ~31;
+    return Cp * D * 2 * sizeof(uint16_t) + Cp * sizeof(float) + static_cast<size_t>(TILE) * XST * sizeof(uint16_t) +
+           TILE * sizeof(uint16_t) + sizeof(int) * (Cmax + 2 * TILE + NW * Cmax + 2 * Cmax);
+  }
+  static int passes(int Cmax) { return ((Cmax + 31) / 32 + NW * CPW - 1) / (NW * CPW); }
+};
+
+__device__ __forceinline__ bf16x8_t onehot_bf16x8(const u16x8_t& lab8, unsigned j) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 jj = {static_cast<unsigned short>(j), static_cast<unsigned short>(j)};
+  const u16x2 one = {1, 1}, val = {0x3F80, 0x3F80};
+  u16x8_t o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u16x2 pr = {lab8[2 * q], lab8[2 * q + 1]};
+    const u16x2 m = __builtin_elementwise_min(pr ^ jj, one);  // 0 where the label is j
+    const u16x2 r = (one - m) * val;
+    o[2 * q] = r[0];
+    o[2 * q + 1] = r[1];
+  }
+  return as_bf16x8(o);
+}
+
 template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW) kmeans_assign_mfma_kernel(KmArgs a, int iter, int last) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int CST = D + 8;
-  constexpr int NKS = D / 16;
+  using Cfg = KmMfmaCfg<D, NW>;
+  constexpr int NKS = Cfg::NKS, XST = Cfg::XST, NDT = Cfg::NDT, TILE = Cfg::TILE, CPW = Cfg::CPW, OPW = Cfg::OPW;
   constexpr int MAXJT = kMaxClusters / 32;
   const KmTensor& t = a.t[blockIdx.z];
   const int C = t.C, Cp = (C + 31) & ~31, njt = Cp / 32;
-  const int bh = blockIdx.y, tile = blockDim.x, tid = threadIdx.x;
+  const int grp = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int tt0 = grp * a.tpg, tt1 = min(a.ntiles, tt0 + a.tpg);
   uint16_t* chi = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* clo = chi + Cp * CST;
-  float* cn2 = reinterpret_cast<float*>(clo + Cp * CST);
-  int* s_lab = reinterpret_cast<int*>(cn2 + Cp);
-  int* s_whist = s_lab + tile;
-  int* s_cnt = s_whist + (tile >> 6) * C;
+  uint16_t* clo = chi + Cp * D;
+  float* bias = reinterpret_cast<float*>(clo + Cp * D);
+  uint16_t* sX = reinterpret_cast<uint16_t*>(bias + Cp);
+  uint16_t* slab = sX + TILE * XST;
+  int* s_gcnt = reinterpret_cast<int*>(slab + TILE);
+  int* s_lab = s_gcnt + C;
+  int* s_whist = s_lab + TILE;
+  int* s_cnt = s_whist + NW * C;
   int* s_start = s_cnt + C;
   int* s_sorted = s_start + C;
-  const long n = static_cast<long>(blockIdx.x) * tile + tid;
-  const bool valid = n < a.N;
   const uint16_t* X = static_cast<const uint16_t*>(t.x) + static_cast<size_t>(bh) * a.N * D;
   const float* cent = t.cent + static_cast<size_t>(bh) * C * D;
+  const bool score = t.labels_in == nullptr;
 
-  int lab = C;
-  if (t.labels_in != nullptr) {
-    if (valid) lab = min(max(t.labels_in[static_cast<size_t>(bh) * a.N + n], 0), C - 1);
-  } else {
-    // the first group of this wave's points, loaded before anything waits on memory
-    u16x8_t xraw[NKS];
-    auto load_group = [&](int gi) {
-      const long p = static_cast<long>(blockIdx.x) * tile + wave * 64 + gi * 32 + c;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        xraw[ks] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        if (p < a.N) xraw[ks] = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(p) * D + 16 * ks + 8 * h);
-      }
-    };
-    load_group(0);
+  if (score) {
     const uint16_t* ghi = t.chi + static_cast<size_t>(bh) * C * D;
     const uint16_t* glo = t.clo + static_cast<size_t>(bh) * C * D;
 #pragma unroll 4
-    for (int e = tid; e < Cp * (D / 8); e += tile) {
+    for (int e = tid; e < Cp * (D / 8); e += TILE) {
       const int j = e / (D / 8), c8 = e % (D / 8);
       u16x8_t h8 = {0, 0, 0, 0, 0, 0, 0, 0}, l8 = {0, 0, 0, 0, 0, 0, 0, 0};
       if (j < C) {
         h8 = *reinterpret_cast<const u16x8_t*>(ghi + static_cast<size_t>(j) * D + c8 * 8);
         l8 = *reinterpret_cast<const u16x8_t*>(glo + static_cast<size_t>(j) * D + c8 * 8);
       }
-      *reinterpret_cast<u16x8_t*>(chi + j * CST + c8 * 8) = h8;
-      *reinterpret_cast<u16x8_t*>(clo + j * CST + c8 * 8) = l8;
+      const int dst = j * D + ((c8 ^ (j & 7)) << 3);
+      *reinterpret_cast<u16x8_t*>(chi + dst) = h8;
+      *reinterpret_cast<u16x8_t*>(clo + dst) = l8;
     }
-    for (int j = tid; j < Cp; j += tile) cn2[j] = j < C ? t.cn2[static_cast<size_t>(bh) * C + j] : 0.f;
-    __syncthreads();
-    float cmax2 = 0.f;
-    for (int j = lane; j < C; j += 64) cmax2 = fmaxf(cmax2, cn2[j]);
+    for (int j = tid; j < Cp; j += TILE) bias[j] = j < C ? -0.5f * t.cn2[static_cast<size_t>(bh) * C + j] : kNegInf;
+  }
+  for (int j = tid; j < C; j += TILE) s_gcnt[j] = 0;
+  __syncthreads();
+  float cmax2 = 0.f;
+  if (score) {
+    for (int j = lane; j < C; j += 64) cmax2 = fmaxf(cmax2, -2.f * bias[j]);
     cmax2 = wave_max(cmax2);
-    const float cmax = sqrtf(cmax2);
-    int labs[2];
+  }
+  const float cmax = sqrtf(cmax2);
+
+  f32x16_t acc[OPW];
+#pragma unroll
+  for (int r = 0; r < OPW; ++r) acc[r] = zero16();
+  const int npass = (njt + NW * CPW - 1) / (NW * CPW);
+
+  // this wave's points of tile tt: group gi, lane (c, h) -> point 64 wave + 32 gi + c, dims 16 ks + 8 h
+  u16x8_t xf[2][NKS];
+  auto load_x = [&](int tt) {
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
-      const long p = static_cast<long>(blockIdx.x) * tile + wave * 64 + gi * 32 + c;
-      const bool pv = p < a.N;
-      bf16x8_t xf[NKS];
-      float xx = 0.f;
-      if (gi == 1) load_group(1);
+      const long p = static_cast<long>(tt) * TILE + wave * 64 + gi * 32 + c;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const u16x8_t u = xraw[ks];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float xv = bf16_to_f32(u[r]);
-          xx = fmaf(xv, xv, xx);
-        }
-        xf[ks] = as_bf16x8(u);
+        xf[gi][ks] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        if (p < a.N) xf[gi][ks] = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(p) * D + 16 * ks + 8 * h);
       }
-      xx += __shfl_xor(xx, 32, 64);
-      // scores of one 32-centroid tile: lane (c, h) holds centroids 32 jt + 8 g + 4 h + r
-      auto score_tile = [&](int jt, f32x16_t& acc) {
-        acc = zero16();
-        const int jr = 32 * jt + c;
+    }
+  };
+  // scores of centroid tile jt for both groups, accumulator preset to the bias
+  auto score_tile = [&](int jt, f32x16_t& s0, f32x16_t& s1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(bias + 32 * jt + 8 * q + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s0[4 * q + e] = b4[e];
+        s1[4 * q + e] = b4[e];
+      }
+    }
+    const int jr = 32 * jt + c;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int off = jr * D + (((2 * ks + h) ^ (c & 7)) << 3);
+      const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const u16x8_t*>(chi + off));
+      const bf16x8_t al = as_bf16x8(*reinterpret_cast<const u16x8_t*>(clo + off));
+      s0 = mfma32(ah, as_bf16x8(xf[0][ks]), s0);
+      s1 = mfma32(ah, as_bf16x8(xf[1][ks]), s1);
+      s0 = mfma32(al, as_bf16x8(xf[0][ks]), s0);
+      s1 = mfma32(al, as_bf16x8(xf[1][ks]), s1);
+    }
+  };
+
+  if (tt0 < tt1) load_x(tt0);
+  for (int tt = tt0; tt < tt1; ++tt) {
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        *reinterpret_cast<u16x8_t*>(sX + (wave * 64 + gi * 32 + c) * XST + 16 * ks + 8 * h) = xf[gi][ks];
+    const long n = static_cast<long>(tt) * TILE + tid;
+    const bool valid = n < a.N;
+    int lab = C;
+    if (!score) {
+      if (valid) lab = min(max(t.labels_in[static_cast<size_t>(bh) * a.N + n], 0), C - 1);
+    } else {
+      float xx[2];
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        float s = 0.f;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const u16x8_t*>(chi + jr * CST + 16 * ks + 8 * h));
-          const bf16x8_t al = as_bf16x8(*reinterpret_cast<const u16x8_t*>(clo + jr * CST + 16 * ks + 8 * h));
-          acc = mfma32(ah, xf[ks], acc);
-          acc = mfma32(al, xf[ks], acc);
-        }
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
-          acc[v] = j < C ? cn2[j] - 2.f * acc[v] : __builtin_huge_valf();
+          for (int e = 0; e < 4; ++e) {
+            const u16x2 uu = {xf[gi][ks][2 * e], xf[gi][ks][2 * e + 1]};
+            const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, uu);
+            s = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, s, false);
+          }
         }
-      };
-      // running best (lowest index on ties) and second-best score
-      float best = __builtin_huge_valf(), second = __builtin_huge_valf();
-      int bj = C;
-      for (int jt = 0; jt < njt; ++jt) {
-        f32x16_t sc;
-        score_tile(jt, sc);
+        xx[gi] = s + __shfl_xor(s, 32, 64);
+      }
+      float best[2] = {kNegInf, kNegInf}, second[2] = {kNegInf, kNegInf};
+      int slot[2] = {0, 0};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
-          const float x = sc[v];
-          if (x < best || (x == best && j < bj)) {
-            second = best;
-            best = x;
-            bj = j;
-          } else {
-            second = fminf(second, x);
+      for (int jt = 0; jt < MAXJT; ++jt) {
+        if (jt < njt) {
+          f32x16_t s0, s1;
+          score_tile(jt, s0, s1);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float x0 = s0[v], x1 = s1[v];
+            slot[0] = x0 > best[0] ? 16 * jt + v : slot[0];
+            second[0] = __builtin_amdgcn_fmed3f(best[0], second[0], x0);
+            best[0] = fmaxf(best[0], x0);
+            slot[1] = x1 > best[1] ? 16 * jt + v : slot[1];
+            second[1] = __builtin_amdgcn_fmed3f(best[1], second[1], x1);
+            best[1] = fmaxf(best[1], x1);
           }
         }
       }
-      {
-        const float ob = __shfl_xor(best, 32, 64);
-        const float os = __shfl_xor(second, 32, 64);
-        const int oj = __shfl_xor(bj, 32, 64);
-        if (ob < best || (ob == best && oj < bj)) {
-          second = fminf(best, os);
-          best = ob;
-          bj = oj;
+      int bj[2];
+      bool need[2];
+      float E[2];
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int sl = slot[gi];
+        bj[gi] = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * h + (sl & 3);
+        const float ob = __shfl_xor(best[gi], 32, 64);
+        const float os = __shfl_xor(second[gi], 32, 64);
+        const int oj = __shfl_xor(bj[gi], 32, 64);
+        if (ob > best[gi] || (ob == best[gi] && oj < bj[gi])) {
+          second[gi] = fmaxf(best[gi], os);
+          best[gi] = ob;
+          bj[gi] = oj;
         } else {
-          second = fminf(second, ob);
+          second[gi] = fmaxf(second[gi], ob);
         }
+        // distance error bound E; scores carry half of it
+        E[gi] = 1e-4f * sqrtf(xx[gi]) * cmax + 2e-5f * cmax2;
+        const long p = static_cast<long>(tt) * TILE + wave * 64 + gi * 32 + c;
+        need[gi] = p < a.N && second[gi] >= best[gi] - E[gi];
       }
-      const float E = 1e-4f * sqrtf(xx) * cmax + 2e-5f * cmax2;
-      const float thr = best + 2.f * E;
-      // a second centroid within the window: re-score every candidate exactly
-      if (__ballot(pv && second <= thr) != 0ull) {
-        const bool need = pv && second <= thr;  // the same for both lanes of the pair
-        float fb = __builtin_huge_valf();
-        int fj = C;
-        const uint16_t* xr = X + static_cast<size_t>(p) * D;
+      // a second centroid within the window: re-score every candidate exactly (fp32 direct form)
+      if (__ballot(need[0] || need[1]) != 0ull) {
+        float fb[2] = {__builtin_huge_valf(), __builtin_huge_valf()};
+        int fj[2] = {C, C};
         for (int jt = 0; jt < njt; ++jt) {
-          f32x16_t sc;
-          score_tile(jt, sc);
-          if (need) {
+          f32x16_t s0, s1;
+          score_tile(jt, s0, s1);
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi) {
+            if (!need[gi]) continue;
+            const long p = static_cast<long>(tt) * TILE + wave * 64 + gi * 32 + c;
+            const uint16_t* xr = X + static_cast<size_t>(p) * D;
+            const float thr = best[gi] - E[gi];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              if (sc[v] > thr) continue;
+              if ((gi == 0 ? s0[v] : s1[v]) < thr) continue;
               const int j = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
               const float* cr = cent + static_cast<size_t>(j) * D;
               float dist = 0.f;
@@ -365,115 +452,79 @@ __global__ void __launch_bounds__(64 * NW) kmeans_assign_mfma_kernel(KmArgs a, i
                 const float diff = bf16_to_f32(xr[d]) - cr[d];
                 dist = fmaf(diff, diff, dist);
               }
-              if (dist < fb || (dist == fb && j < fj)) {
-                fb = dist;
-                fj = j;
+              if (dist < fb[gi] || (dist == fb[gi] && j < fj[gi])) {
+                fb[gi] = dist;
+                fj[gi] = j;
               }
             }
           }
         }
-        const float ob = __shfl_xor(fb, 32, 64);
-        const int oj = __shfl_xor(fj, 32, 64);
-        if (ob < fb || (ob == fb && oj < fj)) fj = oj;
-        if (need) bj = fj;
-      }
-      labs[gi] = bj;
-    }
-    if (valid) lab = h == 0 ? labs[0] : labs[1];
-  }
-  if (valid) {
-    t.labels[static_cast<size_t>(bh) * a.N + n] = lab;
-    if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
-  }
-  const size_t tix = static_cast<size_t>(bh) * a.ntiles + blockIdx.x;
-  if (last) {
-    // bucketing after the last iteration needs the stable order
-    tile_sort<bf16, D>(a, t, lab, valid, s_lab, s_whist, s_cnt, s_start, s_sorted);
-  } else {
-    for (int j = tid; j < C; j += tile) s_cnt[j] = 0;
-    s_lab[tid] = lab;
-    __syncthreads();
-    if (valid) atomicAdd(&s_cnt[lab], 1);  // integer counts: order-independent
-    __syncthreads();
-    for (int j = tid; j < C; j += tile) t.tile_cnt[tix * C + j] = s_cnt[j];
-  }
-  // cluster sums psum^T [D x C] = X^T onehot over 64-point sub-chunks; wave w owns output
-  // tiles w, w + nwaves, ... of the (D/32) x (Cp/32) grid
-  constexpr int XST = 64 + 8;
-  constexpr int NDT = D / 32;
-  constexpr int MAXOT = (NDT * (kMaxClusters / 32) + NW - 1) / NW < 4 ? (NDT * (kMaxClusters / 32) + NW - 1) / NW : 4;
-  uint16_t* sXt = reinterpret_cast<uint16_t*>((reinterpret_cast<uintptr_t>(s_sorted + tile) + 15) & ~uintptr_t(15));
-  const int nwaves = tile >> 6;
-  const int not_ = NDT * njt;
-  const uint16_t bf_one = 0x3F80;
-  float* psum = t.psum + tix * C * D;
-  // a sub-chunk of 64 points is 64*D/8 16-byte pieces; each thread carries kPre of them
-  constexpr int kPre = (64 * (D / 8)) / (64 * NW);
-  auto load_chunk = [&](int p0, u16x8_t* buf) {
 #pragma unroll
-    for (int q = 0; q < kPre; ++q) {
-      const int x = tid + tile * q;
-      buf[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      if (x < 64 * (D / 8)) {
-        const int r = x / (D / 8), c8 = x % (D / 8);
-        const long pn = static_cast<long>(blockIdx.x) * tile + p0 + r;
-        if (pn < a.N) buf[q] = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(pn) * D + c8 * 8);
-      }
-    }
-  };
-  for (int ot0 = 0; ot0 < not_; ot0 += nwaves * MAXOT) {
-    f32x16_t acc[MAXOT];
-#pragma unroll
-    for (int r = 0; r < MAXOT; ++r) acc[r] = zero16();
-    u16x8_t pre[kPre];
-    load_chunk(0, pre);
-    for (int p0 = 0; p0 < tile; p0 += 64) {
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < kPre; ++q) {
-        const int x = tid + tile * q;
-        if (x < 64 * (D / 8)) {
-          const int r = x / (D / 8), c8 = x % (D / 8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sXt[(c8 * 8 + e) * XST + r] = pre[q][e];
+        for (int gi = 0; gi < 2; ++gi) {
+          const float ob = __shfl_xor(fb[gi], 32, 64);
+          const int oj = __shfl_xor(fj[gi], 32, 64);
+          if (ob < fb[gi] || (ob == fb[gi] && oj < fj[gi])) fj[gi] = oj;
+          if (need[gi]) bj[gi] = fj[gi];
         }
       }
-      __syncthreads();
-      if (p0 + 64 < tile) load_chunk(p0 + 64, pre);  // next sub-chunk in flight during this one
+      if (valid) lab = h == 0 ? bj[0] : bj[1];
+    }
+    // the scores no longer need this tile's fragments: fetch the next tile's now
+    if (tt + 1 < tt1) load_x(tt + 1);
+    if (valid) {
+      t.labels[static_cast<size_t>(bh) * a.N + n] = lab;
+      if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
+      atomicAdd(&s_gcnt[lab], 1);  // integer counts: order-independent
+    }
+    slab[tid] = valid ? static_cast<uint16_t>(lab) : static_cast<uint16_t>(0xFFFF);
+    if (last) tile_sort(a, t, lab, valid, tt, s_lab, s_whist, s_cnt, s_start, s_sorted);
+    __syncthreads();  // X tile and labels complete
+
+    for (int pass = 0; pass < npass; ++pass) {
+      if (npass > 1) {
 #pragma unroll
-      for (int r = 0; r < MAXOT; ++r) {
-        const int ot = ot0 + wave + nwaves * r;
-        if (ot >= not_) break;
-        const int dt = ot % NDT, ct = ot / NDT;
+        for (int r = 0; r < OPW; ++r) acc[r] = zero16();
+      }
+      const int ct0 = (pass * NW + wave) * CPW;
+      for (int ks = 0; ks < TILE / 16; ++ks) {
+        const u16x8_t lab8 = *reinterpret_cast<const u16x8_t*>(slab + 16 * ks + 8 * h);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int kk = 16 * ks + 8 * h;
-          const bf16x8_t ax = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sXt + (32 * dt + c) * XST + kk));
-          u16x8_t oh;
+        for (int rc = 0; rc < CPW; ++rc) {
+          const int ct = ct0 + rc;
+          if (ct >= njt) break;
+          const bf16x8_t oh = onehot_bf16x8(lab8, 32 * ct + c);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) oh[e] = s_lab[p0 + kk + e] == 32 * ct + c ? bf_one : 0;
-          acc[r] = mfma32(ax, as_bf16x8(oh), acc[r]);
+          for (int dt = 0; dt < NDT; ++dt) {
+            const bf16x8_t ax = lds_operand_tr(sX, XST, 16 * ks, 32 * dt, lane);
+            acc[rc * NDT + dt] = mfma32(ax, oh, acc[rc * NDT + dt]);
+          }
+        }
+      }
+      if (npass > 1 || tt + 1 == tt1) {
+        // sums of this group (npass > 1 only with one tile per group)
+        float* psum = t.psum + (static_cast<size_t>(bh) * a.ntiles + grp) * C * D;
+#pragma unroll
+        for (int rc = 0; rc < CPW; ++rc) {
+          const int j = 32 * (ct0 + rc) + c;
+          if (j >= C) continue;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4_t f = {acc[rc * NDT + dt][4 * q], acc[rc * NDT + dt][4 * q + 1], acc[rc * NDT + dt][4 * q + 2],
+                                 acc[rc * NDT + dt][4 * q + 3]};
+              *reinterpret_cast<f32x4_t*>(psum + static_cast<size_t>(j) * D + 32 * dt + 8 * q + 4 * h) = f;
+            }
         }
       }
     }
-#pragma unroll
-    for (int r = 0; r < MAXOT; ++r) {
-      const int ot = ot0 + wave + nwaves * r;
-      if (ot >= not_) break;
-      const int dt = ot % NDT, ct = ot / NDT;
-      const int j = 32 * ct + c;
-      if (j >= C) continue;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4_t f = {acc[r][4 * g], acc[r][4 * g + 1], acc[r][4 * g + 2], acc[r][4 * g + 3]};
-        *reinterpret_cast<f32x4_t*>(psum + static_cast<size_t>(j) * D + 32 * dt + 8 * g + 4 * h) = f;
-      }
-    }
+    __syncthreads();  // the next tile overwrites the X tile and labels
   }
+  for (int j = tid; j < C; j += TILE) t.gcnt[(static_cast<size_t>(bh) * a.ntiles + grp) * C + j] = s_gcnt[j];
 }
 
-// One wave per (centroid j, head, tensor), lanes over d: sum the tile partials in tile
-// order; the mean replaces c_j unless the cluster is empty.
+// One wave per (centroid j, head, tensor), lanes over d: sum the tile-group partials in
+// group order; the mean replaces c_j unless the cluster is empty.
 __global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
   const int C = t.C, D = a.D, j = blockIdx.x, bh = blockIdx.y;
@@ -483,11 +534,11 @@ __global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
   float acc[2] = {0.f, 0.f};
   int cnt = 0;
 #pragma unroll 8
-  for (int tt = 0; tt < a.ntiles; ++tt) {
+  for (int tt = 0; tt < a.ngroups; ++tt) {
     const float* ps = t.psum + ((tbase + tt) * C + j) * D;
     acc[0] += ps[lane_id()];
     if (nper > 1) acc[1] += ps[lane_id() + 64];
-    cnt += t.tile_cnt[(tbase + tt) * C + j];
+    cnt += t.gcnt[(tbase + tt) * C + j];
   }
   const size_t row = static_cast<size_t>(bh) * C + j;
   float vals[2];
@@ -565,18 +616,33 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
                      sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax);
   const dim3 g_assign(a.ntiles, a.BH, a.ntensors);
   const dim3 g_update(Cmax, a.BH, a.ntensors);
-  const int Cp = (Cmax + 31) & ~31;
-  const size_t lds_mfma = static_cast<size_t>(Cp) * (a.D + 8) * 2 * sizeof(uint16_t) + Cp * sizeof(float) +
-                          sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax) +
-                          static_cast<size_t>(a.D) * (64 + 8) * sizeof(uint16_t) + 16;
   const bool mf = sizeof(T) == 2;
+  const int nw = a.tile / 64;
+  KmArgs b = a;
+  b.tpg = 1;
+  size_t lds_mfma = 0;
+  int npass = 1;
+#define MUSE_KM_CFG(DD, NN)                               \
+  if (a.D == DD && nw == NN) {                            \
+    lds_mfma = KmMfmaCfg<DD, NN>::lds_bytes(Cmax);        \
+    npass = KmMfmaCfg<DD, NN>::passes(Cmax);              \
+  }
+  MUSE_KM_CFG(64, 1) MUSE_KM_CFG(64, 2) MUSE_KM_CFG(64, 3) MUSE_KM_CFG(64, 4)
+  MUSE_KM_CFG(128, 1) MUSE_KM_CFG(128, 2) MUSE_KM_CFG(128, 3) MUSE_KM_CFG(128, 4)
+#undef MUSE_KM_CFG
+  if (mf && npass == 1) {
+    // several tiles per workgroup amortise the centroid tables; about 1024 workgroups
+    const long total = static_cast<long>(a.ntiles) * a.BH * a.ntensors;
+    b.tpg = static_cast<int>(std::min<long>(8, std::max<long>(1, total / 1024)));
+  }
+  b.ngroups = (a.ntiles + b.tpg - 1) / b.tpg;
+  const dim3 g_group(b.ngroups, a.BH, a.ntensors);
   auto launch_mfma = [&](int it) {
     const int last = it == iters - 1;
-    const int nw = a.tile / 64;
-#define MUSE_KM_CASE(DD, NN)                                                                            \
-  if (a.D == DD && nw == NN) {                                                                          \
-    allow_lds((const void*)kmeans_assign_mfma_kernel<DD, NN>, lds_mfma);                               \
-    hipLaunchKernelGGL((kmeans_assign_mfma_kernel<DD, NN>), g_assign, dim3(a.tile), lds_mfma, s, a, it, last); \
+#define MUSE_KM_CASE(DD, NN)                                                                              \
+  if (a.D == DD && nw == NN) {                                                                            \
+    allow_lds((const void*)kmeans_assign_mfma_kernel<DD, NN>, lds_mfma);                                 \
+    hipLaunchKernelGGL((kmeans_assign_mfma_kernel<DD, NN>), g_group, dim3(a.tile), lds_mfma, s, b, it, last); \
   }
     MUSE_KM_CASE(64, 1) MUSE_KM_CASE(64, 2) MUSE_KM_CASE(64, 3) MUSE_KM_CASE(64, 4)
     MUSE_KM_CASE(128, 1) MUSE_KM_CASE(128, 2) MUSE_KM_CASE(128, 3) MUSE_KM_CASE(128, 4)
@@ -589,13 +655,13 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
     } else {
       ProfScope ps_("kmeans_assign", s);
       if (a.D == 64)
-        hipLaunchKernelGGL((kmeans_assign_kernel<T, 64>), g_assign, dim3(a.tile), lds, s, a, it);
+        hipLaunchKernelGGL((kmeans_assign_kernel<T, 64>), g_assign, dim3(a.tile), lds, s, b, it);
       else
-        hipLaunchKernelGGL((kmeans_assign_kernel<T, 128>), g_assign, dim3(a.tile), lds, s, a, it);
+        hipLaunchKernelGGL((kmeans_assign_kernel<T, 128>), g_assign, dim3(a.tile), lds, s, b, it);
     }
     {
       ProfScope ps_("kmeans_update", s);
-      hipLaunchKernelGGL(kmeans_update_kernel, g_update, dim3(64), 0, s, a);
+      hipLaunchKernelGGL(kmeans_update_kernel, g_update, dim3(64), 0, s, b);
     }
   }
   const size_t lds_off = sizeof(int) * static_cast<size_t>(a.nb) * Cmax;

@@ -122,6 +122,7 @@ int validate_muse(Shape& s, const muse_fwd_params* p) {
 struct Plan {
   size_t chi_q, clo_q, cn2_q, chi_k, clo_k, cn2_k;
   size_t cent_q, cent_k, lab_q, lab_k, tperm_q, tperm_k, tcnt_q, tcnt_k, tst_q, tst_k, psum_q, psum_k;
+  size_t gcnt_q, gcnt_k;
   size_t perm_k, offs_k, perm_q, offs_q;
   size_t t_khi, t_klo, t_vthi, t_vtlo, t_dip, tiles, ntiles, tile_base;
   int max_tiles;
@@ -157,6 +158,10 @@ Plan make_plan(const Shape& s, const muse_fwd_params* p) {
   P.tst_k = L.take(BH * nt * Ck * i4);
   P.psum_q = L.take(BH * nt * Cq * D * f);
   P.psum_k = L.take(BH * nt * Ck * D * f);
+  if (s.dtype == MUSE_BF16) {
+    P.gcnt_q = L.take(BH * nt * Cq * i4);
+    P.gcnt_k = L.take(BH * nt * Ck * i4);
+  }
   P.perm_k = L.take(BH * N * i4);
   P.offs_k = L.take(BH * (nb * Ck + 1) * i4);
   P.perm_q = L.take(BH * N * i4);
@@ -238,6 +243,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   tq.tile_cnt = at<int32_t>(ws, P.tcnt_q);
   tq.tile_start = at<int32_t>(ws, P.tst_q);
   tq.psum = at<float>(ws, P.psum_q);
+  tq.gcnt = s.dtype == MUSE_BF16 ? at<int32_t>(ws, P.gcnt_q) : tq.tile_cnt;
   const bool mf = s.dtype == MUSE_BF16;
   const bool retr = p != nullptr && p->topk_clusters > 0;
   // the matrix-core stage 2 and retrieval need the query buckets
@@ -257,6 +263,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   tk.tile_cnt = at<int32_t>(ws, P.tcnt_k);
   tk.tile_start = at<int32_t>(ws, P.tst_k);
   tk.psum = at<float>(ws, P.psum_k);
+  tk.gcnt = s.dtype == MUSE_BF16 ? at<int32_t>(ws, P.gcnt_k) : tk.tile_cnt;
   tk.perm = at<int32_t>(ws, P.perm_k);
   tk.offs = at<int32_t>(ws, P.offs_k);
   hipError_t e = launch_kmeans(km, s.iters, s.dtype, stream);

@@ -23,9 +23,10 @@ struct KmTensor {
   int32_t* trace;              // [iters, BH, N] or null
   const int32_t* labels_in;    // [BH, N] caller-fixed labels or null
   uint16_t* tile_perm;         // [BH, ntiles, tile] tile-local stable order by label
-  int32_t* tile_cnt;           // [BH, ntiles, C]
+  int32_t* tile_cnt;           // [BH, ntiles, C] (last iteration: per-tile counts for bucketing)
   int32_t* tile_start;         // [BH, ntiles, C]
-  float* psum;                 // [BH, ntiles, C, D] per-tile cluster sums
+  float* psum;                 // [BH, ntiles, C, D] cluster sums, one slab per tile group
+  int32_t* gcnt;               // [BH, ntiles, C] cluster counts, one row per tile group
   int32_t* perm;               // [BH, N] points ordered by (block, label, position), or null
   int32_t* offs;               // [BH, nb*C + 1] bucket offsets into perm
 };
@@ -36,6 +37,7 @@ struct KmArgs {
   int BH, N, D;
   int tile, ntiles;            // points per tile, tiles per head
   int nb, tiles_per_block;     // spatial blocks (1 when acausal) and tiles in one
+  int tpg, ngroups;            // tiles per assign workgroup (set by the launcher), groups per head
 };
 
 hipError_t launch_kmeans(const KmArgs& a, int iters, int dtype, hipStream_t s);
