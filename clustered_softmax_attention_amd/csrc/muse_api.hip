@@ -79,18 +79,10 @@ int validate(Shape& s, const muse_fwd_params* p) {
     s.tiles_per_block = (s.N + s.tile - 1) / s.tile;
   }
   s.ntiles = (s.N + s.tile - 1) / s.tile;
-  // moment sub-blocks: the matrix-core kernel splits long key ranges for parallelism
-  if (s.dtype == MUSE_BF16) {
-    s.mbk = 1024;  // largest multiple of 64 that divides the block and is at most 1024
-    if (s.causal)
-      for (int k = 16; k >= 1; --k)
-        if ((s.block / 64) % k == 0) {
-          s.mbk = 64 * k;
-          break;
-        }
-  } else {
-    s.mbk = s.block;
-  }
+  // moment key ranges: a causal block, or for an acausal bf16 call slices of 1024
+  // positions (parallelism for the matrix-core kernel)
+  if (s.dtype == MUSE_BF16 && !s.causal) s.mbk = 1024;
+  else s.mbk = s.block;
   s.nmb = (s.N + s.mbk - 1) / s.mbk;
   if (p != nullptr) {
     if (p->out_dtype != -1 && p->out_dtype != MUSE_F32 && p->out_dtype != MUSE_BF16)

@@ -14,10 +14,10 @@
 //                  the bucket, then sum w k and sum w v as products K_seg^T W^T, with the
 //                  bucket's key/value rows gathered into a transposed LDS tile and the
 //                  weights split into bf16 hi + lo.
-//   s1_moments_f16 per (sub-block, centroid group): weights w = exp(a - max) from the
+//   s1_moments_f16 per (key range, centroid group): weights w = exp(a - max) from the
 //                  scores (no running rescale), then sum_m w_m v_m k_m^T with fp16
-//                  operands (the weights are applied to V^T with packed fp16 multiplies)
-//                  and fp32 accumulation.
+//                  operands (the weights are applied to the value fragments with packed
+//                  fp16 multiplies) and fp32 accumulation.
 #include "mfma.hpp"
 #include "muse_kernels.hpp"
 
@@ -210,136 +210,167 @@ __global__ void __launch_bounds__(256) s1_atoms_mfma_kernel(S1Args a) {
   }
 }
 
-// Sub-block moments with fp16 operands, over consecutive positions of the bucketed order
-// (a causal block is a contiguous range of positions, so sub-blocks never straddle one). D = 64: 8 centroids per workgroup, 2 per wave;
-// D = 128: 2 centroids, each wave half of the 16 output tiles of one centroid.
-// Static LDS: K^T, V^T [D][64+8] fp16 | weights [G][kMaxMbk] fp16 | max, sum [G].
-constexpr int kMaxMbk = 1024;
+// Block moments with fp16 operands over a contiguous range of positions of the bucketed
+// order (a causal block, or a slice of an acausal sequence): one workgroup of 8 waves
+// per (range, group of G centroids, head). Weights w = exp(a - max over the range) come
+// from the scores; every 64-key chunk of K and V rows is gathered once, converted to
+// fp16 (exact for bf16 values in fp16 range) and stored row-major in LDS, where the
+// transpose read hands both MFMA operands over with the key index along k:
+//   sum_m w_m v_m k_m^T = (V^T diag(w)) K,  A = v fragment * w (packed fp16), B = k fragment.
+// D = 64: 16 centroids per workgroup, 2 per wave, all 4 output tiles of each;
+// D = 128: 4 centroids, wave w takes centroid w/2, value tiles 2(w%2)..2(w%2)+1, all
+// 4 key tiles. Output [dv][dk], normalised by the range's weight sum.
+template <int D>
+struct MomCfg {
+  static constexpr int G = D == 64 ? 16 : 4;   // centroids per workgroup
+  static constexpr int CW = D == 64 ? 2 : 1;   // centroids per wave
+  static constexpr int NDV = 2;                // value tiles per wave
+  static constexpr int NDK = D / 32;           // key tiles per wave
+  static constexpr int KC = 64;                // keys per chunk
+  static constexpr int ST = D + 16;            // LDS row stride (fp16 elements)
+  static constexpr int NPRE = KC * (D / 8) / 512;  // 16-byte row pieces per thread and tensor
+  static constexpr int NWQ = (G * KC + 511) / 512;   // chunk weights per thread
+};
 
 template <int D>
-__global__ void __launch_bounds__(256) s1_moments_f16_kernel(S1Args a) {
-  constexpr int KC = 64;
-  constexpr int TST = KC + 8;
-  constexpr int G = D == 64 ? 8 : 2;
-  constexpr int CPW = D == 64 ? 2 : 1;
-  constexpr int NMT = D / 32;
-  constexpr int NNT = 2;
-  __shared__ __align__(16) _Float16 sKt[D * TST];
-  __shared__ __align__(16) _Float16 sVt[D * TST];
-  __shared__ __align__(16) _Float16 sw[G * kMaxMbk];
+__global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
+  using Cfg = MomCfg<D>;
+  constexpr int G = Cfg::G, CW = Cfg::CW, NDV = Cfg::NDV, NDK = Cfg::NDK, KC = Cfg::KC, ST = Cfg::ST;
+  constexpr int NPRE = Cfg::NPRE, NWQ = Cfg::NWQ;
+  __shared__ __align__(16) uint16_t sK[KC * ST];
+  __shared__ __align__(16) uint16_t sV[KC * ST];
+  __shared__ __align__(16) _Float16 sw[G * KC];
   __shared__ float smx[G], ssum[G];
-  __shared__ int s_perm[kMaxMbk];
   const int mb = blockIdx.x, ig = blockIdx.y, bh = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int Cq = a.Cq, i0 = ig * G, ng = min(G, Cq - i0);
   const int key0 = mb * a.mbk, key1 = min(a.N, key0 + a.mbk), nkeys = key1 - key0;
+  const float* S = a.scores + (static_cast<size_t>(bh) * Cq + i0) * a.N + key0;
 
-  // weights: wave w takes centroids g = w, w + 4
-  for (int g = wave; g < G; g += 4) {
-    const float* Sg = a.scores + (static_cast<size_t>(bh) * Cq + i0 + (g < ng ? g : 0)) * a.N + key0;
+  // max of the scores over the range, per centroid (waves over centroids)
+  for (int g = wave; g < G; g += 8) {
     float mx = kNegInf;
-#pragma unroll 8
-    for (int k = lane; k < nkeys; k += 64) mx = fmaxf(mx, Sg[k]);
+    if (g < ng) {
+#pragma unroll 4
+      for (int k = lane; k < nkeys; k += 64) mx = fmaxf(mx, S[static_cast<size_t>(g) * a.N + k]);
+    }
     mx = wave_max(mx);
-    float sum = 0.f;
-#pragma unroll 8
-    for (int k = lane; k < kMaxMbk; k += 64) {
-      const float w = (k < nkeys && g < ng) ? __expf(Sg[k < nkeys ? k : 0] - mx) : 0.f;
-      sw[g * kMaxMbk + k] = static_cast<_Float16>(w);
-      sum += w;
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      smx[g] = mx;
-      ssum[g] = sum;
-    }
+    if (lane == 0) smx[g] = mx;
   }
-  const int wc0 = D == 64 ? 2 * wave : wave / 2;
-  const int nt0 = D == 64 ? 0 : 2 * (wave & 1);
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + key0;
-  for (int k = tid; k < nkeys; k += 256) s_perm[k] = perm[k];
-  f32x16_t acc[CPW][NMT][NNT];
-#pragma unroll
-  for (int cc = 0; cc < CPW; ++cc)
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NNT; ++nt) acc[cc][mt][nt] = zero16();
-
-  // rows of the next 64 positions travel in registers while the current ones are used
-  constexpr int NPRE = KC * (D / 8) / 256;
   u16x8_t pk[NPRE], pv[NPRE];
   auto load_rows = [&](int c0) {
 #pragma unroll
     for (int q = 0; q < NPRE; ++q) {
-      const int x = tid + 256 * q;
-      const int r = x / (D / 8), cc8 = x % (D / 8);
+      const int x = tid + 512 * q;
+      const int r = x / (D / 8), c8 = x % (D / 8);
       pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       pv[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       if (c0 + r < nkeys) {
-        const size_t row = static_cast<size_t>(s_perm[c0 + r]) * D + cc8 * 8;
+        const size_t row = static_cast<size_t>(perm[c0 + r]) * D + c8 * 8;
         pk[q] = *reinterpret_cast<const u16x8_t*>(K + row);
         pv[q] = *reinterpret_cast<const u16x8_t*>(V + row);
       }
     }
   };
-  __syncthreads();  // s_perm, sw complete
-  if (nkeys > 0) load_rows(0);
+  // bf16 -> fp16 of eight values (exact in fp16's normal range)
+  auto to_f16 = [](const u16x8_t& u) {
+    f16x8_t o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = static_cast<_Float16>(bf16_to_f32(u[e]));
+    return __builtin_bit_cast(u16x8_t, o);
+  };
+  load_rows(0);
+  __syncthreads();  // smx
+  float wsum[NWQ];
+#pragma unroll
+  for (int q = 0; q < NWQ; ++q) wsum[q] = 0.f;
+
+  f32x16_t acc[CW][NDV][NDK];
+#pragma unroll
+  for (int cc = 0; cc < CW; ++cc)
+#pragma unroll
+    for (int dv = 0; dv < NDV; ++dv)
+#pragma unroll
+      for (int dk = 0; dk < NDK; ++dk) acc[cc][dv][dk] = zero16();
+  const int gw = D == 64 ? CW * wave : wave / 2;         // first centroid (in the group) of this wave
+  const int dv0 = D == 64 ? 0 : NDV * (wave & 1);        // first value tile of this wave
+
   for (int c0 = 0; c0 < nkeys; c0 += KC) {
-    __syncthreads();
+    // stage the chunk: rows (fp16) and weights
 #pragma unroll
     for (int q = 0; q < NPRE; ++q) {
-      const int x = tid + 256 * q;
-      const int r = x / (D / 8), cc8 = x % (D / 8);
+      const int x = tid + 512 * q;
+      const int r = x / (D / 8), c8 = x % (D / 8);
+      *reinterpret_cast<u16x8_t*>(sK + r * ST + c8 * 8) = to_f16(pk[q]);
+      *reinterpret_cast<u16x8_t*>(sV + r * ST + c8 * 8) = to_f16(pv[q]);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sKt[(cc8 * 8 + e) * TST + r] = static_cast<_Float16>(bf16_to_f32(pk[q][e]));
-        sVt[(cc8 * 8 + e) * TST + r] = static_cast<_Float16>(bf16_to_f32(pv[q][e]));
-      }
+    for (int q = 0; q < NWQ; ++q) {
+      const int x = tid + 512 * q;
+      if (x >= G * KC) break;
+      const int g = x / KC, k = x % KC;
+      float w = 0.f;
+      if (g < ng && c0 + k < nkeys) w = __expf(S[static_cast<size_t>(g) * a.N + c0 + k] - smx[g]);
+      const _Float16 wh = static_cast<_Float16>(w);
+      sw[x] = wh;
+      wsum[q] += static_cast<float>(wh);
     }
     __syncthreads();
-    if (c0 + KC < nkeys) load_rows(c0 + KC);
-    if (wc0 < ng) {
+    if (c0 + KC < nkeys) load_rows(c0 + KC);  // next chunk in flight during this one
+    if (gw < ng) {
 #pragma unroll
       for (int ks = 0; ks < KC / 16; ++ks) {
-        const int kk = 16 * ks + 8 * h;
-        f16x8_t bk[NNT];
+        f16x8_t wr[CW];
 #pragma unroll
-        for (int nt = 0; nt < NNT; ++nt) bk[nt] = *reinterpret_cast<const f16x8_t*>(sKt + (32 * (nt0 + nt) + c) * TST + kk);
+        for (int cc = 0; cc < CW; ++cc) wr[cc] = *reinterpret_cast<const f16x8_t*>(sw + (gw + cc) * KC + 16 * ks + 8 * h);
+        f16x8_t bk[NDK];
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-          const f16x8_t vr = *reinterpret_cast<const f16x8_t*>(sVt + (32 * mt + c) * TST + kk);
+        for (int dk = 0; dk < NDK; ++dk)
+          bk[dk] = __builtin_bit_cast(f16x8_t, lds_operand_tr(sK, ST, 16 * ks, 32 * dk, lane));
 #pragma unroll
-          for (int cc = 0; cc < CPW; ++cc) {
-            const f16x8_t wr = *reinterpret_cast<const f16x8_t*>(sw + (wc0 + cc) * kMaxMbk + c0 + kk);
-            const f16x8_t av = vr * wr;
+        for (int dv = 0; dv < NDV; ++dv) {
+          const f16x8_t vr = __builtin_bit_cast(f16x8_t, lds_operand_tr(sV, ST, 16 * ks, 32 * (dv0 + dv), lane));
 #pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) acc[cc][mt][nt] = mfma32_f16(av, bk[nt], acc[cc][mt][nt]);
+          for (int cc = 0; cc < CW; ++cc) {
+            const f16x8_t av = vr * wr[cc];
+#pragma unroll
+            for (int dk = 0; dk < NDK; ++dk) acc[cc][dv][dk] = mfma32_f16(av, bk[dk], acc[cc][dv][dk]);
           }
         }
       }
     }
+    __syncthreads();  // the next chunk overwrites the tiles
   }
+  // weight sums: the KC threads of one centroid are one wave
 #pragma unroll
-  for (int cc = 0; cc < CPW; ++cc) {
-    const int g = wc0 + cc;
+  for (int q = 0; q < NWQ; ++q) {
+    const int x = tid + 512 * q;
+    if (x >= G * KC) break;  // uniform per wave
+    const float s = wave_sum(wsum[q]);
+    if (lane == 0) ssum[x / KC] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int cc = 0; cc < CW; ++cc) {
+    const int g = gw + cc;
     if (g >= ng) continue;
     const int i = i0 + g;
     const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
     const float sum = ssum[g];
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
-    if (lane == 0 && nt0 == 0) a.blk_lmass[bidx] = sum > 0.f ? smx[g] + __logf(sum) : kNegInf;
+    if (lane == 0 && dv0 == 0) a.blk_lmass[bidx] = sum > 0.f ? smx[g] + __logf(sum) : kNegInf;
     float* out = a.blk_mom + bidx * D * D;
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+    for (int dv = 0; dv < NDV; ++dv)
 #pragma unroll
-      for (int nt = 0; nt < NNT; ++nt)
+      for (int dk = 0; dk < NDK; ++dk)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int dv = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
-          out[static_cast<size_t>(dv) * D + 32 * (nt0 + nt) + c] = acc[cc][mt][nt][v] * inv;
+          const int row = 32 * (dv0 + dv) + 8 * (v >> 2) + 4 * h + (v & 3);
+          out[static_cast<size_t>(row) * D + 32 * dk + c] = acc[cc][dv][dk][v] * inv;
         }
   }
 }
@@ -355,9 +386,9 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
     ProfScope ps_("s1_atoms_mfma", s);
     hipLaunchKernelGGL((s1_atoms_mfma_kernel<D>), dim3((a.nb * a.Ck + 3) / 4, a.BH), dim3(256), 0, s, a);
   } else {
-    constexpr int G = D == 64 ? 8 : 2;
+    constexpr int G = MomCfg<D>::G;
     ProfScope ps_("s1_moments_f16", s);
-    hipLaunchKernelGGL((s1_moments_f16_kernel<D>), dim3(a.nmb, (a.Cq + G - 1) / G, a.BH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((s1_moments_f16_kernel<D>), dim3(a.nmb, (a.Cq + G - 1) / G, a.BH), dim3(512), 0, s, a);
   }
 }
 
