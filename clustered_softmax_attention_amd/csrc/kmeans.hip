@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_kernel(KmArgs a, int i
 //
 // Cluster sums psum^T [D x C] = X^T onehot run on the matrix cores too: the tile's rows
 // sit row-major in LDS and reach the A operand through the transpose read; the one-hot
-// B operand is built from the tile's labels with packed 16-bit compares. Wave w owns a
+// B operand is built from the tile's labels with packed 16-bit integer operations. Wave w owns a
 // fixed set of output tiles (one cluster tile and all D/32 feature tiles when NW = 4),
 // accumulated over all tiles of the group and written once.
 //
@@ -248,24 +248,26 @@ struct KmMfmaCfg {
   static int passes(int Cmax) { return ((Cmax + 31) / 32 + NW * CPW - 1) / (NW * CPW); }
 };
 
-__device__ __forceinline__ bf16x8_t onehot_bf16x8(const u16x8_t& lab8, unsigned j) {
-  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-  const u16x2 jj = {static_cast<unsigned short>(j), static_cast<unsigned short>(j)};
-  const u16x2 one = {1, 1}, val = {0x3F80, 0x3F80};
-  u16x8_t o;
+// bf16 one-hot of eight 16-bit labels against label j: per 16-bit half,
+// m = min(lab ^ j, 1) is 0 exactly where lab == j, and 0x3F80 - 0x3F80 m is bf16 1.0
+// there and 0 elsewhere (labels and j are below 2^15).
+__device__ __forceinline__ bf16x8_t onehot_bf16x8(const u16x8_t& lab8, uint32_t jj, uint32_t one2, uint32_t neg2,
+                                                  uint32_t val2) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(&lab8);
+  uint32_t o[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const u16x2 pr = {lab8[2 * q], lab8[2 * q + 1]};
-    const u16x2 m = __builtin_elementwise_min(pr ^ jj, one);  // 0 where the label is j
-    const u16x2 r = (one - m) * val;
-    o[2 * q] = r[0];
-    o[2 * q + 1] = r[1];
+    uint32_t m;
+    asm volatile("v_xor_b32 %0, %1, %2\n\tv_pk_min_u16 %0, %0, %3\n\tv_pk_mad_u16 %0, %0, %4, %5"
+                 : "=&v"(m)
+                 : "v"(p[q]), "v"(jj), "v"(one2), "v"(neg2), "v"(val2));
+    o[q] = m;
   }
-  return as_bf16x8(o);
+  return __builtin_bit_cast(bf16x8_t, o);
 }
 
 template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW) kmeans_assign_mfma_kernel(KmArgs a, int iter, int last) {
+__global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_assign_mfma_kernel(KmArgs a, int iter, int last) {
   extern __shared__ __align__(16) unsigned char smem[];
   using Cfg = KmMfmaCfg<D, NW>;
   constexpr int NKS = Cfg::NKS, XST = Cfg::XST, NDT = Cfg::NDT, TILE = Cfg::TILE, CPW = Cfg::CPW, OPW = Cfg::OPW;
@@ -273,7 +275,7 @@ __global__ void __launch_bounds__(64 * NW) kmeans_assign_mfma_kernel(KmArgs a, i
   const KmTensor& t = a.t[blockIdx.z];
   const int C = t.C, Cp = (C + 31) & ~31, njt = Cp / 32;
   const int grp = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int tt0 = grp * a.tpg, tt1 = min(a.ntiles, tt0 + a.tpg);
   uint16_t* chi = reinterpret_cast<uint16_t*>(smem);
   uint16_t* clo = chi + Cp * D;
@@ -390,21 +392,26 @@ __global__ void __launch_bounds__(64 * NW) kmeans_assign_mfma_kernel(KmArgs a, i
       }
       float best[2] = {kNegInf, kNegInf}, second[2] = {kNegInf, kNegInf};
       int slot[2] = {0, 0};
+      // tile jt + 1 is on the matrix cores while tile jt is ranked
+      f32x16_t sa0, sa1, sb0, sb1;
+      score_tile(0, sa0, sa1);
 #pragma unroll
       for (int jt = 0; jt < MAXJT; ++jt) {
         if (jt < njt) {
-          f32x16_t s0, s1;
-          score_tile(jt, s0, s1);
+          if (jt + 1 < MAXJT && jt + 1 < njt) score_tile(jt + 1, sb0, sb1);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const float x0 = s0[v], x1 = s1[v];
-            slot[0] = x0 > best[0] ? 16 * jt + v : slot[0];
+            const float x0 = sa0[v], x1 = sa1[v];
+            const bool g0 = x0 > best[0], g1 = x1 > best[1];
+            slot[0] = g0 ? 16 * jt + v : slot[0];
             second[0] = __builtin_amdgcn_fmed3f(best[0], second[0], x0);
-            best[0] = fmaxf(best[0], x0);
-            slot[1] = x1 > best[1] ? 16 * jt + v : slot[1];
+            best[0] = g0 ? x0 : best[0];
+            slot[1] = g1 ? 16 * jt + v : slot[1];
             second[1] = __builtin_amdgcn_fmed3f(best[1], second[1], x1);
-            best[1] = fmaxf(best[1], x1);
+            best[1] = g1 ? x1 : best[1];
           }
+          sa0 = sb0;
+          sa1 = sb1;
         }
       }
       int bj[2];
@@ -418,11 +425,11 @@ __global__ void __launch_bounds__(64 * NW) kmeans_assign_mfma_kernel(KmArgs a, i
         const float os = __shfl_xor(second[gi], 32, 64);
         const int oj = __shfl_xor(bj[gi], 32, 64);
         if (ob > best[gi] || (ob == best[gi] && oj < bj[gi])) {
-          second[gi] = fmaxf(best[gi], os);
+          second[gi] = best[gi] > os ? best[gi] : os;
           best[gi] = ob;
           bj[gi] = oj;
         } else {
-          second[gi] = fmaxf(second[gi], ob);
+          second[gi] = second[gi] > ob ? second[gi] : ob;
         }
         // distance error bound E; scores carry half of it
         E[gi] = 1e-4f * sqrtf(xx[gi]) * cmax + 2e-5f * cmax2;
@@ -486,17 +493,23 @@ __global__ void __launch_bounds__(64 * NW) kmeans_assign_mfma_kernel(KmArgs a, i
         for (int r = 0; r < OPW; ++r) acc[r] = zero16();
       }
       const int ct0 = (pass * NW + wave) * CPW;
-      for (int ks = 0; ks < TILE / 16; ++ks) {
-        const u16x8_t lab8 = *reinterpret_cast<const u16x8_t*>(slab + 16 * ks + 8 * h);
+      const int nct = min(CPW, njt - ct0);  // uniform; may be <= 0
+      if (nct > 0) {
+        uint32_t jj[CPW];
 #pragma unroll
-        for (int rc = 0; rc < CPW; ++rc) {
-          const int ct = ct0 + rc;
-          if (ct >= njt) break;
-          const bf16x8_t oh = onehot_bf16x8(lab8, 32 * ct + c);
+        for (int rc = 0; rc < CPW; ++rc) jj[rc] = (32u * (ct0 + rc) + c) * 0x10001u;
+        const uint32_t one2 = 0x00010001u, neg2 = 0xC080C080u, val2 = 0x3F803F80u;
+        for (int ks = 0; ks < TILE / 16; ++ks) {
+          const u16x8_t lab8 = *reinterpret_cast<const u16x8_t*>(slab + 16 * ks + 8 * h);
+          bf16x8_t ax[NDT];
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8_t ax = lds_operand_tr(sX, XST, 16 * ks, 32 * dt, lane);
-            acc[rc * NDT + dt] = mfma32(ax, oh, acc[rc * NDT + dt]);
+          for (int dt = 0; dt < NDT; ++dt) ax[dt] = lds_operand_tr(sX, XST, 16 * ks, 32 * dt, lane);
+#pragma unroll
+          for (int rc = 0; rc < CPW; ++rc) {
+            if (rc > 0 && rc >= nct) break;
+            const bf16x8_t oh = onehot_bf16x8(lab8, jj[rc], one2, neg2, val2);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[rc * NDT + dt] = mfma32(ax[dt], oh, acc[rc * NDT + dt]);
           }
         }
       }
@@ -631,9 +644,9 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
   MUSE_KM_CFG(128, 1) MUSE_KM_CFG(128, 2) MUSE_KM_CFG(128, 3) MUSE_KM_CFG(128, 4)
 #undef MUSE_KM_CFG
   if (mf && npass == 1) {
-    // several tiles per workgroup amortise the centroid tables; about 1024 workgroups
+    // several tiles per workgroup amortise the centroid tables; about 512 workgroups
     const long total = static_cast<long>(a.ntiles) * a.BH * a.ntensors;
-    b.tpg = static_cast<int>(std::min<long>(8, std::max<long>(1, total / 1024)));
+    b.tpg = static_cast<int>(std::min<long>(8, std::max<long>(1, total / 512)));
   }
   b.ngroups = (a.ntiles + b.tpg - 1) / b.tpg;
   const dim3 g_group(b.ngroups, a.BH, a.ntensors);

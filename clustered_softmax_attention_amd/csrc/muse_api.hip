@@ -79,10 +79,20 @@ int validate(Shape& s, const muse_fwd_params* p) {
     s.tiles_per_block = (s.N + s.tile - 1) / s.tile;
   }
   s.ntiles = (s.N + s.tile - 1) / s.tile;
-  // moment key ranges: a causal block, or for an acausal bf16 call slices of 1024
-  // positions (parallelism for the matrix-core kernel)
-  if (s.dtype == MUSE_BF16 && !s.causal) s.mbk = 1024;
-  else s.mbk = s.block;
+  // moment key ranges: a causal block (split into equal ranges of at most kMaxMomKeys
+  // positions for the matrix-core kernel), or for an acausal bf16 call slices of 1024
+  // positions (parallelism)
+  if (s.dtype == MUSE_BF16 && !s.causal) {
+    s.mbk = 1024;
+  } else {
+    s.mbk = s.block;
+    if (s.dtype == MUSE_BF16)
+      for (int k = s.block / 64; k >= 1; --k)
+        if ((s.block / 64) % k == 0 && 64 * k <= muse::kMaxMomKeys) {
+          s.mbk = 64 * k;
+          break;
+        }
+  }
   s.nmb = (s.N + s.mbk - 1) / s.mbk;
   if (p != nullptr) {
     if (p->out_dtype != -1 && p->out_dtype != MUSE_F32 && p->out_dtype != MUSE_BF16)

@@ -9,6 +9,7 @@ constexpr int kChunkC = 32;    // centroids staged in LDS at a time by the fp32 
 constexpr int kMaxTile = 512;  // K-means tile (points per workgroup) upper bound, fp32 path
 constexpr int kMaxTileMfma = 256;  // the same for the matrix-core (bf16) path
 constexpr int kMaxClusters = 128;
+constexpr int kMaxMomKeys = 8192;  // positions per block-moment range (matrix-core path)
 
 // ------------------------------------------------------------------ K-means
 

@@ -211,9 +211,10 @@ __global__ void __launch_bounds__(256) s1_atoms_mfma_kernel(S1Args a) {
 }
 
 // Block moments with fp16 operands over a contiguous range of positions of the bucketed
-// order (a causal block, or a slice of an acausal sequence): one workgroup of 8 waves
+// order (a causal block, or a slice of an acausal sequence; at most kMaxMomKeys
+// positions, whose permutation entries are staged in LDS): one workgroup of 8 waves
 // per (range, group of G centroids, head). Weights w = exp(a - max over the range) come
-// from the scores; every 64-key chunk of K and V rows is gathered once, converted to
+// from the scores; every 128-key chunk of K and V rows is gathered once, converted to
 // fp16 (exact for bf16 values in fp16 range) and stored row-major in LDS, where the
 // transpose read hands both MFMA operands over with the key index along k:
 //   sum_m w_m v_m k_m^T = (V^T diag(w)) K,  A = v fragment * w (packed fp16), B = k fragment.
@@ -226,7 +227,7 @@ struct MomCfg {
   static constexpr int CW = D == 64 ? 2 : 1;   // centroids per wave
   static constexpr int NDV = 2;                // value tiles per wave
   static constexpr int NDK = D / 32;           // key tiles per wave
-  static constexpr int KC = 64;                // keys per chunk
+  static constexpr int KC = 128;               // keys per chunk
   static constexpr int ST = D + 16;            // LDS row stride (fp16 elements)
   static constexpr int NPRE = KC * (D / 8) / 512;  // 16-byte row pieces per thread and tensor
   static constexpr int NWQ = (G * KC + 511) / 512;   // chunk weights per thread
@@ -240,12 +241,15 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
   __shared__ __align__(16) uint16_t sK[KC * ST];
   __shared__ __align__(16) uint16_t sV[KC * ST];
   __shared__ __align__(16) _Float16 sw[G * KC];
-  __shared__ float smx[G], ssum[G];
+  __shared__ int s_perm[kMaxMomKeys];
+  __shared__ float smx[G], ssum[G], spart[G * KC / 64];
   const int mb = blockIdx.x, ig = blockIdx.y, bh = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
   const int Cq = a.Cq, i0 = ig * G, ng = min(G, Cq - i0);
   const int key0 = mb * a.mbk, key1 = min(a.N, key0 + a.mbk), nkeys = key1 - key0;
   const float* S = a.scores + (static_cast<size_t>(bh) * Cq + i0) * a.N + key0;
+  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + key0;
+  for (int k = tid; k < nkeys; k += 512) s_perm[k] = perm[k];
 
   // max of the scores over the range, per centroid (waves over centroids)
   for (int g = wave; g < G; g += 8) {
@@ -259,9 +263,10 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
   }
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
-  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + key0;
+  // the next chunk's rows and scores travel in registers while the current one is used
   u16x8_t pk[NPRE], pv[NPRE];
-  auto load_rows = [&](int c0) {
+  float ps[NWQ];
+  auto load_chunk = [&](int c0) {
 #pragma unroll
     for (int q = 0; q < NPRE; ++q) {
       const int x = tid + 512 * q;
@@ -269,10 +274,17 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
       pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       pv[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       if (c0 + r < nkeys) {
-        const size_t row = static_cast<size_t>(perm[c0 + r]) * D + c8 * 8;
+        const size_t row = static_cast<size_t>(s_perm[c0 + r]) * D + c8 * 8;
         pk[q] = *reinterpret_cast<const u16x8_t*>(K + row);
         pv[q] = *reinterpret_cast<const u16x8_t*>(V + row);
       }
+    }
+#pragma unroll
+    for (int q = 0; q < NWQ; ++q) {
+      const int x = tid + 512 * q;
+      const int g = x / KC, k = x % KC;
+      ps[q] = kNegInf;
+      if (x < G * KC && g < ng && c0 + k < nkeys) ps[q] = S[static_cast<size_t>(g) * a.N + c0 + k];
     }
   };
   // bf16 -> fp16 of eight values (exact in fp16's normal range)
@@ -282,8 +294,8 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
     for (int e = 0; e < 8; ++e) o[e] = static_cast<_Float16>(bf16_to_f32(u[e]));
     return __builtin_bit_cast(u16x8_t, o);
   };
-  load_rows(0);
-  __syncthreads();  // smx
+  __syncthreads();  // s_perm, smx
+  load_chunk(0);
   float wsum[NWQ];
 #pragma unroll
   for (int q = 0; q < NWQ; ++q) wsum[q] = 0.f;
@@ -311,15 +323,13 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
     for (int q = 0; q < NWQ; ++q) {
       const int x = tid + 512 * q;
       if (x >= G * KC) break;
-      const int g = x / KC, k = x % KC;
-      float w = 0.f;
-      if (g < ng && c0 + k < nkeys) w = __expf(S[static_cast<size_t>(g) * a.N + c0 + k] - smx[g]);
-      const _Float16 wh = static_cast<_Float16>(w);
+      const int g = x / KC;
+      const _Float16 wh = static_cast<_Float16>(ps[q] == kNegInf ? 0.f : __expf(ps[q] - smx[g]));
       sw[x] = wh;
       wsum[q] += static_cast<float>(wh);
     }
     __syncthreads();
-    if (c0 + KC < nkeys) load_rows(c0 + KC);  // next chunk in flight during this one
+    if (c0 + KC < nkeys) load_chunk(c0 + KC);  // next chunk in flight during this one
     if (gw < ng) {
 #pragma unroll
       for (int ks = 0; ks < KC / 16; ++ks) {
@@ -344,15 +354,23 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
     }
     __syncthreads();  // the next chunk overwrites the tiles
   }
-  // weight sums: the KC threads of one centroid are one wave
+  // weight sums: per wave (64 consecutive weights of one centroid), then per centroid
+  // in wave order
 #pragma unroll
   for (int q = 0; q < NWQ; ++q) {
     const int x = tid + 512 * q;
     if (x >= G * KC) break;  // uniform per wave
-    const float s = wave_sum(wsum[q]);
-    if (lane == 0) ssum[x / KC] = s;
+    const float sp = wave_sum(wsum[q]);
+    if (lane == 0) spart[x / 64] = sp;
   }
   __syncthreads();
+  if (tid < G) {
+    float sum = 0.f;
+    for (int p = 0; p < KC / 64; ++p) sum += spart[tid * (KC / 64) + p];
+    ssum[tid] = sum;
+  }
+  __syncthreads();
+  const int c = lane & 31;
 #pragma unroll
   for (int cc = 0; cc < CW; ++cc) {
     const int g = gw + cc;
