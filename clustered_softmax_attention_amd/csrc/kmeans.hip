@@ -221,7 +221,9 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_kernel(KmArgs a, int i
 // wave scores its 64 points as two 32-point groups that share every centroid fragment.
 // A running best, second best (med3) and best slot are kept per lane, then merged with
 // the partner lane l^32. An error of E in distance is E/2 in score; a second centroid
-// within E of the best (2E in distance) sends the point to the exact fp32 rescoring.
+// within E of the best (2E in distance) sends the point to the exact rescoring, where
+// the whole wave computes the fp32 direct-form distance of each candidate (lanes over
+// d, fixed-order tree sum).
 //
 // Cluster sums psum^T [D x C] = X^T onehot run on the matrix cores too: the tile's rows
 // sit row-major in LDS and reach the A operand through the transpose read; the one-hot
@@ -436,42 +438,51 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
         const long p = static_cast<long>(tt) * TILE + wave * 64 + gi * 32 + c;
         need[gi] = p < a.N && second[gi] >= best[gi] - E[gi];
       }
-      // a second centroid within the window: re-score every candidate exactly (fp32 direct form)
+      // a second centroid within the window: re-score every candidate exactly, fp32
+      // direct form sum_d (x_d - c_jd)^2 with lanes over d and a fixed-order tree sum
       if (__ballot(need[0] || need[1]) != 0ull) {
-        float fb[2] = {__builtin_huge_valf(), __builtin_huge_valf()};
-        int fj[2] = {C, C};
+        uint64_t cm[2] = {0ull, 0ull};  // candidate slots 16 jt + v of this lane
         for (int jt = 0; jt < njt; ++jt) {
           f32x16_t s0, s1;
           score_tile(jt, s0, s1);
 #pragma unroll
-          for (int gi = 0; gi < 2; ++gi) {
-            if (!need[gi]) continue;
-            const long p = static_cast<long>(tt) * TILE + wave * 64 + gi * 32 + c;
-            const uint16_t* xr = X + static_cast<size_t>(p) * D;
-            const float thr = best[gi] - E[gi];
+          for (int v = 0; v < 16; ++v) {
+            if (need[0] && s0[v] >= best[0] - E[0]) cm[0] |= 1ull << (16 * jt + v);
+            if (need[1] && s1[v] >= best[1] - E[1]) cm[1] |= 1ull << (16 * jt + v);
+          }
+        }
+        float fb[2] = {__builtin_huge_valf(), __builtin_huge_valf()};
+        int fj[2] = {C, C};
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              if ((gi == 0 ? s0[v] : s1[v]) < thr) continue;
-              const int j = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
+        for (int gi = 0; gi < 2; ++gi) {
+          uint64_t lanes = __ballot(cm[gi] != 0ull);
+          while (lanes != 0ull) {
+            const int L = __ffsll(static_cast<unsigned long long>(lanes)) - 1;
+            lanes &= lanes - 1;
+            const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(cm[gi]), L);
+            const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(cm[gi] >> 32), L);
+            uint64_t m = (static_cast<uint64_t>(hi) << 32) | lo;
+            const int cL = L & 31, hL = L >> 5;
+            const uint16_t* xr = sX + (wave * 64 + gi * 32 + cL) * XST;
+            while (m != 0ull) {
+              const int sl = __ffsll(static_cast<unsigned long long>(m)) - 1;
+              m &= m - 1;
+              const int j = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * hL + (sl & 3);
               const float* cr = cent + static_cast<size_t>(j) * D;
-              float dist = 0.f;
-              for (int d = 0; d < D; ++d) {
+              float part = 0.f;
+#pragma unroll
+              for (int d = lane; d < D; d += 64) {
                 const float diff = bf16_to_f32(xr[d]) - cr[d];
-                dist = fmaf(diff, diff, dist);
+                part = fmaf(diff, diff, part);
               }
-              if (dist < fb[gi] || (dist == fb[gi] && j < fj[gi])) {
+              const float dist = wave_sum(part);
+              if (c == cL && (dist < fb[gi] || (dist == fb[gi] && j < fj[gi]))) {
                 fb[gi] = dist;
                 fj[gi] = j;
               }
             }
           }
-        }
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          const float ob = __shfl_xor(fb[gi], 32, 64);
-          const int oj = __shfl_xor(fj[gi], 32, 64);
-          if (ob < fb[gi] || (ob == fb[gi] && oj < fj[gi])) fj[gi] = oj;
-          if (need[gi]) bj[gi] = fj[gi];
+          if (need[gi] && fj[gi] < C) bj[gi] = fj[gi];
         }
       }
       if (valid) lab = h == 0 ? bj[0] : bj[1];

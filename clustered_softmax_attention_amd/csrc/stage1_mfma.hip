@@ -393,6 +393,177 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
   }
 }
 
+// Acausal tables for the matrix-core stage 2 in one pass: one workgroup (4 waves) per
+// (query centroid i, head). From the atoms of the single key block and the moment
+// slices it writes log Z_ij, the bf16 hi/lo tables of K_ij (row-major) and V_ij
+// (transposed), and s * D_i with
+//   D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T,
+// E_i[v k^T] the mass-weighted mean of the slice moments, preset (negated) in the
+// accumulator layout, and sum_j P_ij V_ij K_ij^T on the matrix cores with both operands
+// split into bf16 hi + lo (hi.hi + hi.lo + lo.hi) and read through the transpose read
+// from row-major LDS tiles of 64 key clusters.
+template <int D>
+__global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
+  constexpr int JC = 64;
+  constexpr int ST = D + 16;
+  constexpr int NDT = D / 32;
+  constexpr int TPW = NDT * NDT / 4;  // dipole output tiles per wave
+  __shared__ __align__(16) uint16_t sKh[JC * ST];
+  __shared__ __align__(16) uint16_t sKl[JC * ST];
+  __shared__ __align__(16) uint16_t sVh[JC * ST];
+  __shared__ __align__(16) uint16_t sVl[JC * ST];
+  __shared__ __align__(16) float sP[kMaxClusters];
+  __shared__ float red[8];
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int Cq = a.Cq, Ck = a.Ck;
+  const size_t sidx = static_cast<size_t>(bh) * Cq + i;  // one table entry per (head, i)
+  const size_t aidx0 = sidx * Ck;                         // atoms of the single block
+
+  // log Z_ij and P_ij = softmax_j log Z_ij
+  float lz = kNegInf;
+  if (tid < Ck) {
+    const float m = a.at_m[aidx0 + tid], z = a.at_z[aidx0 + tid];
+    lz = z > 0.f ? m + __logf(z) : kNegInf;
+    a.s_logz[sidx * Ck + tid] = lz;
+  }
+  float mx = wave_max(lz);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float p = (tid < Ck && lz != kNegInf) ? __expf(lz - mx) : 0.f;
+  const float ps = wave_sum(p);
+  __syncthreads();
+  if (lane == 0) red[wave] = ps;
+  __syncthreads();
+  const float psum = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid < kMaxClusters) sP[tid] = psum > 0.f ? p / psum : 0.f;
+
+  // -E_i[v k^T] in the accumulator layout: rows dv = 32 dvt + 8 (v/4) + 4 h + v%4, col dk = 32 dkt + c
+  f32x16_t acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = zero16();
+  if (a.dipole) {
+    float Rm = kNegInf;
+    for (int mb = 0; mb < a.nmb; ++mb) Rm = fmaxf(Rm, a.blk_lmass[(static_cast<size_t>(bh) * a.nmb + mb) * Cq + i]);
+    float ws = 0.f;
+    for (int mb = 0; mb < a.nmb; ++mb) {
+      const float R = a.blk_lmass[(static_cast<size_t>(bh) * a.nmb + mb) * Cq + i];
+      ws += R == kNegInf ? 0.f : __expf(R - Rm);
+    }
+    const float winv = ws > 0.f ? 1.f / ws : 0.f;
+    for (int mb = 0; mb < a.nmb; ++mb) {
+      const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
+      const float R = a.blk_lmass[bidx];
+      if (R == kNegInf) continue;
+      const float w = __expf(R - Rm) * winv;
+      const float* M = a.blk_mom + bidx * D * D;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = 32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3);
+          acc[t][v] = fmaf(-w, M[static_cast<size_t>(row) * D + 32 * dkt + c], acc[t][v]);
+        }
+      }
+    }
+  }
+
+  for (int j0 = 0; j0 < Ck; j0 += JC) {
+    __syncthreads();  // sP complete / previous chunk consumed
+    // normalised K_ij, V_ij of this chunk: global K tables, LDS hi/lo tiles
+    for (int e = tid; e < JC * D / 4; e += 256) {
+      const int jj = e / (D / 4), d4 = (e % (D / 4)) * 4, j = j0 + jj;
+      float kk[4] = {0.f, 0.f, 0.f, 0.f}, vv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (j < Ck) {
+        const float z = a.at_z[aidx0 + j];
+        const float inv = z > 0.f ? 1.f / z : 0.f;
+        const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(a.at_k + (aidx0 + j) * D + d4);
+        const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(a.at_v + (aidx0 + j) * D + d4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          kk[q] = k4[q] * inv;
+          vv[q] = v4[q] * inv;
+        }
+      }
+      u16x4_t kh, kl, vh, vl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        kh[q] = f32_to_bf16_bits(kk[q]);
+        kl[q] = f32_to_bf16_bits(kk[q] - bf16_to_f32(kh[q]));
+        vh[q] = f32_to_bf16_bits(vv[q]);
+        vl[q] = f32_to_bf16_bits(vv[q] - bf16_to_f32(vh[q]));
+      }
+      if (j < Ck) {
+        *reinterpret_cast<u16x4_t*>(a.t_khi + (sidx * Ck + j) * D + d4) = kh;
+        *reinterpret_cast<u16x4_t*>(a.t_klo + (sidx * Ck + j) * D + d4) = kl;
+      }
+      *reinterpret_cast<u16x4_t*>(sKh + jj * ST + d4) = kh;
+      *reinterpret_cast<u16x4_t*>(sKl + jj * ST + d4) = kl;
+      *reinterpret_cast<u16x4_t*>(sVh + jj * ST + d4) = vh;
+      *reinterpret_cast<u16x4_t*>(sVl + jj * ST + d4) = vl;
+    }
+    __syncthreads();
+    // V_ij transposed: eight consecutive j of one d per lane through the transpose read
+    for (int pr = wave; pr < NDT * (JC / 16); pr += 4) {
+      const int dt = pr % NDT, ks = pr / NDT;
+      const int jb = j0 + 16 * ks + 8 * h, d = 32 * dt + c;
+      const bf16x8_t th = lds_operand_tr(sVh, ST, 16 * ks, 32 * dt, lane);
+      const bf16x8_t tl = lds_operand_tr(sVl, ST, 16 * ks, 32 * dt, lane);
+      uint16_t* oh = a.t_vthi + (sidx * D + d) * Ck + jb;
+      uint16_t* ol = a.t_vtlo + (sidx * D + d) * Ck + jb;
+      if (jb + 8 <= Ck && (Ck & 7) == 0) {
+        *reinterpret_cast<u16x8_t*>(oh) = __builtin_bit_cast(u16x8_t, th);
+        *reinterpret_cast<u16x8_t*>(ol) = __builtin_bit_cast(u16x8_t, tl);
+      } else {
+        const u16x8_t uh = __builtin_bit_cast(u16x8_t, th), ul = __builtin_bit_cast(u16x8_t, tl);
+        for (int e = 0; e < 8 && jb + e < Ck; ++e) {
+          oh[e] = uh[e];
+          ol[e] = ul[e];
+        }
+      }
+    }
+    // sum_j P_ij V_ij K_ij^T over the chunk
+    if (a.dipole) {
+#pragma unroll
+      for (int ks = 0; ks < JC / 16; ++ks) {
+        const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(sP + j0 + 16 * ks + 8 * h);
+        const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(sP + j0 + 16 * ks + 8 * h + 4);
+        const float pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
+          const u16x8_t vh = __builtin_bit_cast(u16x8_t, lds_operand_tr(sVh, ST, 16 * ks, 32 * dvt, lane));
+          const u16x8_t vl = __builtin_bit_cast(u16x8_t, lds_operand_tr(sVl, ST, 16 * ks, 32 * dvt, lane));
+          float av[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) av[e] = (bf16_to_f32(vh[e]) + bf16_to_f32(vl[e])) * pw[e];
+          bf16x8_t ah, al;
+          split_bf16x8(av, ah, al);
+          const bf16x8_t kh = lds_operand_tr(sKh, ST, 16 * ks, 32 * dkt, lane);
+          const bf16x8_t kl = lds_operand_tr(sKl, ST, 16 * ks, 32 * dkt, lane);
+          acc[t] = mfma32(ah, kh, acc[t]);
+          acc[t] = mfma32(ah, kl, acc[t]);
+          acc[t] = mfma32(al, kh, acc[t]);
+        }
+      }
+    }
+  }
+  if (a.dipole) {
+    // acc = sum P V K^T - E = -D_i
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3);
+        a.t_dip[(sidx * D + row) * D + 32 * dkt + c] = f32_to_bf16_bits(-a.scale * acc[t][v]);
+      }
+    }
+  }
+}
+
 template <int D>
 static void launch_t(const S1Args& a, int which, hipStream_t s) {
   if (which == 0) {
@@ -403,14 +574,17 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
   } else if (which == 1) {
     ProfScope ps_("s1_atoms_mfma", s);
     hipLaunchKernelGGL((s1_atoms_mfma_kernel<D>), dim3((a.nb * a.Ck + 3) / 4, a.BH), dim3(256), 0, s, a);
-  } else {
+  } else if (which == 2) {
     constexpr int G = MomCfg<D>::G;
     ProfScope ps_("s1_moments_f16", s);
     hipLaunchKernelGGL((s1_moments_f16_kernel<D>), dim3(a.nmb, (a.Cq + G - 1) / G, a.BH), dim3(512), 0, s, a);
+  } else {
+    ProfScope ps_("s1_finalize", s);
+    hipLaunchKernelGGL((s1_finalize_acausal_kernel<D>), dim3(a.Cq, a.BH), dim3(256), 0, s, a);
   }
 }
 
-// which: 0 scores, 1 atoms, 2 moments
+// which: 0 scores, 1 atoms, 2 moments, 3 acausal table finalise
 void launch_stage1_mfma(const S1Args& a, int which, hipStream_t s) {
   if (a.D == 64) launch_t<64>(a, which, s);
   else launch_t<128>(a, which, s);
