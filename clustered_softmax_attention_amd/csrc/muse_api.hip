@@ -192,7 +192,7 @@ Plan make_plan(const Shape& s, const muse_fwd_params* p) {
     P.t_vthi = L.take(BH * nbS * Cq * Ck * D * h2);
     P.t_vtlo = L.take(BH * nbS * Cq * Ck * D * h2);
     P.t_dip = L.take(BH * nbS * Cq * D * D * h2);
-    P.max_tiles = static_cast<int>((N + 31) / 32 + nb * Cq);
+    P.max_tiles = static_cast<int>((N + 127) / 128 + nb * Cq);  // 128-query chunks of the buckets
     P.tiles = L.take(BH * P.max_tiles * 2 * i4);
     P.ntiles = L.take(BH * i4);
     P.tile_base = L.take(BH * (nb * Cq + 1) * i4);

@@ -144,7 +144,7 @@ struct S2Args {
   const int32_t* perm_q;       // [BH, N] queries by (block, label)
   const int32_t* offs_q;       // [BH, nb*Cq + 1]
   int nb;                      // query blocks (1 when acausal)
-  int2* tiles;                 // [BH, max_tiles] (bucket, first position) of 32-query tiles
+  int2* tiles;                 // [BH, max_tiles] (bucket, first position) of 128-query chunks
   int32_t* ntiles;             // [BH]
   int32_t* tile_base;          // [BH, nb*Cq + 1] scratch: first tile of every bucket
   int max_tiles;

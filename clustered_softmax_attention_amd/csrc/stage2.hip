@@ -6,8 +6,8 @@
 // causal calls, 0 otherwise):
 //   l_j = log Z_ij + s qt . K_ij,   p = softmax_j(l),   L_n = logsumexp_j l_j,
 //   o_n = sum_j p_j V_ij + s D_i qt.
-// bf16 inputs (s2_mfma): queries are bucketed by (block, cluster) and cut into tiles
-// of 32; one wave per tile computes on the matrix cores
+// bf16 inputs (s2_mfma): queries are bucketed by (block, cluster) and cut into chunks
+// of up to 128 (a workgroup; 32 per wave); on the matrix cores
 //   l^T = K_i qt^T (Ck x 32), P = softmax over the Ck rows, O^T = V_i^T P^T + (s D_i) qt^T,
 // with K_i, qt, V_i and P split into bf16 hi + lo parts (three products hi*hi, hi*lo,
 // lo*hi; error ~2^-16 relative) and the dipole product in plain bf16 (a small term).
@@ -20,6 +20,7 @@
 namespace muse {
 
 constexpr int kS2Threads = 128;
+constexpr int kS2Chunk = 128;  // queries per matrix-core stage-2 workgroup
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kS2Threads) s2_refine_kernel(S2Args a) {
@@ -107,48 +108,70 @@ __global__ void __launch_bounds__(kS2Threads) s2_refine_kernel(S2Args a) {
   }
 }
 
-// One workgroup per head: tiles of at most 32 consecutive queries inside one
-// (block, cluster) bucket of the query permutation.
-__global__ void s2_tiles_kernel(S2Args a) {
-  const int bh = blockIdx.x;
+// One workgroup per head: chunks of at most kS2Chunk consecutive queries inside one
+// (block, cluster) bucket of the query permutation. Per-bucket chunk counts are scanned
+// in parallel (threads over consecutive buckets, then a scan of the thread totals).
+__global__ void __launch_bounds__(256) s2_tiles_kernel(S2Args a) {
+  __shared__ int s_tot[256];
+  const int bh = blockIdx.x, tid = threadIdx.x;
   const int nbk = a.nb * a.Cq;
   const int32_t* offs = a.offs_q + static_cast<size_t>(bh) * (nbk + 1);
   int2* tiles = a.tiles + static_cast<size_t>(bh) * a.max_tiles;
-  int* s_base = a.tile_base + static_cast<size_t>(bh) * (nbk + 1);
-  // per-bucket tile counts, scanned by one thread (a few thousand buckets at most in practice)
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int u = 0; u < nbk; ++u) {
-      s_base[u] = run;
-      run += (offs[u + 1] - offs[u] + 31) / 32;
-    }
-    s_base[nbk] = run;
-    a.ntiles[bh] = run;
-  }
+  const int per = (nbk + 255) / 256, u0 = min(nbk, tid * per), u1 = min(nbk, u0 + per);
+  int cnt = 0;
+  for (int u = u0; u < u1; ++u) cnt += (offs[u + 1] - offs[u] + kS2Chunk - 1) / kS2Chunk;
+  s_tot[tid] = cnt;
   __syncthreads();
-  for (int u = threadIdx.x; u < nbk; u += blockDim.x) {
-    const int n0 = offs[u], n1 = offs[u + 1];
-    int t = s_base[u];
-    for (int st = n0; st < n1; st += 32) tiles[t++] = make_int2(u, st);
+  // exclusive scan of the 256 thread totals (Hillis-Steele in LDS)
+  for (int o = 1; o < 256; o <<= 1) {
+    const int x = tid >= o ? s_tot[tid - o] : 0;
+    __syncthreads();
+    s_tot[tid] += x;
+    __syncthreads();
   }
+  int t = s_tot[tid] - cnt;
+  if (tid == 255) a.ntiles[bh] = s_tot[255];
+  for (int u = u0; u < u1; ++u)
+    for (int st = offs[u]; st < offs[u + 1]; st += kS2Chunk) tiles[t++] = make_int2(u, st);
 }
 
+// Matrix-core stage 2: one workgroup of 4 waves per chunk of up to 128 queries of one
+// bucket (wave w: queries 32 w .. 32 w + 31 of the chunk). The bucket's tables stream
+// through LDS in chunks of 32 key clusters (cooperative 16-byte loads, the next chunk in
+// registers while the current one is used), with an online softmax across chunks.
+// LDS: K hi/lo [32][D+8] | V^T hi/lo [D][32+8] | log Z [32] | s D_i [D][D+8] (bf16).
 template <int D>
-__global__ void __launch_bounds__(256) s2_mfma_kernel(S2Args a) {
-  constexpr int NKS = D / 16;
-  constexpr int NMT = D / 32;
-  constexpr int MAXJT = kMaxClusters / 32;
-  const int bh = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= a.ntiles[bh]) return;  // whole wave leaves together
-  const int2 tile = a.tiles[static_cast<size_t>(bh) * a.max_tiles + t];
-  const int u = tile.x, st = tile.y;
-  const int b = u / a.Cq, i = u % a.Cq;
+struct S2Cfg {
+  static constexpr int JC = 32;
+  static constexpr int KST = D + 8;
+  static constexpr int VST = JC + 8;
+  static constexpr int DST = D + 8;
+  static constexpr int NK = JC * D / 8 / 256;   // 16-byte K pieces per thread and part (hi, lo)
+  static constexpr int NV = D * JC / 8 / 256;   // 16-byte V^T pieces per thread and part
+  static constexpr int ND = D * D / 8 / 256;    // 16-byte dipole pieces per thread
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a) {
+  using Cfg = S2Cfg<D>;
+  constexpr int NKS = D / 16, NMT = D / 32, JC = Cfg::JC, KST = Cfg::KST, VST = Cfg::VST, DST = Cfg::DST;
+  constexpr int NK = Cfg::NK, NV = Cfg::NV, ND = Cfg::ND;
+  __shared__ __align__(16) uint16_t sKh[JC * KST];
+  __shared__ __align__(16) uint16_t sKl[JC * KST];
+  __shared__ __align__(16) uint16_t sVh[D * VST];
+  __shared__ __align__(16) uint16_t sVl[D * VST];
+  __shared__ __align__(16) uint16_t sDip[D * DST];
+  __shared__ float slz[JC];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
+  if (static_cast<int>(blockIdx.x) >= a.ntiles[bh]) return;  // whole workgroup leaves together
+  const int2 tile = a.tiles[static_cast<size_t>(bh) * a.max_tiles + blockIdx.x];
+  const int u = tile.x, b = u / a.Cq, i = u % a.Cq;
   const int32_t* offs = a.offs_q + static_cast<size_t>(bh) * (a.nb * a.Cq + 1);
-  const int n = min(32, offs[u + 1] - st);
-  const bool valid = c < n;
-  const int qn = a.perm_q[static_cast<size_t>(bh) * a.N + st + (valid ? c : 0)];
+  const int st = tile.y + 32 * wave;
+  const int nw = max(0, min(32, offs[u + 1] - st));  // queries of this wave
+  const bool valid = c < nw;
+  const int qn = a.perm_q[static_cast<size_t>(bh) * a.N + (valid ? st + c : tile.y)];
   const size_t row = static_cast<size_t>(bh) * a.N + qn;
   if (a.causal && b == 0) {  // the first block has no far field
     if (valid) {
@@ -162,8 +185,56 @@ __global__ void __launch_bounds__(256) s2_mfma_kernel(S2Args a) {
   }
   const int e = a.causal ? b : 0;
   const size_t sidx = (static_cast<size_t>(bh) * a.nbS + e) * a.Cq + i;
-  const int Ck = a.Ck;
-  const int njt = (Ck + 31) / 32;
+  const int Ck = a.Ck, njc = (Ck + JC - 1) / JC;
+  const uint16_t* khi = a.t_khi + sidx * Ck * D;
+  const uint16_t* klo = a.t_klo + sidx * Ck * D;
+  const uint16_t* vthi = a.t_vthi + sidx * Ck * D;
+  const uint16_t* vtlo = a.t_vtlo + sidx * Ck * D;
+  const float* lz = a.s_logz + sidx * Ck;
+  const bool vec = (Ck & 7) == 0;  // 16-byte aligned rows of V^T
+
+  // chunk jc of the tables into registers
+  u16x8_t pkh[NK], pkl[NK], pvh[NV], pvl[NV];
+  float plz = kNegInf;
+  auto load_chunk = [&](int jc) {
+    const int j0 = jc * JC;
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+      const int x = tid + 256 * q, jj = x / (D / 8), d8 = (x % (D / 8)) * 8;
+      pkh[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      pkl[q] = pkh[q];
+      if (j0 + jj < Ck) {
+        pkh[q] = *reinterpret_cast<const u16x8_t*>(khi + static_cast<size_t>(j0 + jj) * D + d8);
+        pkl[q] = *reinterpret_cast<const u16x8_t*>(klo + static_cast<size_t>(j0 + jj) * D + d8);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int x = tid + 256 * q, d = x / (JC / 8), j8 = (x % (JC / 8)) * 8;
+      const size_t o = static_cast<size_t>(d) * Ck + j0 + j8;
+      pvh[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      pvl[q] = pvh[q];
+      if (vec && j0 + j8 + 8 <= Ck) {
+        pvh[q] = *reinterpret_cast<const u16x8_t*>(vthi + o);
+        pvl[q] = *reinterpret_cast<const u16x8_t*>(vtlo + o);
+      } else {
+        for (int r = 0; r < 8 && j0 + j8 + r < Ck; ++r) {
+          pvh[q][r] = vthi[o + r];
+          pvl[q][r] = vtlo[o + r];
+        }
+      }
+    }
+    plz = (tid < JC && j0 + tid < Ck) ? lz[j0 + tid] : kNegInf;
+  };
+  load_chunk(0);
+  if (a.dipole) {
+    const uint16_t* dip = a.t_dip + sidx * D * D;
+#pragma unroll
+    for (int q = 0; q < ND; ++q) {
+      const int x = tid + 256 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
+      *reinterpret_cast<u16x8_t*>(sDip + r * DST + c8) = *reinterpret_cast<const u16x8_t*>(dip + static_cast<size_t>(r) * D + c8);
+    }
+  }
 
   // residual query fragments (B operand: column = query c, k = d)
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
@@ -179,125 +250,102 @@ __global__ void __launch_bounds__(256) s2_mfma_kernel(S2Args a) {
     split_bf16x8(x, qhi[ks], qlo[ks]);
   }
 
-  // logits^T, in log2 units
-  const float* lz = a.s_logz + sidx * Ck;
-  const uint16_t* khi = a.t_khi + sidx * Ck * D;
-  const uint16_t* klo = a.t_klo + sidx * Ck * D;
   const float sl2 = a.scale * 1.4426950408889634f;
-  f32x16_t lg[MAXJT];
-  float mx = -1e30f;
-#pragma unroll
-  for (int jt = 0; jt < MAXJT; ++jt) {
-    if (jt >= njt) break;
-    f32x16_t acc = zero16();
-    const int j = 32 * jt + c;
-    const bool jok = j < Ck;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u16x8_t ah = {0, 0, 0, 0, 0, 0, 0, 0}, al = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (jok) {
-        ah = *reinterpret_cast<const u16x8_t*>(khi + static_cast<size_t>(j) * D + 16 * ks + 8 * h);
-        al = *reinterpret_cast<const u16x8_t*>(klo + static_cast<size_t>(j) * D + 16 * ks + 8 * h);
-      }
-      acc = mfma32(as_bf16x8(ah), qhi[ks], acc);
-      acc = mfma32(as_bf16x8(ah), qlo[ks], acc);
-      acc = mfma32(as_bf16x8(al), qhi[ks], acc);
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int jj = 32 * jt + 8 * (v >> 2) + 4 * h + (v & 3);
-      const float l0 = jj < Ck ? lz[jj] : kNegInf;
-      const float x = (l0 == kNegInf) ? kNegInf : l0 * 1.4426950408889634f + sl2 * acc[v];
-      acc[v] = x;
-      mx = fmaxf(mx, x);
-    }
-    lg[jt] = acc;
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  float z = 0.f;
-#pragma unroll
-  for (int jt = 0; jt < MAXJT; ++jt) {
-    if (jt >= njt) break;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = fast_exp2(lg[jt][v] - mx);
-      lg[jt][v] = p;
-      z += p;
-    }
-  }
-  z += __shfl_xor(z, 32, 64);
-  const float invz = z > 0.f ? 1.f / z : 0.f;  // z == 0: no far-field key at all
-
-  // O^T = V^T P^T (split), then / z, then + (s D_i) qt^T
-  const uint16_t* vthi = a.t_vthi + sidx * Ck * D;
-  const uint16_t* vtlo = a.t_vtlo + sidx * Ck * D;
+  float mx = kNegInf, z = 0.f;  // running max (log2 units) and sum of this lane pair's query
   f32x16_t o[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) o[mt] = zero16();
+  for (int jc = 0; jc < njc; ++jc) {
+    __syncthreads();  // previous chunk consumed
 #pragma unroll
-  for (int jt = 0; jt < MAXJT; ++jt) {
-    if (jt >= njt) break;
+    for (int q = 0; q < NK; ++q) {
+      const int x = tid + 256 * q, jj = x / (D / 8), d8 = (x % (D / 8)) * 8;
+      *reinterpret_cast<u16x8_t*>(sKh + jj * KST + d8) = pkh[q];
+      *reinterpret_cast<u16x8_t*>(sKl + jj * KST + d8) = pkl[q];
+    }
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int x = tid + 256 * q, d = x / (JC / 8), j8 = (x % (JC / 8)) * 8;
+      *reinterpret_cast<u16x8_t*>(sVh + d * VST + j8) = pvh[q];
+      *reinterpret_cast<u16x8_t*>(sVl + d * VST + j8) = pvl[q];
+    }
+    if (tid < JC) slz[tid] = plz;
+    __syncthreads();
+    if (jc + 1 < njc) load_chunk(jc + 1);
+    if (nw == 0) continue;
+    // logits^T of the chunk (rows j, column = query), log2 units
+    f32x16_t lg = zero16();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sKh + c * KST + 16 * ks + 8 * h));
+      const bf16x8_t al = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sKl + c * KST + 16 * ks + 8 * h));
+      lg = mfma32(ah, qhi[ks], lg);
+      lg = mfma32(ah, qlo[ks], lg);
+      lg = mfma32(al, qhi[ks], lg);
+    }
+    float cm = kNegInf;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(slz + 8 * g + 4 * h);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float l0 = l4[r];
+        const float x = l0 == kNegInf ? kNegInf : l0 * 1.4426950408889634f + sl2 * lg[4 * g + r];
+        lg[4 * g + r] = x;
+        cm = fmaxf(cm, x);
+      }
+    }
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float mn = fmaxf(mx, cm);
+    if (mn == kNegInf) continue;  // no key cluster yet: nothing to add (same for the lane pair)
+    const float alpha = mx == kNegInf ? 0.f : fast_exp2(mx - mn);
+    mx = mn;
+    float zs = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = fast_exp2(lg[v] - mn);
+      lg[v] = p;
+      zs += p;
+    }
+    z = z * alpha + zs + __shfl_xor(zs, 32, 64);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+    // O^T += V^T P^T (split): k-slots of step ss are rows 16 ss + 4 h + 0..3 and 16 ss + 8 + 4 h + 0..3
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss) {
       float pv[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) pv[r] = lg[jt][8 * ss + r];
+      for (int r = 0; r < 8; ++r) pv[r] = lg[8 * ss + r];
       bf16x8_t phi, plo;
       split_bf16x8(pv, phi, plo);
-      const int j0 = 32 * jt + 16 * ss + 4 * h;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
-        const size_t rofs = static_cast<size_t>(32 * mt + c) * Ck;
-        u16x8_t vh = {0, 0, 0, 0, 0, 0, 0, 0}, vl = {0, 0, 0, 0, 0, 0, 0, 0};
-        if ((Ck & 3) == 0) {  // 8-byte aligned groups of 4 (j0 is a multiple of 4)
-          if (j0 < Ck) {
-            const u16x4_t h4 = *reinterpret_cast<const u16x4_t*>(vthi + rofs + j0);
-            const u16x4_t l4 = *reinterpret_cast<const u16x4_t*>(vtlo + rofs + j0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              vh[r] = h4[r];
-              vl[r] = l4[r];
-            }
-          }
-          if (j0 + 8 < Ck) {
-            const u16x4_t h4 = *reinterpret_cast<const u16x4_t*>(vthi + rofs + j0 + 8);
-            const u16x4_t l4 = *reinterpret_cast<const u16x4_t*>(vtlo + rofs + j0 + 8);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              vh[4 + r] = h4[r];
-              vl[4 + r] = l4[r];
-            }
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (j0 + r < Ck) {
-              vh[r] = vthi[rofs + j0 + r];
-              vl[r] = vtlo[rofs + j0 + r];
-            }
-            if (j0 + 8 + r < Ck) {
-              vh[4 + r] = vthi[rofs + j0 + 8 + r];
-              vl[4 + r] = vtlo[rofs + j0 + 8 + r];
-            }
-          }
-        }
-        o[mt] = mfma32(as_bf16x8(vh), phi, o[mt]);
-        o[mt] = mfma32(as_bf16x8(vh), plo, o[mt]);
-        o[mt] = mfma32(as_bf16x8(vl), phi, o[mt]);
+        const uint16_t* vh = sVh + (32 * mt + c) * VST + 16 * ss + 4 * h;
+        const uint16_t* vl = sVl + (32 * mt + c) * VST + 16 * ss + 4 * h;
+        const u16x4_t h0 = *reinterpret_cast<const u16x4_t*>(vh), h1 = *reinterpret_cast<const u16x4_t*>(vh + 8);
+        const u16x4_t l0 = *reinterpret_cast<const u16x4_t*>(vl), l1 = *reinterpret_cast<const u16x4_t*>(vl + 8);
+        const u16x8_t hv = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        const u16x8_t lv = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        o[mt] = mfma32(as_bf16x8(hv), phi, o[mt]);
+        o[mt] = mfma32(as_bf16x8(hv), plo, o[mt]);
+        o[mt] = mfma32(as_bf16x8(lv), phi, o[mt]);
       }
     }
   }
+  if (nw == 0) return;
+  const float invz = z > 0.f ? 1.f / z : 0.f;  // z == 0: no far-field key at all
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[mt][v] *= invz;
   if (a.dipole) {
-    const uint16_t* dip = a.t_dip + sidx * D * D;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const u16x8_t ad = *reinterpret_cast<const u16x8_t*>(dip + static_cast<size_t>(32 * mt + c) * D + 16 * ks + 8 * h);
+        const u16x8_t ad = *reinterpret_cast<const u16x8_t*>(sDip + (32 * mt + c) * DST + 16 * ks + 8 * h);
         o[mt] = mfma32(as_bf16x8(ad), qhi[ks], o[mt]);
       }
   }
@@ -339,7 +387,7 @@ hipError_t launch_stage2(const S2Args& a, int dtype, hipStream_t s) {
       hipLaunchKernelGGL(s2_tiles_kernel, dim3(a.BH), dim3(256), 0, s, a);
     }
     ProfScope ps_("s2_mfma", s);
-    const dim3 gm((a.max_tiles + 3) / 4, a.BH);
+    const dim3 gm(a.max_tiles, a.BH);
     if (a.D == 64) hipLaunchKernelGGL((s2_mfma_kernel<64>), gm, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((s2_mfma_kernel<128>), gm, dim3(256), 0, s, a);
     return hipGetLastError();
