@@ -577,31 +577,53 @@ __global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
   write_centroid_tables(t, D, row, vals, nper);
 }
 
-// One workgroup per (head, tensor): counts per (block, cluster) and their exclusive
-// scan -> offs[nb*C + 1].
-__global__ void bucket_offsets_kernel(KmArgs a) {
+// One workgroup per (head, tensor): per (block, cluster) the exclusive prefix of the
+// tile counts over the block's tiles (written over tile_cnt, which the scatter then
+// reads in O(1)), the bucket totals, and their exclusive scan -> offs[nb*C + 1]
+// (threads over consecutive buckets, then a scan of the thread totals).
+__global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
   if (t.perm == nullptr) return;
-  const int C = t.C, bh = blockIdx.y;
+  __shared__ int s_run[256];
+  const int C = t.C, bh = blockIdx.y, tid = threadIdx.x;
   const int nbC = a.nb * C;
-  extern __shared__ int s_tot[];  // [nb*C]
-  for (int e = threadIdx.x; e < nbC; e += blockDim.x) {
+  const int per = (nbC + 255) / 256, e0 = min(nbC, tid * per), e1 = min(nbC, e0 + per);
+  int* offs = t.offs + static_cast<size_t>(bh) * (nbC + 1);
+  int tot = 0;
+  for (int e = e0; e < e1; ++e) {
     const int b = e / C, j = e % C;
-    int s = 0;
-    for (int tt = b * a.tiles_per_block; tt < min(a.ntiles, (b + 1) * a.tiles_per_block); ++tt)
-      s += t.tile_cnt[(static_cast<size_t>(bh) * a.ntiles + tt) * C + j];
-    s_tot[e] = s;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int* offs = t.offs + static_cast<size_t>(bh) * (nbC + 1);
     int run = 0;
-    for (int e = 0; e < nbC; ++e) {
-      offs[e] = run;
-      run += s_tot[e];
+    const int t0 = b * a.tiles_per_block, t1 = min(a.ntiles, (b + 1) * a.tiles_per_block);
+    int32_t* pc = t.tile_cnt + (static_cast<size_t>(bh) * a.ntiles + t0) * C + j;
+    for (int tt = t0; tt < t1; tt += 8) {
+      // eight loads in flight, then the prefixes (members of (b, j) in earlier tiles)
+      int cnt[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) cnt[q] = tt + q < t1 ? pc[static_cast<size_t>(tt - t0 + q) * C] : 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (tt + q < t1) pc[static_cast<size_t>(tt - t0 + q) * C] = run;
+        run += cnt[q];
+      }
     }
-    offs[nbC] = run;
+    offs[e] = run;  // bucket total for now (only this thread touches entry e)
+    tot += run;
   }
+  s_run[tid] = tot;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int x = tid >= o ? s_run[tid - o] : 0;
+    __syncthreads();
+    s_run[tid] += x;
+    __syncthreads();
+  }
+  int pos = s_run[tid] - tot;
+  for (int e = e0; e < e1; ++e) {
+    const int cnt = offs[e];
+    offs[e] = pos;
+    pos += cnt;
+  }
+  if (tid == 255) offs[nbC] = s_run[255];
 }
 
 // One workgroup per tile: scatter the tile's stably sorted points into the head's
@@ -618,11 +640,7 @@ __global__ void bucket_scatter_kernel(KmArgs a) {
   for (int pos = threadIdx.x; pos < npts; pos += blockDim.x) {
     const int p = t.tile_perm[tix * a.tile + pos];
     const int j = t.labels[static_cast<size_t>(bh) * a.N + tile0 + p];
-    // members of (b, j) in earlier tiles of the same block come first
-    int before = 0;
-    for (int t2 = b * a.tiles_per_block; t2 < tt; ++t2)
-      before += t.tile_cnt[(static_cast<size_t>(bh) * a.ntiles + t2) * C + j];
-    const int dst = offs[b * C + j] + before + (pos - t.tile_start[tix * C + j]);
+    const int dst = offs[b * C + j] + t.tile_cnt[tix * C + j] + (pos - t.tile_start[tix * C + j]);
     t.perm[static_cast<size_t>(bh) * a.N + dst] = static_cast<int>(tile0 + p);
   }
 }
@@ -688,10 +706,9 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
       hipLaunchKernelGGL(kmeans_update_kernel, g_update, dim3(64), 0, s, b);
     }
   }
-  const size_t lds_off = sizeof(int) * static_cast<size_t>(a.nb) * Cmax;
   {
     ProfScope ps_("bucket_offsets", s);
-    hipLaunchKernelGGL(bucket_offsets_kernel, dim3(1, a.BH, a.ntensors), dim3(256), lds_off, s, a);
+    hipLaunchKernelGGL(bucket_offsets_kernel, dim3(1, a.BH, a.ntensors), dim3(256), 0, s, a);
   }
   {
     ProfScope ps_("bucket_scatter", s);
