@@ -268,14 +268,13 @@ __device__ __forceinline__ bf16x8_t onehot_bf16x8(const u16x8_t& lab8, uint32_t 
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_assign_mfma_kernel(KmArgs a, int iter, int last) {
-  extern __shared__ __align__(16) unsigned char smem[];
+template <int D, int NW, int NJT>
+__device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int last, unsigned char* smem) {
   using Cfg = KmMfmaCfg<D, NW>;
   constexpr int NKS = Cfg::NKS, XST = Cfg::XST, NDT = Cfg::NDT, TILE = Cfg::TILE, CPW = Cfg::CPW, OPW = Cfg::OPW;
-  constexpr int MAXJT = kMaxClusters / 32;
+  constexpr int MAXJT = NJT, njt = NJT;  // centroid tiles of 32
   const KmTensor& t = a.t[blockIdx.z];
-  const int C = t.C, Cp = (C + 31) & ~31, njt = Cp / 32;
+  const int C = t.C, Cp = 32 * NJT;
   const int grp = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int tt0 = grp * a.tpg, tt1 = min(a.ntiles, tt0 + a.tpg);
@@ -292,7 +291,21 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
   int* s_sorted = s_start + C;
   const uint16_t* X = static_cast<const uint16_t*>(t.x) + static_cast<size_t>(bh) * a.N * D;
   const float* cent = t.cent + static_cast<size_t>(bh) * C * D;
+  // this wave's points of tile tt: group gi, lane (c, h) -> point 64 wave + 32 gi + c, dims 16 ks + 8 h
+  u16x8_t xf[2][NKS];
+  auto load_x = [&](int tt) {
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const long p = static_cast<long>(tt) * TILE + wave * 64 + gi * 32 + c;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        xf[gi][ks] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        if (p < a.N) xf[gi][ks] = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(p) * D + 16 * ks + 8 * h);
+      }
+    }
+  };
   const bool score = t.labels_in == nullptr;
+  if (tt0 < tt1) load_x(tt0);  // the first tile's rows travel while the tables are staged
 
   if (score) {
     const uint16_t* ghi = t.chi + static_cast<size_t>(bh) * C * D;
@@ -325,19 +338,6 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
   for (int r = 0; r < OPW; ++r) acc[r] = zero16();
   const int npass = (njt + NW * CPW - 1) / (NW * CPW);
 
-  // this wave's points of tile tt: group gi, lane (c, h) -> point 64 wave + 32 gi + c, dims 16 ks + 8 h
-  u16x8_t xf[2][NKS];
-  auto load_x = [&](int tt) {
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const long p = static_cast<long>(tt) * TILE + wave * 64 + gi * 32 + c;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        xf[gi][ks] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        if (p < a.N) xf[gi][ks] = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(p) * D + 16 * ks + 8 * h);
-      }
-    }
-  };
   // scores of centroid tile jt for both groups, accumulator preset to the bias
   auto score_tile = [&](int jt, f32x16_t& s0, f32x16_t& s1) {
 #pragma unroll
@@ -362,7 +362,6 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
     }
   };
 
-  if (tt0 < tt1) load_x(tt0);
   for (int tt = tt0; tt < tt1; ++tt) {
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
@@ -394,24 +393,28 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
       }
       float best[2] = {kNegInf, kNegInf}, second[2] = {kNegInf, kNegInf};
       int slot[2] = {0, 0};
-      // tile jt + 1 is on the matrix cores while tile jt is ranked
-      f32x16_t sa0, sa1, sb0, sb1;
+      // tile jt + 1 goes to the matrix cores while tile jt is ranked; the centroid-tile
+      // loop has compile-time bounds, and a scheduling barrier per step keeps the
+      // compiler from hoisting later tiles (register pressure)
+      f32x16_t sa0, sa1;
       score_tile(0, sa0, sa1);
 #pragma unroll
-      for (int jt = 0; jt < MAXJT; ++jt) {
-        if (jt < njt) {
-          if (jt + 1 < MAXJT && jt + 1 < njt) score_tile(jt + 1, sb0, sb1);
+      for (int jt = 0; jt < NJT; ++jt) {
+        f32x16_t sb0, sb1;
+        if (jt + 1 < NJT) score_tile(jt + 1, sb0, sb1);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float x0 = sa0[v], x1 = sa1[v];
-            const bool g0 = x0 > best[0], g1 = x1 > best[1];
-            slot[0] = g0 ? 16 * jt + v : slot[0];
-            second[0] = __builtin_amdgcn_fmed3f(best[0], second[0], x0);
-            best[0] = g0 ? x0 : best[0];
-            slot[1] = g1 ? 16 * jt + v : slot[1];
-            second[1] = __builtin_amdgcn_fmed3f(best[1], second[1], x1);
-            best[1] = g1 ? x1 : best[1];
-          }
+        for (int v = 0; v < 16; ++v) {
+          const float x0 = sa0[v], x1 = sa1[v];
+          const bool g0 = x0 > best[0], g1 = x1 > best[1];
+          slot[0] = g0 ? 16 * jt + v : slot[0];
+          second[0] = __builtin_amdgcn_fmed3f(best[0], second[0], x0);
+          best[0] = g0 ? x0 : best[0];
+          slot[1] = g1 ? 16 * jt + v : slot[1];
+          second[1] = __builtin_amdgcn_fmed3f(best[1], second[1], x1);
+          best[1] = g1 ? x1 : best[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (jt + 1 < NJT) {
           sa0 = sb0;
           sa1 = sb1;
         }
@@ -465,20 +468,36 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
             const int cL = L & 31, hL = L >> 5;
             const uint16_t* xr = sX + (wave * 64 + gi * 32 + cL) * XST;
             while (m != 0ull) {
-              const int sl = __ffsll(static_cast<unsigned long long>(m)) - 1;
-              m &= m - 1;
-              const int j = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * hL + (sl & 3);
-              const float* cr = cent + static_cast<size_t>(j) * D;
-              float part = 0.f;
+              // up to four candidates per round: their rows are loaded together
+              int jc[4];
+              float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int d = lane; d < D; d += 64) {
-                const float diff = bf16_to_f32(xr[d]) - cr[d];
-                part = fmaf(diff, diff, part);
+              for (int q = 0; q < 4; ++q) {
+                jc[q] = -1;
+                if (m != 0ull) {
+                  const int sl = __ffsll(static_cast<unsigned long long>(m)) - 1;
+                  m &= m - 1;
+                  jc[q] = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * hL + (sl & 3);
+                }
               }
-              const float dist = wave_sum(part);
-              if (c == cL && (dist < fb[gi] || (dist == fb[gi] && j < fj[gi]))) {
-                fb[gi] = dist;
-                fj[gi] = j;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                if (jc[q] < 0) continue;
+                const float* cr = cent + static_cast<size_t>(jc[q]) * D;
+#pragma unroll
+                for (int d = lane; d < D; d += 64) {
+                  const float diff = bf16_to_f32(xr[d]) - cr[d];
+                  part[q] = fmaf(diff, diff, part[q]);
+                }
+              }
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                if (jc[q] < 0) continue;
+                const float dist = wave_sum(part[q]);
+                if (c == cL && (dist < fb[gi] || (dist == fb[gi] && jc[q] < fj[gi]))) {
+                  fb[gi] = dist;
+                  fj[gi] = jc[q];
+                }
               }
             }
           }
@@ -510,6 +529,7 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
 #pragma unroll
         for (int rc = 0; rc < CPW; ++rc) jj[rc] = (32u * (ct0 + rc) + c) * 0x10001u;
         const uint32_t one2 = 0x00010001u, neg2 = 0xC080C080u, val2 = 0x3F803F80u;
+#pragma unroll 4
         for (int ks = 0; ks < TILE / 16; ++ks) {
           const u16x8_t lab8 = *reinterpret_cast<const u16x8_t*>(slab + 16 * ks + 8 * h);
           bf16x8_t ax[NDT];
@@ -545,6 +565,19 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
     __syncthreads();  // the next tile overwrites the X tile and labels
   }
   for (int j = tid; j < C; j += TILE) t.gcnt[(static_cast<size_t>(bh) * a.ntiles + grp) * C + j] = s_gcnt[j];
+}
+
+// The centroid-tile count is a template parameter of the body so that the score loop
+// has no runtime bounds (the two tensors of one launch may differ).
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_assign_mfma_kernel(KmArgs a, int iter, int last) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  switch ((a.t[blockIdx.z].C + 31) / 32) {
+    case 1: km_assign_body<D, NW, 1>(a, iter, last, smem); break;
+    case 2: km_assign_body<D, NW, 2>(a, iter, last, smem); break;
+    case 3: km_assign_body<D, NW, 3>(a, iter, last, smem); break;
+    default: km_assign_body<D, NW, 4>(a, iter, last, smem); break;
+  }
 }
 
 // One wave per (centroid j, head, tensor), lanes over d: sum the tile-group partials in
