@@ -55,6 +55,18 @@ __device__ __forceinline__ bf16x8_t lds_operand_tr(const uint16_t* tile, int ld,
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
+// The same with the k order of an accumulator reused as B operand: lane l receives rows
+// kbase + 4*(l/32) + 0..3 and kbase + 8 + 4*(l/32) + 0..3 of column cbase + l%32, i.e. the
+// rows that accumulator elements 8s..8s+7 of a 32-row tile hold for kbase = 16 s.
+__device__ __forceinline__ bf16x8_t lds_operand_tr_acc(const uint16_t* tile, int ld, int kbase, int cbase, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const uint16_t* p = tile + (kbase + 4 * (g >> 1) + (s >> 2)) * ld + cbase + 16 * (g & 1) + 4 * (s & 3);
+  const u16x4_t r0 = lds_read_tr16(p);
+  const u16x4_t r1 = lds_read_tr16(p + 8 * ld);
+  const u16x8_t u = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
 #pragma unroll

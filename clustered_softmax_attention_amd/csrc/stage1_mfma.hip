@@ -10,10 +10,11 @@
 // positions:
 //   s1_scores      a_i(pos) = s qbar_i . k_perm[pos] for every centroid and position,
 //                  [BH, Cq, N] fp32 (qbar split into bf16 hi + lo; keys are exact).
-//   s1_atoms_mfma  one wave per (block, key cluster) bucket: per-centroid max of a over
-//                  the bucket, then sum w k and sum w v as products K_seg^T W^T, with the
-//                  bucket's key/value rows gathered into a transposed LDS tile and the
-//                  weights split into bf16 hi + lo.
+//   s1_atoms_mfma  one wave per (block, key cluster) bucket: the bucket's scores
+//                  recomputed on the matrix cores in steps of 32 keys (keys as rows, so
+//                  the max is lane-local, online across steps), and sum w k, sum w v as
+//                  K^T W, V^T W with the weight accumulator as B operand and the key and
+//                  value rows read from a row-major LDS tile by the transpose read.
 //   s1_moments_f16 per (key range, centroid group): weights w = exp(a - max) from the
 //                  scores (no running rescale), then sum_m w_m v_m k_m^T with fp16
 //                  operands (the weights are applied to the value fragments with packed
@@ -90,18 +91,23 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
   }
 }
 
-// One wave per (block b', key cluster j) bucket; 4 buckets per workgroup. The bucket's
-// positions are visited kAtomPass at a time: their key and value rows are gathered through
-// the permutation (all loads of a pass in flight together) into a wave-private transposed
-// LDS tile [D][kAtomPass + 8].
-constexpr int kAtomPass = 32;  // bucket positions staged per pass
+constexpr int kAtomChunk = 32;  // bucket positions per step
 
+// One wave per (block, key cluster) bucket, for every query centroid in tiles of 32:
+// keys of the bucket arrive in steps of 32 (rows gathered through the permutation into
+// a wave-private row-major LDS tile), and on the matrix cores
+//   S = K_step (s qbar)^T   (32 keys x 32 centroids; qbar split into bf16 hi + lo, keys exact),
+// so that lane (c, h) holds 16 keys of centroid c and the max over the bucket is
+// lane-local plus the partner lane l^32 (online across steps, sums rescaled when it
+// grows). The weights w = exp(S - max), split into hi + lo, are directly the B operand
+// of  sum w k = K^T W  and  sum w v = V^T W,  whose A operands come from the same LDS
+// tile through the transpose read in the accumulator's key order.
 template <int D>
-__global__ void __launch_bounds__(256) s1_atoms_mfma_kernel(S1Args a) {
-  constexpr int NMT = D / 32;
-  constexpr int PST = kAtomPass + 8;
-  __shared__ __align__(16) uint16_t sKt[4][D * PST];
-  __shared__ __align__(16) uint16_t sVt[4][D * PST];
+__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) s1_atoms_mfma_kernel(S1Args a) {
+  constexpr int NKS = D / 16, NMT = D / 32, KC = kAtomChunk, ST = D + 8;
+  constexpr int NP = KC * (D / 8) / 64;  // 16-byte row pieces per lane and tensor
+  __shared__ __align__(16) uint16_t sK[4][KC * ST];
+  __shared__ __align__(16) uint16_t sV[4][KC * ST];
   const int bh = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
   const int Cq = a.Cq, Ck = a.Ck;
   const int u = blockIdx.x * 4 + wave;
@@ -112,82 +118,109 @@ __global__ void __launch_bounds__(256) s1_atoms_mfma_kernel(S1Args a) {
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + s0;
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
-  uint16_t* kt = sKt[wave];
-  uint16_t* vt = sVt[wave];
+  uint16_t* kt = sK[wave];
+  uint16_t* vt = sV[wave];
   const size_t abase = (static_cast<size_t>(bh) * a.nb + bp) * Cq;
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
   for (int nt = 0; nt < (Cq + 31) / 32; ++nt) {
     const int i = 32 * nt + c;
     const bool iv = i < Cq;
-    const float* Si = a.scores + (static_cast<size_t>(bh) * Cq + (iv ? i : 0)) * a.N + s0;
-    float mx = kNegInf;
-#pragma unroll 8
-    for (int k = h; k < n; k += 2) mx = fmaxf(mx, Si[k]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // B operand of S: column = centroid c, k = d
+    bf16x8_t qh[NKS], ql[NKS];
+    {
+      const float* qb = a.qbar + (static_cast<size_t>(bh) * Cq + (iv ? i : 0)) * D;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) x[r] = iv ? a.scale * qb[16 * ks + 8 * h + r] : 0.f;
+        split_bf16x8(x, qh[ks], ql[ks]);
+      }
+    }
     f32x16_t ak[NMT], av[NMT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       ak[mt] = zero16();
       av[mt] = zero16();
     }
-    float z = 0.f;
-    for (int p0 = 0; p0 < n; p0 += kAtomPass) {
-      // gather up to kAtomPass rows (D/8 16-byte chunks each) and store them transposed
-      constexpr int NCH = kAtomPass * (D / 8) / 64;
-      u16x8_t kv[NCH], vv[NCH];
+    float mx = kNegInf, z = 0.f;
+    u16x8_t pk[NP], pv[NP];
+    auto load_rows = [&](int p0) {
 #pragma unroll
-      for (int q = 0; q < NCH; ++q) {
-        const int x = lane + 64 * q;
-        const int r = x / (D / 8), c8 = x % (D / 8);
-        kv[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        vv[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int q = 0; q < NP; ++q) {
+        const int x = lane + 64 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
+        pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        pv[q] = pk[q];
         if (p0 + r < n) {
-          const size_t row = static_cast<size_t>(perm[p0 + r]) * D + c8 * 8;
-          kv[q] = *reinterpret_cast<const u16x8_t*>(K + row);
-          vv[q] = *reinterpret_cast<const u16x8_t*>(V + row);
+          const size_t row = static_cast<size_t>(perm[p0 + r]) * D + c8;
+          pk[q] = *reinterpret_cast<const u16x8_t*>(K + row);
+          pv[q] = *reinterpret_cast<const u16x8_t*>(V + row);
         }
       }
-      float w[kAtomPass / 16][8];
+    };
+    if (n > 0) load_rows(0);
+    for (int p0 = 0; p0 < n; p0 += KC) {
+      wave_sync();  // the previous step's tiles are consumed
 #pragma unroll
-      for (int ks = 0; ks < kAtomPass / 16; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int kk = p0 + 16 * ks + 8 * h + e;
-          w[ks][e] = (kk < n && iv) ? __expf(Si[kk] - mx) : 0.f;
-        }
-#pragma unroll
-      for (int q = 0; q < NCH; ++q) {
-        const int x = lane + 64 * q;
-        const int r = x / (D / 8), c8 = x % (D / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kt[(c8 * 8 + e) * PST + r] = kv[q][e];
-          vt[(c8 * 8 + e) * PST + r] = vv[q][e];
-        }
+      for (int q = 0; q < NP; ++q) {
+        const int x = lane + 64 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
+        *reinterpret_cast<u16x8_t*>(kt + r * ST + c8) = pk[q];
+        *reinterpret_cast<u16x8_t*>(vt + r * ST + c8) = pv[q];
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_sync();
+      if (p0 + KC < n) load_rows(p0 + KC);  // next step's rows in flight
+      f32x16_t sc = zero16();
 #pragma unroll
-      for (int ks = 0; ks < kAtomPass / 16; ++ks) {
-        if (p0 + 16 * ks >= n) break;
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u16x8_t*>(kt + c * ST + 16 * ks + 8 * h));
+        sc = mfma32(ka, qh[ks], sc);
+        sc = mfma32(ka, ql[ks], sc);
+      }
+      // rows of sc: keys p0 + 8 (v/4) + 4 h + v%4
+      float cm = kNegInf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) z += w[ks][e];
+      for (int v = 0; v < 16; ++v) {
+        const int key = p0 + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (key >= n) sc[v] = kNegInf;
+        cm = fmaxf(cm, sc[v]);
+      }
+      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      if (cm > mx) {  // the same for the lane pair
+        const float f = mx == kNegInf ? 0.f : __expf(mx - cm);
+        z *= f;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            ak[mt][v] *= f;
+            av[mt][v] *= f;
+          }
+        mx = cm;
+      }
+      float w[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        w[v] = __expf(sc[v] - mx);
+        z += w[v];
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
         bf16x8_t whi, wlo;
-        split_bf16x8(w[ks], whi, wlo);
+        split_bf16x8(w + 8 * s, whi, wlo);
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
-          const int o = (32 * mt + c) * PST + 16 * ks + 8 * h;
-          const bf16x8_t akf = as_bf16x8(*reinterpret_cast<const u16x8_t*>(kt + o));
-          const bf16x8_t avf = as_bf16x8(*reinterpret_cast<const u16x8_t*>(vt + o));
-          ak[mt] = mfma32(akf, whi, ak[mt]);
-          ak[mt] = mfma32(akf, wlo, ak[mt]);
-          av[mt] = mfma32(avf, whi, av[mt]);
-          av[mt] = mfma32(avf, wlo, av[mt]);
+          const bf16x8_t kf = lds_operand_tr_acc(kt, ST, 16 * s, 32 * mt, lane);
+          const bf16x8_t vf = lds_operand_tr_acc(vt, ST, 16 * s, 32 * mt, lane);
+          ak[mt] = mfma32(kf, whi, ak[mt]);
+          ak[mt] = mfma32(kf, wlo, ak[mt]);
+          av[mt] = mfma32(vf, whi, av[mt]);
+          av[mt] = mfma32(vf, wlo, av[mt]);
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     z += __shfl_xor(z, 32, 64);
     if (!iv) continue;
