@@ -1,6 +1,6 @@
 """Throughput of the MuSe forward pass on one MI355X, with roofline and CPU-oracle baseline.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload acausal_8k] [--no-cpu]
 
 A step is one muse_attn_fwd call over the whole workload batch (K-means, stage 1,
 stage 2 and, when causal, the exact diagonal blocks), with inputs resident in HBM and
@@ -30,39 +30,100 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_FP32_VALU_TFLOPS = 157.3
 
 WORKLOAD_TEXT = {
-    "c1": "acausal MuSe fwd, B=1 H=1 N=1024 D=64 fp32, Cq=8 Ck=32, 5 Lloyd iterations",
-    "c2": "acausal MuSe fwd, B=4 H=8 N=8192 D=64 bf16 (fp32 accumulate), Cq=32 Ck=128, 5 Lloyd iterations",
-    "c3": "causal MuSe fwd, B=8 H=8 N=16384 D=64 bf16, block 1024, Cq=16 Ck=64, 5 Lloyd iterations",
-    "c4": "causal MuSe fwd, B=1 H=16 N=65536 D=128 bf16, block 2048, Cq=32 Ck=128, 5 Lloyd iterations",
-    "c5": "causal MuSe fwd with retrieval k1=4 k2=2, B=2 H=8 N=16384 D=64 bf16, block 1024, Cq=16 Ck=64",
+    "acausal_1k_f32": "acausal MuSe fwd, B=1 H=1 N=1024 D=64 fp32, Cq=8 Ck=32, 5 Lloyd iterations",
+    "acausal_8k": "acausal MuSe fwd, B=4 H=8 N=8192 D=64 bf16 (fp32 accumulate), Cq=32 Ck=128, 5 Lloyd iterations",
+    "causal_16k": "causal MuSe fwd, B=8 H=8 N=16384 D=64 bf16, block 1024, Cq=16 Ck=64, 5 Lloyd iterations",
+    "causal_64k_d128": "causal MuSe fwd, B=1 H=16 N=65536 D=128 bf16, block 2048, Cq=32 Ck=128, 5 Lloyd iterations",
+    "retrieval_16k": "causal MuSe fwd with retrieval k1=4 k2=2, B=2 H=8 N=16384 D=64 bf16, block 1024, Cq=16 Ck=64",
 }
 
 
-def kernel_work(name: str, cfg) -> tuple:
-    """(bound, algorithmic amount per launch, unit, peak) of a library kernel on this workload.
+RIDGE = PEAK_BF16_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/byte where the two roofs meet
 
-    Flop counts are multiply-add = 2 flops, per head, times B*H heads."""
+
+def kernel_work(name: str, cfg):
+    """(algorithmic bytes, algorithmic flops) of ONE launch of a library kernel on this
+    workload, or None when the kernel is not listed. Bytes count every tensor a launch
+    must read or write at least once (inputs read once, outputs written once); flops count
+    the arithmetic the method defines (multiply-add = 2), not the extra products of the
+    bf16 hi/lo splits. Causal tables have one entry per block (nbS = nb)."""
     BH, N, D, Cq, Ck = cfg.B * cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck
-    nb = cfg.N // cfg.block if cfg.causal else 1
     e = 2 if cfg.dtype == "bf16" else 4
-    valu = ("alu", "TFLOP/s", PEAK_FP32_VALU_TFLOPS)
-    mfma = ("mfma", "TFLOP/s", PEAK_BF16_MFMA_TFLOPS)
-    tbl = {
-        "kmeans_assign": (valu, 2.0 * N * (Cq + Ck) * D * BH),
-        "kmeans_assign_mfma": (mfma, 2.0 * N * (Cq + Ck) * D * BH),
-        "s1_atoms": (valu, 6.0 * Cq * N * D * BH),
-        "s1_moments": (valu, (2.0 * Cq * N * D * D + 2.0 * Cq * N * D) * BH),
-        "s1_moments_mfma": (mfma, (2.0 * Cq * N * D * D + 2.0 * Cq * N * D) * BH),
-        "s1_dip_final": (valu, 2.0 * nb * Cq * Ck * D * D * BH),
-        "s2_refine": (valu, 2.0 * N * (2 * Ck * D + D * D) * BH),
-        "exact_valu": (valu, (2.0 if cfg.causal else 4.0) * N * N * D * BH),
-        "local_block_exact": (valu, 2.0 * N * cfg.block * D * BH),
+    nb = cfg.N // cfg.block if cfg.causal else 1
+    mbk = cfg.block if cfg.causal else (1024 if cfg.dtype == "bf16" else N)
+    nmb = (N + mbk - 1) // mbk
+    x = BH * N * D * e                      # one [B, H, N, D] input tensor
+    table = BH * nb * Cq * Ck               # (entry, i, j) cells
+    tbytes = table * (4 + 8 * D)            # log Z + bf16 hi/lo of K_ij and of V_ij
+    ftab = table * (1 + 2 * D) * 4          # fp32 log Z, K_ij, V_ij
+    dip32 = BH * nb * Cq * D * D * 4         # fp32 dipole (or E[v k^T]) per table entry
+    w = {
+        "kmeans_assign_mfma": (2 * x + 2 * BH * N * 4, 2.0 * BH * N * (Cq + Ck) * D),
+        "kmeans_assign": (2 * x + 2 * BH * N * 4, 2.0 * BH * N * (Cq + Ck) * D),
+        "s1_scores": (x + BH * Cq * N * 4, 2.0 * BH * Cq * N * D),
+        "s1_atoms_mfma": (2 * x + table * (2 + 2 * D) * 4, 6.0 * BH * Cq * N * D),
+        "s1_atoms": (2 * x + table * (2 + 2 * D) * 4, 6.0 * BH * Cq * N * D),
+        "s1_moments_f16": (2 * x + BH * Cq * N * 4 + BH * nmb * Cq * (D * D + 1) * 4, 2.0 * BH * Cq * N * D * D),
+        "s1_moments": (2 * x + BH * nmb * Cq * (D * D + 1) * 4, 2.0 * BH * Cq * N * D * D),
+        "s1_finalize": (table * (2 + 2 * D) * 4 + BH * nmb * Cq * (D * D + 1) * 4 + tbytes + BH * Cq * D * D * 2,
+                        2.0 * BH * Cq * Ck * D * D),
+        "s1_prefix": (table * (2 + 2 * D) * 4 + ftab, 0.0),
+        "s1_mom_prefix": (BH * nmb * Cq * (D * D + 1) * 4 + dip32, 0.0),
+        "s1_dip_final": (ftab + 2 * dip32, 2.0 * BH * nb * Cq * Ck * D * D),
+        "s1_pack": (ftab + dip32 + tbytes + dip32 // 2, 0.0),
+        "s2_mfma": (x + x + tbytes + BH * nb * Cq * D * D * 2, 2.0 * BH * N * (2 * Ck * D + D * D)),
+        "s2_refine": (x + x + table * (1 + 2 * D) * 4 + BH * nb * Cq * D * D * 4, 2.0 * BH * N * (2 * Ck * D + D * D)),
+        "local_block_mfma": (3 * x + BH * N * D * 4, 4.0 * BH * N * (cfg.block / 2) * D),
+        "exact_mfma": (4 * x, (2.0 if cfg.causal else 4.0) * BH * N * N * D),
+        "exact_valu": (4 * x, (2.0 if cfg.causal else 4.0) * BH * N * N * D),
     }
-    if name in tbl:
-        (bound, unit, peak), amount = tbl[name]
-        return bound, amount / 1e12, unit, peak
-    # streaming kernels: minimum bytes (inputs read once, outputs written once)
-    return "hbm", 2.0 * N * D * e * BH / 1e9, "GB/s", PEAK_HBM_GBS
+    return w.get(name)
+
+
+def roofline_entry(name: str, cfg, avg_s: float):
+    """Roofline of one kernel from its measured average launch duration: memory-bound when
+    its arithmetic intensity is below the ridge point, else matrix-core-bound."""
+    wk = kernel_work(name, cfg)
+    if wk is None:
+        return None
+    nbytes, flops = wk
+    if flops / nbytes < RIDGE or flops == 0:
+        return {"bound": "hbm", "achieved": nbytes / avg_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": nbytes / avg_s / 1e9 / PEAK_HBM_GBS, "bytes_per_launch": nbytes, "flops_per_launch": flops}
+    return {"bound": "mfma", "achieved": flops / avg_s / 1e12, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": flops / avg_s / 1e12 / PEAK_BF16_MFMA_TFLOPS, "bytes_per_launch": nbytes, "flops_per_launch": flops}
+
+
+def csrc_sha() -> str:
+    """Hash of the library sources (kernels, launchers, public header)."""
+    import hashlib
+    h = hashlib.sha1()
+    d = os.path.join(ROOT, "clustered_softmax_attention_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "muse.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE) recorded in the rocprofv3 summary
+    profiles/muse_fwd_<workload>.md, or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"muse_fwd_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic-json: "):
+                rec = json.loads(line[len("traffic-json: "):])
+                if rec.get("csrc_sha") != csrc_sha() or kernel not in rec["kernels"]:
+                    return None
+                k = rec["kernels"][kernel]
+                return k["fetch_bytes"] + k["write_bytes"]
+    return None
 
 
 def timed(fn, steps: int, warmup: int):
@@ -115,7 +176,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="acausal_8k", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-exact", action="store_true", help="skip the exact-attention comparator")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -171,12 +232,16 @@ def main():
     prof = binding.prof_collect()
     binding.prof_enable(False)
     kernels = {n: {"avg_us": 1e3 * t / c, "launches_per_step": c / args.steps} for n, (t, c) in prof.items()}
-    dom = max(prof.items(), key=lambda kv: kv[1][0])[0]
-    bound, amount, unit, peak = kernel_work(dom, cfg)
+    # dominant kernel: the largest share of the step among those with a defined roofline
+    ranked = sorted(prof.items(), key=lambda kv: -kv[1][0])
+    dom = next(n for n, _ in ranked if kernel_work(n, cfg) is not None)
     avg_s = prof[dom][0] / prof[dom][1] / 1e3
-    achieved = amount / avg_s
-    roofline = {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": None}
+    roofline = {"kernel": dom, **roofline_entry(dom, cfg, avg_s), "traffic": measured_traffic(args.workload, dom),
+                "share_of_step": prof[dom][0] / sum(t for t, _ in prof.values())}
+    for n, d in kernels.items():
+        r = roofline_entry(n, cfg, prof[n][0] / prof[n][1] / 1e3)
+        if r is not None:
+            d.update({"bound": r["bound"], "frac": r["frac"]})
     print(f"# kernels: " + ", ".join(f"{n} {d['avg_us']:.1f}us x{d['launches_per_step']:.0f}"
                                      for n, d in sorted(kernels.items(), key=lambda kv: -prof[kv[0]][0])),
           file=sys.stderr, flush=True)

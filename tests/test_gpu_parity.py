@@ -19,67 +19,67 @@ pytestmark = pytest.mark.gpu
 
 # ------------------------------------------------------------ small cases: whole tensors
 
-def test_c1_full_fp32(muse_lib):
-    check_config(CONFIGS["c1"], [(0, 0)])
+def test_acausal_1k_f32_full(muse_lib):
+    check_config(CONFIGS["acausal_1k_f32"], [(0, 0)])
 
 
 @pytest.mark.parametrize("N", [1000, 1536])
 def test_acausal_bf16_ragged(muse_lib, N):
     # several 512-point K-means tiles plus a ragged tail (N=1000)
-    cfg = scaled_config("c2", B=1, H=2, N=N)
+    cfg = scaled_config("acausal_8k", B=1, H=2, N=N)
     check_config(cfg, [(0, 0), (0, 1)])
 
 
 def test_acausal_bf16_d128(muse_lib):
-    cfg = scaled_config("c4", B=1, H=2, N=2048, causal=False, block=0)
+    cfg = scaled_config("causal_64k_d128", B=1, H=2, N=2048, causal=False, block=0)
     check_config(cfg, [(0, 0), (0, 1)])
 
 
 def test_acausal_fp32_d128_monopole(muse_lib):
-    cfg = scaled_config("c1", H=2, N=777, D=128, Cq=5, Ck=17)
+    cfg = scaled_config("acausal_1k_f32", H=2, N=777, D=128, Cq=5, Ck=17)
     check_config(cfg, [(0, 0), (0, 1)], dipole=False)
 
 
 def test_causal_bf16_small_blocks(muse_lib):
-    cfg = scaled_config("c3", B=1, H=2, N=2048, block=256)
+    cfg = scaled_config("causal_16k", B=1, H=2, N=2048, block=256)
     check_config(cfg, [(0, 0), (0, 1)])
 
 
 def test_causal_bf16_block64(muse_lib):
     # one-wave K-means tiles and 64-token diagonal blocks
-    cfg = scaled_config("c3", B=1, H=1, N=512, block=64, Cq=8, Ck=16)
+    cfg = scaled_config("causal_16k", B=1, H=1, N=512, block=64, Cq=8, Ck=16)
     check_config(cfg, [(0, 0)])
 
 
-def test_causal_c3_shape_reduced(muse_lib):
-    cfg = scaled_config("c3", B=1, H=2, N=4096)
+def test_causal_16k_shape_reduced(muse_lib):
+    cfg = scaled_config("causal_16k", B=1, H=2, N=4096)
     check_config(cfg, [(0, 0), (0, 1)])
 
 
-def test_causal_c4_shape_reduced(muse_lib):
-    cfg = scaled_config("c4", B=1, H=2, N=8192)
+def test_causal_64k_d128_shape_reduced(muse_lib):
+    cfg = scaled_config("causal_64k_d128", B=1, H=2, N=8192)
     check_config(cfg, [(0, 1)])
 
 
 def test_causal_fp32(muse_lib):
-    cfg = scaled_config("c1", H=2, N=1024, causal=True, block=256, Cq=8, Ck=32)
+    cfg = scaled_config("acausal_1k_f32", H=2, N=1024, causal=True, block=256, Cq=8, Ck=32)
     check_config(cfg, [(0, 0), (0, 1)])
 
 
-def test_retrieval_c5_shape_reduced(muse_lib):
-    cfg = scaled_config("c5", B=1, H=2, N=4096)
+def test_retrieval_16k_shape_reduced(muse_lib):
+    cfg = scaled_config("retrieval_16k", B=1, H=2, N=4096)
     check_config(cfg, [(0, 0), (0, 1)])
 
 
 def test_retrieval_small_blocks_fp32(muse_lib):
-    cfg = scaled_config("c5", B=1, H=1, N=2048, block=256, dtype="f32", Cq=8, Ck=16, topk_clusters=3,
+    cfg = scaled_config("retrieval_16k", B=1, H=1, N=2048, block=256, dtype="f32", Cq=8, Ck=16, topk_clusters=3,
                         topk_blocks=2)
     check_config(cfg, [(0, 0)])
 
 
 def test_retrieval_of_everything_is_exact(muse_lib):
     # k1 = Ck and k2 = number of blocks: every earlier key is attended exactly
-    cfg = scaled_config("c5", B=1, H=1, N=2048, block=256, Cq=8, Ck=16, topk_clusters=16, topk_blocks=8)
+    cfg = scaled_config("retrieval_16k", B=1, H=1, N=2048, block=256, Cq=8, Ck=16, topk_clusters=16, topk_blocks=8)
     q, k, v = make_inputs(cfg)
     out, _ = run_gpu(cfg, q, k, v)
     o, _ = exact_attention(q[0, 0], k[0, 0], v[0, 0], causal=True)
@@ -89,14 +89,14 @@ def test_retrieval_of_everything_is_exact(muse_lib):
 
 
 def test_bf16_output_within_tolerance(muse_lib):
-    cfg = scaled_config("c2", B=1, H=1, N=2048)
+    cfg = scaled_config("acausal_8k", B=1, H=1, N=2048)
     check_config(cfg, [(0, 0)], out_dtype=torch.bfloat16)
 
 
 def test_fixed_labels_path(muse_lib):
     # caller-fixed labels: the library uses member means as centroids and skips K-means
     from oracle import muse_acausal
-    cfg = scaled_config("c2", B=1, H=1, N=1024, Cq=8, Ck=16)
+    cfg = scaled_config("acausal_8k", B=1, H=1, N=1024, Cq=8, Ck=16)
     q, k, v = make_inputs(cfg)
     rng = np.random.default_rng(5)
     lq = rng.integers(0, cfg.Cq, size=(1, 1, cfg.N)).astype(np.int32)
@@ -110,7 +110,7 @@ def test_fixed_labels_path(muse_lib):
 
 
 def test_deterministic_bitwise(muse_lib):
-    cfg = scaled_config("c3", B=1, H=2, N=2048, block=512)
+    cfg = scaled_config("causal_16k", B=1, H=2, N=2048, block=512)
     q, k, v = make_inputs(cfg)
     a, _ = run_gpu(cfg, q, k, v)
     b, _ = run_gpu(cfg, q, k, v)
@@ -138,21 +138,21 @@ def test_exact_attention(muse_lib, dtype, D, causal):
 
 # ------------------------------------------------------------ full-size configurations (sampled)
 
-def test_c2_full_size_sampled_heads(muse_lib):
-    cfg = CONFIGS["c2"]
+def test_acausal_8k_full_size_sampled_heads(muse_lib):
+    cfg = CONFIGS["acausal_8k"]
     check_config(cfg, [(0, 0), (3, 7)])
 
 
-def test_c3_full_size_sampled_blocks(muse_lib):
-    cfg = CONFIGS["c3"]
+def test_causal_16k_full_size_sampled_blocks(muse_lib):
+    cfg = CONFIGS["causal_16k"]
     check_config(cfg, [(7, 5)], blocks=[1, 15])
 
 
-def test_c5_full_size_sampled_blocks(muse_lib):
-    cfg = CONFIGS["c5"]
+def test_retrieval_16k_full_size_sampled_blocks(muse_lib):
+    cfg = CONFIGS["retrieval_16k"]
     check_config(cfg, [(1, 6)], blocks=[1, 15])
 
 
-def test_c4_full_size_sampled_blocks(muse_lib):
-    cfg = CONFIGS["c4"]
+def test_causal_64k_d128_full_size_sampled_blocks(muse_lib):
+    cfg = CONFIGS["causal_64k_d128"]
     check_config(cfg, [(0, 9)], blocks=[1, 31])

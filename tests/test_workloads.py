@@ -17,7 +17,7 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_heads_are_deterministic_and_distinct():
-    cfg = scaled_config("c2", N=512)
+    cfg = scaled_config("acausal_8k", N=512)
     a = make_head(cfg, 0, 1)
     b = make_head(cfg, 0, 1)
     c = make_head(cfg, 1, 1)
@@ -30,19 +30,19 @@ def test_heads_are_deterministic_and_distinct():
 
 
 def test_outliers_and_drift():
-    cfg = scaled_config("c5", N=2048)
+    cfg = scaled_config("retrieval_16k", N=2048)
     q, k, v = make_head(cfg, 0, 0)
     norms = np.linalg.norm(k, axis=1)
     n_out = int(0.01 * 2048)
     assert np.sum(norms > 3 * np.median(norms)) == n_out
-    c4 = scaled_config("c4", N=1024, drift=1.0)  # exaggerated drift is visible in the mean
+    c4 = scaled_config("causal_64k_d128", N=1024, drift=1.0)  # exaggerated drift is visible in the mean
     q4, _, _ = make_head(c4, 0, 0)
-    base = make_head(scaled_config("c4", N=1024, drift=0.0), 0, 0)[0]
+    base = make_head(scaled_config("causal_64k_d128", N=1024, drift=0.0), 0, 0)[0]
     d = (q4 - base).mean(axis=1)
     assert np.allclose(d, np.sin(np.arange(1024) / 4096.0), atol=2e-2)
 
 
 def test_config_table():
-    assert CONFIGS["c2"].tokens == 32768 and CONFIGS["c4"].N == 65536 and CONFIGS["c4"].D == 128
-    assert CONFIGS["c5"].topk_clusters == 4 and CONFIGS["c5"].topk_blocks == 2
+    assert CONFIGS["acausal_8k"].tokens == 32768 and CONFIGS["causal_64k_d128"].N == 65536 and CONFIGS["causal_64k_d128"].D == 128
+    assert CONFIGS["retrieval_16k"].topk_clusters == 4 and CONFIGS["retrieval_16k"].topk_blocks == 2
     assert all(c.N % c.block == 0 for c in CONFIGS.values() if c.causal)

@@ -61,16 +61,16 @@ class WorkloadConfig:
 
 CONFIGS: Dict[str, WorkloadConfig] = {
     # 1k acausal, fp32, one head.
-    "c1": WorkloadConfig("c1", 1, 1, 1, 1024, 64, "f32", 32, 0.10, 8, 32, 5, False, 0),
+    "acausal_1k_f32": WorkloadConfig("acausal_1k_f32", 1, 1, 1, 1024, 64, "f32", 32, 0.10, 8, 32, 5, False, 0),
     # 8k acausal isolated-layer shape.
-    "c2": WorkloadConfig("c2", 2, 4, 8, 8192, 64, "bf16", 128, 0.15, 32, 128, 5, False, 0),
+    "acausal_8k": WorkloadConfig("acausal_8k", 2, 4, 8, 8192, 64, "bf16", 128, 0.15, 32, 128, 5, False, 0),
     # 16k causal, block 1024.
-    "c3": WorkloadConfig("c3", 3, 8, 8, 16384, 64, "bf16", 256, 0.20, 16, 64, 5, True, 1024),
+    "causal_16k": WorkloadConfig("causal_16k", 3, 8, 8, 16384, 64, "bf16", 256, 0.20, 16, 64, 5, True, 1024),
     # 64k causal, D=128, block 2048, slow positional drift.
-    "c4": WorkloadConfig("c4", 4, 1, 16, 65536, 128, "bf16", 512, 0.20, 32, 128, 5, True, 2048,
+    "causal_64k_d128": WorkloadConfig("causal_64k_d128", 4, 1, 16, 65536, 128, "bf16", 512, 0.20, 32, 128, 5, True, 2048,
                          drift=0.01, drift_period=4096.0),
     # 16k causal with retrieval (k1=4 clusters, k2=2 blocks) and 1% planted 5x outlier keys.
-    "c5": WorkloadConfig("c5", 5, 2, 8, 16384, 64, "bf16", 256, 0.20, 16, 64, 5, True, 1024,
+    "retrieval_16k": WorkloadConfig("retrieval_16k", 5, 2, 8, 16384, 64, "bf16", 256, 0.20, 16, 64, 5, True, 1024,
                          topk_clusters=4, topk_blocks=2, outlier_frac=0.01, outlier_scale=5.0),
 }
 
