@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(256) flash_bf16_kernel(ExactArgs a, int nqt) {
         s[t][v] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, xor32(mx));
     const float mn = fmaxf(m, mx);
     const float alpha = fast_exp2(m - mn);
     m = mn;
@@ -243,7 +243,7 @@ __global__ void __launch_bounds__(256) flash_bf16_kernel(ExactArgs a, int nqt) {
         }
       }
   }
-  const float lt = l + __shfl_xor(l, 32, 64);
+  const float lt = l + xor32(l);
   if (!qvalid) return;
   const float inv = 1.f / lt;
   float L = (m + __log2f(lt)) * 0.6931471805599453f;

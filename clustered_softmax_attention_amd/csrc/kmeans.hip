@@ -233,6 +233,8 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_kernel(KmArgs a, int i
 //
 // Dynamic LDS: c_hi, c_lo [Cp][D] bf16 (16-byte chunks XOR-swizzled by row) | bias [Cp] |
 // X tile [64 NW][XST] bf16 | labels [64 NW] u16 | counts [C] | sort buffers.
+constexpr int kCandMax = 64;  // rescoring candidates listed per wave and round
+
 template <int D, int NW>
 struct KmMfmaCfg {
   static constexpr int NKS = D / 16;
@@ -245,7 +247,7 @@ struct KmMfmaCfg {
   static size_t lds_bytes(int Cmax) {
     const size_t Cp = (Cmax + 31) & ~31;
     return Cp * D * 2 * sizeof(uint16_t) + Cp * sizeof(float) + static_cast<size_t>(TILE) * XST * sizeof(uint16_t) +
-           TILE * sizeof(uint16_t) + sizeof(int) * (Cmax + 2 * TILE + NW * Cmax + 2 * Cmax);
+           TILE * sizeof(uint16_t) + sizeof(int) * (Cmax + 2 * TILE + NW * Cmax + 2 * Cmax + NW * kCandMax);
   }
   static int passes(int Cmax) { return ((Cmax + 31) / 32 + NW * CPW - 1) / (NW * CPW); }
 };
@@ -289,6 +291,7 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
   int* s_cnt = s_whist + NW * C;
   int* s_start = s_cnt + C;
   int* s_sorted = s_start + C;
+  int* s_cand = s_sorted + TILE;  // [NW][kCandMax] rescoring candidates: (tile row << 8) | j
   const uint16_t* X = static_cast<const uint16_t*>(t.x) + static_cast<size_t>(bh) * a.N * D;
   const float* cent = t.cent + static_cast<size_t>(bh) * C * D;
   // this wave's points of tile tt: group gi, lane (c, h) -> point 64 wave + 32 gi + c, dims 16 ks + 8 h
@@ -323,6 +326,16 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
       *reinterpret_cast<u16x8_t*>(clo + dst) = l8;
     }
     for (int j = tid; j < Cp; j += TILE) bias[j] = j < C ? -0.5f * t.cn2[static_cast<size_t>(bh) * C + j] : kNegInf;
+    // bring the fp32 centroid rows that a near-tie rescoring reads into this XCD's L2
+    // now, while the tables are in flight anyway (a cold miss later costs a full round
+    // trip under load); the sum only keeps the loads alive
+    float warm = 0.f;
+#pragma unroll 4
+    for (int e = tid; e < C * D / 4; e += TILE) {
+      const f32x4_t c4 = *reinterpret_cast<const f32x4_t*>(cent + 4 * static_cast<size_t>(e));
+      warm += c4[0];
+    }
+    if (warm == 1.2345e-30f && tid == TILE) s_gcnt[0] = 0;  // never true: tid < TILE
   }
   for (int j = tid; j < C; j += TILE) s_gcnt[j] = 0;
   __syncthreads();
@@ -389,7 +402,7 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
             s = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, s, false);
           }
         }
-        xx[gi] = s + __shfl_xor(s, 32, 64);
+        xx[gi] = s + xor32(s);
       }
       float best[2] = {kNegInf, kNegInf}, second[2] = {kNegInf, kNegInf};
       int slot[2] = {0, 0};
@@ -426,9 +439,9 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
       for (int gi = 0; gi < 2; ++gi) {
         const int sl = slot[gi];
         bj[gi] = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * h + (sl & 3);
-        const float ob = __shfl_xor(best[gi], 32, 64);
-        const float os = __shfl_xor(second[gi], 32, 64);
-        const int oj = __shfl_xor(bj[gi], 32, 64);
+        const float ob = xor32(best[gi]);
+        const float os = xor32(second[gi]);
+        const int oj = xor32(bj[gi]);
         if (ob > best[gi] || (ob == best[gi] && oj < bj[gi])) {
           second[gi] = best[gi] > os ? best[gi] : os;
           best[gi] = ob;
@@ -456,6 +469,11 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
         }
         float fb[2] = {__builtin_huge_valf(), __builtin_huge_valf()};
         int fj[2] = {C, C};
+        // list the wave's (point, candidate) pairs (uniform loops over the lanes that hold
+        // candidates), then evaluate them eight at a time with all centroid-row loads of a
+        // batch in flight together
+        int* clist = s_cand + wave * kCandMax;
+        int tot = 0;
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
           uint64_t lanes = __ballot(cm[gi] != 0ull);
@@ -465,44 +483,96 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
             const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(cm[gi]), L);
             const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(cm[gi] >> 32), L);
             uint64_t m = (static_cast<uint64_t>(hi) << 32) | lo;
-            const int cL = L & 31, hL = L >> 5;
-            const uint16_t* xr = sX + (wave * 64 + gi * 32 + cL) * XST;
+            const int row = wave * 64 + gi * 32 + (L & 31), hL = L >> 5;
             while (m != 0ull) {
-              // up to four candidates per round: their rows are loaded together
-              int jc[4];
-              float part[4] = {0.f, 0.f, 0.f, 0.f};
+              const int sl = __ffsll(static_cast<unsigned long long>(m)) - 1;
+              m &= m - 1;
+              if (lane == 0 && tot < kCandMax)
+                clist[tot] = (row << 8) | (32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * hL + (sl & 3));
+              ++tot;
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int nl = min(tot, kCandMax);
+        for (int b0 = 0; b0 < nl; b0 += 8) {
+          int ent[8];
+          float part[8];
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                jc[q] = -1;
-                if (m != 0ull) {
-                  const int sl = __ffsll(static_cast<unsigned long long>(m)) - 1;
-                  m &= m - 1;
-                  jc[q] = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * hL + (sl & 3);
-                }
-              }
+          for (int q = 0; q < 8; ++q) {
+            ent[q] = b0 + q < nl ? clist[b0 + q] : -1;
+            part[q] = 0.f;
+          }
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                if (jc[q] < 0) continue;
-                const float* cr = cent + static_cast<size_t>(jc[q]) * D;
+          for (int q = 0; q < 8; ++q) {
+            if (ent[q] < 0) continue;
+            const float* cr = cent + static_cast<size_t>(ent[q] & 255) * D;
+            const uint16_t* xr = sX + (ent[q] >> 8) * XST;
 #pragma unroll
-                for (int d = lane; d < D; d += 64) {
-                  const float diff = bf16_to_f32(xr[d]) - cr[d];
-                  part[q] = fmaf(diff, diff, part[q]);
-                }
-              }
+            for (int d = lane; d < D; d += 64) {
+              const float diff = bf16_to_f32(xr[d]) - cr[d];
+              part[q] = fmaf(diff, diff, part[q]);
+            }
+          }
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                if (jc[q] < 0) continue;
-                const float dist = wave_sum(part[q]);
-                if (c == cL && (dist < fb[gi] || (dist == fb[gi] && jc[q] < fj[gi]))) {
-                  fb[gi] = dist;
-                  fj[gi] = jc[q];
+          for (int q = 0; q < 8; ++q) {
+            if (ent[q] < 0) continue;
+            const float dist = wave_sum(part[q]);
+            const int j = ent[q] & 255, pl = (ent[q] >> 8) - wave * 64;
+            if (c == (pl & 31)) {
+              const int gq = pl >> 5;
+              const float f = gq == 0 ? fb[0] : fb[1];
+              const int jj = gq == 0 ? fj[0] : fj[1];
+              if (dist < f || (dist == f && j < jj)) {
+                if (gq == 0) {
+                  fb[0] = dist;
+                  fj[0] = j;
+                } else {
+                  fb[1] = dist;
+                  fj[1] = j;
                 }
               }
             }
           }
-          if (need[gi] && fj[gi] < C) bj[gi] = fj[gi];
         }
+        if (tot > kCandMax) {
+          // more candidates than the list holds (rare): one lane's candidates at a time
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi) {
+            uint64_t lanes = __ballot(cm[gi] != 0ull);
+            while (lanes != 0ull) {
+              const int L = __ffsll(static_cast<unsigned long long>(lanes)) - 1;
+              lanes &= lanes - 1;
+              const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(cm[gi]), L);
+              const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(cm[gi] >> 32), L);
+              uint64_t m = (static_cast<uint64_t>(hi) << 32) | lo;
+              const int cL = L & 31, hL = L >> 5;
+              const uint16_t* xr = sX + (wave * 64 + gi * 32 + cL) * XST;
+              while (m != 0ull) {
+                const int sl = __ffsll(static_cast<unsigned long long>(m)) - 1;
+                m &= m - 1;
+                const int j = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * hL + (sl & 3);
+                const float* cr = cent + static_cast<size_t>(j) * D;
+                float part = 0.f;
+#pragma unroll
+                for (int d = lane; d < D; d += 64) {
+                  const float diff = bf16_to_f32(xr[d]) - cr[d];
+                  part = fmaf(diff, diff, part);
+                }
+                const float dist = wave_sum(part);
+                if (c == cL && (dist < fb[gi] || (dist == fb[gi] && j < fj[gi]))) {
+                  fb[gi] = dist;
+                  fj[gi] = j;
+                }
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+          if (need[gi] && fj[gi] < C) bj[gi] = fj[gi];
       }
       if (valid) lab = h == 0 ? bj[0] : bj[1];
     }

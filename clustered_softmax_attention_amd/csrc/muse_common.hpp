@@ -45,22 +45,89 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
-// Wave-wide reductions (64 lanes) through shuffles; every lane gets the result.
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+// Cross-lane moves on the VALU (no LDS crossbar). Lane-order facts, checked on the
+// device: DPP quad_perm(1,0,3,2) / (2,3,0,1) exchange lanes l^1 / l^2, row_half_mirror
+// maps lane i of each 8-lane half-row to 7 - i, row_ror:8 exchanges l^8 inside a
+// 16-lane row; permlane16_swap(x, x) leaves in its two results the values of rows
+// {r, r^1} of lane l, and permlane32_swap(x, x) the values of lanes {l, l^32}.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
+// permlane{16,32}_swap of x with itself. The second operand is passed through an empty
+// asm statement so that the compiler keeps the two swapped registers apart (with one
+// value for both operands it has been seen to feed the swap a stale register).
+struct SwapPair {
+  unsigned r0, r1;
+};
+__device__ __forceinline__ SwapPair self_swap32(unsigned u) {
+  unsigned b = u;
+  asm volatile("" : "+v"(b));
+  const auto r = __builtin_amdgcn_permlane32_swap(u, b, false, false);
+  return {r[0], r[1]};
+}
+__device__ __forceinline__ SwapPair self_swap16(unsigned u) {
+  unsigned b = u;
+  asm volatile("" : "+v"(b));
+  const auto r = __builtin_amdgcn_permlane16_swap(u, b, false, false);
+  return {r[0], r[1]};
+}
+
+// The value of lane l ^ 32.
+__device__ __forceinline__ float xor32(float x) {
+  const SwapPair r = self_swap32(__builtin_bit_cast(unsigned, x));
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r.r0 : r.r1);
+}
+__device__ __forceinline__ int xor32(int x) {
+  const SwapPair r = self_swap32(static_cast<unsigned>(x));
+  return static_cast<int>((threadIdx.x & 32) ? r.r0 : r.r1);
+}
+
+// Wave-wide reductions (64 lanes); every step pairs two lanes symmetrically, so all
+// lanes compute the same operands in the same order and get bit-identical results.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float x, Op op) {
+  x = op(x, dpp_f32<0xB1>(x));   // l ^ 1
+  x = op(x, dpp_f32<0x4E>(x));   // l ^ 2
+  x = op(x, dpp_f32<0x141>(x));  // the other quad of the half-row
+  x = op(x, dpp_f32<0x128>(x));  // l ^ 8
+  {
+    const SwapPair r = self_swap16(__builtin_bit_cast(unsigned, x));
+    x = op(__builtin_bit_cast(float, r.r0), __builtin_bit_cast(float, r.r1));
+  }
+  {
+    const SwapPair r = self_swap32(__builtin_bit_cast(unsigned, x));
+    x = op(__builtin_bit_cast(float, r.r0), __builtin_bit_cast(float, r.r1));
+  }
   return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  return wave_reduce(x, [](float p, float q) { return fmaxf(p, q); });
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  return wave_reduce(x, [](float p, float q) { return p + q; });
 }
 
 __device__ __forceinline__ int wave_sum_int(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  x += dpp_i32<0xB1>(x);
+  x += dpp_i32<0x4E>(x);
+  x += dpp_i32<0x141>(x);
+  x += dpp_i32<0x128>(x);
+  {
+    const SwapPair r = self_swap16(static_cast<unsigned>(x));
+    x = static_cast<int>(r.r0 + r.r1);
+  }
+  {
+    const SwapPair r = self_swap32(static_cast<unsigned>(x));
+    x = static_cast<int>(r.r0 + r.r1);
+  }
   return x;
 }
 

@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) s1_atoms_mfma_kernel(S1A
         if (key >= n) sc[v] = kNegInf;
         cm = fmaxf(cm, sc[v]);
       }
-      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      cm = fmaxf(cm, xor32(cm));
       if (cm > mx) {  // the same for the lane pair
         const float f = mx == kNegInf ? 0.f : __expf(mx - cm);
         z *= f;
@@ -222,7 +222,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) s1_atoms_mfma_kernel(S1A
         }
       }
     }
-    z += __shfl_xor(z, 32, 64);
+    z += xor32(z);
     if (!iv) continue;
     const size_t aidx = (abase + i) * Ck + j;
     if (h == 0) {

@@ -295,7 +295,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
         cm = fmaxf(cm, x);
       }
     }
-    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    cm = fmaxf(cm, xor32(cm));
     const float mn = fmaxf(mx, cm);
     if (mn == kNegInf) continue;  // no key cluster yet: nothing to add (same for the lane pair)
     const float alpha = mx == kNegInf ? 0.f : fast_exp2(mx - mn);
@@ -307,7 +307,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
       lg[v] = p;
       zs += p;
     }
-    z = z * alpha + zs + __shfl_xor(zs, 32, 64);
+    z = z * alpha + zs + xor32(zs);
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
