@@ -126,7 +126,7 @@ struct Plan {
   size_t cent_q, cent_k, lab_q, lab_k, tperm_q, tperm_k, tcnt_q, tcnt_k, tst_q, tst_k, psum_q, psum_k;
   size_t gcnt_q, gcnt_k;
   size_t perm_k, offs_k, perm_q, offs_q;
-  size_t t_khi, t_klo, t_vthi, t_vtlo, t_dip, tiles, ntiles, tile_base;
+  size_t t_khi, t_klo, t_vhi, t_vlo, t_dip, tiles, ntiles, tile_base;
   int max_tiles;
   size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores;
   size_t s_logz, s_k, s_v, s_dip;
@@ -189,8 +189,8 @@ Plan make_plan(const Shape& s, const muse_fwd_params* p) {
     const size_t h2 = sizeof(uint16_t);
     P.t_khi = L.take(BH * nbS * Cq * Ck * D * h2);
     P.t_klo = L.take(BH * nbS * Cq * Ck * D * h2);
-    P.t_vthi = L.take(BH * nbS * Cq * Ck * D * h2);
-    P.t_vtlo = L.take(BH * nbS * Cq * Ck * D * h2);
+    P.t_vhi = L.take(BH * nbS * Cq * Ck * D * h2);
+    P.t_vlo = L.take(BH * nbS * Cq * Ck * D * h2);
     P.t_dip = L.take(BH * nbS * Cq * D * D * h2);
     P.max_tiles = static_cast<int>((N + 127) / 128 + nb * Cq);  // 128-query chunks of the buckets
     P.tiles = L.take(BH * P.max_tiles * 2 * i4);
@@ -304,8 +304,8 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   if (mf) {
     a1.t_khi = at<uint16_t>(ws, P.t_khi);
     a1.t_klo = at<uint16_t>(ws, P.t_klo);
-    a1.t_vthi = at<uint16_t>(ws, P.t_vthi);
-    a1.t_vtlo = at<uint16_t>(ws, P.t_vtlo);
+    a1.t_vhi = at<uint16_t>(ws, P.t_vhi);
+    a1.t_vlo = at<uint16_t>(ws, P.t_vlo);
     a1.t_dip = at<uint16_t>(ws, P.t_dip);
   }
   RetrArgs ra{};
@@ -368,8 +368,8 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a2.s_dip = a1.s_dip;
   a2.t_khi = a1.t_khi;
   a2.t_klo = a1.t_klo;
-  a2.t_vthi = a1.t_vthi;
-  a2.t_vtlo = a1.t_vtlo;
+  a2.t_vhi = a1.t_vhi;
+  a2.t_vlo = a1.t_vlo;
   a2.t_dip = a1.t_dip;
   a2.perm_q = tq.perm;
   a2.offs_q = tq.offs;

@@ -107,8 +107,8 @@ struct S1Args {
   // bf16 copies for the matrix-core stage 2 (null on the fp32 path)
   uint16_t* t_khi;             // [BH, nbS, Cq, Ck, D]  K_ij = hi + lo
   uint16_t* t_klo;
-  uint16_t* t_vthi;            // [BH, nbS, Cq, D, Ck]  V_ij transposed, = hi + lo
-  uint16_t* t_vtlo;
+  uint16_t* t_vhi;             // [BH, nbS, Cq, Ck, D]  V_ij = hi + lo (row-major like K)
+  uint16_t* t_vlo;
   uint16_t* t_dip;             // [BH, nbS, Cq, D(v), D(k)]  s * D_i, value index first
   const RetrArgs* retr;        // retrieval: rewrites table entries before the dipole finalise
 };
@@ -138,8 +138,8 @@ struct S2Args {
   // matrix-core path (bf16 inputs)
   const uint16_t* t_khi;
   const uint16_t* t_klo;
-  const uint16_t* t_vthi;
-  const uint16_t* t_vtlo;
+  const uint16_t* t_vhi;
+  const uint16_t* t_vlo;
   const uint16_t* t_dip;
   const int32_t* perm_q;       // [BH, N] queries by (block, label)
   const int32_t* offs_q;       // [BH, nb*Cq + 1]

@@ -347,41 +347,30 @@ __global__ void __launch_bounds__(256) s1_dip_final_kernel(S1Args a) {
     }
 }
 
-// bf16 hi/lo copies of one table entry (i, e) for the matrix-core stage 2: K_ij
-// (row-major), V_ij transposed to [d][j] through 32 x 32 LDS tiles (reads and writes
-// both coalesced), and s * D_i (value index first, a straight copy).
+// bf16 hi/lo copies of one table entry (i, e) for the matrix-core stage 2: K_ij and
+// V_ij row-major, and s * D_i (value index first).
 __global__ void __launch_bounds__(256) s1_pack_kernel(S1Args a) {
-  __shared__ float tileV[32][33];
   const int i = blockIdx.x, e = blockIdx.y, bh = blockIdx.z;
   const int D = a.D, Ck = a.Ck, tid = threadIdx.x;
   const size_t sidx = (static_cast<size_t>(bh) * a.nbS + e) * a.Cq + i;
   const float* K = a.s_k + sidx * Ck * D;
   const float* V = a.s_v + sidx * Ck * D;
-  for (int x = tid; x < Ck * D; x += 256) {
-    const float k = K[x];
-    const uint16_t kh = f32_to_bf16_bits(k);
-    a.t_khi[sidx * Ck * D + x] = kh;
-    a.t_klo[sidx * Ck * D + x] = f32_to_bf16_bits(k - bf16_to_f32(kh));
-  }
-  const int tx = tid & 31, ty = tid >> 5;  // 32 x 8 threads
-  for (int j0 = 0; j0 < Ck; j0 += 32)
-    for (int d0 = 0; d0 < D; d0 += 32) {
-      __syncthreads();
-      for (int r = ty; r < 32; r += 8) {
-        const int j = j0 + r, d = d0 + tx;
-        tileV[r][tx] = j < Ck ? V[static_cast<size_t>(j) * D + d] : 0.f;
-      }
-      __syncthreads();
-      for (int r = ty; r < 32; r += 8) {
-        const int d = d0 + r, j = j0 + tx;
-        if (j >= Ck) continue;
-        const float v = tileV[tx][r];
-        const uint16_t vh = f32_to_bf16_bits(v);
-        const size_t o = sidx * Ck * D + static_cast<size_t>(d) * Ck + j;
-        a.t_vthi[o] = vh;
-        a.t_vtlo[o] = f32_to_bf16_bits(v - bf16_to_f32(vh));
-      }
+  for (int x = 4 * tid; x < Ck * D; x += 4 * 256) {
+    const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(K + x);
+    const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(V + x);
+    u16x4_t kh, kl, vh, vl;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      kh[q] = f32_to_bf16_bits(k4[q]);
+      kl[q] = f32_to_bf16_bits(k4[q] - bf16_to_f32(kh[q]));
+      vh[q] = f32_to_bf16_bits(v4[q]);
+      vl[q] = f32_to_bf16_bits(v4[q] - bf16_to_f32(vh[q]));
     }
+    *reinterpret_cast<u16x4_t*>(a.t_khi + sidx * Ck * D + x) = kh;
+    *reinterpret_cast<u16x4_t*>(a.t_klo + sidx * Ck * D + x) = kl;
+    *reinterpret_cast<u16x4_t*>(a.t_vhi + sidx * Ck * D + x) = vh;
+    *reinterpret_cast<u16x4_t*>(a.t_vlo + sidx * Ck * D + x) = vl;
+  }
   if (a.dipole) {
     const float* dip = a.s_dip + sidx * D * D;  // [dv][dk]
     for (int x = tid; x < D * D; x += 256) a.t_dip[sidx * D * D + x] = f32_to_bf16_bits(a.scale * dip[x]);

@@ -428,8 +428,8 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
 
 // Acausal tables for the matrix-core stage 2 in one pass: one workgroup (4 waves) per
 // (query centroid i, head). From the atoms of the single key block and the moment
-// slices it writes log Z_ij, the bf16 hi/lo tables of K_ij (row-major) and V_ij
-// (transposed), and s * D_i with
+// slices it writes log Z_ij, the bf16 hi/lo tables of K_ij and V_ij (row-major), and
+// s * D_i with
 //   D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T,
 // E_i[v k^T] the mass-weighted mean of the slice moments, preset (negated) in the
 // accumulator layout, and sum_j P_ij V_ij K_ij^T on the matrix cores with both operands
@@ -531,6 +531,8 @@ __global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
       if (j < Ck) {
         *reinterpret_cast<u16x4_t*>(a.t_khi + (sidx * Ck + j) * D + d4) = kh;
         *reinterpret_cast<u16x4_t*>(a.t_klo + (sidx * Ck + j) * D + d4) = kl;
+        *reinterpret_cast<u16x4_t*>(a.t_vhi + (sidx * Ck + j) * D + d4) = vh;
+        *reinterpret_cast<u16x4_t*>(a.t_vlo + (sidx * Ck + j) * D + d4) = vl;
       }
       *reinterpret_cast<u16x4_t*>(sKh + jj * ST + d4) = kh;
       *reinterpret_cast<u16x4_t*>(sKl + jj * ST + d4) = kl;
@@ -538,25 +540,6 @@ __global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
       *reinterpret_cast<u16x4_t*>(sVl + jj * ST + d4) = vl;
     }
     __syncthreads();
-    // V_ij transposed: eight consecutive j of one d per lane through the transpose read
-    for (int pr = wave; pr < NDT * (JC / 16); pr += 4) {
-      const int dt = pr % NDT, ks = pr / NDT;
-      const int jb = j0 + 16 * ks + 8 * h, d = 32 * dt + c;
-      const bf16x8_t th = lds_operand_tr(sVh, ST, 16 * ks, 32 * dt, lane);
-      const bf16x8_t tl = lds_operand_tr(sVl, ST, 16 * ks, 32 * dt, lane);
-      uint16_t* oh = a.t_vthi + (sidx * D + d) * Ck + jb;
-      uint16_t* ol = a.t_vtlo + (sidx * D + d) * Ck + jb;
-      if (jb + 8 <= Ck && (Ck & 7) == 0) {
-        *reinterpret_cast<u16x8_t*>(oh) = __builtin_bit_cast(u16x8_t, th);
-        *reinterpret_cast<u16x8_t*>(ol) = __builtin_bit_cast(u16x8_t, tl);
-      } else {
-        const u16x8_t uh = __builtin_bit_cast(u16x8_t, th), ul = __builtin_bit_cast(u16x8_t, tl);
-        for (int e = 0; e < 8 && jb + e < Ck; ++e) {
-          oh[e] = uh[e];
-          ol[e] = ul[e];
-        }
-      }
-    }
     // sum_j P_ij V_ij K_ij^T over the chunk
     if (a.dipole) {
 #pragma unroll

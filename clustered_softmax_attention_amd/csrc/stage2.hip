@@ -139,27 +139,27 @@ __global__ void __launch_bounds__(256) s2_tiles_kernel(S2Args a) {
 // bucket (wave w: queries 32 w .. 32 w + 31 of the chunk). The bucket's tables stream
 // through LDS in chunks of 32 key clusters (cooperative 16-byte loads, the next chunk in
 // registers while the current one is used), with an online softmax across chunks.
-// LDS: K hi/lo [32][D+8] | V^T hi/lo [D][32+8] | log Z [32] | s D_i [D][D+8] (bf16).
+// LDS: K hi/lo, V hi/lo [32][D+16] row-major | log Z [32] | s D_i [D][D+8] (bf16); the
+// V^T operand of O^T = V^T P^T comes from the row-major V rows by the transpose read in
+// the key order of the P accumulator.
 template <int D>
 struct S2Cfg {
   static constexpr int JC = 32;
-  static constexpr int KST = D + 8;
-  static constexpr int VST = JC + 8;
+  static constexpr int KST = D + 16;
   static constexpr int DST = D + 8;
-  static constexpr int NK = JC * D / 8 / 256;   // 16-byte K pieces per thread and part (hi, lo)
-  static constexpr int NV = D * JC / 8 / 256;   // 16-byte V^T pieces per thread and part
+  static constexpr int NK = JC * D / 8 / 256;   // 16-byte K (and V) pieces per thread and part (hi, lo)
   static constexpr int ND = D * D / 8 / 256;    // 16-byte dipole pieces per thread
 };
 
 template <int D>
 __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a) {
   using Cfg = S2Cfg<D>;
-  constexpr int NKS = D / 16, NMT = D / 32, JC = Cfg::JC, KST = Cfg::KST, VST = Cfg::VST, DST = Cfg::DST;
-  constexpr int NK = Cfg::NK, NV = Cfg::NV, ND = Cfg::ND;
+  constexpr int NKS = D / 16, NMT = D / 32, JC = Cfg::JC, KST = Cfg::KST, DST = Cfg::DST;
+  constexpr int NK = Cfg::NK, ND = Cfg::ND;
   __shared__ __align__(16) uint16_t sKh[JC * KST];
   __shared__ __align__(16) uint16_t sKl[JC * KST];
-  __shared__ __align__(16) uint16_t sVh[D * VST];
-  __shared__ __align__(16) uint16_t sVl[D * VST];
+  __shared__ __align__(16) uint16_t sVh[JC * KST];
+  __shared__ __align__(16) uint16_t sVl[JC * KST];
   __shared__ __align__(16) uint16_t sDip[D * DST];
   __shared__ float slz[JC];
   const int bh = blockIdx.y, tid = threadIdx.x;
@@ -188,13 +188,12 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
   const int Ck = a.Ck, njc = (Ck + JC - 1) / JC;
   const uint16_t* khi = a.t_khi + sidx * Ck * D;
   const uint16_t* klo = a.t_klo + sidx * Ck * D;
-  const uint16_t* vthi = a.t_vthi + sidx * Ck * D;
-  const uint16_t* vtlo = a.t_vtlo + sidx * Ck * D;
+  const uint16_t* vhi = a.t_vhi + sidx * Ck * D;
+  const uint16_t* vlo = a.t_vlo + sidx * Ck * D;
   const float* lz = a.s_logz + sidx * Ck;
-  const bool vec = (Ck & 7) == 0;  // 16-byte aligned rows of V^T
 
   // chunk jc of the tables into registers
-  u16x8_t pkh[NK], pkl[NK], pvh[NV], pvl[NV];
+  u16x8_t pkh[NK], pkl[NK], pvh[NK], pvl[NK];
   float plz = kNegInf;
   auto load_chunk = [&](int jc) {
     const int j0 = jc * JC;
@@ -203,25 +202,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
       const int x = tid + 256 * q, jj = x / (D / 8), d8 = (x % (D / 8)) * 8;
       pkh[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       pkl[q] = pkh[q];
+      pvh[q] = pkh[q];
+      pvl[q] = pkh[q];
       if (j0 + jj < Ck) {
-        pkh[q] = *reinterpret_cast<const u16x8_t*>(khi + static_cast<size_t>(j0 + jj) * D + d8);
-        pkl[q] = *reinterpret_cast<const u16x8_t*>(klo + static_cast<size_t>(j0 + jj) * D + d8);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      const int x = tid + 256 * q, d = x / (JC / 8), j8 = (x % (JC / 8)) * 8;
-      const size_t o = static_cast<size_t>(d) * Ck + j0 + j8;
-      pvh[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      pvl[q] = pvh[q];
-      if (vec && j0 + j8 + 8 <= Ck) {
-        pvh[q] = *reinterpret_cast<const u16x8_t*>(vthi + o);
-        pvl[q] = *reinterpret_cast<const u16x8_t*>(vtlo + o);
-      } else {
-        for (int r = 0; r < 8 && j0 + j8 + r < Ck; ++r) {
-          pvh[q][r] = vthi[o + r];
-          pvl[q][r] = vtlo[o + r];
-        }
+        const size_t o = static_cast<size_t>(j0 + jj) * D + d8;
+        pkh[q] = *reinterpret_cast<const u16x8_t*>(khi + o);
+        pkl[q] = *reinterpret_cast<const u16x8_t*>(klo + o);
+        pvh[q] = *reinterpret_cast<const u16x8_t*>(vhi + o);
+        pvl[q] = *reinterpret_cast<const u16x8_t*>(vlo + o);
       }
     }
     plz = (tid < JC && j0 + tid < Ck) ? lz[j0 + tid] : kNegInf;
@@ -262,12 +250,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
       const int x = tid + 256 * q, jj = x / (D / 8), d8 = (x % (D / 8)) * 8;
       *reinterpret_cast<u16x8_t*>(sKh + jj * KST + d8) = pkh[q];
       *reinterpret_cast<u16x8_t*>(sKl + jj * KST + d8) = pkl[q];
-    }
-#pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      const int x = tid + 256 * q, d = x / (JC / 8), j8 = (x % (JC / 8)) * 8;
-      *reinterpret_cast<u16x8_t*>(sVh + d * VST + j8) = pvh[q];
-      *reinterpret_cast<u16x8_t*>(sVl + d * VST + j8) = pvl[q];
+      *reinterpret_cast<u16x8_t*>(sVh + jj * KST + d8) = pvh[q];
+      *reinterpret_cast<u16x8_t*>(sVl + jj * KST + d8) = pvl[q];
     }
     if (tid < JC) slz[tid] = plz;
     __syncthreads();
@@ -322,15 +306,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
       split_bf16x8(pv, phi, plo);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
-        const uint16_t* vh = sVh + (32 * mt + c) * VST + 16 * ss + 4 * h;
-        const uint16_t* vl = sVl + (32 * mt + c) * VST + 16 * ss + 4 * h;
-        const u16x4_t h0 = *reinterpret_cast<const u16x4_t*>(vh), h1 = *reinterpret_cast<const u16x4_t*>(vh + 8);
-        const u16x4_t l0 = *reinterpret_cast<const u16x4_t*>(vl), l1 = *reinterpret_cast<const u16x4_t*>(vl + 8);
-        const u16x8_t hv = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-        const u16x8_t lv = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-        o[mt] = mfma32(as_bf16x8(hv), phi, o[mt]);
-        o[mt] = mfma32(as_bf16x8(hv), plo, o[mt]);
-        o[mt] = mfma32(as_bf16x8(lv), phi, o[mt]);
+        const bf16x8_t hv = lds_operand_tr_acc(sVh, KST, 16 * ss, 32 * mt, lane);
+        const bf16x8_t lv = lds_operand_tr_acc(sVl, KST, 16 * ss, 32 * mt, lane);
+        o[mt] = mfma32(hv, phi, o[mt]);
+        o[mt] = mfma32(hv, plo, o[mt]);
+        o[mt] = mfma32(lv, phi, o[mt]);
       }
     }
   }
