@@ -381,12 +381,13 @@ template <typename T, int D>
 static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   constexpr int kS1Keys = S1Keys<D>::value;
   const bool mf = sizeof(T) == 2;  // bf16 inputs: matrix-core kernels
-  if (mf && !a.causal) {
-    // acausal: one table entry per (head, i), finalised in a single pass
+  if (mf && a.retr == nullptr) {
+    // acausal: one table entry per (head, i), finalised in a single pass; causal without
+    // retrieval: one scan over the blocks writes every entry
     launch_stage1_mfma(a, 0, s);
     launch_stage1_mfma(a, 1, s);
     if (a.dipole) launch_stage1_mfma(a, 2, s);
-    launch_stage1_mfma(a, 3, s);
+    launch_stage1_mfma(a, a.causal ? 4 : 3, s);
     return;
   }
   if (mf) {

@@ -580,6 +580,273 @@ __global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
   }
 }
 
+// Causal tables in one scan over the blocks: one workgroup (8 or 16 waves) per (query
+// centroid i, head) walks the blocks in order with the prefix over earlier blocks in
+// registers — per key cluster j the log-sum-exp fold (m_j, z_j, sum w k, sum w v) of the
+// atoms, and the mass-weighted sum of the block moments — and at every block b >= 1
+// writes entry b of the stage-2 tables: log Z_ij, bf16 hi/lo K_ij and V_ij (row-major),
+// and  s * D_i = s * (E_i[v k^T] - sum_j P_ij V_ij K_ij^T)  with the sum over j on the
+// matrix cores (operands split into bf16 hi + lo, read by the transpose read from LDS
+// tiles of 32 clusters). Then block b is folded in.
+// Thread mapping: float4 e4 = tid + T r of the [Ck][D] sums, i.e. cluster
+// j = e4 / (D/4); the 32-cluster chunk cc holds the thread's float4s r = RPC cc .. RPC cc + RPC - 1.
+template <int D>
+struct ScanCfg {
+  static constexpr int NW = D == 128 ? 16 : 8;
+  static constexpr int T = 64 * NW;
+  static constexpr int NE4 = kMaxClusters * D / 4 / T;  // float4s per thread and tensor
+  static constexpr int RPC = 32 * (D / 4) / T;          // of them per 32-cluster chunk
+  static constexpr int NDT = D / 32;
+  static constexpr int NT = NDT * NDT;                  // dipole output tiles
+  static constexpr int TPW = NT / NW > 0 ? NT / NW : 1;  // per wave
+  static constexpr int ST = D + 16;
+  static constexpr bool PREF = D == 64;  // atoms requested before the entry is written (registers allow)
+};
+
+template <int D>
+__global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a) {
+  using Cfg = ScanCfg<D>;
+  constexpr int NW = Cfg::NW, T = Cfg::T, NE4 = Cfg::NE4, RPC = Cfg::RPC, NDT = Cfg::NDT, NT = Cfg::NT;
+  constexpr int TPW = Cfg::TPW, ST = Cfg::ST;
+  constexpr int JC = 32;
+  __shared__ __align__(16) uint16_t sKh[JC * ST];
+  __shared__ __align__(16) uint16_t sKl[JC * ST];
+  __shared__ __align__(16) uint16_t sVh[JC * ST];
+  __shared__ __align__(16) uint16_t sVl[JC * ST];
+  __shared__ __align__(16) float sP[kMaxClusters];
+  __shared__ float sm[kMaxClusters], sz[kMaxClusters], sfo[kMaxClusters], sfn[kMaxClusters], sinv[kMaxClusters];
+  __shared__ float red[2 * NW];
+  __shared__ float sE[D * D];  // sum over folded ranges of exp(R - Rm) * moment, [dv][dk]
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int Cq = a.Cq, Ck = a.Ck, nb = a.nb;
+  const int per = a.block / a.mbk;  // moment ranges per block
+  auto tile_of = [&](int t, int& dvt, int& dkt) {
+    const int ot = wave * TPW + t;
+    dvt = ot / NDT;
+    dkt = ot % NDT;
+    return ot < NT;
+  };
+
+  // prefix state
+  f32x4_t ks[NE4], vs[NE4];
+#pragma unroll
+  for (int r = 0; r < NE4; ++r) {
+    ks[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    vs[r] = ks[r];
+  }
+  if (tid < kMaxClusters) {
+    sm[tid] = kNegInf;
+    sz[tid] = 0.f;
+  }
+  for (int e = tid; e < D * D; e += T) sE[e] = 0.f;
+  float Rm = kNegInf, W = 0.f;
+
+  for (int b = 0; b < nb; ++b) {
+    const bool fold = b + 1 < nb;
+    const size_t abase = ((static_cast<size_t>(bh) * nb + b) * Cq + i) * Ck;
+    f32x4_t pk[Cfg::PREF ? NE4 : 1], pv[Cfg::PREF ? NE4 : 1];
+    auto load_atoms = [&] {
+#pragma unroll
+      for (int r = 0; r < NE4; ++r) {
+        const int e4 = tid + T * r;
+        pk[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pv[r] = pk[r];
+        if (e4 < Ck * D / 4) {
+          pk[r] = *reinterpret_cast<const f32x4_t*>(a.at_k + abase * D + 4 * static_cast<size_t>(e4));
+          pv[r] = *reinterpret_cast<const f32x4_t*>(a.at_v + abase * D + 4 * static_cast<size_t>(e4));
+        }
+      }
+    };
+    if (Cfg::PREF && fold) load_atoms();  // lands while entry b is written
+    __syncthreads();  // sm, sz of the prefix are final
+    if (b > 0) {
+      // ---- entry b: log Z, P, normalised tables ----
+      float lz = kNegInf;
+      if (tid < Ck) {
+        const float z = sz[tid];
+        lz = z > 0.f ? sm[tid] + __logf(z) : kNegInf;
+        a.s_logz[((static_cast<size_t>(bh) * a.nbS + b) * Cq + i) * Ck + tid] = lz;
+        sinv[tid] = z > 0.f ? 1.f / z : 0.f;
+      }
+      float mx = wave_max(lz);
+      if (lane == 0) red[wave] = mx;
+      __syncthreads();
+      mx = kNegInf;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red[w]);
+      const float p = (tid < Ck && lz != kNegInf) ? __expf(lz - mx) : 0.f;
+      const float ps = wave_sum(p);
+      if (lane == 0) red[NW + wave] = ps;
+      __syncthreads();
+      float psum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) psum += red[NW + w];
+      if (tid < kMaxClusters) sP[tid] = psum > 0.f ? p / psum : 0.f;
+      const size_t tbase = ((static_cast<size_t>(bh) * a.nbS + b) * Cq + i) * static_cast<size_t>(Ck) * D;
+      f32x16_t dacc[TPW];
+      {
+        const float winv = W > 0.f ? 1.f / W : 0.f;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          int dvt, dkt;
+          dacc[t] = zero16();
+          if (!tile_of(t, dvt, dkt)) continue;
+#pragma unroll
+          for (int v = 0; v < 16; ++v)  // -E_i[v k^T] of the prefix
+            dacc[t][v] = -sE[(32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3)) * D + 32 * dkt + c] * winv;
+        }
+      }
+#pragma unroll
+      for (int cc = 0; cc < kMaxClusters / JC; ++cc) {
+        if (cc * JC >= Ck) break;  // uniform
+#pragma unroll
+        for (int q = 0; q < RPC; ++q) {
+          const int r = cc * RPC + q;  // compile-time after unrolling
+          const int e4 = tid + T * r, j = e4 / (D / 4), d4 = (e4 % (D / 4)) * 4, jj = j - JC * cc;
+          const f32x4_t kf = ks[r], vf = vs[r];
+          const float inv = j < Ck ? sinv[j] : 0.f;
+          u16x4_t kh, kl, vh, vl;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float kk = kf[e] * inv, vv = vf[e] * inv;
+            kh[e] = f32_to_bf16_bits(kk);
+            kl[e] = f32_to_bf16_bits(kk - bf16_to_f32(kh[e]));
+            vh[e] = f32_to_bf16_bits(vv);
+            vl[e] = f32_to_bf16_bits(vv - bf16_to_f32(vh[e]));
+          }
+          if (j < Ck) {
+            *reinterpret_cast<u16x4_t*>(a.t_khi + tbase + 4 * static_cast<size_t>(e4)) = kh;
+            *reinterpret_cast<u16x4_t*>(a.t_klo + tbase + 4 * static_cast<size_t>(e4)) = kl;
+            *reinterpret_cast<u16x4_t*>(a.t_vhi + tbase + 4 * static_cast<size_t>(e4)) = vh;
+            *reinterpret_cast<u16x4_t*>(a.t_vlo + tbase + 4 * static_cast<size_t>(e4)) = vl;
+          }
+          if (a.dipole) {
+            *reinterpret_cast<u16x4_t*>(sKh + jj * ST + d4) = kh;
+            *reinterpret_cast<u16x4_t*>(sKl + jj * ST + d4) = kl;
+            *reinterpret_cast<u16x4_t*>(sVh + jj * ST + d4) = vh;
+            *reinterpret_cast<u16x4_t*>(sVl + jj * ST + d4) = vl;
+          }
+        }
+        if (!a.dipole) continue;
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          int dvt, dkt;
+          if (!tile_of(t, dvt, dkt)) break;
+#pragma unroll
+          for (int ks2 = 0; ks2 < 2; ++ks2) {
+            const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(sP + JC * cc + 16 * ks2 + 8 * h);
+            const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(sP + JC * cc + 16 * ks2 + 8 * h + 4);
+            const float pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            const u16x8_t uh = __builtin_bit_cast(u16x8_t, lds_operand_tr(sVh, ST, 16 * ks2, 32 * dvt, lane));
+            const u16x8_t ul = __builtin_bit_cast(u16x8_t, lds_operand_tr(sVl, ST, 16 * ks2, 32 * dvt, lane));
+            float av[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) av[e] = (bf16_to_f32(uh[e]) + bf16_to_f32(ul[e])) * pw[e];
+            bf16x8_t ah, al;
+            split_bf16x8(av, ah, al);
+            const bf16x8_t kh8 = lds_operand_tr(sKh, ST, 16 * ks2, 32 * dkt, lane);
+            const bf16x8_t kl8 = lds_operand_tr(sKl, ST, 16 * ks2, 32 * dkt, lane);
+            dacc[t] = mfma32(ah, kh8, dacc[t]);
+            dacc[t] = mfma32(ah, kl8, dacc[t]);
+            dacc[t] = mfma32(al, kh8, dacc[t]);
+          }
+        }
+        __syncthreads();  // the next chunk overwrites the tiles
+      }
+      if (a.dipole) {
+        // dacc = sum P V K^T - E = -D_i
+        uint16_t* dip = a.t_dip + ((static_cast<size_t>(bh) * a.nbS + b) * Cq + i) * D * D;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          int dvt, dkt;
+          if (!tile_of(t, dvt, dkt)) break;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = 32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3);
+            dip[static_cast<size_t>(row) * D + 32 * dkt + c] = f32_to_bf16_bits(-a.scale * dacc[t][v]);
+          }
+        }
+      }
+    }
+    if (!fold) break;
+    // ---- fold block b ----
+    if (tid < Ck) {
+      const float am = a.at_m[abase + tid], az = a.at_z[abase + tid];
+      const float m0 = sm[tid], z0 = sz[tid];
+      float fo = 1.f, fn = 0.f;
+      if (az > 0.f) {
+        const float mn = fmaxf(m0, am);
+        fo = z0 > 0.f ? __expf(m0 - mn) : 0.f;
+        fn = __expf(am - mn);
+        sm[tid] = mn;
+        sz[tid] = z0 * fo + az * fn;
+      }
+      sfo[tid] = fo;
+      sfn[tid] = fn;
+    }
+    if (a.dipole) {
+      for (int sub = 0; sub < per; ++sub) {
+        const size_t bidx = (static_cast<size_t>(bh) * a.nmb + b * per + sub) * Cq + i;
+        const float R = a.blk_lmass[bidx];
+        if (R == kNegInf) continue;
+        const float* M = a.blk_mom + bidx * D * D;
+        const float Rn = fmaxf(Rm, R);
+        const float fo = Rm == kNegInf ? 0.f : __expf(Rm - Rn), fn = __expf(R - Rn);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          int dvt, dkt;
+          if (!tile_of(t, dvt, dkt)) break;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = 32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3);
+            float* pe = sE + row * D + 32 * dkt + c;  // this lane's element
+            *pe = *pe * fo + M[static_cast<size_t>(row) * D + 32 * dkt + c] * fn;
+          }
+        }
+        W = W * fo + fn;
+        Rm = Rn;
+      }
+    }
+    __syncthreads();  // sfo, sfn
+    if (Cfg::PREF) {
+#pragma unroll
+      for (int r = 0; r < NE4; ++r) {
+        const int e4 = tid + T * r, j = e4 / (D / 4);
+        if (j >= Ck) continue;
+        const float fo = sfo[j], fn = sfn[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ks[r][q] = ks[r][q] * fo + pk[r][q] * fn;
+          vs[r][q] = vs[r][q] * fo + pv[r][q] * fn;
+        }
+      }
+    } else {
+      // one tensor at a time (registers)
+      auto fold_tensor = [&](const float* src, f32x4_t (&st)[NE4]) {
+        f32x4_t pr[NE4];
+#pragma unroll
+        for (int r = 0; r < NE4; ++r) {
+          const int e4 = tid + T * r;
+          pr[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (e4 < Ck * D / 4) pr[r] = *reinterpret_cast<const f32x4_t*>(src + abase * D + 4 * static_cast<size_t>(e4));
+        }
+#pragma unroll
+        for (int r = 0; r < NE4; ++r) {
+          const int e4 = tid + T * r, j = e4 / (D / 4);
+          if (j >= Ck) continue;
+          const float fo = sfo[j], fn = sfn[j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) st[r][q] = st[r][q] * fo + pr[r][q] * fn;
+        }
+      };
+      fold_tensor(a.at_k, ks);
+      fold_tensor(a.at_v, vs);
+    }
+  }
+}
+
 template <int D>
 static void launch_t(const S1Args& a, int which, hipStream_t s) {
   if (which == 0) {
@@ -594,13 +861,16 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
     constexpr int G = MomCfg<D>::G;
     ProfScope ps_("s1_moments_f16", s);
     hipLaunchKernelGGL((s1_moments_f16_kernel<D>), dim3(a.nmb, (a.Cq + G - 1) / G, a.BH), dim3(512), 0, s, a);
-  } else {
+  } else if (which == 3) {
     ProfScope ps_("s1_finalize", s);
     hipLaunchKernelGGL((s1_finalize_acausal_kernel<D>), dim3(a.Cq, a.BH), dim3(256), 0, s, a);
+  } else {
+    ProfScope ps_("s1_causal_scan", s);
+    hipLaunchKernelGGL((s1_causal_scan_kernel<D>), dim3(a.Cq, a.BH), dim3(ScanCfg<D>::T), 0, s, a);
   }
 }
 
-// which: 0 scores, 1 atoms, 2 moments, 3 acausal table finalise
+// which: 0 scores, 1 atoms, 2 moments, 3 acausal table finalise, 4 causal scan
 void launch_stage1_mfma(const S1Args& a, int which, hipStream_t s) {
   if (a.D == 64) launch_t<64>(a, which, s);
   else launch_t<128>(a, which, s);
