@@ -5,9 +5,10 @@
 //   L = log(e^L_loc + e^L_far),  o = e^(L_loc - L) o_loc + e^(L_far - L) o_far.
 //
 // bf16 path (flash_bf16): workgroup of 4 waves = 128 queries; key/value tiles of 64
-// keys staged in LDS (K row-major, V transposed); per wave S^T = K Q^T on the matrix
-// cores (32 keys x 32 queries per tile), online softmax along accumulator rows (one
-// lane and its partner), O^T += V^T P^T with P rounded to bf16. Workgroups are
+// keys staged row-major in LDS (the next tile in registers meanwhile); per wave
+// S^T = K Q^T on the matrix cores (32 keys x 32 queries per tile), online softmax along
+// accumulator rows (one lane and its partner), O^T += V^T P^T with P rounded to bf16 and
+// V^T read by the transpose read in the key order of the P accumulator. Workgroups are
 // renumbered so that those of one head run on one XCD and share its L2.
 // fp32 path: one thread per query, online softmax over chunks of 32 keys; all lanes
 // of a wave visit the same key at the same time, so key and value rows are read
@@ -120,15 +121,15 @@ __device__ __forceinline__ int xcd_swizzle(int id, int total) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(256) flash_bf16_kernel(ExactArgs a, int nqt) {
+__global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt) {
   constexpr int BQ = 128, BK = 64;
-  constexpr int KST = D + 8;  // bf16 elements per K row in LDS (padded)
-  constexpr int VST = BK + 8; // bf16 elements per V^T row in LDS (padded)
+  constexpr int KST = D + 16;  // bf16 elements per K and V row in LDS (padded)
   constexpr int NKS = D / 16;
   constexpr int NMT = D / 32;
-  constexpr int CH = D / 8;   // 16-byte chunks per row
+  constexpr int CH = D / 8;    // 16-byte chunks per row
+  constexpr int NP = BK * CH / 256;  // 16-byte pieces per thread and tensor
   __shared__ __align__(16) uint16_t sK[BK * KST];
-  __shared__ __align__(16) uint16_t sVt[D * VST];
+  __shared__ __align__(16) uint16_t sV[BK * KST];
 
   const int total = nqt * a.BH;
   const int id = xcd_swizzle(blockIdx.x, total);
@@ -167,21 +168,31 @@ __global__ void __launch_bounds__(256) flash_bf16_kernel(ExactArgs a, int nqt) {
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) o[mt] = zero16();
 
-  for (int kt = gkb; kt < gke; kt += BK) {
-    __syncthreads();
-    for (int e = tid; e < BK * CH; e += 256) {
-      const int r = e / CH, cc = e % CH;
-      const int key = kt + r;
-      u16x8_t kv = {0, 0, 0, 0, 0, 0, 0, 0}, vv = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (key < N) {
-        kv = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(key) * D + cc * 8);
-        vv = *reinterpret_cast<const u16x8_t*>(V + static_cast<size_t>(key) * D + cc * 8);
-      }
-      *reinterpret_cast<u16x8_t*>(sK + r * KST + cc * 8) = kv;
+  // the next tile's rows travel in registers while the current one is used
+  u16x8_t pk[NP], pv[NP];
+  auto load_tile = [&](int kt) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sVt[(cc * 8 + i) * VST + r] = vv[i];
+    for (int q = 0; q < NP; ++q) {
+      const int e = tid + 256 * q, r = e / CH, cc = e % CH, key = kt + r;
+      pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      pv[q] = pk[q];
+      if (key < N) {
+        pk[q] = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(key) * D + cc * 8);
+        pv[q] = *reinterpret_cast<const u16x8_t*>(V + static_cast<size_t>(key) * D + cc * 8);
+      }
+    }
+  };
+  if (gkb < gke) load_tile(gkb);
+  for (int kt = gkb; kt < gke; kt += BK) {
+    __syncthreads();  // the previous tile is consumed
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int e = tid + 256 * q, r = e / CH, cc = e % CH;
+      *reinterpret_cast<u16x8_t*>(sK + r * KST + cc * 8) = pk[q];
+      *reinterpret_cast<u16x8_t*>(sV + r * KST + cc * 8) = pv[q];
     }
     __syncthreads();
+    if (kt + BK < gke) load_tile(kt + BK);
     if (kt >= wke_max || kt + BK <= wkb_min) continue;  // tile outside every row of this wave
     const bool full = kt >= wkb_max && kt + BK <= wke_min && kt + BK <= N;
 
@@ -234,13 +245,8 @@ __global__ void __launch_bounds__(256) flash_bf16_kernel(ExactArgs a, int nqt) {
         for (int i = 0; i < 8; ++i) pv[i] = s[t][8 * ss + i];
         const bf16x8_t bfr = pack_bf16x8(pv);
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-          const uint16_t* row = sVt + (32 * mt + c) * VST + 32 * t + 16 * ss + 4 * h;
-          const u16x4_t lo4 = *reinterpret_cast<const u16x4_t*>(row);
-          const u16x4_t hi4 = *reinterpret_cast<const u16x4_t*>(row + 8);
-          const u16x8_t u = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-          o[mt] = mfma32(as_bf16x8(u), bfr, o[mt]);
-        }
+        for (int mt = 0; mt < NMT; ++mt)
+          o[mt] = mfma32(lds_operand_tr_acc(sV, KST, 32 * t + 16 * ss, 32 * mt, lane), bfr, o[mt]);
       }
   }
   const float lt = l + xor32(l);
