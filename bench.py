@@ -50,7 +50,12 @@ def kernel_work(name: str, cfg):
     BH, N, D, Cq, Ck = cfg.B * cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck
     e = 2 if cfg.dtype == "bf16" else 4
     nb = cfg.N // cfg.block if cfg.causal else 1
-    mbk = cfg.block if cfg.causal else (1024 if cfg.dtype == "bf16" else N)
+    if cfg.causal or cfg.dtype != "bf16":
+        mbk = cfg.block if cfg.causal else N
+    else:  # the library's acausal moment slices: about 256 workgroups, multiples of 128 keys
+        groups = -(-Cq // (16 if D == 64 else 4))
+        want = max(1, -(-256 // (groups * BH)))
+        mbk = min(-(-(-(-N // want)) // 128) * 128, 8192)
     nmb = (N + mbk - 1) // mbk
     x = BH * N * D * e                      # one [B, H, N, D] input tensor
     table = BH * nb * Cq * Ck               # (entry, i, j) cells

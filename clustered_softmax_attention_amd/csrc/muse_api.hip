@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -80,10 +81,14 @@ int validate(Shape& s, const muse_fwd_params* p) {
   }
   s.ntiles = (s.N + s.tile - 1) / s.tile;
   // moment key ranges: a causal block (split into equal ranges of at most kMaxMomKeys
-  // positions for the matrix-core kernel), or for an acausal bf16 call slices of 1024
-  // positions (parallelism)
+  // positions for the matrix-core kernel); for an acausal bf16 call, slices sized so that
+  // the moment kernel has about 256 workgroups (multiples of its 128-key chunk)
   if (s.dtype == MUSE_BF16 && !s.causal) {
-    s.mbk = 1024;
+    const int groups = (s.Cq + muse::moments_group(s.D) - 1) / muse::moments_group(s.D);
+    const int want = std::max(1, (256 + groups * s.BH - 1) / (groups * s.BH));
+    int slice = (s.N + want - 1) / want;
+    slice = (slice + 127) / 128 * 128;
+    s.mbk = std::min(slice, muse::kMaxMomKeys);
   } else {
     s.mbk = s.block;
     if (s.dtype == MUSE_BF16)

@@ -10,6 +10,8 @@ constexpr int kMaxTile = 512;  // K-means tile (points per workgroup) upper boun
 constexpr int kMaxTileMfma = 256;  // the same for the matrix-core (bf16) path
 constexpr int kMaxClusters = 128;
 constexpr int kMaxMomKeys = 8192;  // positions per block-moment range (matrix-core path)
+// query centroids per workgroup of the matrix-core moment kernel
+constexpr int moments_group(int D) { return D == 64 ? 16 : 4; }
 
 // ------------------------------------------------------------------ K-means
 

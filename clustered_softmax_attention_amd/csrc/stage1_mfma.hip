@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) s1_atoms_mfma_kernel(S1A
 // 4 key tiles. Output [dv][dk], normalised by the range's weight sum.
 template <int D>
 struct MomCfg {
-  static constexpr int G = D == 64 ? 16 : 4;   // centroids per workgroup
+  static constexpr int G = moments_group(D);   // centroids per workgroup
   static constexpr int CW = D == 64 ? 2 : 1;   // centroids per wave
   static constexpr int NDV = 2;                // value tiles per wave
   static constexpr int NDK = D / 32;           // key tiles per wave
