@@ -247,7 +247,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) s1_atoms_mfma_kernel(S1A
 // order (a causal block, or a slice of an acausal sequence; at most kMaxMomKeys
 // positions, whose permutation entries are staged in LDS): one workgroup of 8 waves
 // per (range, group of G centroids, head). Weights w = exp(a - max over the range) come
-// from the scores; every 128-key chunk of K and V rows is gathered once, converted to
+// from the scores; every chunk of K and V rows (128 keys at D = 64, 64 at D = 128) is
+// gathered once, converted to
 // fp16 (exact for bf16 values in fp16 range) and stored row-major in LDS, where the
 // transpose read hands both MFMA operands over with the key index along k:
 //   sum_m w_m v_m k_m^T = (V^T diag(w)) K,  A = v fragment * w (packed fp16), B = k fragment.
@@ -260,20 +261,22 @@ struct MomCfg {
   static constexpr int CW = D == 64 ? 2 : 1;   // centroids per wave
   static constexpr int NDV = 2;                // value tiles per wave
   static constexpr int NDK = D / 32;           // key tiles per wave
-  static constexpr int KC = 128;               // keys per chunk
+  static constexpr int KC = D == 64 ? 128 : 64;  // keys per chunk (two chunks are in LDS)
   static constexpr int ST = D + 16;            // LDS row stride (fp16 elements)
   static constexpr int NPRE = KC * (D / 8) / 512;  // 16-byte row pieces per thread and tensor
   static constexpr int NWQ = (G * KC + 511) / 512;   // chunk weights per thread
 };
 
+// LDS holds two chunks (rows and weights): chunk c is used from one buffer while chunk
+// c + 1 is written to the other and chunk c + 2 travels in registers; one barrier per chunk.
 template <int D>
 __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
   using Cfg = MomCfg<D>;
   constexpr int G = Cfg::G, CW = Cfg::CW, NDV = Cfg::NDV, NDK = Cfg::NDK, KC = Cfg::KC, ST = Cfg::ST;
   constexpr int NPRE = Cfg::NPRE, NWQ = Cfg::NWQ;
-  __shared__ __align__(16) uint16_t sK[KC * ST];
-  __shared__ __align__(16) uint16_t sV[KC * ST];
-  __shared__ __align__(16) _Float16 sw[G * KC];
+  __shared__ __align__(16) uint16_t sK[2][KC * ST];
+  __shared__ __align__(16) uint16_t sV[2][KC * ST];
+  __shared__ __align__(16) _Float16 sw[2][G * KC];
   __shared__ int s_perm[kMaxMomKeys];
   __shared__ float smx[G], ssum[G], spart[G * KC / 64];
   const int mb = blockIdx.x, ig = blockIdx.y, bh = blockIdx.z;
@@ -296,7 +299,6 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
   }
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
-  // the next chunk's rows and scores travel in registers while the current one is used
   u16x8_t pk[NPRE], pv[NPRE];
   float ps[NWQ];
   auto load_chunk = [&](int c0) {
@@ -327,11 +329,36 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
     for (int e = 0; e < 8; ++e) o[e] = static_cast<_Float16>(bf16_to_f32(u[e]));
     return __builtin_bit_cast(u16x8_t, o);
   };
-  __syncthreads();  // s_perm, smx
-  load_chunk(0);
   float wsum[NWQ];
 #pragma unroll
   for (int q = 0; q < NWQ; ++q) wsum[q] = 0.f;
+  // registers -> LDS buffer bf
+  auto stage = [&](int bf) {
+#pragma unroll
+    for (int q = 0; q < NPRE; ++q) {
+      const int x = tid + 512 * q;
+      const int r = x / (D / 8), c8 = x % (D / 8);
+      *reinterpret_cast<u16x8_t*>(&sK[bf][r * ST + c8 * 8]) = to_f16(pk[q]);
+      *reinterpret_cast<u16x8_t*>(&sV[bf][r * ST + c8 * 8]) = to_f16(pv[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < NWQ; ++q) {
+      const int x = tid + 512 * q;
+      if (x >= G * KC) break;
+      const int g = x / KC;
+      const _Float16 wh = static_cast<_Float16>(ps[q] == kNegInf ? 0.f : __expf(ps[q] - smx[g]));
+      sw[bf][x] = wh;
+      wsum[q] += static_cast<float>(wh);
+    }
+  };
+  __syncthreads();  // s_perm, smx
+  const int nch = (nkeys + KC - 1) / KC;
+  if (nch > 0) {
+    load_chunk(0);
+    stage(0);
+  }
+  if (nch > 1) load_chunk(KC);
+  __syncthreads();
 
   f32x16_t acc[CW][NDV][NDK];
 #pragma unroll
@@ -343,39 +370,21 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
   const int gw = D == 64 ? CW * wave : wave / 2;         // first centroid (in the group) of this wave
   const int dv0 = D == 64 ? 0 : NDV * (wave & 1);        // first value tile of this wave
 
-  for (int c0 = 0; c0 < nkeys; c0 += KC) {
-    // stage the chunk: rows (fp16) and weights
-#pragma unroll
-    for (int q = 0; q < NPRE; ++q) {
-      const int x = tid + 512 * q;
-      const int r = x / (D / 8), c8 = x % (D / 8);
-      *reinterpret_cast<u16x8_t*>(sK + r * ST + c8 * 8) = to_f16(pk[q]);
-      *reinterpret_cast<u16x8_t*>(sV + r * ST + c8 * 8) = to_f16(pv[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < NWQ; ++q) {
-      const int x = tid + 512 * q;
-      if (x >= G * KC) break;
-      const int g = x / KC;
-      const _Float16 wh = static_cast<_Float16>(ps[q] == kNegInf ? 0.f : __expf(ps[q] - smx[g]));
-      sw[x] = wh;
-      wsum[q] += static_cast<float>(wh);
-    }
-    __syncthreads();
-    if (c0 + KC < nkeys) load_chunk(c0 + KC);  // next chunk in flight during this one
+  for (int ch = 0; ch < nch; ++ch) {
+    const int bf = ch & 1;
     if (gw < ng) {
 #pragma unroll
       for (int ks = 0; ks < KC / 16; ++ks) {
         f16x8_t wr[CW];
 #pragma unroll
-        for (int cc = 0; cc < CW; ++cc) wr[cc] = *reinterpret_cast<const f16x8_t*>(sw + (gw + cc) * KC + 16 * ks + 8 * h);
+        for (int cc = 0; cc < CW; ++cc) wr[cc] = *reinterpret_cast<const f16x8_t*>(&sw[bf][(gw + cc) * KC + 16 * ks + 8 * h]);
         f16x8_t bk[NDK];
 #pragma unroll
         for (int dk = 0; dk < NDK; ++dk)
-          bk[dk] = __builtin_bit_cast(f16x8_t, lds_operand_tr(sK, ST, 16 * ks, 32 * dk, lane));
+          bk[dk] = __builtin_bit_cast(f16x8_t, lds_operand_tr(sK[bf], ST, 16 * ks, 32 * dk, lane));
 #pragma unroll
         for (int dv = 0; dv < NDV; ++dv) {
-          const f16x8_t vr = __builtin_bit_cast(f16x8_t, lds_operand_tr(sV, ST, 16 * ks, 32 * (dv0 + dv), lane));
+          const f16x8_t vr = __builtin_bit_cast(f16x8_t, lds_operand_tr(sV[bf], ST, 16 * ks, 32 * (dv0 + dv), lane));
 #pragma unroll
           for (int cc = 0; cc < CW; ++cc) {
             const f16x8_t av = vr * wr[cc];
@@ -385,7 +394,9 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
         }
       }
     }
-    __syncthreads();  // the next chunk overwrites the tiles
+    if (ch + 1 < nch) stage(bf ^ 1);                 // chunk ch + 1 into the other buffer
+    if (ch + 2 < nch) load_chunk((ch + 2) * KC);     // chunk ch + 2 in flight
+    __syncthreads();
   }
   // weight sums: per wave (64 consecutive weights of one centroid), then per centroid
   // in wave order
