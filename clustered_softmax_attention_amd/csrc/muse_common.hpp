@@ -107,6 +107,16 @@ __device__ __forceinline__ float wave_reduce(float x, Op op) {
   return x;
 }
 
+// Max over each 32-lane half of the wave (both halves reduced independently).
+__device__ __forceinline__ float half_wave_max(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));
+  x = fmaxf(x, dpp_f32<0x4E>(x));
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  x = fmaxf(x, dpp_f32<0x128>(x));
+  const SwapPair r = self_swap16(__builtin_bit_cast(unsigned, x));
+  return fmaxf(__builtin_bit_cast(float, r.r0), __builtin_bit_cast(float, r.r1));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   return wave_reduce(x, [](float p, float q) { return fmaxf(p, q); });
 }

@@ -287,15 +287,26 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + key0;
   for (int k = tid; k < nkeys; k += 512) s_perm[k] = perm[k];
 
-  // max of the scores over the range, per centroid (waves over centroids)
-  for (int g = wave; g < G; g += 8) {
+  // max of the scores over the range, per centroid: 32 lanes (a half-wave) per centroid,
+  // 16 loads of each lane in flight at once
+  for (int g0 = 2 * wave; g0 < G; g0 += 16) {
+    const int g = g0 + h;
     float mx = kNegInf;
     if (g < ng) {
-#pragma unroll 4
-      for (int k = lane; k < nkeys; k += 64) mx = fmaxf(mx, S[static_cast<size_t>(g) * a.N + k]);
+      const float* Sg = S + static_cast<size_t>(g) * a.N;
+      for (int k0 = 0; k0 < nkeys; k0 += 32 * 16) {
+        float x[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int k = k0 + (lane & 31) + 32 * q;
+          x[q] = k < nkeys ? Sg[k] : kNegInf;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) mx = fmaxf(mx, x[q]);
+      }
     }
-    mx = wave_max(mx);
-    if (lane == 0) smx[g] = mx;
+    mx = half_wave_max(mx);
+    if ((lane & 31) == 0 && g < G) smx[g] = mx;
   }
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
