@@ -683,16 +683,20 @@ __global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
 // One workgroup per (head, tensor): per (block, cluster) the exclusive prefix of the
 // tile counts over the block's tiles (written over tile_cnt, which the scatter then
 // reads in O(1)), the bucket totals, and their exclusive scan -> offs[nb*C + 1]
-// (threads over consecutive buckets, then a scan of the thread totals).
+// (threads over consecutive buckets, then a scan of the thread totals). With items
+// set, the same pass lists the atom work items (runs of at most kAtomSeg positions of
+// a bucket), pads the list with empty items, and lists the buckets of several items
+// with their partial slots.
 __global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
   if (t.perm == nullptr) return;
-  __shared__ int s_run[256];
+  __shared__ int s_run[4][256];
   const int C = t.C, bh = blockIdx.y, tid = threadIdx.x;
   const int nbC = a.nb * C;
+  const bool segs = t.items != nullptr;
   const int per = (nbC + 255) / 256, e0 = min(nbC, tid * per), e1 = min(nbC, e0 + per);
   int* offs = t.offs + static_cast<size_t>(bh) * (nbC + 1);
-  int tot = 0;
+  int tot[4] = {0, 0, 0, 0};  // positions, items, partial slots, buckets of several items
   for (int e = e0; e < e1; ++e) {
     const int b = e / C, j = e % C;
     int run = 0;
@@ -710,23 +714,48 @@ __global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
       }
     }
     offs[e] = run;  // bucket total for now (only this thread touches entry e)
-    tot += run;
+    const int ni = max(1, (run + kAtomSeg - 1) / kAtomSeg);
+    tot[0] += run;
+    tot[1] += ni;
+    tot[2] += ni > 1 ? ni : 0;
+    tot[3] += ni > 1 ? 1 : 0;
   }
-  s_run[tid] = tot;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s_run[r][tid] = tot[r];
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
-    const int x = tid >= o ? s_run[tid - o] : 0;
+    int x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = tid >= o ? s_run[r][tid - o] : 0;
     __syncthreads();
-    s_run[tid] += x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_run[r][tid] += x[r];
     __syncthreads();
   }
-  int pos = s_run[tid] - tot;
+  int pos = s_run[0][tid] - tot[0], it = s_run[1][tid] - tot[1], pt = s_run[2][tid] - tot[2],
+      mb = s_run[3][tid] - tot[3];
+  const int max_items = atom_max_items(nbC, a.N);
+  int4* items = segs ? t.items + static_cast<size_t>(bh) * max_items : nullptr;
+  int4* multi = segs ? t.multi + static_cast<size_t>(bh) * (1 + atom_max_multi(a.N)) : nullptr;
   for (int e = e0; e < e1; ++e) {
     const int cnt = offs[e];
     offs[e] = pos;
+    if (segs) {
+      const int ni = max(1, (cnt + kAtomSeg - 1) / kAtomSeg);
+      for (int q = 0; q < ni; ++q)
+        items[it + q] = make_int4(pos + kAtomSeg * q, min(kAtomSeg, cnt - kAtomSeg * q), ni > 1 ? pt + q : -1, e);
+      if (ni > 1) multi[1 + mb++] = make_int4(e, pt, ni, 0);
+      it += ni;
+      pt += ni > 1 ? ni : 0;
+    }
     pos += cnt;
   }
-  if (tid == 255) offs[nbC] = s_run[255];
+  if (tid == 255) offs[nbC] = s_run[0][255];
+  if (segs) {
+    const int nit = s_run[1][255];
+    for (int g = nit + tid; g < max_items; g += 256) items[g] = make_int4(0, -1, -1, 0);
+    if (tid == 255) multi[0] = make_int4(s_run[3][255], 0, 0, 0);
+  }
 }
 
 // One workgroup per tile: scatter the tile's stably sorted points into the head's

@@ -12,6 +12,15 @@ constexpr int kMaxClusters = 128;
 constexpr int kMaxMomKeys = 8192;  // positions per block-moment range (matrix-core path)
 // query centroids per workgroup of the matrix-core moment kernel
 constexpr int moments_group(int D) { return D == 64 ? 16 : 4; }
+// Key buckets are cut into atom work items of at most kAtomSeg positions, so that one
+// large cluster does not serialise the atoms; a bucket of n keys gives max(1, ceil(n /
+// kAtomSeg)) items, hence at most nb*Ck + ceil(N / kAtomSeg) per head. Buckets of more
+// than one item (fewer than ceil(N / kAtomSeg) of them) hold fewer than 2 ceil(N /
+// kAtomSeg) items together, each with a partial-atom slot.
+constexpr int kAtomSeg = 64;
+__host__ __device__ constexpr int atom_max_items(int nbC, int N) { return nbC + (N + kAtomSeg - 1) / kAtomSeg; }
+__host__ __device__ constexpr int atom_max_multi(int N) { return (N + kAtomSeg - 1) / kAtomSeg; }
+__host__ __device__ constexpr int atom_max_partials(int N) { return 2 * atom_max_multi(N); }
 
 // ------------------------------------------------------------------ K-means
 
@@ -32,6 +41,10 @@ struct KmTensor {
   int32_t* gcnt;               // [BH, ntiles, C] cluster counts, one row per tile group
   int32_t* perm;               // [BH, N] points ordered by (block, label, position), or null
   int32_t* offs;               // [BH, nb*C + 1] bucket offsets into perm
+  // atom work items (key tensor, matrix-core path; null otherwise):
+  int4* items;                 // [BH, atom_max_items] (first position, positions (-1: none), partial slot or -1, bucket)
+  int4* multi;                 // [BH, 1 + atom_max_multi]: (count), then (bucket, first partial slot, items) per
+                               // bucket of several items
 };
 
 struct KmArgs {
@@ -92,6 +105,13 @@ struct S1Args {
   const float* qbar;           // [BH, Cq, D] query centroids
   const int32_t* perm_k;       // [BH, N] keys by (block, label)
   const int32_t* offs_k;       // [BH, nb*Ck + 1]
+  const int4* items_k;         // [BH, atom_max_items] atom work items (matrix-core path)
+  const int4* multi_k;         // [BH, 1 + atom_max_multi] buckets of several items
+  // partial atoms of buckets with several work items: [BH, atom_max_partials, Cq(, D)]
+  float* pt_m;
+  float* pt_z;
+  float* pt_k;
+  float* pt_v;
   // atoms: one (query cluster i, key cluster j, key block b') each
   float* at_m;                 // [BH, nb, Cq, Ck] max logit
   float* at_z;                 // [BH, nb, Cq, Ck] sum exp(a - m)
@@ -116,7 +136,7 @@ struct S1Args {
 };
 
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);
-void launch_stage1_mfma(const S1Args& a, int which, hipStream_t s);  // 0 scores, 1 atoms, 2 moments, 3 finalise, 4 scan
+void launch_stage1_mfma(const S1Args& a, int which, hipStream_t s);  // 0 scores, 1 atoms (+ merge), 2 moments, 3 finalise, 4 scan
 
 // ------------------------------------------------------------------ stage 2
 

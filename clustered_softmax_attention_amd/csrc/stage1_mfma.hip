@@ -10,7 +10,9 @@
 // positions:
 //   s1_scores      a_i(pos) = s qbar_i . k_perm[pos] for every centroid and position,
 //                  [BH, Cq, N] fp32 (qbar split into bf16 hi + lo; keys are exact).
-//   s1_atoms_mfma  one wave per (block, key cluster) bucket: the bucket's scores
+//   s1_atoms_mfma  one wave per work item (a run of at most kAtomSeg positions of one
+//                  (block, key cluster) bucket; s1_atoms_merge folds the items of a
+//                  bucket): the item's scores
 //                  recomputed on the matrix cores in steps of 32 keys (keys as rows, so
 //                  the max is lane-local, online across steps), and sum w k, sum w v as
 //                  K^T W, V^T W with the weight accumulator as B operand and the key and
@@ -21,6 +23,8 @@
 //                  fp16 multiplies) and fp32 accumulation.
 #include "mfma.hpp"
 #include "muse_kernels.hpp"
+
+#include <algorithm>
 
 namespace muse {
 
@@ -91,56 +95,83 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
   }
 }
 
-constexpr int kAtomChunk = 32;  // bucket positions per step
+constexpr int kAtomChunk = 32;  // positions per step
+constexpr int kMergeGrid = 64;  // merge workgroups per head (each loops over the multi-item buckets)
 
-// One wave per (block, key cluster) bucket, for every query centroid in tiles of 32:
-// keys of the bucket arrive in steps of 32 (rows gathered through the permutation into
-// a wave-private row-major LDS tile), and on the matrix cores
-//   S = K_step (s qbar)^T   (32 keys x 32 centroids; qbar split into bf16 hi + lo, keys exact),
-// so that lane (c, h) holds 16 keys of centroid c and the max over the bucket is
+// One wave per atom work item (a run of at most kAtomSeg positions of one (block, key
+// cluster) bucket), for every query centroid in tiles of 32. The workgroup first stages
+// s qbar (split into bf16 hi + lo) in LDS for its four waves; each wave gathers its
+// item's permutation entries once (lane l holds position l) and hands them to the row
+// loads by a lane shuffle. Keys arrive in steps of 32 (rows gathered into a wave-private
+// row-major LDS tile, the next step's rows in flight meanwhile), and on the matrix cores
+//   S = K_step (s qbar)^T   (32 keys x 32 centroids; keys exact),
+// so that lane (c, h) holds 16 keys of centroid c and the max over the item is
 // lane-local plus the partner lane l^32 (online across steps, sums rescaled when it
 // grows). The weights w = exp(S - max), split into hi + lo, are directly the B operand
 // of  sum w k = K^T W  and  sum w v = V^T W,  whose A operands come from the same LDS
-// tile through the transpose read in the accumulator's key order.
+// tile through the transpose read in the accumulator's key order. A bucket of one item
+// writes its atom; the items of a larger bucket write partial atoms that
+// s1_atoms_merge folds.
 template <int D>
-__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) s1_atoms_mfma_kernel(S1Args a) {
-  constexpr int NKS = D / 16, NMT = D / 32, KC = kAtomChunk, ST = D + 8;
+__global__ void __launch_bounds__(256, D == 64 ? 3 : 1) s1_atoms_mfma_kernel(S1Args a) {
+  constexpr int NKS = D / 16, NMT = D / 32, KC = kAtomChunk, ST = D + 8, QST = D + 8;
   constexpr int NP = KC * (D / 8) / 64;  // 16-byte row pieces per lane and tensor
+  static_assert(kAtomSeg <= 64, "one permutation entry per lane");
   __shared__ __align__(16) uint16_t sK[4][KC * ST];
   __shared__ __align__(16) uint16_t sV[4][KC * ST];
-  const int bh = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
-  const int Cq = a.Cq, Ck = a.Ck;
-  const int u = blockIdx.x * 4 + wave;
-  if (u >= a.nb * Ck) return;  // no workgroup barrier below: waves are independent
-  const int bp = u / Ck, j = u % Ck;
-  const int32_t* offs = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
-  const int s0 = offs[u], n = offs[u + 1] - s0;
+  extern __shared__ __align__(16) uint16_t sq[];  // s qbar hi, lo [Cqp][QST]
+  const int bh = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int Cq = a.Cq, Ck = a.Ck, nbC = a.nb * Ck, Cqp = (Cq + 31) & ~31;
+  const int max_items = atom_max_items(nbC, a.N);
+  const int g = blockIdx.x * 4 + wave;
+  int4 it = make_int4(0, -1, -1, 0);
+  if (g < max_items) it = a.items_k[static_cast<size_t>(bh) * max_items + g];
+  const int s0 = it.x, n = it.y;
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + s0;
+  const int pl = lane < n ? perm[lane] : 0;
+  uint16_t* qhi = sq;
+  uint16_t* qlo = sq + Cqp * QST;
+  for (int x = tid; x < Cqp * D; x += 256) {
+    const int i = x / D, d = x % D;
+    const float v = i < Cq ? a.scale * a.qbar[(static_cast<size_t>(bh) * Cq + i) * D + d] : 0.f;
+    const uint16_t hv = f32_to_bf16_bits(v);
+    qhi[i * QST + d] = hv;
+    qlo[i * QST + d] = f32_to_bf16_bits(v - bf16_to_f32(hv));
+  }
+  __syncthreads();
+  if (n < 0) return;  // padding item; no workgroup barrier below
+  const int u = it.w, bp = u / Ck, j = u % Ck;
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
   uint16_t* kt = sK[wave];
   uint16_t* vt = sV[wave];
   const size_t abase = (static_cast<size_t>(bh) * a.nb + bp) * Cq;
+  const bool part = it.z >= 0;
+  const size_t pbase = (static_cast<size_t>(bh) * atom_max_partials(a.N) + (part ? it.z : 0)) * Cq;
+  float* out_k = part ? a.pt_k : a.at_k;
+  float* out_v = part ? a.pt_v : a.at_v;
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  for (int nt = 0; nt < (Cq + 31) / 32; ++nt) {
-    const int i = 32 * nt + c;
-    const bool iv = i < Cq;
-    // B operand of S: column = centroid c, k = d
-    bf16x8_t qh[NKS], ql[NKS];
-    {
-      const float* qb = a.qbar + (static_cast<size_t>(bh) * Cq + (iv ? i : 0)) * D;
+  u16x8_t pk[NP], pv[NP];
+  auto load_rows = [&](int p0) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) x[r] = iv ? a.scale * qb[16 * ks + 8 * h + r] : 0.f;
-        split_bf16x8(x, qh[ks], ql[ks]);
+    for (int q = 0; q < NP; ++q) {
+      const int x = lane + 64 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
+      const int key = __shfl(pl, p0 + r, 64);
+      pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      pv[q] = pk[q];
+      if (p0 + r < n) {
+        const size_t row = static_cast<size_t>(key) * D + c8;
+        pk[q] = *reinterpret_cast<const u16x8_t*>(K + row);
+        pv[q] = *reinterpret_cast<const u16x8_t*>(V + row);
       }
     }
+  };
+  for (int nt = 0; nt < Cqp / 32; ++nt) {
+    const int i = 32 * nt + c;
     f32x16_t ak[NMT], av[NMT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
@@ -148,20 +179,6 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) s1_atoms_mfma_kernel(S1A
       av[mt] = zero16();
     }
     float mx = kNegInf, z = 0.f;
-    u16x8_t pk[NP], pv[NP];
-    auto load_rows = [&](int p0) {
-#pragma unroll
-      for (int q = 0; q < NP; ++q) {
-        const int x = lane + 64 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
-        pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        pv[q] = pk[q];
-        if (p0 + r < n) {
-          const size_t row = static_cast<size_t>(perm[p0 + r]) * D + c8;
-          pk[q] = *reinterpret_cast<const u16x8_t*>(K + row);
-          pv[q] = *reinterpret_cast<const u16x8_t*>(V + row);
-        }
-      }
-    };
     if (n > 0) load_rows(0);
     for (int p0 = 0; p0 < n; p0 += KC) {
       wave_sync();  // the previous step's tiles are consumed
@@ -177,8 +194,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) s1_atoms_mfma_kernel(S1A
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u16x8_t*>(kt + c * ST + 16 * ks + 8 * h));
-        sc = mfma32(ka, qh[ks], sc);
-        sc = mfma32(ka, ql[ks], sc);
+        const int qo = (32 * nt + c) * QST + 16 * ks + 8 * h;
+        sc = mfma32(ka, as_bf16x8(*reinterpret_cast<const u16x8_t*>(qhi + qo)), sc);
+        sc = mfma32(ka, as_bf16x8(*reinterpret_cast<const u16x8_t*>(qlo + qo)), sc);
       }
       // rows of sc: keys p0 + 8 (v/4) + 4 h + v%4
       float cm = kNegInf;
@@ -223,23 +241,95 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) s1_atoms_mfma_kernel(S1A
       }
     }
     z += xor32(z);
-    if (!iv) continue;
-    const size_t aidx = (abase + i) * Ck + j;
+    if (i >= Cq) continue;
+    // the bucket's atom, or the item's partial when the bucket has several items
+    const size_t aidx = part ? pbase + i : (abase + i) * Ck + j;
     if (h == 0) {
-      a.at_m[aidx] = n > 0 ? mx : kNegInf;
-      a.at_z[aidx] = z;
+      (part ? a.pt_m : a.at_m)[aidx] = n > 0 ? mx : kNegInf;
+      (part ? a.pt_z : a.at_z)[aidx] = z;
     }
     // lane (c, h): column = centroid i, rows d = 32 mt + 8 g + 4 h + r
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * mt + 8 * g + 4 * h;
-        const f32x4_t fk = {ak[mt][4 * g], ak[mt][4 * g + 1], ak[mt][4 * g + 2], ak[mt][4 * g + 3]};
-        const f32x4_t fv = {av[mt][4 * g], av[mt][4 * g + 1], av[mt][4 * g + 2], av[mt][4 * g + 3]};
-        *reinterpret_cast<f32x4_t*>(a.at_k + aidx * D + d0) = fk;
-        *reinterpret_cast<f32x4_t*>(a.at_v + aidx * D + d0) = fv;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * mt + 8 * g4 + 4 * h;
+        const f32x4_t fk = {ak[mt][4 * g4], ak[mt][4 * g4 + 1], ak[mt][4 * g4 + 2], ak[mt][4 * g4 + 3]};
+        const f32x4_t fv = {av[mt][4 * g4], av[mt][4 * g4 + 1], av[mt][4 * g4 + 2], av[mt][4 * g4 + 3]};
+        *reinterpret_cast<f32x4_t*>(out_k + aidx * D + d0) = fk;
+        *reinterpret_cast<f32x4_t*>(out_v + aidx * D + d0) = fv;
       }
+  }
+}
+
+// Buckets of several work items: the items' partial atoms folded in item order with the
+// log-sum-exp rule (running max M, sums rescaled by exp(m - M)) into the bucket's atom.
+// kMergeGrid workgroups of 1024 threads per head walk the list of such buckets; threads
+// over the (centroid, float4 of the K and V sums) pairs, four items per batch with all
+// of a batch's loads in flight (one batch for buckets of up to 4 kAtomSeg keys).
+template <int D>
+__global__ void __launch_bounds__(1024) s1_atoms_merge_kernel(S1Args a) {
+  constexpr int F4 = D / 2;  // float4s of one centroid's K and V sums
+  constexpr int QB = 4;
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int Cq = a.Cq, Ck = a.Ck;
+  const int4* multi = a.multi_k + static_cast<size_t>(bh) * (1 + atom_max_multi(a.N));
+  const float* __restrict__ pm = a.pt_m;
+  const float* __restrict__ pz = a.pt_z;
+  // the list head and this workgroup's first entry travel together (the entry is in
+  // bounds whatever the count: gridDim.x <= atom_max_multi)
+  const int count = multi[0].x;
+  int4 e4 = multi[1 + blockIdx.x];
+  for (int mb = blockIdx.x; mb < count; mb += gridDim.x) {
+    if (mb != static_cast<int>(blockIdx.x)) e4 = multi[1 + mb];
+    const int u = e4.x, ni = e4.z, bp = u / Ck, j = u % Ck;
+    const size_t pb = static_cast<size_t>(bh) * atom_max_partials(a.N) + e4.y;
+    const size_t abase = (static_cast<size_t>(bh) * a.nb + bp) * Cq;
+    for (int e = tid; e < Cq * F4; e += 1024) {
+      const int i = e / F4, f = e % F4;
+      const bool isv = f >= D / 4;
+      const int d4 = 4 * (isv ? f - D / 4 : f);
+      const float* __restrict__ src = isv ? a.pt_v : a.pt_k;
+      float M = kNegInf, z = 0.f;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int q0 = 0; q0 < ni; q0 += QB) {
+        float m[QB], zz[QB];
+        f32x4_t x[QB];
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          m[q] = kNegInf;
+          zz[q] = 0.f;
+          x[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (q0 + q < ni) {
+            const size_t pi = (pb + q0 + q) * Cq + i;
+            m[q] = pm[pi];
+            zz[q] = pz[pi];
+            x[q] = *reinterpret_cast<const f32x4_t*>(src + pi * D + d4);
+          }
+        }
+        float bm = M;
+#pragma unroll
+        for (int q = 0; q < QB; ++q) bm = fmaxf(bm, m[q]);
+        const float rs = M == kNegInf ? 0.f : __expf(M - bm);
+        z *= rs;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] *= rs;
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const float w = m[q] == kNegInf ? 0.f : __expf(m[q] - bm);
+          z = fmaf(w, zz[q], z);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c] = fmaf(w, x[q][c], acc[c]);
+        }
+        M = bm;
+      }
+      const size_t ai = (abase + i) * Ck + j;
+      if (f == 0) {
+        a.at_m[ai] = M;
+        a.at_z[ai] = z;
+      }
+      *reinterpret_cast<f32x4_t*>((isv ? a.at_v : a.at_k) + ai * D + d4) = acc;
+    }
   }
 }
 
@@ -877,8 +967,15 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
     ProfScope ps_("s1_scores", s);
     hipLaunchKernelGGL((s1_scores_kernel<D>), dim3((a.N + 255) / 256, a.BH), dim3(256), lds, s, a);
   } else if (which == 1) {
-    ProfScope ps_("s1_atoms_mfma", s);
-    hipLaunchKernelGGL((s1_atoms_mfma_kernel<D>), dim3((a.nb * a.Ck + 3) / 4, a.BH), dim3(256), 0, s, a);
+    const int nbC = a.nb * a.Ck;
+    const size_t lds = static_cast<size_t>((a.Cq + 31) & ~31) * (D + 8) * 2 * sizeof(uint16_t);
+    allow_lds((const void*)s1_atoms_mfma_kernel<D>, lds + 2 * 4 * kAtomChunk * (D + 8) * sizeof(uint16_t));
+    {
+      ProfScope ps_("s1_atoms_mfma", s);
+      hipLaunchKernelGGL((s1_atoms_mfma_kernel<D>), dim3((atom_max_items(nbC, a.N) + 3) / 4, a.BH), dim3(256), lds, s, a);
+    }
+    ProfScope ps_("s1_atoms_merge", s);
+    hipLaunchKernelGGL((s1_atoms_merge_kernel<D>), dim3(std::min(kMergeGrid, atom_max_multi(a.N)), a.BH), dim3(1024), 0, s, a);
   } else if (which == 2) {
     constexpr int G = MomCfg<D>::G;
     ProfScope ps_("s1_moments_f16", s);
