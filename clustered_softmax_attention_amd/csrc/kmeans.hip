@@ -219,9 +219,12 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_kernel(KmArgs a, int i
 // x.c_j - ||c_j||^2/2 = (||x||^2 - ||x - c_j||^2) / 2, so the nearest centroid is the
 // largest score. Lane (c, h) of a 32 x 32 tile holds 16 centroid rows of point c; each
 // wave scores its 64 points as two 32-point groups that share every centroid fragment.
-// A running best, second best (med3) and best slot are kept per lane, then merged with
-// the partner lane l^32. An error of E in distance is E/2 in score; a second centroid
-// within E of the best (2E in distance) sends the point to the exact rescoring, where
+// Each score is ranked as a key that carries its lane-local slot in the 6 low mantissa
+// bits; a running best and second best per lane (max3 / med3 over pairs of keys) are
+// merged with the partner lane l^32. The error bound E in distance covers the matrix
+// product (bf16 hi + lo centroids, fp32 sums) and the key truncation with a wide
+// margin, and is E/2 in score; a second centroid within E of the best (2E in distance)
+// sends the point to the exact rescoring, where
 // the whole wave computes the fp32 direct-form distance of each candidate (lanes over
 // d, fixed-order tree sum).
 //
@@ -325,7 +328,9 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
       *reinterpret_cast<u16x8_t*>(chi + dst) = h8;
       *reinterpret_cast<u16x8_t*>(clo + dst) = l8;
     }
-    for (int j = tid; j < Cp; j += TILE) bias[j] = j < C ? -0.5f * t.cn2[static_cast<size_t>(bh) * C + j] : kNegInf;
+    // padding centroids: a finite score far below any real one (their rank keys must
+    // not be NaN)
+    for (int j = tid; j < Cp; j += TILE) bias[j] = j < C ? -0.5f * t.cn2[static_cast<size_t>(bh) * C + j] : -1e30f;
     // bring the fp32 centroid rows that a near-tie rescoring reads into this XCD's L2
     // now, while the tables are in flight anyway (a cold miss later costs a full round
     // trip under load); the sum only keeps the loads alive
@@ -404,8 +409,15 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
         }
         xx[gi] = s + xor32(s);
       }
-      float best[2] = {kNegInf, kNegInf}, second[2] = {kNegInf, kNegInf};
-      int slot[2] = {0, 0};
+      // rank keys: the score with its 6 low mantissa bits replaced by the lane-local
+      // slot 16 jt + v (relative change below 2^-17, inside the rescoring window), so
+      // that a max carries its slot; top two of a pair of keys per step:
+      //   best' = max3(best, k0, k1),  second' = max(second, med3(best, k0, k1))
+      const float kLow = -3.0e38f;
+      float best[2] = {kLow, kLow}, second[2] = {kLow, kLow};
+      auto rkey = [](float x, int slot) {
+        return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & ~63u) | static_cast<uint32_t>(slot));
+      };
       // tile jt + 1 goes to the matrix cores while tile jt is ranked; the centroid-tile
       // loop has compile-time bounds, and a scheduling barrier per step keeps the
       // compiler from hoisting later tiles (register pressure)
@@ -416,15 +428,13 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
         f32x16_t sb0, sb1;
         if (jt + 1 < NJT) score_tile(jt + 1, sb0, sb1);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float x0 = sa0[v], x1 = sa1[v];
-          const bool g0 = x0 > best[0], g1 = x1 > best[1];
-          slot[0] = g0 ? 16 * jt + v : slot[0];
-          second[0] = __builtin_amdgcn_fmed3f(best[0], second[0], x0);
-          best[0] = g0 ? x0 : best[0];
-          slot[1] = g1 ? 16 * jt + v : slot[1];
-          second[1] = __builtin_amdgcn_fmed3f(best[1], second[1], x1);
-          best[1] = g1 ? x1 : best[1];
+        for (int v = 0; v < 16; v += 2) {
+          const float a0 = rkey(sa0[v], 16 * jt + v), a1 = rkey(sa0[v + 1], 16 * jt + v + 1);
+          const float b0 = rkey(sa1[v], 16 * jt + v), b1 = rkey(sa1[v + 1], 16 * jt + v + 1);
+          second[0] = fmaxf(second[0], __builtin_amdgcn_fmed3f(best[0], a0, a1));
+          best[0] = fmaxf(best[0], fmaxf(a0, a1));
+          second[1] = fmaxf(second[1], __builtin_amdgcn_fmed3f(best[1], b0, b1));
+          best[1] = fmaxf(best[1], fmaxf(b0, b1));
         }
         __builtin_amdgcn_sched_barrier(0);
         if (jt + 1 < NJT) {
@@ -437,7 +447,7 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
       float E[2];
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
-        const int sl = slot[gi];
+        const int sl = static_cast<int>(__builtin_bit_cast(uint32_t, best[gi]) & 63u);
         bj[gi] = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * h + (sl & 3);
         const float ob = xor32(best[gi]);
         const float os = xor32(second[gi]);
