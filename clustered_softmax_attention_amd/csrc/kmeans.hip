@@ -230,7 +230,8 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_kernel(KmArgs a, int i
 //
 // Cluster sums psum^T [D x C] = X^T onehot run on the matrix cores too: the tile's rows
 // sit row-major in LDS and reach the A operand through the transpose read; the one-hot
-// B operand is built from the tile's labels with packed 16-bit integer operations. Wave w owns a
+// B operand is built from the tile's labels with packed 16-bit integer operations, whose
+// per-lane tallies of mismatches give the cluster counts as well. Wave w owns a
 // fixed set of output tiles (one cluster tile and all D/32 feature tiles when NW = 4),
 // accumulated over all tiles of the group and written once.
 //
@@ -257,17 +258,20 @@ struct KmMfmaCfg {
 
 // bf16 one-hot of eight 16-bit labels against label j: per 16-bit half,
 // m = min(lab ^ j, 1) is 0 exactly where lab == j, and 0x3F80 - 0x3F80 m is bf16 1.0
-// there and 0 elsewhere (labels and j are below 2^15).
+// there and 0 elsewhere (labels and j are below 2^15). The m are also summed into the
+// packed 16-bit counters `miss` (mismatches per half), from which the cluster counts
+// follow.
 __device__ __forceinline__ bf16x8_t onehot_bf16x8(const u16x8_t& lab8, uint32_t jj, uint32_t one2, uint32_t neg2,
-                                                  uint32_t val2) {
+                                                  uint32_t val2, uint32_t& miss) {
   const uint32_t* p = reinterpret_cast<const uint32_t*>(&lab8);
   uint32_t o[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint32_t m;
-    asm volatile("v_xor_b32 %0, %1, %2\n\tv_pk_min_u16 %0, %0, %3\n\tv_pk_mad_u16 %0, %0, %4, %5"
-                 : "=&v"(m)
-                 : "v"(p[q]), "v"(jj), "v"(one2), "v"(neg2), "v"(val2));
+    asm volatile(
+        "v_xor_b32 %0, %2, %3\n\tv_pk_min_u16 %0, %0, %4\n\tv_pk_add_u16 %1, %1, %0\n\tv_pk_mad_u16 %0, %0, %5, %6"
+        : "=&v"(m), "+v"(miss)
+        : "v"(p[q]), "v"(jj), "v"(one2), "v"(neg2), "v"(val2));
     o[q] = m;
   }
   return __builtin_bit_cast(bf16x8_t, o);
@@ -282,7 +286,8 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
   const int C = t.C, Cp = 32 * NJT;
   const int grp = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
-  const int tt0 = grp * a.tpg, tt1 = min(a.ntiles, tt0 + a.tpg);
+  if (grp >= t.ngroups) return;  // this tensor needs fewer workgroups
+  const int tt0 = grp * t.tpg, tt1 = min(a.ntiles, tt0 + t.tpg);
   uint16_t* chi = reinterpret_cast<uint16_t*>(smem);
   uint16_t* clo = chi + Cp * D;
   float* bias = reinterpret_cast<float*>(clo + Cp * D);
@@ -316,7 +321,7 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
   if (score) {
     const uint16_t* ghi = t.chi + static_cast<size_t>(bh) * C * D;
     const uint16_t* glo = t.clo + static_cast<size_t>(bh) * C * D;
-#pragma unroll 4
+#pragma unroll
     for (int e = tid; e < Cp * (D / 8); e += TILE) {
       const int j = e / (D / 8), c8 = e % (D / 8);
       u16x8_t h8 = {0, 0, 0, 0, 0, 0, 0, 0}, l8 = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -331,18 +336,7 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
     // padding centroids: a finite score far below any real one (their rank keys must
     // not be NaN)
     for (int j = tid; j < Cp; j += TILE) bias[j] = j < C ? -0.5f * t.cn2[static_cast<size_t>(bh) * C + j] : -1e30f;
-    // bring the fp32 centroid rows that a near-tie rescoring reads into this XCD's L2
-    // now, while the tables are in flight anyway (a cold miss later costs a full round
-    // trip under load); the sum only keeps the loads alive
-    float warm = 0.f;
-#pragma unroll 4
-    for (int e = tid; e < C * D / 4; e += TILE) {
-      const f32x4_t c4 = *reinterpret_cast<const f32x4_t*>(cent + 4 * static_cast<size_t>(e));
-      warm += c4[0];
-    }
-    if (warm == 1.2345e-30f && tid == TILE) s_gcnt[0] = 0;  // never true: tid < TILE
   }
-  for (int j = tid; j < C; j += TILE) s_gcnt[j] = 0;
   __syncthreads();
   float cmax2 = 0.f;
   if (score) {
@@ -352,8 +346,12 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
   const float cmax = sqrtf(cmax2);
 
   f32x16_t acc[OPW];
+  uint32_t miss[CPW];  // packed per-half mismatch counts of the one-hot operand
+  int nks = 0;         // one-hot steps accumulated (8 labels per lane each)
 #pragma unroll
   for (int r = 0; r < OPW; ++r) acc[r] = zero16();
+#pragma unroll
+  for (int r = 0; r < CPW; ++r) miss[r] = 0u;
   const int npass = (njt + NW * CPW - 1) / (NW * CPW);
 
   // scores of centroid tile jt for both groups, accumulator preset to the bias
@@ -591,7 +589,6 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
     if (valid) {
       t.labels[static_cast<size_t>(bh) * a.N + n] = lab;
       if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
-      atomicAdd(&s_gcnt[lab], 1);  // integer counts: order-independent
     }
     slab[tid] = valid ? static_cast<uint16_t>(lab) : static_cast<uint16_t>(0xFFFF);
     if (last) tile_sort(a, t, lab, valid, tt, s_lab, s_whist, s_cnt, s_start, s_sorted);
@@ -601,6 +598,9 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
       if (npass > 1) {
 #pragma unroll
         for (int r = 0; r < OPW; ++r) acc[r] = zero16();
+#pragma unroll
+        for (int r = 0; r < CPW; ++r) miss[r] = 0u;
+        nks = 0;
       }
       const int ct0 = (pass * NW + wave) * CPW;
       const int nct = min(CPW, njt - ct0);  // uniform; may be <= 0
@@ -618,19 +618,24 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
 #pragma unroll
           for (int rc = 0; rc < CPW; ++rc) {
             if (rc > 0 && rc >= nct) break;
-            const bf16x8_t oh = onehot_bf16x8(lab8, jj[rc], one2, neg2, val2);
+            const bf16x8_t oh = onehot_bf16x8(lab8, jj[rc], one2, neg2, val2, miss[rc]);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) acc[rc * NDT + dt] = mfma32(ax[dt], oh, acc[rc * NDT + dt]);
           }
         }
       }
+      nks += TILE / 16;
       if (npass > 1 || tt + 1 == tt1) {
-        // sums of this group (npass > 1 only with one tile per group)
+        // sums and counts of this group (npass > 1 only with one tile per group)
         float* psum = t.psum + (static_cast<size_t>(bh) * a.ntiles + grp) * C * D;
 #pragma unroll
         for (int rc = 0; rc < CPW; ++rc) {
           const int j = 32 * (ct0 + rc) + c;
-          if (j >= C) continue;
+          // lane (c, h) saw 8 nks labels against cluster j
+          const int hit = 8 * nks - static_cast<int>((miss[rc] & 0xFFFFu) + (miss[rc] >> 16));
+          const int cnt = hit + xor32(hit);
+          if (j >= C || nct <= rc) continue;
+          if (h == 0) t.gcnt[(static_cast<size_t>(bh) * a.ntiles + grp) * C + j] = cnt;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -644,7 +649,6 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
     }
     __syncthreads();  // the next tile overwrites the X tile and labels
   }
-  for (int j = tid; j < C; j += TILE) t.gcnt[(static_cast<size_t>(bh) * a.ntiles + grp) * C + j] = s_gcnt[j];
 }
 
 // The centroid-tile count is a template parameter of the body so that the score loop
@@ -671,7 +675,7 @@ __global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
   float acc[2] = {0.f, 0.f};
   int cnt = 0;
 #pragma unroll 8
-  for (int tt = 0; tt < a.ngroups; ++tt) {
+  for (int tt = 0; tt < t.ngroups; ++tt) {
     const float* ps = t.psum + ((tbase + tt) * C + j) * D;
     acc[0] += ps[lane_id()];
     if (nper > 1) acc[1] += ps[lane_id() + 64];
@@ -803,7 +807,10 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
   const bool mf = sizeof(T) == 2;
   const int nw = a.tile / 64;
   KmArgs b = a;
-  b.tpg = 1;
+  for (int z = 0; z < a.ntensors; ++z) {
+    b.t[z].tpg = 1;
+    b.t[z].ngroups = a.ntiles;
+  }
   size_t lds_mfma = 0;
   int npass = 1;
 #define MUSE_KM_CFG(DD, NN)                               \
@@ -815,11 +822,43 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
   MUSE_KM_CFG(128, 1) MUSE_KM_CFG(128, 2) MUSE_KM_CFG(128, 3) MUSE_KM_CFG(128, 4)
 #undef MUSE_KM_CFG
   if (mf && npass == 1) {
-    // several tiles per workgroup amortise the centroid tables; about 512 workgroups
+    // several tiles per workgroup amortise the centroid tables. Per tensor, the tiles per
+    // workgroup are chosen so that the workgroups of both tensors take about as long
+    // (a tile costs about 3 + C/32 units, staging the tables 3 + C/64) while all of them
+    // fit on the device at once; when they cannot, about 512 workgroups of up to 8 tiles.
+    int dev = 0, cus = 256;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const long slots = static_cast<long>(cus) * (a.D == 64 && nw == 4 ? 2 : 1);
     const long total = static_cast<long>(a.ntiles) * a.BH * a.ntensors;
-    b.tpg = static_cast<int>(std::min<long>(8, std::max<long>(1, total / 512)));
+    const int tdef = static_cast<int>(std::min<long>(8, std::max<long>(1, total / 512)));
+    int best[2] = {tdef, tdef};
+    double best_time = 1e30;
+    const int tmax = a.ntensors > 1 ? 8 : 1;
+    for (int t0 = 1; t0 <= 8; ++t0)
+      for (int t1 = 1; t1 <= tmax; ++t1) {
+        const int tp[2] = {t0, t1};
+        long wgs = 0;
+        double tmx = 0.0;
+        for (int z = 0; z < a.ntensors; ++z) {
+          const double njt = (a.t[z].C + 31) / 32;
+          wgs += static_cast<long>(a.BH) * ((a.ntiles + tp[z] - 1) / tp[z]);
+          tmx = std::max(tmx, 3.0 + 0.5 * njt + tp[z] * (3.0 + njt));
+        }
+        if (wgs > slots) continue;
+        if (tmx < best_time) {
+          best_time = tmx;
+          best[0] = t0;
+          best[1] = t1;
+        }
+      }
+    for (int z = 0; z < a.ntensors; ++z) {
+      b.t[z].tpg = best_time < 1e30 ? best[z] : tdef;
+      b.t[z].ngroups = (a.ntiles + b.t[z].tpg - 1) / b.t[z].tpg;
+    }
   }
-  b.ngroups = (a.ntiles + b.tpg - 1) / b.tpg;
+  b.ngroups = 0;
+  for (int z = 0; z < a.ntensors; ++z) b.ngroups = std::max(b.ngroups, b.t[z].ngroups);
   const dim3 g_group(b.ngroups, a.BH, a.ntensors);
   auto launch_mfma = [&](int it) {
     const int last = it == iters - 1;

@@ -41,6 +41,7 @@ struct KmTensor {
   int32_t* gcnt;               // [BH, ntiles, C] cluster counts, one row per tile group
   int32_t* perm;               // [BH, N] points ordered by (block, label, position), or null
   int32_t* offs;               // [BH, nb*C + 1] bucket offsets into perm
+  int tpg, ngroups;             // tiles per assign workgroup and workgroups per head (set by the launcher)
   // atom work items (key tensor, matrix-core path; null otherwise):
   int4* items;                 // [BH, atom_max_items] (first position, positions (-1: none), partial slot or -1, bucket)
   int4* multi;                 // [BH, 1 + atom_max_multi]: (count), then (bucket, first partial slot, items) per
@@ -53,7 +54,7 @@ struct KmArgs {
   int BH, N, D;
   int tile, ntiles;            // points per tile, tiles per head
   int nb, tiles_per_block;     // spatial blocks (1 when acausal) and tiles in one
-  int tpg, ngroups;            // tiles per assign workgroup (set by the launcher), groups per head
+  int ngroups;                 // assign workgroups per head: the largest of the tensors' (set by the launcher)
 };
 
 hipError_t launch_kmeans(const KmArgs& a, int iters, int dtype, hipStream_t s);
