@@ -666,20 +666,37 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
 
 // One wave per (centroid j, head, tensor), lanes over d: sum the tile-group partials in
 // group order; the mean replaces c_j unless the cluster is empty.
+template <int D>
 __global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
-  const int C = t.C, D = a.D, j = blockIdx.x, bh = blockIdx.y;
+  const int C = t.C, j = blockIdx.x, bh = blockIdx.y;
   if (j >= C) return;
   const size_t tbase = static_cast<size_t>(bh) * a.ntiles;
-  const int nper = D / 64;
+  constexpr int nper = D / 64;
   float acc[2] = {0.f, 0.f};
   int cnt = 0;
-#pragma unroll 8
-  for (int tt = 0; tt < t.ngroups; ++tt) {
-    const float* ps = t.psum + ((tbase + tt) * C + j) * D;
-    acc[0] += ps[lane_id()];
-    if (nper > 1) acc[1] += ps[lane_id() + 64];
-    cnt += t.gcnt[(tbase + tt) * C + j];
+  // sixteen groups' partials in flight at once, summed in group order
+  constexpr int UB = 16;
+  for (int t0 = 0; t0 < t.ngroups; t0 += UB) {
+    float p0[UB], p1[UB];
+    int cn[UB];
+#pragma unroll
+    for (int q = 0; q < UB; ++q) {
+      // unconditional loads (index clamped), so that all of them issue back to back
+      const int tt = min(t0 + q, t.ngroups - 1);
+      const float* ps = t.psum + ((tbase + tt) * C + j) * D;
+      p0[q] = ps[lane_id()];
+      p1[q] = nper > 1 ? ps[lane_id() + 64] : 0.f;
+      cn[q] = t.gcnt[(tbase + tt) * C + j];
+    }
+#pragma unroll
+    for (int q = 0; q < UB; ++q) {
+      if (t0 + q < t.ngroups) {
+        acc[0] += p0[q];
+        acc[1] += p1[q];
+        cnt += cn[q];
+      }
+    }
   }
   const size_t row = static_cast<size_t>(bh) * C + j;
   float vals[2];
@@ -884,7 +901,8 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
     }
     {
       ProfScope ps_("kmeans_update", s);
-      hipLaunchKernelGGL(kmeans_update_kernel, g_update, dim3(64), 0, s, b);
+      if (a.D == 64) hipLaunchKernelGGL(kmeans_update_kernel<64>, g_update, dim3(64), 0, s, b);
+      else hipLaunchKernelGGL(kmeans_update_kernel<128>, g_update, dim3(64), 0, s, b);
     }
   }
   {
