@@ -112,14 +112,6 @@ __global__ void __launch_bounds__(kExThreads) exact_valu_kernel(ExactArgs a) {
   }
 }
 
-// Workgroup id -> (query tile, head) so that consecutive work of a head lands on one XCD
-// (hardware places consecutive ids on XCDs round-robin).
-__device__ __forceinline__ int xcd_swizzle(int id, int total) {
-  constexpr int kXcd = 8;
-  if (total % kXcd != 0) return id;
-  return (id % kXcd) * (total / kXcd) + id / kXcd;
-}
-
 template <int D>
 __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt) {
   constexpr int BQ = 128, BK = 64;
@@ -132,7 +124,9 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
   __shared__ __align__(16) uint16_t sV[BK * KST];
 
   const int total = nqt * a.BH;
-  const int id = xcd_swizzle(blockIdx.x, total);
+  // workgroup id -> (query tile, head) such that each XCD takes a contiguous range: the
+  // query tiles of a head read the same keys and values
+  const int id = xcd_contiguous(blockIdx.x, total);
   int qt = id % nqt;
   const int bh = id / nqt;
   if (a.causal) qt = nqt - 1 - qt;  // longest rows first

@@ -107,6 +107,15 @@ __device__ __forceinline__ float wave_reduce(float x, Op op) {
   return x;
 }
 
+// Workgroups go to the 8 XCDs round-robin by linear index. This maps a linear index to
+// a logical one such that every XCD takes one contiguous range of the logical order, so
+// that neighbouring work items (which read the same data) share that XCD's L2.
+__device__ __forceinline__ int xcd_contiguous(int id, int total) {
+  constexpr int X = 8;
+  const int q = total / X, r = total % X, x = id % X, k = id / X;
+  return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
 // Max over each 32-lane half of the wave (both halves reduced independently).
 __device__ __forceinline__ float half_wave_max(float x) {
   x = fmaxf(x, dpp_f32<0xB1>(x));

@@ -162,10 +162,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
   __shared__ __align__(16) uint16_t sVl[JC * KST];
   __shared__ __align__(16) uint16_t sDip[D * DST];
   __shared__ float slz[JC];
-  const int bh = blockIdx.y, tid = threadIdx.x;
+  // acausal: the chunks of one query cluster (consecutive in the chunk order) read the
+  // same tables, so each XCD takes a contiguous range of (head, chunk); causal tables
+  // are per (block, cluster), read by about one chunk each, and stay round-robin
+  const int lin0 = blockIdx.x + gridDim.x * blockIdx.y;
+  const int lin = a.nbS == 1 ? xcd_contiguous(lin0, gridDim.x * gridDim.y) : lin0;
+  const int bh = lin / gridDim.x, tix = lin % gridDim.x, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
-  if (static_cast<int>(blockIdx.x) >= a.ntiles[bh]) return;  // whole workgroup leaves together
-  const int2 tile = a.tiles[static_cast<size_t>(bh) * a.max_tiles + blockIdx.x];
+  if (tix >= a.ntiles[bh]) return;  // whole workgroup leaves together
+  const int2 tile = a.tiles[static_cast<size_t>(bh) * a.max_tiles + tix];
   const int u = tile.x, b = u / a.Cq, i = u % a.Cq;
   const int32_t* offs = a.offs_q + static_cast<size_t>(bh) * (a.nb * a.Cq + 1);
   const int st = tile.y + 32 * wave;
