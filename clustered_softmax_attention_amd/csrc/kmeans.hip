@@ -716,8 +716,8 @@ __global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
 // reads in O(1)), the bucket totals, and their exclusive scan -> offs[nb*C + 1]
 // (threads over consecutive buckets, then a scan of the thread totals). With items
 // set, the same pass lists the atom work items (runs of at most kAtomSeg positions of
-// a bucket), pads the list with empty items, and lists the buckets of several items
-// with their partial slots.
+// a bucket), pads the list with empty items, lists the buckets of several items with
+// their partial slots, and records per bucket its first partial slot and item count.
 __global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
   if (t.perm == nullptr) return;
@@ -776,6 +776,7 @@ __global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
       for (int q = 0; q < ni; ++q)
         items[it + q] = make_int4(pos + kAtomSeg * q, min(kAtomSeg, cnt - kAtomSeg * q), ni > 1 ? pt + q : -1, e);
       if (ni > 1) multi[1 + mb++] = make_int4(e, pt, ni, 0);
+      t.bmeta[static_cast<size_t>(bh) * nbC + e] = make_int2(ni > 1 ? pt : -1, ni);
       it += ni;
       pt += ni > 1 ? ni : 0;
     }

@@ -131,7 +131,7 @@ struct Plan {
   size_t cent_q, cent_k, lab_q, lab_k, tperm_q, tperm_k, tcnt_q, tcnt_k, tst_q, tst_k, psum_q, psum_k;
   size_t gcnt_q, gcnt_k;
   size_t perm_k, offs_k, perm_q, offs_q;
-  size_t items_k, multi_k, pt_m, pt_z, pt_k, pt_v;
+  size_t items_k, multi_k, bmeta_k, pt_m, pt_z, pt_k, pt_v;
   size_t t_khi, t_klo, t_vhi, t_vlo, t_dip, tiles, ntiles, tile_base;
   int max_tiles;
   size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores;
@@ -179,6 +179,7 @@ Plan make_plan(const Shape& s, const muse_fwd_params* p) {
     const size_t np = muse::atom_max_partials(static_cast<int>(N));
     P.items_k = L.take(BH * ni * 4 * i4);
     P.multi_k = L.take(BH * (1 + muse::atom_max_multi(static_cast<int>(N))) * 4 * i4);
+    P.bmeta_k = L.take(BH * nb * Ck * 2 * i4);
     P.pt_m = L.take(BH * np * Cq * f);
     P.pt_z = L.take(BH * np * Cq * f);
     P.pt_k = L.take(BH * np * Cq * D * f);
@@ -286,6 +287,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   tk.offs = at<int32_t>(ws, P.offs_k);
   tk.items = mf ? at<int4>(ws, P.items_k) : nullptr;
   tk.multi = mf ? at<int4>(ws, P.multi_k) : nullptr;
+  tk.bmeta = mf ? at<int2>(ws, P.bmeta_k) : nullptr;
   hipError_t e = launch_kmeans(km, s.iters, s.dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "K-means launch");
 
@@ -308,6 +310,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.offs_k = tk.offs;
   a1.items_k = tk.items;
   a1.multi_k = tk.multi;
+  a1.bmeta_k = tk.bmeta;
   if (mf) {
     a1.pt_m = at<float>(ws, P.pt_m);
     a1.pt_z = at<float>(ws, P.pt_z);

@@ -46,6 +46,7 @@ struct KmTensor {
   int4* items;                 // [BH, atom_max_items] (first position, positions (-1: none), partial slot or -1, bucket)
   int4* multi;                 // [BH, 1 + atom_max_multi]: (count), then (bucket, first partial slot, items) per
                                // bucket of several items
+  int2* bmeta;                 // [BH, nb*C]: per bucket (first partial slot or -1, items)
 };
 
 struct KmArgs {
@@ -108,6 +109,7 @@ struct S1Args {
   const int32_t* offs_k;       // [BH, nb*Ck + 1]
   const int4* items_k;         // [BH, atom_max_items] atom work items (matrix-core path)
   const int4* multi_k;         // [BH, 1 + atom_max_multi] buckets of several items
+  const int2* bmeta_k;         // [BH, nb*Ck] per bucket (first partial slot or -1, items)
   // partial atoms of buckets with several work items: [BH, atom_max_partials, Cq(, D)]
   float* pt_m;
   float* pt_z;

@@ -97,6 +97,7 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
 
 constexpr int kAtomChunk = 32;  // positions per step
 constexpr int kMergeGrid = 64;  // merge workgroups per head (each loops over the multi-item buckets)
+constexpr int kFinQB = 4;       // work items of a bucket folded per batch by the acausal finalise
 
 // One wave per atom work item (a run of at most kAtomSeg positions of one (block, key
 // cluster) bucket), for every query centroid in tiles of 32. The workgroup first stages
@@ -558,17 +559,55 @@ __global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
   __shared__ __align__(16) uint16_t sVh[JC * ST];
   __shared__ __align__(16) uint16_t sVl[JC * ST];
   __shared__ __align__(16) float sP[kMaxClusters];
+  __shared__ float sM[kMaxClusters], sInv[kMaxClusters];
+  __shared__ float sW[kMaxClusters][kFinQB];  // item weights exp(m_q - M) of the first kFinQB items
+  __shared__ int2 sMeta[kMaxClusters];
   __shared__ float red[8];
   const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int Cq = a.Cq, Ck = a.Ck;
   const size_t sidx = static_cast<size_t>(bh) * Cq + i;  // one table entry per (head, i)
   const size_t aidx0 = sidx * Ck;                         // atoms of the single block
+  const size_t pb = static_cast<size_t>(bh) * atom_max_partials(a.N);
 
-  // log Z_ij and P_ij = softmax_j log Z_ij
+  // log Z_ij and P_ij = softmax_j log Z_ij. The atom of cluster j is the bucket's own,
+  // or the log-sum-exp fold (in item order) of its work items' partial atoms, kFinQB
+  // items' loads in flight at a time.
   float lz = kNegInf;
   if (tid < Ck) {
-    const float m = a.at_m[aidx0 + tid], z = a.at_z[aidx0 + tid];
+    const int2 mt = a.bmeta_k[static_cast<size_t>(bh) * Ck + tid];  // (first partial slot or -1, items)
+    float m = kNegInf, z = 0.f;
+    if (mt.x < 0) {
+      m = a.at_m[aidx0 + tid];
+      z = a.at_z[aidx0 + tid];
+    } else {
+      for (int q0 = 0; q0 < mt.y; q0 += kFinQB) {
+        float mq[kFinQB], zq[kFinQB];
+#pragma unroll
+        for (int q = 0; q < kFinQB; ++q) {
+          const size_t pi = (pb + mt.x + min(q0 + q, mt.y - 1)) * Cq + i;
+          mq[q] = a.pt_m[pi];
+          zq[q] = a.pt_z[pi];
+          if (q0 + q >= mt.y) mq[q] = kNegInf;
+        }
+        float bm = m;
+#pragma unroll
+        for (int q = 0; q < kFinQB; ++q) bm = fmaxf(bm, mq[q]);
+        z *= m == kNegInf ? 0.f : __expf(m - bm);
+#pragma unroll
+        for (int q = 0; q < kFinQB; ++q) z = fmaf(mq[q] == kNegInf ? 0.f : __expf(mq[q] - bm), zq[q], z);
+        m = bm;
+      }
+      // weights of the first items relative to the final max (the rest are recomputed)
+#pragma unroll
+      for (int q = 0; q < kFinQB; ++q) {
+        const float mq = q < mt.y ? a.pt_m[(pb + mt.x + q) * Cq + i] : kNegInf;
+        sW[tid][q] = mq == kNegInf ? 0.f : __expf(mq - m);
+      }
+    }
+    sMeta[tid] = mt;
+    sM[tid] = m;
+    sInv[tid] = z > 0.f ? 1.f / z : 0.f;
     lz = z > 0.f ? m + __logf(z) : kNegInf;
     a.s_logz[sidx * Ck + tid] = lz;
   }
@@ -597,48 +636,104 @@ __global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
       ws += R == kNegInf ? 0.f : __expf(R - Rm);
     }
     const float winv = ws > 0.f ? 1.f / ws : 0.f;
-    for (int mb = 0; mb < a.nmb; ++mb) {
-      const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
-      const float R = a.blk_lmass[bidx];
-      if (R == kNegInf) continue;
-      const float w = __expf(R - Rm) * winv;
-      const float* M = a.blk_mom + bidx * D * D;
+    // MB slices' loads in flight at a time, folded in slice order
+    constexpr int MB = D == 64 ? 4 : 1;
+    for (int mb0 = 0; mb0 < a.nmb; mb0 += MB) {
+      float mv[MB][TPW][16], w[MB];
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
+      for (int u = 0; u < MB; ++u) {
+        const int mb = min(mb0 + u, a.nmb - 1);
+        const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
+        const float R = mb0 + u < a.nmb ? a.blk_lmass[bidx] : kNegInf;
+        w[u] = R == kNegInf ? 0.f : __expf(R - Rm) * winv;
+        const float* M = a.blk_mom + bidx * D * D;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = 32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3);
-          acc[t][v] = fmaf(-w, M[static_cast<size_t>(row) * D + 32 * dkt + c], acc[t][v]);
+        for (int t = 0; t < TPW; ++t) {
+          const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = 32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3);
+            mv[u][t][v] = M[static_cast<size_t>(row) * D + 32 * dkt + c];
+          }
         }
+      }
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        if (w[u] == 0.f) continue;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[t][v] = fmaf(-w[u], mv[u][t][v], acc[t][v]);
       }
     }
   }
 
   for (int j0 = 0; j0 < Ck; j0 += JC) {
     __syncthreads();  // sP complete / previous chunk consumed
-    // normalised K_ij, V_ij of this chunk: global K tables, LDS hi/lo tiles
-    for (int e = tid; e < JC * D / 4; e += 256) {
-      const int jj = e / (D / 4), d4 = (e % (D / 4)) * 4, j = j0 + jj;
-      float kk[4] = {0.f, 0.f, 0.f, 0.f}, vv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (j < Ck) {
-        const float z = a.at_z[aidx0 + j];
-        const float inv = z > 0.f ? 1.f / z : 0.f;
-        const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(a.at_k + (aidx0 + j) * D + d4);
-        const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(a.at_v + (aidx0 + j) * D + d4);
+    // normalised K_ij, V_ij of this chunk: global K tables, LDS hi/lo tiles; all of the
+    // thread's loads first, then the conversions and stores
+    constexpr int NF = JC * D / 4 / 256;
+    float kk[NF][4], vv[NF][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          kk[q] = k4[q] * inv;
-          vv[q] = v4[q] * inv;
+    for (int f = 0; f < NF; ++f) {
+      const int e = tid + 256 * f;
+      const int jj = e / (D / 4), d4 = (e % (D / 4)) * 4, j = j0 + jj;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        kk[f][q] = 0.f;
+        vv[f][q] = 0.f;
+      }
+      if (j < Ck) {
+        const int2 mt = sMeta[j];
+        const float inv = sInv[j];
+        if (mt.x < 0) {
+          const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(a.at_k + (aidx0 + j) * D + d4);
+          const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(a.at_v + (aidx0 + j) * D + d4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            kk[f][q] = k4[q] * inv;
+            vv[f][q] = v4[q] * inv;
+          }
+        } else {
+          for (int q0 = 0; q0 < mt.y; q0 += kFinQB) {
+            f32x4_t k4[kFinQB], v4[kFinQB];
+            float w[kFinQB];
+#pragma unroll
+            for (int q = 0; q < kFinQB; ++q) {
+              const size_t pi = (pb + mt.x + min(q0 + q, mt.y - 1)) * Cq + i;
+              k4[q] = *reinterpret_cast<const f32x4_t*>(a.pt_k + pi * D + d4);
+              v4[q] = *reinterpret_cast<const f32x4_t*>(a.pt_v + pi * D + d4);
+              if (q0 == 0) {
+                w[q] = sW[j][q];
+              } else {
+                const float mq = a.pt_m[pi];
+                w[q] = (q0 + q < mt.y && mq != kNegInf) ? __expf(mq - sM[j]) : 0.f;
+              }
+            }
+#pragma unroll
+            for (int q = 0; q < kFinQB; ++q) {
+              const float wq = w[q] * inv;
+#pragma unroll
+              for (int c4 = 0; c4 < 4; ++c4) {
+                kk[f][c4] = fmaf(wq, k4[q][c4], kk[f][c4]);
+                vv[f][c4] = fmaf(wq, v4[q][c4], vv[f][c4]);
+              }
+            }
+          }
         }
       }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int e = tid + 256 * f;
+      const int jj = e / (D / 4), d4 = (e % (D / 4)) * 4, j = j0 + jj;
       u16x4_t kh, kl, vh, vl;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        kh[q] = f32_to_bf16_bits(kk[q]);
-        kl[q] = f32_to_bf16_bits(kk[q] - bf16_to_f32(kh[q]));
-        vh[q] = f32_to_bf16_bits(vv[q]);
-        vl[q] = f32_to_bf16_bits(vv[q] - bf16_to_f32(vh[q]));
+        kh[q] = f32_to_bf16_bits(kk[f][q]);
+        kl[q] = f32_to_bf16_bits(kk[f][q] - bf16_to_f32(kh[q]));
+        vh[q] = f32_to_bf16_bits(vv[f][q]);
+        vl[q] = f32_to_bf16_bits(vv[f][q] - bf16_to_f32(vh[q]));
       }
       if (j < Ck) {
         *reinterpret_cast<u16x4_t*>(a.t_khi + (sidx * Ck + j) * D + d4) = kh;
@@ -974,8 +1069,12 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
       ProfScope ps_("s1_atoms_mfma", s);
       hipLaunchKernelGGL((s1_atoms_mfma_kernel<D>), dim3((atom_max_items(nbC, a.N) + 3) / 4, a.BH), dim3(256), lds, s, a);
     }
-    ProfScope ps_("s1_atoms_merge", s);
-    hipLaunchKernelGGL((s1_atoms_merge_kernel<D>), dim3(std::min(kMergeGrid, atom_max_multi(a.N)), a.BH), dim3(1024), 0, s, a);
+    // the acausal finalise folds the items itself; the causal scan and retrieval read
+    // merged atoms
+    if (a.causal || a.retr != nullptr) {
+      ProfScope ps_("s1_atoms_merge", s);
+      hipLaunchKernelGGL((s1_atoms_merge_kernel<D>), dim3(std::min(kMergeGrid, atom_max_multi(a.N)), a.BH), dim3(1024), 0, s, a);
+    }
   } else if (which == 2) {
     constexpr int G = MomCfg<D>::G;
     ProfScope ps_("s1_moments_f16", s);
