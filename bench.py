@@ -76,6 +76,8 @@ def kernel_work(name: str, cfg):
         "s1_mom_prefix": (BH * nmb * Cq * (D * D + 1) * 4 + dip32, 0.0),
         "s1_dip_final": (ftab + 2 * dip32, 2.0 * BH * nb * Cq * Ck * D * D),
         "s1_pack": (ftab + dip32 + tbytes + dip32 // 2, 0.0),
+        "s1_causal_scan": (table * (2 + 2 * D) * 4 + BH * nmb * Cq * (D * D + 1) * 4 + tbytes + BH * nb * Cq * D * D * 2,
+                           2.0 * BH * nb * Cq * Ck * D * D),
         "s2_mfma": (x + x + tbytes + BH * nb * Cq * D * D * 2, 2.0 * BH * N * (2 * Ck * D + D * D)),
         "s2_refine": (x + x + table * (1 + 2 * D) * 4 + BH * nb * Cq * D * D * 4, 2.0 * BH * N * (2 * Ck * D + D * D)),
         "local_block_mfma": (3 * x + BH * N * D * 4, 4.0 * BH * N * (cfg.block / 2) * D),
