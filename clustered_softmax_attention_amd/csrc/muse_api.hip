@@ -134,7 +134,7 @@ struct Plan {
   size_t items_k, multi_k, bmeta_k, pt_m, pt_z, pt_k, pt_v;
   size_t t_khi, t_klo, t_vhi, t_vlo, t_dip, tiles, ntiles, tile_base;
   int max_tiles;
-  size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores;
+  size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores, tmax;
   size_t s_logz, s_k, s_v, s_dip;
   size_t o_far, l_far, retr_sel;
   size_t total;
@@ -190,6 +190,7 @@ Plan make_plan(const Shape& s, const muse_fwd_params* p) {
   P.at_k = L.take(BH * nb * Cq * Ck * D * f);
   P.at_v = L.take(BH * nb * Cq * Ck * D * f);
   P.scores = s.dtype == MUSE_BF16 ? L.take(BH * Cq * N * f) : 0;
+  P.tmax = s.dtype == MUSE_BF16 ? L.take(BH * Cq * ((N + 31) / 32) * f) : 0;
   P.blk_lmass = L.take(BH * static_cast<size_t>(s.nmb) * Cq * f);
   P.blk_mom = L.take(BH * static_cast<size_t>(s.nmb) * Cq * D * D * f);
   P.s_logz = L.take(BH * nbS * Cq * Ck * f);
@@ -322,6 +323,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.at_k = at<float>(ws, P.at_k);
   a1.at_v = at<float>(ws, P.at_v);
   a1.scores = mf ? at<float>(ws, P.scores) : nullptr;
+  a1.tmax = mf ? at<float>(ws, P.tmax) : nullptr;
   a1.nmb = s.nmb;
   a1.mbk = s.mbk;
   a1.blk_lmass = at<float>(ws, P.blk_lmass);

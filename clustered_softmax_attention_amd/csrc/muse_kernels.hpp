@@ -122,6 +122,7 @@ struct S1Args {
   float* at_v;                 // [BH, nb, Cq, Ck, D] sum exp(a - m) v
   int nmb, mbk;                // moment sub-blocks: count and keys per sub-block (divides block)
   float* scores;               // [BH, Cq, N] s qbar_i . k_m (matrix-core path) or null
+  float* tmax;                 // [BH, Cq, ceil(N / 32)] max of the scores of every 32 positions
   float* blk_lmass;            // [BH, nmb, Cq] log mass of a sub-block seen by centroid i
   float* blk_mom;              // [BH, nmb, Cq, D, D] sub-block-normalised sum w v k^T (v index first)
   // summary tables

@@ -75,9 +75,18 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
         acc = mfma32(ak[ks], as_bf16x8(*reinterpret_cast<const u16x8_t*>(qhi + o)), acc);
         acc = mfma32(ak[ks], as_bf16x8(*reinterpret_cast<const u16x8_t*>(qlo + o)), acc);
       }
-      // lane (c, h): centroid 32 nt + c, positions kb + 8 g + 4 h + r
+      // lane (c, h): centroid 32 nt + c, positions kb + 8 g + 4 h + r; the max over the
+      // tile's 32 positions goes to tmax (position ranges of the moments are whole tiles)
       const int i = 32 * nt + c;
+      float tm = kNegInf;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kb + 8 * g + 4 * h + r < a.N) tm = fmaxf(tm, a.scale * acc[4 * g + r]);
+      tm = fmaxf(tm, xor32(tm));
       if (i >= Cq) continue;
+      if (h == 0) a.tmax[(static_cast<size_t>(bh) * Cq + i) * ((a.N + 31) / 32) + kb / 32] = tm;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int k0 = kb + 8 * g + 4 * h;
@@ -378,22 +387,23 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + key0;
   for (int k = tid; k < nkeys; k += 512) s_perm[k] = perm[k];
 
-  // max of the scores over the range, per centroid: 32 lanes (a half-wave) per centroid,
-  // 16 loads of each lane in flight at once
+  // max of the scores over the range, per centroid, from the maxima of its 32-position
+  // tiles (the range starts on a tile): 32 lanes (a half-wave) per centroid
+  const int ntl = (a.N + 31) / 32, t0 = key0 / 32, t1 = (key1 + 31) / 32;
   for (int g0 = 2 * wave; g0 < G; g0 += 16) {
     const int g = g0 + h;
     float mx = kNegInf;
     if (g < ng) {
-      const float* Sg = S + static_cast<size_t>(g) * a.N;
-      for (int k0 = 0; k0 < nkeys; k0 += 32 * 16) {
-        float x[16];
+      const float* Tg = a.tmax + (static_cast<size_t>(bh) * Cq + i0 + g) * ntl;
+      for (int tb = t0; tb < t1; tb += 32 * 8) {
+        float x[8];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int k = k0 + (lane & 31) + 32 * q;
-          x[q] = k < nkeys ? Sg[k] : kNegInf;
+        for (int q = 0; q < 8; ++q) {
+          const int tt = tb + (lane & 31) + 32 * q;
+          x[q] = tt < t1 ? Tg[tt] : kNegInf;
         }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) mx = fmaxf(mx, x[q]);
+        for (int q = 0; q < 8; ++q) mx = fmaxf(mx, x[q]);
       }
     }
     mx = half_wave_max(mx);
