@@ -718,16 +718,18 @@ __global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
 // set, the same pass lists the atom work items (runs of at most kAtomSeg positions of
 // a bucket), pads the list with empty items, lists the buckets of several items with
 // their partial slots, and records per bucket its first partial slot and item count.
+// With chunks set (query tensor), it lists the stage-2 chunks: runs of at most kS2Chunk
+// positions of one bucket.
 __global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
   if (t.perm == nullptr) return;
-  __shared__ int s_run[4][256];
+  __shared__ int s_run[5][256];
   const int C = t.C, bh = blockIdx.y, tid = threadIdx.x;
   const int nbC = a.nb * C;
-  const bool segs = t.items != nullptr;
+  const bool segs = t.items != nullptr, chk = t.chunks != nullptr;
   const int per = (nbC + 255) / 256, e0 = min(nbC, tid * per), e1 = min(nbC, e0 + per);
   int* offs = t.offs + static_cast<size_t>(bh) * (nbC + 1);
-  int tot[4] = {0, 0, 0, 0};  // positions, items, partial slots, buckets of several items
+  int tot[5] = {0, 0, 0, 0, 0};  // positions, items, partial slots, buckets of several items, chunks
   for (int e = e0; e < e1; ++e) {
     const int b = e / C, j = e % C;
     int run = 0;
@@ -750,21 +752,23 @@ __global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
     tot[1] += ni;
     tot[2] += ni > 1 ? ni : 0;
     tot[3] += ni > 1 ? 1 : 0;
+    tot[4] += (run + kS2Chunk - 1) / kS2Chunk;
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) s_run[r][tid] = tot[r];
+  for (int r = 0; r < 5; ++r) s_run[r][tid] = tot[r];
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
-    int x[4];
+    int x[5];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = tid >= o ? s_run[r][tid - o] : 0;
+    for (int r = 0; r < 5; ++r) x[r] = tid >= o ? s_run[r][tid - o] : 0;
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s_run[r][tid] += x[r];
+    for (int r = 0; r < 5; ++r) s_run[r][tid] += x[r];
     __syncthreads();
   }
   int pos = s_run[0][tid] - tot[0], it = s_run[1][tid] - tot[1], pt = s_run[2][tid] - tot[2],
-      mb = s_run[3][tid] - tot[3];
+      mb = s_run[3][tid] - tot[3], ck = s_run[4][tid] - tot[4];
+  int2* chunks = chk ? t.chunks + static_cast<size_t>(bh) * t.max_chunks : nullptr;
   const int max_items = atom_max_items(nbC, a.N);
   int4* items = segs ? t.items + static_cast<size_t>(bh) * max_items : nullptr;
   int4* multi = segs ? t.multi + static_cast<size_t>(bh) * (1 + atom_max_multi(a.N)) : nullptr;
@@ -780,9 +784,14 @@ __global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
       it += ni;
       pt += ni > 1 ? ni : 0;
     }
+    if (chk)
+      for (int st = 0; st < cnt; st += kS2Chunk) chunks[ck++] = make_int2(e, pos + st);
     pos += cnt;
   }
-  if (tid == 255) offs[nbC] = s_run[0][255];
+  if (tid == 255) {
+    offs[nbC] = s_run[0][255];
+    if (chk) t.nchunks[bh] = s_run[4][255];
+  }
   if (segs) {
     const int nit = s_run[1][255];
     for (int g = nit + tid; g < max_items; g += 256) items[g] = make_int4(0, -1, -1, 0);

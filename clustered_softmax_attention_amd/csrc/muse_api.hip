@@ -132,7 +132,7 @@ struct Plan {
   size_t gcnt_q, gcnt_k;
   size_t perm_k, offs_k, perm_q, offs_q;
   size_t items_k, multi_k, bmeta_k, pt_m, pt_z, pt_k, pt_v;
-  size_t t_khi, t_klo, t_vhi, t_vlo, t_dip, tiles, ntiles, tile_base;
+  size_t t_khi, t_klo, t_vhi, t_vlo, t_dip, tiles, ntiles;
   int max_tiles;
   size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores, tmax;
   size_t s_logz, s_k, s_v, s_dip;
@@ -210,10 +210,10 @@ Plan make_plan(const Shape& s, const muse_fwd_params* p) {
     P.t_vhi = L.take(BH * nbS * Cq * Ck * D * h2);
     P.t_vlo = L.take(BH * nbS * Cq * Ck * D * h2);
     P.t_dip = L.take(BH * nbS * Cq * D * D * h2);
-    P.max_tiles = static_cast<int>((N + 127) / 128 + nb * Cq);  // 128-query chunks of the buckets
+    // stage-2 chunks of the query buckets: at most ceil(N / kS2Chunk) + nb*Cq per head
+    P.max_tiles = static_cast<int>((N + muse::kS2Chunk - 1) / muse::kS2Chunk + nb * Cq);
     P.tiles = L.take(BH * P.max_tiles * 2 * i4);
     P.ntiles = L.take(BH * i4);
-    P.tile_base = L.take(BH * (nb * Cq + 1) * i4);
   }
   P.total = L.bytes;
   return P;
@@ -269,6 +269,11 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   // the matrix-core stage 2 and retrieval need the query buckets
   tq.perm = (mf || retr) ? at<int32_t>(ws, P.perm_q) : nullptr;
   tq.offs = (mf || retr) ? at<int32_t>(ws, P.offs_q) : nullptr;
+  if (mf) {
+    tq.chunks = at<int2>(ws, P.tiles);
+    tq.nchunks = at<int32_t>(ws, P.ntiles);
+    tq.max_chunks = P.max_tiles;
+  }
   KmTensor& tk = km.t[1];
   tk.x = k;
   tk.C = s.Ck;
@@ -408,7 +413,6 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   if (mf) {
     a2.tiles = at<int2>(ws, P.tiles);
     a2.ntiles = at<int32_t>(ws, P.ntiles);
-    a2.tile_base = at<int32_t>(ws, P.tile_base);
     a2.max_tiles = P.max_tiles;
   }
   if (s.causal) {

@@ -18,6 +18,7 @@ constexpr int moments_group(int D) { return D == 64 ? 16 : 4; }
 // than one item (fewer than ceil(N / kAtomSeg) of them) hold fewer than 2 ceil(N /
 // kAtomSeg) items together, each with a partial-atom slot.
 constexpr int kAtomSeg = 64;
+constexpr int kS2Chunk = 128;  // queries per matrix-core stage-2 workgroup (a run of one query bucket)
 __host__ __device__ constexpr int atom_max_items(int nbC, int N) { return nbC + (N + kAtomSeg - 1) / kAtomSeg; }
 __host__ __device__ constexpr int atom_max_multi(int N) { return (N + kAtomSeg - 1) / kAtomSeg; }
 __host__ __device__ constexpr int atom_max_partials(int N) { return 2 * atom_max_multi(N); }
@@ -47,6 +48,11 @@ struct KmTensor {
   int4* multi;                 // [BH, 1 + atom_max_multi]: (count), then (bucket, first partial slot, items) per
                                // bucket of several items
   int2* bmeta;                 // [BH, nb*C]: per bucket (first partial slot or -1, items)
+  // stage-2 chunks (query tensor, matrix-core path; null otherwise): runs of at most
+  // kS2Chunk positions of one bucket
+  int2* chunks;                // [BH, max_chunks] (bucket, first position)
+  int32_t* nchunks;            // [BH]
+  int max_chunks;
 };
 
 struct KmArgs {
@@ -170,9 +176,8 @@ struct S2Args {
   const int32_t* perm_q;       // [BH, N] queries by (block, label)
   const int32_t* offs_q;       // [BH, nb*Cq + 1]
   int nb;                      // query blocks (1 when acausal)
-  int2* tiles;                 // [BH, max_tiles] (bucket, first position) of 128-query chunks
-  int32_t* ntiles;             // [BH]
-  int32_t* tile_base;          // [BH, nb*Cq + 1] scratch: first tile of every bucket
+  const int2* tiles;           // [BH, max_tiles] (bucket, first position) of kS2Chunk-query chunks
+  const int32_t* ntiles;       // [BH] (both listed by the query tensor's bucket pass)
   int max_tiles;
 };
 

@@ -20,7 +20,6 @@
 namespace muse {
 
 constexpr int kS2Threads = 128;
-constexpr int kS2Chunk = 128;  // queries per matrix-core stage-2 workgroup
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kS2Threads) s2_refine_kernel(S2Args a) {
@@ -106,33 +105,6 @@ __global__ void __launch_bounds__(kS2Threads) s2_refine_kernel(S2Args a) {
       for (int d = 0; d < D; ++d) static_cast<float*>(a.out)[row * D + d] = acc[d];
     }
   }
-}
-
-// One workgroup per head: chunks of at most kS2Chunk consecutive queries inside one
-// (block, cluster) bucket of the query permutation. Per-bucket chunk counts are scanned
-// in parallel (threads over consecutive buckets, then a scan of the thread totals).
-__global__ void __launch_bounds__(256) s2_tiles_kernel(S2Args a) {
-  __shared__ int s_tot[256];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int nbk = a.nb * a.Cq;
-  const int32_t* offs = a.offs_q + static_cast<size_t>(bh) * (nbk + 1);
-  int2* tiles = a.tiles + static_cast<size_t>(bh) * a.max_tiles;
-  const int per = (nbk + 255) / 256, u0 = min(nbk, tid * per), u1 = min(nbk, u0 + per);
-  int cnt = 0;
-  for (int u = u0; u < u1; ++u) cnt += (offs[u + 1] - offs[u] + kS2Chunk - 1) / kS2Chunk;
-  s_tot[tid] = cnt;
-  __syncthreads();
-  // exclusive scan of the 256 thread totals (Hillis-Steele in LDS)
-  for (int o = 1; o < 256; o <<= 1) {
-    const int x = tid >= o ? s_tot[tid - o] : 0;
-    __syncthreads();
-    s_tot[tid] += x;
-    __syncthreads();
-  }
-  int t = s_tot[tid] - cnt;
-  if (tid == 255) a.ntiles[bh] = s_tot[255];
-  for (int u = u0; u < u1; ++u)
-    for (int st = offs[u]; st < offs[u + 1]; st += kS2Chunk) tiles[t++] = make_int2(u, st);
 }
 
 // Matrix-core stage 2: one workgroup of 4 waves per chunk of up to 128 queries of one
@@ -367,10 +339,6 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
 
 hipError_t launch_stage2(const S2Args& a, int dtype, hipStream_t s) {
   if (dtype == 1) {
-    {
-      ProfScope ps_("s2_tiles", s);
-      hipLaunchKernelGGL(s2_tiles_kernel, dim3(a.BH), dim3(256), 0, s, a);
-    }
     ProfScope ps_("s2_mfma", s);
     const dim3 gm(a.max_tiles, a.BH);
     if (a.D == 64) hipLaunchKernelGGL((s2_mfma_kernel<64>), gm, dim3(256), 0, s, a);
