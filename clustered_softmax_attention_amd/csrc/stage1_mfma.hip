@@ -557,13 +557,19 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
 // E_i[v k^T] the mass-weighted mean of the slice moments, preset (negated) in the
 // accumulator layout, and sum_j P_ij V_ij K_ij^T on the matrix cores with both operands
 // split into bf16 hi + lo (hi.hi + hi.lo + lo.hi) and read through the transpose read
-// from row-major LDS tiles of 64 key clusters.
+// from row-major LDS tiles of 64 key clusters. A cluster whose bucket was cut into
+// several work items has its atom folded here from the items' partial atoms (log-sum-exp
+// in item order). Every load that depends on nothing (the atom sums of all clusters, the
+// slices' log masses and the first slices' moments) is issued at the start.
 template <int D>
-__global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
+__global__ void __launch_bounds__(256, 2) s1_finalize_acausal_kernel(S1Args a) {
   constexpr int JC = 64;
   constexpr int ST = D + 16;
   constexpr int NDT = D / 32;
   constexpr int TPW = NDT * NDT / 4;  // dipole output tiles per wave
+  constexpr int NCH = kMaxClusters / JC;  // cluster chunks
+  constexpr int NF = JC * D / 4 / 256;    // float4 of a chunk's K (and V) sums per thread
+  constexpr int MB = D == 64 ? 4 : 1;     // moment slices loaded per batch
   __shared__ __align__(16) uint16_t sKh[JC * ST];
   __shared__ __align__(16) uint16_t sKl[JC * ST];
   __shared__ __align__(16) uint16_t sVh[JC * ST];
@@ -580,17 +586,59 @@ __global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
   const size_t aidx0 = sidx * Ck;                         // atoms of the single block
   const size_t pb = static_cast<size_t>(bh) * atom_max_partials(a.N);
 
-  // log Z_ij and P_ij = softmax_j log Z_ij. The atom of cluster j is the bucket's own,
-  // or the log-sum-exp fold (in item order) of its work items' partial atoms, kFinQB
-  // items' loads in flight at a time.
+  // ---- loads that depend on nothing
+  int2 mt = make_int2(-1, 1);
+  float m0 = kNegInf, z0 = 0.f;
+  if (tid < Ck) {
+    mt = a.bmeta_k[static_cast<size_t>(bh) * Ck + tid];  // (first partial slot or -1, items)
+    m0 = a.at_m[aidx0 + tid];
+    z0 = a.at_z[aidx0 + tid];
+  }
+  // atom sums of every cluster (stale for clusters of several items, which are replaced);
+  // at D = 128 they are loaded chunk by chunk (registers)
+  constexpr int PCH = D == 64 ? NCH : 0;
+  auto load_atoms = [&](int cc, f32x4_t* k4, f32x4_t* v4) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int e = tid + 256 * f;
+      const int j = min(cc * JC + e / (D / 4), Ck - 1), d4 = (e % (D / 4)) * 4;
+      k4[f] = *reinterpret_cast<const f32x4_t*>(a.at_k + (aidx0 + j) * D + d4);
+      v4[f] = *reinterpret_cast<const f32x4_t*>(a.at_v + (aidx0 + j) * D + d4);
+    }
+  };
+  f32x4_t ak4[PCH > 0 ? PCH : 1][NF], av4[PCH > 0 ? PCH : 1][NF];
+#pragma unroll
+  for (int cc = 0; cc < PCH; ++cc)
+    if (cc * JC < Ck) load_atoms(cc, ak4[cc], av4[cc]);
+  // log masses of the first MB slices and their moments in the accumulator layout
+  float R0[MB], mv0[MB][TPW][16];
+  if (a.dipole) {
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const int mb = min(u, a.nmb - 1);
+      const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
+      R0[u] = u < a.nmb ? a.blk_lmass[bidx] : kNegInf;
+      const float* M = a.blk_mom + bidx * D * D;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = 32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3);
+          mv0[u][t][v] = M[static_cast<size_t>(row) * D + 32 * dkt + c];
+        }
+      }
+    }
+  }
+
+  // ---- log Z_ij and P_ij = softmax_j log Z_ij; a cluster of several items folds the
+  // items' (max, sum) kFinQB items' loads at a time
   float lz = kNegInf;
   if (tid < Ck) {
-    const int2 mt = a.bmeta_k[static_cast<size_t>(bh) * Ck + tid];  // (first partial slot or -1, items)
-    float m = kNegInf, z = 0.f;
-    if (mt.x < 0) {
-      m = a.at_m[aidx0 + tid];
-      z = a.at_z[aidx0 + tid];
-    } else {
+    float m = m0, z = z0;
+    if (mt.x >= 0) {
+      m = kNegInf;
+      z = 0.f;
       for (int q0 = 0; q0 < mt.y; q0 += kFinQB) {
         float mq[kFinQB], zq[kFinQB];
 #pragma unroll
@@ -633,22 +681,35 @@ __global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
   const float psum = (red[0] + red[1]) + (red[2] + red[3]);
   if (tid < kMaxClusters) sP[tid] = psum > 0.f ? p / psum : 0.f;
 
-  // -E_i[v k^T] in the accumulator layout: rows dv = 32 dvt + 8 (v/4) + 4 h + v%4, col dk = 32 dkt + c
+  // ---- -E_i[v k^T] in the accumulator layout: rows dv = 32 dvt + 8 (v/4) + 4 h + v%4,
+  // col dk = 32 dkt + c; the slice moments weighted by their normalised masses, folded in
+  // slice order
   f32x16_t acc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) acc[t] = zero16();
   if (a.dipole) {
     float Rm = kNegInf;
-    for (int mb = 0; mb < a.nmb; ++mb) Rm = fmaxf(Rm, a.blk_lmass[(static_cast<size_t>(bh) * a.nmb + mb) * Cq + i]);
+#pragma unroll
+    for (int u = 0; u < MB; ++u) Rm = fmaxf(Rm, R0[u]);
+    for (int mb = MB; mb < a.nmb; ++mb) Rm = fmaxf(Rm, a.blk_lmass[(static_cast<size_t>(bh) * a.nmb + mb) * Cq + i]);
     float ws = 0.f;
-    for (int mb = 0; mb < a.nmb; ++mb) {
+#pragma unroll
+    for (int u = 0; u < MB; ++u) ws += R0[u] == kNegInf ? 0.f : __expf(R0[u] - Rm);
+    for (int mb = MB; mb < a.nmb; ++mb) {
       const float R = a.blk_lmass[(static_cast<size_t>(bh) * a.nmb + mb) * Cq + i];
       ws += R == kNegInf ? 0.f : __expf(R - Rm);
     }
     const float winv = ws > 0.f ? 1.f / ws : 0.f;
-    // MB slices' loads in flight at a time, folded in slice order
-    constexpr int MB = D == 64 ? 4 : 1;
-    for (int mb0 = 0; mb0 < a.nmb; mb0 += MB) {
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const float w = R0[u] == kNegInf ? 0.f : __expf(R0[u] - Rm) * winv;
+      if (w == 0.f) continue;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[t][v] = fmaf(-w, mv0[u][t][v], acc[t][v]);
+    }
+    for (int mb0 = MB; mb0 < a.nmb; mb0 += MB) {
       float mv[MB][TPW][16], w[MB];
 #pragma unroll
       for (int u = 0; u < MB; ++u) {
@@ -678,11 +739,23 @@ __global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
     }
   }
 
-  for (int j0 = 0; j0 < Ck; j0 += JC) {
-    __syncthreads();  // sP complete / previous chunk consumed
-    // normalised K_ij, V_ij of this chunk: global K tables, LDS hi/lo tiles; all of the
-    // thread's loads first, then the conversions and stores
-    constexpr int NF = JC * D / 4 / 256;
+  // ---- per chunk of 64 clusters: normalised K_ij, V_ij (global tables, LDS hi/lo
+  // tiles), then sum_j P_ij V_ij K_ij^T over the chunk
+#pragma unroll
+  for (int cc = 0; cc < NCH; ++cc) {
+    const int j0 = cc * JC;
+    if (j0 >= Ck) break;
+    __syncthreads();  // sP, sMeta complete / previous chunk consumed
+    f32x4_t ck4[NF], cv4[NF];
+    if (cc < PCH) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        ck4[f] = ak4[cc < PCH ? cc : 0][f];
+        cv4[f] = av4[cc < PCH ? cc : 0][f];
+      }
+    } else {
+      load_atoms(cc, ck4, cv4);
+    }
     float kk[NF][4], vv[NF][4];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -694,30 +767,28 @@ __global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
         vv[f][q] = 0.f;
       }
       if (j < Ck) {
-        const int2 mt = sMeta[j];
+        const int2 mj = sMeta[j];
         const float inv = sInv[j];
-        if (mt.x < 0) {
-          const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(a.at_k + (aidx0 + j) * D + d4);
-          const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(a.at_v + (aidx0 + j) * D + d4);
+        if (mj.x < 0) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            kk[f][q] = k4[q] * inv;
-            vv[f][q] = v4[q] * inv;
+            kk[f][q] = ck4[f][q] * inv;
+            vv[f][q] = cv4[f][q] * inv;
           }
         } else {
-          for (int q0 = 0; q0 < mt.y; q0 += kFinQB) {
+          for (int q0 = 0; q0 < mj.y; q0 += kFinQB) {
             f32x4_t k4[kFinQB], v4[kFinQB];
             float w[kFinQB];
 #pragma unroll
             for (int q = 0; q < kFinQB; ++q) {
-              const size_t pi = (pb + mt.x + min(q0 + q, mt.y - 1)) * Cq + i;
+              const size_t pi = (pb + mj.x + min(q0 + q, mj.y - 1)) * Cq + i;
               k4[q] = *reinterpret_cast<const f32x4_t*>(a.pt_k + pi * D + d4);
               v4[q] = *reinterpret_cast<const f32x4_t*>(a.pt_v + pi * D + d4);
               if (q0 == 0) {
                 w[q] = sW[j][q];
               } else {
                 const float mq = a.pt_m[pi];
-                w[q] = (q0 + q < mt.y && mq != kNegInf) ? __expf(mq - sM[j]) : 0.f;
+                w[q] = (q0 + q < mj.y && mq != kNegInf) ? __expf(mq - sM[j]) : 0.f;
               }
             }
 #pragma unroll
@@ -757,7 +828,6 @@ __global__ void __launch_bounds__(256) s1_finalize_acausal_kernel(S1Args a) {
       *reinterpret_cast<u16x4_t*>(sVl + jj * ST + d4) = vl;
     }
     __syncthreads();
-    // sum_j P_ij V_ij K_ij^T over the chunk
     if (a.dipole) {
 #pragma unroll
       for (int ks = 0; ks < JC / 16; ++ks) {
