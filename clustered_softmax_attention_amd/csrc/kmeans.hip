@@ -106,12 +106,19 @@ __device__ void tile_sort(const KmArgs& a, const KmTensor& t, int lab, bool vali
     s_cnt[j] = run;
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int j = 0; j < C; ++j) {
-      s_start[j] = run;
-      run += s_cnt[j];
+  if (wave == 0) {
+    // exclusive scan of the C <= 128 label counts: two per lane, then a wave scan
+    const int lane = tid & 63, j0 = 2 * lane;
+    const int c0 = j0 < C ? s_cnt[j0] : 0, c1 = j0 + 1 < C ? s_cnt[j0 + 1] : 0;
+    int incl = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
     }
+    const int excl = incl - c0 - c1;
+    if (j0 < C) s_start[j0] = excl;
+    if (j0 + 1 < C) s_start[j0 + 1] = excl + c0;
   }
   __syncthreads();
   if (valid) s_sorted[s_start[lab] + s_whist[wave * C + lab] + rank_in_wave] = tid;
