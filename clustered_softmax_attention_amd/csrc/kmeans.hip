@@ -33,6 +33,8 @@
 #include "mfma.hpp"
 #include "muse_kernels.hpp"
 
+#include <type_traits>
+
 namespace muse {
 
 // Derived forms of centroid j used by the matrix-core assign: bf16 hi/lo split and
@@ -727,32 +729,25 @@ __global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
 // their partial slots, and records per bucket its first partial slot and item count.
 // With chunks set (query tensor), it lists the stage-2 chunks: runs of at most kS2Chunk
 // positions of one bucket.
-__global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
+template <int kBoThreads>
+__global__ void __launch_bounds__(kBoThreads) bucket_offsets_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
   if (t.perm == nullptr) return;
-  __shared__ int s_run[5][256];
+  __shared__ int s_run[5][kBoThreads];
   const int C = t.C, bh = blockIdx.y, tid = threadIdx.x;
   const int nbC = a.nb * C;
   const bool segs = t.items != nullptr, chk = t.chunks != nullptr;
-  const int per = (nbC + 255) / 256, e0 = min(nbC, tid * per), e1 = min(nbC, e0 + per);
+  const int per = (nbC + kBoThreads - 1) / kBoThreads, e0 = min(nbC, tid * per), e1 = min(nbC, e0 + per);
   int* offs = t.offs + static_cast<size_t>(bh) * (nbC + 1);
   int tot[5] = {0, 0, 0, 0, 0};  // positions, items, partial slots, buckets of several items, chunks
-  for (int e = e0; e < e1; ++e) {
-    const int b = e / C, j = e % C;
-    int run = 0;
-    const int t0 = b * a.tiles_per_block, t1 = min(a.ntiles, (b + 1) * a.tiles_per_block);
-    int32_t* pc = t.tile_cnt + (static_cast<size_t>(bh) * a.ntiles + t0) * C + j;
-    for (int tt = t0; tt < t1; tt += 8) {
-      // eight loads in flight, then the prefixes (members of (b, j) in earlier tiles)
-      int cnt[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) cnt[q] = tt + q < t1 ? pc[static_cast<size_t>(tt - t0 + q) * C] : 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (tt + q < t1) pc[static_cast<size_t>(tt - t0 + q) * C] = run;
-        run += cnt[q];
-      }
-    }
+  // Each tile's count is replaced by the members of (b, j) in the block's earlier tiles.
+  // Short blocks with many buckets per thread: the thread's (bucket, tile) pairs in order,
+  // 32 count loads in flight per batch, with cursors (bucket e = b C + j, tile ti of the block) that advance without
+  // divisions.
+  const int tpb = a.tiles_per_block;
+  const size_t tbase = static_cast<size_t>(bh) * a.ntiles;
+  int32_t* tcb = t.tile_cnt + tbase * C;  // this head's [ntiles, C] counts
+  auto finish = [&](int e, int run) {
     offs[e] = run;  // bucket total for now (only this thread touches entry e)
     const int ni = max(1, (run + kAtomSeg - 1) / kAtomSeg);
     tot[0] += run;
@@ -760,11 +755,76 @@ __global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
     tot[2] += ni > 1 ? ni : 0;
     tot[3] += ni > 1 ? 1 : 0;
     tot[4] += (run + kS2Chunk - 1) / kS2Chunk;
+  };
+  // long blocks (32 tiles or more, e.g. one block per head) or few buckets per thread:
+  // bucket by bucket, up to 32 tile counts per batch at a fixed stride
+  const bool by_bucket = tpb >= 32 || kBoThreads < 1024;
+  auto by_bucket_pass = [&](auto width) {
+    constexpr int W = decltype(width)::value;
+    for (int e = e0; e < e1; ++e) {
+      const int b = e / C, j = e % C, t0 = b * tpb, t1 = min(a.ntiles, t0 + tpb);
+      int32_t* pc = tcb + static_cast<size_t>(t0) * C + j;
+      int run = 0;
+      for (int tt = t0; tt < t1; tt += W) {
+        int cnt[W];
+#pragma unroll
+        for (int q = 0; q < W; ++q) cnt[q] = tt + q < t1 ? pc[static_cast<size_t>(tt - t0 + q) * C] : 0;
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+          if (tt + q < t1) pc[static_cast<size_t>(tt - t0 + q) * C] = run;
+          run += cnt[q];
+        }
+      }
+      finish(e, run);
+    }
+  };
+  if (by_bucket) {
+    if (tpb >= 32) by_bucket_pass(std::integral_constant<int, 32>{});
+    else by_bucket_pass(std::integral_constant<int, 8>{});
+  }
+  int le = e0, lb = e0 / C, lj = e0 % C, lti = 0;  // load cursor
+  int pe = by_bucket ? e1 : e0, pb = lb, pj = lj, pti = 0;  // processing cursor
+  int run = 0;
+  while (pe < e1) {
+    int cnt[32];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      // unconditional load at a clamped (in-bounds) address, zero when out of range;
+      // branch-free cursor step
+      const int tt = lb * tpb + lti;
+      const bool ok = le < e1 && tt < a.ntiles;
+      const int v = tcb[static_cast<uint32_t>(min(tt, a.ntiles - 1) * C + lj)];
+      cnt[q] = ok ? v : 0;
+      const bool wrap = ++lti == tpb;
+      lti = wrap ? 0 : lti;
+      le += wrap;
+      lj += wrap;
+      const bool wrapc = lj == C;
+      lj = wrapc ? 0 : lj;
+      lb += wrapc;
+    }
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      if (pe >= e1) break;
+      const int tt = pb * tpb + pti;
+      if (pti == 0) run = 0;
+      if (tt < a.ntiles) tcb[static_cast<uint32_t>(tt * C + pj)] = run;
+      run += cnt[q];
+      if (++pti == tpb) {
+        finish(pe, run);
+        pti = 0;
+        ++pe;
+        if (++pj == C) {
+          pj = 0;
+          ++pb;
+        }
+      }
+    }
   }
 #pragma unroll
   for (int r = 0; r < 5; ++r) s_run[r][tid] = tot[r];
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
+  for (int o = 1; o < kBoThreads; o <<= 1) {
     int x[5];
 #pragma unroll
     for (int r = 0; r < 5; ++r) x[r] = tid >= o ? s_run[r][tid - o] : 0;
@@ -795,14 +855,14 @@ __global__ void __launch_bounds__(256) bucket_offsets_kernel(KmArgs a) {
       for (int st = 0; st < cnt; st += kS2Chunk) chunks[ck++] = make_int2(e, pos + st);
     pos += cnt;
   }
-  if (tid == 255) {
-    offs[nbC] = s_run[0][255];
-    if (chk) t.nchunks[bh] = s_run[4][255];
+  if (tid == kBoThreads - 1) {
+    offs[nbC] = s_run[0][kBoThreads - 1];
+    if (chk) t.nchunks[bh] = s_run[4][kBoThreads - 1];
   }
   if (segs) {
-    const int nit = s_run[1][255];
-    for (int g = nit + tid; g < max_items; g += 256) items[g] = make_int4(0, -1, -1, 0);
-    if (tid == 255) multi[0] = make_int4(s_run[3][255], 0, 0, 0);
+    const int nit = s_run[1][kBoThreads - 1];
+    for (int g = nit + tid; g < max_items; g += kBoThreads) items[g] = make_int4(0, -1, -1, 0);
+    if (tid == kBoThreads - 1) multi[0] = make_int4(s_run[3][kBoThreads - 1], 0, 0, 0);
   }
 }
 
@@ -924,7 +984,11 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
   }
   {
     ProfScope ps_("bucket_offsets", s);
-    hipLaunchKernelGGL(bucket_offsets_kernel, dim3(1, a.BH, a.ntensors), dim3(256), 0, s, a);
+    // threads over consecutive buckets: 1024 when there are thousands of buckets
+    if (a.nb * Cmax >= 2048)
+      hipLaunchKernelGGL(bucket_offsets_kernel<1024>, dim3(1, a.BH, a.ntensors), dim3(1024), 0, s, a);
+    else
+      hipLaunchKernelGGL(bucket_offsets_kernel<256>, dim3(1, a.BH, a.ntensors), dim3(256), 0, s, a);
   }
   {
     ProfScope ps_("bucket_scatter", s);
