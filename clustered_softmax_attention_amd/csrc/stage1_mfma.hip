@@ -108,37 +108,42 @@ constexpr int kAtomChunk = 32;  // positions per step
 constexpr int kMergeGrid = 64;  // merge workgroups per head (each loops over the multi-item buckets)
 constexpr int kFinQB = 4;       // work items of a bucket folded per batch by the acausal finalise
 
-// One wave per atom work item (a run of at most kAtomSeg positions of one (block, key
-// cluster) bucket), for every query centroid in tiles of 32. The workgroup first stages
-// s qbar (split into bf16 hi + lo) in LDS for its four waves; each wave gathers its
-// item's permutation entries once (lane l holds position l) and hands them to the row
-// loads by a lane shuffle. Keys arrive in steps of 32 (rows gathered into a wave-private
-// row-major LDS tile, the next step's rows in flight meanwhile), and on the matrix cores
+// Atoms over work items (a run of at most kAtomSeg positions of one (block, key cluster)
+// bucket), for every query centroid in tiles of 32. A wave takes `ipw` consecutive items
+// (chosen by the launcher from the item count: one for a few hundred items per head,
+// more when there are thousands of small buckets) as one pipeline: while a step of 32 keys is on the
+// matrix cores, the rows of the next step (of this item or the next) are in flight, and
+// the permutation entries of the item after next are gathered (lane l holds position l
+// of its item; the row loads take them by lane shuffle). The workgroup first stages
+// s qbar (split into bf16 hi + lo) in LDS for its four waves. Per step, rows gathered into
+// a wave-private row-major LDS tile give on the matrix cores
 //   S = K_step (s qbar)^T   (32 keys x 32 centroids; keys exact),
 // so that lane (c, h) holds 16 keys of centroid c and the max over the item is
 // lane-local plus the partner lane l^32 (online across steps, sums rescaled when it
 // grows). The weights w = exp(S - max), split into hi + lo, are directly the B operand
 // of  sum w k = K^T W  and  sum w v = V^T W,  whose A operands come from the same LDS
 // tile through the transpose read in the accumulator's key order. A bucket of one item
-// writes its atom; the items of a larger bucket write partial atoms that
-// s1_atoms_merge folds.
+// writes its atom; the items of a larger bucket write partial atoms that are folded
+// later (s1_atoms_merge, or the acausal finalise).
 template <int D>
-__global__ void __launch_bounds__(256, D == 64 ? 3 : 1) s1_atoms_mfma_kernel(S1Args a) {
+__global__ void __launch_bounds__(256, D == 64 ? 3 : 1) s1_atoms_mfma_kernel(S1Args a, int ipw) {
   constexpr int NKS = D / 16, NMT = D / 32, KC = kAtomChunk, ST = D + 8, QST = D + 8;
   constexpr int NP = KC * (D / 8) / 64;  // 16-byte row pieces per lane and tensor
   static_assert(kAtomSeg <= 64, "one permutation entry per lane");
   __shared__ __align__(16) uint16_t sK[4][KC * ST];
   __shared__ __align__(16) uint16_t sV[4][KC * ST];
   extern __shared__ __align__(16) uint16_t sq[];  // s qbar hi, lo [Cqp][QST]
-  const int bh = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Cq = a.Cq, Ck = a.Ck, nbC = a.nb * Ck, Cqp = (Cq + 31) & ~31;
   const int max_items = atom_max_items(nbC, a.N);
-  const int g = blockIdx.x * 4 + wave;
-  int4 it = make_int4(0, -1, -1, 0);
-  if (g < max_items) it = a.items_k[static_cast<size_t>(bh) * max_items + g];
-  const int s0 = it.x, n = it.y;
-  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + s0;
-  const int pl = lane < n ? perm[lane] : 0;
+  const int g0 = (blockIdx.x * 4 + wave) * ipw;  // first item of this wave
+  const int4* items = a.items_k + static_cast<size_t>(bh) * max_items;
+  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
+  auto header = [&](int r) { return r < ipw && g0 + r < max_items ? items[g0 + r] : make_int4(0, -1, -1, 0); };
+  auto gather = [&](const int4& hd) { return lane < hd.y ? perm[hd.x + lane] : 0; };
+  int4 hd = header(0), hd_nx = header(1);
+  int pl = gather(hd), pl_nx = gather(hd_nx);
   uint16_t* qhi = sq;
   uint16_t* qlo = sq + Cqp * QST;
   for (int x = tid; x < Cqp * D; x += 256) {
@@ -149,28 +154,23 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 1) s1_atoms_mfma_kernel(S1A
     qlo[i * QST + d] = f32_to_bf16_bits(v - bf16_to_f32(hv));
   }
   __syncthreads();
-  if (n < 0) return;  // padding item; no workgroup barrier below
-  const int u = it.w, bp = u / Ck, j = u % Ck;
+  if (hd.y < 0) return;  // no item (padding); no workgroup barrier below
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
   uint16_t* kt = sK[wave];
   uint16_t* vt = sV[wave];
-  const size_t abase = (static_cast<size_t>(bh) * a.nb + bp) * Cq;
-  const bool part = it.z >= 0;
-  const size_t pbase = (static_cast<size_t>(bh) * atom_max_partials(a.N) + (part ? it.z : 0)) * Cq;
-  float* out_k = part ? a.pt_k : a.at_k;
-  float* out_v = part ? a.pt_v : a.at_v;
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
   u16x8_t pk[NP], pv[NP];
-  auto load_rows = [&](int p0) {
+  // rows p0 .. p0 + 31 of an item whose permutation entries are in pls
+  auto load_rows = [&](int pls, int n, int p0) {
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       const int x = lane + 64 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
-      const int key = __shfl(pl, p0 + r, 64);
+      const int key = __shfl(pls, p0 + r, 64);
       pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       pv[q] = pk[q];
       if (p0 + r < n) {
@@ -182,93 +182,117 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 1) s1_atoms_mfma_kernel(S1A
   };
   for (int nt = 0; nt < Cqp / 32; ++nt) {
     const int i = 32 * nt + c;
-    f32x16_t ak[NMT], av[NMT];
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      ak[mt] = zero16();
-      av[mt] = zero16();
+    if (nt > 0) {  // the pipeline restarts for each tile of 32 centroids
+      hd = header(0);
+      hd_nx = header(1);
+      pl = gather(hd);
+      pl_nx = gather(hd_nx);
     }
-    float mx = kNegInf, z = 0.f;
-    if (n > 0) load_rows(0);
-    for (int p0 = 0; p0 < n; p0 += KC) {
-      wave_sync();  // the previous step's tiles are consumed
+    if (hd.y > 0) load_rows(pl, hd.y, 0);
+    for (int r = 0; r < ipw; ++r) {
+      if (hd.y < 0) break;  // padding items end the list
+      const int n = hd.y, u = hd.w, bp = u / Ck, j = u % Ck;
+      f32x16_t ak[NMT], av[NMT];
 #pragma unroll
-      for (int q = 0; q < NP; ++q) {
-        const int x = lane + 64 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
-        *reinterpret_cast<u16x8_t*>(kt + r * ST + c8) = pk[q];
-        *reinterpret_cast<u16x8_t*>(vt + r * ST + c8) = pv[q];
+      for (int mt = 0; mt < NMT; ++mt) {
+        ak[mt] = zero16();
+        av[mt] = zero16();
       }
-      wave_sync();
-      if (p0 + KC < n) load_rows(p0 + KC);  // next step's rows in flight
-      f32x16_t sc = zero16();
+      float mx = kNegInf, z = 0.f;
+      for (int p0 = 0; p0 < n; p0 += KC) {
+        wave_sync();  // the previous step's tiles are consumed
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u16x8_t*>(kt + c * ST + 16 * ks + 8 * h));
-        const int qo = (32 * nt + c) * QST + 16 * ks + 8 * h;
-        sc = mfma32(ka, as_bf16x8(*reinterpret_cast<const u16x8_t*>(qhi + qo)), sc);
-        sc = mfma32(ka, as_bf16x8(*reinterpret_cast<const u16x8_t*>(qlo + qo)), sc);
-      }
-      // rows of sc: keys p0 + 8 (v/4) + 4 h + v%4
-      float cm = kNegInf;
+        for (int q = 0; q < NP; ++q) {
+          const int x = lane + 64 * q, rr = x / (D / 8), c8 = (x % (D / 8)) * 8;
+          *reinterpret_cast<u16x8_t*>(kt + rr * ST + c8) = pk[q];
+          *reinterpret_cast<u16x8_t*>(vt + rr * ST + c8) = pv[q];
+        }
+        wave_sync();
+        // the next step's rows in flight: this item's, or the next item's first
+        if (p0 + KC < n) load_rows(pl, n, p0 + KC);
+        else if (hd_nx.y > 0) load_rows(pl_nx, hd_nx.y, 0);
+        f32x16_t sc = zero16();
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = p0 + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (key >= n) sc[v] = kNegInf;
-        cm = fmaxf(cm, sc[v]);
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u16x8_t*>(kt + c * ST + 16 * ks + 8 * h));
+          const int qo = (32 * nt + c) * QST + 16 * ks + 8 * h;
+          sc = mfma32(ka, as_bf16x8(*reinterpret_cast<const u16x8_t*>(qhi + qo)), sc);
+          sc = mfma32(ka, as_bf16x8(*reinterpret_cast<const u16x8_t*>(qlo + qo)), sc);
+        }
+        // rows of sc: keys p0 + 8 (v/4) + 4 h + v%4
+        float cm = kNegInf;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = p0 + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (key >= n) sc[v] = kNegInf;
+          cm = fmaxf(cm, sc[v]);
+        }
+        cm = fmaxf(cm, xor32(cm));
+        if (cm > mx) {  // the same for the lane pair
+          const float f = mx == kNegInf ? 0.f : __expf(mx - cm);
+          z *= f;
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              ak[mt][v] *= f;
+              av[mt][v] *= f;
+            }
+          mx = cm;
+        }
+        float w[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          w[v] = __expf(sc[v] - mx);
+          z += w[v];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          bf16x8_t whi, wlo;
+          split_bf16x8(w + 8 * s, whi, wlo);
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt) {
+            const bf16x8_t kf = lds_operand_tr_acc(kt, ST, 16 * s, 32 * mt, lane);
+            const bf16x8_t vf = lds_operand_tr_acc(vt, ST, 16 * s, 32 * mt, lane);
+            ak[mt] = mfma32(kf, whi, ak[mt]);
+            ak[mt] = mfma32(kf, wlo, ak[mt]);
+            av[mt] = mfma32(vf, whi, av[mt]);
+            av[mt] = mfma32(vf, wlo, av[mt]);
+          }
+        }
       }
-      cm = fmaxf(cm, xor32(cm));
-      if (cm > mx) {  // the same for the lane pair
-        const float f = mx == kNegInf ? 0.f : __expf(mx - cm);
-        z *= f;
+      // an empty item issued no rows for the next one
+      if (n == 0 && hd_nx.y > 0) load_rows(pl_nx, hd_nx.y, 0);
+      z += xor32(z);
+      if (i < Cq) {
+        // the bucket's atom, or the item's partial when the bucket has several items
+        const bool part = hd.z >= 0;
+        const size_t aidx = part ? (static_cast<size_t>(bh) * atom_max_partials(a.N) + hd.z) * Cq + i
+                                 : ((static_cast<size_t>(bh) * a.nb + bp) * Cq + i) * Ck + j;
+        float* out_k = part ? a.pt_k : a.at_k;
+        float* out_v = part ? a.pt_v : a.at_v;
+        if (h == 0) {
+          (part ? a.pt_m : a.at_m)[aidx] = n > 0 ? mx : kNegInf;
+          (part ? a.pt_z : a.at_z)[aidx] = z;
+        }
+        // lane (c, h): column = centroid i, rows d = 32 mt + 8 g + 4 h + r
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            ak[mt][v] *= f;
-            av[mt][v] *= f;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * mt + 8 * g4 + 4 * h;
+            const f32x4_t fk = {ak[mt][4 * g4], ak[mt][4 * g4 + 1], ak[mt][4 * g4 + 2], ak[mt][4 * g4 + 3]};
+            const f32x4_t fv = {av[mt][4 * g4], av[mt][4 * g4 + 1], av[mt][4 * g4 + 2], av[mt][4 * g4 + 3]};
+            *reinterpret_cast<f32x4_t*>(out_k + aidx * D + d0) = fk;
+            *reinterpret_cast<f32x4_t*>(out_v + aidx * D + d0) = fv;
           }
-        mx = cm;
       }
-      float w[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        w[v] = __expf(sc[v] - mx);
-        z += w[v];
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8_t whi, wlo;
-        split_bf16x8(w + 8 * s, whi, wlo);
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-          const bf16x8_t kf = lds_operand_tr_acc(kt, ST, 16 * s, 32 * mt, lane);
-          const bf16x8_t vf = lds_operand_tr_acc(vt, ST, 16 * s, 32 * mt, lane);
-          ak[mt] = mfma32(kf, whi, ak[mt]);
-          ak[mt] = mfma32(kf, wlo, ak[mt]);
-          av[mt] = mfma32(vf, whi, av[mt]);
-          av[mt] = mfma32(vf, wlo, av[mt]);
-        }
-      }
+      // advance: the next item becomes current, the one after it is gathered
+      hd = hd_nx;
+      pl = pl_nx;
+      hd_nx = header(r + 2);
+      pl_nx = gather(hd_nx);
     }
-    z += xor32(z);
-    if (i >= Cq) continue;
-    // the bucket's atom, or the item's partial when the bucket has several items
-    const size_t aidx = part ? pbase + i : (abase + i) * Ck + j;
-    if (h == 0) {
-      (part ? a.pt_m : a.at_m)[aidx] = n > 0 ? mx : kNegInf;
-      (part ? a.pt_z : a.at_z)[aidx] = z;
-    }
-    // lane (c, h): column = centroid i, rows d = 32 mt + 8 g + 4 h + r
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * mt + 8 * g4 + 4 * h;
-        const f32x4_t fk = {ak[mt][4 * g4], ak[mt][4 * g4 + 1], ak[mt][4 * g4 + 2], ak[mt][4 * g4 + 3]};
-        const f32x4_t fv = {av[mt][4 * g4], av[mt][4 * g4 + 1], av[mt][4 * g4 + 2], av[mt][4 * g4 + 3]};
-        *reinterpret_cast<f32x4_t*>(out_k + aidx * D + d0) = fk;
-        *reinterpret_cast<f32x4_t*>(out_v + aidx * D + d0) = fv;
-      }
   }
 }
 
@@ -1146,8 +1170,17 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
     const size_t lds = static_cast<size_t>((a.Cq + 31) & ~31) * (D + 8) * 2 * sizeof(uint16_t);
     allow_lds((const void*)s1_atoms_mfma_kernel<D>, lds + 2 * 4 * kAtomChunk * (D + 8) * sizeof(uint16_t));
     {
+      // items per wave: about items / (16 x resident waves), rounded, 1..16 (measured: 2
+      // at 1.3k items per head x 64 heads with D = 64, 4-5 at 5k x 16 with D = 128)
+      int dev = 0, cus = 256;
+      (void)hipGetDevice(&dev);
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      const long resident = static_cast<long>(cus) * 4 * (D == 64 ? 3 : 1);
+      const long items = static_cast<long>(atom_max_items(nbC, a.N)) * a.BH;
+      const int ipw = static_cast<int>(std::max<long>(1, std::min<long>(16, (items + 8 * resident) / (16 * resident))));
+      const int waves = (atom_max_items(nbC, a.N) + ipw - 1) / ipw;
       ProfScope ps_("s1_atoms_mfma", s);
-      hipLaunchKernelGGL((s1_atoms_mfma_kernel<D>), dim3((atom_max_items(nbC, a.N) + 3) / 4, a.BH), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((s1_atoms_mfma_kernel<D>), dim3((waves + 3) / 4, a.BH), dim3(256), lds, s, a, ipw);
     }
     // the acausal finalise folds the items itself; the causal scan and retrieval read
     // merged atoms
