@@ -30,6 +30,17 @@ def test_acausal_bf16_ragged(muse_lib, N):
     check_config(cfg, [(0, 0), (0, 1)])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_odd_cluster_counts_long_buckets(muse_lib, causal):
+    # cluster counts off the 32-centroid tiles, a ragged tail, and key buckets longer
+    # than one 64-key atom work item (folded by the finalise, or merged when causal)
+    if causal:
+        cfg = scaled_config("causal_16k", B=1, H=2, N=3072, block=1024, Cq=12, Ck=20)
+    else:
+        cfg = scaled_config("acausal_8k", B=1, H=2, N=3000, Cq=20, Ck=40)
+    check_config(cfg, [(0, 0), (0, 1)])
+
+
 def test_acausal_bf16_d128(muse_lib):
     cfg = scaled_config("causal_64k_d128", B=1, H=2, N=2048, causal=False, block=0)
     check_config(cfg, [(0, 0), (0, 1)])
