@@ -76,17 +76,18 @@ __global__ void __launch_bounds__(64) kmeans_init_kernel(KmArgs a) {
 }
 
 // Stable counting sort of tile tt's points by label (LDS) and the tile's sort info.
-// Called by every thread of the workgroup (one thread per point of the tile).
-__device__ void tile_sort(const KmArgs& a, const KmTensor& t, int lab, bool valid, int tt, int* s_lab, int* s_whist,
+// Called by every thread of the workgroup; a thread owns point `pidx` of the tile when
+// `valid` (threads that own no point pass lab = C, which sorts nowhere). Points of equal
+// label keep the order of their owners (wave, then lane), which is point order.
+__device__ void tile_sort(const KmArgs& a, const KmTensor& t, int lab, bool valid, int pidx, int tt, int* s_whist,
                           int* s_cnt, int* s_start, int* s_sorted) {
   const int C = t.C;
   const int bh = blockIdx.y;
-  const int tile = blockDim.x;
+  const int nthr = blockDim.x;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  const int nwaves = tile >> 6;
-  for (int e = tid; e < nwaves * C; e += tile) s_whist[e] = 0;
-  s_lab[tid] = lab;
+  const int nwaves = nthr >> 6;
+  for (int e = tid; e < nwaves * C; e += nthr) s_whist[e] = 0;
   __syncthreads();
   // lanes of this wave with the same label (the sentinel C only matches itself)
   uint64_t peers = __ballot(1);
@@ -98,7 +99,7 @@ __device__ void tile_sort(const KmArgs& a, const KmTensor& t, int lab, bool vali
   const int rank_in_wave = __popcll(peers & lanemask_lt());
   if (valid && rank_in_wave == 0) s_whist[wave * C + lab] = __popcll(peers);
   __syncthreads();
-  for (int j = tid; j < C; j += tile) {
+  for (int j = tid; j < C; j += nthr) {
     int run = 0;
     for (int w = 0; w < nwaves; ++w) {
       const int h = s_whist[w * C + j];
@@ -123,16 +124,16 @@ __device__ void tile_sort(const KmArgs& a, const KmTensor& t, int lab, bool vali
     if (j0 + 1 < C) s_start[j0 + 1] = excl + c0;
   }
   __syncthreads();
-  if (valid) s_sorted[s_start[lab] + s_whist[wave * C + lab] + rank_in_wave] = tid;
+  if (valid) s_sorted[s_start[lab] + s_whist[wave * C + lab] + rank_in_wave] = pidx;
   __syncthreads();
 
   // ---- outputs: sort info for bucketing ----
   const size_t tix = static_cast<size_t>(bh) * a.ntiles + tt;
-  for (int j = tid; j < C; j += tile) {
+  for (int j = tid; j < C; j += nthr) {
     t.tile_cnt[tix * C + j] = s_cnt[j];
     t.tile_start[tix * C + j] = s_start[j];
   }
-  t.tile_perm[tix * a.tile + tid] = static_cast<uint16_t>(s_sorted[tid]);
+  for (int pos = tid; pos < a.tile; pos += nthr) t.tile_perm[tix * a.tile + pos] = static_cast<uint16_t>(s_sorted[pos]);
 }
 
 // Per-cluster sums of the tile in sorted order (fp32 path).
@@ -217,7 +218,7 @@ __global__ void __launch_bounds__(kMaxTile) kmeans_assign_kernel(KmArgs a, int i
     if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
   }
 
-  tile_sort(a, t, lab, valid, blockIdx.x, s_lab, s_whist, s_cnt, s_start, s_sorted);
+  tile_sort(a, t, lab, valid, static_cast<int>(threadIdx.x), blockIdx.x, s_whist, s_cnt, s_start, s_sorted);
   tile_sums_valu<T, D>(a, t, s_cnt, s_start, s_sorted);
 }
 
@@ -600,7 +601,7 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
       if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
     }
     slab[tid] = valid ? static_cast<uint16_t>(lab) : static_cast<uint16_t>(0xFFFF);
-    if (last) tile_sort(a, t, lab, valid, tt, s_lab, s_whist, s_cnt, s_start, s_sorted);
+    if (last) tile_sort(a, t, lab, valid, static_cast<int>(threadIdx.x), tt, s_whist, s_cnt, s_start, s_sorted);
     __syncthreads();  // X tile and labels complete
 
     for (int pass = 0; pass < npass; ++pass) {
@@ -657,6 +658,270 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
       }
     }
     __syncthreads();  // the next tile overwrites the X tile and labels
+  }
+}
+
+// Matrix-core assign for bf16 inputs with D = 64, eight waves of 32 points each over
+// 256-point tiles. Same method as km_assign_body; each wave now scores one 32-point
+// group (half the registers), so that two workgroups of eight waves share a compute
+// unit (four waves per SIMD to hide latency). The cluster sums are split over
+// (cluster tile, feature tile) outputs, one per wave. Lane (c, h) of wave w holds point
+// 32 w + c (features 16 ks + 8 h); the lanes h = 0 own the points for labels and sorting.
+constexpr int kW8 = 8;  // waves per workgroup of the 32-point-per-wave assign
+struct Km8Cfg {
+  static constexpr int D = 64, NKS = 4, XST = 72, NDT = 2, NW = kW8, TILE = 32 * kW8, NT = 64 * kW8;
+  static size_t lds_bytes(int Cmax) {
+    const size_t Cp = (Cmax + 31) & ~31;
+    return Cp * D * 2 * sizeof(uint16_t) + Cp * sizeof(float) + static_cast<size_t>(TILE) * XST * sizeof(uint16_t) +
+           TILE * sizeof(uint16_t) + sizeof(int) * (NW * Cmax + 2 * Cmax + TILE);
+  }
+};
+
+template <int NJT>
+__device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int last, unsigned char* smem) {
+  using Cfg = Km8Cfg;
+  constexpr int D = Cfg::D, NKS = Cfg::NKS, XST = Cfg::XST, NDT = Cfg::NDT, NW = Cfg::NW, TILE = Cfg::TILE,
+                NT = Cfg::NT;
+  constexpr int njt = NJT;  // centroid tiles of 32
+  const KmTensor& t = a.t[blockIdx.z];
+  const int C = t.C, Cp = 32 * NJT;
+  const int grp = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
+  if (grp >= t.ngroups) return;  // this tensor needs fewer workgroups
+  const int tt0 = grp * t.tpg, tt1 = min(a.ntiles, tt0 + t.tpg);
+  uint16_t* chi = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* clo = chi + Cp * D;
+  float* bias = reinterpret_cast<float*>(clo + Cp * D);
+  uint16_t* sX = reinterpret_cast<uint16_t*>(bias + Cp);
+  uint16_t* slab = sX + TILE * XST;
+  int* s_whist = reinterpret_cast<int*>(slab + TILE);
+  int* s_cnt = s_whist + NW * C;
+  int* s_start = s_cnt + C;
+  int* s_sorted = s_start + C;
+  const uint16_t* X = static_cast<const uint16_t*>(t.x) + static_cast<size_t>(bh) * a.N * D;
+  const float* cent = t.cent + static_cast<size_t>(bh) * C * D;
+  const int pw = 32 * wave + c;  // this lane's point within the tile
+  u16x8_t xf[NKS];
+  auto load_x = [&](int tt) {
+    const long p = static_cast<long>(tt) * TILE + pw;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      xf[ks] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      if (p < a.N) xf[ks] = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(p) * D + 16 * ks + 8 * h);
+    }
+  };
+  const bool score = t.labels_in == nullptr;
+  if (tt0 < tt1) load_x(tt0);  // the first tile's rows travel while the tables are staged
+
+  if (score) {
+    const uint16_t* ghi = t.chi + static_cast<size_t>(bh) * C * D;
+    const uint16_t* glo = t.clo + static_cast<size_t>(bh) * C * D;
+#pragma unroll
+    for (int e = tid; e < Cp * (D / 8); e += NT) {
+      const int j = e / (D / 8), c8 = e % (D / 8);
+      u16x8_t h8 = {0, 0, 0, 0, 0, 0, 0, 0}, l8 = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (j < C) {
+        h8 = *reinterpret_cast<const u16x8_t*>(ghi + static_cast<size_t>(j) * D + c8 * 8);
+        l8 = *reinterpret_cast<const u16x8_t*>(glo + static_cast<size_t>(j) * D + c8 * 8);
+      }
+      const int dst = j * D + ((c8 ^ (j & 7)) << 3);
+      *reinterpret_cast<u16x8_t*>(chi + dst) = h8;
+      *reinterpret_cast<u16x8_t*>(clo + dst) = l8;
+    }
+    // padding centroids: a finite score far below any real one (their rank keys must
+    // not be NaN)
+    for (int j = tid; j < Cp; j += NT) bias[j] = j < C ? -0.5f * t.cn2[static_cast<size_t>(bh) * C + j] : -1e30f;
+  }
+  __syncthreads();
+  float cmax2 = 0.f;
+  if (score) {
+    for (int j = lane; j < C; j += 64) cmax2 = fmaxf(cmax2, -2.f * bias[j]);
+    cmax2 = wave_max(cmax2);
+  }
+  const float cmax = sqrtf(cmax2);
+
+  // cluster sums: output ot = wave -> cluster tile ot / NDT, feature tile ot % NDT
+  const int ot = wave, oct = ot / NDT, odt = ot % NDT;
+  const bool owns = ot < njt * NDT;
+  f32x16_t acc = zero16();
+  uint32_t miss = 0u;  // packed per-half mismatch counts of the one-hot operand
+  int nks = 0;         // one-hot steps accumulated (8 labels per lane each)
+
+  // scores of centroid tile jt for this wave's group, accumulator preset to the bias
+  auto score_tile = [&](int jt, f32x16_t& s0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(bias + 32 * jt + 8 * q + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s0[4 * q + e] = b4[e];
+    }
+    const int jr = 32 * jt + c;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int off = jr * D + (((2 * ks + h) ^ (c & 7)) << 3);
+      const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const u16x8_t*>(chi + off));
+      const bf16x8_t al = as_bf16x8(*reinterpret_cast<const u16x8_t*>(clo + off));
+      s0 = mfma32(ah, as_bf16x8(xf[ks]), s0);
+      s0 = mfma32(al, as_bf16x8(xf[ks]), s0);
+    }
+  };
+
+  for (int tt = tt0; tt < tt1; ++tt) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<u16x8_t*>(sX + pw * XST + 16 * ks + 8 * h) = xf[ks];
+    const long n = static_cast<long>(tt) * TILE + pw;
+    const bool valid = h == 0 && n < a.N;  // the lanes h = 0 own the points
+    int lab = C;
+    if (!score) {
+      if (valid) lab = min(max(t.labels_in[static_cast<size_t>(bh) * a.N + n], 0), C - 1);
+    } else {
+      float xx;
+      {
+        float s2 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const u16x2 uu = {xf[ks][2 * e], xf[ks][2 * e + 1]};
+            const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, uu);
+            s2 = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, s2, false);
+          }
+        }
+        xx = s2 + xor32(s2);
+      }
+      // rank keys carry the lane-local slot 16 jt + v in their 6 low mantissa bits
+      const float kLow = -3.0e38f;
+      float best = kLow, second = kLow;
+      auto rkey = [](float x, int slot) {
+        return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & ~63u) | static_cast<uint32_t>(slot));
+      };
+      f32x16_t sa;
+      score_tile(0, sa);
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+        f32x16_t sb;
+        if (jt + 1 < NJT) score_tile(jt + 1, sb);
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float a0 = rkey(sa[v], 16 * jt + v), a1 = rkey(sa[v + 1], 16 * jt + v + 1);
+          second = fmaxf(second, __builtin_amdgcn_fmed3f(best, a0, a1));
+          best = fmaxf(best, fmaxf(a0, a1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (jt + 1 < NJT) sa = sb;
+      }
+      int bj;
+      bool need;
+      float E;
+      {
+        const int sl = static_cast<int>(__builtin_bit_cast(uint32_t, best) & 63u);
+        bj = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * h + (sl & 3);
+        const float ob = xor32(best);
+        const float os = xor32(second);
+        const int oj = xor32(bj);
+        if (ob > best || (ob == best && oj < bj)) {
+          second = best > os ? best : os;
+          best = ob;
+          bj = oj;
+        } else {
+          second = second > ob ? second : ob;
+        }
+        // distance error bound E; scores carry half of it
+        E = 1e-4f * sqrtf(xx) * cmax + 2e-5f * cmax2;
+        need = n < a.N && second >= best - E;
+      }
+      // a second centroid within the window: every candidate within it is re-scored with
+      // the fp32 direct form sum_d (x_d - c_jd)^2 (lanes over d, fixed-order tree sum),
+      // one (point, candidate) pair at a time; the smallest distance (then index) wins
+      if (__ballot(need) != 0ull) {
+        uint64_t cm = 0ull;  // candidate slots 16 jt + v of this lane
+        for (int jt = 0; jt < njt; ++jt) {
+          f32x16_t s0;
+          score_tile(jt, s0);
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (need && s0[v] >= best - E) cm |= 1ull << (16 * jt + v);
+        }
+        float fb = __builtin_huge_valf();
+        int fj = C;
+        uint64_t lanes = __ballot(cm != 0ull);
+        while (lanes != 0ull) {
+          const int L = __ffsll(static_cast<unsigned long long>(lanes)) - 1;
+          lanes &= lanes - 1;
+          const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(cm), L);
+          const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(cm >> 32), L);
+          uint64_t m = (static_cast<uint64_t>(hi) << 32) | lo;
+          const int cL = L & 31, hL = L >> 5;
+          const uint16_t* xr = sX + (32 * wave + cL) * XST;
+          while (m != 0ull) {
+            const int sl = __ffsll(static_cast<unsigned long long>(m)) - 1;
+            m &= m - 1;
+            const int j = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * hL + (sl & 3);
+            const float* cr = cent + static_cast<size_t>(j) * D;
+            const float diff = bf16_to_f32(xr[lane]) - cr[lane];
+            const float dist = wave_sum(diff * diff);
+            if (c == cL && (dist < fb || (dist == fb && j < fj))) {
+              fb = dist;
+              fj = j;
+            }
+          }
+        }
+        if (need && fj < C) bj = fj;
+      }
+      if (valid) lab = bj;
+    }
+    // the scores no longer need this tile's fragments: fetch the next tile's now
+    if (tt + 1 < tt1) load_x(tt + 1);
+    if (valid) {
+      t.labels[static_cast<size_t>(bh) * a.N + n] = lab;
+      if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
+    }
+    if (h == 0) slab[pw] = valid ? static_cast<uint16_t>(lab) : static_cast<uint16_t>(0xFFFF);
+    if (last) tile_sort(a, t, lab, valid, pw, tt, s_whist, s_cnt, s_start, s_sorted);
+    __syncthreads();  // X tile and labels complete
+
+    if (owns) {
+      const uint32_t jj = (32u * oct + c) * 0x10001u;
+      const uint32_t one2 = 0x00010001u, neg2 = 0xC080C080u, val2 = 0x3F803F80u;
+#pragma unroll 4
+      for (int ks = 0; ks < TILE / 16; ++ks) {
+        const u16x8_t lab8 = *reinterpret_cast<const u16x8_t*>(slab + 16 * ks + 8 * h);
+        const bf16x8_t ax = lds_operand_tr(sX, XST, 16 * ks, 32 * odt, lane);
+        const bf16x8_t oh = onehot_bf16x8(lab8, jj, one2, neg2, val2, miss);
+        acc = mfma32(ax, oh, acc);
+      }
+    }
+    nks += TILE / 16;
+    if (tt + 1 == tt1 && owns) {
+      // sums and counts of this group
+      float* psum = t.psum + (static_cast<size_t>(bh) * a.ntiles + grp) * C * D;
+      const int j = 32 * oct + c;
+      // lane (c, h) saw 8 nks labels against cluster j
+      const int hit = 8 * nks - static_cast<int>((miss & 0xFFFFu) + (miss >> 16));
+      const int cnt = hit + xor32(hit);
+      if (j < C) {
+        if (odt == 0 && h == 0) t.gcnt[(static_cast<size_t>(bh) * a.ntiles + grp) * C + j] = cnt;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t f = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+          *reinterpret_cast<f32x4_t*>(psum + static_cast<size_t>(j) * D + 32 * odt + 8 * q + 4 * h) = f;
+        }
+      }
+    }
+    __syncthreads();  // the next tile overwrites the X tile and labels
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(64 * kW8, 4) kmeans_assign_mfma8_kernel(KmArgs a, int iter, int last) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  switch ((a.t[blockIdx.z].C + 31) / 32) {
+    case 1: km_assign_body8<1>(a, iter, last, smem); break;
+    case 2: km_assign_body8<2>(a, iter, last, smem); break;
+    case 3: km_assign_body8<3>(a, iter, last, smem); break;
+    default: km_assign_body8<4>(a, iter, last, smem); break;
   }
 }
 
@@ -954,8 +1219,16 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
   b.ngroups = 0;
   for (int z = 0; z < a.ntensors; ++z) b.ngroups = std::max(b.ngroups, b.t[z].ngroups);
   const dim3 g_group(b.ngroups, a.BH, a.ntensors);
+  // D = 64 with 256-point tiles: the eight-wave variant (32 points per wave)
+  const bool w8 = a.D == 64 && a.tile == Km8Cfg::TILE;
   auto launch_mfma = [&](int it) {
     const int last = it == iters - 1;
+    if (w8) {
+      const size_t lds8 = Km8Cfg::lds_bytes(Cmax);
+      allow_lds((const void*)kmeans_assign_mfma8_kernel<64>, lds8);
+      hipLaunchKernelGGL((kmeans_assign_mfma8_kernel<64>), g_group, dim3(Km8Cfg::NT), lds8, s, b, it, last);
+      return;
+    }
 #define MUSE_KM_CASE(DD, NN)                                                                              \
   if (a.D == DD && nw == NN) {                                                                            \
     allow_lds((const void*)kmeans_assign_mfma_kernel<DD, NN>, lds_mfma);                                 \
