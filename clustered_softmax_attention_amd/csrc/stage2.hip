@@ -146,9 +146,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
   const int u = tile.x, b = u / a.Cq, i = u % a.Cq;
   const int32_t* offs = a.offs_q + static_cast<size_t>(bh) * (a.nb * a.Cq + 1);
   const int st = tile.y + 32 * wave;
+  // the permutation entry is requested beside the bucket end, not after it (past the
+  // bucket it is a neighbour's entry, which no lane uses): one dependent round trip fewer
+  const int qn = a.perm_q[static_cast<size_t>(bh) * a.N + min(st + c, a.N - 1)];
   const int nw = max(0, min(32, offs[u + 1] - st));  // queries of this wave
   const bool valid = c < nw;
-  const int qn = a.perm_q[static_cast<size_t>(bh) * a.N + (valid ? st + c : tile.y)];
   const size_t row = static_cast<size_t>(bh) * a.N + qn;
   if (a.causal && b == 0) {  // the first block has no far field
     if (valid) {
@@ -192,26 +194,37 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
     plz = (tid < JC && j0 + tid < Ck) ? lz[j0 + tid] : kNegInf;
   };
   load_chunk(0);
+  u16x8_t pd[ND];
+  const uint16_t* dip = a.t_dip + sidx * D * D;
   if (a.dipole) {
-    const uint16_t* dip = a.t_dip + sidx * D * D;
 #pragma unroll
     for (int q = 0; q < ND; ++q) {
       const int x = tid + 256 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
-      *reinterpret_cast<u16x8_t*>(sDip + r * DST + c8) = *reinterpret_cast<const u16x8_t*>(dip + static_cast<size_t>(r) * D + c8);
+      pd[q] = *reinterpret_cast<const u16x8_t*>(dip + static_cast<size_t>(r) * D + c8);
     }
   }
 
-  // residual query fragments (B operand: column = query c, k = d)
+  // residual query fragments (B operand: column = query c, k = d); the rows are requested
+  // before any of the loads above is waited for
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const float* qb = a.qbar + (static_cast<size_t>(bh) * a.Cq + i) * D;
+  u16x8_t qr[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qr[ks] = *reinterpret_cast<const u16x8_t*>(Q + row * D + 16 * ks + 8 * h);
+  if (a.dipole) {
+#pragma unroll
+    for (int q = 0; q < ND; ++q) {
+      const int x = tid + 256 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
+      *reinterpret_cast<u16x8_t*>(sDip + r * DST + c8) = pd[q];
+    }
+  }
   bf16x8_t qhi[NKS], qlo[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int d0 = 16 * ks + 8 * h;
-    const u16x8_t u8 = *reinterpret_cast<const u16x8_t*>(Q + row * D + d0);
     float x[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) x[r] = valid ? bf16_to_f32(u8[r]) - qb[d0 + r] : 0.f;
+    for (int r = 0; r < 8; ++r) x[r] = valid ? bf16_to_f32(qr[ks][r]) - qb[d0 + r] : 0.f;
     split_bf16x8(x, qhi[ks], qlo[ks]);
   }
 
