@@ -661,15 +661,21 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
   }
 }
 
-// Matrix-core assign for bf16 inputs with D = 64, eight waves of 32 points each over
-// 256-point tiles. Same method as km_assign_body; each wave now scores one 32-point
-// group (half the registers), so that two workgroups of eight waves share a compute
-// unit (four waves per SIMD to hide latency). The cluster sums are split over
-// (cluster tile, feature tile) outputs, one per wave. Lane (c, h) of wave w holds point
-// 32 w + c (features 16 ks + 8 h); the lanes h = 0 own the points for labels and sorting.
+// Matrix-core assign for bf16 inputs over 256-point tiles, eight waves of 32 points
+// each. Same method as km_assign_body; each wave scores one 32-point group (half the
+// registers of the 64-point waves), so that more waves share a SIMD to hide latency:
+// two workgroups per compute unit (four waves per SIMD) with D = 64, one (two waves per
+// SIMD) with D = 128, whose centroid tables fill most of the LDS. The cluster sums are
+// split over (cluster tile, feature tile) outputs: the two waves 2 t, 2 t + 1 of cluster
+// tile t take half of its D / 32 feature tiles each, under one one-hot operand. Lane
+// (c, h) of wave w holds point 32 w + c (features 16 ks + 8 h); the lanes h = 0 own the
+// points for labels and sorting.
 constexpr int kW8 = 8;  // waves per workgroup of the 32-point-per-wave assign
+template <int D>
 struct Km8Cfg {
-  static constexpr int D = 64, NKS = 4, XST = 72, NDT = 2, NW = kW8, TILE = 32 * kW8, NT = 64 * kW8;
+  static constexpr int NKS = D / 16, XST = D == 64 ? D + 8 : D + 16, NDT = D / 32, NW = kW8, TILE = 32 * kW8,
+                       NT = 64 * kW8;
+  static constexpr int OPW = NDT / 2;  // cluster-sum outputs (feature tiles) per wave
   static size_t lds_bytes(int Cmax) {
     const size_t Cp = (Cmax + 31) & ~31;
     return Cp * D * 2 * sizeof(uint16_t) + Cp * sizeof(float) + static_cast<size_t>(TILE) * XST * sizeof(uint16_t) +
@@ -677,11 +683,10 @@ struct Km8Cfg {
   }
 };
 
-template <int NJT>
+template <int D, int NJT>
 __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int last, unsigned char* smem) {
-  using Cfg = Km8Cfg;
-  constexpr int D = Cfg::D, NKS = Cfg::NKS, XST = Cfg::XST, NDT = Cfg::NDT, NW = Cfg::NW, TILE = Cfg::TILE,
-                NT = Cfg::NT;
+  using Cfg = Km8Cfg<D>;
+  constexpr int NKS = Cfg::NKS, XST = Cfg::XST, NW = Cfg::NW, TILE = Cfg::TILE, NT = Cfg::NT, OPW = Cfg::OPW;
   constexpr int njt = NJT;  // centroid tiles of 32
   const KmTensor& t = a.t[blockIdx.z];
   const int C = t.C, Cp = 32 * NJT;
@@ -740,10 +745,12 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
   }
   const float cmax = sqrtf(cmax2);
 
-  // cluster sums: output ot = wave -> cluster tile ot / NDT, feature tile ot % NDT
-  const int ot = wave, oct = ot / NDT, odt = ot % NDT;
-  const bool owns = ot < njt * NDT;
-  f32x16_t acc = zero16();
+  // cluster sums: wave -> cluster tile wave / 2, feature tiles odt0 .. odt0 + OPW - 1
+  const int oct = wave / 2, odt0 = (wave % 2) * OPW;
+  const bool owns = oct < njt;
+  f32x16_t acc[OPW];
+#pragma unroll
+  for (int r = 0; r < OPW; ++r) acc[r] = zero16();
   uint32_t miss = 0u;  // packed per-half mismatch counts of the one-hot operand
   int nks = 0;         // one-hot steps accumulated (8 labels per lane each)
 
@@ -860,8 +867,13 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
             m &= m - 1;
             const int j = 32 * (sl >> 4) + 8 * ((sl >> 2) & 3) + 4 * hL + (sl & 3);
             const float* cr = cent + static_cast<size_t>(j) * D;
-            const float diff = bf16_to_f32(xr[lane]) - cr[lane];
-            const float dist = wave_sum(diff * diff);
+            float part = 0.f;
+#pragma unroll
+            for (int d = lane; d < D; d += 64) {
+              const float diff = bf16_to_f32(xr[d]) - cr[d];
+              part = fmaf(diff, diff, part);
+            }
+            const float dist = wave_sum(part);
             if (c == cL && (dist < fb || (dist == fb && j < fj))) {
               fb = dist;
               fj = j;
@@ -888,9 +900,12 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
 #pragma unroll 4
       for (int ks = 0; ks < TILE / 16; ++ks) {
         const u16x8_t lab8 = *reinterpret_cast<const u16x8_t*>(slab + 16 * ks + 8 * h);
-        const bf16x8_t ax = lds_operand_tr(sX, XST, 16 * ks, 32 * odt, lane);
+        bf16x8_t ax[OPW];  // requested before the one-hot is built
+#pragma unroll
+        for (int r = 0; r < OPW; ++r) ax[r] = lds_operand_tr(sX, XST, 16 * ks, 32 * (odt0 + r), lane);
         const bf16x8_t oh = onehot_bf16x8(lab8, jj, one2, neg2, val2, miss);
-        acc = mfma32(ax, oh, acc);
+#pragma unroll
+        for (int r = 0; r < OPW; ++r) acc[r] = mfma32(ax[r], oh, acc[r]);
       }
     }
     nks += TILE / 16;
@@ -902,12 +917,14 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
       const int hit = 8 * nks - static_cast<int>((miss & 0xFFFFu) + (miss >> 16));
       const int cnt = hit + xor32(hit);
       if (j < C) {
-        if (odt == 0 && h == 0) t.gcnt[(static_cast<size_t>(bh) * a.ntiles + grp) * C + j] = cnt;
+        if (odt0 == 0 && h == 0) t.gcnt[(static_cast<size_t>(bh) * a.ntiles + grp) * C + j] = cnt;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4_t f = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-          *reinterpret_cast<f32x4_t*>(psum + static_cast<size_t>(j) * D + 32 * odt + 8 * q + 4 * h) = f;
-        }
+        for (int r = 0; r < OPW; ++r)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t f = {acc[r][4 * q], acc[r][4 * q + 1], acc[r][4 * q + 2], acc[r][4 * q + 3]};
+            *reinterpret_cast<f32x4_t*>(psum + static_cast<size_t>(j) * D + 32 * (odt0 + r) + 8 * q + 4 * h) = f;
+          }
       }
     }
     __syncthreads();  // the next tile overwrites the X tile and labels
@@ -915,13 +932,13 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
 }
 
 template <int D>
-__global__ void __launch_bounds__(64 * kW8, 4) kmeans_assign_mfma8_kernel(KmArgs a, int iter, int last) {
+__global__ void __launch_bounds__(64 * kW8, D == 64 ? 4 : 2) kmeans_assign_mfma8_kernel(KmArgs a, int iter, int last) {
   extern __shared__ __align__(16) unsigned char smem[];
   switch ((a.t[blockIdx.z].C + 31) / 32) {
-    case 1: km_assign_body8<1>(a, iter, last, smem); break;
-    case 2: km_assign_body8<2>(a, iter, last, smem); break;
-    case 3: km_assign_body8<3>(a, iter, last, smem); break;
-    default: km_assign_body8<4>(a, iter, last, smem); break;
+    case 1: km_assign_body8<D, 1>(a, iter, last, smem); break;
+    case 2: km_assign_body8<D, 2>(a, iter, last, smem); break;
+    case 3: km_assign_body8<D, 3>(a, iter, last, smem); break;
+    default: km_assign_body8<D, 4>(a, iter, last, smem); break;
   }
 }
 
@@ -1219,14 +1236,20 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
   b.ngroups = 0;
   for (int z = 0; z < a.ntensors; ++z) b.ngroups = std::max(b.ngroups, b.t[z].ngroups);
   const dim3 g_group(b.ngroups, a.BH, a.ntensors);
-  // D = 64 with 256-point tiles: the eight-wave variant (32 points per wave)
-  const bool w8 = a.D == 64 && a.tile == Km8Cfg::TILE;
+  // 256-point tiles: the eight-wave variant (32 points per wave)
+  const bool w8 = a.tile == Km8Cfg<64>::TILE;
   auto launch_mfma = [&](int it) {
     const int last = it == iters - 1;
-    if (w8) {
-      const size_t lds8 = Km8Cfg::lds_bytes(Cmax);
+    if (w8 && a.D == 64) {
+      const size_t lds8 = Km8Cfg<64>::lds_bytes(Cmax);
       allow_lds((const void*)kmeans_assign_mfma8_kernel<64>, lds8);
-      hipLaunchKernelGGL((kmeans_assign_mfma8_kernel<64>), g_group, dim3(Km8Cfg::NT), lds8, s, b, it, last);
+      hipLaunchKernelGGL((kmeans_assign_mfma8_kernel<64>), g_group, dim3(Km8Cfg<64>::NT), lds8, s, b, it, last);
+      return;
+    }
+    if (w8) {
+      const size_t lds8 = Km8Cfg<128>::lds_bytes(Cmax);
+      allow_lds((const void*)kmeans_assign_mfma8_kernel<128>, lds8);
+      hipLaunchKernelGGL((kmeans_assign_mfma8_kernel<128>), g_group, dim3(Km8Cfg<128>::NT), lds8, s, b, it, last);
       return;
     }
 #define MUSE_KM_CASE(DD, NN)                                                                              \

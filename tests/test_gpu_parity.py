@@ -25,7 +25,7 @@ def test_acausal_1k_f32_full(muse_lib):
 
 @pytest.mark.parametrize("N", [1000, 1536])
 def test_acausal_bf16_ragged(muse_lib, N):
-    # several 512-point K-means tiles plus a ragged tail (N=1000)
+    # several 256-point K-means tiles plus a ragged tail (N=1000)
     cfg = scaled_config("acausal_8k", B=1, H=2, N=N)
     check_config(cfg, [(0, 0), (0, 1)])
 
@@ -38,6 +38,17 @@ def test_bf16_odd_cluster_counts_long_buckets(muse_lib, causal):
         cfg = scaled_config("causal_16k", B=1, H=2, N=3072, block=1024, Cq=12, Ck=20)
     else:
         cfg = scaled_config("acausal_8k", B=1, H=2, N=3000, Cq=20, Ck=40)
+    check_config(cfg, [(0, 0), (0, 1)])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_d128_odd_cluster_counts(muse_lib, causal):
+    # D = 128: cluster counts off the 32-centroid tiles (one to three tiles of them, so
+    # that some cluster-sum waves own no output) and a ragged tail
+    if causal:
+        cfg = scaled_config("causal_64k_d128", B=1, H=2, N=3072, block=1024, Cq=12, Ck=40)
+    else:
+        cfg = scaled_config("causal_64k_d128", B=1, H=2, N=3000, causal=False, block=0, Cq=20, Ck=72)
     check_config(cfg, [(0, 0), (0, 1)])
 
 
