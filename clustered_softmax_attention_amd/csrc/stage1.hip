@@ -20,6 +20,8 @@
 //   s1_prefix     fold of atoms over blocks -> log Z, K, V tables.
 //   s1_mom_prefix fold of block moments over blocks -> E_i[v k^T] per table entry.
 //   s1_dip_final  D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T (value index first).
+#include <mutex>
+
 #include "mfma.hpp"
 #include "muse_kernels.hpp"
 
@@ -377,16 +379,48 @@ __global__ void __launch_bounds__(256) s1_pack_kernel(S1Args a) {
   }
 }
 
+// A second stream per device (default priority, created on first use and kept until the
+// process ends) on which the atoms run beside the scores and the block moments: the
+// atoms read only the clustering, the moments read the scores, and the tables need both.
+static hipStream_t side_stream() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static hipStream_t streams[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (streams[dev] == nullptr) {
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    streams[dev] = st;
+  }
+  return streams[dev];
+}
+
 template <typename T, int D>
 static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   constexpr int kS1Keys = S1Keys<D>::value;
   const bool mf = sizeof(T) == 2;  // bf16 inputs: matrix-core kernels
   if (mf && a.retr == nullptr) {
     // acausal: one table entry per (head, i), finalised in a single pass; causal without
-    // retrieval: one scan over the blocks writes every entry
+    // retrieval: one scan over the blocks writes every entry. The atoms (with their
+    // merge) go to the side stream, forked from and joined back into the caller's stream
+    // by events; without a side stream or events everything runs on the caller's stream.
+    hipStream_t side = side_stream();
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool two = side != nullptr && hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
+               hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess &&
+               hipEventRecord(fork, s) == hipSuccess && hipStreamWaitEvent(side, fork, 0) == hipSuccess;
+    launch_stage1_mfma(a, 1, two ? side : s);
+    if (two && hipEventRecord(join, side) != hipSuccess) {
+      (void)hipStreamSynchronize(side);  // the join cannot be enqueued: wait on the host
+      two = false;
+    }
     launch_stage1_mfma(a, 0, s);
-    launch_stage1_mfma(a, 1, s);
     if (a.dipole) launch_stage1_mfma(a, 2, s);
+    if (two && hipStreamWaitEvent(s, join, 0) != hipSuccess) (void)hipStreamSynchronize(side);
+    if (fork != nullptr) (void)hipEventDestroy(fork);
+    if (join != nullptr) (void)hipEventDestroy(join);
     launch_stage1_mfma(a, a.causal ? 4 : 3, s);
     return;
   }
