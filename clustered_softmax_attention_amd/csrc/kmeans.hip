@@ -957,10 +957,12 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
 
 // One wave per (centroid j, head, tensor), lanes over d: sum the tile-group partials in
 // group order; the mean replaces c_j unless the cluster is empty.
+constexpr int kUpdWaves = 8;  // centroids (one per wave) per update workgroup
+
 template <int D>
-__global__ void __launch_bounds__(64) kmeans_update_kernel(KmArgs a) {
+__global__ void __launch_bounds__(64 * kUpdWaves) kmeans_update_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
-  const int C = t.C, j = blockIdx.x, bh = blockIdx.y;
+  const int C = t.C, j = blockIdx.x * kUpdWaves + (threadIdx.x >> 6), bh = blockIdx.y;
   if (j >= C) return;
   const size_t tbase = static_cast<size_t>(bh) * a.ntiles;
   constexpr int nper = D / 64;
@@ -1179,7 +1181,7 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
   const size_t lds = static_cast<size_t>(kChunkC) * a.D * sizeof(float) +
                      sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax);
   const dim3 g_assign(a.ntiles, a.BH, a.ntensors);
-  const dim3 g_update(Cmax, a.BH, a.ntensors);
+  const dim3 g_update((Cmax + kUpdWaves - 1) / kUpdWaves, a.BH, a.ntensors);
   const bool mf = sizeof(T) == 2;
   const int nw = a.tile / 64;
   KmArgs b = a;
@@ -1274,8 +1276,8 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
     }
     {
       ProfScope ps_("kmeans_update", s);
-      if (a.D == 64) hipLaunchKernelGGL(kmeans_update_kernel<64>, g_update, dim3(64), 0, s, b);
-      else hipLaunchKernelGGL(kmeans_update_kernel<128>, g_update, dim3(64), 0, s, b);
+      if (a.D == 64) hipLaunchKernelGGL(kmeans_update_kernel<64>, g_update, dim3(64 * kUpdWaves), 0, s, b);
+      else hipLaunchKernelGGL(kmeans_update_kernel<128>, g_update, dim3(64 * kUpdWaves), 0, s, b);
     }
   }
   {
