@@ -321,6 +321,30 @@ def measure(name: str, steps: int, warmup: int, exact: bool) -> dict:
         extra = {"exact_ms_per_step": ms_ex, "speedup_vs_exact": ms_ex / ms, "rse_vs_exact": rse}
         print(f"# exact {ms_ex:.3f} ms/step, MuSe {ms:.3f} ms/step, speedup {ms_ex / ms:.2f}x, RSE {rse:.3e}",
               file=sys.stderr, flush=True)
+        if not cfg.causal:
+            # the same workload with the untilted (per key cluster) dipole
+            ws_u = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, False, 0,
+                                                       1 if cfg.dtype == "bf16" else 0, dipole="untilted"),
+                               dtype=torch.uint8, device="cuda")
+
+            def untilted_step():
+                binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, out=out, dipole="untilted", workspace=ws_u)
+
+            ms_u, _ = timed(untilted_step, steps, warmup)
+            binding.prof_reset()
+            binding.prof_enable(True)
+            untilted_step()
+            torch.cuda.synchronize()
+            prof_u = binding.prof_collect()
+            binding.prof_enable(False)
+            o_u = out.double()
+            rse_u = float(((o_u - o_e) ** 2).sum() / (o_e ** 2).sum())
+            extra["untilted_dipole"] = {
+                "ms_per_step": ms_u, "value": cfg.B * cfg.N / (ms_u / 1e3), "speedup_vs_exact": ms_ex / ms_u,
+                "rse_vs_exact": rse_u,
+                "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in prof_u.items() if "untilted" in n or "cov" in n}}
+            print(f"# untilted dipole: {ms_u:.3f} ms/step, speedup {ms_ex / ms_u:.2f}x, RSE {rse_u:.3e}, "
+                  f"{extra['untilted_dipole']['kernels_us']}", file=sys.stderr, flush=True)
     return {"cfg": cfg, "ms": ms, "wall": wall, "value": value, "kernels": kernels, "roofline": roofline,
             "extra": extra, "host_inputs": (q, k, v)}
 

@@ -135,8 +135,23 @@ def exact_attn_fwd(q, k, v, causal: bool = False, out: Optional[torch.Tensor] = 
     return out
 
 
+DIPOLE_MODES = {"none": 0, "tilted": 1, "untilted": 2}  # MUSE_DIPOLE_* of include/muse.h
+
+
+def dipole_code(dipole) -> int:
+    """MUSE_DIPOLE_* code of a dipole argument: True (tilted), False (none), a name of
+    DIPOLE_MODES, or the code itself."""
+    if isinstance(dipole, bool):
+        return 1 if dipole else 0
+    if isinstance(dipole, str):
+        if dipole not in DIPOLE_MODES:
+            raise ValueError(f"unknown dipole mode {dipole!r}")
+        return DIPOLE_MODES[dipole]
+    return int(dipole)
+
+
 def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False, block: int = 0,
-             out: Optional[torch.Tensor] = None, *, scale: float = 0.0, out_dtype=None, dipole: bool = True,
+             out: Optional[torch.Tensor] = None, *, scale: float = 0.0, out_dtype=None, dipole=True,
              topk_clusters: int = 0, topk_blocks: int = 0, labels_q_in=None, labels_k_in=None,
              return_trace: bool = False, return_centroids: bool = False, return_lse: bool = False,
              workspace: Optional[torch.Tensor] = None):
@@ -156,7 +171,7 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
     lib.muse_fwd_params_init(ctypes.byref(p))
     p.scale = float(scale)
     p.out_dtype = _dtype_code(out)
-    p.dipole = 1 if dipole else 0
+    p.dipole = dipole_code(dipole)
     p.topk_clusters = int(topk_clusters)
     p.topk_blocks = int(topk_blocks)
     extras = {}
@@ -210,11 +225,12 @@ def prof_collect() -> dict:
 
 
 def workspace_bytes(B, H, N, D, Cq, Ck, causal=False, block=0, dtype=MUSE_BF16, topk_clusters=0,
-                    topk_blocks=0) -> int:
+                    topk_blocks=0, dipole=True) -> int:
     lib = load()
     p = FwdParams()
     lib.muse_fwd_params_init(ctypes.byref(p))
     p.topk_clusters, p.topk_blocks = topk_clusters, topk_blocks
+    p.dipole = dipole_code(dipole)
     n = lib.muse_attn_fwd_workspace_bytes(B, H, N, D, Cq, Ck, int(causal), int(block), dtype, ctypes.byref(p))
     if n == 0:
         raise MuseError(-1, lib.muse_last_error().decode())

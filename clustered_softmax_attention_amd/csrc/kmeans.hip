@@ -56,11 +56,13 @@ __device__ __forceinline__ void write_centroid_tables(const KmTensor& t, int D, 
   if (t.cn2 != nullptr && lane_id() == 0) t.cn2[row] = n2;
 }
 
+constexpr int kUpdWaves = 8;  // centroids (one per wave) per init and update workgroup
+
 // One wave per (centroid j, head, tensor): c_j = x[floor(j*N/C)].
 template <typename T>
-__global__ void __launch_bounds__(64) kmeans_init_kernel(KmArgs a) {
+__global__ void __launch_bounds__(64 * kUpdWaves) kmeans_init_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
-  const int j = blockIdx.x, bh = blockIdx.y;
+  const int j = blockIdx.x * kUpdWaves + (threadIdx.x >> 6), bh = blockIdx.y;
   if (t.labels_in != nullptr || j >= t.C) return;
   const T* x = static_cast<const T*>(t.x) + static_cast<size_t>(bh) * a.N * a.D;
   const long src = (static_cast<long>(j) * a.N) / t.C;
@@ -957,8 +959,6 @@ __global__ void __launch_bounds__(64 * NW, D == 64 && NW == 4 ? 2 : 1) kmeans_as
 
 // One wave per (centroid j, head, tensor), lanes over d: sum the tile-group partials in
 // group order; the mean replaces c_j unless the cluster is empty.
-constexpr int kUpdWaves = 8;  // centroids (one per wave) per update workgroup
-
 template <int D>
 __global__ void __launch_bounds__(64 * kUpdWaves) kmeans_update_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
@@ -1176,7 +1176,8 @@ static hipError_t launch_kmeans_t(const KmArgs& a, int iters, hipStream_t s) {
   const int Cmax = max(a.t[0].C, a.ntensors > 1 ? a.t[1].C : 0);
   {
     ProfScope ps_("kmeans_init", s);
-    hipLaunchKernelGGL(kmeans_init_kernel<T>, dim3(Cmax, a.BH, a.ntensors), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(kmeans_init_kernel<T>, dim3((Cmax + kUpdWaves - 1) / kUpdWaves, a.BH, a.ntensors),
+                       dim3(64 * kUpdWaves), 0, s, a);
   }
   const size_t lds = static_cast<size_t>(kChunkC) * a.D * sizeof(float) +
                      sizeof(int) * (2 * a.tile + (a.tile / 64) * Cmax + 2 * Cmax);

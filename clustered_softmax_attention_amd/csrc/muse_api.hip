@@ -102,8 +102,10 @@ int validate(Shape& s, const muse_fwd_params* p) {
   if (p != nullptr) {
     if (p->out_dtype != -1 && p->out_dtype != MUSE_F32 && p->out_dtype != MUSE_BF16)
       return fail(MUSE_ERR_INVALID_ARG, "out_dtype %d invalid", p->out_dtype);
-    if (p->dipole != MUSE_DIPOLE_NONE && p->dipole != MUSE_DIPOLE_TILTED)
+    if (p->dipole != MUSE_DIPOLE_NONE && p->dipole != MUSE_DIPOLE_TILTED && p->dipole != MUSE_DIPOLE_UNTILTED)
       return fail(MUSE_ERR_INVALID_ARG, "dipole mode %d invalid", p->dipole);
+    if (p->dipole == MUSE_DIPOLE_UNTILTED && s.causal)
+      return fail(MUSE_ERR_UNSUPPORTED, "the untilted dipole is implemented for acausal calls only");
     if (p->topk_clusters < 0 || p->topk_blocks < 0) return fail(MUSE_ERR_INVALID_ARG, "retrieval top-k must be >= 0");
     if (p->topk_clusters > 0 && !s.causal) return fail(MUSE_ERR_INVALID_ARG, "retrieval requires causal=1");
     if (p->topk_clusters > 0 && p->topk_blocks < 1) return fail(MUSE_ERR_INVALID_ARG, "retrieval needs topk_blocks >= 1");
@@ -134,7 +136,7 @@ struct Plan {
   size_t items_k, multi_k, bmeta_k, pt_m, pt_z, pt_k, pt_v;
   size_t t_khi, t_klo, t_vhi, t_vlo, t_dip, tiles, ntiles;
   int max_tiles;
-  size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores, tmax;
+  size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores, tmax, cov_k;
   size_t s_logz, s_k, s_v, s_dip;
   size_t o_far, l_far, retr_sel;
   size_t total;
@@ -193,6 +195,7 @@ Plan make_plan(const Shape& s, const muse_fwd_params* p) {
   P.tmax = s.dtype == MUSE_BF16 ? L.take(BH * Cq * ((N + 31) / 32) * f) : 0;
   P.blk_lmass = L.take(BH * static_cast<size_t>(s.nmb) * Cq * f);
   P.blk_mom = L.take(BH * static_cast<size_t>(s.nmb) * Cq * D * D * f);
+  P.cov_k = (p != nullptr && p->dipole == MUSE_DIPOLE_UNTILTED) ? L.take(BH * static_cast<size_t>(Ck) * D * D * f) : 0;
   P.s_logz = L.take(BH * nbS * Cq * Ck * f);
   P.s_k = L.take(BH * nbS * Cq * Ck * D * f);
   P.s_v = L.take(BH * nbS * Cq * Ck * D * f);
@@ -333,6 +336,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.mbk = s.mbk;
   a1.blk_lmass = at<float>(ws, P.blk_lmass);
   a1.blk_mom = at<float>(ws, P.blk_mom);
+  a1.cov_k = dipole == MUSE_DIPOLE_UNTILTED ? at<float>(ws, P.cov_k) : nullptr;
   a1.s_logz = at<float>(ws, P.s_logz);
   a1.s_k = at<float>(ws, P.s_k);
   a1.s_v = at<float>(ws, P.s_v);

@@ -109,7 +109,7 @@ struct S1Args {
   int causal;                  // table entry b holds blocks < b (causal) or all keys (acausal)
   int nbS;                     // table entries: nb when causal, 1 when acausal
   float scale;
-  int dipole;
+  int dipole;                  // 0 none, 1 tilted, 2 untilted (acausal only)
   const float* qbar;           // [BH, Cq, D] query centroids
   const int32_t* perm_k;       // [BH, N] keys by (block, label)
   const int32_t* offs_k;       // [BH, nb*Ck + 1]
@@ -143,6 +143,7 @@ struct S1Args {
   uint16_t* t_vlo;
   uint16_t* t_dip;             // [BH, nbS, Cq, D(v), D(k)]  s * D_i, value index first
   const RetrArgs* retr;        // retrieval: rewrites table entries before the dipole finalise
+  float* cov_k;                // [BH, Ck, D(v), D(k)] untilted dipole: per key cluster covariance
 };
 
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);

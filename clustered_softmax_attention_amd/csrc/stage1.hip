@@ -379,6 +379,198 @@ __global__ void __launch_bounds__(256) s1_pack_kernel(S1Args a) {
   }
 }
 
+// Untilted dipole, acausal (the paper's partially specialised dipole: the tilted C_ij
+// replaced by the plain within-cluster covariance of key cluster j; gist.science
+// Kernmechanismen 2 and the pith.science referee's note on the covariance of Algorithm 3):
+//   Cov_j = (1/n_j) sum_{m in S_j} (v_m - vbar_j)(k_m - kbar_j)^T   (value index first),
+// one workgroup per (cluster j, head), two passes over the cluster's keys (means, then
+// centred products; every sum in key order). Keys are staged KC at a time in LDS as
+// fp32 (four threads per row, each with one permutation entry and 16-byte loads); a
+// cluster of at most KC keys is staged once for both passes. Thread (tr, tc) holds
+// rows TD tr .. TD tr + TD - 1 and columns TD tc .. TD tc + TD - 1 (TD = D / 16).
+template <typename T>
+__device__ __forceinline__ void load8_f32(const T* p, float* out);
+template <>
+__device__ __forceinline__ void load8_f32<bf16>(const bf16* p, float* out) {
+  const u16x8_t u = *reinterpret_cast<const u16x8_t*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = bf16_to_f32(u[e]);
+}
+template <>
+__device__ __forceinline__ void load8_f32<float>(const float* p, float* out) {
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p), b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    out[e] = a[e];
+    out[4 + e] = b[e];
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) s1_cluster_cov_kernel(S1Args a) {
+  constexpr int TD = D / 16, KC = 64, EPT = D / 4, SST = D + 4;  // EPT: staged elements per thread
+  __shared__ __align__(16) float sk[KC * SST];
+  __shared__ __align__(16) float sv[KC * SST];
+  __shared__ float smk[D], smv[D];
+  const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
+  const int32_t* offs = a.offs_k + static_cast<size_t>(bh) * (a.nb * a.Ck + 1);
+  const int m0 = offs[j], m1 = offs[j + 1], n = m1 - m0;
+  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
+  const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+  const int sr = tid / 4, sc = (tid % 4) * EPT;  // staged row and first column of this thread
+  auto stage = [&](int c0) {  // keys c0 .. c0 + KC - 1 of the cluster (zeros past its end)
+    float kf[EPT], vf[EPT];
+    const int m = c0 + sr;
+    if (m < m1) {
+      const size_t row = static_cast<size_t>(perm[m]) * D + sc;
+#pragma unroll
+      for (int q = 0; q < EPT / 8; ++q) {
+        load8_f32<T>(K + row + 8 * q, kf + 8 * q);
+        load8_f32<T>(V + row + 8 * q, vf + 8 * q);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) kf[e] = vf[e] = 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < EPT / 4; ++q) {
+      *reinterpret_cast<f32x4_t*>(sk + sr * SST + sc + 4 * q) = f32x4_t{kf[4 * q], kf[4 * q + 1], kf[4 * q + 2], kf[4 * q + 3]};
+      *reinterpret_cast<f32x4_t*>(sv + sr * SST + sc + 4 * q) = f32x4_t{vf[4 * q], vf[4 * q + 1], vf[4 * q + 2], vf[4 * q + 3]};
+    }
+  };
+  const bool once = n <= KC;  // the staged chunk serves both passes
+  // pass 1: means (thread d < D sums k, D <= thread < 2D sums v)
+  float sum = 0.f;
+  for (int c0 = m0; c0 < m1; c0 += KC) {
+    __syncthreads();
+    stage(c0);
+    __syncthreads();
+    const int nk = min(KC, m1 - c0);
+    if (tid < 2 * D) {
+      const float* col = tid < D ? sk + tid : sv + (tid - D);
+#pragma unroll 8
+      for (int r = 0; r < nk; ++r) sum += col[r * SST];
+    }
+  }
+  if (tid < D) smk[tid] = n > 0 ? sum / static_cast<float>(n) : 0.f;
+  else if (tid < 2 * D) smv[tid - D] = n > 0 ? sum / static_cast<float>(n) : 0.f;
+  __syncthreads();
+  float mk[TD], mv[TD];
+#pragma unroll
+  for (int x = 0; x < TD; ++x) {
+    mv[x] = smv[TD * tr + x];
+    mk[x] = smk[TD * tc + x];
+  }
+  // pass 2: centred products
+  float acc[TD][TD];
+#pragma unroll
+  for (int x = 0; x < TD; ++x)
+#pragma unroll
+    for (int y = 0; y < TD; ++y) acc[x][y] = 0.f;
+  for (int c0 = m0; c0 < m1; c0 += KC) {
+    if (!once) {
+      __syncthreads();
+      stage(c0);
+      __syncthreads();
+    }
+    const int nk = min(KC, m1 - c0);
+#pragma unroll 4
+    for (int r = 0; r < nk; ++r) {
+      float vr[TD], kr[TD];
+#pragma unroll
+      for (int x = 0; x < TD; ++x) {
+        vr[x] = sv[r * SST + TD * tr + x] - mv[x];
+        kr[x] = sk[r * SST + TD * tc + x] - mk[x];
+      }
+#pragma unroll
+      for (int x = 0; x < TD; ++x)
+#pragma unroll
+        for (int y = 0; y < TD; ++y) acc[x][y] = fmaf(vr[x], kr[y], acc[x][y]);
+    }
+  }
+  const float inv = n > 0 ? 1.f / static_cast<float>(n) : 0.f;
+  float* cov = a.cov_k + (static_cast<size_t>(bh) * a.Ck + j) * D * D;
+#pragma unroll
+  for (int x = 0; x < TD; ++x)
+#pragma unroll
+    for (int y = 0; y < TD; y += 4) {
+      const f32x4_t f = {acc[x][y] * inv, acc[x][y + 1] * inv, acc[x][y + 2] * inv, acc[x][y + 3] * inv};
+      *reinterpret_cast<f32x4_t*>(cov + static_cast<size_t>(TD * tr + x) * D + TD * tc + y) = f;
+    }
+}
+
+// Untilted dipole, acausal: D_i = sum_j P_ij Cov_j with P_ij = softmax_j(log Z_ij) from the
+// finalised log Z table, for all query clusters of a head: one workgroup per (256
+// elements of D x D, head), a thread per element, query clusters in groups of 32 (their
+// P rows in LDS, zero past Ck), the covariances of eight clusters requested at a time,
+// sums over j in cluster order. Writes s * D_i in bf16 (matrix-core stage 2) or D_i in
+// fp32.
+template <int D>
+__global__ void __launch_bounds__(256) s1_untilted_dip_kernel(S1Args a) {
+  constexpr int IG = 32, JB = 8;
+  __shared__ float sP[IG][kMaxClusters];
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x * 256 + tid;  // < D * D (the grid covers it exactly)
+  const int Cq = a.Cq, Ck = a.Ck, Ckr = (Ck + JB - 1) / JB * JB;
+  const float* cov = a.cov_k + static_cast<size_t>(bh) * Ck * D * D + e;
+  for (int i0 = 0; i0 < Cq; i0 += IG) {
+    const int ni = min(IG, Cq - i0);
+    __syncthreads();  // the previous group's rows are consumed
+    for (int ii = wave; ii < IG; ii += 4) {  // a wave per query cluster: softmax over j
+      float l[kMaxClusters / 64];
+      float mx = kNegInf;
+      const float* lz = a.s_logz + (static_cast<size_t>(bh) * a.nbS * Cq + i0 + ii) * Ck;
+#pragma unroll
+      for (int q = 0; q < kMaxClusters / 64; ++q) {
+        const int jj = lane + 64 * q;
+        l[q] = ii < ni && jj < Ck ? lz[jj] : kNegInf;
+        mx = fmaxf(mx, l[q]);
+      }
+      mx = wave_max(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxClusters / 64; ++q) {
+        l[q] = l[q] == kNegInf ? 0.f : __expf(l[q] - mx);
+        sum += l[q];
+      }
+      sum = wave_sum(sum);
+      const float inv = sum > 0.f ? 1.f / sum : 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxClusters / 64; ++q) sP[ii][lane + 64 * q] = l[q] * inv;
+    }
+    __syncthreads();
+    float acc[IG];
+#pragma unroll
+    for (int ii = 0; ii < IG; ++ii) acc[ii] = 0.f;
+    for (int j0 = 0; j0 < Ckr; j0 += JB) {
+      float cv[JB];
+#pragma unroll
+      for (int q = 0; q < JB; ++q) cv[q] = j0 + q < Ck ? cov[static_cast<size_t>(j0 + q) * D * D] : 0.f;
+#pragma unroll
+      for (int q = 0; q < JB; ++q)
+#pragma unroll
+        for (int ii = 0; ii < IG; ++ii) acc[ii] = fmaf(sP[ii][j0 + q], cv[q], acc[ii]);
+    }
+    for (int ii = 0; ii < ni; ++ii) {
+      const size_t sidx = static_cast<size_t>(bh) * a.nbS * Cq + i0 + ii;  // entry 0
+      if (a.t_dip != nullptr) a.t_dip[sidx * D * D + e] = f32_to_bf16_bits(a.scale * acc[ii]);
+      else a.s_dip[sidx * D * D + e] = acc[ii];
+    }
+  }
+}
+
+template <typename T, int D>
+static void launch_untilted(const S1Args& a, int part, hipStream_t s) {
+  if (part == 0) {
+    ProfScope ps_("s1_cluster_cov", s);
+    hipLaunchKernelGGL((s1_cluster_cov_kernel<T, D>), dim3(a.Ck, a.BH), dim3(256), 0, s, a);
+  } else {
+    ProfScope ps_("s1_untilted_dip", s);
+    hipLaunchKernelGGL((s1_untilted_dip_kernel<D>), dim3((D * D + 255) / 256, a.BH), dim3(256), 0, s, a);
+  }
+}
+
 // A second stream per device (default priority, created on first use and kept until the
 // process ends) on which the atoms run beside the scores and the block moments: the
 // atoms read only the clustering, the moments read the scores, and the tables need both.
@@ -416,12 +608,24 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
       (void)hipStreamSynchronize(side);  // the join cannot be enqueued: wait on the host
       two = false;
     }
-    launch_stage1_mfma(a, 0, s);
-    if (a.dipole) launch_stage1_mfma(a, 2, s);
+    const bool untilted = a.dipole == 2;  // acausal only (the call is refused otherwise)
+    if (untilted) {
+      launch_untilted<T, D>(a, 0, s);  // per key cluster covariance (needs no scores)
+    } else {
+      launch_stage1_mfma(a, 0, s);
+      if (a.dipole) launch_stage1_mfma(a, 2, s);
+    }
     if (two && hipStreamWaitEvent(s, join, 0) != hipSuccess) (void)hipStreamSynchronize(side);
     if (fork != nullptr) (void)hipEventDestroy(fork);
     if (join != nullptr) (void)hipEventDestroy(join);
-    launch_stage1_mfma(a, a.causal ? 4 : 3, s);
+    if (untilted) {
+      S1Args af = a;
+      af.dipole = 0;  // the tables without the tilted dipole
+      launch_stage1_mfma(af, 3, s);
+      launch_untilted<T, D>(a, 1, s);
+    } else {
+      launch_stage1_mfma(a, a.causal ? 4 : 3, s);
+    }
     return;
   }
   if (mf) {
@@ -437,6 +641,15 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   {
     ProfScope ps_("s1_prefix", s);
     hipLaunchKernelGGL(s1_prefix_kernel, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
+  }
+  if (a.dipole == 2) {  // untilted (acausal, no retrieval): per key cluster covariances
+    launch_untilted<T, D>(a, 0, s);
+    launch_untilted<T, D>(a, 1, s);
+    if (a.t_khi != nullptr) {
+      ProfScope ps_("s1_pack", s);
+      hipLaunchKernelGGL(s1_pack_kernel, dim3(a.Cq, a.nbS, a.BH), dim3(256), 0, s, a);
+    }
+    return;
   }
   if (a.dipole) {
     if (mf) {

@@ -78,6 +78,13 @@ def oracle_head(cfg: WorkloadConfig, q, k, v, trace_q, trace_k, dipole="tilted",
     return r, kq, kk
 
 
+def oracle_dipole(dipole) -> str:
+    """The oracle's dipole mode for a binding dipole argument (True, False or a mode name)."""
+    if isinstance(dipole, bool):
+        return "tilted" if dipole else "none"
+    return str(dipole)
+
+
 def check_config(cfg: WorkloadConfig, heads: List[Tuple[int, int]], tol: Optional[float] = None,
                  blocks: Optional[Sequence[int]] = None, out_dtype=torch.float32, dipole=True,
                  rows: Optional[np.ndarray] = None) -> List[HeadCheck]:
@@ -95,7 +102,7 @@ def check_config(cfg: WorkloadConfig, heads: List[Tuple[int, int]], tol: Optiona
     tol = TOL[cfg.dtype] if tol is None else tol
     for b, h in heads:
         r, kq, kk = oracle_head(cfg, q[b, h], k[b, h], v[b, h], tq[:, b, h], tk[:, b, h],
-                                dipole="tilted" if dipole else "none", blocks=blocks, rows=rows,
+                                dipole=oracle_dipole(dipole), blocks=blocks, rows=rows,
                                 retrieval_trace=None if rtr is None else rtr[b, h])
         assert np.array_equal(kq.labels, tq[-1, b, h]) and np.array_equal(kk.labels, tk[-1, b, h])
         sel = np.isfinite(r.o[:, 0])

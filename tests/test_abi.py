@@ -93,3 +93,28 @@ def test_exact_rejects_bad_shapes(lib):
     assert lib.muse_exact_attn_fwd(vp(1), vp(2), vp(3), vp(4), 1, 1, 64, 80, 0, 1, None) == -2
     assert lib.muse_exact_attn_fwd(vp(1), vp(2), vp(3), None, 1, 1, 64, 64, 0, 1, None) == -1
     assert lib.muse_version() >= 100
+
+
+def test_dipole_modes(lib):
+    # the binding's mode names follow the header's MUSE_DIPOLE_* values
+    from clustered_softmax_attention_amd import binding
+    from clustered_softmax_attention_amd.binding import FwdParams
+    text = open(HEADER).read()
+    for name, code in binding.DIPOLE_MODES.items():
+        assert re.search(rf"\bMUSE_DIPOLE_{name.upper()}\s*=\s*{code}\b", text), name
+    assert binding.dipole_code(True) == 1 and binding.dipole_code(False) == 0
+    assert binding.dipole_code("untilted") == 2
+    with pytest.raises(ValueError):
+        binding.dipole_code("sideways")
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    tilted = lib.muse_attn_fwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, ctypes.byref(p))
+    p.dipole = 2
+    # acausal: the untilted mode adds the per key cluster covariances [B*H, Ck, D, D] fp32
+    untilted = lib.muse_attn_fwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, ctypes.byref(p))
+    assert untilted >= tilted + 32 * 128 * 64 * 64 * 4
+    # causal: not implemented, refused before any launch
+    assert lib.muse_attn_fwd_workspace_bytes(8, 8, 16384, 64, 16, 64, 1, 1024, 1, ctypes.byref(p)) == 0
+    assert "acausal" in lib.muse_last_error().decode()
+    p.dipole = 3
+    assert lib.muse_attn_fwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, ctypes.byref(p)) == 0

@@ -52,6 +52,27 @@ def test_bf16_d128_odd_cluster_counts(muse_lib, causal):
     check_config(cfg, [(0, 0), (0, 1)])
 
 
+@pytest.mark.parametrize("name,over", [
+    ("acausal_1k_f32", {}),
+    ("acausal_8k", {"B": 1, "H": 2, "N": 1536}),
+    ("causal_64k_d128", {"B": 1, "H": 2, "N": 1000, "causal": False, "block": 0, "Cq": 12, "Ck": 40}),
+])
+def test_untilted_dipole(muse_lib, name, over):
+    # the partially specialised (untilted) dipole: per key cluster covariances, fp32 and
+    # bf16 inputs, D = 64 and 128, a ragged tail and cluster counts off the 32-tiles
+    cfg = scaled_config(name, **over) if over else CONFIGS[name]
+    check_config(cfg, [(0, 0)] if cfg.H == 1 else [(0, 0), (0, 1)], dipole="untilted")
+
+
+def test_untilted_dipole_causal_is_refused(muse_lib):
+    from clustered_softmax_attention_amd import binding
+    cfg = scaled_config("causal_16k", B=1, H=1, N=2048, block=1024)
+    q, k, v = (to_device(t, cfg.dtype) for t in make_inputs(cfg))
+    with pytest.raises(binding.MuseError, match="acausal") as err:
+        binding.attn_fwd(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, causal=True, block=cfg.block, dipole="untilted")
+    assert err.value.code == -2  # MUSE_ERR_UNSUPPORTED
+
+
 def test_acausal_bf16_d128(muse_lib):
     cfg = scaled_config("causal_64k_d128", B=1, H=2, N=2048, causal=False, block=0)
     check_config(cfg, [(0, 0), (0, 1)])
