@@ -124,6 +124,34 @@ def test_dipole_aggregation_uses_stage1_cluster_weights():
         assert np.max(np.abs(S.Dip[i] - Dexp)) < 1e-13
 
 
+def test_untilted_dipole_is_the_tilted_one_at_a_zero_centroid():
+    # with qbar_i = 0 every key of a cluster gets the same weight, so the tilted
+    # covariance C_ij is the plain covariance Cov_j (population normalisation, value
+    # index first): the untilted mode must agree with the tilted one there, which is
+    # itself pinned by the finite differences above; at a nonzero centroid they differ
+    rng = np.random.default_rng(17)
+    D, n = 5, 60
+    k = rng.standard_normal((n, D)) + 0.7
+    v = 2.0 * k[:, ::-1] + 0.3 * rng.standard_normal((n, D))  # Cov(v, k) far from symmetric
+    labels = rng.integers(0, 4, n)
+    zero = np.zeros((1, D))
+    St = tilted_summaries(zero, k, v, labels, 4, 0.5, dipole="tilted")
+    Su = tilted_summaries(zero, k, v, labels, 4, 0.5, dipole="untilted")
+    assert np.max(np.abs(St.Dip - Su.Dip)) < 1e-12
+    # and by hand: D = sum_j (n_j / n) Cov_j, since P_j = n_j / n at a zero centroid
+    Dh = np.zeros((D, D))
+    for j in range(4):
+        m = labels == j
+        vc, kc = v[m] - v[m].mean(0), k[m] - k[m].mean(0)
+        Dh += (m.sum() / n) * (vc.T @ kc) / m.sum()
+    assert np.max(np.abs(Su.Dip[0] - Dh)) < 1e-12
+    assert np.max(np.abs(Dh - Dh.T)) > 0.1
+    q = rng.standard_normal((1, D))
+    St2 = tilted_summaries(q, k, v, labels, 4, 0.5, dipole="tilted")
+    Su2 = tilted_summaries(q, k, v, labels, 4, 0.5, dipole="untilted")
+    assert np.max(np.abs(St2.Dip - Su2.Dip)) > 1e-3
+
+
 def test_empty_key_cluster_drops_out():
     rng = np.random.default_rng(15)
     k, v = rng.standard_normal((20, 4)), rng.standard_normal((20, 4))
