@@ -594,10 +594,14 @@ __global__ void __launch_bounds__(256, 2) s1_finalize_acausal_kernel(S1Args a) {
   constexpr int NCH = kMaxClusters / JC;  // cluster chunks
   constexpr int NF = JC * D / 4 / 256;    // float4 of a chunk's K (and V) sums per thread
   constexpr int MB = D == 64 ? 4 : 1;     // moment slices loaded per batch
-  __shared__ __align__(16) uint16_t sKh[JC * ST];
-  __shared__ __align__(16) uint16_t sKl[JC * ST];
-  __shared__ __align__(16) uint16_t sVh[JC * ST];
-  __shared__ __align__(16) uint16_t sVl[JC * ST];
+  // the four chunk tiles, one buffer: after the last chunk it stages s * D_i
+  __shared__ __align__(16) uint16_t sT[4 * JC * ST];
+  uint16_t* const sKh = sT;
+  uint16_t* const sKl = sT + JC * ST;
+  uint16_t* const sVh = sT + 2 * JC * ST;
+  uint16_t* const sVl = sT + 3 * JC * ST;
+  constexpr int DST = D + 8;  // row stride of the staged dipole
+  static_assert(D * DST <= 4 * JC * ST, "the staged dipole fits in the chunk tiles");
   __shared__ __align__(16) float sP[kMaxClusters];
   __shared__ float sM[kMaxClusters], sInv[kMaxClusters];
   __shared__ float sW[kMaxClusters][kFinQB];  // item weights exp(m_q - M) of the first kFinQB items
@@ -878,15 +882,24 @@ __global__ void __launch_bounds__(256, 2) s1_finalize_acausal_kernel(S1Args a) {
     }
   }
   if (a.dipole) {
-    // acc = sum P V K^T - E = -D_i
+    // acc = sum P V K^T - E = -D_i: staged in LDS once every wave is past the last chunk's
+    // products, then stored as whole rows with 16-byte stores
+    __syncthreads();
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = 32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3);
-        a.t_dip[(sidx * D + row) * D + 32 * dkt + c] = f32_to_bf16_bits(-a.scale * acc[t][v]);
+        sT[row * DST + 32 * dkt + c] = f32_to_bf16_bits(-a.scale * acc[t][v]);
       }
+    }
+    __syncthreads();
+    uint16_t* dip = a.t_dip + sidx * D * D;
+    for (int x = tid; x < D * D / 8; x += 256) {
+      const int r = x / (D / 8), c8 = x % (D / 8);
+      *reinterpret_cast<u16x8_t*>(dip + static_cast<size_t>(r) * D + 8 * c8) =
+          *reinterpret_cast<const u16x8_t*>(sT + r * DST + 8 * c8);
     }
   }
 }
@@ -920,10 +933,14 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
   constexpr int NW = Cfg::NW, T = Cfg::T, NE4 = Cfg::NE4, RPC = Cfg::RPC, NDT = Cfg::NDT, NT = Cfg::NT;
   constexpr int TPW = Cfg::TPW, ST = Cfg::ST;
   constexpr int JC = 32;
-  __shared__ __align__(16) uint16_t sKh[JC * ST];
-  __shared__ __align__(16) uint16_t sKl[JC * ST];
-  __shared__ __align__(16) uint16_t sVh[JC * ST];
-  __shared__ __align__(16) uint16_t sVl[JC * ST];
+  // the four chunk tiles, one buffer: after an entry's products it stages s * D_i
+  __shared__ __align__(16) uint16_t sT[4 * JC * ST];
+  uint16_t* const sKh = sT;
+  uint16_t* const sKl = sT + JC * ST;
+  uint16_t* const sVh = sT + 2 * JC * ST;
+  uint16_t* const sVl = sT + 3 * JC * ST;
+  constexpr int DST = D + 8;  // row stride of the staged dipole
+  static_assert(D * DST <= 4 * JC * ST, "the staged dipole fits in the chunk tiles");
   __shared__ __align__(16) float sP[kMaxClusters];
   __shared__ float sm[kMaxClusters], sz[kMaxClusters], sfo[kMaxClusters], sfn[kMaxClusters], sinv[kMaxClusters];
   __shared__ float red[2 * NW];
@@ -1067,7 +1084,8 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
         __syncthreads();  // the next chunk overwrites the tiles
       }
       if (a.dipole) {
-        // dacc = sum P V K^T - E = -D_i
+        // dacc = sum P V K^T - E = -D_i: staged in LDS (the chunk tiles are free after the
+        // last chunk's barrier), then stored as whole rows with 16-byte stores
         uint16_t* dip = a.t_dip + ((static_cast<size_t>(bh) * a.nbS + b) * Cq + i) * D * D;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
@@ -1076,8 +1094,14 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int row = 32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3);
-            dip[static_cast<size_t>(row) * D + 32 * dkt + c] = f32_to_bf16_bits(-a.scale * dacc[t][v]);
+            sT[row * DST + 32 * dkt + c] = f32_to_bf16_bits(-a.scale * dacc[t][v]);
           }
+        }
+        __syncthreads();
+        for (int x = tid; x < D * D / 8; x += T) {
+          const int r = x / (D / 8), c8 = x % (D / 8);
+          *reinterpret_cast<u16x8_t*>(dip + static_cast<size_t>(r) * D + 8 * c8) =
+              *reinterpret_cast<const u16x8_t*>(sT + r * DST + 8 * c8);
         }
       }
     }
