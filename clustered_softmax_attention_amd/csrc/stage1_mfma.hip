@@ -911,15 +911,16 @@ __global__ void __launch_bounds__(256, 2) s1_finalize_acausal_kernel(S1Args a) {
 // writes entry b of the stage-2 tables: log Z_ij, bf16 hi/lo K_ij and V_ij (row-major),
 // and  s * D_i = s * (E_i[v k^T] - sum_j P_ij V_ij K_ij^T)  with the sum over j on the
 // matrix cores (operands split into bf16 hi + lo, read by the transpose read from LDS
-// tiles of 32 clusters). Then block b is folded in.
+// tiles of 64 clusters). Then block b is folded in.
 // Thread mapping: float4 e4 = tid + T r of the [Ck][D] sums, i.e. cluster
-// j = e4 / (D/4); the 32-cluster chunk cc holds the thread's float4s r = RPC cc .. RPC cc + RPC - 1.
+// j = e4 / (D/4); the JC-cluster chunk cc holds the thread's float4s r = RPC cc .. RPC cc + RPC - 1.
 template <int D>
 struct ScanCfg {
   static constexpr int NW = D == 128 ? 16 : 8;
   static constexpr int T = 64 * NW;
+  static constexpr int JC = 64;                         // key clusters per LDS chunk
   static constexpr int NE4 = kMaxClusters * D / 4 / T;  // float4s per thread and tensor
-  static constexpr int RPC = 32 * (D / 4) / T;          // of them per 32-cluster chunk
+  static constexpr int RPC = JC * (D / 4) / T;          // of them per chunk
   static constexpr int NDT = D / 32;
   static constexpr int NT = NDT * NDT;                  // dipole output tiles
   static constexpr int TPW = NT / NW > 0 ? NT / NW : 1;  // per wave
@@ -931,8 +932,7 @@ template <int D>
 __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a) {
   using Cfg = ScanCfg<D>;
   constexpr int NW = Cfg::NW, T = Cfg::T, NE4 = Cfg::NE4, RPC = Cfg::RPC, NDT = Cfg::NDT, NT = Cfg::NT;
-  constexpr int TPW = Cfg::TPW, ST = Cfg::ST;
-  constexpr int JC = 32;
+  constexpr int TPW = Cfg::TPW, ST = Cfg::ST, JC = Cfg::JC;
   // the four chunk tiles, one buffer: after an entry's products it stages s * D_i
   __shared__ __align__(16) uint16_t sT[4 * JC * ST];
   uint16_t* const sKh = sT;
@@ -1063,7 +1063,7 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
           int dvt, dkt;
           if (!tile_of(t, dvt, dkt)) break;
 #pragma unroll
-          for (int ks2 = 0; ks2 < 2; ++ks2) {
+          for (int ks2 = 0; ks2 < JC / 16; ++ks2) {
             const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(sP + JC * cc + 16 * ks2 + 8 * h);
             const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(sP + JC * cc + 16 * ks2 + 8 * h + 4);
             const float pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
