@@ -470,7 +470,7 @@ __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int la
           second[gi] = second[gi] > ob ? second[gi] : ob;
         }
         // distance error bound E; scores carry half of it
-        E[gi] = 1e-4f * sqrtf(xx[gi]) * cmax + 2e-5f * cmax2;
+        E[gi] = 1e-4f * sqrtf(xx[gi]) * cmax + (2e-5f * (D / 64)) * cmax2;  // the max|c|^2 part grows with the 2D + 1 summed terms
         const long p = static_cast<long>(tt) * TILE + wave * 64 + gi * 32 + c;
         need[gi] = p < a.N && second[gi] >= best[gi] - E[gi];
       }
@@ -838,7 +838,7 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
           second = second > ob ? second : ob;
         }
         // distance error bound E; scores carry half of it
-        E = 1e-4f * sqrtf(xx) * cmax + 2e-5f * cmax2;
+        E = 1e-4f * sqrtf(xx) * cmax + (2e-5f * (D / 64)) * cmax2;  // the max|c|^2 part grows with the 2D + 1 summed terms
         need = n < a.N && second >= best - E;
       }
       // a second centroid within the window: every candidate within it is re-scored with
