@@ -181,9 +181,10 @@ def test_exact_attention(muse_lib, dtype, D, causal):
 
 # ------------------------------------------------------------ full-size configurations (sampled)
 
-def test_acausal_8k_full_size_sampled_heads(muse_lib):
+@pytest.mark.parametrize("dipole", [True, "untilted"])
+def test_acausal_8k_full_size_sampled_heads(muse_lib, dipole):
     cfg = CONFIGS["acausal_8k"]
-    check_config(cfg, [(0, 0), (3, 7)])
+    check_config(cfg, [(0, 0), (3, 7)], dipole=dipole)
 
 
 def test_causal_16k_full_size_sampled_blocks(muse_lib):
