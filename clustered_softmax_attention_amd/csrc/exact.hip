@@ -215,13 +215,15 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
       }
     mx = fmaxf(mx, xor32(mx));
     const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mn);
+    if (__ballot(mn > m) != 0ull) {  // rescale only when a row's running max grew (else alpha = 1)
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+    }
     m = mn;
-    l *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll

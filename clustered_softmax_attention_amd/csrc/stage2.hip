@@ -273,6 +273,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
     const float mn = fmaxf(mx, cm);
     if (mn == kNegInf) continue;  // no key cluster yet: nothing to add (same for the lane pair)
     const float alpha = mx == kNegInf ? 0.f : fast_exp2(mx - mn);
+    // the sums need rescaling only when a lane's running max grew and it had summed before
+    const bool grow = mn > mx && mx != kNegInf;
     mx = mn;
     float zs = 0.f;
 #pragma unroll
@@ -282,10 +284,12 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
       zs += p;
     }
     z = z * alpha + zs + xor32(zs);
+    if (__ballot(grow) != 0ull) {
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+      for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+        for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+    }
     // O^T += V^T P^T (split): k-slots of step ss are rows 16 ss + 4 h + 0..3 and 16 ss + 8 + 4 h + 0..3
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss) {
