@@ -24,7 +24,12 @@
  *     16-bit patterns). All arithmetic accumulates in fp32.
  *   - hip_stream: a hipStream_t (NULL = the default stream). Calls only enqueue
  *     work on it and return; there is no host synchronisation inside. Pointers
- *     must stay valid until that work completes.
+ *     must stay valid until that work completes. Part of a bf16 call (the stage-1
+ *     atoms) runs on a stream the library keeps per device, forked from and joined
+ *     back into hip_stream by events recorded in the call, so the whole call is
+ *     still ordered after earlier work on hip_stream and before later work on it
+ *     (a graph capture of hip_stream captures both branches). Concurrent calls on
+ *     several caller streams of one device serialise on that stream's share.
  *   - Errors: arguments are validated on the host before anything is launched; a
  *     negative status is returned and muse_last_error() describes it. A launch
  *     failure returns MUSE_ERR_HIP. Faults during execution surface at the
