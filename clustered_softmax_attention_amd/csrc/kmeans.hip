@@ -20,13 +20,14 @@
 //                   (block, label), i.e. the key (or query) permutation used by
 //                   the summary kernels.
 //
-// bf16 inputs (kmeans_assign_mfma): the distance scores ||c_j||^2 - 2 x.c_j come from
-// the matrix cores, with each fp32 centroid split into bf16 hi + lo parts (x is exact
-// in bf16). Their error is bounded by E = 1e-4 ||x|| max||c|| + 2e-5 max||c||^2 (about
-// 2.5x the worst case of the split residual 2^-16 and the fp32 accumulation); when a
-// second centroid scores within 2E of the best, every such candidate is re-scored with
-// the exact fp32 direct form sum_d (x_d - c_jd)^2 of the fp32 path, so labels are the
-// same as the fp32 path's.
+// bf16 inputs (kmeans_assign_mfma): the scores x.c_j - ||c_j||^2 / 2 (the distance is
+// ||x||^2 minus twice the score) come from the matrix cores, with each fp32 centroid
+// split into bf16 hi + lo parts (x is exact in bf16). Two scores can swap only within
+// E = 1e-4 ||x|| max||c|| + 2e-5 (D / 64) max||c||^2, above twice the worst case of the
+// split residual, the fp32 accumulation over 2D + 1 terms, the fp32 norm and the rank
+// key's truncation; when a second centroid scores within E of the best, every such
+// candidate is re-scored with the exact fp32 direct form sum_d (x_d - c_jd)^2 of the
+// fp32 path, so labels are the same as the fp32 path's.
 //
 // Every sum runs in a fixed order, so labels and centroids are bitwise
 // reproducible.

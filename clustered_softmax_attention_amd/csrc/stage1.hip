@@ -20,6 +20,10 @@
 //   s1_prefix     fold of atoms over blocks -> log Z, K, V tables.
 //   s1_mom_prefix fold of block moments over blocks -> E_i[v k^T] per table entry.
 //   s1_dip_final  D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T (value index first).
+//   s1_cluster_cov, s1_untilted_dip  the untilted dipole (acausal): per key cluster
+//                 covariance Cov_j, then D_i = sum_j P_ij Cov_j.
+// The bf16 kernels (matrix cores) are in stage1_mfma.hip; this file launches them, the
+// atoms on a second stream beside the scores and moments.
 #include <mutex>
 
 #include "mfma.hpp"
