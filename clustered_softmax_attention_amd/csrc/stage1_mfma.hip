@@ -1192,7 +1192,7 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
   } else if (which == 1) {
     const int nbC = a.nb * a.Ck;
     const size_t lds = static_cast<size_t>((a.Cq + 31) & ~31) * (D + 8) * 2 * sizeof(uint16_t);
-    allow_lds((const void*)s1_atoms_mfma_kernel<D>, lds + 2 * 4 * kAtomChunk * (D + 8) * sizeof(uint16_t));
+    allow_lds((const void*)s1_atoms_mfma_kernel<D>, lds);  // the dynamic part (s qbar); the row tiles are static
     {
       // items per wave: about items / (16 x resident waves), rounded, 1..16 (measured: 2
       // at 1.3k items per head x 64 heads with D = 64, 4-5 at 5k x 16 with D = 128)

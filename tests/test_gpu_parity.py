@@ -41,6 +41,25 @@ def test_bf16_odd_cluster_counts_long_buckets(muse_lib, causal):
     check_config(cfg, [(0, 0), (0, 1)])
 
 
+@pytest.mark.parametrize("name,over", [
+    # fewer points than one 256-point K-means tile, one cluster of each kind
+    ("acausal_8k", {"B": 1, "H": 1, "N": 200, "Cq": 1, "Ck": 1}),
+    # the largest cluster counts, many of them small or empty
+    ("acausal_8k", {"B": 1, "H": 1, "N": 700, "Cq": 128, "Ck": 128}),
+    # one query cluster against the largest key count, 64-token causal blocks (64-point tiles)
+    ("causal_16k", {"B": 1, "H": 1, "N": 1024, "block": 64, "Cq": 1, "Ck": 128}),
+    # fp32, and D = 128 with one key cluster
+    ("acausal_1k_f32", {"N": 300, "Cq": 3, "Ck": 128}),
+    ("causal_64k_d128", {"B": 1, "H": 1, "N": 256, "causal": False, "block": 0, "Cq": 128, "Ck": 1}),
+    # D = 128 with the largest query cluster count (the atoms' centroid tables exceed 64 KB
+    # of LDS), fp32 and causal bf16
+    ("acausal_1k_f32", {"N": 512, "D": 128, "Cq": 128, "Ck": 128}),
+    ("causal_64k_d128", {"B": 1, "H": 1, "N": 2048, "block": 512, "Cq": 128, "Ck": 64}),
+])
+def test_cluster_count_extremes(muse_lib, name, over):
+    check_config(scaled_config(name, **over), [(0, 0)])
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_d128_odd_cluster_counts(muse_lib, causal):
     # D = 128: cluster counts off the 32-centroid tiles (one to three tiles of them, so
