@@ -60,6 +60,18 @@ def test_cluster_count_extremes(muse_lib, name, over):
     check_config(scaled_config(name, **over), [(0, 0)])
 
 
+@pytest.mark.parametrize("name,over", [
+    ("acausal_8k", {"B": 1, "H": 1, "N": 1024, "iters": 1}),           # one Lloyd iteration
+    ("causal_16k", {"B": 1, "H": 1, "N": 1536, "block": 192, "iters": 3}),  # 192-point tiles
+    ("causal_16k", {"B": 1, "H": 1, "N": 1024, "block": 1024}),          # one block: no far field
+    ("retrieval_16k", {"B": 1, "H": 1, "N": 2048, "D": 128, "block": 512}),  # retrieval at D = 128
+    ("acausal_8k", {"B": 8, "H": 8, "N": 256, "Cq": 4, "Ck": 16}),       # many short heads
+])
+def test_shapes(muse_lib, name, over):
+    cfg = scaled_config(name, **over)
+    check_config(cfg, [(0, 0)] if cfg.B * cfg.H == 1 else [(0, 0), (cfg.B - 1, cfg.H - 1)])
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_d128_odd_cluster_counts(muse_lib, causal):
     # D = 128: cluster counts off the 32-centroid tiles (one to three tiles of them, so
