@@ -118,3 +118,24 @@ def test_dipole_modes(lib):
     assert "acausal" in lib.muse_last_error().decode()
     p.dipole = 3
     assert lib.muse_attn_fwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, ctypes.byref(p)) == 0
+
+
+def test_ex_entry_rejects_before_launch(lib):
+    # everything below fails in the host-side checks, before any device call
+    from clustered_softmax_attention_amd.binding import FwdParams
+    vp = ctypes.c_void_p
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    need = lib.muse_attn_fwd_workspace_bytes(1, 1, 1024, 64, 8, 32, 0, 0, 1, ctypes.byref(p))
+    p.workspace = 0x1000
+    p.workspace_bytes = need - 1
+    args = (vp(1), vp(2), vp(3), vp(4), 1, 1, 1024, 64, 8, 32, 5, 0, 0, 1, None)
+    assert lib.muse_attn_fwd_ex(*args, ctypes.byref(p)) == -5  # MUSE_ERR_WORKSPACE
+    assert "workspace" in lib.muse_last_error().decode()
+    p.workspace_bytes = need
+    p.dipole = 2
+    causal = (vp(1), vp(2), vp(3), vp(4), 1, 1, 1024, 64, 8, 32, 5, 1, 256, 1, None)
+    assert lib.muse_attn_fwd_ex(*causal, ctypes.byref(p)) == -2  # untilted dipole: acausal only
+    p.dipole = 1
+    aliased = (vp(1), vp(2), vp(3), vp(1), 1, 1, 1024, 64, 8, 32, 5, 0, 0, 1, None)
+    assert lib.muse_attn_fwd_ex(*aliased, ctypes.byref(p)) == -1  # out aliases q
