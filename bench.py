@@ -197,7 +197,7 @@ def main():
                     help="only run K device-to-device copies of MIB MiB (to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(heads are independent, so a multi-GPU run would shard (b, h) heads with no communication).",
               file=sys.stderr)
         sys.exit(2)

@@ -55,7 +55,7 @@ typedef enum { MUSE_F32 = 0, MUSE_BF16 = 1 } muse_dtype_t;
 enum {
   MUSE_OK = 0,
   MUSE_ERR_INVALID_ARG = -1, /* a pointer, size or flag is out of range         */
-  MUSE_ERR_UNSUPPORTED = -2, /* valid, but not a shape this build implements    */
+  MUSE_ERR_UNSUPPORTED = -2, /* valid, but not a shape the library implements  */
   MUSE_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed      */
   MUSE_ERR_NO_MEMORY = -4,   /* workspace allocation failed                     */
   MUSE_ERR_WORKSPACE = -5    /* caller workspace too small                      */

@@ -9,13 +9,13 @@ Softmax Attention for Pretraining"):
   [REVIEW]  pith.science review page of the paper: "What carries the argument",
             "Core claim", "Circularity Check", "Assumptions & free parameters",
             "Referee Report" (minor comment on Algorithm 3), caption of Figure 2.
-  [VERDICT] pith.science verdict record of the paper, field "key_machinery".
+  [RECORD] pith.science verdict record of the paper, field "key_machinery".
   [GIST]    gist.science technical summary (Dutch), "Methodologie",
             "Kernmechanismen" items 1 to 4.
   [ABS2]    fugumt.com listing of the v2 abstract.
 The paper's own equations are not reproduced on any page; the formulas below
 are the cumulant-expansion reading spelled out in each docstring. Readings of
-points the pages leave open are tagged [R1]..[R14] and listed in the design doc.
+points the pages leave open are tagged [R1]..[R14]; each is stated where it is used.
 
 Pins (tests/test_oracle_*.py, CPU only):
   exact_attention      pinned: hand-worked closed form; torch SDPA (fp64, CPU).
@@ -183,7 +183,7 @@ def lloyd_kmeans(x, C: int, iters: int, follow_trace: Optional[Sequence[np.ndarr
 
 # --------------------------------------------------------------------------------------
 # Stage 1: coarse query centroids attend to fine key clusters
-# ([REVIEW] "What carries the argument", "Core claim"; [VERDICT] key_machinery;
+# ([REVIEW] "What carries the argument", "Core claim"; [RECORD] key_machinery;
 #  [GIST] Kernmechanismen 2, "Fase 1" and "Exponential Tilting")
 # --------------------------------------------------------------------------------------
 
