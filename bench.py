@@ -1,15 +1,17 @@
 """Throughput of the MuSe forward pass on one MI355X, with roofline and CPU-oracle baseline.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload acausal_8k] [--no-cpu]
-                [--no-exact] [--no-secondary]
+                [--no-exact] [--no-secondary] [--no-peaks]
 
 A step is one muse_attn_fwd call over the whole workload batch (K-means, stage 1,
 stage 2 and, when causal, the exact diagonal blocks), with inputs resident in HBM and
 the workspace allocated beforehand. Prints ONE JSON line: `value` is the 8k workload's
 tokens/s (or the chosen workload's). Extra fields: the in-library exact attention time
 on the same shape (speedup), the relative squared error of MuSe against it, per-kernel
-average durations measured with HIP events on the stream the kernels run on, and, with
-the default workload, `secondary`: the same figures for the 64k causal configuration.
+average durations measured with HIP events on the stream the kernels run on, the
+untilted-dipole run of an acausal workload, `measured_peaks` (a device copy and a bf16
+GEMM on this GPU, beside the published peaks the roofline uses) and, with the default
+workload, `secondary`: the same figures for the 64k causal configuration.
 """
 
 from __future__ import annotations
@@ -193,6 +195,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true",
                     help="with the default workload, skip the 64k causal configuration reported beside it")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-peaks", action="store_true", help="skip the copy and GEMM reference measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run K device-to-device copies of MIB MiB (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -230,6 +233,8 @@ def main():
         secondary = {"workload": WORKLOAD_TEXT[SECONDARY], "name": SECONDARY, "value": sec["value"],
                      "unit": "tokens/s", "ms_per_step": sec["ms"], "roofline": sec["roofline"], **sec["extra"]}
 
+    peaks = None if args.no_peaks else measured_peaks()
+
     line = {
         "metric": METRIC,
         "value": res["value"],
@@ -252,8 +257,48 @@ def main():
         "wall_s_timed": res["wall"],
         **res["extra"],
         "secondary": secondary,
+        "measured_peaks": peaks,
     }
+    if peaks is not None:
+        # the dominant kernel against what this GPU reaches for plain streaming / GEMM work
+        for rf in [res["roofline"]] + ([secondary["roofline"]] if secondary else []):
+            ref = peaks["copy_GBps"] if rf["bound"] == "hbm" else peaks["bf16_gemm_TFLOPs"]
+            rf["frac_of_measured_peak"] = rf["achieved"] / ref
     print(json.dumps(line), flush=True)
+
+
+def measured_peaks() -> dict:
+    """What this GPU reaches on plain work, as context for the published peaks: a 1 GiB
+    device-to-device copy (bytes read + written per second) and a bf16 8192^3 GEMM
+    (torch.matmul, contiguous operands; 2 flops per multiply-add), 10 timed runs each."""
+    import torch
+
+    def timed_events(fn, reps=10):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3  # seconds per run
+
+    n = 1 << 28  # floats: 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = timed_events(lambda: dst.copy_(src))
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(m, m, device="cuda", dtype=torch.bfloat16)
+    t_gemm = timed_events(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_GBps": 2 * 4 * n / t_copy / 1e9, "bf16_gemm_TFLOPs": 2 * m ** 3 / t_gemm / 1e12,
+            "published_hbm_GBps": PEAK_HBM_GBS, "published_bf16_TFLOPs": PEAK_BF16_MFMA_TFLOPS}
 
 
 def measure(name: str, steps: int, warmup: int, exact: bool) -> dict:
