@@ -358,6 +358,49 @@ def test_retrieval_selection_by_brute_force_ranking():
     assert take2.tolist() == [True, False, False, False, False, False, True, False, False, True]
 
 
+def test_retrieval_cluster_score_is_total_prefix_mass():
+    # The cluster score is the log of the cluster's whole mass in the prefix (a
+    # log-sum-exp over its atoms), not its best atom: cluster 0 has one atom of log-mass
+    # 1.0, cluster 1 three atoms of 0.8 each, so sigma(1) = 0.8 + log 3 > 1.0 and cluster 1
+    # wins although its best atom is weaker. Its three atoms tie; the lowest block wins.
+    labels = np.array([0, 1, 1, 1])
+    blocks = np.array([0, 0, 1, 2])
+    a = np.array([1.0, 0.8, 0.8, 0.8])
+    assert 0.8 + math.log(3) > 1.0
+    take = retrieval_selection(a, labels, blocks, 2, 3, k1=1, k2=1)
+    assert take.tolist() == [False, True, False, False]
+    # two keys of one atom add up too: cluster 1's block-2 atom (two keys at 0.5,
+    # log-mass 0.5 + log 2 = 1.19) outranks its block-0 atom (one key at 1.0)
+    labels2 = np.array([1, 1, 1, 0])
+    blocks2 = np.array([0, 2, 2, 1])
+    a2 = np.array([1.0, 0.5, 0.5, -5.0])
+    take2 = retrieval_selection(a2, labels2, blocks2, 2, 3, k1=1, k2=1)
+    assert take2.tolist() == [False, True, True, False]
+
+
+def test_partial_retrieval_with_degenerate_keys_is_exact_causal():
+    # Every key equals its cluster centroid, so the far summaries are exact over whatever
+    # keys they cover. With retrieval of some (cluster, block) atoms, the exact part and
+    # the far part must then split the prefix keys between them, each key counted once,
+    # and the merge is exact causal attention whatever was retrieved.
+    rng = np.random.default_rng(30)
+    base = rng.standard_normal((8, 6))
+    n = np.arange(96)
+    k = base[(n // 12 + n % 12) % 8]          # rows 12j (the strided init) hold group j
+    q = mixture(rng, 96, 6, 4, 0.5)
+    v = rng.standard_normal((96, 6))
+    o, L = exact_attention(q, k, v, causal=True)
+    for k1, k2 in ((1, 1), (2, 2), (3, 1)):
+        r = muse_causal(q, k, v, 4, 8, 2, block=24, topk_clusters=k1, topk_blocks=k2)
+        assert rel_l2(r.o, o) < 1e-12 and np.max(np.abs(r.lse - L)) < 1e-12
+    # and the retrieval did change which keys are summarised: without the degenerate keys
+    # the same selections give a result that differs from plain MuSe
+    k3 = k + 0.3 * rng.standard_normal(k.shape)
+    plain = muse_causal(q, k3, v, 4, 8, 2, block=24)
+    ret = muse_causal(q, k3, v, 4, 8, 2, block=24, topk_clusters=2, topk_blocks=1)
+    assert rel_l2(ret.o, plain.o) > 1e-4
+
+
 def test_retrieval_finds_planted_outliers():
     rng = np.random.default_rng(29)
     N, D, blk = 256, 8, 32
