@@ -14,6 +14,7 @@ from .muse_ref import (  # noqa: F401
     Summaries,
     default_scale,
     exact_attention,
+    hierarchy_squares,
     lloyd_kmeans,
     lse_merge,
     muse_acausal,

@@ -15,7 +15,7 @@ Softmax Attention for Pretraining"):
   [ABS2]    fugumt.com listing of the v2 abstract.
 The paper's own equations are not reproduced on any page; the formulas below
 are the cumulant-expansion reading spelled out in each docstring. Readings of
-points the pages leave open are tagged [R1]..[R14]; each is stated where it is used.
+points the pages leave open are tagged [R1]..[R15]; each is stated where it is used.
 
 Pins (tests/test_oracle_*.py, CPU only):
   exact_attention      pinned: hand-worked closed form; torch SDPA (fp64, CPU).
@@ -29,7 +29,10 @@ Pins (tests/test_oracle_*.py, CPU only):
                        tilted dipole); key-translation invariance; linearity in V.
   muse_acausal         pinned through the above.
   muse_causal          pinned: block = N and singleton clusters -> exact causal;
-                       causality in V; retrieval of everything -> exact causal.
+                       causality in V; retrieval of everything -> exact causal;
+                       hierarchical: squares tile the strictly lower block triangle
+                       once, two blocks = the prefix form, singleton and degenerate
+                       clusters -> exact causal, causality in V.
   retrieval_selection  pinned: planted high-score atoms are selected; brute-force
                        ranking on tiny inputs.
 """
@@ -430,12 +433,45 @@ def retrieval_selection(a_prefix: np.ndarray, labels_prefix: np.ndarray,
     return mask_of(sel), 0, 1
 
 
+def hierarchy_squares(nb: int) -> List[Tuple[int, int, int, int]]:
+    """Below-diagonal squares of the hierarchical causal decomposition [R15], in block units.
+
+    The pages draw the causal attention matrix cut into exact diagonal blocks and
+    below-diagonal squares handled by MuSe, with one square per level and position so
+    that the cost grows as N C D log N ([REVIEW] Figure 2 caption; "free parameters":
+    causal block size of the hierarchical decomposition; "invented entities":
+    hierarchical block decomposition). Reading: the grid of nb x nb blocks is padded to
+    the next power of two P and split recursively; a diagonal square of side w > 1
+    splits into two diagonal halves and the square below the diagonal (queries of the
+    lower half, keys of the upper half), which MuSe covers. Squares are clipped to the
+    nb real query blocks and dropped when empty. Returns (q0, q1, k0, k1): query blocks
+    [q0, q1) attend to key blocks [k0, k1) through one two-stage approximation."""
+    P = 1
+    while P < nb:
+        P *= 2
+    out: List[Tuple[int, int, int, int]] = []
+
+    def split(lo: int, w: int):
+        if w <= 1:
+            return
+        h = w // 2
+        q0, q1 = lo + h, min(lo + w, nb)
+        if q0 < q1:
+            out.append((q0, q1, lo, lo + h))
+        split(lo, h)
+        split(lo + h, h)
+
+    split(0, P)
+    return out
+
+
 def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
                 scale: Optional[float] = None, dipole: str = "tilted",
                 topk_clusters: int = 0, topk_blocks: int = 0,
                 labels_q=None, labels_k=None, follow_q=None, follow_k=None,
                 tie_rel: float = 1e-5, blocks_to_eval: Optional[Sequence[int]] = None,
-                retrieval_follow: Optional[np.ndarray] = None) -> MuseResult:
+                retrieval_follow: Optional[np.ndarray] = None,
+                hierarchical: bool = False) -> MuseResult:
     """Causal MuSe forward of one head [R8].
 
     Clusters are fitted once per head over the whole sequence. For a query n in
@@ -455,7 +491,12 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
     retrieval_follow: optional [nblocks, Cq, k1, 1 + k2] selections of another
     implementation (cluster id then block ids per chosen cluster, -1 padded), adopted
     where they are valid up to near-ties (see retrieval_selection); the counts are
-    returned in MuseResult.retrieval_near_ties / retrieval_mismatches."""
+    returned in MuseResult.retrieval_near_ties / retrieval_mismatches.
+
+    hierarchical: the far field of a block is not one summary of all earlier keys but
+    the log-sum-exp merge of one two-stage approximation per square of the hierarchy
+    (hierarchy_squares, [R15]), each over its own key range with the global clusters.
+    Retrieval is not combined with it."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -471,6 +512,27 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
     key_block = np.arange(N) // block
     near = mism = 0
     todo = range(nb) if blocks_to_eval is None else blocks_to_eval
+    if hierarchical:
+        if topk_clusters > 0:
+            raise ValueError("retrieval is not combined with the hierarchy")
+        want = set(int(b) for b in todo)
+        far = {b: (np.zeros((block, v.shape[1])), np.full(block, NEG_INF)) for b in want}
+        for q0, q1, k0, k1 in hierarchy_squares(nb):
+            hit = [b for b in range(q0, q1) if b in want]
+            if not hit:
+                continue
+            ks = slice(k0 * block, k1 * block)
+            S = tilted_summaries(qbar, k[ks], v[ks], lk[ks], Ck, s, dipole)
+            for b in hit:
+                rs = slice(b * block, (b + 1) * block)
+                o_s, L_s = refine(q[rs], lq[rs], qbar, S, s, dipole != "none")
+                far[b] = lse_merge(far[b][0], far[b][1], o_s, L_s)
+        for b in want:
+            r0, r1 = b * block, (b + 1) * block
+            rows = np.arange(r0, r1)
+            o_loc, L_loc = _attend(q[r0:r1], k[r0:r1], v[r0:r1], s, rows[None, :] <= rows[:, None])
+            o[r0:r1], L[r0:r1] = lse_merge(far[b][0], far[b][1], o_loc, L_loc)
+        return MuseResult(o, L, km_q, km_k, lq, lk, qbar)
     for b in todo:
         r0, r1 = b * block, (b + 1) * block
         rows = np.arange(r0, r1)

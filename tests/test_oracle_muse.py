@@ -10,8 +10,8 @@ import math
 import numpy as np
 import pytest
 
-from oracle import (exact_attention, lloyd_kmeans, muse_acausal, muse_causal, refine,
-                    retrieval_selection, tilted_summaries)
+from oracle import (exact_attention, hierarchy_squares, lloyd_kmeans, muse_acausal, muse_causal,
+                    refine, retrieval_selection, tilted_summaries)
 
 
 def rel_l2(a, b):
@@ -323,6 +323,86 @@ def test_causal_far_field_matches_acausal_summaries_of_the_prefix():
     om = np.exp(L_far - Lm)[:, None] * o_far + np.exp(L_loc - Lm)[:, None] * o_loc
     assert rel_l2(r.o[b * blk:], om) < 1e-13
     assert far.o.shape == om.shape
+
+
+# ------------------------------------------------------------ hierarchical causal decomposition
+
+@pytest.mark.parametrize("nb", list(range(1, 21)) + [32, 33])
+def test_hierarchy_squares_tile_the_lower_block_triangle(nb):
+    # every (query block b, key block b' < b) is covered by exactly one square and no
+    # square reaches the diagonal; squares are aligned, of side 2^l before clipping, and
+    # query block b is covered by popcount(b) of them (the binary digits of the prefix
+    # [0, b), one per level: log-many squares per block, [REVIEW] "invented entities")
+    cover = np.zeros((nb, nb), int)
+    per_block = np.zeros(nb, int)
+    for q0, q1, k0, k1 in hierarchy_squares(nb):
+        w = k1 - k0
+        assert w >= 1 and (w & (w - 1)) == 0 and k0 % w == 0
+        assert q0 == k1 and k1 < q1 <= k1 + w and q1 <= nb
+        cover[q0:q1, k0:k1] += 1
+        per_block[q0:q1] += 1
+    assert np.array_equal(cover, np.tril(np.ones((nb, nb), int), -1))
+    assert all(per_block[b] == bin(b).count("1") for b in range(nb))
+
+
+def _hier_inputs(seed, N=128, D=8):
+    rng = np.random.default_rng(seed)
+    return mixture(rng, N, D, 5, 0.4), mixture(rng, N, D, 5, 0.4), rng.standard_normal((N, D))
+
+
+def test_hierarchical_equals_prefix_form_on_power_of_two_blocks():
+    # a block whose index is a power of two has a single square, [0, b): the same key
+    # set as the prefix form, so its rows agree exactly; two blocks (the single-level
+    # instance the paper ran: one exact diagonal block and one MuSe block, [REVIEW]
+    # "free parameters") agree everywhere
+    q, k, v = _hier_inputs(40)
+    a = muse_causal(q, k, v, 4, 8, 2, block=64)
+    b = muse_causal(q, k, v, 4, 8, 2, block=64, hierarchical=True)
+    assert np.array_equal(a.o, b.o) and np.array_equal(a.lse, b.lse)
+    a = muse_causal(q, k, v, 4, 8, 2, block=16)
+    b = muse_causal(q, k, v, 4, 8, 2, block=16, hierarchical=True)
+    for blk in (0, 1, 2, 4):
+        r = slice(16 * blk, 16 * (blk + 1))
+        assert np.array_equal(a.o[r], b.o[r])
+    # blocks with two or more squares are split into finer summaries: they differ
+    for blk in (3, 5, 6, 7):
+        r = slice(16 * blk, 16 * (blk + 1))
+        assert rel_l2(b.o[r], a.o[r]) > 1e-4
+
+
+@pytest.mark.parametrize("block", [16, 24])
+def test_hierarchical_singletons_are_exact_causal(block):
+    rng = np.random.default_rng(41)
+    N = 96
+    q, k, v = (rng.standard_normal((N, 8)) for _ in range(3))
+    r = muse_causal(q, k, v, N, N, 2, block=block, hierarchical=True)
+    o, L = exact_attention(q, k, v, causal=True)
+    assert rel_l2(r.o, o) < 1e-13 and np.max(np.abs(r.lse - L)) < 1e-12
+
+
+def test_hierarchical_degenerate_keys_are_exact_causal():
+    rng = np.random.default_rng(42)
+    base = rng.standard_normal((8, 6))
+    n = np.arange(120)
+    k = base[(n // 15 + n % 15) % 8]          # rows 15j (the strided init) hold group j
+    q = rng.standard_normal((120, 6))
+    v = rng.standard_normal((120, 6))
+    for dipole in ("tilted", "none"):
+        r = muse_causal(q, k, v, 5, 8, 2, block=24, dipole=dipole, hierarchical=True)
+        o, L = exact_attention(q, k, v, causal=True)
+        assert rel_l2(r.o, o) < 1e-12 and np.max(np.abs(r.lse - L)) < 1e-12
+
+
+def test_hierarchical_outputs_ignore_future_values():
+    q, k, v = _hier_inputs(43)
+    a = muse_causal(q, k, v, 4, 8, 2, block=16, hierarchical=True)
+    v2 = v.copy()
+    v2[75:] += 5.0
+    b = muse_causal(q, k, v2, 4, 8, 2, block=16, hierarchical=True)
+    assert np.array_equal(a.o[:75], b.o[:75])
+    assert not np.allclose(a.o[75:], b.o[75:])
+    sub = muse_causal(q, k, v, 4, 8, 2, block=16, hierarchical=True, blocks_to_eval=[5, 7])
+    assert np.array_equal(sub.o[80:96], a.o[80:96]) and np.array_equal(sub.o[112:], a.o[112:])
 
 
 # ------------------------------------------------------------ retrieval

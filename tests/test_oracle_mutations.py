@@ -92,6 +92,10 @@ MUTATIONS = [
      "loc_allowed = (np.arange(r0, r1)[None, :] < rows[:, None]) | (rows[:, None] == r0)"),
     ("causal_far_includes_own_block", "pre = slice(0, r0)", "pre = slice(0, r1)"),
     ("causal_far_skips_previous_block", "pre = slice(0, r0)", "pre = slice(0, max(r0 - block, 1))"),
+    # hierarchical causal decomposition
+    ("hier_square_reaches_diagonal", "out.append((q0, q1, lo, lo + h))", "out.append((q0, q1, lo, min(lo + w, nb)))"),
+    ("hier_upper_half_not_split", "        split(lo, h)\n        split(lo + h, h)", "        split(lo, h)"),
+    ("hier_squares_overwrite", "far[b] = lse_merge(far[b][0], far[b][1], o_s, L_s)", "far[b] = (o_s, L_s)"),
     # retrieval
     ("retrieval_smallest_first", 'order = np.argsort(-values, kind="stable")', 'order = np.argsort(values, kind="stable")'),
     ("retrieval_cluster_score_max", "sj = _lse_rows(sig)", "sj = np.max(sig, axis=1)"),
