@@ -9,7 +9,8 @@ the workspace allocated beforehand. Prints ONE JSON line: `value` is the 8k work
 tokens/s (or the chosen workload's). Extra fields: the in-library exact attention time
 on the same shape (speedup), the relative squared error of MuSe against it, per-kernel
 average durations measured with HIP events on the stream the kernels run on, the
-untilted-dipole run of an acausal workload, `measured_peaks` (a device copy and a bf16
+untilted-dipole run of an acausal workload, the hierarchical-decomposition run of a causal
+one without retrieval, `measured_peaks` (a device copy and a bf16
 GEMM on this GPU, beside the published peaks the roofline uses) and, with the default
 workload, `secondary`: the same figures for the 64k causal configuration.
 """
@@ -390,6 +391,32 @@ def measure(name: str, steps: int, warmup: int, exact: bool) -> dict:
                 "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in prof_u.items() if "untilted" in n or "cov" in n}}
             print(f"# untilted dipole: {ms_u:.3f} ms/step, speedup {ms_ex / ms_u:.2f}x, RSE {rse_u:.3e}, "
                   f"{extra['untilted_dipole']['kernels_us']}", file=sys.stderr, flush=True)
+        elif cfg.topk_clusters == 0:
+            # the same workload with the hierarchical block decomposition (one two-stage
+            # approximation per square below the diagonal, log-sum-exp merged)
+            ws_h = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, True, cfg.block,
+                                                       1 if cfg.dtype == "bf16" else 0, hierarchy=True),
+                               dtype=torch.uint8, device="cuda")
+
+            def hier_step():
+                binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=True, block=cfg.block, out=out,
+                                 workspace=ws_h, hierarchy=True)
+
+            ms_h, _ = timed(hier_step, steps, warmup)
+            binding.prof_reset()
+            binding.prof_enable(True)
+            hier_step()
+            torch.cuda.synchronize()
+            prof_h = binding.prof_collect()
+            binding.prof_enable(False)
+            o_h = out.double()
+            rse_h = float(((o_h - o_e) ** 2).sum() / (o_e ** 2).sum())
+            extra["hierarchy"] = {
+                "ms_per_step": ms_h, "value": cfg.B * cfg.N / (ms_h / 1e3), "speedup_vs_exact": ms_ex / ms_h,
+                "rse_vs_exact": rse_h,
+                "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in sorted(prof_h.items(), key=lambda kv: -kv[1][0])}}
+            print(f"# hierarchy: {ms_h:.3f} ms/step, speedup {ms_ex / ms_h:.2f}x, RSE {rse_h:.3e}, "
+                  f"{extra['hierarchy']['kernels_us']}", file=sys.stderr, flush=True)
     return {"cfg": cfg, "ms": ms, "wall": wall, "value": value, "kernels": kernels, "roofline": roofline,
             "extra": extra, "host_inputs": (q, k, v)}
 

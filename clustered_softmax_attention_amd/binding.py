@@ -52,6 +52,7 @@ class FwdParams(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("retrieval_trace", ctypes.c_void_p),
+        ("hierarchy", ctypes.c_int),
     ]
 
 
@@ -154,7 +155,7 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
              out: Optional[torch.Tensor] = None, *, scale: float = 0.0, out_dtype=None, dipole=True,
              topk_clusters: int = 0, topk_blocks: int = 0, labels_q_in=None, labels_k_in=None,
              return_trace: bool = False, return_centroids: bool = False, return_lse: bool = False,
-             workspace: Optional[torch.Tensor] = None):
+             workspace: Optional[torch.Tensor] = None, hierarchy: bool = False):
     """muse_attn_fwd_ex. Returns out, or (out, extras) when any return_* flag is set, where
     extras holds 'labels_q_trace', 'labels_k_trace' [iters,B,H,N] int32, 'centroids_q',
     'centroids_k' [B,H,C,D] float32, 'lse' [B,H,N] float32 and, with retrieval,
@@ -174,6 +175,7 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
     p.dipole = dipole_code(dipole)
     p.topk_clusters = int(topk_clusters)
     p.topk_blocks = int(topk_blocks)
+    p.hierarchy = int(hierarchy)
     extras = {}
     keep = []
     for name, lab in (("labels_q_in", labels_q_in), ("labels_k_in", labels_k_in)):
@@ -225,12 +227,13 @@ def prof_collect() -> dict:
 
 
 def workspace_bytes(B, H, N, D, Cq, Ck, causal=False, block=0, dtype=MUSE_BF16, topk_clusters=0,
-                    topk_blocks=0, dipole=True) -> int:
+                    topk_blocks=0, dipole=True, hierarchy=False) -> int:
     lib = load()
     p = FwdParams()
     lib.muse_fwd_params_init(ctypes.byref(p))
     p.topk_clusters, p.topk_blocks = topk_clusters, topk_blocks
     p.dipole = dipole_code(dipole)
+    p.hierarchy = int(hierarchy)
     n = lib.muse_attn_fwd_workspace_bytes(B, H, N, D, Cq, Ck, int(causal), int(block), dtype, ctypes.byref(p))
     if n == 0:
         raise MuseError(-1, lib.muse_last_error().decode())

@@ -111,6 +111,10 @@ int validate(Shape& s, const muse_fwd_params* p) {
     if (p->topk_clusters > 0 && p->topk_blocks < 1) return fail(MUSE_ERR_INVALID_ARG, "retrieval needs topk_blocks >= 1");
     if (p->topk_clusters > 0 && p->topk_clusters * (1 + p->topk_blocks) > muse::kMaxRetrRow)
       return fail(MUSE_ERR_UNSUPPORTED, "topk_clusters * (1 + topk_blocks) must be at most %d", muse::kMaxRetrRow);
+    if (p->hierarchy != 0 && p->hierarchy != 1) return fail(MUSE_ERR_INVALID_ARG, "hierarchy must be 0 or 1");
+    if (p->hierarchy && !s.causal) return fail(MUSE_ERR_INVALID_ARG, "the hierarchical decomposition requires causal=1");
+    if (p->hierarchy && p->topk_clusters > 0)
+      return fail(MUSE_ERR_UNSUPPORTED, "retrieval is not combined with the hierarchical decomposition");
     if (p->topk_clusters > 0 && s.nb > muse::kMaxRetrBlocks)
       return fail(MUSE_ERR_UNSUPPORTED, "retrieval supports at most %d blocks", muse::kMaxRetrBlocks);
   }
@@ -314,6 +318,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.nbS = s.nbS;
   a1.scale = scale;
   a1.dipole = dipole;
+  a1.hier = (p != nullptr && p->hierarchy) ? 1 : 0;
   a1.qbar = tq.cent;
   a1.perm_k = tk.perm;
   a1.offs_k = tk.offs;
@@ -399,6 +404,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a2.nbS = s.nbS;
   a2.scale = scale;
   a2.dipole = dipole;
+  a2.hier = a1.hier;
   a2.out_bf16 = out_is_bf16(s, p);
   a2.labels_q = tq.labels;
   a2.qbar = tq.cent;
@@ -581,7 +587,7 @@ void muse_fwd_params_init(muse_fwd_params* p) {
 
 const char* muse_last_error(void) { return g_last_error.c_str(); }
 
-int muse_version(void) { return 100; }
+int muse_version(void) { return 101; }
 
 size_t muse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int Cq, int Ck, int causal, int block,
                                      int dtype, const muse_fwd_params* p) {

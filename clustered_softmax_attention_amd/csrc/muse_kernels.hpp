@@ -110,6 +110,8 @@ struct S1Args {
   int nbS;                     // table entries: nb when causal, 1 when acausal
   float scale;
   int dipole;                  // 0 none, 1 tilted, 2 untilted (acausal only)
+  int hier;                    // causal: table entry e covers key blocks [e - lowbit(e), e)
+                               // (hierarchical squares) instead of [0, e)
   const float* qbar;           // [BH, Cq, D] query centroids
   const int32_t* perm_k;       // [BH, N] keys by (block, label)
   const int32_t* offs_k;       // [BH, nb*Ck + 1]
@@ -161,6 +163,7 @@ struct S2Args {
   int causal, block, nbS;
   float scale;
   int dipole;
+  int hier;                    // causal: merge the entries b, b & (b - 1), ... > 0
   int out_bf16;
   const int32_t* labels_q;     // [BH, N]
   const float* qbar;           // [BH, Cq, D]

@@ -19,6 +19,9 @@
 //   s1_moments    one workgroup per (i, b', head): block-normalised sum w v k^T.
 //   s1_prefix     fold of atoms over blocks -> log Z, K, V tables.
 //   s1_mom_prefix fold of block moments over blocks -> E_i[v k^T] per table entry.
+//                 Causal entry e covers blocks [0, e), or with the hierarchical
+//                 decomposition the square's key blocks [e - lowbit(e), e) (pith.science
+//                 review, Figure 2 caption: MuSe on the squares below the diagonal).
 //   s1_dip_final  D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T (value index first).
 //   s1_cluster_cov, s1_untilted_dip  the untilted dipole (acausal): per key cluster
 //                 covariance Cov_j, then D_i = sum_j P_ij Cov_j.
@@ -240,8 +243,7 @@ __global__ void s1_prefix_kernel(S1Args a) {
     float* dst = isK ? a.s_k : a.s_v;
     dst[sidx * D + d] = any ? racc / rz : 0.f;
   };
-  for (int b = 0; b < a.nb; ++b) {
-    if (a.causal) emit(b);  // entry b: blocks < b
+  auto add = [&](int b) {
     const size_t aidx = ((static_cast<size_t>(bh) * a.nb + b) * Cq + i) * Ck + j;
     const float m = a.at_m[aidx], z = a.at_z[aidx];
     if (z > 0.f) {
@@ -253,6 +255,21 @@ __global__ void s1_prefix_kernel(S1Args a) {
       racc = racc * f0 + x * f1;
       rm = nm;
     }
+  };
+  if (a.causal && a.hier) {
+    // entry e: the square's key blocks [e - lowbit(e), e) (entry 0 stays empty)
+    for (int e = 0; e < a.nb; ++e) {
+      rm = kNegInf;
+      rz = 0.f;
+      racc = 0.f;
+      for (int b = e - (e & -e); b < e; ++b) add(b);
+      emit(e);
+    }
+    return;
+  }
+  for (int b = 0; b < a.nb; ++b) {
+    if (a.causal) emit(b);  // entry b: blocks < b
+    add(b);
   }
   if (!a.causal) emit(0);
 }
@@ -270,8 +287,7 @@ __global__ void s1_mom_prefix_kernel(S1Args a) {
     const size_t sbase = ((static_cast<size_t>(bh) * a.nbS + b) * Cq + i) * D * D;
     a.s_dip[sbase + e] = (rR == kNegInf) ? 0.f : racc;  // [dv][dk]
   };
-  for (int mb = 0; mb < a.nmb; ++mb) {
-    if (a.causal && mb % per_block == 0) emit(mb / per_block);
+  auto add = [&](int mb) {
     const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
     const float R = a.blk_lmass[bidx];
     if (R != kNegInf) {
@@ -282,6 +298,20 @@ __global__ void s1_mom_prefix_kernel(S1Args a) {
       racc = racc * f0 + x * f1;
       rR = nR;
     }
+  };
+  if (a.causal && a.hier) {
+    // entry b: the sub-blocks of the square's key blocks [b - lowbit(b), b)
+    for (int b = 0; b < a.nb; ++b) {
+      rR = kNegInf;
+      racc = 0.f;
+      for (int mb = (b - (b & -b)) * per_block; mb < b * per_block; ++mb) add(mb);
+      emit(b);
+    }
+    return;
+  }
+  for (int mb = 0; mb < a.nmb; ++mb) {
+    if (a.causal && mb % per_block == 0) emit(mb / per_block);
+    add(mb);
   }
   if (!a.causal) emit(0);
 }
@@ -597,9 +627,10 @@ template <typename T, int D>
 static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   constexpr int kS1Keys = S1Keys<D>::value;
   const bool mf = sizeof(T) == 2;  // bf16 inputs: matrix-core kernels
-  if (mf && a.retr == nullptr) {
+  if (mf && a.retr == nullptr && !a.hier) {
     // acausal: one table entry per (head, i), finalised in a single pass; causal without
-    // retrieval: one scan over the blocks writes every entry. The atoms (with their
+    // retrieval: one scan over the blocks writes every entry (the hierarchical squares
+    // take the general path below: per entry folds of the merged atoms and moments). The atoms (with their
     // merge) go to the side stream, forked from and joined back into the caller's stream
     // by events; without a side stream or events everything runs on the caller's stream.
     hipStream_t side = side_stream();

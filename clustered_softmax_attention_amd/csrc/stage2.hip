@@ -14,6 +14,10 @@
 // fp32 inputs (s2_refine): one thread per query; the residual is kept in registers for
 // the logits and in LDS (lane-major) for the dipole product, whose table is stored key
 // index first so that a row of D_i^T is contiguous.
+// With the hierarchical decomposition (pith.science review, Figure 2 caption) a query of
+// block b sees the entries e = b, b & (b - 1), ... > 0, one per square below the
+// diagonal; their (o, L) are merged by log-sum-exp, L = log(e^L1 + e^L2),
+// o = e^(L1 - L) o1 + e^(L2 - L) o2.
 #include "mfma.hpp"
 #include "muse_kernels.hpp"
 
@@ -47,63 +51,75 @@ __global__ void __launch_bounds__(kS2Threads) s2_refine_kernel(S2Args a) {
     qt[d] = Elem<T>::load(Q, row * D + d) - qb[d];
     s_q[d][tid] = qt[d];
   }
-  const int e = a.causal ? b : 0;
-  const size_t sidx = (static_cast<size_t>(bh) * a.nbS + e) * a.Cq + i;
-  const float* lz = a.s_logz + sidx * a.Ck;
-  const float* Kt = a.s_k + sidx * a.Ck * D;
-  const float* Vt = a.s_v + sidx * a.Ck * D;
+  int e = a.causal ? b : 0;
+  for (bool first = true;; first = false) {
+    const size_t sidx = (static_cast<size_t>(bh) * a.nbS + e) * a.Cq + i;
+    const float* lz = a.s_logz + sidx * a.Ck;
+    const float* Kt = a.s_k + sidx * a.Ck * D;
+    const float* Vt = a.s_v + sidx * a.Ck * D;
 
-  float mx = kNegInf;
-  for (int j = 0; j < a.Ck; ++j) {
-    const float l0 = lz[j];
-    if (l0 == kNegInf) continue;
-    float dot = 0.f;
-#pragma unroll
-    for (int d = 0; d < D; ++d) dot = fmaf(qt[d], Kt[j * D + d], dot);
-    mx = fmaxf(mx, l0 + a.scale * dot);
-  }
-  float acc[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) acc[d] = 0.f;
-  float z = 0.f;
-  for (int j = 0; j < a.Ck; ++j) {
-    const float l0 = lz[j];
-    if (l0 == kNegInf) continue;
-    float dot = 0.f;
-#pragma unroll
-    for (int d = 0; d < D; ++d) dot = fmaf(qt[d], Kt[j * D + d], dot);
-    const float p = __expf(l0 + a.scale * dot - mx);
-    z += p;
-#pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] = fmaf(p, Vt[j * D + d], acc[d]);
-  }
-  const bool empty = !(z > 0.f);  // no far-field key at all
-  const float inv = empty ? 0.f : 1.f / z;
-#pragma unroll
-  for (int d = 0; d < D; ++d) acc[d] *= inv;
-  if (a.dipole && !empty) {
-    const float* dip = a.s_dip + sidx * D * D;  // [dv][dk]
-    for (int dk = 0; dk < D; ++dk) {
-      const float x = a.scale * s_q[dk][tid];
-#pragma unroll
-      for (int dv = 0; dv < D; ++dv) acc[dv] = fmaf(dip[dv * D + dk], x, acc[dv]);
+    float mx = kNegInf;
+    for (int j = 0; j < a.Ck; ++j) {
+      const float l0 = lz[j];
+      if (l0 == kNegInf) continue;
+      float dot = 0.f;
+  #pragma unroll
+      for (int d = 0; d < D; ++d) dot = fmaf(qt[d], Kt[j * D + d], dot);
+      mx = fmaxf(mx, l0 + a.scale * dot);
     }
-  }
-  const float L = empty ? kNegInf : mx + __logf(z);
-  if (!valid) return;
-  if (a.causal) {
-    a.l_far[row] = L;
-#pragma unroll
-    for (int d = 0; d < D; ++d) a.o_far[row * D + d] = acc[d];
-  } else {
-    if (a.lse_out) a.lse_out[row] = L;
-    if (a.out_bf16) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) static_cast<bf16*>(a.out)[row * D + d].bits = f32_to_bf16_bits(acc[d]);
+    float acc[D];
+  #pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = 0.f;
+    float z = 0.f;
+    for (int j = 0; j < a.Ck; ++j) {
+      const float l0 = lz[j];
+      if (l0 == kNegInf) continue;
+      float dot = 0.f;
+  #pragma unroll
+      for (int d = 0; d < D; ++d) dot = fmaf(qt[d], Kt[j * D + d], dot);
+      const float p = __expf(l0 + a.scale * dot - mx);
+      z += p;
+  #pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, Vt[j * D + d], acc[d]);
+    }
+    const bool empty = !(z > 0.f);  // no far-field key at all
+    const float inv = empty ? 0.f : 1.f / z;
+  #pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] *= inv;
+    if (a.dipole && !empty) {
+      const float* dip = a.s_dip + sidx * D * D;  // [dv][dk]
+      for (int dk = 0; dk < D; ++dk) {
+        const float x = a.scale * s_q[dk][tid];
+  #pragma unroll
+        for (int dv = 0; dv < D; ++dv) acc[dv] = fmaf(dip[dv * D + dk], x, acc[dv]);
+      }
+    }
+    const float L = empty ? kNegInf : mx + __logf(z);
+    if (!valid) return;
+    if (a.causal && !first) {
+      // a further square: merge into the far field written so far (this thread's row)
+      const float L0 = a.l_far[row];
+      const float Ln = L0 == kNegInf ? L : (L == kNegInf ? L0 : fmaxf(L0, L) + log1pf(__expf(-fabsf(L0 - L))));
+      const float w0 = L0 == kNegInf ? 0.f : __expf(L0 - Ln), w1 = L == kNegInf ? 0.f : __expf(L - Ln);
+      a.l_far[row] = Ln;
+  #pragma unroll
+      for (int d = 0; d < D; ++d) a.o_far[row * D + d] = w0 * a.o_far[row * D + d] + w1 * acc[d];
+    } else if (a.causal) {
+      a.l_far[row] = L;
+  #pragma unroll
+      for (int d = 0; d < D; ++d) a.o_far[row * D + d] = acc[d];
     } else {
-#pragma unroll
-      for (int d = 0; d < D; ++d) static_cast<float*>(a.out)[row * D + d] = acc[d];
+      if (a.lse_out) a.lse_out[row] = L;
+      if (a.out_bf16) {
+  #pragma unroll
+        for (int d = 0; d < D; ++d) static_cast<bf16*>(a.out)[row * D + d].bits = f32_to_bf16_bits(acc[d]);
+      } else {
+  #pragma unroll
+        for (int d = 0; d < D; ++d) static_cast<float*>(a.out)[row * D + d] = acc[d];
+      }
     }
+    e = a.hier ? (e & (e - 1)) : 0;
+    if (e == 0) break;
   }
 }
 
@@ -123,7 +139,9 @@ struct S2Cfg {
   static constexpr int ND = D * D / 8 / 256;    // 16-byte dipole pieces per thread
 };
 
-template <int D>
+// HIER: the hierarchical squares (entries b, b & (b - 1), ...); each further square is
+// merged into the far field already written (o_far, l_far: this lane's own elements).
+template <int D, bool HIER>
 __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a) {
   using Cfg = S2Cfg<D>;
   constexpr int NKS = D / 16, NMT = D / 32, JC = Cfg::JC, KST = Cfg::KST, DST = Cfg::DST;
@@ -162,14 +180,22 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
     }
     return;
   }
-  const int e = a.causal ? b : 0;
-  const size_t sidx = (static_cast<size_t>(bh) * a.nbS + e) * a.Cq + i;
+  // table entries: e = b (one entry; acausal: 0), or with the hierarchy the squares
+  // e = b, b & (b - 1), ... > 0, merged by log-sum-exp in that order
+  int e = a.causal ? b : 0;
   const int Ck = a.Ck, njc = (Ck + JC - 1) / JC;
-  const uint16_t* khi = a.t_khi + sidx * Ck * D;
-  const uint16_t* klo = a.t_klo + sidx * Ck * D;
-  const uint16_t* vhi = a.t_vhi + sidx * Ck * D;
-  const uint16_t* vlo = a.t_vlo + sidx * Ck * D;
-  const float* lz = a.s_logz + sidx * Ck;
+  const uint16_t *khi, *klo, *vhi, *vlo, *dip;
+  const float* lz;
+  auto set_entry = [&](int ee) {
+    const size_t sidx = (static_cast<size_t>(bh) * a.nbS + ee) * a.Cq + i;
+    khi = a.t_khi + sidx * Ck * D;
+    klo = a.t_klo + sidx * Ck * D;
+    vhi = a.t_vhi + sidx * Ck * D;
+    vlo = a.t_vlo + sidx * Ck * D;
+    dip = a.t_dip + sidx * D * D;
+    lz = a.s_logz + sidx * Ck;
+  };
+  set_entry(e);
 
   // chunk jc of the tables into registers
   u16x8_t pkh[NK], pkl[NK], pvh[NK], pvl[NK];
@@ -193,16 +219,27 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
     }
     plz = (tid < JC && j0 + tid < Ck) ? lz[j0 + tid] : kNegInf;
   };
-  load_chunk(0);
   u16x8_t pd[ND];
-  const uint16_t* dip = a.t_dip + sidx * D * D;
-  if (a.dipole) {
+  auto load_dip = [&]() {
+    if (a.dipole) {
 #pragma unroll
-    for (int q = 0; q < ND; ++q) {
-      const int x = tid + 256 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
-      pd[q] = *reinterpret_cast<const u16x8_t*>(dip + static_cast<size_t>(r) * D + c8);
+      for (int q = 0; q < ND; ++q) {
+        const int x = tid + 256 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
+        pd[q] = *reinterpret_cast<const u16x8_t*>(dip + static_cast<size_t>(r) * D + c8);
+      }
     }
-  }
+  };
+  auto store_dip = [&]() {
+    if (a.dipole) {
+#pragma unroll
+      for (int q = 0; q < ND; ++q) {
+        const int x = tid + 256 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
+        *reinterpret_cast<u16x8_t*>(sDip + r * DST + c8) = pd[q];
+      }
+    }
+  };
+  load_chunk(0);
+  load_dip();
 
   // residual query fragments (B operand: column = query c, k = d); the rows are requested
   // before any of the loads above is waited for
@@ -211,13 +248,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
   u16x8_t qr[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) qr[ks] = *reinterpret_cast<const u16x8_t*>(Q + row * D + 16 * ks + 8 * h);
-  if (a.dipole) {
-#pragma unroll
-    for (int q = 0; q < ND; ++q) {
-      const int x = tid + 256 * q, r = x / (D / 8), c8 = (x % (D / 8)) * 8;
-      *reinterpret_cast<u16x8_t*>(sDip + r * DST + c8) = pd[q];
-    }
-  }
+  store_dip();
   bf16x8_t qhi[NKS], qlo[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
@@ -229,128 +260,159 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
   }
 
   const float sl2 = a.scale * 1.4426950408889634f;
-  float mx = kNegInf, z = 0.f;  // running max (log2 units) and sum of this lane pair's query
-  f32x16_t o[NMT];
+  float Lf = kNegInf;  // log-mass of the far field merged so far (this lane's query)
+  for (bool first = true;; first = false) {
+    float mx = kNegInf, z = 0.f;  // running max (log2 units) and sum of this lane pair's query
+    f32x16_t o[NMT];
 #pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) o[mt] = zero16();
-  for (int jc = 0; jc < njc; ++jc) {
-    __syncthreads();  // previous chunk consumed
+    for (int mt = 0; mt < NMT; ++mt) o[mt] = zero16();
+    for (int jc = 0; jc < njc; ++jc) {
+      __syncthreads();  // previous chunk consumed
 #pragma unroll
-    for (int q = 0; q < NK; ++q) {
-      const int x = tid + 256 * q, jj = x / (D / 8), d8 = (x % (D / 8)) * 8;
-      *reinterpret_cast<u16x8_t*>(sKh + jj * KST + d8) = pkh[q];
-      *reinterpret_cast<u16x8_t*>(sKl + jj * KST + d8) = pkl[q];
-      *reinterpret_cast<u16x8_t*>(sVh + jj * KST + d8) = pvh[q];
-      *reinterpret_cast<u16x8_t*>(sVl + jj * KST + d8) = pvl[q];
-    }
-    if (tid < JC) slz[tid] = plz;
-    __syncthreads();
-    if (jc + 1 < njc) load_chunk(jc + 1);
-    if (nw == 0) continue;
-    // logits^T of the chunk (rows j, column = query), log2 units
-    f32x16_t lg = zero16();
+      for (int q = 0; q < NK; ++q) {
+        const int x = tid + 256 * q, jj = x / (D / 8), d8 = (x % (D / 8)) * 8;
+        *reinterpret_cast<u16x8_t*>(sKh + jj * KST + d8) = pkh[q];
+        *reinterpret_cast<u16x8_t*>(sKl + jj * KST + d8) = pkl[q];
+        *reinterpret_cast<u16x8_t*>(sVh + jj * KST + d8) = pvh[q];
+        *reinterpret_cast<u16x8_t*>(sVl + jj * KST + d8) = pvl[q];
+      }
+      if (tid < JC) slz[tid] = plz;
+      __syncthreads();
+      if (jc + 1 < njc) load_chunk(jc + 1);
+      if (nw == 0) continue;
+      // logits^T of the chunk (rows j, column = query), log2 units
+      f32x16_t lg = zero16();
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sKh + c * KST + 16 * ks + 8 * h));
-      const bf16x8_t al = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sKl + c * KST + 16 * ks + 8 * h));
-      lg = mfma32(ah, qhi[ks], lg);
-      lg = mfma32(ah, qlo[ks], lg);
-      lg = mfma32(al, qhi[ks], lg);
-    }
-    float cm = kNegInf;
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8_t ah = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sKh + c * KST + 16 * ks + 8 * h));
+        const bf16x8_t al = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sKl + c * KST + 16 * ks + 8 * h));
+        lg = mfma32(ah, qhi[ks], lg);
+        lg = mfma32(ah, qlo[ks], lg);
+        lg = mfma32(al, qhi[ks], lg);
+      }
+      float cm = kNegInf;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(slz + 8 * g + 4 * h);
+      for (int g = 0; g < 4; ++g) {
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(slz + 8 * g + 4 * h);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float l0 = l4[r];
-        const float x = l0 == kNegInf ? kNegInf : l0 * 1.4426950408889634f + sl2 * lg[4 * g + r];
-        lg[4 * g + r] = x;
-        cm = fmaxf(cm, x);
+        for (int r = 0; r < 4; ++r) {
+          const float l0 = l4[r];
+          const float x = l0 == kNegInf ? kNegInf : l0 * 1.4426950408889634f + sl2 * lg[4 * g + r];
+          lg[4 * g + r] = x;
+          cm = fmaxf(cm, x);
+        }
+      }
+      cm = fmaxf(cm, xor32(cm));
+      const float mn = fmaxf(mx, cm);
+      if (mn == kNegInf) continue;  // no key cluster yet: nothing to add (same for the lane pair)
+      const float alpha = mx == kNegInf ? 0.f : fast_exp2(mx - mn);
+      // the sums need rescaling only when a lane's running max grew and it had summed before
+      const bool grow = mn > mx && mx != kNegInf;
+      mx = mn;
+      float zs = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(lg[v] - mn);
+        lg[v] = p;
+        zs += p;
+      }
+      z = z * alpha + zs + xor32(zs);
+      if (__ballot(grow) != 0ull) {
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+      }
+      // O^T += V^T P^T (split): k-slots of step ss are rows 16 ss + 4 h + 0..3 and 16 ss + 8 + 4 h + 0..3
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        float pv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) pv[r] = lg[8 * ss + r];
+        bf16x8_t phi, plo;
+        split_bf16x8(pv, phi, plo);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          const bf16x8_t hv = lds_operand_tr_acc(sVh, KST, 16 * ss, 32 * mt, lane);
+          const bf16x8_t lv = lds_operand_tr_acc(sVl, KST, 16 * ss, 32 * mt, lane);
+          o[mt] = mfma32(hv, phi, o[mt]);
+          o[mt] = mfma32(hv, plo, o[mt]);
+          o[mt] = mfma32(lv, phi, o[mt]);
+        }
       }
     }
-    cm = fmaxf(cm, xor32(cm));
-    const float mn = fmaxf(mx, cm);
-    if (mn == kNegInf) continue;  // no key cluster yet: nothing to add (same for the lane pair)
-    const float alpha = mx == kNegInf ? 0.f : fast_exp2(mx - mn);
-    // the sums need rescaling only when a lane's running max grew and it had summed before
-    const bool grow = mn > mx && mx != kNegInf;
-    mx = mn;
-    float zs = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = fast_exp2(lg[v] - mn);
-      lg[v] = p;
-      zs += p;
+    // the next square's first chunk and dipole travel while this one is finished
+    const int enext = HIER ? (e & (e - 1)) : 0;
+    if (enext > 0) {
+      set_entry(enext);
+      load_chunk(0);
+      load_dip();
     }
-    z = z * alpha + zs + xor32(zs);
-    if (__ballot(grow) != 0ull) {
+    if (nw > 0) {
+      const float invz = z > 0.f ? 1.f / z : 0.f;  // z == 0: no far-field key at all
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
-    }
-    // O^T += V^T P^T (split): k-slots of step ss are rows 16 ss + 4 h + 0..3 and 16 ss + 8 + 4 h + 0..3
+        for (int v = 0; v < 16; ++v) o[mt][v] *= invz;
+      if (a.dipole) {
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      float pv[8];
+        for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 8; ++r) pv[r] = lg[8 * ss + r];
-      bf16x8_t phi, plo;
-      split_bf16x8(pv, phi, plo);
+          for (int ks = 0; ks < NKS; ++ks) {
+            const u16x8_t ad = *reinterpret_cast<const u16x8_t*>(sDip + (32 * mt + c) * DST + 16 * ks + 8 * h);
+            o[mt] = mfma32(as_bf16x8(ad), qhi[ks], o[mt]);
+          }
+      }
+      float L = z > 0.f ? (mx + __log2f(z)) * 0.6931471805599453f : kNegInf;
+      // lanes (c, h) hold rows d = 32 mt + 8 g + 4 h + r of query c
+      if (valid && !first) {
+        // log-sum-exp merge of this square into the far field written so far (each lane
+        // reads back only the elements it wrote itself)
+        const float L0 = Lf;
+        const float Ln = L0 == kNegInf ? L : (L == kNegInf ? L0 : fmaxf(L0, L) + log1pf(__expf(-fabsf(L0 - L))));
+        const float w0 = L0 == kNegInf ? 0.f : __expf(L0 - Ln), w1 = L == kNegInf ? 0.f : __expf(L - Ln);
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        const bf16x8_t hv = lds_operand_tr_acc(sVh, KST, 16 * ss, 32 * mt, lane);
-        const bf16x8_t lv = lds_operand_tr_acc(sVl, KST, 16 * ss, 32 * mt, lane);
-        o[mt] = mfma32(hv, phi, o[mt]);
-        o[mt] = mfma32(hv, plo, o[mt]);
-        o[mt] = mfma32(lv, phi, o[mt]);
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4_t f = *reinterpret_cast<const f32x4_t*>(a.o_far + row * D + 32 * mt + 8 * g + 4 * h);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[mt][4 * g + r] = w0 * f[r] + w1 * o[mt][4 * g + r];
+          }
+        L = Ln;
+      }
+      Lf = L;
+      if (valid && a.causal) {
+        if (h == 0) a.l_far[row] = L;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4_t f = {o[mt][4 * g], o[mt][4 * g + 1], o[mt][4 * g + 2], o[mt][4 * g + 3]};
+            *reinterpret_cast<f32x4_t*>(a.o_far + row * D + 32 * mt + 8 * g + 4 * h) = f;
+          }
+      } else if (valid) {
+        if (a.lse_out != nullptr && h == 0) a.lse_out[row] = L;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * mt + 8 * g + 4 * h;
+            if (a.out_bf16) {
+              const u16x4_t u4 = {f32_to_bf16_bits(o[mt][4 * g]), f32_to_bf16_bits(o[mt][4 * g + 1]),
+                                  f32_to_bf16_bits(o[mt][4 * g + 2]), f32_to_bf16_bits(o[mt][4 * g + 3])};
+              *reinterpret_cast<u16x4_t*>(static_cast<uint16_t*>(a.out) + row * D + d0) = u4;
+            } else {
+              const f32x4_t f = {o[mt][4 * g], o[mt][4 * g + 1], o[mt][4 * g + 2], o[mt][4 * g + 3]};
+              *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + row * D + d0) = f;
+            }
+          }
       }
     }
-  }
-  if (nw == 0) return;
-  const float invz = z > 0.f ? 1.f / z : 0.f;  // z == 0: no far-field key at all
-#pragma unroll
-  for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[mt][v] *= invz;
-  if (a.dipole) {
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const u16x8_t ad = *reinterpret_cast<const u16x8_t*>(sDip + (32 * mt + c) * DST + 16 * ks + 8 * h);
-        o[mt] = mfma32(as_bf16x8(ad), qhi[ks], o[mt]);
-      }
-  }
-  // lanes (c, h) hold rows d = 32 mt + 8 g + 4 h + r of query c
-  if (!valid) return;
-  const float L = z > 0.f ? (mx + __log2f(z)) * 0.6931471805599453f : kNegInf;
-  if (a.causal) {
-    if (h == 0) a.l_far[row] = L;
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4_t f = {o[mt][4 * g], o[mt][4 * g + 1], o[mt][4 * g + 2], o[mt][4 * g + 3]};
-        *reinterpret_cast<f32x4_t*>(a.o_far + row * D + 32 * mt + 8 * g + 4 * h) = f;
-      }
-  } else {
-    if (a.lse_out != nullptr && h == 0) a.lse_out[row] = L;
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * mt + 8 * g + 4 * h;
-        if (a.out_bf16) {
-          const u16x4_t u4 = {f32_to_bf16_bits(o[mt][4 * g]), f32_to_bf16_bits(o[mt][4 * g + 1]),
-                              f32_to_bf16_bits(o[mt][4 * g + 2]), f32_to_bf16_bits(o[mt][4 * g + 3])};
-          *reinterpret_cast<u16x4_t*>(static_cast<uint16_t*>(a.out) + row * D + d0) = u4;
-        } else {
-          const f32x4_t f = {o[mt][4 * g], o[mt][4 * g + 1], o[mt][4 * g + 2], o[mt][4 * g + 3]};
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + row * D + d0) = f;
-        }
-      }
+    if (enext == 0) break;
+    e = enext;
+    __syncthreads();  // every wave has read this square's dipole
+    store_dip();
   }
 }
 
@@ -358,8 +420,13 @@ hipError_t launch_stage2(const S2Args& a, int dtype, hipStream_t s) {
   if (dtype == 1) {
     ProfScope ps_("s2_mfma", s);
     const dim3 gm(a.max_tiles, a.BH);
-    if (a.D == 64) hipLaunchKernelGGL((s2_mfma_kernel<64>), gm, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((s2_mfma_kernel<128>), gm, dim3(256), 0, s, a);
+    if (a.D == 64) {
+      if (a.hier) hipLaunchKernelGGL((s2_mfma_kernel<64, true>), gm, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((s2_mfma_kernel<64, false>), gm, dim3(256), 0, s, a);
+    } else {
+      if (a.hier) hipLaunchKernelGGL((s2_mfma_kernel<128, true>), gm, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((s2_mfma_kernel<128, false>), gm, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
   }
   const dim3 g((a.N + kS2Threads - 1) / kS2Threads, a.BH);

@@ -124,9 +124,24 @@ typedef struct muse_fwd_params {
   int32_t* retrieval_trace;    /* device [B,H,N/block,Cq,k1*(1+k2)]: per (block, query
                                   cluster) the k1 chosen key clusters, each followed by
                                   its k2 chosen earlier blocks; -1 = none (block 0: all -1) */
+  int hierarchy;               /* causal far field. 0 (default): one two-stage approximation
+                                  over all keys of the earlier blocks (summaries accumulated
+                                  block by block; gist.science, Kernmechanismen 3). 1: the
+                                  hierarchical block decomposition (pith.science review,
+                                  Figure 2 caption and "invented entities": exact diagonal
+                                  blocks, MuSe on the squares below the diagonal, N C D log N):
+                                  the block grid, padded to a power of two, is split
+                                  recursively into two diagonal halves and the square below
+                                  the diagonal; block b >= 1 sees the earlier keys through
+                                  popcount(b) squares, the one covering key blocks
+                                  [e - lowbit(e), e) for e = b, b & (b - 1), ... > 0, each a
+                                  two-stage approximation over its own keys (clusters fitted
+                                  once per head), merged by log-sum-exp. Needs causal = 1
+                                  (else MUSE_ERR_INVALID_ARG); not combined with retrieval
+                                  (MUSE_ERR_UNSUPPORTED)                                    */
 } muse_fwd_params;
 
-/* Defaults: scale 0, out_dtype -1, dipole tilted, retrieval off, all pointers NULL. */
+/* Defaults: scale 0, out_dtype -1, dipole tilted, retrieval off, hierarchy 0, all pointers NULL. */
 void muse_fwd_params_init(muse_fwd_params* p);
 
 /* muse_attn_fwd with optional controls; p == NULL means defaults. With fixed

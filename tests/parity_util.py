@@ -45,7 +45,7 @@ class HeadCheck:
 
 
 def run_gpu(cfg: WorkloadConfig, q, k, v, out_dtype=torch.float32, dipole=True, labels_q_in=None,
-            labels_k_in=None, topk=None):
+            labels_k_in=None, topk=None, hierarchy=False):
     if topk is None:
         topk = (cfg.topk_clusters, cfg.topk_blocks)
     from clustered_softmax_attention_amd import attn_fwd
@@ -53,14 +53,14 @@ def run_gpu(cfg: WorkloadConfig, q, k, v, out_dtype=torch.float32, dipole=True, 
     out, ex = attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=cfg.causal, block=cfg.block,
                        out_dtype=out_dtype, dipole=dipole, return_trace=True, return_lse=True,
                        labels_q_in=labels_q_in, labels_k_in=labels_k_in,
-                       topk_clusters=topk[0], topk_blocks=topk[1])
+                       topk_clusters=topk[0], topk_blocks=topk[1], hierarchy=hierarchy)
     torch.cuda.synchronize()
     return out, ex
 
 
 def oracle_head(cfg: WorkloadConfig, q, k, v, trace_q, trace_k, dipole="tilted",
                 blocks: Optional[Sequence[int]] = None, rows: Optional[np.ndarray] = None,
-                retrieval_trace: Optional[np.ndarray] = None):
+                retrieval_trace: Optional[np.ndarray] = None, hierarchy: bool = False):
     """Oracle of one head in follow mode (near-tie labels adopted from the GPU traces)."""
     kq = lloyd_kmeans(q, cfg.Cq, cfg.iters, follow_trace=trace_q)
     kk = lloyd_kmeans(k, cfg.Ck, cfg.iters, follow_trace=trace_k)
@@ -70,7 +70,7 @@ def oracle_head(cfg: WorkloadConfig, q, k, v, trace_q, trace_k, dipole="tilted",
         r = muse_causal(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, cfg.block, dipole=dipole,
                         topk_clusters=cfg.topk_clusters, topk_blocks=cfg.topk_blocks,
                         labels_q=kq.labels, labels_k=kk.labels, blocks_to_eval=blocks,
-                        retrieval_follow=retrieval_trace)
+                        retrieval_follow=retrieval_trace, hierarchical=hierarchy)
         assert r.retrieval_mismatches == 0, "retrieval selections differ beyond near-ties"
     else:
         r = muse_acausal(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, dipole=dipole,
@@ -87,11 +87,11 @@ def oracle_dipole(dipole) -> str:
 
 def check_config(cfg: WorkloadConfig, heads: List[Tuple[int, int]], tol: Optional[float] = None,
                  blocks: Optional[Sequence[int]] = None, out_dtype=torch.float32, dipole=True,
-                 rows: Optional[np.ndarray] = None) -> List[HeadCheck]:
+                 rows: Optional[np.ndarray] = None, hierarchy: bool = False) -> List[HeadCheck]:
     """Run the whole [B,H,N,D] workload on the GPU and compare the listed heads."""
     t0 = time.time()
     q, k, v = make_inputs(cfg)
-    out, ex = run_gpu(cfg, q, k, v, out_dtype=out_dtype, dipole=dipole)
+    out, ex = run_gpu(cfg, q, k, v, out_dtype=out_dtype, dipole=dipole, hierarchy=hierarchy)
     o_gpu = out.float().cpu().numpy()
     tq = ex["labels_q_trace"].cpu().numpy()
     tk = ex["labels_k_trace"].cpu().numpy()
@@ -103,7 +103,7 @@ def check_config(cfg: WorkloadConfig, heads: List[Tuple[int, int]], tol: Optiona
     for b, h in heads:
         r, kq, kk = oracle_head(cfg, q[b, h], k[b, h], v[b, h], tq[:, b, h], tk[:, b, h],
                                 dipole=oracle_dipole(dipole), blocks=blocks, rows=rows,
-                                retrieval_trace=None if rtr is None else rtr[b, h])
+                                retrieval_trace=None if rtr is None else rtr[b, h], hierarchy=hierarchy)
         assert np.array_equal(kq.labels, tq[-1, b, h]) and np.array_equal(kk.labels, tk[-1, b, h])
         sel = np.isfinite(r.o[:, 0])
         rel = rel_l2(o_gpu[b, h][sel], r.o[sel])

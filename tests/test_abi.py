@@ -52,8 +52,9 @@ def test_params_struct_layout_matches(lib):
     from clustered_softmax_attention_amd.binding import FwdParams
     p = FwdParams()
     lib.muse_fwd_params_init(ctypes.byref(p))
-    assert p.out_dtype == -1 and p.dipole == 1 and p.scale == 0.0 and p.topk_clusters == 0
-    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8 + 8  # 5 ints/floats, pad, 8 pointers, size_t, ptr
+    assert p.out_dtype == -1 and p.dipole == 1 and p.scale == 0.0 and p.topk_clusters == 0 and p.hierarchy == 0
+    # 5 ints/floats, pad, 8 pointers, size_t, pointer, int, tail pad
+    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8 + 8 + 4 + 4
 
 
 def _call(lib, **kw):
@@ -137,5 +138,14 @@ def test_ex_entry_rejects_before_launch(lib):
     causal = (vp(1), vp(2), vp(3), vp(4), 1, 1, 1024, 64, 8, 32, 5, 1, 256, 1, None)
     assert lib.muse_attn_fwd_ex(*causal, ctypes.byref(p)) == -2  # untilted dipole: acausal only
     p.dipole = 1
+    p.hierarchy = 1
+    acausal = (vp(1), vp(2), vp(3), vp(4), 1, 1, 1024, 64, 8, 32, 5, 0, 0, 1, None)
+    assert lib.muse_attn_fwd_ex(*acausal, ctypes.byref(p)) == -1  # hierarchy needs causal
+    p.topk_clusters, p.topk_blocks = 2, 1
+    assert lib.muse_attn_fwd_ex(*causal, ctypes.byref(p)) == -2  # not combined with retrieval
+    p.topk_clusters, p.topk_blocks = 0, 0
+    p.hierarchy = 2
+    assert lib.muse_attn_fwd_ex(*causal, ctypes.byref(p)) == -1  # 0 or 1
+    p.hierarchy = 0
     aliased = (vp(1), vp(2), vp(3), vp(1), 1, 1, 1024, 64, 8, 32, 5, 0, 0, 1, None)
     assert lib.muse_attn_fwd_ex(*aliased, ctypes.byref(p)) == -1  # out aliases q

@@ -140,6 +140,39 @@ def test_causal_fp32(muse_lib):
     check_config(cfg, [(0, 0), (0, 1)])
 
 
+@pytest.mark.parametrize("name,over,dipole", [
+    # 7 blocks (not a power of two: blocks 3, 5, 6 see two squares, block 6 [0,4) and [4,6))
+    ("causal_16k", {"B": 1, "H": 2, "N": 1792, "block": 256}, True),
+    # 16 blocks of 128 tokens, up to four squares per block, monopole only
+    ("causal_16k", {"B": 1, "H": 1, "N": 2048, "block": 128, "Cq": 8, "Ck": 24}, False),
+    # D = 128, 12 blocks
+    ("causal_64k_d128", {"B": 1, "H": 2, "N": 3072, "block": 256}, True),
+    # fp32 inputs, 5 blocks, cluster counts off the 32-tiles
+    ("acausal_1k_f32", {"H": 2, "N": 1280, "causal": True, "block": 256, "Cq": 7, "Ck": 29}, True),
+    # two blocks: the single-level instance (one exact diagonal block, one MuSe square)
+    ("causal_16k", {"B": 1, "H": 1, "N": 2048, "block": 1024}, True),
+])
+def test_hierarchical_causal(muse_lib, name, over, dipole):
+    # the hierarchical block decomposition: a block's far field merges one two-stage
+    # approximation per square below the diagonal (log-sum-exp), squares from the oracle's
+    # recursive split, entries e = b, b & (b - 1), ... on the GPU
+    cfg = scaled_config(name, **over)
+    check_config(cfg, [(0, 0)] if cfg.H == 1 else [(0, 0), (0, 1)], dipole=dipole, hierarchy=True)
+
+
+def test_hierarchical_refusals(muse_lib):
+    from clustered_softmax_attention_amd import binding
+    cfg = scaled_config("retrieval_16k", B=1, H=1, N=2048, block=256)
+    q, k, v = (to_device(t, cfg.dtype) for t in make_inputs(cfg))
+    with pytest.raises(binding.MuseError, match="retrieval") as err:
+        binding.attn_fwd(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, causal=True, block=cfg.block, topk_clusters=2,
+                         topk_blocks=1, hierarchy=True)
+    assert err.value.code == -2  # MUSE_ERR_UNSUPPORTED
+    with pytest.raises(binding.MuseError, match="causal") as err:
+        binding.attn_fwd(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, hierarchy=True)
+    assert err.value.code == -1  # MUSE_ERR_INVALID_ARG
+
+
 def test_retrieval_16k_shape_reduced(muse_lib):
     cfg = scaled_config("retrieval_16k", B=1, H=2, N=4096)
     check_config(cfg, [(0, 0), (0, 1)])
@@ -221,6 +254,12 @@ def test_acausal_8k_full_size_sampled_heads(muse_lib, dipole):
 def test_causal_16k_full_size_sampled_blocks(muse_lib):
     cfg = CONFIGS["causal_16k"]
     check_config(cfg, [(7, 5)], blocks=[1, 15])
+
+
+def test_causal_16k_hierarchical_full_size_sampled_blocks(muse_lib):
+    # block 15 sees four squares ([0,8), [8,12), [12,14), [14,15) in blocks), block 8 one
+    cfg = CONFIGS["causal_16k"]
+    check_config(cfg, [(5, 2)], blocks=[8, 15], hierarchy=True)
 
 
 def test_retrieval_16k_full_size_sampled_blocks(muse_lib):
