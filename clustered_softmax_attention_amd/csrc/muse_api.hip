@@ -385,6 +385,11 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
     ra.trace = p->retrieval_trace;
     ra.o_far = at<float>(ws, P.o_far);
     ra.l_far = at<float>(ws, P.l_far);
+    if (mf) {
+      ra.tiles = at<int2>(ws, P.tiles);
+      ra.ntiles = at<int32_t>(ws, P.ntiles);
+      ra.max_tiles = P.max_tiles;
+    }
     a1.retr = &ra;
   }
   e = launch_stage1(a1, s.dtype, stream);

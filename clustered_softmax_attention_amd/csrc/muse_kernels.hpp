@@ -95,6 +95,10 @@ struct RetrArgs {
   int32_t* trace;              // copy of sel for the caller, or null
   float* o_far;                // [BH, N, D] far-field partial result (merged in place)
   float* l_far;                // [BH, N]
+  // matrix-core exact part (bf16 inputs): the stage-2 query chunks
+  const int2* tiles;           // [BH, max_tiles] (bucket, first position)
+  const int32_t* ntiles;       // [BH]
+  int max_tiles;
 };
 
 hipError_t launch_retrieval(const RetrArgs& a, int phase, int dtype, hipStream_t s);  // 0 tables, 1 exact

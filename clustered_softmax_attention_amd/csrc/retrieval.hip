@@ -17,6 +17,9 @@
 //                prefix mass.
 //   retr_exact   one workgroup per (i, b): exact softmax over the retrieved keys for the
 //                bucket's queries, merged by log-sum-exp into the far-field partial result.
+//   retr_exact_mfma  (bf16 inputs) the same on the matrix cores, one workgroup per
+//                chunk of up to 128 queries of one bucket (the stage-2 chunks).
+#include "mfma.hpp"
 #include "muse_kernels.hpp"
 
 namespace muse {
@@ -320,6 +323,179 @@ __global__ void __launch_bounds__(256) retr_exact_kernel(RetrArgs a) {
   }
 }
 
+// Matrix-core exact part for bf16 inputs: one workgroup of 4 waves per chunk of up to 128
+// queries of bucket (b, i) (wave w: queries 32 w .. 32 w + 31). The retrieved keys are the
+// concatenation of the chosen atoms' ranges of the key permutation; they stream through
+// LDS 32 at a time (K and V rows, bf16, gathered by 16-byte loads), and on the matrix
+// cores
+//   l^T = K q^T (32 keys x 32 queries; bf16 operands are exact, fp32 accumulation),
+//   online softmax over the keys, O^T += V^T P^T (P split into bf16 hi + lo),
+// as in the stage-2 kernel; the result is merged into the far field by log-sum-exp.
+template <int D>
+__global__ void __launch_bounds__(256, 2) retr_exact_mfma_kernel(RetrArgs a) {
+  constexpr int NKS = D / 16, NMT = D / 32, JC = 32, KST = D + 16;
+  constexpr int NK = JC * D / 8 / 256;  // 16-byte row pieces per thread and tensor
+  __shared__ __align__(16) uint16_t sK[JC * KST];
+  __shared__ __align__(16) uint16_t sV[JC * KST];
+  __shared__ int s_start[kMaxRetrRow];    // first permutation position of each range
+  __shared__ int s_cum[kMaxRetrRow + 1];  // exclusive prefix of the range lengths
+  __shared__ int s_nr;
+  const int bh = blockIdx.y, tix = blockIdx.x, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
+  if (tix >= a.ntiles[bh]) return;  // whole workgroup leaves together
+  const int2 tile = a.tiles[static_cast<size_t>(bh) * a.max_tiles + tix];
+  const int u = tile.x, b = u / a.Cq, i = u % a.Cq;
+  if (b == 0) return;  // the first block retrieves nothing
+  const int Ck = a.Ck, k1 = a.k1, k2 = a.k2, row = k1 * (1 + k2);
+  if (tid == 0) {
+    // the chosen atoms as ranges of the key permutation, in selection order
+    const int32_t* sel = a.sel + ((static_cast<size_t>(bh) * a.nb + b) * a.Cq + i) * row;
+    const int32_t* offk = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
+    int n = 0, cum = 0;
+    for (int t = 0; t < k1; ++t) {
+      const int j = sel[t * (1 + k2)];
+      if (j < 0) continue;
+      for (int v = 0; v < k2; ++v) {
+        const int bb = sel[t * (1 + k2) + 1 + v];
+        if (bb < 0) continue;
+        const int p0 = offk[bb * Ck + j], p1 = offk[bb * Ck + j + 1];
+        if (p1 > p0) {
+          s_start[n] = p0;
+          s_cum[n] = cum;
+          cum += p1 - p0;
+          ++n;
+        }
+      }
+    }
+    s_cum[n] = cum;
+    s_nr = n;
+  }
+  __syncthreads();
+  const int nr = s_nr, nR = s_cum[nr];
+  if (nR == 0) return;  // nothing retrieved (uniform: read from LDS by every thread)
+  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (a.nb * a.Cq + 1);
+  const int st = tile.y + 32 * wave;
+  const int qn = a.perm_q[static_cast<size_t>(bh) * a.N + min(st + c, a.N - 1)];
+  const int nw = max(0, min(32, offq[u + 1] - st));  // queries of this wave
+  const bool valid = c < nw;
+  const size_t rowq = static_cast<size_t>(bh) * a.N + qn;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+  const int32_t* permk = a.perm_k + static_cast<size_t>(bh) * a.N;
+  // query fragments (B operand: column = query c, k = d); exact in bf16
+  bf16x8_t qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(Q + rowq * D + 16 * ks + 8 * h));
+  // rows of chunk ch into registers: position pos of the concatenated ranges
+  u16x8_t pk[NK], pv[NK];
+  auto load_chunk = [&](int ch) {
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+      const int x = tid + 256 * q, r = x / (D / 8), d8 = (x % (D / 8)) * 8;
+      const int pos = ch * JC + r;
+      pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      pv[q] = pk[q];
+      if (pos < nR) {
+        int lo = 0, hi = nr - 1;  // last range with s_cum <= pos
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_cum[mid] <= pos) lo = mid;
+          else hi = mid - 1;
+        }
+        const size_t kr = static_cast<size_t>(permk[s_start[lo] + pos - s_cum[lo]]) * D + d8;
+        pk[q] = *reinterpret_cast<const u16x8_t*>(K + kr);
+        pv[q] = *reinterpret_cast<const u16x8_t*>(V + kr);
+      }
+    }
+  };
+  const int nch = (nR + JC - 1) / JC;
+  load_chunk(0);
+  const float sl2 = a.scale * 1.4426950408889634f;
+  float mx = kNegInf, z = 0.f;  // running max (log2 units) and sum of this lane pair's query
+  f32x16_t o[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) o[mt] = zero16();
+  for (int ch = 0; ch < nch; ++ch) {
+    __syncthreads();  // previous chunk consumed
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+      const int x = tid + 256 * q, r = x / (D / 8), d8 = (x % (D / 8)) * 8;
+      *reinterpret_cast<u16x8_t*>(sK + r * KST + d8) = pk[q];
+      *reinterpret_cast<u16x8_t*>(sV + r * KST + d8) = pv[q];
+    }
+    __syncthreads();
+    if (ch + 1 < nch) load_chunk(ch + 1);
+    if (nw == 0) continue;
+    // logits^T of the chunk (rows = keys, column = query), log2 units
+    f32x16_t lg = zero16();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      lg = mfma32(as_bf16x8(*reinterpret_cast<const u16x8_t*>(sK + c * KST + 16 * ks + 8 * h)), qf[ks], lg);
+    float cm = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = ch * JC + 8 * (v >> 2) + 4 * h + (v & 3);
+      const float x = key < nR ? sl2 * lg[v] : kNegInf;
+      lg[v] = x;
+      cm = fmaxf(cm, x);
+    }
+    cm = fmaxf(cm, xor32(cm));
+    const float mn = fmaxf(mx, cm);  // finite: every chunk holds at least one key
+    const float alpha = mx == kNegInf ? 0.f : fast_exp2(mx - mn);
+    const bool grow = mn > mx && mx != kNegInf;
+    mx = mn;
+    float zs = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = fast_exp2(lg[v] - mn);
+      lg[v] = p;
+      zs += p;
+    }
+    z = z * alpha + zs + xor32(zs);
+    if (__ballot(grow) != 0ull) {
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+    }
+    // O^T += V^T P^T: k-slots of step ss are rows 16 ss + 4 h + 0..3 and 16 ss + 8 + 4 h + 0..3
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      float pv8[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) pv8[r] = lg[8 * ss + r];
+      bf16x8_t phi, plo;
+      split_bf16x8(pv8, phi, plo);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const bf16x8_t hv = lds_operand_tr_acc(sV, KST, 16 * ss, 32 * mt, lane);
+        o[mt] = mfma32(hv, phi, o[mt]);
+        o[mt] = mfma32(hv, plo, o[mt]);
+      }
+    }
+  }
+  if (!valid) return;
+  // merge with the far field of the query: L = log(e^LR + e^Lf), o = e^(LR-L) o_R + e^(Lf-L) o_f
+  const float LR = (mx + __log2f(z)) * 0.6931471805599453f;
+  const float lf = a.l_far[rowq];
+  const float Lt = lf == kNegInf ? LR : fmaxf(LR, lf) + log1pf(__expf(-fabsf(LR - lf)));
+  const float w0 = __expf(LR - Lt) / z, w1 = lf == kNegInf ? 0.f : __expf(lf - Lt);
+  // lanes (c, h) hold rows d = 32 mt + 8 g + 4 h + r of query c
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float* dst = a.o_far + rowq * D + 32 * mt + 8 * g + 4 * h;
+      const f32x4_t f = *reinterpret_cast<const f32x4_t*>(dst);
+      f32x4_t r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = w0 * o[mt][4 * g + e] + w1 * f[e];
+      *reinterpret_cast<f32x4_t*>(dst) = r;
+    }
+  if (h == 0) a.l_far[rowq] = Lt;
+}
+
 hipError_t launch_retrieval(const RetrArgs& a, int phase, int dtype, hipStream_t s) {
   const dim3 g(a.Cq, a.nb, a.BH);
   if (phase == 0) {
@@ -337,7 +513,11 @@ hipError_t launch_retrieval(const RetrArgs& a, int phase, int dtype, hipStream_t
     }
   } else {
     ProfScope ps_("retr_exact", s);
-    if (dtype == 0) {
+    if (dtype == 1 && a.tiles != nullptr) {
+      const dim3 gm(a.max_tiles, a.BH);
+      if (a.D == 64) hipLaunchKernelGGL((retr_exact_mfma_kernel<64>), gm, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((retr_exact_mfma_kernel<128>), gm, dim3(256), 0, s, a);
+    } else if (dtype == 0) {
       if (a.D == 64) hipLaunchKernelGGL((retr_exact_kernel<float, 64>), g, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((retr_exact_kernel<float, 128>), g, dim3(256), 0, s, a);
     } else {
