@@ -122,6 +122,10 @@ __global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
   __shared__ float s_q[D];
   __shared__ float s_red[2];
   __shared__ int s_sel[kMaxRetrRow];
+  __shared__ int s_start[kMaxRetrRow];    // retrieved atoms as ranges of the key permutation
+  __shared__ int s_cum[kMaxRetrRow + 1];  // exclusive prefix of the range lengths
+  __shared__ int s_row[KCH];              // key rows of the staged chunk
+  __shared__ int s_nr;
   const int i = blockIdx.x, b = blockIdx.y, bh = blockIdx.z;
   const int tid = threadIdx.x;
   if (b == 0) return;
@@ -155,18 +159,32 @@ __global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
       const bool isK = x < D;
       const int d = isK ? x : x - D;
       float rm = kNegInf, rz = 0.f, racc = 0.f;
-      for (int bb = 0; bb < b; ++bb) {
-        if (atom_selected(sr, k2, bb)) continue;
-        const size_t aidx = ((static_cast<size_t>(bh) * a.nb + bb) * a.Cq + i) * Ck + j;
-        const float m = a.at_m[aidx], z = a.at_z[aidx];
-        if (!(z > 0.f)) continue;
-        const float xv = (isK ? a.at_k : a.at_v)[aidx * D + d];
-        const float nm = fmaxf(rm, m);
-        const float f0 = rz > 0.f ? __expf(rm - nm) : 0.f;
-        const float f1 = __expf(m - nm);
-        rz = rz * f0 + z * f1;
-        racc = racc * f0 + xv * f1;
-        rm = nm;
+      // eight blocks' atoms requested at a time, folded in block order
+      for (int bb0 = 0; bb0 < b; bb0 += 8) {
+        float m8[8], z8[8], x8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int bb = bb0 + q;
+          m8[q] = kNegInf;
+          z8[q] = 0.f;
+          x8[q] = 0.f;
+          if (bb < b && !atom_selected(sr, k2, bb)) {
+            const size_t aidx = ((static_cast<size_t>(bh) * a.nb + bb) * a.Cq + i) * Ck + j;
+            m8[q] = a.at_m[aidx];
+            z8[q] = a.at_z[aidx];
+            x8[q] = (isK ? a.at_k : a.at_v)[aidx * D + d];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (!(z8[q] > 0.f)) continue;
+          const float nm = fmaxf(rm, m8[q]);
+          const float f0 = rz > 0.f ? __expf(rm - nm) : 0.f;
+          const float f1 = __expf(m8[q] - nm);
+          rz = rz * f0 + z8[q] * f1;
+          racc = racc * f0 + x8[q] * f1;
+          rm = nm;
+        }
       }
       const bool any = rz > 0.f;
       if (x == 0) a.s_logz[sidx * Ck + j] = any ? rm + __logf(rz) : kNegInf;
@@ -187,43 +205,69 @@ __global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
   const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * a.N * D;
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
   const int32_t* offs = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
-  for (int t = 0; t < k1; ++t) {
-    const int j = s_sel[t * (1 + k2)];
-    if (j < 0) continue;
-    for (int u = 0; u < k2; ++u) {
-      const int bb = s_sel[t * (1 + k2) + 1 + u];
-      if (bb < 0) continue;
-      const int p0 = offs[bb * Ck + j], p1 = offs[bb * Ck + j + 1];
-      for (int c0 = p0; c0 < p1; c0 += KCH) {
-        const int nk = min(KCH, p1 - c0);
-        __syncthreads();
-        for (int x = tid; x < nk * D; x += 256) {
-          const int r = x / D, d = x % D;
-          const size_t rowi = static_cast<size_t>(perm[c0 + r]) * D + d;
-          s_k[x] = Elem<T>::load(K, rowi);
-          s_v[x] = Elem<T>::load(V, rowi);
-        }
-        __syncthreads();
-        if (tid < 64) {
-          float w = 0.f;
-          if (tid < nk) {
-            float dot = 0.f;
-            for (int d = 0; d < D; ++d) dot = fmaf(s_q[d], s_k[tid * D + d], dot);
-            w = __expf(a.scale * dot - Rpre);
-          }
-          s_w[tid] = w;
-          const float ws = wave_sum(w);
-          if (tid == 0) wsum += ws;
-        }
-        __syncthreads();
-        for (int m = 0; m < nk; ++m) {
-          const float wm = s_w[m];
-#pragma unroll
-          for (int x = 0; x < TD; ++x)
-#pragma unroll
-            for (int y = 0; y < TD; ++y) acc[x][y] = fmaf(wm * s_v[m * D + tr * TD + x], s_k[m * D + tc * TD + y], acc[x][y]);
+  if (tid == 0) {
+    // the chosen atoms as ranges of the key permutation, in selection order
+    int n = 0, cum = 0;
+    for (int t = 0; t < k1; ++t) {
+      const int j = s_sel[t * (1 + k2)];
+      if (j < 0) continue;
+      for (int u = 0; u < k2; ++u) {
+        const int bb = s_sel[t * (1 + k2) + 1 + u];
+        if (bb < 0) continue;
+        const int p0 = offs[bb * Ck + j], p1 = offs[bb * Ck + j + 1];
+        if (p1 > p0) {
+          s_start[n] = p0;
+          s_cum[n] = cum;
+          cum += p1 - p0;
+          ++n;
         }
       }
+    }
+    s_cum[n] = cum;
+    s_nr = n;
+  }
+  __syncthreads();
+  const int nr = s_nr, nR = s_cum[nr];
+  // the retrieved keys in chunks of KCH of their concatenation (several atoms per chunk)
+  for (int c0 = 0; c0 < nR; c0 += KCH) {
+    const int nk = min(KCH, nR - c0);
+    __syncthreads();  // previous chunk consumed
+    if (tid < nk) {
+      const int pos = c0 + tid;
+      int lo = 0, hi = nr - 1;  // last range with s_cum <= pos
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_cum[mid] <= pos) lo = mid;
+        else hi = mid - 1;
+      }
+      s_row[tid] = perm[s_start[lo] + pos - s_cum[lo]];
+    }
+    __syncthreads();
+    for (int x = tid; x < nk * D; x += 256) {
+      const int r = x / D, d = x % D;
+      const size_t rowi = static_cast<size_t>(s_row[r]) * D + d;
+      s_k[x] = Elem<T>::load(K, rowi);
+      s_v[x] = Elem<T>::load(V, rowi);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float w = 0.f;
+      if (tid < nk) {
+        float dot = 0.f;
+        for (int d = 0; d < D; ++d) dot = fmaf(s_q[d], s_k[tid * D + d], dot);
+        w = __expf(a.scale * dot - Rpre);
+      }
+      s_w[tid] = w;
+      const float ws = wave_sum(w);
+      if (tid == 0) wsum += ws;
+    }
+    __syncthreads();
+    for (int m = 0; m < nk; ++m) {
+      const float wm = s_w[m];
+#pragma unroll
+      for (int x = 0; x < TD; ++x)
+#pragma unroll
+        for (int y = 0; y < TD; ++y) acc[x][y] = fmaf(wm * s_v[m * D + tr * TD + x], s_k[m * D + tc * TD + y], acc[x][y]);
     }
   }
   if (tid == 0) s_red[1] = wsum;
