@@ -229,6 +229,9 @@ __global__ void __launch_bounds__(256) s1_moments_kernel(S1Args a) {
 }
 
 // Fold atoms over blocks: one workgroup per (j, i, head), 2*D threads (K then V dims).
+// HIER: causal entries of the hierarchical squares (an instance of its own, so that the
+// batched prefix fold does not change its register allocation).
+template <bool HIER>
 __global__ void s1_prefix_kernel(S1Args a) {
   const int j = blockIdx.x, i = blockIdx.y, bh = blockIdx.z;
   const int D = a.D, Cq = a.Cq, Ck = a.Ck;
@@ -243,39 +246,70 @@ __global__ void s1_prefix_kernel(S1Args a) {
     float* dst = isK ? a.s_k : a.s_v;
     dst[sidx * D + d] = any ? racc / rz : 0.f;
   };
-  auto add = [&](int b) {
-    const size_t aidx = ((static_cast<size_t>(bh) * a.nb + b) * Cq + i) * Ck + j;
-    const float m = a.at_m[aidx], z = a.at_z[aidx];
-    if (z > 0.f) {
-      const float x = (isK ? a.at_k : a.at_v)[aidx * D + d];
-      const float nm = fmaxf(rm, m);
-      const float f0 = (rz > 0.f) ? __expf(rm - nm) : 0.f;
-      const float f1 = __expf(m - nm);
-      rz = rz * f0 + z * f1;
-      racc = racc * f0 + x * f1;
-      rm = nm;
+  // blocks [b0, b1) folded in order, their atoms requested eight at a time; with
+  // prefix_emit, entry b is written before block b joins (entry b: blocks < b)
+  auto fold = [&](int b0, int b1, bool prefix_emit) {
+    for (int c0 = b0; c0 < b1; c0 += 8) {
+      float m8[8], z8[8], x8[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        m8[q] = kNegInf;
+        z8[q] = 0.f;
+        x8[q] = 0.f;
+        if (c0 + q < b1) {
+          const size_t aidx = ((static_cast<size_t>(bh) * a.nb + c0 + q) * Cq + i) * Ck + j;
+          m8[q] = a.at_m[aidx];
+          z8[q] = a.at_z[aidx];
+          x8[q] = (isK ? a.at_k : a.at_v)[aidx * D + d];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (c0 + q >= b1) break;
+        if (prefix_emit) emit(c0 + q);
+        if (z8[q] > 0.f) {
+          const float nm = fmaxf(rm, m8[q]);
+          const float f0 = (rz > 0.f) ? __expf(rm - nm) : 0.f;
+          const float f1 = __expf(m8[q] - nm);
+          rz = rz * f0 + z8[q] * f1;
+          racc = racc * f0 + x8[q] * f1;
+          rm = nm;
+        }
+      }
     }
   };
-  if (a.causal && a.hier) {
-    // entry e: the square's key blocks [e - lowbit(e), e) (entry 0 stays empty)
+  if (HIER) {
+    // entry e: the square's key blocks [e - lowbit(e), e) (entry 0 stays empty); one
+    // block at a time (measured faster here than the batched fold: most squares hold
+    // one or two blocks)
     for (int e = 0; e < a.nb; ++e) {
       rm = kNegInf;
       rz = 0.f;
       racc = 0.f;
-      for (int b = e - (e & -e); b < e; ++b) add(b);
+      for (int b = e - (e & -e); b < e; ++b) {
+        const size_t aidx = ((static_cast<size_t>(bh) * a.nb + b) * Cq + i) * Ck + j;
+        const float m = a.at_m[aidx], z = a.at_z[aidx];
+        if (z > 0.f) {
+          const float x = (isK ? a.at_k : a.at_v)[aidx * D + d];
+          const float nm = fmaxf(rm, m);
+          const float f0 = (rz > 0.f) ? __expf(rm - nm) : 0.f;
+          const float f1 = __expf(m - nm);
+          rz = rz * f0 + z * f1;
+          racc = racc * f0 + x * f1;
+          rm = nm;
+        }
+      }
       emit(e);
     }
     return;
   }
-  for (int b = 0; b < a.nb; ++b) {
-    if (a.causal) emit(b);  // entry b: blocks < b
-    add(b);
-  }
+  fold(0, a.nb, a.causal != 0);
   if (!a.causal) emit(0);
 }
 
 // Fold sub-block moments: thread per (dv, dk) element; every table entry is normalised
-// by its mass. Causal entry b holds the sub-blocks of blocks < b.
+// by its mass. Causal entry b holds the sub-blocks of blocks < b (HIER: of its square).
+template <bool HIER>
 __global__ void s1_mom_prefix_kernel(S1Args a) {
   const int D = a.D, Cq = a.Cq;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -287,32 +321,59 @@ __global__ void s1_mom_prefix_kernel(S1Args a) {
     const size_t sbase = ((static_cast<size_t>(bh) * a.nbS + b) * Cq + i) * D * D;
     a.s_dip[sbase + e] = (rR == kNegInf) ? 0.f : racc;  // [dv][dk]
   };
-  auto add = [&](int mb) {
-    const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
-    const float R = a.blk_lmass[bidx];
-    if (R != kNegInf) {
-      const float x = a.blk_mom[bidx * D * D + e];
-      const float nR = (rR == kNegInf) ? R : fmaxf(rR, R) + __logf(1.f + __expf(-fabsf(rR - R)));
-      const float f0 = (rR == kNegInf) ? 0.f : __expf(rR - nR);
-      const float f1 = __expf(R - nR);
-      racc = racc * f0 + x * f1;
-      rR = nR;
+  // sub-blocks [m0, m1) folded in order, requested eight at a time; with prefix_emit,
+  // entry b is written before the first sub-block of block b joins
+  auto fold = [&](int m0, int m1, bool prefix_emit) {
+    for (int c0 = m0; c0 < m1; c0 += 8) {
+      float R8[8], x8[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        R8[q] = kNegInf;
+        x8[q] = 0.f;
+        if (c0 + q < m1) {
+          const size_t bidx = (static_cast<size_t>(bh) * a.nmb + c0 + q) * Cq + i;
+          R8[q] = a.blk_lmass[bidx];
+          x8[q] = a.blk_mom[bidx * D * D + e];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int mb = c0 + q;
+        if (mb >= m1) break;
+        if (prefix_emit && mb % per_block == 0) emit(mb / per_block);
+        const float R = R8[q];
+        if (R != kNegInf) {
+          const float nR = (rR == kNegInf) ? R : fmaxf(rR, R) + __logf(1.f + __expf(-fabsf(rR - R)));
+          const float f0 = (rR == kNegInf) ? 0.f : __expf(rR - nR);
+          const float f1 = __expf(R - nR);
+          racc = racc * f0 + x8[q] * f1;
+          rR = nR;
+        }
+      }
     }
   };
-  if (a.causal && a.hier) {
-    // entry b: the sub-blocks of the square's key blocks [b - lowbit(b), b)
+  if (HIER) {
+    // entry b: the sub-blocks of the square's key blocks [b - lowbit(b), b), one at a time
     for (int b = 0; b < a.nb; ++b) {
       rR = kNegInf;
       racc = 0.f;
-      for (int mb = (b - (b & -b)) * per_block; mb < b * per_block; ++mb) add(mb);
+      for (int mb = (b - (b & -b)) * per_block; mb < b * per_block; ++mb) {
+        const size_t bidx = (static_cast<size_t>(bh) * a.nmb + mb) * Cq + i;
+        const float R = a.blk_lmass[bidx];
+        if (R != kNegInf) {
+          const float x = a.blk_mom[bidx * D * D + e];
+          const float nR = (rR == kNegInf) ? R : fmaxf(rR, R) + __logf(1.f + __expf(-fabsf(rR - R)));
+          const float f0 = (rR == kNegInf) ? 0.f : __expf(rR - nR);
+          const float f1 = __expf(R - nR);
+          racc = racc * f0 + x * f1;
+          rR = nR;
+        }
+      }
       emit(b);
     }
     return;
   }
-  for (int mb = 0; mb < a.nmb; ++mb) {
-    if (a.causal && mb % per_block == 0) emit(mb / per_block);
-    add(mb);
-  }
+  fold(0, a.nmb, a.causal != 0);
   if (!a.causal) emit(0);
 }
 
@@ -675,7 +736,8 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   }
   {
     ProfScope ps_("s1_prefix", s);
-    hipLaunchKernelGGL(s1_prefix_kernel, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
+    if (a.causal && a.hier) hipLaunchKernelGGL(s1_prefix_kernel<true>, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
+    else hipLaunchKernelGGL(s1_prefix_kernel<false>, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
   }
   if (a.dipole == 2) {  // untilted (acausal, no retrieval): per key cluster covariances
     launch_untilted<T, D>(a, 0, s);
@@ -697,7 +759,10 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
     }
     {
       ProfScope ps_("s1_mom_prefix", s);
-      hipLaunchKernelGGL(s1_mom_prefix_kernel, dim3((D * D + 255) / 256, a.Cq, a.BH), dim3(256), 0, s, a);
+      if (a.causal && a.hier)
+        hipLaunchKernelGGL(s1_mom_prefix_kernel<true>, dim3((D * D + 255) / 256, a.Cq, a.BH), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL(s1_mom_prefix_kernel<false>, dim3((D * D + 255) / 256, a.Cq, a.BH), dim3(256), 0, s, a);
     }
   }
   if (a.retr != nullptr) launch_retrieval(*a.retr, 0, sizeof(T) == 2 ? 1 : 0, s);
