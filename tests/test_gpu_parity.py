@@ -184,6 +184,25 @@ def test_retrieval_small_blocks_fp32(muse_lib):
     check_config(cfg, [(0, 0)])
 
 
+def test_retrieval_bf16_d128(muse_lib):
+    # D = 128: the matrix-core exact part on retrieved keys (several 32-key chunks per
+    # bucket) and the retrieval tables, cluster counts off the 32-tiles
+    cfg = scaled_config("causal_64k_d128", B=1, H=2, N=4096, block=512, Cq=12, Ck=40, topk_clusters=3,
+                        topk_blocks=2)
+    check_config(cfg, [(0, 0), (0, 1)])
+
+
+def test_retrieval_of_everything_is_exact_d128(muse_lib):
+    cfg = scaled_config("causal_64k_d128", B=1, H=1, N=2048, block=256, Cq=8, Ck=16, topk_clusters=16,
+                        topk_blocks=8)
+    q, k, v = make_inputs(cfg)
+    out, _ = run_gpu(cfg, q, k, v)
+    o, _ = exact_attention(q[0, 0], k[0, 0], v[0, 0], causal=True)
+    rel = rel_l2(out.float().cpu().numpy()[0, 0], o)
+    log(f"[retrieval everything, D=128] rel-L2 vs exact {rel:.3e}")
+    assert rel <= TOL["bf16"]
+
+
 def test_retrieval_of_everything_is_exact(muse_lib):
     # k1 = Ck and k2 = number of blocks: every earlier key is attended exactly
     cfg = scaled_config("retrieval_16k", B=1, H=1, N=2048, block=256, Cq=8, Ck=16, topk_clusters=16, topk_blocks=8)
