@@ -228,6 +228,8 @@ __global__ void __launch_bounds__(256) s1_moments_kernel(S1Args a) {
     for (int y = 0; y < TD; ++y) out[(tr * TD + x) * D + tc * TD + y] = acc[x][y];
 }
 
+constexpr int kHierLevels = 12;  // binary-counter depth of the hierarchical folds (nb < 2^11)
+
 // Fold atoms over blocks: one workgroup per (j, i, head), 2*D threads (K then V dims).
 // HIER: causal entries of the hierarchical squares (an instance of its own, so that the
 // batched prefix fold does not change its register allocation).
@@ -278,10 +280,60 @@ __global__ void s1_prefix_kernel(S1Args a) {
       }
     }
   };
+  if (HIER && a.nb < (1 << (kHierLevels - 1))) {
+    // entry e: the square's key blocks [e - lowbit(e), e), by a binary counter over the
+    // blocks: block b is pushed as a node and merged with the ctz(b + 1) nodes on top of
+    // the stack (each the fold of the blocks just before it), which leaves exactly entry
+    // b + 1's square on top. Left (earlier) operands first; entry 0 stays empty.
+    float sm[kHierLevels], sz[kHierLevels], sa[kHierLevels];
+    int top = 0;
+    emit(0);
+    for (int c0 = 0; c0 < a.nb; c0 += 8) {
+      float m8[8], z8[8], x8[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        m8[q] = kNegInf;
+        z8[q] = 0.f;
+        x8[q] = 0.f;
+        if (c0 + q < a.nb) {
+          const size_t aidx = ((static_cast<size_t>(bh) * a.nb + c0 + q) * Cq + i) * Ck + j;
+          m8[q] = a.at_m[aidx];
+          z8[q] = a.at_z[aidx];
+          x8[q] = (isK ? a.at_k : a.at_v)[aidx * D + d];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int b = c0 + q;
+        if (b >= a.nb) break;
+        const bool has = z8[q] > 0.f;
+        float cm = has ? m8[q] : kNegInf, cz = has ? z8[q] : 0.f, ca = has ? x8[q] : 0.f;
+        for (int t = __builtin_ctz(b + 1); t > 0; --t) {
+          --top;
+          const float lm = sm[top], lz = sz[top], la = sa[top];
+          const float nm = fmaxf(lm, cm);
+          const float f0 = lz > 0.f ? __expf(lm - nm) : 0.f;
+          const float f1 = cz > 0.f ? __expf(cm - nm) : 0.f;
+          cz = lz * f0 + cz * f1;
+          ca = la * f0 + ca * f1;
+          cm = nm;
+        }
+        sm[top] = cm;
+        sz[top] = cz;
+        sa[top] = ca;
+        ++top;
+        if (b + 1 < a.nb) {
+          rm = cm;
+          rz = cz;
+          racc = ca;
+          emit(b + 1);
+        }
+      }
+    }
+    return;
+  }
   if (HIER) {
-    // entry e: the square's key blocks [e - lowbit(e), e) (entry 0 stays empty); one
-    // block at a time (measured faster here than the batched fold: most squares hold
-    // one or two blocks)
+    // very many blocks: entry e folded directly from its square's blocks, one at a time
     for (int e = 0; e < a.nb; ++e) {
       rm = kNegInf;
       rz = 0.f;
@@ -352,8 +404,65 @@ __global__ void s1_mom_prefix_kernel(S1Args a) {
       }
     }
   };
+  if (HIER && a.nb < (1 << (kHierLevels - 1))) {
+    // entry b: the sub-blocks of the square's key blocks [b - lowbit(b), b), by a binary
+    // counter over the blocks as in s1_prefix (a block's node is the fold of its
+    // sub-blocks; left operands first; entry 0 stays empty)
+    float sR[kHierLevels], sA[kHierLevels];
+    int top = 0;
+    emit(0);
+    float cR = kNegInf, cA = 0.f;  // the block being built
+    for (int c0 = 0; c0 < a.nmb; c0 += 8) {
+      float R8[8], x8[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        R8[q] = kNegInf;
+        x8[q] = 0.f;
+        if (c0 + q < a.nmb) {
+          const size_t bidx = (static_cast<size_t>(bh) * a.nmb + c0 + q) * Cq + i;
+          R8[q] = a.blk_lmass[bidx];
+          x8[q] = a.blk_mom[bidx * D * D + e];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int mb = c0 + q;
+        if (mb >= a.nmb) break;
+        const float R = R8[q];
+        if (R != kNegInf) {
+          const float nR = (cR == kNegInf) ? R : fmaxf(cR, R) + __logf(1.f + __expf(-fabsf(cR - R)));
+          const float f0 = (cR == kNegInf) ? 0.f : __expf(cR - nR);
+          const float f1 = __expf(R - nR);
+          cA = cA * f0 + x8[q] * f1;
+          cR = nR;
+        }
+        if ((mb + 1) % per_block != 0) continue;
+        const int b = mb / per_block;
+        for (int t = __builtin_ctz(b + 1); t > 0; --t) {
+          --top;
+          const float lR = sR[top], lA = sA[top];
+          const float nR = lR == kNegInf ? cR : (cR == kNegInf ? lR : fmaxf(lR, cR) + __logf(1.f + __expf(-fabsf(lR - cR))));
+          const float f0 = lR == kNegInf ? 0.f : __expf(lR - nR);
+          const float f1 = cR == kNegInf ? 0.f : __expf(cR - nR);
+          cA = lA * f0 + cA * f1;
+          cR = nR;
+        }
+        sR[top] = cR;
+        sA[top] = cA;
+        ++top;
+        if (b + 1 < a.nb) {
+          rR = cR;
+          racc = cA;
+          emit(b + 1);
+        }
+        cR = kNegInf;
+        cA = 0.f;
+      }
+    }
+    return;
+  }
   if (HIER) {
-    // entry b: the sub-blocks of the square's key blocks [b - lowbit(b), b), one at a time
+    // very many blocks: entry b folded directly from its square's sub-blocks
     for (int b = 0; b < a.nb; ++b) {
       rR = kNegInf;
       racc = 0.f;
