@@ -150,12 +150,14 @@ __global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
   __syncthreads();
   const float Rpre = s_red[0];
 
-  // 1. remainder summaries of the chosen clusters (re-merged from unselected atoms)
-  for (int t = 0; t < k1; ++t) {
+  // 1. remainder summaries of the chosen clusters (re-merged from unselected atoms): the
+  // k1 x 2D (cluster, feature) folds spread over all threads
+  for (int w = tid; w < k1 * 2 * D; w += 256) {
+    const int t = w / (2 * D), x = w % (2 * D);
     const int* sr = s_sel + t * (1 + k2);
     const int j = sr[0];
     if (j < 0) continue;
-    for (int x = tid; x < 2 * D; x += 256) {
+    {
       const bool isK = x < D;
       const int d = isK ? x : x - D;
       float rm = kNegInf, rz = 0.f, racc = 0.f;
