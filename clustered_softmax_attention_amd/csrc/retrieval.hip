@@ -105,6 +105,42 @@ __device__ __forceinline__ bool atom_selected(const int32_t* selrow, int k2, int
   return false;
 }
 
+// The retrieved atoms of (b, i) as ranges of the key permutation, in selection order
+// (cluster t, then its blocks): range w = t k2 + u starts at start[w] and holds the
+// concatenated positions [cum[w], cum[w + 1]); unchosen or empty atoms are empty ranges.
+// Called by one whole wave (a pair per lane, then a wave prefix sum); returns the number
+// of ranges, k1 k2.
+__device__ int retr_ranges(const int32_t* selrow, const int32_t* offk, int Ck, int k1, int k2, int* start,
+                           int* cum) {
+  const int lane = lane_id(), np = k1 * k2;
+  int run = 0;
+  for (int w0 = 0; w0 < np; w0 += 64) {
+    const int w = w0 + lane;
+    int p0 = 0, len = 0;
+    if (w < np) {
+      const int t = w / k2, u = w % k2;
+      const int j = selrow[t * (1 + k2)], bb = selrow[t * (1 + k2) + 1 + u];
+      if (j >= 0 && bb >= 0) {
+        p0 = offk[bb * Ck + j];
+        len = offk[bb * Ck + j + 1] - p0;
+      }
+    }
+    int incl = len;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (w < np) {
+      start[w] = p0;
+      cum[w] = run + incl - len;
+    }
+    run += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) cum[np] = run;
+  return np;
+}
+
 // keys staged per step (LDS stays under 64 KiB)
 template <int D>
 struct RetrChunk {
@@ -207,26 +243,9 @@ __global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
   const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * a.N * D;
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
   const int32_t* offs = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
-  if (tid == 0) {
-    // the chosen atoms as ranges of the key permutation, in selection order
-    int n = 0, cum = 0;
-    for (int t = 0; t < k1; ++t) {
-      const int j = s_sel[t * (1 + k2)];
-      if (j < 0) continue;
-      for (int u = 0; u < k2; ++u) {
-        const int bb = s_sel[t * (1 + k2) + 1 + u];
-        if (bb < 0) continue;
-        const int p0 = offs[bb * Ck + j], p1 = offs[bb * Ck + j + 1];
-        if (p1 > p0) {
-          s_start[n] = p0;
-          s_cum[n] = cum;
-          cum += p1 - p0;
-          ++n;
-        }
-      }
-    }
-    s_cum[n] = cum;
-    s_nr = n;
+  if (tid < 64) {
+    const int n = retr_ranges(s_sel, offs, Ck, k1, k2, s_start, s_cum);
+    if (tid == 0) s_nr = n;
   }
   __syncthreads();
   const int nr = s_nr, nR = s_cum[nr];
@@ -393,28 +412,11 @@ __global__ void __launch_bounds__(256, 2) retr_exact_mfma_kernel(RetrArgs a) {
   const int u = tile.x, b = u / a.Cq, i = u % a.Cq;
   if (b == 0) return;  // the first block retrieves nothing
   const int Ck = a.Ck, k1 = a.k1, k2 = a.k2, row = k1 * (1 + k2);
-  if (tid == 0) {
-    // the chosen atoms as ranges of the key permutation, in selection order
+  if (wave == 0) {
     const int32_t* sel = a.sel + ((static_cast<size_t>(bh) * a.nb + b) * a.Cq + i) * row;
     const int32_t* offk = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
-    int n = 0, cum = 0;
-    for (int t = 0; t < k1; ++t) {
-      const int j = sel[t * (1 + k2)];
-      if (j < 0) continue;
-      for (int v = 0; v < k2; ++v) {
-        const int bb = sel[t * (1 + k2) + 1 + v];
-        if (bb < 0) continue;
-        const int p0 = offk[bb * Ck + j], p1 = offk[bb * Ck + j + 1];
-        if (p1 > p0) {
-          s_start[n] = p0;
-          s_cum[n] = cum;
-          cum += p1 - p0;
-          ++n;
-        }
-      }
-    }
-    s_cum[n] = cum;
-    s_nr = n;
+    const int n = retr_ranges(sel, offk, Ck, k1, k2, s_start, s_cum);
+    if (lane == 0) s_nr = n;
   }
   __syncthreads();
   const int nr = s_nr, nR = s_cum[nr];
