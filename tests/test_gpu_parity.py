@@ -160,6 +160,13 @@ def test_hierarchical_causal(muse_lib, name, over, dipole):
     check_config(cfg, [(0, 0)] if cfg.H == 1 else [(0, 0), (0, 1)], dipole=dipole, hierarchy=True)
 
 
+def test_hierarchical_many_blocks(muse_lib):
+    # 2048 blocks of 64 tokens: the stage-1 folds build each square directly from its
+    # blocks instead of by the binary counter over the blocks; block 2047 sees 11 squares
+    cfg = scaled_config("causal_16k", B=1, H=1, N=131072, block=64, Cq=8, Ck=16)
+    check_config(cfg, [(0, 0)], blocks=[1, 1024, 2047], hierarchy=True)
+
+
 def test_hierarchical_refusals(muse_lib):
     from clustered_softmax_attention_amd import binding
     cfg = scaled_config("retrieval_16k", B=1, H=1, N=2048, block=256)
