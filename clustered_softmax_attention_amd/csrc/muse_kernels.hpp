@@ -153,7 +153,7 @@ struct S1Args {
 };
 
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);
-void launch_stage1_mfma(const S1Args& a, int which, hipStream_t s);  // 0 scores, 1 atoms (+ merge), 2 moments, 3 finalise, 4 scan
+void launch_stage1_mfma(const S1Args& a, int which, hipStream_t s);  // 0 scores, 1 atoms (+ merge), 2 moments, 3 finalise, 4 scan, 5 general-path dipole
 
 // ------------------------------------------------------------------ stage 2
 

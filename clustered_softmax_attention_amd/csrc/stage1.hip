@@ -487,9 +487,8 @@ __global__ void s1_mom_prefix_kernel(S1Args a) {
 }
 
 // D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T for one table entry; one workgroup per
-// (i, b, head); thread tiles as in s1_moments. With bf16 tables (the matrix-core stage 2)
-// it also writes the bf16 hi/lo copies of K_ij and V_ij as it stages them, and s * D_i
-// in bf16 instead of D_i in fp32 (the packing of s1_pack, in the same pass).
+// (i, b, head); thread tiles as in s1_moments. fp32 tables; the bf16 path uses
+// s1_dip_final_mfma (stage1_mfma.hip), which also packs the tables.
 template <int D>
 __global__ void __launch_bounds__(256) s1_dip_final_kernel(S1Args a) {
   constexpr int TD = D / 16;
@@ -524,7 +523,6 @@ __global__ void __launch_bounds__(256) s1_dip_final_kernel(S1Args a) {
   for (int x = 0; x < TD; ++x)
 #pragma unroll
     for (int y = 0; y < TD; ++y) acc[x][y] = 0.f;
-  const bool pack = a.t_khi != nullptr;
   for (int j0 = 0; j0 < Ck; j0 += 32) {
     const int nj = min(32, Ck - j0);
     __syncthreads();
@@ -534,20 +532,6 @@ __global__ void __launch_bounds__(256) s1_dip_final_kernel(S1Args a) {
       const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(a.s_v + g);
       *reinterpret_cast<f32x4_t*>(kc + e) = k4;
       *reinterpret_cast<f32x4_t*>(vc + e) = v4;
-      if (pack) {
-        u16x4_t kh, kl, vh, vl;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          kh[q] = f32_to_bf16_bits(k4[q]);
-          kl[q] = f32_to_bf16_bits(k4[q] - bf16_to_f32(kh[q]));
-          vh[q] = f32_to_bf16_bits(v4[q]);
-          vl[q] = f32_to_bf16_bits(v4[q] - bf16_to_f32(vh[q]));
-        }
-        *reinterpret_cast<u16x4_t*>(a.t_khi + g) = kh;
-        *reinterpret_cast<u16x4_t*>(a.t_klo + g) = kl;
-        *reinterpret_cast<u16x4_t*>(a.t_vhi + g) = vh;
-        *reinterpret_cast<u16x4_t*>(a.t_vlo + g) = vl;
-      }
     }
     __syncthreads();
     for (int jj = 0; jj < nj; ++jj) {
@@ -569,9 +553,7 @@ __global__ void __launch_bounds__(256) s1_dip_final_kernel(S1Args a) {
 #pragma unroll
     for (int y = 0; y < TD; ++y) {
       const size_t o = static_cast<size_t>(tr * TD + x) * D + (tc * TD + y);  // [dv][dk]
-      const float dv = dip[o] - acc[x][y];
-      if (pack) a.t_dip[sidx * D * D + o] = f32_to_bf16_bits(a.scale * dv);
-      else dip[o] = dv;
+      dip[o] = dip[o] - acc[x][y];
     }
 }
 
@@ -898,9 +880,11 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   }
   if (a.retr != nullptr) launch_retrieval(*a.retr, 0, sizeof(T) == 2 ? 1 : 0, s);
   if (a.dipole) {
-    const size_t lds_fin = sizeof(float) * (kMaxClusters + 64 * D + 4);
-    allow_lds((const void*)s1_dip_final_kernel<D>, lds_fin);
-    {
+    if (a.t_khi != nullptr) {
+      launch_stage1_mfma(a, 5, s);  // matrix cores, with the packing of the bf16 tables
+    } else {
+      const size_t lds_fin = sizeof(float) * (kMaxClusters + 64 * D + 4);
+      allow_lds((const void*)s1_dip_final_kernel<D>, lds_fin);
       ProfScope ps_("s1_dip_final", s);
       hipLaunchKernelGGL((s1_dip_final_kernel<D>), dim3(a.Cq, a.nbS, a.BH), dim3(256), lds_fin, s, a);
     }

@@ -21,6 +21,10 @@
 //                  scores (no running rescale), then sum_m w_m v_m k_m^T with fp16
 //                  operands (the weights are applied to the value fragments with packed
 //                  fp16 multiplies) and fp32 accumulation.
+//   s1_finalize_acausal, s1_causal_scan  the tables of stage 2 (acausal: one entry;
+//                  causal: every block's prefix), below.
+//   s1_dip_final_mfma  the dipole and bf16 tables of one entry on the general path
+//                  (retrieval, hierarchy), from the folded atoms and moments.
 #include "mfma.hpp"
 #include "muse_kernels.hpp"
 
@@ -1182,6 +1186,114 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
   }
 }
 
+// Dipole of one table entry on the general path (causal entries with retrieval or the
+// hierarchy), bf16 tables: one workgroup of 4 waves per (i, e, head):
+//   D_i = E_i[v k^T] - sum_j P_ij V_ij K_ij^T,  P_ij = softmax_j(log Z_ij),
+// with E_i[v k^T] the folded block moments (fp32, [dv][dk]). Key clusters are staged 32 at
+// a time: K_ij and V_ij split into bf16 hi + lo (also written out as the stage-2 tables),
+// row-major in LDS; on the matrix cores (P V)^T K with both operands split
+// (hi.hi + hi.lo + lo.hi) and read through the transpose read, as in the acausal
+// finalise. Writes s * D_i in bf16.
+template <int D>
+__global__ void __launch_bounds__(256) s1_dip_final_mfma_kernel(S1Args a) {
+  constexpr int JC = 32, ST = D + 8, NDT = D / 32, TPW = NDT * NDT / 4;
+  __shared__ float sP[kMaxClusters];
+  __shared__ __align__(16) uint16_t sKh[JC * ST];
+  __shared__ __align__(16) uint16_t sKl[JC * ST];
+  __shared__ __align__(16) uint16_t sVh[JC * ST];
+  __shared__ __align__(16) uint16_t sVl[JC * ST];
+  const int i = blockIdx.x, e = blockIdx.y, bh = blockIdx.z;
+  const int Cq = a.Cq, Ck = a.Ck, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, h = lane >> 5, c = lane & 31;
+  if (a.causal && e == 0) return;  // block 0 has no far field
+  const size_t sidx = (static_cast<size_t>(bh) * a.nbS + e) * Cq + i;
+  const int nch = (Ck + JC - 1) / JC;
+  if (tid < 64) {
+    float mx = kNegInf;
+    for (int j = tid; j < Ck; j += 64) mx = fmaxf(mx, a.s_logz[sidx * Ck + j]);
+    mx = wave_max(mx);
+    float sm = 0.f;
+    for (int j = tid; j < Ck; j += 64) {
+      const float l = a.s_logz[sidx * Ck + j];
+      sm += l == kNegInf ? 0.f : __expf(l - mx);
+    }
+    sm = wave_sum(sm);
+    const float inv = sm > 0.f ? 1.f / sm : 0.f;
+    for (int j = tid; j < nch * JC; j += 64) {
+      const float l = j < Ck ? a.s_logz[sidx * Ck + j] : kNegInf;
+      sP[j] = l == kNegInf ? 0.f : __expf(l - mx) * inv;
+    }
+  }
+  f32x16_t acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = zero16();
+  for (int ch = 0; ch < nch; ++ch) {
+    const int j0 = ch * JC;
+    __syncthreads();  // sP written; the previous chunk consumed
+    for (int x = tid; x < JC * D / 4; x += 256) {
+      const int jj = x / (D / 4), d4 = (x % (D / 4)) * 4, j = j0 + jj;
+      f32x4_t k4 = {0.f, 0.f, 0.f, 0.f}, v4 = {0.f, 0.f, 0.f, 0.f};
+      if (j < Ck) {
+        k4 = *reinterpret_cast<const f32x4_t*>(a.s_k + (sidx * Ck + j) * D + d4);
+        v4 = *reinterpret_cast<const f32x4_t*>(a.s_v + (sidx * Ck + j) * D + d4);
+      }
+      u16x4_t kh, kl, vh, vl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        kh[q] = f32_to_bf16_bits(k4[q]);
+        kl[q] = f32_to_bf16_bits(k4[q] - bf16_to_f32(kh[q]));
+        vh[q] = f32_to_bf16_bits(v4[q]);
+        vl[q] = f32_to_bf16_bits(v4[q] - bf16_to_f32(vh[q]));
+      }
+      if (j < Ck) {
+        *reinterpret_cast<u16x4_t*>(a.t_khi + (sidx * Ck + j) * D + d4) = kh;
+        *reinterpret_cast<u16x4_t*>(a.t_klo + (sidx * Ck + j) * D + d4) = kl;
+        *reinterpret_cast<u16x4_t*>(a.t_vhi + (sidx * Ck + j) * D + d4) = vh;
+        *reinterpret_cast<u16x4_t*>(a.t_vlo + (sidx * Ck + j) * D + d4) = vl;
+      }
+      *reinterpret_cast<u16x4_t*>(sKh + jj * ST + d4) = kh;
+      *reinterpret_cast<u16x4_t*>(sKl + jj * ST + d4) = kl;
+      *reinterpret_cast<u16x4_t*>(sVh + jj * ST + d4) = vh;
+      *reinterpret_cast<u16x4_t*>(sVl + jj * ST + d4) = vl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < JC / 16; ++ks) {
+      const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(sP + j0 + 16 * ks + 8 * h);
+      const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(sP + j0 + 16 * ks + 8 * h + 4);
+      const float pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
+        const u16x8_t vh = __builtin_bit_cast(u16x8_t, lds_operand_tr(sVh, ST, 16 * ks, 32 * dvt, lane));
+        const u16x8_t vl = __builtin_bit_cast(u16x8_t, lds_operand_tr(sVl, ST, 16 * ks, 32 * dvt, lane));
+        float av[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) av[q] = (bf16_to_f32(vh[q]) + bf16_to_f32(vl[q])) * pw[q];
+        bf16x8_t ah, al;
+        split_bf16x8(av, ah, al);
+        const bf16x8_t kh = lds_operand_tr(sKh, ST, 16 * ks, 32 * dkt, lane);
+        const bf16x8_t kl = lds_operand_tr(sKl, ST, 16 * ks, 32 * dkt, lane);
+        acc[t] = mfma32(ah, kh, acc[t]);
+        acc[t] = mfma32(ah, kl, acc[t]);
+        acc[t] = mfma32(al, kh, acc[t]);
+      }
+    }
+  }
+  // lanes (c, h) hold rows dv = 32 dvt + 8 (v / 4) + 4 h + v % 4 of column dk = 32 dkt + c
+  const float* E = a.s_dip + sidx * D * D;
+  uint16_t* dip = a.t_dip + sidx * D * D;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const size_t o = static_cast<size_t>(32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3)) * D + 32 * dkt + c;
+      dip[o] = f32_to_bf16_bits(a.scale * (E[o] - acc[t][v]));
+    }
+  }
+}
+
 template <int D>
 static void launch_t(const S1Args& a, int which, hipStream_t s) {
   if (which == 0) {
@@ -1216,6 +1328,9 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
     constexpr int G = MomCfg<D>::G;
     ProfScope ps_("s1_moments_f16", s);
     hipLaunchKernelGGL((s1_moments_f16_kernel<D>), dim3(a.nmb, (a.Cq + G - 1) / G, a.BH), dim3(512), 0, s, a);
+  } else if (which == 5) {
+    ProfScope ps_("s1_dip_final", s);
+    hipLaunchKernelGGL((s1_dip_final_mfma_kernel<D>), dim3(a.Cq, a.nbS, a.BH), dim3(256), 0, s, a);
   } else if (which == 3) {
     ProfScope ps_("s1_finalize", s);
     hipLaunchKernelGGL((s1_finalize_acausal_kernel<D>), dim3(a.Cq, a.BH), dim3(256), 0, s, a);
@@ -1225,7 +1340,8 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
   }
 }
 
-// which: 0 scores, 1 atoms, 2 moments, 3 acausal table finalise, 4 causal scan
+// which: 0 scores, 1 atoms, 2 moments, 3 acausal table finalise, 4 causal scan,
+// 5 dipole finalise of the general path (bf16 tables)
 void launch_stage1_mfma(const S1Args& a, int which, hipStream_t s) {
   if (a.D == 64) launch_t<64>(a, which, s);
   else launch_t<128>(a, which, s);
