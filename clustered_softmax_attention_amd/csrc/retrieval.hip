@@ -19,6 +19,9 @@
 //                bucket's queries, merged by log-sum-exp into the far-field partial result.
 //   retr_exact_mfma  (bf16 inputs) the same on the matrix cores, one workgroup per
 //                chunk of up to 128 queries of one bucket (the stage-2 chunks).
+//   retr_moment_mfma (bf16 inputs) the second-moment part of retr_tables on the matrix
+//                cores, run before it (it needs the prefix log mass of the unmodified
+//                entry).
 #include "mfma.hpp"
 #include "muse_kernels.hpp"
 
@@ -229,7 +232,8 @@ __global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
       (isK ? a.s_k : a.s_v)[(sidx * Ck + j) * D + d] = any ? racc / rz : 0.f;
     }
   }
-  if (!a.dipole || Rpre == kNegInf) return;
+  // bf16 inputs: the second moment was handled by retr_moment_mfma
+  if (!a.dipole || Rpre == kNegInf || sizeof(T) == 2) return;
 
   // 2. second moment without the retrieved keys
   const int tr = tid / 16, tc = tid % 16;
@@ -544,12 +548,141 @@ __global__ void __launch_bounds__(256, 2) retr_exact_mfma_kernel(RetrArgs a) {
   if (h == 0) a.l_far[rowq] = Lt;
 }
 
+// Second moment without the retrieved keys for bf16 inputs, one workgroup of 4 waves per
+// (i, b): E_i[v k^T] of the entry becomes (E - sum_R w v k^T) / (1 - sum_R w), with
+// w_m = exp(s qbar_i . k_m - R) relative to the prefix log mass R. The retrieved keys
+// stream through LDS 32 at a time (K and V rows, exact in bf16); the weights in fp32, one
+// thread per key; sum_R (w v) k^T on the matrix cores with w v split into bf16 hi + lo.
+template <int D>
+__global__ void __launch_bounds__(256) retr_moment_mfma_kernel(RetrArgs a) {
+  constexpr int JC = 32, ST = D + 8, NDT = D / 32, TPW = NDT * NDT / 4, NP = JC * D / 8 / 256;
+  __shared__ __align__(16) uint16_t sK[JC * ST];
+  __shared__ __align__(16) uint16_t sV[JC * ST];
+  __shared__ float s_q[D];
+  __shared__ float sW[JC];
+  __shared__ float s_red[2];
+  __shared__ int s_start[kMaxRetrRow];
+  __shared__ int s_cum[kMaxRetrRow + 1];
+  __shared__ int s_nr;
+  const int i = blockIdx.x, b = blockIdx.y, bh = blockIdx.z;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int h = lane >> 5, c = lane & 31;
+  if (b == 0) return;
+  const int Ck = a.Ck, k1 = a.k1, k2 = a.k2, row = k1 * (1 + k2);
+  const size_t sidx = (static_cast<size_t>(bh) * a.nb + b) * a.Cq + i;
+  for (int d = tid; d < D; d += 256) s_q[d] = a.qbar[(static_cast<size_t>(bh) * a.Cq + i) * D + d];
+  if (wave == 0) {
+    // prefix log mass of the entry
+    float mx = kNegInf;
+    for (int j = lane; j < Ck; j += 64) mx = fmaxf(mx, a.s_logz[sidx * Ck + j]);
+    mx = wave_max(mx);
+    float sm = 0.f;
+    for (int j = lane; j < Ck; j += 64) {
+      const float l = a.s_logz[sidx * Ck + j];
+      if (l != kNegInf) sm += __expf(l - mx);
+    }
+    sm = wave_sum(sm);
+    if (lane == 0) s_red[0] = mx == kNegInf ? kNegInf : mx + __logf(sm);
+  } else if (wave == 1) {
+    const int32_t* sel = a.sel + sidx * row;
+    const int32_t* offk = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
+    const int n = retr_ranges(sel, offk, Ck, k1, k2, s_start, s_cum);
+    if (lane == 0) s_nr = n;
+  }
+  __syncthreads();
+  const float Rpre = s_red[0];
+  const int nr = s_nr, nR = s_cum[nr];
+  if (Rpre == kNegInf || nR == 0) return;  // uniform (LDS values)
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+  const int32_t* permk = a.perm_k + static_cast<size_t>(bh) * a.N;
+  f32x16_t acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = zero16();
+  float wsum = 0.f;  // threads 0..31: their keys' weights
+  for (int c0 = 0; c0 < nR; c0 += JC) {
+    __syncthreads();  // previous chunk consumed
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int x = tid + 256 * q, r = x / (D / 8), d8 = (x % (D / 8)) * 8, pos = c0 + r;
+      u16x8_t k8 = {0, 0, 0, 0, 0, 0, 0, 0}, v8 = k8;
+      if (pos < nR) {
+        int lo = 0, hi = nr - 1;  // last range with s_cum <= pos
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_cum[mid] <= pos) lo = mid;
+          else hi = mid - 1;
+        }
+        const size_t kr = static_cast<size_t>(permk[s_start[lo] + pos - s_cum[lo]]) * D + d8;
+        k8 = *reinterpret_cast<const u16x8_t*>(K + kr);
+        v8 = *reinterpret_cast<const u16x8_t*>(V + kr);
+      }
+      *reinterpret_cast<u16x8_t*>(sK + r * ST + d8) = k8;
+      *reinterpret_cast<u16x8_t*>(sV + r * ST + d8) = v8;
+    }
+    __syncthreads();
+    if (tid < JC) {
+      float w = 0.f;
+      if (c0 + tid < nR) {
+        float dot = 0.f;
+        for (int d = 0; d < D; ++d) dot = fmaf(s_q[d], bf16_to_f32(sK[tid * ST + d]), dot);
+        w = __expf(a.scale * dot - Rpre);
+      }
+      sW[tid] = w;
+      wsum += w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < JC / 16; ++ks) {
+      float pw[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pw[q] = sW[16 * ks + 8 * h + q];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
+        const u16x8_t vb = __builtin_bit_cast(u16x8_t, lds_operand_tr(sV, ST, 16 * ks, 32 * dvt, lane));
+        float av[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) av[q] = bf16_to_f32(vb[q]) * pw[q];
+        bf16x8_t ah, al;
+        split_bf16x8(av, ah, al);
+        const bf16x8_t kb = lds_operand_tr(sK, ST, 16 * ks, 32 * dkt, lane);
+        acc[t] = mfma32(ah, kb, acc[t]);
+        acc[t] = mfma32(al, kb, acc[t]);
+      }
+    }
+  }
+  if (wave == 0) {
+    const float ws = wave_sum(wsum);
+    if (lane == 0) s_red[1] = ws;
+  }
+  __syncthreads();
+  const float rest = 1.f - s_red[1];
+  const float inv = rest > 1e-30f ? 1.f / rest : 0.f;
+  float* dip = a.s_dip + sidx * D * D;  // [dv][dk], holds the prefix E[v k^T]
+  // lanes (c, h) hold rows dv = 32 dvt + 8 (v / 4) + 4 h + v % 4 of column dk = 32 dkt + c
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const size_t o = static_cast<size_t>(32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3)) * D + 32 * dkt + c;
+      dip[o] = (dip[o] - acc[t][v]) * inv;
+    }
+  }
+}
+
 hipError_t launch_retrieval(const RetrArgs& a, int phase, int dtype, hipStream_t s) {
   const dim3 g(a.Cq, a.nb, a.BH);
   if (phase == 0) {
     {
       ProfScope ps_("retr_select", s);
       hipLaunchKernelGGL(retr_select_kernel, g, dim3(64), 0, s, a);
+    }
+    if (dtype == 1 && a.dipole) {
+      ProfScope ps_("retr_moment_mfma", s);
+      if (a.D == 64) hipLaunchKernelGGL((retr_moment_mfma_kernel<64>), g, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((retr_moment_mfma_kernel<128>), g, dim3(256), 0, s, a);
     }
     ProfScope ps_("retr_tables", s);
     if (dtype == 0) {
