@@ -81,7 +81,10 @@ def kernel_work(name: str, cfg):
                         2.0 * BH * Cq * Ck * D * D),
         "s1_prefix": (table * (2 + 2 * D) * 4 + ftab, 0.0),
         "s1_mom_prefix": (BH * nmb * Cq * (D * D + 1) * 4 + dip32, 0.0),
-        "s1_dip_final": (ftab + 2 * dip32, 2.0 * BH * nb * Cq * Ck * D * D),
+        # fp32 tables: read K, V, E and write D_i; bf16 (matrix cores): read K, V, E and write the
+        # bf16 hi/lo tables and s D_i
+        "s1_dip_final": ((ftab + dip32 + tbytes + dip32 // 2) if e == 2 else (ftab + 2 * dip32),
+                         2.0 * BH * nb * Cq * Ck * D * D),
         "s1_pack": (ftab + dip32 + tbytes + dip32 // 2, 0.0),
         "s1_causal_scan": (table * (2 + 2 * D) * 4 + BH * nmb * Cq * (D * D + 1) * 4 + tbytes + BH * nb * Cq * D * D * 2,
                            2.0 * BH * nb * Cq * Ck * D * D),
