@@ -242,6 +242,25 @@ def test_fixed_labels_path(muse_lib):
     assert rel <= TOL["bf16"]
 
 
+def test_fixed_labels_hierarchical(muse_lib):
+    # caller-fixed labels with the hierarchical decomposition (6 blocks: blocks 3 and 5 see
+    # two squares) and an empty key cluster
+    from oracle import muse_causal
+    cfg = scaled_config("causal_16k", B=1, H=1, N=1536, block=256, Cq=6, Ck=20)
+    q, k, v = make_inputs(cfg)
+    rng = np.random.default_rng(6)
+    lq = rng.integers(0, cfg.Cq, size=(1, 1, cfg.N)).astype(np.int32)
+    lk = rng.integers(0, cfg.Ck, size=(1, 1, cfg.N)).astype(np.int32)
+    lk[0, 0, lk[0, 0] == 7] = 8
+    out, _ = run_gpu(cfg, q, k, v, labels_q_in=torch.from_numpy(lq), labels_k_in=torch.from_numpy(lk),
+                     hierarchy=True)
+    r = muse_causal(q[0, 0], k[0, 0], v[0, 0], cfg.Cq, cfg.Ck, 1, cfg.block, labels_q=lq[0, 0],
+                    labels_k=lk[0, 0], hierarchical=True)
+    rel = rel_l2(out.float().cpu().numpy()[0, 0], r.o)
+    log(f"fixed labels, hierarchy: rel-L2 {rel:.3e}")
+    assert rel <= TOL["bf16"]
+
+
 def test_deterministic_bitwise(muse_lib):
     cfg = scaled_config("causal_16k", B=1, H=2, N=2048, block=512)
     q, k, v = make_inputs(cfg)
