@@ -11,20 +11,25 @@ from workloads import make_inputs, scaled_config
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,over", [
-    ("acausal_8k", {"B": 1, "H": 2, "N": 1536}),
-    ("causal_16k", {"B": 1, "H": 2, "N": 2048, "block": 512}),
+@pytest.mark.parametrize("name,over,hier", [
+    ("acausal_8k", {"B": 1, "H": 2, "N": 1536}, False),
+    ("causal_16k", {"B": 1, "H": 2, "N": 2048, "block": 512}, False),
+    # the general stage-1 path: the hierarchical squares, and retrieval
+    ("causal_16k", {"B": 1, "H": 2, "N": 3072, "block": 512}, True),
+    ("retrieval_16k", {"B": 1, "H": 2, "N": 2048, "block": 256}, False),
 ])
-def test_graph_replay_matches_eager(muse_lib, name, over):
+def test_graph_replay_matches_eager(muse_lib, name, over, hier):
     from clustered_softmax_attention_amd import binding
     cfg = scaled_config(name, **over)
     q, k, v = (to_device(t, cfg.dtype) for t in make_inputs(cfg))
-    ws = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, cfg.causal, cfg.block, 1),
+    ws = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, cfg.causal, cfg.block, 1,
+                                             cfg.topk_clusters, cfg.topk_blocks, hierarchy=hier),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)
 
     def step():
         binding.attn_fwd(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, causal=cfg.causal, block=cfg.block, out=out,
+                         topk_clusters=cfg.topk_clusters, topk_blocks=cfg.topk_blocks, hierarchy=hier,
                          workspace=ws)
 
     s = torch.cuda.Stream()
