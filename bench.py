@@ -48,12 +48,14 @@ METRIC = "MuSe fwd tokens/s at 8k and 64k; speedup vs exact attn; % MFMA/HBM roo
 SECONDARY = "causal_64k_d128"  # the 64k configuration reported beside the 8k one
 
 
-def kernel_work(name: str, cfg):
+def kernel_work(name: str, cfg, hier: bool = False):
     """(algorithmic bytes, algorithmic flops) of ONE launch of a library kernel on this
     workload, or None when the kernel is not listed. Bytes count every tensor a launch
     must read or write at least once (inputs read once, outputs written once); flops count
     the arithmetic the method defines (multiply-add = 2), not the extra products of the
-    bf16 hi/lo splits. Causal tables have one entry per block (nbS = nb)."""
+    bf16 hi/lo splits. Causal tables have one entry per block (nbS = nb). With the
+    hierarchical decomposition (hier) stage 2 of block b reads popcount(b) entries, so
+    entry e is read lowbit(e) times: its table reads scale by sum_b popcount(b) / (nb - 1)."""
     BH, N, D, Cq, Ck = cfg.B * cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck
     e = 2 if cfg.dtype == "bf16" else 4
     nb = cfg.N // cfg.block if cfg.causal else 1
@@ -69,6 +71,7 @@ def kernel_work(name: str, cfg):
     tbytes = table * (4 + 8 * D)            # log Z + bf16 hi/lo of K_ij and of V_ij
     ftab = table * (1 + 2 * D) * 4          # fp32 log Z, K_ij, V_ij
     dip32 = BH * nb * Cq * D * D * 4         # fp32 dipole (or E[v k^T]) per table entry
+    reads = (sum(bin(b).count("1") for b in range(nb)) / (nb - 1)) if (hier and nb > 1) else 1.0
     w = {
         "kmeans_assign_mfma": (2 * x + 2 * BH * N * 4, 2.0 * BH * N * (Cq + Ck) * D),
         "kmeans_assign": (2 * x + 2 * BH * N * 4, 2.0 * BH * N * (Cq + Ck) * D),
@@ -88,7 +91,8 @@ def kernel_work(name: str, cfg):
         "s1_pack": (ftab + dip32 + tbytes + dip32 // 2, 0.0),
         "s1_causal_scan": (table * (2 + 2 * D) * 4 + BH * nmb * Cq * (D * D + 1) * 4 + tbytes + BH * nb * Cq * D * D * 2,
                            2.0 * BH * nb * Cq * Ck * D * D),
-        "s2_mfma": (x + x + tbytes + BH * nb * Cq * D * D * 2, 2.0 * BH * N * (2 * Ck * D + D * D)),
+        "s2_mfma": (x + x + reads * (tbytes + BH * nb * Cq * D * D * 2),
+                    2.0 * BH * N * (2 * Ck * D + D * D) * reads),
         "s2_refine": (x + x + table * (1 + 2 * D) * 4 + BH * nb * Cq * D * D * 4, 2.0 * BH * N * (2 * Ck * D + D * D)),
         "local_block_mfma": (3 * x + BH * N * D * 4, 4.0 * BH * N * (cfg.block / 2) * D),
         "exact_mfma": (4 * x, (2.0 if cfg.causal else 4.0) * BH * N * N * D),
@@ -97,10 +101,10 @@ def kernel_work(name: str, cfg):
     return w.get(name)
 
 
-def roofline_entry(name: str, cfg, avg_s: float):
+def roofline_entry(name: str, cfg, avg_s: float, hier: bool = False):
     """Roofline of one kernel from its measured average launch duration: memory-bound when
     its arithmetic intensity is below the ridge point, else matrix-core-bound."""
-    wk = kernel_work(name, cfg)
+    wk = kernel_work(name, cfg, hier)
     if wk is None:
         return None
     nbytes, flops = wk
@@ -200,6 +204,9 @@ def main():
                     help="with the default workload, skip the 64k causal configuration reported beside it")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-peaks", action="store_true", help="skip the copy and GEMM reference measurements")
+    ap.add_argument("--hierarchy", action="store_true",
+                    help="time the hierarchical causal decomposition instead of the prefix form "
+                         "(causal workloads without retrieval)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run K device-to-device copies of MIB MiB (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -223,7 +230,7 @@ def main():
     from clustered_softmax_attention_amd import binding
 
     binding.load()
-    res = measure(args.workload, args.steps, args.warmup, not args.no_exact)
+    res = measure(args.workload, args.steps, args.warmup, not args.no_exact, args.hierarchy)
     cfg = res["cfg"]
     cpu = None
     if not args.no_cpu:
@@ -254,7 +261,8 @@ def main():
         "data": "synthetic Gaussian-mixture Q/K/V (seeded), no dataset",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload, "global_batch": cfg.B,
                    "seq_len": cfg.N, "heads": cfg.H, "head_dim": cfg.D, "Cq": cfg.Cq, "Ck": cfg.Ck,
-                   "kmeans_iters": cfg.iters, "causal": cfg.causal, "block": cfg.block},
+                   "kmeans_iters": cfg.iters, "causal": cfg.causal, "block": cfg.block,
+                   "hierarchy": bool(args.hierarchy)},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "kernels": res["kernels"],
@@ -305,7 +313,7 @@ def measured_peaks() -> dict:
             "published_hbm_GBps": PEAK_HBM_GBS, "published_bf16_TFLOPs": PEAK_BF16_MFMA_TFLOPS}
 
 
-def measure(name: str, steps: int, warmup: int, exact: bool) -> dict:
+def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = False) -> dict:
     """Time `steps` MuSe forward calls of workload `name` after `warmup` (whole step on
     the GPU, inputs resident), then the per-kernel HIP-event durations over a second pass,
     the roofline of the dominant kernel and, with `exact`, the in-library exact attention."""
@@ -314,18 +322,21 @@ def measure(name: str, steps: int, warmup: int, exact: bool) -> dict:
     from workloads import CONFIGS, make_inputs
 
     cfg = CONFIGS[name]
+    if hierarchy and (not cfg.causal or cfg.topk_clusters > 0):
+        raise SystemExit(f"--hierarchy needs a causal workload without retrieval, not {name}")
     q, k, v = make_inputs(cfg)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     Q, K, V = (torch.from_numpy(t).cuda().to(tdt) for t in (q, k, v))
     ws = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, cfg.causal,
                                              cfg.block, 1 if cfg.dtype == "bf16" else 0,
-                                             cfg.topk_clusters, cfg.topk_blocks),
+                                             cfg.topk_clusters, cfg.topk_blocks, hierarchy=hierarchy),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(Q)
 
     def muse_step():
         binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=cfg.causal, block=cfg.block, out=out,
-                         topk_clusters=cfg.topk_clusters, topk_blocks=cfg.topk_blocks, workspace=ws)
+                         topk_clusters=cfg.topk_clusters, topk_blocks=cfg.topk_blocks, workspace=ws,
+                         hierarchy=hierarchy)
 
     print(f"# timing {name}: {warmup} warmup + {steps} steps", file=sys.stderr, flush=True)
     ms, wall = timed(muse_step, steps, warmup)
@@ -342,12 +353,13 @@ def measure(name: str, steps: int, warmup: int, exact: bool) -> dict:
     kernels = {n: {"avg_us": 1e3 * t / c, "launches_per_step": c / steps} for n, (t, c) in prof.items()}
     # dominant kernel: the largest share of the step among those with a defined roofline
     ranked = sorted(prof.items(), key=lambda kv: -kv[1][0])
-    dom = next(n for n, _ in ranked if kernel_work(n, cfg) is not None)
+    dom = next(n for n, _ in ranked if kernel_work(n, cfg, hierarchy) is not None)
     avg_s = prof[dom][0] / prof[dom][1] / 1e3
-    roofline = {"kernel": dom, **roofline_entry(dom, cfg, avg_s), "traffic": measured_traffic(name, dom),
+    profile = name + ("_hierarchy" if hierarchy else "")
+    roofline = {"kernel": dom, **roofline_entry(dom, cfg, avg_s, hierarchy), "traffic": measured_traffic(profile, dom),
                 "share_of_step": prof[dom][0] / sum(t for t, _ in prof.values())}
     for n, d in kernels.items():
-        r = roofline_entry(n, cfg, prof[n][0] / prof[n][1] / 1e3)
+        r = roofline_entry(n, cfg, prof[n][0] / prof[n][1] / 1e3, hierarchy)
         if r is not None:
             d.update({"bound": r["bound"], "frac": r["frac"]})
     print(f"# kernels: " + ", ".join(f"{n} {d['avg_us']:.1f}us x{d['launches_per_step']:.0f}"
@@ -394,7 +406,7 @@ def measure(name: str, steps: int, warmup: int, exact: bool) -> dict:
                 "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in prof_u.items() if "untilted" in n or "cov" in n}}
             print(f"# untilted dipole: {ms_u:.3f} ms/step, speedup {ms_ex / ms_u:.2f}x, RSE {rse_u:.3e}, "
                   f"{extra['untilted_dipole']['kernels_us']}", file=sys.stderr, flush=True)
-        elif cfg.topk_clusters == 0:
+        elif cfg.topk_clusters == 0 and not hierarchy:
             # the same workload with the hierarchical block decomposition (one two-stage
             # approximation per square below the diagonal, log-sum-exp merged)
             ws_h = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, True, cfg.block,

@@ -38,6 +38,17 @@ def test_moments_accounting_by_hand():
     assert flops == 2.0 * 16 * 32 * 65536 * 128 * 128
 
 
+def test_hierarchical_stage2_reads_by_hand():
+    # 32 blocks: block b reads popcount(b) table entries, 80 reads over blocks 1..31
+    cfg = CONFIGS["causal_64k_d128"]
+    base, fl = bench.kernel_work("s2_mfma", cfg)
+    hb, hfl = bench.kernel_work("s2_mfma", cfg, hier=True)
+    assert sum(bin(b).count("1") for b in range(32)) == 80
+    x = 16 * 65536 * 128 * 2
+    assert hb - 2 * x == pytest.approx((base - 2 * x) * 80 / 31)
+    assert hfl == pytest.approx(fl * 80 / 31)
+
+
 def test_roofline_classification_and_fraction():
     cfg = CONFIGS["acausal_8k"]
     nbytes, flops = bench.kernel_work("kmeans_assign_mfma", cfg)
