@@ -1,7 +1,7 @@
 """Throughput of the MuSe forward pass on one MI355X, with roofline and CPU-oracle baseline.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload acausal_8k] [--no-cpu]
-                [--no-exact] [--no-secondary] [--no-peaks]
+                [--no-exact] [--no-secondary] [--no-peaks] [--hierarchy]
 
 A step is one muse_attn_fwd call over the whole workload batch (K-means, stage 1,
 stage 2 and, when causal, the exact diagonal blocks), with inputs resident in HBM and
