@@ -302,11 +302,12 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 1) s1_atoms_mfma_kernel(S1A
 
 // Buckets of several work items: the items' partial atoms folded in item order with the
 // log-sum-exp rule (running max M, sums rescaled by exp(m - M)) into the bucket's atom.
-// kMergeGrid workgroups of 1024 threads per head walk the list of such buckets; threads
-// over the (centroid, float4 of the K and V sums) pairs, four items per batch with all
-// of a batch's loads in flight (one batch for buckets of up to 4 kAtomSeg keys).
-template <int D>
-__global__ void __launch_bounds__(1024) s1_atoms_merge_kernel(S1Args a) {
+// kMergeGrid workgroups of NT threads per head walk the list of such buckets (NT = 512
+// when the Cq D / 2 pairs fit, else 1024); threads over the (centroid, float4 of the K
+// and V sums) pairs, four items per batch with all of a batch's loads in flight (one
+// batch for buckets of up to 4 kAtomSeg keys).
+template <int D, int NT>
+__global__ void __launch_bounds__(NT) s1_atoms_merge_kernel(S1Args a) {
   constexpr int F4 = D / 2;  // float4s of one centroid's K and V sums
   constexpr int QB = 4;
   const int bh = blockIdx.y, tid = threadIdx.x;
@@ -323,7 +324,7 @@ __global__ void __launch_bounds__(1024) s1_atoms_merge_kernel(S1Args a) {
     const int u = e4.x, ni = e4.z, bp = u / Ck, j = u % Ck;
     const size_t pb = static_cast<size_t>(bh) * atom_max_partials(a.N) + e4.y;
     const size_t abase = (static_cast<size_t>(bh) * a.nb + bp) * Cq;
-    for (int e = tid; e < Cq * F4; e += 1024) {
+    for (int e = tid; e < Cq * F4; e += NT) {
       const int i = e / F4, f = e % F4;
       const bool isv = f >= D / 4;
       const int d4 = 4 * (isv ? f - D / 4 : f);
@@ -1322,7 +1323,9 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
     // merged atoms
     if (a.causal || a.retr != nullptr) {
       ProfScope ps_("s1_atoms_merge", s);
-      hipLaunchKernelGGL((s1_atoms_merge_kernel<D>), dim3(std::min(kMergeGrid, atom_max_multi(a.N)), a.BH), dim3(1024), 0, s, a);
+      const dim3 gm(std::min(kMergeGrid, atom_max_multi(a.N)), a.BH);
+      if (a.Cq * (D / 2) <= 512) hipLaunchKernelGGL((s1_atoms_merge_kernel<D, 512>), gm, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((s1_atoms_merge_kernel<D, 1024>), gm, dim3(1024), 0, s, a);
     }
   } else if (which == 2) {
     constexpr int G = MomCfg<D>::G;
