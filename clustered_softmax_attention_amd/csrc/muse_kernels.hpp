@@ -168,6 +168,7 @@ struct S2Args {
   float scale;
   int dipole;
   int hier;                    // causal: merge the entries b, b & (b - 1), ... > 0
+  int level;                   // matrix-core path with hier: the chain entry of this launch
   int out_bf16;
   const int32_t* labels_q;     // [BH, N]
   const float* qbar;           // [BH, Cq, D]

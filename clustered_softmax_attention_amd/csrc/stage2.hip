@@ -139,8 +139,10 @@ struct S2Cfg {
   static constexpr int ND = D * D / 8 / 256;    // 16-byte dipole pieces per thread
 };
 
-// HIER: the hierarchical squares (entries b, b & (b - 1), ...); each further square is
-// merged into the far field already written (o_far, l_far: this lane's own elements).
+// HIER: one further square of the hierarchy per launch: entry e = b with its lowest set
+// bit cleared `level` times (blocks with fewer squares leave at once), merged by
+// log-sum-exp into the far field the earlier launches wrote (o_far, l_far); the first
+// square of every block is the single entry of the HIER = false instance.
 template <int D, bool HIER>
 __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a) {
   using Cfg = S2Cfg<D>;
@@ -180,9 +182,12 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
     }
     return;
   }
-  // table entries: e = b (one entry; acausal: 0), or with the hierarchy the squares
-  // e = b, b & (b - 1), ... > 0, merged by log-sum-exp in that order
+  // the table entry: e = b (acausal: 0), or the level-th square of the block's chain
   int e = a.causal ? b : 0;
+  if (HIER) {
+    for (int t = 0; t < a.level; ++t) e &= e - 1;
+    if (e == 0) return;  // fewer squares: the whole workgroup leaves together
+  }
   const int Ck = a.Ck, njc = (Ck + JC - 1) / JC;
   const uint16_t *khi, *klo, *vhi, *vlo, *dip;
   const float* lz;
@@ -260,8 +265,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
   }
 
   const float sl2 = a.scale * 1.4426950408889634f;
-  float Lf = kNegInf;  // log-mass of the far field merged so far (this lane's query)
-  for (bool first = true;; first = false) {
+  {
     float mx = kNegInf, z = 0.f;  // running max (log2 units) and sum of this lane pair's query
     f32x16_t o[NMT];
 #pragma unroll
@@ -341,13 +345,6 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
         }
       }
     }
-    // the next square's first chunk and dipole travel while this one is finished
-    const int enext = HIER ? (e & (e - 1)) : 0;
-    if (enext > 0) {
-      set_entry(enext);
-      load_chunk(0);
-      load_dip();
-    }
     if (nw > 0) {
       const float invz = z > 0.f ? 1.f / z : 0.f;  // z == 0: no far-field key at all
 #pragma unroll
@@ -365,10 +362,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
       }
       float L = z > 0.f ? (mx + __log2f(z)) * 0.6931471805599453f : kNegInf;
       // lanes (c, h) hold rows d = 32 mt + 8 g + 4 h + r of query c
-      if (valid && !first) {
-        // log-sum-exp merge of this square into the far field written so far (each lane
-        // reads back only the elements it wrote itself)
-        const float L0 = Lf;
+      if (valid && HIER) {
+        // log-sum-exp merge of this square into the far field of the earlier launches
+        const float L0 = a.l_far[row];
         const float Ln = L0 == kNegInf ? L : (L == kNegInf ? L0 : fmaxf(L0, L) + log1pf(__expf(-fabsf(L0 - L))));
         const float w0 = L0 == kNegInf ? 0.f : __expf(L0 - Ln), w1 = L == kNegInf ? 0.f : __expf(L - Ln);
 #pragma unroll
@@ -381,7 +377,6 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
           }
         L = Ln;
       }
-      Lf = L;
       if (valid && a.causal) {
         if (h == 0) a.l_far[row] = L;
 #pragma unroll
@@ -409,10 +404,6 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
           }
       }
     }
-    if (enext == 0) break;
-    e = enext;
-    __syncthreads();  // every wave has read this square's dipole
-    store_dip();
   }
 }
 
@@ -421,11 +412,21 @@ hipError_t launch_stage2(const S2Args& a, int dtype, hipStream_t s) {
     ProfScope ps_("s2_mfma", s);
     const dim3 gm(a.max_tiles, a.BH);
     if (a.D == 64) {
-      if (a.hier) hipLaunchKernelGGL((s2_mfma_kernel<64, true>), gm, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((s2_mfma_kernel<64, false>), gm, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((s2_mfma_kernel<64, false>), gm, dim3(256), 0, s, a);
     } else {
-      if (a.hier) hipLaunchKernelGGL((s2_mfma_kernel<128, true>), gm, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((s2_mfma_kernel<128, false>), gm, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((s2_mfma_kernel<128, false>), gm, dim3(256), 0, s, a);
+    }
+    if (a.causal && a.hier) {
+      // the further squares of the hierarchy, one chain level per launch (at most the bit
+      // length of nb - 1 squares per block)
+      int levels = 0;
+      for (int x = a.nb - 1; x > 0; x >>= 1) ++levels;
+      S2Args al = a;
+      for (int lv = 1; lv < levels; ++lv) {
+        al.level = lv;
+        if (a.D == 64) hipLaunchKernelGGL((s2_mfma_kernel<64, true>), gm, dim3(256), 0, s, al);
+        else hipLaunchKernelGGL((s2_mfma_kernel<128, true>), gm, dim3(256), 0, s, al);
+      }
     }
     return hipGetLastError();
   }
