@@ -48,20 +48,56 @@ METRIC = "MuSe fwd tokens/s at 8k and 64k; speedup vs exact attn; % MFMA/HBM roo
 SECONDARY = "causal_64k_d128"  # the 64k configuration reported beside the 8k one
 
 
-def kernel_work(name: str, cfg, hier: bool = False):
+def retrieval_counts(cfg, ex) -> dict:
+    """Per-call sums over (head, query cluster i, block b >= 1) of the retrieved key count
+    nR(i, b) and of nq(i, b) * nR(i, b) (queries of cluster i in block b times the keys they
+    attend exactly), from a traced call's selections and bucket offsets (integer outputs of
+    the library: [B,H,nb,Cq,k1,1+k2] cluster ids then block ids, -1 = none)."""
+    sel = ex["retrieval_trace"].cpu().numpy()
+    offs_k = ex["offs_k"].cpu().numpy().astype(np.int64)
+    offs_q = ex["offs_q"].cpu().numpy().astype(np.int64)
+    Ck, Cq = cfg.Ck, cfg.Cq
+    nr_sum = nqr_sum = 0
+    B, H, nb = sel.shape[:3]
+    for b_ in range(B):
+        for h in range(H):
+            bucket = np.diff(offs_k[b_, h])          # [nb*Ck] keys per (block, cluster)
+            qcount = np.diff(offs_q[b_, h])          # [nb*Cq]
+            for b in range(1, nb):
+                for i in range(Cq):
+                    nr = 0
+                    for row in sel[b_, h, b, i]:
+                        j = int(row[0])
+                        if j < 0:
+                            continue
+                        for bp in row[1:]:
+                            if bp >= 0:
+                                nr += int(bucket[int(bp) * Ck + j])
+                    nr_sum += nr
+                    nqr_sum += nr * int(qcount[b * Cq + i])
+    return {"nR": nr_sum, "nqR": nqr_sum}
+
+
+def kernel_work(name: str, cfg, hier: bool = False, ctx: dict = None):
     """(algorithmic bytes, algorithmic flops) of ONE launch of a library kernel on this
     workload, or None when the kernel is not listed. Bytes count every tensor a launch
     must read or write at least once (inputs read once, outputs written once); flops count
     the arithmetic the method defines (multiply-add = 2), not the extra products of the
-    bf16 hi/lo splits. Causal tables have one entry per block (nbS = nb). With the
-    hierarchical decomposition (hier) stage 2 of block b reads popcount(b) entries, so
-    entry e is read lowbit(e) times: its table reads scale by sum_b popcount(b) / (nb - 1);
-    stage 2 then runs one launch per chain level (the bit length of nb - 1), each reading
-    the queries and writing the far field; the figure is per call, as the library's
-    HIP-event scope covers those launches together."""
+    bf16 hi/lo splits. Causal tables have one entry per block (nbS = nb); a causal far
+    field exists for blocks b >= 1 only and is an fp32 partial result (o_far, l_far).
+
+    Hierarchical decomposition (hier): block b >= 1 sees popcount(b) squares; stage 2 runs
+    one launch per chain level, and the launch that adds a square to block b reads the
+    block's queries and the square's table entry and writes the fp32 far field, which
+    every launch after the first also reads. The figure is per call, as the library's
+    HIP-event scope covers those launches together.
+
+    Retrieval kernels need ctx = retrieval_counts(...): the retrieved key counts are
+    data-dependent."""
     BH, N, D, Cq, Ck = cfg.B * cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck
     e = 2 if cfg.dtype == "bf16" else 4
     nb = cfg.N // cfg.block if cfg.causal else 1
+    blk = cfg.block if cfg.causal else N
     if cfg.causal or cfg.dtype != "bf16":
         mbk = cfg.block if cfg.causal else N
     else:  # the library's acausal moment slices: about 256 workgroups, multiples of 128 keys
@@ -74,8 +110,21 @@ def kernel_work(name: str, cfg, hier: bool = False):
     tbytes = table * (4 + 8 * D)            # log Z + bf16 hi/lo of K_ij and of V_ij
     ftab = table * (1 + 2 * D) * 4          # fp32 log Z, K_ij, V_ij
     dip32 = BH * nb * Cq * D * D * 4         # fp32 dipole (or E[v k^T]) per table entry
-    reads = (sum(bin(b).count("1") for b in range(nb)) / (nb - 1)) if (hier and nb > 1) else 1.0
-    levels = (nb - 1).bit_length() if (hier and nb > 1) else 1
+    far_rows = BH * (N - blk) if cfg.causal else 0   # rows with a far field
+    far = far_rows * (D + 1) * 4            # fp32 o_far + l_far of those rows
+    s2_flops_row = 2.0 * (2 * Ck * D + D * D)
+    if cfg.causal:
+        # one entry per block b >= 1: bf16 tables and s D_i
+        entry = Cq * Ck * (4 + 8 * D) + Cq * D * D * 2 if e == 2 else Cq * Ck * (1 + 2 * D) * 4 + Cq * D * D * 4
+        if hier and nb > 1:
+            pc = [bin(b).count("1") for b in range(nb)]
+            per_head = sum(c * (blk * D * e + entry + blk * (D + 1) * 4) + (c - 1) * blk * (D + 1) * 4
+                           for c in pc[1:])
+            s2 = (BH * per_head, BH * s2_flops_row * blk * sum(pc[1:]))
+        else:
+            s2 = (far_rows * D * e + far + BH * (nb - 1) * entry, s2_flops_row * far_rows)
+    else:
+        s2 = (2 * x + tbytes + BH * Cq * D * D * 2, s2_flops_row * BH * N)
     w = {
         "kmeans_assign_mfma": (2 * x + 2 * BH * N * 4, 2.0 * BH * N * (Cq + Ck) * D),
         "kmeans_assign": (2 * x + 2 * BH * N * 4, 2.0 * BH * N * (Cq + Ck) * D),
@@ -95,20 +144,42 @@ def kernel_work(name: str, cfg, hier: bool = False):
         "s1_pack": (ftab + dip32 + tbytes + dip32 // 2, 0.0),
         "s1_causal_scan": (table * (2 + 2 * D) * 4 + BH * nmb * Cq * (D * D + 1) * 4 + tbytes + BH * nb * Cq * D * D * 2,
                            2.0 * BH * nb * Cq * Ck * D * D),
-        "s2_mfma": (levels * 2 * x + reads * (tbytes + BH * nb * Cq * D * D * 2),
-                    2.0 * BH * N * (2 * Ck * D + D * D) * reads),
-        "s2_refine": (x + x + table * (1 + 2 * D) * 4 + BH * nb * Cq * D * D * 4, 2.0 * BH * N * (2 * Ck * D + D * D)),
-        "local_block_mfma": (3 * x + BH * N * D * 4, 4.0 * BH * N * (cfg.block / 2) * D),
+        "s2_mfma": s2,
+        "s2_refine": (x + (far if cfg.causal else x) + table * (1 + 2 * D) * 4 + BH * nb * Cq * D * D * 4,
+                      s2_flops_row * (far_rows if cfg.causal else BH * N)),
+        # the diagonal blocks: Q, K, V and the far field read, the output written
+        "local_block_mfma": (4 * x + far, 4.0 * BH * N * (blk / 2) * D),
         "exact_mfma": (4 * x, (2.0 if cfg.causal else 4.0) * BH * N * N * D),
         "exact_valu": (4 * x, (2.0 if cfg.causal else 4.0) * BH * N * N * D),
+        # untilted dipole: per key cluster covariance (keys and values read once), then
+        # D_i = sum_j P_ij Cov_j (covariances and log Z read, s D_i written)
+        "s1_cluster_cov": (2 * x + BH * Ck * D * D * 4, 2.0 * BH * N * D * D),
+        "s1_untilted_dip": (BH * Ck * D * D * 4 + BH * Cq * Ck * 4 + BH * Cq * D * D * e, 2.0 * BH * Cq * Ck * D * D),
     }
+    if cfg.topk_clusters and ctx is not None:
+        k1, k2 = cfg.topk_clusters, cfg.topk_blocks
+        cells = BH * (nb - 1) * Cq                   # (head, i, b >= 1)
+        w.update({
+            # prefix log Z and every atom's log mass read once, the selections written
+            "retr_select": (BH * nb * Cq * Ck * 4 * 3 + cells * k1 * (1 + k2) * 4, 0.0),
+            # per (i, b): the chosen clusters' prefix entries and retrieved atoms read, their
+            # remainder entries written
+            "retr_tables": (cells * (k1 * (1 + k2) * (2 + 2 * D) * 4 + k1 * (1 + 2 * D) * 4), 0.0),
+            # per (i, b): the retrieved rows of K and V, the entry's moment read and written;
+            # sum over retrieved keys of w v k^T
+            "retr_moment_mfma": (ctx["nR"] * 2 * D * e + cells * D * D * 8, 2.0 * D * D * ctx["nR"]),
+            # queries with a far field, the retrieved rows (once per (i, b)), the far field
+            # read and written; q.k and p v for every (query, retrieved key)
+            "retr_exact_mfma": (far_rows * D * e + ctx["nR"] * 2 * D * e + 2 * far, 4.0 * D * ctx["nqR"]),
+            "retr_exact": (far_rows * D * e + ctx["nR"] * 2 * D * e + 2 * far, 4.0 * D * ctx["nqR"]),
+        })
     return w.get(name)
 
 
-def roofline_entry(name: str, cfg, avg_s: float, hier: bool = False):
+def roofline_entry(name: str, cfg, avg_s: float, hier: bool = False, ctx: dict = None):
     """Roofline of one kernel from its measured average launch duration: memory-bound when
     its arithmetic intensity is below the ridge point, else matrix-core-bound."""
-    wk = kernel_work(name, cfg, hier)
+    wk = kernel_work(name, cfg, hier, ctx)
     if wk is None:
         return None
     nbytes, flops = wk
@@ -168,16 +239,42 @@ def timed(fn, steps: int, warmup: int):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def cpu_baseline(cfg, q, k, v, budget_s: float):
-    """The CPU oracle (unchanged) on whole heads of the same workload until the time budget
-    is used; tokens/s scaled to the whole job (every token needs all H heads)."""
-    from oracle import muse_acausal, muse_causal
+def host_cpu_info() -> dict:
+    """The host the CPU baseline ran on: logical CPUs, those this process may use, the CPU
+    model (from /proc/cpuinfo) and the BLAS thread pool size (threadpoolctl, else
+    OMP_NUM_THREADS)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    blas = None
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] or [os.cpu_count() or 1])
+        blas = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [0]) or None
     except Exception:
-        threads = os.cpu_count() or 1
+        pass
+    if blas is None:
+        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    return {"host_cpus": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model, "blas_threads": blas}
+
+
+def cpu_baseline(cfg, q, k, v, budget_s: float):
+    """The CPU oracle (unchanged) on whole heads of the same workload until the time budget
+    is used; tokens/s scaled to the whole job (every token needs all H heads). `cores` is
+    the number of threads the oracle computes with: its matrix products run on the BLAS
+    thread pool, everything else on one thread."""
+    from oracle import muse_acausal, muse_causal
+    host = host_cpu_info()
     heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
     t0 = time.perf_counter()
     done = 0
@@ -191,9 +288,9 @@ def cpu_baseline(cfg, q, k, v, budget_s: float):
             break
     t = time.perf_counter() - t0
     tok_s = cfg.N * done / (t * cfg.H)
-    return {"value": tok_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": tok_s, "unit": "tokens/s", "cores": int(host["blas_threads"]), "kind": "oracle",
             "sample": f"{done} of {cfg.B * cfg.H} heads of the same workload ({t:.1f} s), "
-                      f"scaled as N*heads_done/(t*H)"}
+                      f"scaled as N*heads_done/(t*H)", **host}
 
 
 def main():
@@ -355,18 +452,27 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
     prof = binding.prof_collect()
     binding.prof_enable(False)
     kernels = {n: {"avg_us": 1e3 * t / c, "launches_per_step": c / steps} for n, (t, c) in prof.items()}
+    ctx = None
+    if cfg.topk_clusters:
+        # retrieved key counts (data-dependent) from one traced call: selections and buckets
+        _, ex_r = binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=cfg.causal, block=cfg.block,
+                                   topk_clusters=cfg.topk_clusters, topk_blocks=cfg.topk_blocks,
+                                   return_trace=True, return_buckets=True)
+        torch.cuda.synchronize()
+        ctx = retrieval_counts(cfg, ex_r)
+        del ex_r
     # dominant kernel: the largest share of the step among those with a defined roofline
     ranked = sorted(prof.items(), key=lambda kv: -kv[1][0])
-    dom = next(n for n, _ in ranked if kernel_work(n, cfg, hierarchy) is not None)
+    dom = next(n for n, _ in ranked if kernel_work(n, cfg, hierarchy, ctx) is not None)
     avg_s = prof[dom][0] / prof[dom][1] / 1e3
     profile = name + ("_hierarchy" if hierarchy else "")
     # with the hierarchy, stage 2 is several dispatches per call (one per chain level) while
     # the counters are per dispatch: no per-call traffic figure for it
     traffic = None if (hierarchy and dom == "s2_mfma") else measured_traffic(profile, dom)
-    roofline = {"kernel": dom, **roofline_entry(dom, cfg, avg_s, hierarchy), "traffic": traffic,
+    roofline = {"kernel": dom, **roofline_entry(dom, cfg, avg_s, hierarchy, ctx), "traffic": traffic,
                 "share_of_step": prof[dom][0] / sum(t for t, _ in prof.values())}
     for n, d in kernels.items():
-        r = roofline_entry(n, cfg, prof[n][0] / prof[n][1] / 1e3, hierarchy)
+        r = roofline_entry(n, cfg, prof[n][0] / prof[n][1] / 1e3, hierarchy, ctx)
         if r is not None:
             d.update({"bound": r["bound"], "frac": r["frac"]})
     print(f"# kernels: " + ", ".join(f"{n} {d['avg_us']:.1f}us x{d['launches_per_step']:.0f}"
@@ -439,6 +545,8 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
                 "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in sorted(prof_h.items(), key=lambda kv: -kv[1][0])}}
             print(f"# hierarchy: {ms_h:.3f} ms/step, speedup {ms_ex / ms_h:.2f}x, RSE {rse_h:.3e}, "
                   f"{extra['hierarchy']['kernels_us']}", file=sys.stderr, flush=True)
+    if ctx is not None:
+        extra["retrieved_keys"] = ctx
     return {"cfg": cfg, "ms": ms, "wall": wall, "value": value, "kernels": kernels, "roofline": roofline,
             "extra": extra, "host_inputs": (q, k, v)}
 

@@ -5,4 +5,4 @@ The computation lives in hand-written HIP kernels behind the C ABI of
 tensors into those calls. See ``binding.attn_fwd`` and ``binding.exact_attn_fwd``.
 """
 
-from .binding import MuseError, attn_fwd, exact_attn_fwd, load, workspace_bytes  # noqa: F401
+from .binding import MuseError, attn_fwd, attn_fwd_plain, exact_attn_fwd, load, workspace_bytes  # noqa: F401

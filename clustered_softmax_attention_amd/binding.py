@@ -53,6 +53,10 @@ class FwdParams(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("retrieval_trace", ctypes.c_void_p),
         ("hierarchy", ctypes.c_int),
+        ("perm_q_out", ctypes.c_void_p),
+        ("offs_q_out", ctypes.c_void_p),
+        ("perm_k_out", ctypes.c_void_p),
+        ("offs_k_out", ctypes.c_void_p),
     ]
 
 
@@ -155,10 +159,11 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
              out: Optional[torch.Tensor] = None, *, scale: float = 0.0, out_dtype=None, dipole=True,
              topk_clusters: int = 0, topk_blocks: int = 0, labels_q_in=None, labels_k_in=None,
              return_trace: bool = False, return_centroids: bool = False, return_lse: bool = False,
-             workspace: Optional[torch.Tensor] = None, hierarchy: bool = False):
+             return_buckets: bool = False, workspace: Optional[torch.Tensor] = None, hierarchy: bool = False):
     """muse_attn_fwd_ex. Returns out, or (out, extras) when any return_* flag is set, where
     extras holds 'labels_q_trace', 'labels_k_trace' [iters,B,H,N] int32, 'centroids_q',
-    'centroids_k' [B,H,C,D] float32, 'lse' [B,H,N] float32 and, with retrieval,
+    'centroids_k' [B,H,C,D] float32, 'lse' [B,H,N] float32, 'perm_q', 'perm_k' [B,H,N] and
+    'offs_q', 'offs_k' [B,H,nb*C+1] int32 (bucket order) and, with retrieval,
     'retrieval_trace' [B,H,N/block,Cq,k1,1+k2] int32 as requested."""
     lib = load()
     _check_qkv(q, k, v)
@@ -201,6 +206,13 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
     if return_lse:
         extras["lse"] = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         p.lse_out = extras["lse"].data_ptr()
+    if return_buckets:
+        nb = N // block if causal else 1
+        for name, C in (("q", Cq), ("k", Ck)):
+            extras["perm_" + name] = torch.full((B, H, N), -1, dtype=torch.int32, device=dev)
+            extras["offs_" + name] = torch.full((B, H, nb * C + 1), -1, dtype=torch.int32, device=dev)
+            setattr(p, f"perm_{name}_out", extras["perm_" + name].data_ptr())
+            setattr(p, f"offs_{name}_out", extras["offs_" + name].data_ptr())
     if workspace is not None:
         p.workspace = workspace.data_ptr()
         p.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -208,6 +220,19 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
                                 int(causal), int(block), _dtype_code(q), _stream(), ctypes.byref(p)))
     del keep
     return (out, extras) if extras else out
+
+
+def attn_fwd_plain(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False, block: int = 0,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """muse_attn_fwd: defaults only (scale 1/sqrt(D), tilted dipole, out dtype = input dtype)."""
+    lib = load()
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.muse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, D, Cq, Ck, kmeans_iters, int(causal),
+                             int(block), _dtype_code(q), _stream()))
+    return out
 
 
 def prof_enable(on: bool = True):

@@ -66,8 +66,11 @@ int validate(Shape& s, const muse_fwd_params* p) {
   s.BH = s.B * s.H;
   const int max_tile = s.dtype == MUSE_BF16 ? muse::kMaxTileMfma : muse::kMaxTile;
   if (s.causal) {
-    if (s.block < 64 || s.block > s.N || s.N % s.block != 0 || s.block % 64 != 0)
-      return fail(MUSE_ERR_INVALID_ARG, "causal block=%d must divide N=%d, be >= 64 and a multiple of 64", s.block, s.N);
+    if (s.block < 1 || s.block > s.N || s.N % s.block != 0)
+      return fail(MUSE_ERR_INVALID_ARG, "causal block=%d must lie in [1, N=%d] and divide N", s.block, s.N);
+    if (s.block < 64 || s.block % 64 != 0)
+      return fail(MUSE_ERR_UNSUPPORTED, "causal block=%d: blocks of at least 64 tokens, multiples of 64, are implemented",
+                  s.block);
     s.nb = s.N / s.block;
     s.nbS = s.nb;
     s.tile = tile_for_block(s.block, max_tile);
@@ -274,8 +277,9 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   const bool mf = s.dtype == MUSE_BF16;
   const bool retr = p != nullptr && p->topk_clusters > 0;
   // the matrix-core stage 2 and retrieval need the query buckets
-  tq.perm = (mf || retr) ? at<int32_t>(ws, P.perm_q) : nullptr;
-  tq.offs = (mf || retr) ? at<int32_t>(ws, P.offs_q) : nullptr;
+  const bool want_qb = p != nullptr && (p->perm_q_out != nullptr || p->offs_q_out != nullptr);
+  tq.perm = (mf || retr || want_qb) ? at<int32_t>(ws, P.perm_q) : nullptr;
+  tq.offs = (mf || retr || want_qb) ? at<int32_t>(ws, P.offs_q) : nullptr;
   if (mf) {
     tq.chunks = at<int2>(ws, P.tiles);
     tq.nchunks = at<int32_t>(ws, P.ntiles);
@@ -459,6 +463,21 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
     ax.out_bf16 = a2.out_bf16;
     e = launch_exact(ax, s.dtype, stream);
     if (e != hipSuccess) return hip_fail(e, "local block launch");
+  }
+  if (p != nullptr) {
+    // copies of the bucket order (position permutation and offsets) for the caller
+    const size_t nq = static_cast<size_t>(s.nb) * s.Cq + 1, nk = static_cast<size_t>(s.nb) * s.Ck + 1;
+    const struct {
+      int32_t* dst;
+      const int32_t* src;
+      size_t n;
+    } cp[4] = {{p->perm_q_out, tq.perm, static_cast<size_t>(s.N)}, {p->offs_q_out, tq.offs, nq},
+               {p->perm_k_out, tk.perm, static_cast<size_t>(s.N)}, {p->offs_k_out, tk.offs, nk}};
+    for (const auto& c : cp) {
+      if (c.dst == nullptr) continue;
+      e = hipMemcpyAsync(c.dst, c.src, sizeof(int32_t) * s.BH * c.n, hipMemcpyDeviceToDevice, stream);
+      if (e != hipSuccess) return hip_fail(e, "bucket order copy");
+    }
   }
   if (p != nullptr && p->centroids_q_out != nullptr) {
     e = hipMemcpyAsync(p->centroids_q_out, tq.cent, sizeof(float) * s.BH * s.Cq * s.D, hipMemcpyDeviceToDevice, stream);

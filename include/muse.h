@@ -36,9 +36,13 @@
  *     caller's next synchronisation. No exception or abort crosses the ABI.
  *   - Determinism: identical inputs on the same device give bitwise identical
  *     outputs (no floating-point atomics anywhere).
- *   - Supported shapes: B, H, N >= 1; D in {64, 128}; 1 <= Cq, Ck <= min(N, 128);
- *     kmeans_iters >= 1. Causal: 64 <= block <= N, N % block == 0,
- *     block % 64 == 0.
+ *   - Valid shapes: B, H, N >= 1; 1 <= Cq, Ck <= N; kmeans_iters >= 1; causal:
+ *     1 <= block <= N with N % block == 0. A valid shape outside what the kernels
+ *     implement returns MUSE_ERR_UNSUPPORTED: D not in {64, 128}, Cq or Ck above
+ *     128, a causal block below 64 or not a multiple of 64.
+ *   - Value range (bf16 inputs): the block second moments take keys and values as
+ *     fp16 operands (bf16 converts exactly), so every |k| and |v| element must stay
+ *     below 65504; larger elements give infinite or NaN outputs.
  */
 #ifndef MUSE_H_
 #define MUSE_H_
@@ -139,6 +143,17 @@ typedef struct muse_fwd_params {
                                   once per head), merged by log-sum-exp. Needs causal = 1
                                   (else MUSE_ERR_INVALID_ARG); not combined with retrieval
                                   (MUSE_ERR_UNSUPPORTED)                                    */
+  /* Bucket order of the last K-means assignment (optional copies, device memory). The
+     library replaces the paper's ragged cluster tensors, padded per cluster
+     (pith.science review, "Assumptions & free parameters": cluster size cap), by a
+     stable counting sort of each head's positions by (block, cluster): perm lists the
+     positions of bucket (b, j) = (block b, cluster j) in ascending position order,
+     buckets in ascending b * C + j; offs[b * C + j] is the bucket's first index in
+     perm and offs[nb * C] = N (nb = N / block when causal, else 1).                    */
+  int32_t* perm_q_out;         /* device [B,H,N]          query positions in bucket order */
+  int32_t* offs_q_out;         /* device [B,H,nb*Cq + 1]  query bucket offsets            */
+  int32_t* perm_k_out;         /* device [B,H,N]          key positions in bucket order   */
+  int32_t* offs_k_out;         /* device [B,H,nb*Ck + 1]  key bucket offsets              */
 } muse_fwd_params;
 
 /* Defaults: scale 0, out_dtype -1, dipole tilted, retrieval off, hierarchy 0, all pointers NULL. */

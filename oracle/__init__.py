@@ -12,6 +12,7 @@ from .muse_ref import (  # noqa: F401
     KMeansResult,
     MuseResult,
     Summaries,
+    bucket_order,
     default_scale,
     exact_attention,
     hierarchy_squares,

@@ -35,6 +35,8 @@ Pins (tests/test_oracle_*.py, CPU only):
                        clusters -> exact causal, causality in V.
   retrieval_selection  pinned: planted high-score atoms are selected; brute-force
                        ranking on tiny inputs.
+  bucket_order         pinned: hand-worked example (ties kept in position order,
+                       empty buckets, causal blocks); permutation and offset invariants.
 """
 
 from __future__ import annotations
@@ -182,6 +184,27 @@ def lloyd_kmeans(x, C: int, iters: int, follow_trace: Optional[Sequence[np.ndarr
     res.labels = labels
     res.centroids = c
     return res
+
+
+def bucket_order(labels, C: int, block: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Positions of one head grouped by (spatial block, cluster): the stable sort of
+    the positions by the key block * C + label, and the start of every bucket.
+
+    The paper gathers each cluster's members into a ragged tensor padded per cluster
+    ([REVIEW] "Assumptions & free parameters": cluster size cap, "caps the ragged-tensor
+    block size"); this replaces it by the members listed bucket after bucket (block b,
+    cluster j) with positions ascending inside a bucket. block = 0: one block (acausal).
+    Returns perm [n] and offs [nb * C + 1] with perm[offs[b*C+j]:offs[b*C+j+1]] the
+    positions of bucket (b, j) and offs[-1] = n."""
+    labels = np.asarray(labels).astype(np.int64)
+    n = labels.shape[0]
+    blk = np.zeros(n, np.int64) if block <= 0 else np.arange(n) // block
+    nb = 1 if block <= 0 else n // block
+    key = blk * C + labels
+    perm = np.argsort(key, kind="stable")
+    counts = np.bincount(key, minlength=nb * C)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    return perm, offs
 
 
 # --------------------------------------------------------------------------------------

@@ -53,8 +53,9 @@ def test_params_struct_layout_matches(lib):
     p = FwdParams()
     lib.muse_fwd_params_init(ctypes.byref(p))
     assert p.out_dtype == -1 and p.dipole == 1 and p.scale == 0.0 and p.topk_clusters == 0 and p.hierarchy == 0
-    # 5 ints/floats, pad, 8 pointers, size_t, pointer, int, tail pad
-    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8 + 8 + 4 + 4
+    # 5 ints/floats, pad, 8 pointers, size_t, pointer, int, pad, 4 bucket-order pointers
+    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8 + 8 + 4 + 4 + 4 * 8
+    assert p.perm_q_out is None and p.offs_k_out is None
 
 
 def _call(lib, **kw):
@@ -71,8 +72,19 @@ def _call(lib, **kw):
     (dict(Cq=200, N=4096), -2), (dict(iters=0), -1), (dict(dtype=7), -1),
     (dict(causal=1, block=100), -1), (dict(causal=1, block=0), -1), (dict(causal=1, block=2048), -1),
     (dict(causal=2), -1), (dict(out=1), -1),
+    # valid blocks (divisors of N) that the kernels do not implement: below 64 tokens or
+    # not a multiple of 64
+    (dict(causal=1, block=1), -2), (dict(causal=1, block=32), -2), (dict(causal=1, block=512, N=1536), 0),
+    (dict(causal=1, block=192, N=1536), 0), (dict(causal=1, block=96, N=1536), -2),
 ])
 def test_invalid_arguments_are_rejected_before_launch(lib, kw, code):
+    if code == 0:
+        # accepted shapes: checked through the workspace query, which launches nothing
+        a = dict(B=1, H=1, N=1024, D=64, Cq=8, Ck=32, causal=0, block=0, dtype=0)
+        a.update({k: v for k, v in kw.items() if k in a})
+        assert lib.muse_attn_fwd_workspace_bytes(a["B"], a["H"], a["N"], a["D"], a["Cq"], a["Ck"], a["causal"],
+                                                 a["block"], a["dtype"], None) > 0
+        return
     assert _call(lib, **kw) == code
     assert lib.muse_last_error().decode() != ""
 

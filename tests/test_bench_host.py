@@ -39,16 +39,49 @@ def test_moments_accounting_by_hand():
 
 
 def test_hierarchical_stage2_reads_by_hand():
-    # 32 blocks: block b reads popcount(b) table entries, 80 reads over blocks 1..31
+    # 32 blocks of 2048 queries: block b >= 1 sees popcount(b) squares (80 over blocks 1..31).
+    # Each square's launch reads the block's bf16 queries and one table entry and writes the
+    # fp32 far field (o_far and l_far); every launch after a block's first also reads it.
     cfg = CONFIGS["causal_64k_d128"]
-    base, fl = bench.kernel_work("s2_mfma", cfg)
     hb, hfl = bench.kernel_work("s2_mfma", cfg, hier=True)
-    # in 5 launches per call (the bit length of 31), each reading the queries and writing
-    # the far field; the figure is per call
     assert sum(bin(b).count("1") for b in range(32)) == 80
-    x = 16 * 65536 * 128 * 2
-    assert hb == pytest.approx(5 * 2 * x + (base - 2 * x) * 80 / 31)
-    assert hfl == pytest.approx(fl * 80 / 31)
+    BH, blk, D, Cq, Ck = 16, 2048, 128, 32, 128
+    q_blk = blk * D * 2
+    entry = Cq * Ck * 4 + 4 * Cq * Ck * D * 2 + Cq * D * D * 2  # log Z, K hi/lo, V hi/lo, s D_i
+    far = blk * (D + 1) * 4
+    assert hb == BH * (80 * (q_blk + entry + far) + (80 - 31) * far)
+    assert hfl == BH * 80 * blk * 2.0 * (2 * Ck * D + D * D)
+    # the prefix form: every block b >= 1 once
+    pb, pfl = bench.kernel_work("s2_mfma", cfg)
+    assert pb == BH * 31 * (q_blk + entry + far)
+    assert pfl == BH * 31 * blk * 2.0 * (2 * Ck * D + D * D)
+
+
+def test_retrieval_accounting_by_hand():
+    # one head, 3 blocks, Cq = 2, Ck = 2, k1 = 1, k2 = 1: the retrieved key counts come from
+    # the selections and the bucket sizes
+    import numpy as np
+    import torch
+    from workloads import scaled_config
+    cfg = scaled_config("retrieval_16k", B=1, H=1, N=12, block=4, Cq=2, Ck=2, topk_clusters=1, topk_blocks=1)
+    sel = -np.ones((1, 1, 3, 2, 1, 2), np.int32)
+    sel[0, 0, 1, 0, 0] = [1, 0]   # block 1, query cluster 0: key cluster 1 in block 0
+    sel[0, 0, 2, 1, 0] = [0, 1]   # block 2, query cluster 1: key cluster 0 in block 1
+    offs_k = np.array([[[0, 1, 4, 6, 6, 8, 12]]], np.int32)   # buckets (b, j): 1,3 | 2,0 | 2,4
+    offs_q = np.array([[[0, 2, 4, 7, 8, 9, 12]]], np.int32)   # queries (b, i): 2,2 | 3,1 | 1,3
+    ex = {"retrieval_trace": torch.from_numpy(sel), "offs_k": torch.from_numpy(offs_k),
+          "offs_q": torch.from_numpy(offs_q)}
+    c = bench.retrieval_counts(cfg, ex)
+    # (b=1, i=0): 3 keys for 3 queries; (b=2, i=1): 2 keys for 3 queries
+    assert c == {"nR": 5, "nqR": 3 * 3 + 2 * 3}
+    nbytes, flops = bench.kernel_work("retr_exact_mfma", cfg, ctx=c)
+    assert flops == 4.0 * 64 * 15
+    assert bench.kernel_work("retr_exact_mfma", cfg) is None  # needs the counts
+
+
+def test_cpu_info_fields():
+    info = bench.host_cpu_info()
+    assert info["host_cpus"] == os.cpu_count() and info["affinity_cpus"] >= 1 and info["blas_threads"] >= 1
 
 
 def test_roofline_classification_and_fraction():
