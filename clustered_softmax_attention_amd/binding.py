@@ -19,6 +19,7 @@ _lib = None
 
 MUSE_F32, MUSE_BF16 = 0, 1
 MUSE_OK = 0
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MUSE_NOALLOC_SCRATCH_BYTES of include/muse.h
 STATUS = {0: "MUSE_OK", -1: "MUSE_ERR_INVALID_ARG", -2: "MUSE_ERR_UNSUPPORTED", -3: "MUSE_ERR_HIP",
           -4: "MUSE_ERR_NO_MEMORY", -5: "MUSE_ERR_WORKSPACE"}
 
@@ -26,7 +27,7 @@ STATUS = {0: "MUSE_OK", -1: "MUSE_ERR_INVALID_ARG", -2: "MUSE_ERR_UNSUPPORTED", 
 EXPORTED = ("muse_attn_fwd", "muse_exact_attn_fwd", "muse_attn_fwd_ex", "muse_fwd_params_init",
             "muse_attn_fwd_workspace_bytes", "muse_last_error", "muse_version", "muse_prof_enable",
             "muse_prof_collect", "muse_prof_name", "muse_prof_total_ms", "muse_prof_launches",
-            "muse_prof_reset")
+            "muse_prof_reset", "muse_attn_fwd_noalloc")
 
 
 class MuseError(RuntimeError):
@@ -73,6 +74,8 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.muse_attn_fwd.restype = i
     lib.muse_attn_fwd_ex.argtypes = [vp, vp, vp, vp] + [i] * 10 + [vp, ctypes.POINTER(FwdParams)]
     lib.muse_attn_fwd_ex.restype = i
+    lib.muse_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp] + [i] * 10 + [vp, ctypes.POINTER(FwdParams)]
+    lib.muse_attn_fwd_noalloc.restype = i
     lib.muse_exact_attn_fwd.argtypes = [vp, vp, vp, vp] + [i] * 6 + [vp]
     lib.muse_exact_attn_fwd.restype = i
     lib.muse_fwd_params_init.argtypes = [ctypes.POINTER(FwdParams)]
@@ -159,7 +162,8 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
              out: Optional[torch.Tensor] = None, *, scale: float = 0.0, out_dtype=None, dipole=True,
              topk_clusters: int = 0, topk_blocks: int = 0, labels_q_in=None, labels_k_in=None,
              return_trace: bool = False, return_centroids: bool = False, return_lse: bool = False,
-             return_buckets: bool = False, workspace: Optional[torch.Tensor] = None, hierarchy: bool = False):
+             return_buckets: bool = False, workspace: Optional[torch.Tensor] = None, hierarchy: bool = False,
+             _entry: str = "muse_attn_fwd_ex"):
     """muse_attn_fwd_ex. Returns out, or (out, extras) when any return_* flag is set, where
     extras holds 'labels_q_trace', 'labels_k_trace' [iters,B,H,N] int32, 'centroids_q',
     'centroids_k' [B,H,C,D] float32, 'lse' [B,H,N] float32, 'perm_q', 'perm_k' [B,H,N] and
@@ -216,10 +220,21 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
     if workspace is not None:
         p.workspace = workspace.data_ptr()
         p.workspace_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.muse_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, D, Cq, Ck, kmeans_iters,
+    _check(getattr(lib, _entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, D, Cq, Ck, kmeans_iters,
                                 int(causal), int(block), _dtype_code(q), _stream(), ctypes.byref(p)))
     del keep
     return (out, extras) if extras else out
+
+
+def attn_fwd_noalloc(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False, block: int = 0,
+                     out: Optional[torch.Tensor] = None, **kw):
+    """muse_attn_fwd_noalloc: attn_fwd on the library's fixed per-device scratch (no device
+    allocation in the call; shapes whose workspace exceeds the scratch are refused). Takes
+    attn_fwd's keyword arguments except `workspace`. Output tensors the caller does not
+    pass (out, and those of return_* flags) are still created here by torch."""
+    if kw.get("workspace") is not None:
+        raise ValueError("the allocation-free entry takes no workspace")
+    return attn_fwd(q, k, v, Cq, Ck, kmeans_iters, causal, block, out, _entry="muse_attn_fwd_noalloc", **kw)
 
 
 def attn_fwd_plain(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False, block: int = 0,

@@ -244,7 +244,7 @@ int out_is_bf16(const Shape& s, const muse_fwd_params* p) {
 }
 
 int run_muse(const void* q, const void* k, const void* v, void* out, const Shape& s,
-             const muse_fwd_params* p, hipStream_t stream, void* ws) {
+             const muse_fwd_params* p, hipStream_t stream, void* ws, bool one_stream = false) {
   using namespace muse;
   const Plan P = make_plan(s, p);
   const float scale = scale_of(s, p);
@@ -323,6 +323,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.scale = scale;
   a1.dipole = dipole;
   a1.hier = (p != nullptr && p->hierarchy) ? 1 : 0;
+  a1.one_stream = one_stream ? 1 : 0;
   a1.qbar = tq.cent;
   a1.perm_k = tk.perm;
   a1.offs_k = tk.offs;
@@ -490,6 +491,44 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   return MUSE_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free scratch
+
+}  // namespace
+
+// Scratch of muse_attn_fwd_noalloc: device memory that is part of the library's code
+// object, so no call allocates it. Each device holds its own copy from the library's
+// load until the process ends. In host code `scratch` names a host-side shadow, not the
+// device memory: kernels only ever receive the address hipGetSymbolAddress returns for
+// the current device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[MUSE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept; MUSE_ERR_HIP when the lookup fails.
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxScratchDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(MUSE_ERR_UNSUPPORTED, "device %d: the allocation-free entry serves devices 0..%d", dev,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(MUSE_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return MUSE_OK;
+}
+
 // ---------------------------------------------------------------- per-kernel timing
 
 struct ProfRec {
@@ -647,6 +686,34 @@ int muse_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int
     const hipError_t e = hipFreeAsync(ws, stream);
     if (e != hipSuccess && r == MUSE_OK) r = hip_fail(e, "hipFreeAsync");
   }
+  if (r == MUSE_OK && getenv("MUSE_DEBUG_SYNC") != nullptr) {
+    const hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) r = hip_fail(e, "debug sync");
+  }
+  return r;
+}
+
+int muse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int D,
+                          int Cq, int Ck, int kmeans_iters, int causal, int block, int dtype, void* hip_stream,
+                          const muse_fwd_params* p) {
+  g_last_error.clear();
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(MUSE_ERR_INVALID_ARG, "q, k, v and out must be non-null device pointers");
+  Shape s{B, H, N, D, Cq, Ck, kmeans_iters, causal, block, dtype};
+  int r = validate_muse(s, p);
+  if (r != MUSE_OK) return r;
+  if (out == q || out == k || out == v) return fail(MUSE_ERR_INVALID_ARG, "out must not alias an input");
+  if (p != nullptr && p->workspace != nullptr)
+    return fail(MUSE_ERR_INVALID_ARG, "the allocation-free entry uses the library's own scratch: workspace must be NULL");
+  const size_t need = make_plan(s, p).total;
+  if (need > static_cast<size_t>(MUSE_NOALLOC_SCRATCH_BYTES))
+    return fail(MUSE_ERR_WORKSPACE, "this call needs %zu bytes of scratch, more than the %zu the allocation-free entry holds",
+                need, static_cast<size_t>(MUSE_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  r = scratch_address(&ws);
+  if (r != MUSE_OK) return r;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  r = run_muse(q, k, v, out, s, p, stream, ws, /*one_stream=*/true);
   if (r == MUSE_OK && getenv("MUSE_DEBUG_SYNC") != nullptr) {
     const hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) r = hip_fail(e, "debug sync");

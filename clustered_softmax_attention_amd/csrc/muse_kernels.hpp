@@ -149,6 +149,7 @@ struct S1Args {
   uint16_t* t_vlo;
   uint16_t* t_dip;             // [BH, nbS, Cq, D(v), D(k)]  s * D_i, value index first
   const RetrArgs* retr;        // retrieval: rewrites table entries before the dipole finalise
+  int one_stream;              // 1: every kernel on the caller's stream (no side stream, no events)
   float* cov_k;                // [BH, Ck, D(v), D(k)] untilted dipole: per key cluster covariance
 };
 

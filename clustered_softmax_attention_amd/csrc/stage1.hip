@@ -807,7 +807,7 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
     // take the general path below: per entry folds of the merged atoms and moments). The atoms (with their
     // merge) go to the side stream, forked from and joined back into the caller's stream
     // by events; without a side stream or events everything runs on the caller's stream.
-    hipStream_t side = side_stream();
+    hipStream_t side = a.one_stream ? nullptr : side_stream();
     hipEvent_t fork = nullptr, join = nullptr;
     bool two = side != nullptr && hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
                hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess &&

@@ -172,6 +172,29 @@ size_t muse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int Cq, int Ck,
                                      int causal, int block, int dtype,
                                      const muse_fwd_params* p);
 
+/*
+ * muse_attn_fwd_ex that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, semantics and outputs as muse_attn_fwd_ex (p == NULL means
+ * defaults; p->workspace must be NULL). Instead of a caller or stream-ordered workspace
+ * the call uses a fixed scratch array inside the library's device code,
+ * MUSE_NOALLOC_SCRATCH_BYTES per device, held by every device the library runs on from
+ * the library's load until the process ends. A shape whose workspace
+ * (muse_attn_fwd_workspace_bytes) exceeds it returns MUSE_ERR_WORKSPACE before anything
+ * is launched; 64 MiB holds, e.g., one 8k head (D 64, Cq 32, Ck 128) or one causal 16k
+ * head (block 1024, Cq 16, Ck 64). All work runs on hip_stream (no side stream, no
+ * events), and the call makes no allocation (with muse_prof_enable on, the timing hooks
+ * still create their HIP events). Nothing in the scratch has to start at zero. Every
+ * call on a device shares that device's scratch: calls that overlap in time on one
+ * device (on different streams, or from several threads) race and give wrong results;
+ * order them on one stream.
+ */
+#define MUSE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int muse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                          int B, int H, int N, int D, int Cq, int Ck,
+                          int kmeans_iters, int causal, int block,
+                          int dtype, void* hip_stream, const muse_fwd_params* p);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* muse_last_error(void);
 

@@ -161,3 +161,27 @@ def test_ex_entry_rejects_before_launch(lib):
     p.hierarchy = 0
     aliased = (vp(1), vp(2), vp(3), vp(1), 1, 1, 1024, 64, 8, 32, 5, 0, 0, 1, None)
     assert lib.muse_attn_fwd_ex(*aliased, ctypes.byref(p)) == -1  # out aliases q
+
+
+def test_noalloc_entry_rejects_before_launch(lib):
+    # the allocation-free entry: host-side checks only (no device call is reached)
+    from clustered_softmax_attention_amd import binding
+    from clustered_softmax_attention_amd.binding import FwdParams
+    text = open(HEADER).read()
+    m = re.search(r"#define MUSE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
+    vp = ctypes.c_void_p
+    # the 8k workload (all 32 heads) needs far more than the scratch: refused, nothing launched
+    big = (vp(1), vp(2), vp(3), vp(4), 4, 8, 8192, 64, 32, 128, 5, 0, 0, 1, None)
+    assert lib.muse_attn_fwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, None) > binding.NOALLOC_SCRATCH_BYTES
+    assert lib.muse_attn_fwd_noalloc(*big, None) == -5  # MUSE_ERR_WORKSPACE
+    assert "scratch" in lib.muse_last_error().decode()
+    # a caller workspace is refused: the entry only uses its own scratch
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    p.workspace, p.workspace_bytes = 0x1000, 1 << 30
+    small = (vp(1), vp(2), vp(3), vp(4), 1, 1, 1024, 64, 8, 32, 5, 0, 0, 0, None)
+    assert lib.muse_attn_fwd_noalloc(*small, ctypes.byref(p)) == -1
+    # the usual validation still runs first
+    bad = (vp(1), vp(2), vp(3), vp(4), 1, 1, 1024, 96, 8, 32, 5, 0, 0, 0, None)
+    assert lib.muse_attn_fwd_noalloc(*bad, None) == -2
