@@ -25,3 +25,8 @@ from .muse_ref import (  # noqa: F401
     squared_distances,
     tilted_summaries,
 )
+from .muse_bwd_ref import (  # noqa: F401
+    exact_attention_bwd,
+    muse_acausal_bwd,
+    muse_causal_bwd,
+)
