@@ -1,7 +1,7 @@
 """Throughput of the MuSe forward pass on one MI355X, with roofline and CPU-oracle baseline.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload acausal_8k] [--no-cpu]
-                [--no-exact] [--no-secondary] [--no-peaks] [--hierarchy]
+                [--no-exact] [--no-secondary] [--no-peaks] [--hierarchy] [--single-stream]
 
 A step is one muse_attn_fwd call over the whole workload batch (K-means, stage 1,
 stage 2 and, when causal, the exact diagonal blocks), with inputs resident in HBM and
@@ -205,9 +205,11 @@ def csrc_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE) recorded in the rocprofv3 summary
-    profiles/muse_fwd_<workload>.md, or None when absent or taken on other kernel sources."""
+def profile_record(workload: str, kernel: str):
+    """The per-launch figures of `kernel` in the rocprofv3 summary profiles/muse_fwd_<workload>.md
+    (bytes read and written at the L2-to-memory interface from the raw EA request counters,
+    matrix-core busy fraction, counted matrix-core flops), or None when absent or taken on
+    other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"muse_fwd_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -217,9 +219,14 @@ def measured_traffic(workload: str, kernel: str):
                 rec = json.loads(line[len("traffic-json: "):])
                 if rec.get("csrc_sha") != csrc_sha() or kernel not in rec["kernels"]:
                     return None
-                k = rec["kernels"][kernel]
-                return k["fetch_bytes"] + k["write_bytes"]
+                return rec["kernels"][kernel]
     return None
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch (read + written) from the profile summary, or None."""
+    k = profile_record(workload, kernel)
+    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
 
 
 def timed(fn, steps: int, warmup: int):
@@ -305,6 +312,8 @@ def main():
                     help="with the default workload, skip the 64k causal configuration reported beside it")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-peaks", action="store_true", help="skip the copy and GEMM reference measurements")
+    ap.add_argument("--single-stream", action="store_true",
+                    help="run every library kernel on one stream (no side stream), e.g. to profile each alone")
     ap.add_argument("--hierarchy", action="store_true",
                     help="time the hierarchical causal decomposition instead of the prefix form "
                          "(causal workloads without retrieval)")
@@ -331,7 +340,7 @@ def main():
     from clustered_softmax_attention_amd import binding
 
     binding.load()
-    res = measure(args.workload, args.steps, args.warmup, not args.no_exact, args.hierarchy)
+    res = measure(args.workload, args.steps, args.warmup, not args.no_exact, args.hierarchy, args.single_stream)
     cfg = res["cfg"]
     cpu = None
     if not args.no_cpu:
@@ -363,7 +372,7 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload, "global_batch": cfg.B,
                    "seq_len": cfg.N, "heads": cfg.H, "head_dim": cfg.D, "Cq": cfg.Cq, "Ck": cfg.Ck,
                    "kmeans_iters": cfg.iters, "causal": cfg.causal, "block": cfg.block,
-                   "hierarchy": bool(args.hierarchy)},
+                   "hierarchy": bool(args.hierarchy), "single_stream": bool(args.single_stream)},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "kernels": res["kernels"],
@@ -414,7 +423,8 @@ def measured_peaks() -> dict:
             "published_hbm_GBps": PEAK_HBM_GBS, "published_bf16_TFLOPs": PEAK_BF16_MFMA_TFLOPS}
 
 
-def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = False) -> dict:
+def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = False,
+            single_stream: bool = False) -> dict:
     """Time `steps` MuSe forward calls of workload `name` after `warmup` (whole step on
     the GPU, inputs resident), then the per-kernel HIP-event durations over a second pass,
     the roofline of the dominant kernel and, with `exact`, the in-library exact attention."""
@@ -437,7 +447,7 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
     def muse_step():
         binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=cfg.causal, block=cfg.block, out=out,
                          topk_clusters=cfg.topk_clusters, topk_blocks=cfg.topk_blocks, workspace=ws,
-                         hierarchy=hierarchy)
+                         hierarchy=hierarchy, single_stream=single_stream)
 
     print(f"# timing {name}: {warmup} warmup + {steps} steps", file=sys.stderr, flush=True)
     ms, wall = timed(muse_step, steps, warmup)
@@ -469,7 +479,9 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
     # with the hierarchy, stage 2 is several dispatches per call (one per chain level) while
     # the counters are per dispatch: no per-call traffic figure for it
     traffic = None if (hierarchy and dom == "s2_mfma") else measured_traffic(profile, dom)
+    rec = profile_record(profile, dom)
     roofline = {"kernel": dom, **roofline_entry(dom, cfg, avg_s, hierarchy, ctx), "traffic": traffic,
+                "mfma_busy_counter": None if rec is None else rec.get("mfma_busy"),
                 "share_of_step": prof[dom][0] / sum(t for t, _ in prof.values())}
     for n, d in kernels.items():
         r = roofline_entry(n, cfg, prof[n][0] / prof[n][1] / 1e3, hierarchy, ctx)

@@ -58,6 +58,7 @@ class FwdParams(ctypes.Structure):
         ("offs_q_out", ctypes.c_void_p),
         ("perm_k_out", ctypes.c_void_p),
         ("offs_k_out", ctypes.c_void_p),
+        ("single_stream", ctypes.c_int),
     ]
 
 
@@ -163,7 +164,7 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
              topk_clusters: int = 0, topk_blocks: int = 0, labels_q_in=None, labels_k_in=None,
              return_trace: bool = False, return_centroids: bool = False, return_lse: bool = False,
              return_buckets: bool = False, workspace: Optional[torch.Tensor] = None, hierarchy: bool = False,
-             _entry: str = "muse_attn_fwd_ex"):
+             single_stream: bool = False, _entry: str = "muse_attn_fwd_ex"):
     """muse_attn_fwd_ex. Returns out, or (out, extras) when any return_* flag is set, where
     extras holds 'labels_q_trace', 'labels_k_trace' [iters,B,H,N] int32, 'centroids_q',
     'centroids_k' [B,H,C,D] float32, 'lse' [B,H,N] float32, 'perm_q', 'perm_k' [B,H,N] and
@@ -185,6 +186,7 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
     p.topk_clusters = int(topk_clusters)
     p.topk_blocks = int(topk_blocks)
     p.hierarchy = int(hierarchy)
+    p.single_stream = int(single_stream)
     extras = {}
     keep = []
     for name, lab in (("labels_q_in", labels_q_in), ("labels_k_in", labels_k_in)):

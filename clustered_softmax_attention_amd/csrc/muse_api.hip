@@ -115,6 +115,7 @@ int validate(Shape& s, const muse_fwd_params* p) {
     if (p->topk_clusters > 0 && p->topk_clusters * (1 + p->topk_blocks) > muse::kMaxRetrRow)
       return fail(MUSE_ERR_UNSUPPORTED, "topk_clusters * (1 + topk_blocks) must be at most %d", muse::kMaxRetrRow);
     if (p->hierarchy != 0 && p->hierarchy != 1) return fail(MUSE_ERR_INVALID_ARG, "hierarchy must be 0 or 1");
+    if (p->single_stream != 0 && p->single_stream != 1) return fail(MUSE_ERR_INVALID_ARG, "single_stream must be 0 or 1");
     if (p->hierarchy && !s.causal) return fail(MUSE_ERR_INVALID_ARG, "the hierarchical decomposition requires causal=1");
     if (p->hierarchy && p->topk_clusters > 0)
       return fail(MUSE_ERR_UNSUPPORTED, "retrieval is not combined with the hierarchical decomposition");
@@ -323,7 +324,7 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.scale = scale;
   a1.dipole = dipole;
   a1.hier = (p != nullptr && p->hierarchy) ? 1 : 0;
-  a1.one_stream = one_stream ? 1 : 0;
+  a1.one_stream = (one_stream || (p != nullptr && p->single_stream != 0)) ? 1 : 0;
   a1.qbar = tq.cent;
   a1.perm_k = tk.perm;
   a1.offs_k = tk.offs;

@@ -154,6 +154,10 @@ typedef struct muse_fwd_params {
   int32_t* offs_q_out;         /* device [B,H,nb*Cq + 1]  query bucket offsets            */
   int32_t* perm_k_out;         /* device [B,H,N]          key positions in bucket order   */
   int32_t* offs_k_out;         /* device [B,H,nb*Ck + 1]  key bucket offsets              */
+  int single_stream;           /* 1: every kernel on hip_stream, one after the other (no
+                                  side stream, no events; e.g. to time each kernel alone);
+                                  0 (default): the stage-1 atoms run beside the scores and
+                                  block moments on the library's second stream             */
 } muse_fwd_params;
 
 /* Defaults: scale 0, out_dtype -1, dipole tilted, retrieval off, hierarchy 0, all pointers NULL. */

@@ -53,8 +53,9 @@ def test_params_struct_layout_matches(lib):
     p = FwdParams()
     lib.muse_fwd_params_init(ctypes.byref(p))
     assert p.out_dtype == -1 and p.dipole == 1 and p.scale == 0.0 and p.topk_clusters == 0 and p.hierarchy == 0
-    # 5 ints/floats, pad, 8 pointers, size_t, pointer, int, pad, 4 bucket-order pointers
-    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8 + 8 + 4 + 4 + 4 * 8
+    # 5 ints/floats, pad, 8 pointers, size_t, pointer, int, pad, 4 bucket-order pointers, int, pad
+    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8 + 8 + 4 + 4 + 4 * 8 + 4 + 4
+    assert p.single_stream == 0
     assert p.perm_q_out is None and p.offs_k_out is None
 
 
