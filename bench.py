@@ -507,14 +507,15 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
         extra = {"exact_ms_per_step": ms_ex, "speedup_vs_exact": ms_ex / ms, "rse_vs_exact": rse}
         print(f"# exact {ms_ex:.3f} ms/step, MuSe {ms:.3f} ms/step, speedup {ms_ex / ms:.2f}x, RSE {rse:.3e}",
               file=sys.stderr, flush=True)
-        if not cfg.causal:
+        if cfg.topk_clusters == 0 and not hierarchy:
             # the same workload with the untilted (per key cluster) dipole
-            ws_u = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, False, 0,
-                                                       1 if cfg.dtype == "bf16" else 0, dipole="untilted"),
+            ws_u = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, cfg.causal,
+                                                       cfg.block, 1 if cfg.dtype == "bf16" else 0, dipole="untilted"),
                                dtype=torch.uint8, device="cuda")
 
             def untilted_step():
-                binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, out=out, dipole="untilted", workspace=ws_u)
+                binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=cfg.causal, block=cfg.block, out=out,
+                                 dipole="untilted", workspace=ws_u)
 
             ms_u, _ = timed(untilted_step, steps, warmup)
             binding.prof_reset()
@@ -531,7 +532,8 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
                 "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in prof_u.items() if "untilted" in n or "cov" in n}}
             print(f"# untilted dipole: {ms_u:.3f} ms/step, speedup {ms_ex / ms_u:.2f}x, RSE {rse_u:.3e}, "
                   f"{extra['untilted_dipole']['kernels_us']}", file=sys.stderr, flush=True)
-        elif cfg.topk_clusters == 0 and not hierarchy:
+            del ws_u
+        if cfg.causal and cfg.topk_clusters == 0 and not hierarchy:
             # the same workload with the hierarchical block decomposition (one two-stage
             # approximation per square below the diagonal, log-sum-exp merged)
             ws_h = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, True, cfg.block,

@@ -107,8 +107,9 @@ int validate(Shape& s, const muse_fwd_params* p) {
       return fail(MUSE_ERR_INVALID_ARG, "out_dtype %d invalid", p->out_dtype);
     if (p->dipole != MUSE_DIPOLE_NONE && p->dipole != MUSE_DIPOLE_TILTED && p->dipole != MUSE_DIPOLE_UNTILTED)
       return fail(MUSE_ERR_INVALID_ARG, "dipole mode %d invalid", p->dipole);
-    if (p->dipole == MUSE_DIPOLE_UNTILTED && s.causal)
-      return fail(MUSE_ERR_UNSUPPORTED, "the untilted dipole is implemented for acausal calls only");
+    if (p->dipole == MUSE_DIPOLE_UNTILTED && s.causal && (p->topk_clusters > 0 || p->hierarchy))
+      return fail(MUSE_ERR_UNSUPPORTED,
+                  "the untilted dipole is not combined with retrieval or the hierarchical decomposition");
     if (p->topk_clusters < 0 || p->topk_blocks < 0) return fail(MUSE_ERR_INVALID_ARG, "retrieval top-k must be >= 0");
     if (p->topk_clusters > 0 && !s.causal) return fail(MUSE_ERR_INVALID_ARG, "retrieval requires causal=1");
     if (p->topk_clusters > 0 && p->topk_blocks < 1) return fail(MUSE_ERR_INVALID_ARG, "retrieval needs topk_blocks >= 1");
@@ -145,6 +146,7 @@ struct Plan {
   size_t t_khi, t_klo, t_vhi, t_vlo, t_dip, tiles, ntiles;
   int max_tiles;
   size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores, tmax, cov_k;
+  size_t ub_n, ub_mk, ub_mv, ub_c, up_n, up_mk, up_mv;
   size_t s_logz, s_k, s_v, s_dip;
   size_t o_far, l_far, retr_sel;
   size_t total;
@@ -203,7 +205,18 @@ Plan make_plan(const Shape& s, const muse_fwd_params* p) {
   P.tmax = s.dtype == MUSE_BF16 ? L.take(BH * Cq * ((N + 31) / 32) * f) : 0;
   P.blk_lmass = L.take(BH * static_cast<size_t>(s.nmb) * Cq * f);
   P.blk_mom = L.take(BH * static_cast<size_t>(s.nmb) * Cq * D * D * f);
-  P.cov_k = (p != nullptr && p->dipole == MUSE_DIPOLE_UNTILTED) ? L.take(BH * static_cast<size_t>(Ck) * D * D * f) : 0;
+  const bool untilted = p != nullptr && p->dipole == MUSE_DIPOLE_UNTILTED;
+  P.cov_k = (untilted && !s.causal) ? L.take(BH * static_cast<size_t>(Ck) * D * D * f) : 0;
+  if (untilted && s.causal) {
+    // per (key block, key cluster) bucket statistics and their prefix over the blocks
+    P.ub_n = L.take(BH * nb * Ck * f);
+    P.ub_mk = L.take(BH * nb * Ck * D * f);
+    P.ub_mv = L.take(BH * nb * Ck * D * f);
+    P.ub_c = L.take(BH * nb * Ck * D * D * f);
+    P.up_n = L.take(BH * nb * Ck * f);
+    P.up_mk = L.take(BH * nb * Ck * D * f);
+    P.up_mv = L.take(BH * nb * Ck * D * f);
+  }
   P.s_logz = L.take(BH * nbS * Cq * Ck * f);
   P.s_k = L.take(BH * nbS * Cq * Ck * D * f);
   P.s_v = L.take(BH * nbS * Cq * Ck * D * f);
@@ -347,7 +360,16 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.mbk = s.mbk;
   a1.blk_lmass = at<float>(ws, P.blk_lmass);
   a1.blk_mom = at<float>(ws, P.blk_mom);
-  a1.cov_k = dipole == MUSE_DIPOLE_UNTILTED ? at<float>(ws, P.cov_k) : nullptr;
+  a1.cov_k = (dipole == MUSE_DIPOLE_UNTILTED && !s.causal) ? at<float>(ws, P.cov_k) : nullptr;
+  if (dipole == MUSE_DIPOLE_UNTILTED && s.causal) {
+    a1.ub_n = at<float>(ws, P.ub_n);
+    a1.ub_mk = at<float>(ws, P.ub_mk);
+    a1.ub_mv = at<float>(ws, P.ub_mv);
+    a1.ub_c = at<float>(ws, P.ub_c);
+    a1.up_n = at<float>(ws, P.up_n);
+    a1.up_mk = at<float>(ws, P.up_mk);
+    a1.up_mv = at<float>(ws, P.up_mv);
+  }
   a1.s_logz = at<float>(ws, P.s_logz);
   a1.s_k = at<float>(ws, P.s_k);
   a1.s_v = at<float>(ws, P.s_v);

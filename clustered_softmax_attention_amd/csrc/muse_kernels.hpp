@@ -151,6 +151,15 @@ struct S1Args {
   const RetrArgs* retr;        // retrieval: rewrites table entries before the dipole finalise
   int one_stream;              // 1: every kernel on the caller's stream (no side stream, no events)
   float* cov_k;                // [BH, Ck, D(v), D(k)] untilted dipole: per key cluster covariance
+  // untilted dipole, causal: statistics of every (key block, key cluster) bucket and
+  // their prefix over the blocks (entry b: the keys of blocks < b)
+  float* ub_n;                 // [BH, nb*Ck] keys in the bucket
+  float* ub_mk;                // [BH, nb*Ck, D] their key mean
+  float* ub_mv;                // [BH, nb*Ck, D] their value mean
+  float* ub_c;                 // [BH, nb*Ck, D(v), D(k)] centred sum of (v - mv)(k - mk)^T
+  float* up_n;                 // [BH, nb, Ck] keys of cluster j in the blocks before b
+  float* up_mk;                // [BH, nb, Ck, D] their key mean
+  float* up_mv;                // [BH, nb, Ck, D] their value mean
 };
 
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);

@@ -620,6 +620,7 @@ __global__ void __launch_bounds__(256) s1_cluster_cov_kernel(S1Args a) {
   __shared__ __align__(16) float sk[KC * SST];
   __shared__ __align__(16) float sv[KC * SST];
   __shared__ float smk[D], smv[D];
+  // acausal: bucket j = key cluster j; causal: bucket u = b * Ck + j (key block b)
   const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
   const int32_t* offs = a.offs_k + static_cast<size_t>(bh) * (a.nb * a.Ck + 1);
   const int m0 = offs[j], m1 = offs[j + 1], n = m1 - m0;
@@ -664,6 +665,12 @@ __global__ void __launch_bounds__(256) s1_cluster_cov_kernel(S1Args a) {
   if (tid < D) smk[tid] = n > 0 ? sum / static_cast<float>(n) : 0.f;
   else if (tid < 2 * D) smv[tid - D] = n > 0 ? sum / static_cast<float>(n) : 0.f;
   __syncthreads();
+  if (a.causal) {
+    const size_t u = static_cast<size_t>(bh) * a.nb * a.Ck + j;
+    if (tid < D) a.ub_mk[u * D + tid] = smk[tid];
+    else if (tid < 2 * D) a.ub_mv[u * D + tid - D] = smv[tid - D];
+    if (tid == 0) a.ub_n[u] = static_cast<float>(n);
+  }
   float mk[TD], mv[TD];
 #pragma unroll
   for (int x = 0; x < TD; ++x) {
@@ -697,8 +704,10 @@ __global__ void __launch_bounds__(256) s1_cluster_cov_kernel(S1Args a) {
         for (int y = 0; y < TD; ++y) acc[x][y] = fmaf(vr[x], kr[y], acc[x][y]);
     }
   }
-  const float inv = n > 0 ? 1.f / static_cast<float>(n) : 0.f;
-  float* cov = a.cov_k + (static_cast<size_t>(bh) * a.Ck + j) * D * D;
+  // acausal: the covariance (1/n); causal: the bucket's centred sum, combined over blocks later
+  const float inv = a.causal ? 1.f : (n > 0 ? 1.f / static_cast<float>(n) : 0.f);
+  float* cov = a.causal ? a.ub_c + (static_cast<size_t>(bh) * a.nb * a.Ck + j) * D * D
+                        : a.cov_k + (static_cast<size_t>(bh) * a.Ck + j) * D * D;
 #pragma unroll
   for (int x = 0; x < TD; ++x)
 #pragma unroll
@@ -768,11 +777,155 @@ __global__ void __launch_bounds__(256) s1_untilted_dip_kernel(S1Args a) {
   }
 }
 
+// Untilted dipole, causal: per (head, key cluster j) the count and means of the cluster's
+// keys in the blocks before b, for every entry b (entry 0: none), folded block by block in
+// block order: n' = n + n_b, mean' = mean + (mean_b - mean) n_b / n'. Thread d holds
+// dimension d of the key and the value mean.
+template <int D>
+__global__ void __launch_bounds__(D) s1_untilted_prefix_kernel(S1Args a) {
+  const int j = blockIdx.x, bh = blockIdx.y, d = threadIdx.x, Ck = a.Ck;
+  float n = 0.f, mk = 0.f, mv = 0.f;
+  for (int b = 0; b < a.nb; ++b) {
+    const size_t e = (static_cast<size_t>(bh) * a.nb + b) * Ck + j;  // entry b and bucket (b, j)
+    a.up_mk[e * D + d] = mk;
+    a.up_mv[e * D + d] = mv;
+    if (d == 0) a.up_n[e] = n;
+    const float nb_ = a.ub_n[e];
+    if (nb_ > 0.f) {
+      const float n1 = n + nb_, f = nb_ / n1;
+      mk += (a.ub_mk[e * D + d] - mk) * f;
+      mv += (a.ub_mv[e * D + d] - mv) * f;
+      n = n1;
+    }
+  }
+}
+
+// Untilted dipole, causal: D_i^{<b} = sum_j P_ij^{<b} Cov_j^{<b} for every entry b >= 1,
+// with Cov_j^{<b} the plain covariance of key cluster j over the keys of the blocks
+// before b and P_ij^{<b} = softmax_j log Z_ij^{<b} from the entry's tables. One workgroup
+// per (64 consecutive elements of D x D, head) walks the blocks in order and keeps, for
+// each of its elements, the running centred sum C_j of every cluster, spread over four
+// threads (clusters q, q + 4, ... of thread q). Adding block b - 1 to it is the pairwise
+// combination of centred sums,
+//   C_j += C_(b-1,j) + n n_b / (n + n_b) (mv_b - mv)[dv] (mk_b - mk)[dk],
+// with the prefix (n, mk, mv) of entry b - 1 and the bucket's own (n_b, mk_b, mv_b); then
+// D_i = sum_j (P_ij / n_j) C_j for 32 query clusters at a time (the weights in LDS),
+// summed over the four threads of an element. Entry 0 (no earlier keys) is zero. Writes
+// s * D_i in bf16 (matrix-core stage 2) or D_i in fp32.
+template <int D>
+__global__ void __launch_bounds__(256) s1_untilted_causal_kernel(S1Args a) {
+  constexpr int EL = 64, IG = 32, JR = kMaxClusters / 4;
+  __shared__ float sA[kMaxClusters * EL];
+  __shared__ float sW[IG * kMaxClusters];
+  __shared__ float sF[kMaxClusters];
+  __shared__ float sN[kMaxClusters];
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int el = tid >> 2, q = tid & 3;
+  const int e0 = blockIdx.x * EL;            // first element; the grid covers D * D exactly
+  const int e = e0 + el;
+  const int dv = e0 / D;                     // one value row per workgroup (EL <= D)
+  const int Cq = a.Cq, Ck = a.Ck;
+  const size_t hb = static_cast<size_t>(bh) * a.nb;
+  float C[JR];
+#pragma unroll
+  for (int r = 0; r < JR; ++r) C[r] = 0.f;
+  auto store = [&](int b, int i, float val) {
+    const size_t sidx = (hb + b) * Cq + i;
+    if (a.t_dip != nullptr) a.t_dip[sidx * D * D + e] = f32_to_bf16_bits(a.scale * val);
+    else a.s_dip[sidx * D * D + e] = val;
+  };
+  if (q == 0)
+    for (int i = 0; i < Cq; ++i) store(0, i, 0.f);
+  for (int b = 1; b < a.nb; ++b) {
+    const size_t u = (hb + b - 1) * Ck;      // buckets (b - 1, j) and prefix entry b - 1
+    __syncthreads();                         // the previous block's LDS is consumed
+    for (int jj = tid; jj < Ck; jj += 256) {
+      const float n0 = a.up_n[u + jj], n1 = a.ub_n[u + jj];
+      const float f = (n0 > 0.f && n1 > 0.f) ? n0 * n1 / (n0 + n1) : 0.f;
+      sF[jj] = f * (a.ub_mv[(u + jj) * D + dv] - a.up_mv[(u + jj) * D + dv]);
+      sN[jj] = n0 + n1;
+    }
+    __syncthreads();
+    for (int x = tid; x < Ck * EL; x += 256) {
+      const int jj = x / EL, ex = x % EL, dk = (e0 + ex) % D;
+      const float dkv = a.ub_mk[(u + jj) * D + dk] - a.up_mk[(u + jj) * D + dk];
+      sA[x] = a.ub_c[(u + jj) * D * D + e0 + ex] + sF[jj] * dkv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < JR; ++r) {
+      const int jj = q + 4 * r;
+      if (jj < Ck) C[r] += sA[jj * EL + el];
+    }
+    for (int i0 = 0; i0 < Cq; i0 += IG) {
+      const int ni = min(IG, Cq - i0);
+      __syncthreads();                       // sW of the previous group is consumed
+      for (int ii = wave; ii < IG; ii += 4) {  // a wave per query cluster: softmax over j
+        float l[kMaxClusters / 64];
+        float mx = kNegInf;
+        const float* lz = a.s_logz + ((hb + b) * Cq + i0 + ii) * Ck;
+#pragma unroll
+        for (int t = 0; t < kMaxClusters / 64; ++t) {
+          const int jj = lane + 64 * t;
+          l[t] = ii < ni && jj < Ck ? lz[jj] : kNegInf;
+          mx = fmaxf(mx, l[t]);
+        }
+        mx = wave_max(mx);
+        float sum = 0.f;
+#pragma unroll
+        for (int t = 0; t < kMaxClusters / 64; ++t) {
+          l[t] = l[t] == kNegInf ? 0.f : __expf(l[t] - mx);
+          sum += l[t];
+        }
+        sum = wave_sum(sum);
+        const float inv = sum > 0.f ? 1.f / sum : 0.f;
+#pragma unroll
+        for (int t = 0; t < kMaxClusters / 64; ++t) {
+          const int jj = lane + 64 * t;
+          const float nj = jj < Ck ? sN[jj] : 0.f;
+          sW[ii * kMaxClusters + jj] = nj > 0.f ? l[t] * inv / nj : 0.f;
+        }
+      }
+      __syncthreads();
+      float acc[IG];
+#pragma unroll
+      for (int ii = 0; ii < IG; ++ii) acc[ii] = 0.f;
+#pragma unroll
+      for (int r = 0; r < JR; ++r) {
+        const int jj = q + 4 * r;
+        if (jj >= Ck) break;
+#pragma unroll
+        for (int ii = 0; ii < IG; ++ii) acc[ii] = fmaf(sW[ii * kMaxClusters + jj], C[r], acc[ii]);
+      }
+      // sum over the four threads of the element (lanes 4 el .. 4 el + 3, a DPP quad)
+#pragma unroll
+      for (int ii = 0; ii < IG; ++ii) {
+        float v = acc[ii];
+        v += dpp_f32<0xB1>(v);  // l ^ 1
+        v += dpp_f32<0x4E>(v);  // l ^ 2
+        acc[ii] = v;
+      }
+#pragma unroll
+      for (int ii = 0; ii < IG; ii += 4)
+        if (i0 + ii + q < Cq) store(b, i0 + ii + q, acc[ii + q]);
+    }
+  }
+}
+
 template <typename T, int D>
 static void launch_untilted(const S1Args& a, int part, hipStream_t s) {
   if (part == 0) {
-    ProfScope ps_("s1_cluster_cov", s);
-    hipLaunchKernelGGL((s1_cluster_cov_kernel<T, D>), dim3(a.Ck, a.BH), dim3(256), 0, s, a);
+    {
+      ProfScope ps_("s1_cluster_cov", s);
+      hipLaunchKernelGGL((s1_cluster_cov_kernel<T, D>), dim3(a.nb * a.Ck, a.BH), dim3(256), 0, s, a);
+    }
+    if (a.causal) {
+      ProfScope ps_("s1_untilted_prefix", s);
+      hipLaunchKernelGGL(s1_untilted_prefix_kernel<D>, dim3(a.Ck, a.BH), dim3(D), 0, s, a);
+    }
+  } else if (a.causal) {
+    ProfScope ps_("s1_untilted_causal", s);
+    hipLaunchKernelGGL(s1_untilted_causal_kernel<D>, dim3(D * D / 64, a.BH), dim3(256), 0, s, a);
   } else {
     ProfScope ps_("s1_untilted_dip", s);
     hipLaunchKernelGGL((s1_untilted_dip_kernel<D>), dim3((D * D + 255) / 256, a.BH), dim3(256), 0, s, a);
@@ -817,7 +970,7 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
       (void)hipStreamSynchronize(side);  // the join cannot be enqueued: wait on the host
       two = false;
     }
-    const bool untilted = a.dipole == 2;  // acausal only (the call is refused otherwise)
+    const bool untilted = a.dipole == 2;
     if (untilted) {
       launch_untilted<T, D>(a, 0, s);  // per key cluster covariance (needs no scores)
     } else {
@@ -830,7 +983,7 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
     if (untilted) {
       S1Args af = a;
       af.dipole = 0;  // the tables without the tilted dipole
-      launch_stage1_mfma(af, 3, s);
+      launch_stage1_mfma(af, a.causal ? 4 : 3, s);
       launch_untilted<T, D>(a, 1, s);
     } else {
       launch_stage1_mfma(a, a.causal ? 4 : 3, s);
@@ -852,7 +1005,7 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
     if (a.causal && a.hier) hipLaunchKernelGGL(s1_prefix_kernel<true>, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
     else hipLaunchKernelGGL(s1_prefix_kernel<false>, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
   }
-  if (a.dipole == 2) {  // untilted (acausal, no retrieval): per key cluster covariances
+  if (a.dipole == 2) {  // untilted (no retrieval, no hierarchy): per key cluster covariances
     launch_untilted<T, D>(a, 0, s);
     launch_untilted<T, D>(a, 1, s);
     if (a.t_khi != nullptr) {

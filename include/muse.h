@@ -71,8 +71,10 @@ enum {
  * exponentially tilted distribution; gist.science, Kernmechanismen 2). UNTILTED: C_ij
  * replaced by the plain within-cluster covariance Cov_j of key cluster j, the same for
  * every query cluster (the paper's partially specialised dipole; pith.science review,
- * referee's minor comment on Algorithm 3); acausal calls only: a causal call with it
- * returns MUSE_ERR_UNSUPPORTED. NONE: monopole terms only.
+ * referee's minor comment on Algorithm 3). In causal calls Cov_j covers the keys of
+ * cluster j in the blocks before the query's block and P_ij the same keys' log masses
+ * (the prefix tables); it is not combined with retrieval or the hierarchical
+ * decomposition (MUSE_ERR_UNSUPPORTED). NONE: monopole terms only.
  */
 enum { MUSE_DIPOLE_NONE = 0, MUSE_DIPOLE_TILTED = 1, MUSE_DIPOLE_UNTILTED = 2 };
 
@@ -109,7 +111,7 @@ int muse_exact_attn_fwd(const void* q, const void* k, const void* v, void* out,
 typedef struct muse_fwd_params {
   float scale;          /* softmax scale; <= 0 means 1/sqrt(D)                        */
   int out_dtype;        /* -1: same as input; else MUSE_F32 or MUSE_BF16              */
-  int dipole;           /* MUSE_DIPOLE_TILTED (default), _UNTILTED (acausal) or _NONE  */
+  int dipole;           /* MUSE_DIPOLE_TILTED (default), _UNTILTED or _NONE           */
   int topk_clusters;    /* retrieval k1 (causal only); 0 = off. Per (block b >= 1,
                            query cluster i): the k1 key clusters of largest log Z^{<b}_ij,
                            then inside each the k2 earlier blocks of largest atom log

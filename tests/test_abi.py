@@ -127,9 +127,17 @@ def test_dipole_modes(lib):
     # acausal: the untilted mode adds the per key cluster covariances [B*H, Ck, D, D] fp32
     untilted = lib.muse_attn_fwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, ctypes.byref(p))
     assert untilted >= tilted + 32 * 128 * 64 * 64 * 4
-    # causal: not implemented, refused before any launch
+    # causal: the bucket statistics [B*H, nb*Ck, D, D] fp32 and their prefix means
+    causal = lib.muse_attn_fwd_workspace_bytes(8, 8, 16384, 64, 16, 64, 1, 1024, 1, ctypes.byref(p))
+    p.dipole = 1
+    causal_tilted = lib.muse_attn_fwd_workspace_bytes(8, 8, 16384, 64, 16, 64, 1, 1024, 1, ctypes.byref(p))
+    assert causal >= causal_tilted + 64 * 16 * 64 * 64 * 64 * 4
+    # not combined with retrieval: refused before any launch
+    p.dipole = 2
+    p.topk_clusters, p.topk_blocks = 4, 2
     assert lib.muse_attn_fwd_workspace_bytes(8, 8, 16384, 64, 16, 64, 1, 1024, 1, ctypes.byref(p)) == 0
-    assert "acausal" in lib.muse_last_error().decode()
+    assert "retrieval" in lib.muse_last_error().decode()
+    p.topk_clusters, p.topk_blocks = 0, 0
     p.dipole = 3
     assert lib.muse_attn_fwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, ctypes.byref(p)) == 0
 
@@ -148,8 +156,10 @@ def test_ex_entry_rejects_before_launch(lib):
     assert "workspace" in lib.muse_last_error().decode()
     p.workspace_bytes = need
     p.dipole = 2
+    p.hierarchy = 1
     causal = (vp(1), vp(2), vp(3), vp(4), 1, 1, 1024, 64, 8, 32, 5, 1, 256, 1, None)
-    assert lib.muse_attn_fwd_ex(*causal, ctypes.byref(p)) == -2  # untilted dipole: acausal only
+    assert lib.muse_attn_fwd_ex(*causal, ctypes.byref(p)) == -2  # untilted dipole: not with the hierarchy
+    p.hierarchy = 0
     p.dipole = 1
     p.hierarchy = 1
     acausal = (vp(1), vp(2), vp(3), vp(4), 1, 1, 1024, 64, 8, 32, 5, 0, 0, 1, None)

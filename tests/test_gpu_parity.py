@@ -95,13 +95,34 @@ def test_untilted_dipole(muse_lib, name, over):
     check_config(cfg, [(0, 0)] if cfg.H == 1 else [(0, 0), (0, 1)], dipole="untilted")
 
 
-def test_untilted_dipole_causal_is_refused(muse_lib):
+@pytest.mark.parametrize("name,over", [
+    ("causal_16k", {"B": 1, "H": 2, "N": 4096, "block": 1024}),
+    # D = 128, cluster counts off the 32-tiles, 8 blocks
+    ("causal_64k_d128", {"B": 1, "H": 1, "N": 4096, "block": 512, "Cq": 12, "Ck": 40}),
+    # fp32 inputs (the general causal path), 4 blocks
+    ("acausal_1k_f32", {"H": 2, "N": 1024, "causal": True, "block": 256, "Cq": 8, "Ck": 32}),
+    # 64-token blocks: many small buckets, some empty
+    ("causal_16k", {"B": 1, "H": 1, "N": 1024, "block": 64, "Cq": 8, "Ck": 24}),
+])
+def test_untilted_dipole_causal(muse_lib, name, over):
+    # the untilted dipole in causal calls: per block, the plain covariance of every key
+    # cluster over the keys of the earlier blocks, aggregated with the prefix weights P_ij
+    cfg = scaled_config(name, **over)
+    check_config(cfg, [(0, 0)] if cfg.H == 1 else [(0, 0), (0, 1)], dipole="untilted")
+
+
+def test_untilted_dipole_causal_64k_full_size_sampled_blocks(muse_lib):
+    check_config(CONFIGS["causal_64k_d128"], [(0, 3)], blocks=[1, 16, 31], dipole="untilted")
+
+
+def test_untilted_dipole_refused_with_retrieval_or_hierarchy(muse_lib):
     from clustered_softmax_attention_amd import binding
-    cfg = scaled_config("causal_16k", B=1, H=1, N=2048, block=1024)
+    cfg = scaled_config("retrieval_16k", B=1, H=1, N=2048, block=256)
     q, k, v = (to_device(t, cfg.dtype) for t in make_inputs(cfg))
-    with pytest.raises(binding.MuseError, match="acausal") as err:
-        binding.attn_fwd(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, causal=True, block=cfg.block, dipole="untilted")
-    assert err.value.code == -2  # MUSE_ERR_UNSUPPORTED
+    for kw in ({"topk_clusters": 2, "topk_blocks": 1}, {"hierarchy": True}):
+        with pytest.raises(binding.MuseError, match="untilted") as err:
+            binding.attn_fwd(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, causal=True, block=cfg.block, dipole="untilted", **kw)
+        assert err.value.code == -2  # MUSE_ERR_UNSUPPORTED
 
 
 def test_acausal_bf16_d128(muse_lib):

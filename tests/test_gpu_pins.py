@@ -43,6 +43,15 @@ def test_scale_one(muse_lib, name, over, hier):
     check_config(cfg, _heads(cfg), scale=1.0, hierarchy=hier)
 
 
+@pytest.mark.parametrize("name,over", [
+    ("acausal_8k", {"B": 1, "H": 1, "N": 2048}),
+    ("causal_16k", {"B": 1, "H": 1, "N": 4096, "block": 1024}),
+])
+def test_scale_one_untilted(muse_lib, name, over):
+    cfg = scaled_config(name, **over)
+    check_config(cfg, _heads(cfg), scale=1.0, dipole="untilted")
+
+
 # ------------------------------------------------------------ key translation
 
 def _translate_exactly(k: np.ndarray, c: float, dtype: str):
