@@ -200,23 +200,25 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
         s[t] = mfma32(af, qf[ks], s[t]);
       }
     }
+    // running max on the raw products q.k (the scale is folded into the exponent below)
     float mx = -1e30f;
+    if (!full) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kt + 32 * t + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (key < kbeg || key >= kend) s[t][v] = kNegInf;
+        }
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = s[t][v] * sl2;
-        if (!full) {
-          const int key = kt + 32 * t + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (key < kbeg || key >= kend) x = kNegInf;
-        }
-        s[t][v] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[t][v], s[t][v + 1]));
     mx = fmaxf(mx, xor32(mx));
     const float mn = fmaxf(m, mx);
     if (__ballot(mn > m) != 0ull) {  // rescale only when a row's running max grew (else alpha = 1)
-      const float alpha = fast_exp2(m - mn);
+      const float alpha = fast_exp2((m - mn) * sl2);
       l *= alpha;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
@@ -224,22 +226,25 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
         for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
     }
     m = mn;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(s[t][v] - mn);
-        s[t][v] = p;
-        l += p;
-      }
+    const float nb = -mn * sl2;
+    // p = 2^(s sl2 - mn sl2), rounded to bf16 for the product with V; the row sum is taken
+    // of the same rounded weights (packed dot products with ones), so that numerator and
+    // normaliser use identical values
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
         float pv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = s[t][8 * ss + i];
+        for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(s[t][8 * ss + i], sl2, nb));
         const bf16x8_t bfr = pack_bf16x8(pv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2_t p2 = {bfr[2 * i], bfr[2 * i + 1]};
+          l = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l, false);
+        }
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
           o[mt] = mfma32(lds_operand_tr_acc(sV, KST, 32 * t + 16 * ss, 32 * mt, lane), bfr, o[mt]);
@@ -248,7 +253,7 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
   const float lt = l + xor32(l);
   if (!qvalid) return;
   const float inv = 1.f / lt;
-  float L = (m + __log2f(lt)) * 0.6931471805599453f;
+  float L = (m * sl2 + __log2f(lt)) * 0.6931471805599453f;
   const size_t row = base + qi;
   float w0 = inv, w1 = 0.f;
   bool merge = false;
