@@ -290,6 +290,23 @@ __device__ __forceinline__ bf16x8_t onehot_bf16x8(const u16x8_t& lab8, uint32_t 
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
+// The same one-hot without the mismatch tallies (counts kept elsewhere): three packed
+// operations per pair of labels.
+__device__ __forceinline__ bf16x8_t onehot_bf16x8_nc(const u16x8_t& lab8, uint32_t jj, uint32_t one2, uint32_t neg2,
+                                                     uint32_t val2) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(&lab8);
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t m;
+    asm volatile("v_xor_b32 %0, %1, %2\n\tv_pk_min_u16 %0, %0, %3\n\tv_pk_mad_u16 %0, %0, %4, %5"
+                 : "=&v"(m)
+                 : "v"(p[q]), "v"(jj), "v"(one2), "v"(neg2), "v"(val2));
+    o[q] = m;
+  }
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
 template <int D, int NW, int NJT>
 __device__ __forceinline__ void km_assign_body(const KmArgs& a, int iter, int last, unsigned char* smem) {
   using Cfg = KmMfmaCfg<D, NW>;
@@ -682,7 +699,7 @@ struct Km8Cfg {
   static size_t lds_bytes(int Cmax) {
     const size_t Cp = (Cmax + 31) & ~31;
     return Cp * D * 2 * sizeof(uint16_t) + Cp * sizeof(float) + static_cast<size_t>(TILE) * XST * sizeof(uint16_t) +
-           TILE * sizeof(uint16_t) + sizeof(int) * (NW * Cmax + 2 * Cmax + TILE);
+           TILE * sizeof(uint16_t) + sizeof(int) * (NW * Cmax + 3 * Cmax + TILE);
   }
 };
 
@@ -706,6 +723,7 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
   int* s_cnt = s_whist + NW * C;
   int* s_start = s_cnt + C;
   int* s_sorted = s_start + C;
+  int* s_gcnt = s_sorted + TILE;  // [C] members of each cluster in the group's tiles
   const uint16_t* X = static_cast<const uint16_t*>(t.x) + static_cast<size_t>(bh) * a.N * D;
   const float* cent = t.cent + static_cast<size_t>(bh) * C * D;
   const int pw = 32 * wave + c;  // this lane's point within the tile
@@ -740,6 +758,7 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
     // not be NaN)
     for (int j = tid; j < Cp; j += NT) bias[j] = j < C ? -0.5f * t.cn2[static_cast<size_t>(bh) * C + j] : -1e30f;
   }
+  for (int j = tid; j < C; j += NT) s_gcnt[j] = 0;
   __syncthreads();
   float cmax2 = 0.f;
   if (score) {
@@ -748,14 +767,13 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
   }
   const float cmax = sqrtf(cmax2);
 
-  // cluster sums: wave -> cluster tile wave / 2, feature tiles odt0 .. odt0 + OPW - 1
+  // cluster sums: wave -> cluster tile wave / 2, feature tiles odt0 .. odt0 + OPW - 1; the
+  // counts come from an LDS histogram of the labels (s_gcnt)
   const int oct = wave / 2, odt0 = (wave % 2) * OPW;
   const bool owns = oct < njt;
   f32x16_t acc[OPW];
 #pragma unroll
   for (int r = 0; r < OPW; ++r) acc[r] = zero16();
-  uint32_t miss = 0u;  // packed per-half mismatch counts of the one-hot operand
-  int nks = 0;         // one-hot steps accumulated (8 labels per lane each)
 
   // scores of centroid tile jt for this wave's group, accumulator preset to the bias
   auto score_tile = [&](int jt, f32x16_t& s0) {
@@ -807,6 +825,7 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
       auto rkey = [](float x, int slot) {
         return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & ~63u) | static_cast<uint32_t>(slot));
       };
+      // tile jt + 1 goes to the matrix cores while tile jt is ranked
       f32x16_t sa;
       score_tile(0, sa);
 #pragma unroll
@@ -892,6 +911,7 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
     if (valid) {
       t.labels[static_cast<size_t>(bh) * a.N + n] = lab;
       if (t.trace != nullptr) t.trace[(static_cast<size_t>(iter) * a.BH + bh) * a.N + n] = lab;
+      atomicAdd(&s_gcnt[lab], 1);  // integer counts: exact in any order
     }
     if (h == 0) slab[pw] = valid ? static_cast<uint16_t>(lab) : static_cast<uint16_t>(0xFFFF);
     if (last) tile_sort(a, t, lab, valid, pw, tt, s_whist, s_cnt, s_start, s_sorted);
@@ -906,21 +926,16 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
         bf16x8_t ax[OPW];  // requested before the one-hot is built
 #pragma unroll
         for (int r = 0; r < OPW; ++r) ax[r] = lds_operand_tr(sX, XST, 16 * ks, 32 * (odt0 + r), lane);
-        const bf16x8_t oh = onehot_bf16x8(lab8, jj, one2, neg2, val2, miss);
+        const bf16x8_t oh = onehot_bf16x8_nc(lab8, jj, one2, neg2, val2);
 #pragma unroll
         for (int r = 0; r < OPW; ++r) acc[r] = mfma32(ax[r], oh, acc[r]);
       }
     }
-    nks += TILE / 16;
-    if (tt + 1 == tt1 && owns) {
+    if (tt + 1 == tt1) {
       // sums and counts of this group
       float* psum = t.psum + (static_cast<size_t>(bh) * a.ntiles + grp) * C * D;
       const int j = 32 * oct + c;
-      // lane (c, h) saw 8 nks labels against cluster j
-      const int hit = 8 * nks - static_cast<int>((miss & 0xFFFFu) + (miss >> 16));
-      const int cnt = hit + xor32(hit);
-      if (j < C) {
-        if (odt0 == 0 && h == 0) t.gcnt[(static_cast<size_t>(bh) * a.ntiles + grp) * C + j] = cnt;
+      if (owns && j < C) {
 #pragma unroll
         for (int r = 0; r < OPW; ++r)
 #pragma unroll
@@ -929,6 +944,7 @@ __device__ __forceinline__ void km_assign_body8(const KmArgs& a, int iter, int l
             *reinterpret_cast<f32x4_t*>(psum + static_cast<size_t>(j) * D + 32 * (odt0 + r) + 8 * q + 4 * h) = f;
           }
       }
+      for (int jc = tid; jc < C; jc += NT) t.gcnt[(static_cast<size_t>(bh) * a.ntiles + grp) * C + jc] = s_gcnt[jc];
     }
     __syncthreads();  // the next tile overwrites the X tile and labels
   }
