@@ -13,6 +13,7 @@ from .muse_ref import (  # noqa: F401
     MuseResult,
     Summaries,
     bucket_order,
+    cap_key_labels,
     default_scale,
     exact_attention,
     hierarchy_squares,

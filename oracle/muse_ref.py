@@ -37,6 +37,10 @@ Pins (tests/test_oracle_*.py, CPU only):
                        ranking on tiny inputs.
   bucket_order         pinned: hand-worked example (ties kept in position order,
                        empty buckets, causal blocks); permutation and offset invariants.
+  cap_key_labels       pinned: hand-worked cap sizes and kept members; a cap above every
+                       cluster size changes nothing; capped MuSe equals MuSe on the inputs
+                       with the dropped keys removed (acausal), exact in-block attention
+                       keeps them (causal).
 """
 
 from __future__ import annotations
@@ -359,19 +363,41 @@ def _cluster(x, C, iters, labels_in, follow, tie_rel):
     return km, km.labels, km.centroids
 
 
+def cap_key_labels(labels, Ck: int, cap_ratio: Optional[float]) -> np.ndarray:
+    """Key clusters capped at U = ceil(cap_ratio * n / Ck) members [R16].
+
+    The paper pads each cluster's members into a ragged tensor whose row length is the
+    cap ([REVIEW] "Assumptions & free parameters": cluster size cap ratio 1.5, 1.25 to 4.0
+    explored, "caps the ragged-tensor block size"). Reading: the members of key cluster j,
+    taken in position order, fill its row; those beyond the first U do not fit and take no
+    part in the stage-1 summaries of their cluster (log-normaliser, tilted means, dipole).
+    Returns the labels with every dropped key set to -1 (a label no cluster has);
+    cap_ratio None means no cap."""
+    labels = np.asarray(labels).astype(np.int64).copy()
+    if cap_ratio is None:
+        return labels
+    n = labels.shape[0]
+    U = int(np.ceil(cap_ratio * n / Ck))
+    for j in range(Ck):
+        members = np.nonzero(labels == j)[0]     # ascending positions
+        labels[members[U:]] = -1
+    return labels
+
+
 def muse_acausal(q, k, v, Cq: int, Ck: int, iters: int, scale: Optional[float] = None,
                  dipole: str = "tilted", labels_q=None, labels_k=None,
                  follow_q=None, follow_k=None, tie_rel: float = 1e-5,
-                 rows: Optional[np.ndarray] = None) -> MuseResult:
+                 rows: Optional[np.ndarray] = None, cap_ratio: Optional[float] = None) -> MuseResult:
     """Acausal MuSe forward of one head: K-means on Q (Cq) and on K (Ck), stage 1
-    summaries, stage 2 refinement. Two-stage scheme per [REVIEW] "Core claim"."""
+    summaries, stage 2 refinement. Two-stage scheme per [REVIEW] "Core claim".
+    cap_ratio: key clusters capped in stage 1 (cap_key_labels)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     s = default_scale(q.shape[1]) if scale is None else scale
     km_q, lq, qbar = _cluster(q, Cq, iters, labels_q, follow_q, tie_rel)
     km_k, lk, _ = _cluster(k, Ck, iters, labels_k, follow_k, tie_rel)
-    S = tilted_summaries(qbar, k, v, lk, Ck, s, dipole)
+    S = tilted_summaries(qbar, k, v, cap_key_labels(lk, Ck, cap_ratio), Ck, s, dipole)
     o, L = refine(q, lq, qbar, S, s, dipole != "none", rows)
     return MuseResult(o, L, km_q, km_k, lq, lk, qbar)
 
@@ -494,7 +520,7 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
                 labels_q=None, labels_k=None, follow_q=None, follow_k=None,
                 tie_rel: float = 1e-5, blocks_to_eval: Optional[Sequence[int]] = None,
                 retrieval_follow: Optional[np.ndarray] = None,
-                hierarchical: bool = False) -> MuseResult:
+                hierarchical: bool = False, cap_ratio: Optional[float] = None) -> MuseResult:
     """Causal MuSe forward of one head [R8].
 
     Clusters are fitted once per head over the whole sequence. For a query n in
@@ -519,7 +545,11 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
     hierarchical: the far field of a block is not one summary of all earlier keys but
     the log-sum-exp merge of one two-stage approximation per square of the hierarchy
     (hierarchy_squares, [R15]), each over its own key range with the global clusters.
-    Retrieval is not combined with it."""
+    Retrieval is not combined with it.
+
+    cap_ratio: key clusters capped (cap_key_labels, over the whole sequence: a cluster
+    keeps its earliest U members); the dropped keys leave the far-field summaries and are
+    still attended exactly inside their own block. Not combined with retrieval."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -530,6 +560,9 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
     nb = N // block
     km_q, lq, qbar = _cluster(q, Cq, iters, labels_q, follow_q, tie_rel)
     km_k, lk, _ = _cluster(k, Ck, iters, labels_k, follow_k, tie_rel)
+    if cap_ratio is not None and topk_clusters > 0:
+        raise ValueError("the cluster cap is not combined with retrieval")
+    lk_s = cap_key_labels(lk, Ck, cap_ratio)   # labels seen by the stage-1 summaries
     o = np.full((N, v.shape[1]), np.nan)
     L = np.full(N, np.nan)
     key_block = np.arange(N) // block
@@ -545,7 +578,7 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
             if not hit:
                 continue
             ks = slice(k0 * block, k1 * block)
-            S = tilted_summaries(qbar, k[ks], v[ks], lk[ks], Ck, s, dipole)
+            S = tilted_summaries(qbar, k[ks], v[ks], lk_s[ks], Ck, s, dipole)
             for b in hit:
                 rs = slice(b * block, (b + 1) * block)
                 o_s, L_s = refine(q[rs], lq[rs], qbar, S, s, dipole != "none")
@@ -566,7 +599,7 @@ def muse_causal(q, k, v, Cq: int, Ck: int, iters: int, block: int,
         pre = slice(0, r0)
         if topk_clusters <= 0:
             o_loc, L_loc = _attend(q[r0:r1], k[r0:r1], v[r0:r1], s, loc_allowed)
-            S = tilted_summaries(qbar, k[pre], v[pre], lk[pre], Ck, s, dipole)
+            S = tilted_summaries(qbar, k[pre], v[pre], lk_s[pre], Ck, s, dipole)
             o_far, L_far = refine(q[r0:r1], lq[r0:r1], qbar, S, s, dipole != "none")
             o[r0:r1], L[r0:r1] = lse_merge(o_far, L_far, o_loc, L_loc)
             continue

@@ -22,7 +22,7 @@ import pytest
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ORACLE_SRC_PATH = os.path.join(os.path.dirname(HERE), "oracle", "muse_ref.py")
-PIN_MODULES = ("test_oracle_exact_kmeans.py", "test_oracle_muse.py")
+PIN_MODULES = ("test_oracle_exact_kmeans.py", "test_oracle_muse.py", "test_oracle_cap.py", "test_oracle_buckets.py")
 
 with open(ORACLE_SRC_PATH) as _f:
     ORACLE_SRC = _f.read()
@@ -31,6 +31,12 @@ with open(ORACLE_SRC_PATH) as _f:
 # (name, text in the oracle, replacement). Each text must occur exactly once, so an
 # edit of the oracle that removes it fails here instead of silently testing nothing.
 MUTATIONS = [
+    # capped key clusters and the bucket order
+    ("cap_keeps_last_members", "labels[members[U:]] = -1", "labels[members[:max(len(members) - U, 0)]] = -1"),
+    ("cap_rounds_down", "U = int(np.ceil(cap_ratio * n / Ck))", "U = int(np.floor(cap_ratio * n / Ck))"),
+    ("cap_ignored_when_causal", "S = tilted_summaries(qbar, k[pre], v[pre], lk_s[pre], Ck, s, dipole)",
+     "S = tilted_summaries(qbar, k[pre], v[pre], lk[pre], Ck, s, dipole)"),
+    ("buckets_unstable", 'perm = np.argsort(key, kind="stable")', 'perm = np.argsort(-key, kind="stable")[::-1]'),
     # softmax temperature and exact attention
     ("scale_1_over_D", "return 1.0 / np.sqrt(D)", "return 1.0 / D"),
     ("exact_drops_scale", "a = scale * (qrows @ keys.T)", "a = (qrows @ keys.T)"),
@@ -83,9 +89,9 @@ MUTATIONS = [
      "oi[finite] += scale * (qt[finite] @ S.Dip[i])"),
     # whole passes
     ("acausal_key_clusters_use_Cq", "km_k, lk, _ = _cluster(k, Ck, iters, labels_k, follow_k, tie_rel)\n"
-     "    S = tilted_summaries(qbar, k, v, lk, Ck, s, dipole)",
+     "    S = tilted_summaries(qbar, k, v, cap_key_labels(lk, Ck, cap_ratio), Ck, s, dipole)",
      "km_k, lk, _ = _cluster(k, Cq, iters, labels_k, follow_k, tie_rel)\n"
-     "    S = tilted_summaries(qbar, k, v, lk, Ck, s, dipole)"),
+     "    S = tilted_summaries(qbar, k, v, cap_key_labels(lk, Ck, cap_ratio), Ck, s, dipole)"),
     ("fixed_labels_sum_centroid", "            if m.any():\n                c[j] = x[m].mean(axis=0)",
      "            if m.any():\n                c[j] = x[m].sum(axis=0)"),
     ("causal_local_strict", "loc_allowed = (np.arange(r0, r1)[None, :] <= rows[:, None])",
