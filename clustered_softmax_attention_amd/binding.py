@@ -59,6 +59,7 @@ class FwdParams(ctypes.Structure):
         ("perm_k_out", ctypes.c_void_p),
         ("offs_k_out", ctypes.c_void_p),
         ("single_stream", ctypes.c_int),
+        ("cap_ratio", ctypes.c_double),
     ]
 
 
@@ -164,12 +165,13 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
              topk_clusters: int = 0, topk_blocks: int = 0, labels_q_in=None, labels_k_in=None,
              return_trace: bool = False, return_centroids: bool = False, return_lse: bool = False,
              return_buckets: bool = False, workspace: Optional[torch.Tensor] = None, hierarchy: bool = False,
-             single_stream: bool = False, _entry: str = "muse_attn_fwd_ex"):
+             single_stream: bool = False, cap_ratio: float = 0.0, _entry: str = "muse_attn_fwd_ex"):
     """muse_attn_fwd_ex. Returns out, or (out, extras) when any return_* flag is set, where
     extras holds 'labels_q_trace', 'labels_k_trace' [iters,B,H,N] int32, 'centroids_q',
     'centroids_k' [B,H,C,D] float32, 'lse' [B,H,N] float32, 'perm_q', 'perm_k' [B,H,N] and
     'offs_q', 'offs_k' [B,H,nb*C+1] int32 (bucket order) and, with retrieval,
-    'retrieval_trace' [B,H,N/block,Cq,k1,1+k2] int32 as requested."""
+    'retrieval_trace' [B,H,N/block,Cq,k1,1+k2] int32 as requested. cap_ratio > 0 caps the
+    key clusters of the stage-1 summaries at ceil(cap_ratio * N / Ck) members."""
     lib = load()
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
@@ -187,6 +189,7 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
     p.topk_blocks = int(topk_blocks)
     p.hierarchy = int(hierarchy)
     p.single_stream = int(single_stream)
+    p.cap_ratio = float(cap_ratio)
     extras = {}
     keep = []
     for name, lab in (("labels_q_in", labels_q_in), ("labels_k_in", labels_k_in)):

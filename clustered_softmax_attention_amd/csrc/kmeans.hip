@@ -1029,7 +1029,9 @@ __global__ void __launch_bounds__(64 * kUpdWaves) kmeans_update_kernel(KmArgs a)
 // a bucket), pads the list with empty items, lists the buckets of several items with
 // their partial slots, and records per bucket its first partial slot and item count.
 // With chunks set (query tensor), it lists the stage-2 chunks: runs of at most kS2Chunk
-// positions of one bucket.
+// positions of one bucket. With a cluster size cap (klen set), each bucket's kept length
+// (a prefix of the bucket, since a cluster keeps its earliest members) goes to klen and
+// the work items cover the kept prefixes only; the scatter then flags the left-out points.
 template <int kBoThreads>
 __global__ void __launch_bounds__(kBoThreads) bucket_offsets_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
@@ -1037,9 +1039,10 @@ __global__ void __launch_bounds__(kBoThreads) bucket_offsets_kernel(KmArgs a) {
   __shared__ int s_run[5][kBoThreads];
   const int C = t.C, bh = blockIdx.y, tid = threadIdx.x;
   const int nbC = a.nb * C;
-  const bool segs = t.items != nullptr, chk = t.chunks != nullptr;
+  const bool segs = t.items != nullptr, chk = t.chunks != nullptr, capped = t.klen != nullptr;
   const int per = (nbC + kBoThreads - 1) / kBoThreads, e0 = min(nbC, tid * per), e1 = min(nbC, e0 + per);
   int* offs = t.offs + static_cast<size_t>(bh) * (nbC + 1);
+  int* klen = capped ? t.klen + static_cast<size_t>(bh) * nbC : nullptr;
   int tot[5] = {0, 0, 0, 0, 0};  // positions, items, partial slots, buckets of several items, chunks
   // Each tile's count is replaced by the members of (b, j) in the block's earlier tiles.
   // Short blocks with many buckets per thread: the thread's (bucket, tile) pairs in order,
@@ -1048,13 +1051,17 @@ __global__ void __launch_bounds__(kBoThreads) bucket_offsets_kernel(KmArgs a) {
   const int tpb = a.tiles_per_block;
   const size_t tbase = static_cast<size_t>(bh) * a.ntiles;
   int32_t* tcb = t.tile_cnt + tbase * C;  // this head's [ntiles, C] counts
-  auto finish = [&](int e, int run) {
-    offs[e] = run;  // bucket total for now (only this thread touches entry e)
-    const int ni = max(1, (run + kAtomSeg - 1) / kAtomSeg);
-    tot[0] += run;
+  // work items of a bucket of `kept` positions
+  auto count_items = [&](int kept) {
+    const int ni = max(1, (kept + kAtomSeg - 1) / kAtomSeg);
     tot[1] += ni;
     tot[2] += ni > 1 ? ni : 0;
     tot[3] += ni > 1 ? 1 : 0;
+  };
+  auto finish = [&](int e, int run) {
+    offs[e] = run;  // bucket total for now (only this thread touches entry e)
+    tot[0] += run;
+    if (!capped) count_items(run);
     tot[4] += (run + kS2Chunk - 1) / kS2Chunk;
   };
   // long blocks (32 tiles or more, e.g. one block per head) or few buckets per thread:
@@ -1122,6 +1129,27 @@ __global__ void __launch_bounds__(kBoThreads) bucket_offsets_kernel(KmArgs a) {
       }
     }
   }
+  if (capped) {
+    // kept members: bucket (b, j) keeps what still fits under the cap after the members of
+    // cluster j in the blocks before b (a thread per cluster, over the blocks in order,
+    // 16 bucket totals in flight per batch)
+    __syncthreads();  // every bucket total is in offs
+    for (int j = tid; j < C; j += kBoThreads) {
+      int seen = 0;
+      for (int b0 = 0; b0 < a.nb; b0 += 16) {
+        int n[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) n[q] = b0 + q < a.nb ? offs[(b0 + q) * C + j] : 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          if (b0 + q < a.nb) klen[(b0 + q) * C + j] = min(n[q], max(0, t.cap - seen));
+          seen += n[q];
+        }
+      }
+    }
+    __syncthreads();
+    for (int e = e0; e < e1; ++e) count_items(klen[e]);
+  }
 #pragma unroll
   for (int r = 0; r < 5; ++r) s_run[r][tid] = tot[r];
   __syncthreads();
@@ -1144,9 +1172,10 @@ __global__ void __launch_bounds__(kBoThreads) bucket_offsets_kernel(KmArgs a) {
     const int cnt = offs[e];
     offs[e] = pos;
     if (segs) {
-      const int ni = max(1, (cnt + kAtomSeg - 1) / kAtomSeg);
+      const int kept = capped ? klen[e] : cnt;  // the items cover the bucket's kept prefix
+      const int ni = max(1, (kept + kAtomSeg - 1) / kAtomSeg);
       for (int q = 0; q < ni; ++q)
-        items[it + q] = make_int4(pos + kAtomSeg * q, min(kAtomSeg, cnt - kAtomSeg * q), ni > 1 ? pt + q : -1, e);
+        items[it + q] = make_int4(pos + kAtomSeg * q, min(kAtomSeg, kept - kAtomSeg * q), ni > 1 ? pt + q : -1, e);
       if (ni > 1) multi[1 + mb++] = make_int4(e, pt, ni, 0);
       t.bmeta[static_cast<size_t>(bh) * nbC + e] = make_int2(ni > 1 ? pt : -1, ni);
       it += ni;
@@ -1168,7 +1197,7 @@ __global__ void __launch_bounds__(kBoThreads) bucket_offsets_kernel(KmArgs a) {
 }
 
 // One workgroup per tile: scatter the tile's stably sorted points into the head's
-// (block, label) buckets.
+// (block, label) buckets (and, with a cap, flag each point beyond its bucket's kept length).
 __global__ void bucket_scatter_kernel(KmArgs a) {
   const KmTensor& t = a.t[blockIdx.z];
   if (t.perm == nullptr) return;
@@ -1181,8 +1210,11 @@ __global__ void bucket_scatter_kernel(KmArgs a) {
   for (int pos = threadIdx.x; pos < npts; pos += blockDim.x) {
     const int p = t.tile_perm[tix * a.tile + pos];
     const int j = t.labels[static_cast<size_t>(bh) * a.N + tile0 + p];
-    const int dst = offs[b * C + j] + t.tile_cnt[tix * C + j] + (pos - t.tile_start[tix * C + j]);
-    t.perm[static_cast<size_t>(bh) * a.N + dst] = static_cast<int>(tile0 + p);
+    const int rank = t.tile_cnt[tix * C + j] + (pos - t.tile_start[tix * C + j]);  // in the bucket
+    t.perm[static_cast<size_t>(bh) * a.N + offs[b * C + j] + rank] = static_cast<int>(tile0 + p);
+    if (t.kdrop != nullptr)
+      t.kdrop[static_cast<size_t>(bh) * a.N + tile0 + p] =
+          rank >= t.klen[static_cast<size_t>(bh) * a.nb * C + b * C + j] ? 1 : 0;
   }
 }
 

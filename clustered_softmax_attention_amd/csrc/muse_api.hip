@@ -122,8 +122,19 @@ int validate(Shape& s, const muse_fwd_params* p) {
       return fail(MUSE_ERR_UNSUPPORTED, "retrieval is not combined with the hierarchical decomposition");
     if (p->topk_clusters > 0 && s.nb > muse::kMaxRetrBlocks)
       return fail(MUSE_ERR_UNSUPPORTED, "retrieval supports at most %d blocks", muse::kMaxRetrBlocks);
+    if (!(p->cap_ratio >= 0.0)) return fail(MUSE_ERR_INVALID_ARG, "cap_ratio must be >= 0 (0: no cap)");
+    if (p->cap_ratio > 0.0 && p->topk_clusters > 0)
+      return fail(MUSE_ERR_UNSUPPORTED, "the cluster size cap is not combined with retrieval");
   }
   return MUSE_OK;
+}
+
+// Members kept per key cluster under the cap, ceil(cap_ratio * N / Ck) (at most N), or 0
+// for no cap.
+int cap_members(const Shape& s, const muse_fwd_params* p) {
+  if (p == nullptr || !(p->cap_ratio > 0.0)) return 0;
+  const double u = ceil(p->cap_ratio * s.N / s.Ck);
+  return u >= static_cast<double>(s.N) ? s.N : static_cast<int>(u);
 }
 
 int validate_muse(Shape& s, const muse_fwd_params* p) {
@@ -147,6 +158,7 @@ struct Plan {
   int max_tiles;
   size_t at_m, at_z, at_k, at_v, blk_lmass, blk_mom, scores, tmax, cov_k;
   size_t ub_n, ub_mk, ub_mv, ub_c, up_n, up_mk, up_mv;
+  size_t klen, kdrop;
   size_t s_logz, s_k, s_v, s_dip;
   size_t o_far, l_far, retr_sel;
   size_t total;
@@ -186,6 +198,10 @@ Plan make_plan(const Shape& s, const muse_fwd_params* p) {
   P.offs_k = L.take(BH * (nb * Ck + 1) * i4);
   P.perm_q = L.take(BH * N * i4);
   P.offs_q = L.take(BH * (nb * Cq + 1) * i4);
+  if (cap_members(s, p) > 0) {
+    P.klen = L.take(BH * nb * Ck * i4);
+    P.kdrop = L.take(BH * N);
+  }
   if (s.dtype == MUSE_BF16) {
     const size_t ni = muse::atom_max_items(static_cast<int>(nb * Ck), static_cast<int>(N));
     const size_t np = muse::atom_max_partials(static_cast<int>(N));
@@ -319,6 +335,9 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   tk.items = mf ? at<int4>(ws, P.items_k) : nullptr;
   tk.multi = mf ? at<int4>(ws, P.multi_k) : nullptr;
   tk.bmeta = mf ? at<int2>(ws, P.bmeta_k) : nullptr;
+  tk.cap = cap_members(s, p);
+  tk.klen = tk.cap > 0 ? at<int32_t>(ws, P.klen) : nullptr;
+  tk.kdrop = tk.cap > 0 ? at<uint8_t>(ws, P.kdrop) : nullptr;
   hipError_t e = launch_kmeans(km, s.iters, s.dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "K-means launch");
 
@@ -344,6 +363,8 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.items_k = tk.items;
   a1.multi_k = tk.multi;
   a1.bmeta_k = tk.bmeta;
+  a1.klen = tk.klen;
+  a1.kdrop = tk.kdrop;
   if (mf) {
     a1.pt_m = at<float>(ws, P.pt_m);
     a1.pt_z = at<float>(ws, P.pt_z);
@@ -673,7 +694,7 @@ void muse_fwd_params_init(muse_fwd_params* p) {
 
 const char* muse_last_error(void) { return g_last_error.c_str(); }
 
-int muse_version(void) { return 101; }
+int muse_version(void) { return 102; }
 
 size_t muse_attn_fwd_workspace_bytes(int B, int H, int N, int D, int Cq, int Ck, int causal, int block,
                                      int dtype, const muse_fwd_params* p) {

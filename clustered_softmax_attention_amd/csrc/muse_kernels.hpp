@@ -53,6 +53,11 @@ struct KmTensor {
   int2* chunks;                // [BH, max_chunks] (bucket, first position)
   int32_t* nchunks;            // [BH]
   int max_chunks;
+  // cluster size cap (key tensor; null: no cap): a cluster keeps its first `cap` members
+  // in position order, so bucket (b, j) keeps a prefix of its positions
+  int cap;
+  int32_t* klen;               // [BH, nb*C] kept members of every bucket (items cover only these)
+  uint8_t* kdrop;              // [BH, N] 1 for a point left out (by position in the input)
 };
 
 struct KmArgs {
@@ -160,6 +165,10 @@ struct S1Args {
   float* up_n;                 // [BH, nb, Ck] keys of cluster j in the blocks before b
   float* up_mk;                // [BH, nb, Ck, D] their key mean
   float* up_mv;                // [BH, nb, Ck, D] their value mean
+  // cluster size cap (null: none): kept keys of every bucket (a prefix of it) and a flag
+  // per key (input position) that is 1 when the key is left out of the summaries
+  const int32_t* klen;         // [BH, nb*Ck]
+  const uint8_t* kdrop;        // [BH, N]
 };
 
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);

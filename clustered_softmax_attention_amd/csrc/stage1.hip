@@ -56,7 +56,9 @@ __global__ void __launch_bounds__(256) s1_atoms_kernel(S1Args a) {
   float* salpha = sz + Cq;
 
   const int32_t* offs = a.offs_k + static_cast<size_t>(bh) * (a.nb * Ck + 1);
-  const int seg0 = offs[bp * Ck + j], seg1 = offs[bp * Ck + j + 1];
+  // the bucket's positions, or with a cluster size cap its kept prefix
+  const int seg0 = offs[bp * Ck + j];
+  const int seg1 = a.klen ? seg0 + a.klen[static_cast<size_t>(bh) * a.nb * Ck + bp * Ck + j] : offs[bp * Ck + j + 1];
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
   const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * a.N * D;
@@ -204,7 +206,9 @@ __global__ void __launch_bounds__(256) s1_moments_kernel(S1Args a) {
 #pragma unroll 16
           for (int d = 0; d < D; ++d) dot = fmaf(qb[d], kc[tid * D + d], dot);
         }
-        w[tid] = (tid < nk) ? __expf(a.scale * dot - R) : 0.f;
+        // keys left out by a cluster size cap weigh nothing
+        const bool in = tid < nk && (a.kdrop == nullptr || a.kdrop[static_cast<size_t>(bh) * a.N + c0 + tid] == 0);
+        w[tid] = in ? __expf(a.scale * dot - R) : 0.f;
       }
       __syncthreads();
       for (int m = 0; m < nk; ++m) {
@@ -623,7 +627,9 @@ __global__ void __launch_bounds__(256) s1_cluster_cov_kernel(S1Args a) {
   // acausal: bucket j = key cluster j; causal: bucket u = b * Ck + j (key block b)
   const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
   const int32_t* offs = a.offs_k + static_cast<size_t>(bh) * (a.nb * a.Ck + 1);
-  const int m0 = offs[j], m1 = offs[j + 1], n = m1 - m0;
+  // the bucket's members, or with a cluster size cap its kept prefix
+  const int m0 = offs[j], m1 = a.klen ? m0 + a.klen[static_cast<size_t>(bh) * a.nb * a.Ck + j] : offs[j + 1];
+  const int n = m1 - m0;
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
   const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * a.N * D;

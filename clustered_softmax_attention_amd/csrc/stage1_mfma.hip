@@ -64,6 +64,9 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
     if (kb >= a.N) break;
     const int pos = kb + c;
     const int key = pos < a.N ? perm[pos] : 0;
+    // bit p of dmask: position kb + p is left out by a cluster size cap (score -inf)
+    const bool drop = a.kdrop != nullptr && pos < a.N && a.kdrop[static_cast<size_t>(bh) * a.N + key] != 0;
+    const uint32_t dmask = static_cast<uint32_t>(__ballot(drop));
     bf16x8_t ak[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -82,12 +85,19 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
       // lane (c, h): centroid 32 nt + c, positions kb + 8 g + 4 h + r; the max over the
       // tile's 32 positions goes to tmax (position ranges of the moments are whole tiles)
       const int i = 32 * nt + c;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[4 * g + r] *= a.scale;
+          if ((dmask >> (8 * g + 4 * h + r)) & 1u) acc[4 * g + r] = kNegInf;
+        }
       float tm = kNegInf;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (kb + 8 * g + 4 * h + r < a.N) tm = fmaxf(tm, a.scale * acc[4 * g + r]);
+          if (kb + 8 * g + 4 * h + r < a.N) tm = fmaxf(tm, acc[4 * g + r]);
       tm = fmaxf(tm, xor32(tm));
       if (i >= Cq) continue;
       if (h == 0) a.tmax[(static_cast<size_t>(bh) * Cq + i) * ((a.N + 31) / 32) + kb / 32] = tm;
@@ -95,13 +105,12 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
       for (int g = 0; g < 4; ++g) {
         const int k0 = kb + 8 * g + 4 * h;
         if (k0 + 3 < a.N) {
-          const f32x4_t f = {a.scale * acc[4 * g], a.scale * acc[4 * g + 1], a.scale * acc[4 * g + 2],
-                             a.scale * acc[4 * g + 3]};
+          const f32x4_t f = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
           *reinterpret_cast<f32x4_t*>(S + static_cast<size_t>(i) * a.N + k0) = f;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (k0 + r < a.N) S[static_cast<size_t>(i) * a.N + k0 + r] = a.scale * acc[4 * g + r];
+            if (k0 + r < a.N) S[static_cast<size_t>(i) * a.N + k0 + r] = acc[4 * g + r];
         }
       }
     }

@@ -160,9 +160,22 @@ typedef struct muse_fwd_params {
                                   side stream, no events; e.g. to time each kernel alone);
                                   0 (default): the stage-1 atoms run beside the scores and
                                   block moments on the library's second stream             */
+  double cap_ratio;            /* key cluster size cap (pith.science review, "Assumptions &
+                                  free parameters": ratio 1.5, 1.25 to 4.0 explored, the
+                                  row length of the padded per-cluster tensors). 0 (default):
+                                  no cap. > 0: key cluster j takes part in the stage-1
+                                  summaries (log Z_ij, K_ij, V_ij, dipole) with its first
+                                  U = ceil(cap_ratio * N / Ck) members in position order only;
+                                  the others are left out of them (causal: counted over the
+                                  whole sequence, so a bucket (b, j) keeps the members that
+                                  still fit after the blocks before b; every key is still
+                                  attended exactly inside its own block). Not combined with
+                                  retrieval (MUSE_ERR_UNSUPPORTED); negative or NaN:
+                                  MUSE_ERR_INVALID_ARG                                       */
 } muse_fwd_params;
 
-/* Defaults: scale 0, out_dtype -1, dipole tilted, retrieval off, hierarchy 0, all pointers NULL. */
+/* Defaults: scale 0, out_dtype -1, dipole tilted, retrieval off, hierarchy 0, single_stream 0,
+ * cap_ratio 0, all pointers NULL. */
 void muse_fwd_params_init(muse_fwd_params* p);
 
 /* muse_attn_fwd with optional controls; p == NULL means defaults. With fixed

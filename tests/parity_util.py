@@ -11,7 +11,7 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-from oracle import bucket_order, exact_attention, lloyd_kmeans, muse_acausal, muse_causal
+from oracle import bucket_order, cap_key_labels, exact_attention, lloyd_kmeans, muse_acausal, muse_causal
 from workloads import WorkloadConfig, make_inputs
 
 # Tolerances on relative L2 error (whole checked tensor) for fp32 and bf16 inputs with
@@ -42,10 +42,12 @@ class HeadCheck:
     rel: float
     near_ties_q: int
     near_ties_k: int
+    dropped_k: int = 0   # keys left out of the stage-1 summaries by a cluster size cap
 
 
 def run_gpu(cfg: WorkloadConfig, q, k, v, out_dtype=torch.float32, dipole=True, labels_q_in=None,
-            labels_k_in=None, topk=None, hierarchy=False, scale: float = 0.0, extra_returns: bool = False):
+            labels_k_in=None, topk=None, hierarchy=False, scale: float = 0.0, extra_returns: bool = False,
+            cap_ratio: float = 0.0):
     if topk is None:
         topk = (cfg.topk_clusters, cfg.topk_blocks)
     from clustered_softmax_attention_amd import attn_fwd
@@ -54,7 +56,8 @@ def run_gpu(cfg: WorkloadConfig, q, k, v, out_dtype=torch.float32, dipole=True, 
                        out_dtype=out_dtype, dipole=dipole, return_trace=True, return_lse=True,
                        return_centroids=extra_returns, return_buckets=extra_returns,
                        labels_q_in=labels_q_in, labels_k_in=labels_k_in,
-                       topk_clusters=topk[0], topk_blocks=topk[1], hierarchy=hierarchy, scale=scale)
+                       topk_clusters=topk[0], topk_blocks=topk[1], hierarchy=hierarchy, scale=scale,
+                       cap_ratio=cap_ratio)
     torch.cuda.synchronize()
     return out, ex
 
@@ -62,7 +65,7 @@ def run_gpu(cfg: WorkloadConfig, q, k, v, out_dtype=torch.float32, dipole=True, 
 def oracle_head(cfg: WorkloadConfig, q, k, v, trace_q, trace_k, dipole="tilted",
                 blocks: Optional[Sequence[int]] = None, rows: Optional[np.ndarray] = None,
                 retrieval_trace: Optional[np.ndarray] = None, hierarchy: bool = False,
-                scale: Optional[float] = None):
+                scale: Optional[float] = None, cap_ratio: Optional[float] = None):
     """Oracle of one head in follow mode (near-tie labels adopted from the GPU traces).
     Retrieval selections must equal the GPU's exactly (no near-tie adoption)."""
     kq = lloyd_kmeans(q, cfg.Cq, cfg.iters, follow_trace=trace_q)
@@ -73,12 +76,12 @@ def oracle_head(cfg: WorkloadConfig, q, k, v, trace_q, trace_k, dipole="tilted",
         r = muse_causal(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, cfg.block, dipole=dipole, scale=scale,
                         topk_clusters=cfg.topk_clusters, topk_blocks=cfg.topk_blocks,
                         labels_q=kq.labels, labels_k=kk.labels, blocks_to_eval=blocks,
-                        retrieval_follow=retrieval_trace, hierarchical=hierarchy)
+                        retrieval_follow=retrieval_trace, hierarchical=hierarchy, cap_ratio=cap_ratio)
         assert r.retrieval_mismatches == 0, "retrieval selections differ beyond near-ties"
         assert r.retrieval_near_ties == 0, "retrieval selections adopted from the GPU at near-ties"
     else:
         r = muse_acausal(q, k, v, cfg.Cq, cfg.Ck, cfg.iters, dipole=dipole, scale=scale,
-                         labels_q=kq.labels, labels_k=kk.labels, rows=rows)
+                         labels_q=kq.labels, labels_k=kk.labels, rows=rows, cap_ratio=cap_ratio)
     return r, kq, kk
 
 
@@ -106,17 +109,19 @@ def oracle_dipole(dipole) -> str:
 def check_config(cfg: WorkloadConfig, heads: List[Tuple[int, int]], tol: Optional[float] = None,
                  blocks: Optional[Sequence[int]] = None, out_dtype=torch.float32, dipole=True,
                  rows: Optional[np.ndarray] = None, hierarchy: bool = False, scale: Optional[float] = None,
-                 inputs=None) -> List[HeadCheck]:
+                 inputs=None, cap_ratio: Optional[float] = None) -> List[HeadCheck]:
     """Run the whole [B,H,N,D] workload on the GPU and compare the listed heads.
 
     scale: softmax scale passed to both sides (None: the library's and the oracle's
     default 1/sqrt(D)). inputs: (q, k, v) to use instead of the workload's generator.
+    cap_ratio: key cluster size cap passed to both sides (None: no cap).
     Besides the output and LSE, the final centroids (relative L2 <= 1e-5 per head: fp32
     member means against float64 ones) and the bucket order (bit-exact) are compared."""
     t0 = time.time()
     q, k, v = make_inputs(cfg) if inputs is None else inputs
     out, ex = run_gpu(cfg, q, k, v, out_dtype=out_dtype, dipole=dipole, hierarchy=hierarchy,
-                      scale=0.0 if scale is None else scale, extra_returns=True)
+                      scale=0.0 if scale is None else scale, extra_returns=True,
+                      cap_ratio=0.0 if cap_ratio is None else cap_ratio)
     o_gpu = out.float().cpu().numpy()
     tq = ex["labels_q_trace"].cpu().numpy()
     tk = ex["labels_k_trace"].cpu().numpy()
@@ -129,7 +134,7 @@ def check_config(cfg: WorkloadConfig, heads: List[Tuple[int, int]], tol: Optiona
         r, kq, kk = oracle_head(cfg, q[b, h], k[b, h], v[b, h], tq[:, b, h], tk[:, b, h],
                                 dipole=oracle_dipole(dipole), blocks=blocks, rows=rows,
                                 retrieval_trace=None if rtr is None else rtr[b, h], hierarchy=hierarchy,
-                                scale=scale)
+                                scale=scale, cap_ratio=cap_ratio)
         assert np.array_equal(kq.labels, tq[-1, b, h]) and np.array_equal(kk.labels, tk[-1, b, h])
         check_centroids_and_buckets(cfg, ex, b, h, kq, kk)
         sel = np.isfinite(r.o[:, 0])
@@ -140,5 +145,8 @@ def check_config(cfg: WorkloadConfig, heads: List[Tuple[int, int]], tol: Optiona
             f"rows checked {int(sel.sum())}")
         assert rel <= tol, f"rel-L2 {rel} > {tol}"
         assert lse_err <= (1e-4 if cfg.dtype == "f32" else 2e-3)
-        res.append(HeadCheck(b, h, rel, kq.near_ties, kk.near_ties))
+        dropped = int((cap_key_labels(kk.labels, cfg.Ck, cap_ratio) < 0).sum())
+        if cap_ratio is not None:
+            log(f"[{cfg.name}] head ({b},{h}): cap ratio {cap_ratio}: {dropped} keys left out")
+        res.append(HeadCheck(b, h, rel, kq.near_ties, kk.near_ties, dropped))
     return res

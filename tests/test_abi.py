@@ -53,9 +53,11 @@ def test_params_struct_layout_matches(lib):
     p = FwdParams()
     lib.muse_fwd_params_init(ctypes.byref(p))
     assert p.out_dtype == -1 and p.dipole == 1 and p.scale == 0.0 and p.topk_clusters == 0 and p.hierarchy == 0
-    # 5 ints/floats, pad, 8 pointers, size_t, pointer, int, pad, 4 bucket-order pointers, int, pad
-    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8 + 8 + 4 + 4 + 4 * 8 + 4 + 4
-    assert p.single_stream == 0
+    # 5 ints/floats, pad, 8 pointers, size_t, pointer, int, pad, 4 bucket-order pointers, int,
+    # pad, double
+    assert ctypes.sizeof(FwdParams) == 4 * 5 + 4 + 8 * 8 + 8 + 8 + 4 + 4 + 4 * 8 + 4 + 4 + 8
+    assert FwdParams.cap_ratio.offset == ctypes.sizeof(FwdParams) - 8
+    assert p.single_stream == 0 and p.cap_ratio == 0.0
     assert p.perm_q_out is None and p.offs_k_out is None
 
 
@@ -196,3 +198,31 @@ def test_noalloc_entry_rejects_before_launch(lib):
     # the usual validation still runs first
     bad = (vp(1), vp(2), vp(3), vp(4), 1, 1, 1024, 96, 8, 32, 5, 0, 0, 0, None)
     assert lib.muse_attn_fwd_noalloc(*bad, None) == -2
+
+
+def test_cluster_cap_arguments(lib):
+    from clustered_softmax_attention_amd.binding import FwdParams
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    base = lib.muse_attn_fwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, ctypes.byref(p))
+    p.cap_ratio = 1.5
+    # kept lengths [B*H, nb*Ck] int32 and a flag byte per key, each region 256-byte aligned
+    capped = lib.muse_attn_fwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, ctypes.byref(p))
+    assert capped == base + 32 * 128 * 4 + 32 * 8192
+    causal = lib.muse_attn_fwd_workspace_bytes(1, 1, 4096, 64, 16, 64, 1, 1024, 1, ctypes.byref(p))
+    p.hierarchy = 1  # with the hierarchical decomposition: accepted
+    assert lib.muse_attn_fwd_workspace_bytes(1, 1, 4096, 64, 16, 64, 1, 1024, 1, ctypes.byref(p)) == causal > 0
+    p.hierarchy = 0
+    p.dipole = 2  # untilted dipole: accepted
+    assert lib.muse_attn_fwd_workspace_bytes(1, 1, 4096, 64, 16, 64, 1, 1024, 0, ctypes.byref(p)) > 0
+    p.dipole = 1
+    vp = ctypes.c_void_p
+    causal_args = (vp(1), vp(2), vp(3), vp(4), 1, 1, 4096, 64, 16, 64, 5, 1, 1024, 1, None)
+    p.topk_clusters, p.topk_blocks = 2, 1  # not with retrieval
+    assert lib.muse_attn_fwd_ex(*causal_args, ctypes.byref(p)) == -2
+    assert "cap" in lib.muse_last_error().decode()
+    p.topk_clusters, p.topk_blocks = 0, 0
+    for bad in (-1.0, float("nan")):
+        p.cap_ratio = bad
+        assert lib.muse_attn_fwd_ex(*causal_args, ctypes.byref(p)) == -1
+        assert "cap_ratio" in lib.muse_last_error().decode()
