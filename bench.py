@@ -9,8 +9,9 @@ the workspace allocated beforehand. Prints ONE JSON line: `value` is the 8k work
 tokens/s (or the chosen workload's). Extra fields: the in-library exact attention time
 on the same shape (speedup), the relative squared error of MuSe against it, per-kernel
 average durations measured with HIP events on the stream the kernels run on, the
-untilted-dipole run of an acausal workload, the hierarchical-decomposition run of a causal
-one without retrieval, `measured_peaks` (a device copy and a bf16
+untilted-dipole run and the paper's speed setting (key clusters capped at 1.5 N / Ck
+members, one Lloyd iteration) of a workload without retrieval, the hierarchical-decomposition
+run of a causal one without retrieval, `measured_peaks` (a device copy and a bf16
 GEMM on this GPU, beside the published peaks the roofline uses) and, with the default
 workload, `secondary`: the same figures for the 64k causal configuration.
 """
@@ -507,58 +508,44 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
         extra = {"exact_ms_per_step": ms_ex, "speedup_vs_exact": ms_ex / ms, "rse_vs_exact": rse}
         print(f"# exact {ms_ex:.3f} ms/step, MuSe {ms:.3f} ms/step, speedup {ms_ex / ms:.2f}x, RSE {rse:.3e}",
               file=sys.stderr, flush=True)
+        def variant(label: str, iters: int, kernel_filter, **kw):
+            # the same workload with other options, timed like the main step; RSE against
+            # exact attention and the per-kernel durations of one profiled call
+            ws_x = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, cfg.causal,
+                                                       cfg.block, 1 if cfg.dtype == "bf16" else 0, **kw),
+                               dtype=torch.uint8, device="cuda")
+
+            def step():
+                binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, iters, causal=cfg.causal, block=cfg.block, out=out,
+                                 workspace=ws_x, **kw)
+
+            ms_x, _ = timed(step, steps, warmup)
+            binding.prof_reset()
+            binding.prof_enable(True)
+            step()
+            torch.cuda.synchronize()
+            prof_x = binding.prof_collect()
+            binding.prof_enable(False)
+            o_x = out.double()
+            rse_x = float(((o_x - o_e) ** 2).sum() / (o_e ** 2).sum())
+            extra[label] = {
+                "ms_per_step": ms_x, "value": cfg.B * cfg.N / (ms_x / 1e3), "speedup_vs_exact": ms_ex / ms_x,
+                "rse_vs_exact": rse_x,
+                "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in sorted(prof_x.items(), key=lambda kv: -kv[1][0])
+                               if kernel_filter(n)}}
+            print(f"# {label}: {ms_x:.3f} ms/step, speedup {ms_ex / ms_x:.2f}x, RSE {rse_x:.3e}, "
+                  f"{extra[label]['kernels_us']}", file=sys.stderr, flush=True)
+
         if cfg.topk_clusters == 0 and not hierarchy:
-            # the same workload with the untilted (per key cluster) dipole
-            ws_u = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, cfg.causal,
-                                                       cfg.block, 1 if cfg.dtype == "bf16" else 0, dipole="untilted"),
-                               dtype=torch.uint8, device="cuda")
-
-            def untilted_step():
-                binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=cfg.causal, block=cfg.block, out=out,
-                                 dipole="untilted", workspace=ws_u)
-
-            ms_u, _ = timed(untilted_step, steps, warmup)
-            binding.prof_reset()
-            binding.prof_enable(True)
-            untilted_step()
-            torch.cuda.synchronize()
-            prof_u = binding.prof_collect()
-            binding.prof_enable(False)
-            o_u = out.double()
-            rse_u = float(((o_u - o_e) ** 2).sum() / (o_e ** 2).sum())
-            extra["untilted_dipole"] = {
-                "ms_per_step": ms_u, "value": cfg.B * cfg.N / (ms_u / 1e3), "speedup_vs_exact": ms_ex / ms_u,
-                "rse_vs_exact": rse_u,
-                "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in prof_u.items() if "untilted" in n or "cov" in n}}
-            print(f"# untilted dipole: {ms_u:.3f} ms/step, speedup {ms_ex / ms_u:.2f}x, RSE {rse_u:.3e}, "
-                  f"{extra['untilted_dipole']['kernels_us']}", file=sys.stderr, flush=True)
-            del ws_u
+            # the untilted (per key cluster) dipole
+            variant("untilted_dipole", cfg.iters, lambda n: "untilted" in n or "cov" in n, dipole="untilted")
+            # the paper's speed setting: key clusters capped at 1.5 N / Ck members, one
+            # Lloyd iteration
+            variant("cap1.5_iters1", 1, lambda n: True, cap_ratio=1.5)
         if cfg.causal and cfg.topk_clusters == 0 and not hierarchy:
-            # the same workload with the hierarchical block decomposition (one two-stage
-            # approximation per square below the diagonal, log-sum-exp merged)
-            ws_h = torch.empty(binding.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, True, cfg.block,
-                                                       1 if cfg.dtype == "bf16" else 0, hierarchy=True),
-                               dtype=torch.uint8, device="cuda")
-
-            def hier_step():
-                binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=True, block=cfg.block, out=out,
-                                 workspace=ws_h, hierarchy=True)
-
-            ms_h, _ = timed(hier_step, steps, warmup)
-            binding.prof_reset()
-            binding.prof_enable(True)
-            hier_step()
-            torch.cuda.synchronize()
-            prof_h = binding.prof_collect()
-            binding.prof_enable(False)
-            o_h = out.double()
-            rse_h = float(((o_h - o_e) ** 2).sum() / (o_e ** 2).sum())
-            extra["hierarchy"] = {
-                "ms_per_step": ms_h, "value": cfg.B * cfg.N / (ms_h / 1e3), "speedup_vs_exact": ms_ex / ms_h,
-                "rse_vs_exact": rse_h,
-                "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in sorted(prof_h.items(), key=lambda kv: -kv[1][0])}}
-            print(f"# hierarchy: {ms_h:.3f} ms/step, speedup {ms_ex / ms_h:.2f}x, RSE {rse_h:.3e}, "
-                  f"{extra['hierarchy']['kernels_us']}", file=sys.stderr, flush=True)
+            # the hierarchical block decomposition (one two-stage approximation per square
+            # below the diagonal, log-sum-exp merged)
+            variant("hierarchy", cfg.iters, lambda n: True, hierarchy=True)
     if ctx is not None:
         extra["retrieved_keys"] = ctx
     return {"cfg": cfg, "ms": ms, "wall": wall, "value": value, "kernels": kernels, "roofline": roofline,

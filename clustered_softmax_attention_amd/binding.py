@@ -272,13 +272,14 @@ def prof_collect() -> dict:
 
 
 def workspace_bytes(B, H, N, D, Cq, Ck, causal=False, block=0, dtype=MUSE_BF16, topk_clusters=0,
-                    topk_blocks=0, dipole=True, hierarchy=False) -> int:
+                    topk_blocks=0, dipole=True, hierarchy=False, cap_ratio=0.0) -> int:
     lib = load()
     p = FwdParams()
     lib.muse_fwd_params_init(ctypes.byref(p))
     p.topk_clusters, p.topk_blocks = topk_clusters, topk_blocks
     p.dipole = dipole_code(dipole)
     p.hierarchy = int(hierarchy)
+    p.cap_ratio = float(cap_ratio)
     n = lib.muse_attn_fwd_workspace_bytes(B, H, N, D, Cq, Ck, int(causal), int(block), dtype, ctypes.byref(p))
     if n == 0:
         raise MuseError(-1, lib.muse_last_error().decode())
