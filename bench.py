@@ -542,6 +542,10 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
             # the paper's speed setting: key clusters capped at 1.5 N / Ck members, one
             # Lloyd iteration
             variant("cap1.5_iters1", 1, lambda n: True, cap_ratio=1.5)
+        if cfg.topk_clusters > 0:
+            # the same workload with retrieval off (k1 = 0): what retrieval changes in time
+            # and in error against exact attention
+            variant("retrieval_off", cfg.iters, lambda n: True)
         if cfg.causal and cfg.topk_clusters == 0 and not hierarchy:
             # the hierarchical block decomposition (one two-stage approximation per square
             # below the diagonal, log-sum-exp merged)

@@ -27,7 +27,7 @@ STATUS = {0: "MUSE_OK", -1: "MUSE_ERR_INVALID_ARG", -2: "MUSE_ERR_UNSUPPORTED", 
 EXPORTED = ("muse_attn_fwd", "muse_exact_attn_fwd", "muse_attn_fwd_ex", "muse_fwd_params_init",
             "muse_attn_fwd_workspace_bytes", "muse_last_error", "muse_version", "muse_prof_enable",
             "muse_prof_collect", "muse_prof_name", "muse_prof_total_ms", "muse_prof_launches",
-            "muse_prof_reset", "muse_attn_fwd_noalloc")
+            "muse_prof_reset", "muse_attn_fwd_noalloc", "muse_attn_bwd", "muse_attn_bwd_workspace_bytes")
 
 
 class MuseError(RuntimeError):
@@ -78,6 +78,10 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.muse_attn_fwd_ex.restype = i
     lib.muse_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp] + [i] * 10 + [vp, ctypes.POINTER(FwdParams)]
     lib.muse_attn_fwd_noalloc.restype = i
+    lib.muse_attn_bwd.argtypes = [vp] * 9 + [i] * 9 + [vp, ctypes.POINTER(FwdParams)]
+    lib.muse_attn_bwd.restype = i
+    lib.muse_attn_bwd_workspace_bytes.argtypes = [i] * 9 + [ctypes.POINTER(FwdParams)]
+    lib.muse_attn_bwd_workspace_bytes.restype = sz
     lib.muse_exact_attn_fwd.argtypes = [vp, vp, vp, vp] + [i] * 6 + [vp]
     lib.muse_exact_attn_fwd.restype = i
     lib.muse_fwd_params_init.argtypes = [ctypes.POINTER(FwdParams)]
@@ -229,6 +233,44 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
                                 int(causal), int(block), _dtype_code(q), _stream(), ctypes.byref(p)))
     del keep
     return (out, extras) if extras else out
+
+
+def attn_bwd(q, k, v, dout, labels_q, labels_k, Cq: int, Ck: int, causal: bool = False, block: int = 0, *,
+             scale: float = 0.0, dipole=True, workspace: Optional[torch.Tensor] = None):
+    """muse_attn_bwd: (dq, dk, dv) float32 [B,H,N,D] of the forward output for the upstream
+    gradient dout (the inputs' dtype), with the forward's final labels [B,H,N] held fixed."""
+    lib = load()
+    _check_qkv(q, k, v)
+    if not (dout.is_cuda and dout.is_contiguous() and dout.shape == q.shape and dout.dtype == q.dtype):
+        raise ValueError("dout must be a contiguous device tensor of q's shape and dtype")
+    B, H, N, D = q.shape
+    lq = labels_q.to(device=q.device, dtype=torch.int32).contiguous()
+    lk = labels_k.to(device=q.device, dtype=torch.int32).contiguous()
+    if lq.shape != (B, H, N) or lk.shape != (B, H, N):
+        raise ValueError("labels must be [B, H, N]")
+    dq, dk, dv = (torch.empty((B, H, N, D), dtype=torch.float32, device=q.device) for _ in range(3))
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    p.scale = float(scale)
+    p.dipole = dipole_code(dipole)
+    if workspace is not None:
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.muse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lq), _ptr(lk), _ptr(dq), _ptr(dk),
+                             _ptr(dv), B, H, N, D, Cq, Ck, int(causal), int(block), _dtype_code(q), _stream(),
+                             ctypes.byref(p)))
+    return dq, dk, dv
+
+
+def bwd_workspace_bytes(B, H, N, D, Cq, Ck, causal=False, block=0, dtype=MUSE_BF16, dipole=True) -> int:
+    lib = load()
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    p.dipole = dipole_code(dipole)
+    n = lib.muse_attn_bwd_workspace_bytes(B, H, N, D, Cq, Ck, int(causal), int(block), dtype, ctypes.byref(p))
+    if n == 0:
+        raise MuseError(-1, lib.muse_last_error().decode())
+    return n
 
 
 def attn_fwd_noalloc(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False, block: int = 0,

@@ -1,0 +1,755 @@
+// Backward pass of the acausal MuSe forward (gfx950).
+//
+// The reviews note that the method's backward pass uses the same approximations as its
+// forward and that its error was never measured (pith.science review, "Reading between
+// the lines"). Differentiated here: the forward output o(q, k, v) with the K-means labels
+// held fixed (the clustering is piecewise constant in q and k). With s the softmax scale,
+// for query n of query cluster i (qt_n = q_n - qbar_i, qbar_i the member mean) and key m
+// of key cluster j:
+//   stage 2  o_n = sum_j p_nj V_ij + s D_i qt_n,   p_n = softmax_j (log Z_ij + s qt_n . K_ij)
+//   stage 1  a_im = s qbar_i . k_m,  w_im = exp(a_im - log Z_ij),  log Z_ij = lse_{m in j} a_im,
+//            K_ij = sum w k,  V_ij = sum w v,  P_ij = softmax_j log Z_ij,
+//            D_i = sum_j P_ij C_ij  with  C_ij = sum w v k^T - V_ij K_ij^T  (tilted)  or
+//            C_ij = Cov_j (untilted: the plain covariance of cluster j)
+// (pith.science review, "What carries the argument" and "Assumptions & free parameters";
+// gist.science summary, Kernmechanismen 2). The gradients, in reverse:
+//   bw_refine    per query cluster i: dL/dlog Z_i., dL/dK_i., dL/dV_i., dL/dD_i (G_Dip_i),
+//                the residual part of dq and its sum (the stage-2 part of dL/dqbar_i).
+//   bw_prep_i    per i: P_i., log sum_j Z_ij, G_Dip_i in bf16 hi + lo (both layouts), and
+//                dK'_ij = dL/dK_ij - P_ij G_Dip_i^T V_ij, dV'_ij = dL/dV_ij - P_ij G_Dip_i K_ij
+//                (the tilted dipole's C_ij depends on K_ij and V_ij), V_ij^T G_Dip_i K_ij.
+//   bw_prep_j    (untilted) per j: dL/dP_ij = <G_Dip_i, Cov_j>, sum_i P_ij G_Dip_i, means.
+//   bw_scores    a_im at every key position (bucket order).
+//   bw_keys_a    (tilted) per 128 keys, on the matrix cores: Q_im = v_m^T G_Dip_i k_m, and
+//                the dipole's direct terms  dk_m = sum_i p_im G_Dip_i^T v_m,
+//                dv_m = sum_i p_im G_Dip_i k_m  (p_im = w_im P_ij = exp(a_im) / sum_j Z_ij).
+//   bw_dlogz     per i: dL/dP_ij = sum_{m in j} w_im Q_im - V_ij^T G_Dip_i K_ij (tilted),
+//                dL/dlog Z_ij through P, and sum_{m in j} w_im dL/dw_im in closed form.
+//   bw_keys_b    per 64 keys: dL/dw_im, da_im = w_im (dL/dw_im - sum_j + dL/dlog Z_ij), the
+//                rest of dk_m and dv_m, and per tile s sum_m w dL/dw k_m for dL/dqbar.
+//   bw_centroid  per i: dL/dqbar_i, spread over the members (qbar is their mean).
+// All arithmetic in fp32 (bf16 inputs are exact in it); the matrix-core products split
+// G_Dip (and fp32 keys and values) into bf16 hi + lo. Every sum runs in a fixed order.
+#include "mfma.hpp"
+#include "muse_kernels.hpp"
+
+namespace muse {
+
+constexpr int kBwQT = 16;   // queries per tile of the stage-2 backward
+constexpr int kBwGST = kBwD + 8;  // LDS row stride (bf16) of the staged G_Dip tiles
+
+// dL/dlog Z, dL/dK, dL/dV, dL/dD of one query cluster and the residual part of dq.
+// LDS: K_i. and V_i. rows (fp32, padded), D_i, the tile's residuals and upstream
+// gradients, and the tile's weights p and dl = dL/dlogit.
+template <typename T>
+__global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
+  constexpr int D = kBwD, DP = D + 1, CP = kMaxClusters + 1, QT = kBwQT;
+  __shared__ float sK[kMaxClusters * DP];
+  __shared__ float sV[kMaxClusters * DP];
+  __shared__ float sDip[D * DP];
+  __shared__ float sQt[QT * DP];
+  __shared__ float sG[QT * DP];
+  __shared__ float sL[QT * CP];
+  __shared__ float sDl[QT * CP];
+  __shared__ float sLz[kMaxClusters];
+  __shared__ float sQbar[D];
+  __shared__ int sRow[QT];
+  __shared__ float sRed[4][D];
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Cq = a.Cq, Ck = a.Ck, N = a.N;
+  const float s = a.scale;
+  const bool dip = a.dipole != 0;
+  const size_t ti = static_cast<size_t>(bh) * Cq + i;
+  for (int e = tid; e < Ck * D; e += 256) {
+    const int j = e / D, d = e % D;
+    sK[j * DP + d] = a.tk[ti * Ck * D + e];
+    sV[j * DP + d] = a.tv[ti * Ck * D + e];
+  }
+  if (dip)
+    for (int e = tid; e < D * D; e += 256) sDip[(e / D) * DP + e % D] = a.dip[ti * D * D + e];
+  for (int j = tid; j < Ck; j += 256) sLz[j] = a.logz[ti * Ck + j];
+  if (tid < D) sQbar[tid] = a.qbar[ti * D + tid];
+  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (Cq + 1);
+  const int o0 = offq[i], o1 = offq[i + 1];
+  const int32_t* perm = a.perm_q + static_cast<size_t>(bh) * N;
+  const T* Q = static_cast<const T*>(a.q) + static_cast<size_t>(bh) * N * D;
+  const T* G = static_cast<const T*>(a.dout) + static_cast<size_t>(bh) * N * D;
+  float* dq = a.dq + static_cast<size_t>(bh) * N * D;
+  // summary-gradient accumulators: dL/dK, dL/dV of cluster aj, dims ad0 .. ad0 + 31
+  const int aj = tid >> 1, ad0 = (tid & 1) * 32;
+  float gk[32], gv[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) gk[r] = gv[r] = 0.f;
+  // dL/dD_i: row pv (value index), columns pd0 .. pd0 + 15
+  const int pv = tid >> 2, pd0 = (tid & 3) * 16;
+  float gdp[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) gdp[r] = 0.f;
+  float glz = 0.f;                         // dL/dlog Z_ij for j = tid
+  const int ed = tid & 63, eg = tid >> 6;  // dq rows: dimension ed of queries 4 eg .. 4 eg + 3
+  float qbs = 0.f;                         // - sum of this thread's dq values
+  __syncthreads();
+  for (int t0 = o0; t0 < o1; t0 += QT) {
+    const int nq = min(QT, o1 - t0);
+    for (int e = tid; e < QT * D; e += 256) {
+      const int qq = e / D, d = e % D;
+      float qt = 0.f, g = 0.f;
+      if (qq < nq) {
+        const int n = perm[t0 + qq];
+        qt = Elem<T>::load(Q, static_cast<size_t>(n) * D + d) - sQbar[d];
+        g = Elem<T>::load(G, static_cast<size_t>(n) * D + d);
+        if (d == 0) sRow[qq] = n;
+      }
+      sQt[qq * DP + d] = qt;
+      sG[qq * DP + d] = g;
+    }
+    __syncthreads();
+    {
+      // logits and dp_nj = g_n . V_ij: cluster j, queries q0 .. q0 + 7
+      const int j = tid & 127, q0 = (tid >> 7) * 8;
+      if (j < Ck) {
+        float l[8], dp[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) l[r] = dp[r] = 0.f;
+        for (int d = 0; d < D; ++d) {
+          const float kj = sK[j * DP + d], vj = sV[j * DP + d];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            l[r] = fmaf(sQt[(q0 + r) * DP + d], kj, l[r]);
+            dp[r] = fmaf(sG[(q0 + r) * DP + d], vj, dp[r]);
+          }
+        }
+        const float lz = sLz[j];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          sL[(q0 + r) * CP + j] = lz == kNegInf ? kNegInf : lz + s * l[r];
+          sDl[(q0 + r) * CP + j] = dp[r];
+        }
+      }
+    }
+    __syncthreads();
+    // softmax over the key clusters and dl = p (dp - sum_j p dp): a wave per row
+    for (int qq = wave; qq < QT; qq += 4) {
+      float lv[2], dv2[2], mx = kNegInf;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int j = lane + 64 * t;
+        lv[t] = j < Ck ? sL[qq * CP + j] : kNegInf;
+        dv2[t] = j < Ck ? sDl[qq * CP + j] : 0.f;
+        mx = fmaxf(mx, lv[t]);
+      }
+      mx = wave_max(mx);
+      float e2[2], z = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        e2[t] = lv[t] == kNegInf ? 0.f : __expf(lv[t] - mx);
+        z += e2[t];
+      }
+      z = wave_sum(z);
+      const float inv = (z > 0.f && qq < nq) ? 1.f / z : 0.f;
+      float rs = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        e2[t] *= inv;
+        rs = fmaf(e2[t], dv2[t], rs);
+      }
+      rs = wave_sum(rs);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int j = lane + 64 * t;
+        if (j < Ck) {
+          sL[qq * CP + j] = e2[t];
+          sDl[qq * CP + j] = e2[t] * (dv2[t] - rs);
+        }
+      }
+    }
+    __syncthreads();
+    if (aj < Ck) {
+      for (int qq = 0; qq < nq; ++qq) {
+        const float p = sL[qq * CP + aj], dl = sDl[qq * CP + aj];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+          gv[r] = fmaf(p, sG[qq * DP + ad0 + r], gv[r]);
+          gk[r] = fmaf(dl, sQt[qq * DP + ad0 + r], gk[r]);
+        }
+      }
+    }
+    if (tid < Ck)
+      for (int qq = 0; qq < nq; ++qq) glz += sDl[qq * CP + tid];
+    if (dip) {
+      for (int qq = 0; qq < nq; ++qq) {
+        const float g = sG[qq * DP + pv];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gdp[r] = fmaf(g, sQt[qq * DP + pd0 + r], gdp[r]);
+      }
+    }
+    {
+      // dq_n = s sum_j dl_nj K_ij + s D_i^T g_n  (dimension ed)
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < Ck; ++j) {
+        const float kd = sK[j * DP + ed];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf(sDl[(4 * eg + r) * CP + j], kd, acc[r]);
+      }
+      if (dip) {
+        for (int vv = 0; vv < D; ++vv) {
+          const float dd = sDip[vv * DP + ed];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] = fmaf(sG[(4 * eg + r) * DP + vv], dd, acc[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qq = 4 * eg + r;
+        if (qq < nq) {
+          const float x = s * acc[r];
+          dq[static_cast<size_t>(sRow[qq]) * D + ed] = x;
+          qbs -= x;
+        }
+      }
+    }
+    __syncthreads();  // the tile buffers are rewritten next
+  }
+  if (aj < Ck) {
+    const size_t o = (ti * Ck + aj) * D + ad0;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      a.g_k[o + r] = s * gk[r];
+      a.g_v[o + r] = gv[r];
+    }
+  }
+  if (tid < Ck) a.g_logz[ti * Ck + tid] = glz;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a.g_dip[ti * D * D + static_cast<size_t>(pv) * D + pd0 + r] = dip ? s * gdp[r] : 0.f;
+  sRed[eg][ed] = qbs;
+  __syncthreads();
+  if (tid < D) a.dqbar2[ti * D + tid] = (sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid]);
+}
+
+// Per query cluster i: P_i., log sum_j Z_ij, the bf16 hi/lo copies of G_Dip_i (tilted), and
+// for every key cluster j: dK'_ij, dV'_ij and V_ij^T G_Dip_i K_ij. Two clusters at a time
+// (threads 0-127: j, 128-255: j + 1; of each half, 64 threads per output dimension).
+__global__ void __launch_bounds__(256) bw_prep_i_kernel(BwArgs a) {
+  constexpr int D = kBwD, DP = D + 1;
+  __shared__ float sGd[D * DP];
+  __shared__ float sP[kMaxClusters];
+  __shared__ float sKr[2][D], sVr[2][D], sY[2][D];
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Cq = a.Cq, Ck = a.Ck;
+  const size_t ti = static_cast<size_t>(bh) * Cq + i;
+  const bool tilted = a.dipole == 1;
+  if (wave == 0) {
+    float l[2], mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = lane + 64 * t;
+      l[t] = j < Ck ? a.logz[ti * Ck + j] : kNegInf;
+      mx = fmaxf(mx, l[t]);
+    }
+    mx = wave_max(mx);
+    float e2[2], z = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      e2[t] = l[t] == kNegInf ? 0.f : __expf(l[t] - mx);
+      z += e2[t];
+    }
+    z = wave_sum(z);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = lane + 64 * t;
+      if (j < Ck) {
+        sP[j] = e2[t] / z;
+        a.P[ti * Ck + j] = e2[t] / z;
+      }
+    }
+    if (lane == 0) a.lz[ti] = mx + __logf(z);
+  }
+  if (tilted)
+    for (int e = tid; e < D * D; e += 256) sGd[(e / D) * DP + e % D] = a.g_dip[ti * D * D + e];
+  __syncthreads();
+  if (tilted) {
+    uint16_t* gd = a.gd + ti * 4 * D * D;
+    for (int e = tid; e < D * D; e += 256) {
+      const int r = e / D, c = e % D;
+      const float x = sGd[r * DP + c];   // G_Dip[v = r][d = c]
+      const float y = sGd[c * DP + r];   // transpose: row d = r, column v = c
+      const uint16_t xh = f32_to_bf16_bits(x), yh = f32_to_bf16_bits(y);
+      gd[e] = xh;
+      gd[D * D + e] = f32_to_bf16_bits(x - bf16_to_f32(xh));
+      gd[2 * D * D + e] = yh;
+      gd[3 * D * D + e] = f32_to_bf16_bits(y - bf16_to_f32(yh));
+    }
+  }
+  const int half = tid >> 7, t = tid & 127;
+  for (int j0 = 0; j0 < Ck; j0 += 2) {
+    const int j = j0 + half;
+    const bool ok = j < Ck;
+    const size_t tj = (ti * Ck + (ok ? j : 0)) * D;
+    __syncthreads();  // the previous pair's rows are consumed
+    if (t < D) {
+      sKr[half][t] = ok ? a.tk[tj + t] : 0.f;
+      sVr[half][t] = ok ? a.tv[tj + t] : 0.f;
+    }
+    __syncthreads();
+    if (ok) {
+      const float pj = sP[j];
+      if (t < D) {  // dK'[d] = dL/dK[d] - P sum_v G_Dip[v][d] V[v]
+        float x = 0.f;
+        if (tilted)
+          for (int vv = 0; vv < D; ++vv) x = fmaf(sGd[vv * DP + t], sVr[half][vv], x);
+        a.dKp[tj + t] = a.g_k[tj + t] - pj * x;
+      } else {      // y[v] = sum_d G_Dip[v][d] K[d];  dV'[v] = dL/dV[v] - P y[v]
+        const int vv = t - D;
+        float y = 0.f;
+        if (tilted)
+          for (int d = 0; d < D; ++d) y = fmaf(sGd[vv * DP + d], sKr[half][d], y);
+        a.dVp[tj + vv] = a.g_v[tj + vv] - pj * y;
+        sY[half][vv] = y;
+      }
+    }
+    __syncthreads();
+    if (tilted && ok && t < D) {  // one whole wave (0 or 2) per half
+      const float z = wave_sum(sVr[half][t] * sY[half][t]);
+      if (t == 0) a.vgk[ti * Ck + j] = z;
+    }
+  }
+}
+
+// Untilted dipole, per key cluster j: dL/dP_ij = <G_Dip_i, Cov_j> for every i, the matrix
+// sum_i P_ij G_Dip_i and the cluster's key and value means.
+template <typename T>
+__global__ void __launch_bounds__(256) bw_prep_j_kernel(BwArgs a) {
+  constexpr int D = kBwD, EPT = D * D / 256;
+  __shared__ float sRed[4];
+  const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Cq = a.Cq, Ck = a.Ck, N = a.N;
+  const size_t tj = static_cast<size_t>(bh) * Ck + j;
+  float cv[EPT], dc[EPT];
+#pragma unroll
+  for (int r = 0; r < EPT; ++r) {
+    cv[r] = a.cov[tj * D * D + tid + 256 * r];
+    dc[r] = 0.f;
+  }
+  for (int i = 0; i < Cq; ++i) {
+    const size_t ti = static_cast<size_t>(bh) * Cq + i;
+    const float p = a.P[ti * Ck + j];
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const float g = a.g_dip[ti * D * D + tid + 256 * r];
+      dc[r] = fmaf(p, g, dc[r]);
+      part = fmaf(g, cv[r], part);
+    }
+    part = wave_sum(part);
+    __syncthreads();  // the previous value was read
+    if (lane == 0) sRed[wave] = part;
+    __syncthreads();
+    if (tid == 0) a.dP[ti * Ck + j] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+  }
+#pragma unroll
+  for (int r = 0; r < EPT; ++r) a.dcov[tj * D * D + tid + 256 * r] = dc[r];
+  const int32_t* offk = a.offs_k + static_cast<size_t>(bh) * (Ck + 1);
+  const int m0 = offk[j], m1 = offk[j + 1];
+  if (tid < 2 * D) {
+    const T* X = static_cast<const T*>(tid < D ? a.k : a.v) + static_cast<size_t>(bh) * N * D;
+    const int d = tid % D;
+    const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * N;
+    float sum = 0.f;
+    for (int pp = m0; pp < m1; ++pp) sum += Elem<T>::load(X, static_cast<size_t>(perm[pp]) * D + d);
+    const float mean = m1 > m0 ? sum / static_cast<float>(m1 - m0) : 0.f;
+    (tid < D ? a.kmean : a.vmean)[tj * D + d] = mean;
+  }
+}
+
+// a_im = s qbar_i . k_m at every key position (bucket order): four threads per key
+// (16 dimensions each, summed over the quad).
+template <typename T>
+__global__ void __launch_bounds__(256) bw_scores_kernel(BwArgs a) {
+  constexpr int D = kBwD, KT = kBwKeyTile, DQ = D / 4;
+  __shared__ float sQb[kMaxClusters * D];
+  const int bh = blockIdx.y, tid = threadIdx.x, kk = tid >> 2, d0 = (tid & 3) * DQ;
+  const int N = a.N, Cq = a.Cq;
+  for (int e = tid; e < Cq * D; e += 256) sQb[e] = a.qbar[static_cast<size_t>(bh) * Cq * D + e];
+  const int pos = blockIdx.x * KT + kk;
+  const bool valid = pos < N;
+  const int key = valid ? a.perm_k[static_cast<size_t>(bh) * N + pos] : 0;
+  const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * N * D;
+  float kf[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) kf[e] = valid ? Elem<T>::load(K, static_cast<size_t>(key) * D + d0 + e) : 0.f;
+  __syncthreads();
+  float* A = a.A + static_cast<size_t>(bh) * Cq * N;
+  for (int i = 0; i < Cq; ++i) {
+    float x = 0.f;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) x = fmaf(sQb[i * D + d0 + e], kf[e], x);
+    x += dpp_f32<0xB1>(x);  // lane ^ 1
+    x += dpp_f32<0x4E>(x);  // lane ^ 2
+    if (valid && (tid & 3) == 0) A[static_cast<size_t>(i) * N + pos] = a.scale * x;
+  }
+}
+
+// Tilted dipole, 128 keys per workgroup (a wave per 32 consecutive key positions), query
+// clusters in order with G_Dip_i (bf16 hi + lo, both layouts) staged in LDS, double
+// buffered: on the matrix cores u^T = G_Dip_i K^T (rows v, column = key) and
+// t^T = G_Dip_i^T V^T (rows d); then Q_im = v_m . u_m, and the accumulators
+// dv_m += p_im u_m, dk_m += p_im t_m, written as the dipole terms of dk and dv.
+template <typename T>
+__global__ void __launch_bounds__(256) bw_keys_a_kernel(BwArgs a) {
+  constexpr int D = kBwD, GST = kBwGST, NKS = D / 16, NMT = D / 32;
+  constexpr int NPF = 4 * D * D / 8 / 256;  // 16-byte pieces of the four tiles per thread
+  constexpr bool F32 = sizeof(T) == 4;
+  __shared__ __align__(16) uint16_t sGd[2][4 * D * GST];
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int wave = tid >> 6;
+  const int N = a.N, Cq = a.Cq, Ck = a.Ck;
+  const int pos = blockIdx.x * 128 + wave * 32 + c;
+  const bool valid = pos < N;
+  const int key = valid ? a.perm_k[static_cast<size_t>(bh) * N + pos] : 0;
+  const int j = valid ? min(max(a.labels_k[static_cast<size_t>(bh) * N + key], 0), Ck - 1) : 0;
+  const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * N * D;
+  const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * N * D;
+  // B operands: key c, dimensions 16 ks + 8 h .. + 7 (bf16 hi, and lo for fp32 inputs)
+  bf16x8_t kh[NKS], kl[NKS], vh[NKS], vl[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    float x[8], y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const size_t o = static_cast<size_t>(key) * D + 16 * ks + 8 * h + e;
+      x[e] = valid ? Elem<T>::load(K, o) : 0.f;
+      y[e] = valid ? Elem<T>::load(V, o) : 0.f;
+    }
+    split_bf16x8(x, kh[ks], kl[ks]);
+    split_bf16x8(y, vh[ks], vl[ks]);
+  }
+  // v_m at the accumulator rows 32 mt + 8 g + 4 h + r
+  float vq[NMT * 16];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      vq[16 * mt + v] = valid ? Elem<T>::load(V, static_cast<size_t>(key) * D + 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3)) : 0.f;
+  u16x8_t pf[NPF];
+  auto fetch = [&](int i) {
+    const uint16_t* src = a.gd + (static_cast<size_t>(bh) * Cq + i) * 4 * D * D;
+#pragma unroll
+    for (int q = 0; q < NPF; ++q) pf[q] = *reinterpret_cast<const u16x8_t*>(src + 8 * (tid + 256 * q));
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < NPF; ++q) {
+      const int e = 8 * (tid + 256 * q), arr = e / (D * D), rem = e % (D * D);
+      *reinterpret_cast<u16x8_t*>(&sGd[buf][arr * D * GST + (rem / D) * GST + rem % D]) = pf[q];
+    }
+  };
+  f32x16_t adk[NMT], adv[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) adk[mt] = adv[mt] = zero16();
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  const float* Arow = a.A + static_cast<size_t>(bh) * Cq * N;
+  for (int i = 0; i < Cq; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < Cq) fetch(i + 1);  // the next tiles travel during this cluster's products
+    const size_t ti = static_cast<size_t>(bh) * Cq + i;
+    const float av = valid ? Arow[static_cast<size_t>(i) * N + pos] : 0.f;
+    const float lzij = a.logz[ti * Ck + j];
+    const float w = (valid && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
+    const float p = valid ? __expf(av - a.lz[ti]) : 0.f;
+    const uint16_t* g = sGd[buf];
+    f32x16_t u[NMT], t[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) u[mt] = t[mt] = zero16();
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int o = (32 * mt + c) * GST + 16 * ks + 8 * h;
+        const bf16x8_t gh = as_bf16x8(*reinterpret_cast<const u16x8_t*>(g + o));
+        const bf16x8_t gl = as_bf16x8(*reinterpret_cast<const u16x8_t*>(g + D * GST + o));
+        const bf16x8_t th = as_bf16x8(*reinterpret_cast<const u16x8_t*>(g + 2 * D * GST + o));
+        const bf16x8_t tl = as_bf16x8(*reinterpret_cast<const u16x8_t*>(g + 3 * D * GST + o));
+        u[mt] = mfma32(gh, kh[ks], u[mt]);
+        u[mt] = mfma32(gl, kh[ks], u[mt]);
+        t[mt] = mfma32(th, vh[ks], t[mt]);
+        t[mt] = mfma32(tl, vh[ks], t[mt]);
+        if (F32) {
+          u[mt] = mfma32(gh, kl[ks], u[mt]);
+          t[mt] = mfma32(th, vl[ks], t[mt]);
+        }
+      }
+    float qp = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        qp = fmaf(vq[16 * mt + v], u[mt][v], qp);
+        adv[mt][v] = fmaf(p, u[mt][v], adv[mt][v]);
+        adk[mt][v] = fmaf(p, t[mt][v], adk[mt][v]);
+      }
+    const float qv = qp + xor32(qp);
+    if (valid && h == 0) {
+      const size_t o = (static_cast<size_t>(bh) * Cq + i) * N + pos;
+      a.Q[o] = qv;
+      a.WQ[o] = w * qv;
+    }
+    if (i + 1 < Cq) stage(buf ^ 1);
+    __syncthreads();
+  }
+  if (valid) {
+    float* dk = a.dk + (static_cast<size_t>(bh) * N + key) * D;
+    float* dv = a.dv + (static_cast<size_t>(bh) * N + key) * D;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * mt + 8 * g4 + 4 * h;
+        *reinterpret_cast<f32x4_t*>(dk + d0) = f32x4_t{adk[mt][4 * g4], adk[mt][4 * g4 + 1], adk[mt][4 * g4 + 2], adk[mt][4 * g4 + 3]};
+        *reinterpret_cast<f32x4_t*>(dv + d0) = f32x4_t{adv[mt][4 * g4], adv[mt][4 * g4 + 1], adv[mt][4 * g4 + 2], adv[mt][4 * g4 + 3]};
+      }
+  }
+}
+
+// Per query cluster i: dL/dP_ij (tilted: sum over the bucket of w Q, a wave per cluster in
+// a fixed reduction order, minus V^T G_Dip K; untilted: from bw_prep_j), then
+//   dL/dlog Z_ij = G_logZ_ij + P_ij (dL/dP_ij - sum_j' P_ij' dL/dP_ij'),
+//   S_ij = sum_{m in j} w_im dL/dw_im = dK'.K + dV'.V (+ P (dL/dP + V^T G_Dip K), tilted),
+// and the part  s sum_j (dL/dlog Z_ij - S_ij) K_ij  of dL/dqbar_i (sum_m w_im k_m = K_ij).
+__global__ void __launch_bounds__(256) bw_dlogz_kernel(BwArgs a) {
+  constexpr int D = kBwD;
+  __shared__ float sdP[kMaxClusters], sdl[kMaxClusters], sS[kMaxClusters];
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Cq = a.Cq, Ck = a.Ck, N = a.N;
+  const size_t ti = static_cast<size_t>(bh) * Cq + i;
+  const bool tilted = a.dipole == 1;
+  const int32_t* offk = a.offs_k + static_cast<size_t>(bh) * (Ck + 1);
+  for (int j = wave; j < Ck; j += 4) {
+    float x = 0.f;
+    if (tilted) {
+      const int m0 = offk[j], m1 = offk[j + 1];
+      const float* wq = a.WQ + ti * N;
+      for (int pp = m0 + lane; pp < m1; pp += 64) x += wq[pp];
+      x = wave_sum(x) - a.vgk[ti * Ck + j];
+    } else if (a.dipole == 2) {
+      x = a.dP[ti * Ck + j];
+    }
+    if (lane == 0) sdP[j] = x;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float pd = 0.f;
+    for (int j = lane; j < Ck; j += 64) pd = fmaf(a.P[ti * Ck + j], sdP[j], pd);
+    pd = wave_sum(pd);
+    for (int j = lane; j < Ck; j += 64) {
+      const float x = a.g_logz[ti * Ck + j] + (a.logz[ti * Ck + j] == kNegInf ? 0.f : a.P[ti * Ck + j] * (sdP[j] - pd));
+      sdl[j] = x;
+      a.dlogz[ti * Ck + j] = x;
+    }
+  }
+  for (int j = wave; j < Ck; j += 4) {
+    const size_t tj = (ti * Ck + j) * D;
+    float x = 0.f;
+    if (a.logz[ti * Ck + j] != kNegInf) {
+      x = wave_sum(fmaf(a.dKp[tj + lane], a.tk[tj + lane], a.dVp[tj + lane] * a.tv[tj + lane]));
+      if (tilted) x += a.P[ti * Ck + j] * (sdP[j] + a.vgk[ti * Ck + j]);
+    }
+    if (lane == 0) {
+      sS[j] = x;
+      a.sij[ti * Ck + j] = x;
+    }
+  }
+  __syncthreads();
+  if (tid < D) {
+    float acc = 0.f;
+    for (int j = 0; j < Ck; ++j)
+      if (a.logz[ti * Ck + j] != kNegInf) acc = fmaf(sdl[j] - sS[j], a.tk[(ti * Ck + j) * D + tid], acc);
+    a.dqbar1[ti * D + tid] = a.scale * acc;
+  }
+}
+
+// 64 keys per workgroup (four threads per key, 16 dimensions each): over the query
+// clusters in order, dL/dw_im = dK'_ij . k_m + dV'_ij . v_m (+ P_ij Q_im, tilted),
+// da_im = w_im (dL/dw_im - S_ij + dL/dlog Z_ij), and
+//   dk_m += sum_i (w_im dK'_ij + s da_im qbar_i),  dv_m += sum_i w_im dV'_ij
+// on top of the tilted dipole's terms (bw_keys_a) or, untilted, plus the covariance terms
+// (sum_i P_ij G_Dip_i)^T (v_m - mean v) / n_j and (sum_i P_ij G_Dip_i)(k_m - mean k) / n_j.
+// Then the tile's s sum_m w_im dL/dw_im k_m for every i (one partial per tile).
+template <typename T>
+__global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
+  constexpr int D = kBwD, KT = kBwKeyTile, DQ = D / 4, RP = D + 1;
+  __shared__ float sQb[kMaxClusters * D];
+  __shared__ float sWd[kMaxClusters * (KT + 1)];
+  __shared__ float sKr[KT * RP];
+  __shared__ float sVr[KT * RP];
+  const int bh = blockIdx.y, tid = threadIdx.x, kk = tid >> 2, d0 = (tid & 3) * DQ;
+  const int N = a.N, Cq = a.Cq, Ck = a.Ck;
+  const float s = a.scale;
+  for (int e = tid; e < Cq * D; e += 256) sQb[e] = a.qbar[static_cast<size_t>(bh) * Cq * D + e];
+  const int pos = blockIdx.x * KT + kk;
+  const bool valid = pos < N;
+  const int key = valid ? a.perm_k[static_cast<size_t>(bh) * N + pos] : 0;
+  const int j = valid ? min(max(a.labels_k[static_cast<size_t>(bh) * N + key], 0), Ck - 1) : 0;
+  const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * N * D;
+  const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * N * D;
+  float kf[DQ], vf[DQ], dk[DQ], dv[DQ];
+  float* dkr = a.dk + (static_cast<size_t>(bh) * N + key) * D + d0;
+  float* dvr = a.dv + (static_cast<size_t>(bh) * N + key) * D + d0;
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) {
+    kf[e] = valid ? Elem<T>::load(K, static_cast<size_t>(key) * D + d0 + e) : 0.f;
+    vf[e] = valid ? Elem<T>::load(V, static_cast<size_t>(key) * D + d0 + e) : 0.f;
+    sKr[kk * RP + d0 + e] = kf[e];
+    sVr[kk * RP + d0 + e] = vf[e];
+    dk[e] = (a.dipole == 1 && valid) ? dkr[e] : 0.f;
+    dv[e] = (a.dipole == 1 && valid) ? dvr[e] : 0.f;
+  }
+  __syncthreads();
+  const float* Arow = a.A;
+  for (int i = 0; i < Cq; ++i) {
+    const size_t ti = static_cast<size_t>(bh) * Cq + i;
+    float x = 0.f;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) x = fmaf(sQb[i * D + d0 + e], kf[e], x);
+    x += dpp_f32<0xB1>(x);
+    x += dpp_f32<0x4E>(x);
+    const float av = s * x;
+    const size_t tij = ti * Ck + j;
+    const float lzij = a.logz[tij];
+    const float w = (valid && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
+    const float* kp = a.dKp + tij * D + d0;
+    const float* vp = a.dVp + tij * D + d0;
+    float kpv[DQ], vpv[DQ];
+#pragma unroll
+    for (int e = 0; e < DQ; e += 4) {
+      const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(kp + e);
+      const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(vp + e);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kpv[e + r] = k4[r];
+        vpv[e + r] = v4[r];
+      }
+    }
+    float y = 0.f;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) y = fmaf(kpv[e], kf[e], fmaf(vpv[e], vf[e], y));
+    y += dpp_f32<0xB1>(y);
+    y += dpp_f32<0x4E>(y);
+    if (a.dipole == 1 && valid) y += a.P[tij] * a.Q[ti * N + pos];
+    const float da = w * (y - a.sij[tij] + a.dlogz[tij]);
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) {
+      dk[e] = fmaf(w, kpv[e], fmaf(s * da, sQb[i * D + d0 + e], dk[e]));
+      dv[e] = fmaf(w, vpv[e], dv[e]);
+    }
+    if ((tid & 3) == 0) sWd[i * (KT + 1) + kk] = w * y;
+  }
+  (void)Arow;
+  if (a.dipole == 2 && valid) {
+    // covariance terms with the cluster's dL/dCov = sum_i P_ij G_Dip_i
+    const size_t tj = static_cast<size_t>(bh) * Ck + j;
+    const float* dc = a.dcov + tj * D * D;
+    const float* km = a.kmean + tj * D;
+    const float* vm = a.vmean + tj * D;
+    const int32_t* offk = a.offs_k + static_cast<size_t>(bh) * (Ck + 1);
+    const float inv_n = 1.f / static_cast<float>(max(1, offk[j + 1] - offk[j]));
+    for (int d = 0; d < D; ++d) {
+      const float kc = sKr[kk * RP + d] - km[d];  // k_m - mean k, dimension d
+      const float vc = sVr[kk * RP + d] - vm[d];  // v_m - mean v, dimension (value) d
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        dv[e] = fmaf(dc[static_cast<size_t>(d0 + e) * D + d] * inv_n, kc, dv[e]);  // row v = d0 + e
+        dk[e] = fmaf(dc[static_cast<size_t>(d) * D + d0 + e] * inv_n, vc, dk[e]);  // row v = d, col d0 + e
+      }
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) {
+      dkr[e] = dk[e];
+      dvr[e] = dv[e];
+    }
+  }
+  __syncthreads();
+  // s sum over the tile's keys of w dL/dw k, for every (i, d)
+  float* part = a.dqbar_part + (static_cast<size_t>(bh) * a.ntb + blockIdx.x) * Cq * D;
+  for (int e = tid; e < Cq * D; e += 256) {
+    const int i = e / D, d = e % D;
+    float acc = 0.f;
+    for (int q = 0; q < KT; ++q) acc = fmaf(sWd[i * (KT + 1) + q], sKr[q * RP + d], acc);
+    part[e] = s * acc;
+  }
+}
+
+// dL/dqbar_i = stage-2 part + s sum_j (dL/dlog Z_ij - S_ij) K_ij + the key tiles' partials
+// (in tile order), then dq_n += dL/dqbar_i / n_i for every member n of cluster i.
+__global__ void __launch_bounds__(256) bw_centroid_kernel(BwArgs a) {
+  constexpr int D = kBwD;
+  __shared__ float sRed[4][D];
+  __shared__ float sTot[D];
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, d = tid & 63, g = tid >> 6;
+  const int Cq = a.Cq, N = a.N;
+  const size_t ti = static_cast<size_t>(bh) * Cq + i;
+  float acc = 0.f;
+  for (int tb = g; tb < a.ntb; tb += 4) acc += a.dqbar_part[((static_cast<size_t>(bh) * a.ntb + tb) * Cq + i) * D + d];
+  sRed[g][d] = acc;
+  __syncthreads();
+  if (tid < D) sTot[tid] = a.dqbar2[ti * D + tid] + a.dqbar1[ti * D + tid] + ((sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid]));
+  __syncthreads();
+  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (Cq + 1);
+  const int o0 = offq[i], o1 = offq[i + 1];
+  if (o1 <= o0) return;
+  const float inv = 1.f / static_cast<float>(o1 - o0);
+  const int32_t* perm = a.perm_q + static_cast<size_t>(bh) * N;
+  float* dq = a.dq + static_cast<size_t>(bh) * N * D;
+  for (int e = tid; e < (o1 - o0) * D; e += 256) {
+    const int n = perm[o0 + e / D], dd = e % D;
+    dq[static_cast<size_t>(n) * D + dd] += sTot[dd] * inv;
+  }
+}
+
+template <typename T>
+static void launch_backward_t(const BwArgs& a, hipStream_t s) {
+  const dim3 gi(a.Cq, a.BH), gj(a.Ck, a.BH), gk((a.N + kBwKeyTile - 1) / kBwKeyTile, a.BH);
+  {
+    ProfScope ps_("bw_refine", s);
+    hipLaunchKernelGGL((bw_refine_kernel<T>), gi, dim3(256), 0, s, a);
+  }
+  {
+    ProfScope ps_("bw_prep_i", s);
+    hipLaunchKernelGGL(bw_prep_i_kernel, gi, dim3(256), 0, s, a);
+  }
+  if (a.dipole == 2) {
+    ProfScope ps_("bw_prep_j", s);
+    hipLaunchKernelGGL((bw_prep_j_kernel<T>), gj, dim3(256), 0, s, a);
+  }
+  if (a.dipole == 1) {
+    {
+      ProfScope ps_("bw_scores", s);
+      hipLaunchKernelGGL((bw_scores_kernel<T>), gk, dim3(256), 0, s, a);
+    }
+    ProfScope ps_("bw_keys_a", s);
+    hipLaunchKernelGGL((bw_keys_a_kernel<T>), dim3((a.N + 127) / 128, a.BH), dim3(256), 0, s, a);
+  }
+  {
+    ProfScope ps_("bw_dlogz", s);
+    hipLaunchKernelGGL(bw_dlogz_kernel, gi, dim3(256), 0, s, a);
+  }
+  {
+    ProfScope ps_("bw_keys_b", s);
+    hipLaunchKernelGGL((bw_keys_b_kernel<T>), gk, dim3(256), 0, s, a);
+  }
+  {
+    ProfScope ps_("bw_centroid", s);
+    hipLaunchKernelGGL(bw_centroid_kernel, gi, dim3(256), 0, s, a);
+  }
+}
+
+hipError_t launch_backward(const BwArgs& a, int dtype, hipStream_t s) {
+  if (dtype == 0) launch_backward_t<float>(a, s);
+  else launch_backward_t<bf16>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace muse

@@ -273,13 +273,10 @@ int out_is_bf16(const Shape& s, const muse_fwd_params* p) {
   return od == MUSE_BF16;
 }
 
-int run_muse(const void* q, const void* k, const void* v, void* out, const Shape& s,
-             const muse_fwd_params* p, hipStream_t stream, void* ws, bool one_stream = false) {
+// K-means arguments of one call: both tensors, their tables and buckets in the workspace.
+muse::KmArgs kmeans_args(const void* q, const void* k, const Shape& s, const Plan& P, void* ws) {
   using namespace muse;
-  const Plan P = make_plan(s, p);
-  const float scale = scale_of(s, p);
-  const int dipole = p ? p->dipole : MUSE_DIPOLE_TILTED;
-
+  const bool mf = s.dtype == MUSE_BF16;
   KmArgs km{};
   km.ntensors = 2;
   km.BH = s.BH;
@@ -293,23 +290,15 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   tq.x = q;
   tq.C = s.Cq;
   tq.cent = at<float>(ws, P.cent_q);
-  tq.chi = s.dtype == MUSE_BF16 ? at<uint16_t>(ws, P.chi_q) : nullptr;
-  tq.clo = s.dtype == MUSE_BF16 ? at<uint16_t>(ws, P.clo_q) : nullptr;
+  tq.chi = mf ? at<uint16_t>(ws, P.chi_q) : nullptr;
+  tq.clo = mf ? at<uint16_t>(ws, P.clo_q) : nullptr;
   tq.cn2 = at<float>(ws, P.cn2_q);
   tq.labels = at<int32_t>(ws, P.lab_q);
-  tq.trace = p ? p->labels_q_trace : nullptr;
-  tq.labels_in = p ? p->labels_q_in : nullptr;
   tq.tile_perm = at<uint16_t>(ws, P.tperm_q);
   tq.tile_cnt = at<int32_t>(ws, P.tcnt_q);
   tq.tile_start = at<int32_t>(ws, P.tst_q);
   tq.psum = at<float>(ws, P.psum_q);
-  tq.gcnt = s.dtype == MUSE_BF16 ? at<int32_t>(ws, P.gcnt_q) : tq.tile_cnt;
-  const bool mf = s.dtype == MUSE_BF16;
-  const bool retr = p != nullptr && p->topk_clusters > 0;
-  // the matrix-core stage 2 and retrieval need the query buckets
-  const bool want_qb = p != nullptr && (p->perm_q_out != nullptr || p->offs_q_out != nullptr);
-  tq.perm = (mf || retr || want_qb) ? at<int32_t>(ws, P.perm_q) : nullptr;
-  tq.offs = (mf || retr || want_qb) ? at<int32_t>(ws, P.offs_q) : nullptr;
+  tq.gcnt = mf ? at<int32_t>(ws, P.gcnt_q) : tq.tile_cnt;
   if (mf) {
     tq.chunks = at<int2>(ws, P.tiles);
     tq.nchunks = at<int32_t>(ws, P.ntiles);
@@ -319,28 +308,30 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   tk.x = k;
   tk.C = s.Ck;
   tk.cent = at<float>(ws, P.cent_k);
-  tk.chi = s.dtype == MUSE_BF16 ? at<uint16_t>(ws, P.chi_k) : nullptr;
-  tk.clo = s.dtype == MUSE_BF16 ? at<uint16_t>(ws, P.clo_k) : nullptr;
+  tk.chi = mf ? at<uint16_t>(ws, P.chi_k) : nullptr;
+  tk.clo = mf ? at<uint16_t>(ws, P.clo_k) : nullptr;
   tk.cn2 = at<float>(ws, P.cn2_k);
   tk.labels = at<int32_t>(ws, P.lab_k);
-  tk.trace = p ? p->labels_k_trace : nullptr;
-  tk.labels_in = p ? p->labels_k_in : nullptr;
   tk.tile_perm = at<uint16_t>(ws, P.tperm_k);
   tk.tile_cnt = at<int32_t>(ws, P.tcnt_k);
   tk.tile_start = at<int32_t>(ws, P.tst_k);
   tk.psum = at<float>(ws, P.psum_k);
-  tk.gcnt = s.dtype == MUSE_BF16 ? at<int32_t>(ws, P.gcnt_k) : tk.tile_cnt;
+  tk.gcnt = mf ? at<int32_t>(ws, P.gcnt_k) : tk.tile_cnt;
   tk.perm = at<int32_t>(ws, P.perm_k);
   tk.offs = at<int32_t>(ws, P.offs_k);
   tk.items = mf ? at<int4>(ws, P.items_k) : nullptr;
   tk.multi = mf ? at<int4>(ws, P.multi_k) : nullptr;
   tk.bmeta = mf ? at<int2>(ws, P.bmeta_k) : nullptr;
-  tk.cap = cap_members(s, p);
-  tk.klen = tk.cap > 0 ? at<int32_t>(ws, P.klen) : nullptr;
-  tk.kdrop = tk.cap > 0 ? at<uint8_t>(ws, P.kdrop) : nullptr;
-  hipError_t e = launch_kmeans(km, s.iters, s.dtype, stream);
-  if (e != hipSuccess) return hip_fail(e, "K-means launch");
+  return km;
+}
 
+// Stage-1 arguments of one call (tables in the workspace; the caller sets the options).
+muse::S1Args stage1_args(const void* k, const void* v, const Shape& s, const Plan& P, void* ws,
+                         const muse::KmArgs& km, float scale, int dipole) {
+  using namespace muse;
+  const bool mf = s.dtype == MUSE_BF16;
+  const KmTensor& tq = km.t[0];
+  const KmTensor& tk = km.t[1];
   S1Args a1{};
   a1.k = k;
   a1.v = v;
@@ -355,8 +346,6 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
   a1.nbS = s.nbS;
   a1.scale = scale;
   a1.dipole = dipole;
-  a1.hier = (p != nullptr && p->hierarchy) ? 1 : 0;
-  a1.one_stream = (one_stream || (p != nullptr && p->single_stream != 0)) ? 1 : 0;
   a1.qbar = tq.cent;
   a1.perm_k = tk.perm;
   a1.offs_k = tk.offs;
@@ -402,6 +391,38 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
     a1.t_vlo = at<uint16_t>(ws, P.t_vlo);
     a1.t_dip = at<uint16_t>(ws, P.t_dip);
   }
+  return a1;
+}
+
+int run_muse(const void* q, const void* k, const void* v, void* out, const Shape& s,
+             const muse_fwd_params* p, hipStream_t stream, void* ws, bool one_stream = false) {
+  using namespace muse;
+  const Plan P = make_plan(s, p);
+  const float scale = scale_of(s, p);
+  const int dipole = p ? p->dipole : MUSE_DIPOLE_TILTED;
+  const bool mf = s.dtype == MUSE_BF16;
+  const bool retr = p != nullptr && p->topk_clusters > 0;
+
+  KmArgs km = kmeans_args(q, k, s, P, ws);
+  KmTensor& tq = km.t[0];
+  KmTensor& tk = km.t[1];
+  tq.trace = p ? p->labels_q_trace : nullptr;
+  tq.labels_in = p ? p->labels_q_in : nullptr;
+  tk.trace = p ? p->labels_k_trace : nullptr;
+  tk.labels_in = p ? p->labels_k_in : nullptr;
+  // the matrix-core stage 2 and retrieval need the query buckets
+  const bool want_qb = p != nullptr && (p->perm_q_out != nullptr || p->offs_q_out != nullptr);
+  tq.perm = (mf || retr || want_qb) ? at<int32_t>(ws, P.perm_q) : nullptr;
+  tq.offs = (mf || retr || want_qb) ? at<int32_t>(ws, P.offs_q) : nullptr;
+  tk.cap = cap_members(s, p);
+  tk.klen = tk.cap > 0 ? at<int32_t>(ws, P.klen) : nullptr;
+  tk.kdrop = tk.cap > 0 ? at<uint8_t>(ws, P.kdrop) : nullptr;
+  hipError_t e = launch_kmeans(km, s.iters, s.dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "K-means launch");
+
+  S1Args a1 = stage1_args(k, v, s, P, ws, km, scale, dipole);
+  a1.hier = (p != nullptr && p->hierarchy) ? 1 : 0;
+  a1.one_stream = (one_stream || (p != nullptr && p->single_stream != 0)) ? 1 : 0;
   RetrArgs ra{};
   if (retr) {
     ra.q = q;
@@ -532,6 +553,152 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
     e = hipMemcpyAsync(p->centroids_k_out, tk.cent, sizeof(float) * s.BH * s.Ck * s.D, hipMemcpyDeviceToDevice, stream);
     if (e != hipSuccess) return hip_fail(e, "centroid copy");
   }
+  return MUSE_OK;
+}
+
+// ---------------------------------------------------------------- backward pass
+
+int validate_bwd(Shape& s, const muse_fwd_params* p) {
+  const int r = validate_muse(s, p);
+  if (r != MUSE_OK) return r;
+  if (s.causal) return fail(MUSE_ERR_UNSUPPORTED, "the backward pass is implemented for acausal calls");
+  if (s.D != muse::kBwD) return fail(MUSE_ERR_UNSUPPORTED, "the backward pass is implemented for D=%d", muse::kBwD);
+  if (p != nullptr) {
+    if (p->topk_clusters > 0 || p->hierarchy || p->cap_ratio > 0.0)
+      return fail(MUSE_ERR_UNSUPPORTED, "the backward pass takes no retrieval, hierarchy or cluster size cap");
+    if (p->labels_q_in != nullptr || p->labels_k_in != nullptr || p->labels_q_trace != nullptr ||
+        p->labels_k_trace != nullptr || p->centroids_q_out != nullptr || p->centroids_k_out != nullptr ||
+        p->lse_out != nullptr || p->retrieval_trace != nullptr || p->perm_q_out != nullptr ||
+        p->offs_q_out != nullptr || p->perm_k_out != nullptr || p->offs_k_out != nullptr)
+      return fail(MUSE_ERR_INVALID_ARG, "the backward pass takes the labels as arguments and returns no forward outputs");
+  }
+  return MUSE_OK;
+}
+
+struct BwPlan {
+  Plan f;  // the forward's regions (clustering with the fixed labels and the stage-1 tables)
+  size_t g_logz, g_k, g_v, g_dip, P, lz, gd, dKp, dVp, vgk, dP, dlogz, sij, A, Q, WQ, dcov, kmean, vmean;
+  size_t dqbar1, dqbar2, dqbar_part;
+  int ntb;
+  size_t total;
+};
+
+BwPlan make_bwd_plan(const Shape& s, const muse_fwd_params* p) {
+  BwPlan B{};
+  B.f = make_plan(s, p);
+  Layout L;
+  L.bytes = B.f.total;
+  const size_t BH = s.BH, N = s.N, D = s.D, Cq = s.Cq, Ck = s.Ck, f = sizeof(float);
+  const int dipole = p ? p->dipole : MUSE_DIPOLE_TILTED;
+  B.ntb = (s.N + muse::kBwKeyTile - 1) / muse::kBwKeyTile;
+  B.g_logz = L.take(BH * Cq * Ck * f);
+  B.g_k = L.take(BH * Cq * Ck * D * f);
+  B.g_v = L.take(BH * Cq * Ck * D * f);
+  B.g_dip = L.take(BH * Cq * D * D * f);
+  B.P = L.take(BH * Cq * Ck * f);
+  B.lz = L.take(BH * Cq * f);
+  B.dKp = L.take(BH * Cq * Ck * D * f);
+  B.dVp = L.take(BH * Cq * Ck * D * f);
+  B.dP = L.take(BH * Cq * Ck * f);
+  B.dlogz = L.take(BH * Cq * Ck * f);
+  B.sij = L.take(BH * Cq * Ck * f);
+  if (dipole == MUSE_DIPOLE_TILTED) {
+    B.gd = L.take(BH * Cq * 4 * D * D * sizeof(uint16_t));
+    B.vgk = L.take(BH * Cq * Ck * f);
+    B.A = L.take(BH * Cq * N * f);
+    B.Q = L.take(BH * Cq * N * f);
+    B.WQ = L.take(BH * Cq * N * f);
+  }
+  if (dipole == MUSE_DIPOLE_UNTILTED) {
+    B.dcov = L.take(BH * Ck * D * D * f);
+    B.kmean = L.take(BH * Ck * D * f);
+    B.vmean = L.take(BH * Ck * D * f);
+  }
+  B.dqbar1 = L.take(BH * Cq * D * f);
+  B.dqbar2 = L.take(BH * Cq * D * f);
+  B.dqbar_part = L.take(BH * static_cast<size_t>(B.ntb) * Cq * D * f);
+  B.total = L.bytes;
+  return B;
+}
+
+int run_muse_bwd(const void* q, const void* k, const void* v, const void* dout, const int32_t* labels_q,
+                 const int32_t* labels_k, float* dq, float* dk, float* dv, const Shape& s,
+                 const muse_fwd_params* p, hipStream_t stream, void* ws) {
+  using namespace muse;
+  const BwPlan B = make_bwd_plan(s, p);
+  const Plan& P = B.f;
+  const float scale = scale_of(s, p);
+  const int dipole = p ? p->dipole : MUSE_DIPOLE_TILTED;
+  // the clustering with the labels held fixed: member-mean centroids and the buckets
+  KmArgs km = kmeans_args(q, k, s, P, ws);
+  km.t[0].labels_in = labels_q;
+  km.t[1].labels_in = labels_k;
+  km.t[0].perm = at<int32_t>(ws, P.perm_q);
+  km.t[0].offs = at<int32_t>(ws, P.offs_q);
+  hipError_t e = launch_kmeans(km, 1, s.dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "K-means launch");
+  // the forward's stage-1 summaries as fp32 tables
+  S1Args a1 = stage1_args(k, v, s, P, ws, km, scale, dipole);
+  a1.one_stream = 1;
+  a1.tables_f32 = 1;
+  a1.t_khi = a1.t_klo = a1.t_vhi = a1.t_vlo = a1.t_dip = nullptr;
+  e = launch_stage1(a1, s.dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
+  BwArgs b{};
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.dout = dout;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.BH = s.BH;
+  b.N = s.N;
+  b.D = s.D;
+  b.Cq = s.Cq;
+  b.Ck = s.Ck;
+  b.scale = scale;
+  b.dipole = dipole;
+  b.labels_k = labels_k;
+  b.qbar = km.t[0].cent;
+  b.perm_q = km.t[0].perm;
+  b.offs_q = km.t[0].offs;
+  b.perm_k = km.t[1].perm;
+  b.offs_k = km.t[1].offs;
+  b.logz = a1.s_logz;
+  b.tk = a1.s_k;
+  b.tv = a1.s_v;
+  b.dip = a1.s_dip;
+  b.cov = a1.cov_k;
+  b.g_logz = at<float>(ws, B.g_logz);
+  b.g_k = at<float>(ws, B.g_k);
+  b.g_v = at<float>(ws, B.g_v);
+  b.g_dip = at<float>(ws, B.g_dip);
+  b.P = at<float>(ws, B.P);
+  b.lz = at<float>(ws, B.lz);
+  b.dKp = at<float>(ws, B.dKp);
+  b.dVp = at<float>(ws, B.dVp);
+  b.dP = at<float>(ws, B.dP);
+  b.dlogz = at<float>(ws, B.dlogz);
+  b.sij = at<float>(ws, B.sij);
+  if (dipole == MUSE_DIPOLE_TILTED) {
+    b.gd = at<uint16_t>(ws, B.gd);
+    b.vgk = at<float>(ws, B.vgk);
+    b.A = at<float>(ws, B.A);
+    b.Q = at<float>(ws, B.Q);
+    b.WQ = at<float>(ws, B.WQ);
+  }
+  if (dipole == MUSE_DIPOLE_UNTILTED) {
+    b.dcov = at<float>(ws, B.dcov);
+    b.kmean = at<float>(ws, B.kmean);
+    b.vmean = at<float>(ws, B.vmean);
+  }
+  b.dqbar1 = at<float>(ws, B.dqbar1);
+  b.dqbar2 = at<float>(ws, B.dqbar2);
+  b.dqbar_part = at<float>(ws, B.dqbar_part);
+  b.ntb = B.ntb;
+  e = launch_backward(b, s.dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
   return MUSE_OK;
 }
 
@@ -758,6 +925,56 @@ int muse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out
   if (r != MUSE_OK) return r;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   r = run_muse(q, k, v, out, s, p, stream, ws, /*one_stream=*/true);
+  if (r == MUSE_OK && getenv("MUSE_DEBUG_SYNC") != nullptr) {
+    const hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) r = hip_fail(e, "debug sync");
+  }
+  return r;
+}
+
+size_t muse_attn_bwd_workspace_bytes(int B, int H, int N, int D, int Cq, int Ck, int causal, int block,
+                                     int dtype, const muse_fwd_params* p) {
+  Shape s{B, H, N, D, Cq, Ck, 1, causal, block, dtype};
+  if (validate_bwd(s, p) != MUSE_OK) return 0;
+  return make_bwd_plan(s, p).total;
+}
+
+int muse_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const int32_t* labels_q,
+                  const int32_t* labels_k, float* dq, float* dk, float* dv, int B, int H, int N, int D, int Cq,
+                  int Ck, int causal, int block, int dtype, void* hip_stream, const muse_fwd_params* p) {
+  g_last_error.clear();
+  if (q == nullptr || k == nullptr || v == nullptr || dout == nullptr)
+    return fail(MUSE_ERR_INVALID_ARG, "q, k, v and dout must be non-null device pointers");
+  if (labels_q == nullptr || labels_k == nullptr)
+    return fail(MUSE_ERR_INVALID_ARG, "labels_q and labels_k (the forward's final labels) are required");
+  if (dq == nullptr || dk == nullptr || dv == nullptr)
+    return fail(MUSE_ERR_INVALID_ARG, "dq, dk and dv must be non-null device pointers");
+  Shape s{B, H, N, D, Cq, Ck, 1, causal, block, dtype};
+  int r = validate_bwd(s, p);
+  if (r != MUSE_OK) return r;
+  const void* ins[] = {q, k, v, dout, labels_q, labels_k};
+  const void* outs[] = {dq, dk, dv};
+  for (const void* o : outs)
+    for (const void* in : ins)
+      if (o == in) return fail(MUSE_ERR_INVALID_ARG, "dq, dk and dv must not alias an input");
+  if (dq == dk || dq == dv || dk == dv) return fail(MUSE_ERR_INVALID_ARG, "dq, dk and dv must be distinct");
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const size_t need = make_bwd_plan(s, p).total;
+  void* ws = p ? p->workspace : nullptr;
+  bool owned = false;
+  if (ws != nullptr) {
+    if (p->workspace_bytes < need)
+      return fail(MUSE_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", p->workspace_bytes, need);
+  } else {
+    const hipError_t e = hipMallocAsync(&ws, need, stream);
+    if (e != hipSuccess) return fail(MUSE_ERR_NO_MEMORY, "hipMallocAsync(%zu): %s", need, hipGetErrorString(e));
+    owned = true;
+  }
+  r = run_muse_bwd(q, k, v, dout, labels_q, labels_k, dq, dk, dv, s, p, stream, ws);
+  if (owned) {
+    const hipError_t e = hipFreeAsync(ws, stream);
+    if (e != hipSuccess && r == MUSE_OK) r = hip_fail(e, "hipFreeAsync");
+  }
   if (r == MUSE_OK && getenv("MUSE_DEBUG_SYNC") != nullptr) {
     const hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) r = hip_fail(e, "debug sync");

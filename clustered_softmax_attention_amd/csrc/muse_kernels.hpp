@@ -169,6 +169,9 @@ struct S1Args {
   // per key (input position) that is 1 when the key is left out of the summaries
   const int32_t* klen;         // [BH, nb*Ck]
   const uint8_t* kdrop;        // [BH, N]
+  // 1: fp32 tables only (s_logz, s_k, s_v, s_dip; no bf16 packing), on the general path
+  // for either dtype (used by the backward pass)
+  int tables_f32;
 };
 
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);
@@ -229,5 +232,61 @@ struct ExactArgs {
 };
 
 hipError_t launch_exact(const ExactArgs& a, int dtype, hipStream_t s);
+
+// ------------------------------------------------------------------ backward (acausal)
+
+constexpr int kBwD = 64;       // head dimension of the backward kernels
+constexpr int kBwKeyTile = 64; // keys per tile of the per-key backward pass
+
+struct BwArgs {
+  const void* q;               // [BH, N, D] inputs of the forward (dtype of the call)
+  const void* k;
+  const void* v;
+  const void* dout;            // [BH, N, D] upstream gradient (dtype of the call)
+  float* dq;                   // [BH, N, D] outputs
+  float* dk;
+  float* dv;
+  int BH, N, D, Cq, Ck;
+  float scale;
+  int dipole;                  // 0 none, 1 tilted, 2 untilted
+  const int32_t* labels_k;     // [BH, N] fixed key labels (clamped to [0, Ck) on read)
+  const float* qbar;           // [BH, Cq, D] query centroids (member means)
+  const int32_t* perm_q;       // [BH, N] / [BH, Cq + 1] query buckets
+  const int32_t* offs_q;
+  const int32_t* perm_k;       // [BH, N] / [BH, Ck + 1] key buckets
+  const int32_t* offs_k;
+  // forward summaries (fp32, the single acausal entry)
+  const float* logz;           // [BH, Cq, Ck]
+  const float* tk;             // [BH, Cq, Ck, D] K_ij
+  const float* tv;             // [BH, Cq, Ck, D] V_ij
+  const float* dip;            // [BH, Cq, D(v), D(k)] D_i
+  const float* cov;            // [BH, Ck, D(v), D(k)] untilted: Cov_j
+  // gradients with respect to the summaries and intermediates
+  float* g_logz;               // [BH, Cq, Ck]
+  float* g_k;                  // [BH, Cq, Ck, D]
+  float* g_v;                  // [BH, Cq, Ck, D]
+  float* g_dip;                // [BH, Cq, D(v), D(k)]
+  float* P;                    // [BH, Cq, Ck] softmax_j log Z_ij
+  float* lz;                   // [BH, Cq] log sum_j Z_ij
+  uint16_t* gd;                // [BH, Cq, 4, D, D] bf16: hi, lo of G_Dip (row v), hi, lo of its transpose
+  float* dKp;                  // [BH, Cq, Ck, D] dL/dK_ij after the dipole's dependence on K_ij
+  float* dVp;                  // [BH, Cq, Ck, D]
+  float* vgk;                  // [BH, Cq, Ck] V_ij^T G_Dip_i K_ij
+  float* dP;                   // [BH, Cq, Ck] dL/dP_ij
+  float* dlogz;                // [BH, Cq, Ck] total dL/dlog Z_ij
+  float* sij;                  // [BH, Cq, Ck] sum over the cluster's keys of w dL/dw
+  float* A;                    // [BH, Cq, N] s qbar_i . k at key positions in bucket order
+  float* Q;                    // [BH, Cq, N] v^T G_Dip_i k
+  float* WQ;                   // [BH, Cq, N] w Q
+  float* dcov;                 // [BH, Ck, D, D] untilted: sum_i P_ij G_Dip_i
+  float* kmean;                // [BH, Ck, D] untilted: cluster means
+  float* vmean;
+  float* dqbar1;               // [BH, Cq, D] stage-1 part of dL/dqbar through K_ij
+  float* dqbar2;               // [BH, Cq, D] stage-2 part
+  float* dqbar_part;           // [BH, ntb, Cq, D] per key tile: s sum_m w dL/dw k_m
+  int ntb;                     // key tiles of kBwKeyTile positions
+};
+
+hipError_t launch_backward(const BwArgs& a, int dtype, hipStream_t s);
 
 }  // namespace muse

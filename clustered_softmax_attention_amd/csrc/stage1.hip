@@ -960,7 +960,7 @@ template <typename T, int D>
 static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   constexpr int kS1Keys = S1Keys<D>::value;
   const bool mf = sizeof(T) == 2;  // bf16 inputs: matrix-core kernels
-  if (mf && a.retr == nullptr && !a.hier) {
+  if (mf && a.retr == nullptr && !a.hier && !a.tables_f32) {
     // acausal: one table entry per (head, i), finalised in a single pass; causal without
     // retrieval: one scan over the blocks writes every entry (the hierarchical squares
     // take the general path below: per entry folds of the merged atoms and moments). The atoms (with their

@@ -1328,9 +1328,9 @@ static void launch_t(const S1Args& a, int which, hipStream_t s) {
       ProfScope ps_("s1_atoms_mfma", s);
       hipLaunchKernelGGL((s1_atoms_mfma_kernel<D>), dim3((waves + 3) / 4, a.BH), dim3(256), lds, s, a, ipw);
     }
-    // the acausal finalise folds the items itself; the causal scan and retrieval read
-    // merged atoms
-    if (a.causal || a.retr != nullptr) {
+    // the acausal finalise folds the items itself; the causal scan, retrieval and the
+    // fp32-table path read merged atoms
+    if (a.causal || a.retr != nullptr || a.tables_f32) {
       ProfScope ps_("s1_atoms_merge", s);
       const dim3 gm(std::min(kMergeGrid, atom_max_multi(a.N)), a.BH);
       if (a.Cq * (D / 2) <= 512) hipLaunchKernelGGL((s1_atoms_merge_kernel<D, 512>), gm, dim3(512), 0, s, a);

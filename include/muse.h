@@ -214,6 +214,45 @@ int muse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out
                           int kmeans_iters, int causal, int block,
                           int dtype, void* hip_stream, const muse_fwd_params* p);
 
+/*
+ * Backward pass of the acausal MuSe forward: the vector-Jacobian products dq, dk, dv of
+ * muse_attn_fwd_ex's output o(q, k, v) for an upstream gradient dout = dLoss/do. The
+ * reviews note that the method's backward pass uses the same approximations as its
+ * forward and that its gradient error was never measured (pith.science review, "Reading
+ * between the lines"; Referee Report, Section 7.2 / Q4). Differentiated: the forward with
+ * the K-means labels held fixed (the clustering is piecewise constant in q and k, so it
+ * has no gradient). The query centroids are the member means of labels_q and pass their
+ * gradient to every member; stage 1 (log Z_ij, the tilted means K_ij and V_ij, P_ij and
+ * the dipole D_i, tilted or untilted as p->dipole says) and stage 2 (the refinement) are
+ * differentiated exactly; the no-dipole mode drops D_i from both.
+ *   q, k, v, dout   device [B,H,N,D] in dtype (MUSE_F32 or MUSE_BF16), as in the forward
+ *   labels_q/_k     device int32 [B,H,N]: the forward call's final labels (the last row
+ *                   of labels_*_trace, or the labels_*_in it was given); values outside
+ *                   [0, C) are clamped like labels_*_in
+ *   dq, dk, dv      device float32 [B,H,N,D], written (not accumulated); distinct from
+ *                   each other and from every input
+ *   p               scale and dipole as in the forward call (NULL: defaults); workspace
+ *                   and workspace_bytes as in muse_attn_fwd_ex, sized by
+ *                   muse_attn_bwd_workspace_bytes. Every other field keeps its default
+ *                   (MUSE_ERR_INVALID_ARG for the forward's output pointers).
+ * Implemented for causal = 0 and D = 64; causal calls, other head sizes, retrieval, the
+ * hierarchy and the cluster size cap return MUSE_ERR_UNSUPPORTED before any launch. All
+ * arithmetic in fp32 (bf16 inputs are exact in it); results are deterministic (fixed
+ * summation orders, no floating-point atomics). Work is queued on hip_stream.
+ */
+int muse_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                  const int32_t* labels_q, const int32_t* labels_k,
+                  float* dq, float* dk, float* dv,
+                  int B, int H, int N, int D, int Cq, int Ck,
+                  int causal, int block, int dtype, void* hip_stream,
+                  const muse_fwd_params* p);
+
+/* Device scratch bytes muse_attn_bwd needs for this shape (0 on invalid or unsupported
+ * arguments, with muse_last_error() set). */
+size_t muse_attn_bwd_workspace_bytes(int B, int H, int N, int D, int Cq, int Ck,
+                                     int causal, int block, int dtype,
+                                     const muse_fwd_params* p);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* muse_last_error(void);
 

@@ -226,3 +226,40 @@ def test_cluster_cap_arguments(lib):
         p.cap_ratio = bad
         assert lib.muse_attn_fwd_ex(*causal_args, ctypes.byref(p)) == -1
         assert "cap_ratio" in lib.muse_last_error().decode()
+
+
+def test_backward_entry_rejects_before_launch(lib):
+    # muse_attn_bwd: host-side checks only (no device call is reached)
+    from clustered_softmax_attention_amd.binding import FwdParams
+    vp = ctypes.c_void_p
+    p = FwdParams()
+    lib.muse_fwd_params_init(ctypes.byref(p))
+    ins = (vp(1), vp(2), vp(3), vp(4), vp(5), vp(6))
+    outs = (vp(7), vp(8), vp(9))
+
+    def call(B=1, H=1, N=1024, D=64, Cq=8, Ck=32, causal=0, block=0, dtype=1, ins=ins, outs=outs, pp=None):
+        return lib.muse_attn_bwd(*ins, *outs, B, H, N, D, Cq, Ck, causal, block, dtype, None,
+                                 None if pp is None else ctypes.byref(pp))
+
+    assert lib.muse_attn_bwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, None) > 0
+    assert call(causal=1, block=256) == -2 and "acausal" in lib.muse_last_error().decode()
+    assert lib.muse_attn_bwd_workspace_bytes(1, 1, 1024, 64, 8, 32, 1, 256, 1, None) == 0
+    assert call(D=128) == -2
+    assert call(ins=ins[:4] + (None, vp(6))) == -1  # labels are required
+    assert call(outs=(vp(7), vp(7), vp(9))) == -1   # distinct outputs
+    assert call(outs=(vp(1), vp(8), vp(9))) == -1   # no output aliases an input
+    p.cap_ratio = 1.5
+    assert call(pp=p) == -2
+    p.cap_ratio = 0.0
+    p.lse_out = 0x1000                              # no forward outputs
+    assert call(pp=p) == -1
+    p.lse_out = None
+    p.workspace, p.workspace_bytes = 0x1000, 16
+    assert call(pp=p) == -5                          # workspace too small
+    # the untilted mode needs the covariance regions, the tilted one the per-key tables
+    p.workspace, p.workspace_bytes = None, 0
+    p.dipole = 0
+    none = lib.muse_attn_bwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, ctypes.byref(p))
+    p.dipole = 1
+    tilted = lib.muse_attn_bwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, ctypes.byref(p))
+    assert tilted >= none + 3 * 32 * 32 * 8192 * 4
