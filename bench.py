@@ -11,7 +11,9 @@ on the same shape (speedup), the relative squared error of MuSe against it, per-
 average durations measured with HIP events on the stream the kernels run on, the
 untilted-dipole run and the paper's speed setting (key clusters capped at 1.5 N / Ck
 members, one Lloyd iteration) of a workload without retrieval, the hierarchical-decomposition
-run of a causal one without retrieval, `measured_peaks` (a device copy and a bf16
+run of a causal one without retrieval, the backward pass of an acausal one (`backward`:
+dq, dk, dv for an upstream gradient with the forward's labels fixed), `measured_peaks` (a
+device copy and a bf16
 GEMM on this GPU, beside the published peaks the roofline uses) and, with the default
 workload, `secondary`: the same figures for the 64k causal configuration.
 """
@@ -550,6 +552,34 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
             # the hierarchical block decomposition (one two-stage approximation per square
             # below the diagonal, log-sum-exp merged)
             variant("hierarchy", cfg.iters, lambda n: True, hierarchy=True)
+    if not cfg.causal and cfg.D == 64:
+        # the backward pass (dq, dk, dv for an upstream gradient, labels of one forward call
+        # held fixed), timed like the forward step
+        _, ex_b = binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, return_trace=True)
+        lq = ex_b["labels_q_trace"][-1].contiguous()
+        lk = ex_b["labels_k_trace"][-1].contiguous()
+        del ex_b
+        gen = torch.Generator(device="cuda").manual_seed(11)
+        dO = torch.randn(Q.shape, generator=gen, device="cuda", dtype=torch.float32).to(Q.dtype)
+        ws_b = torch.empty(binding.bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, False, 0,
+                                                       1 if cfg.dtype == "bf16" else 0),
+                           dtype=torch.uint8, device="cuda")
+
+        def bwd_step():
+            binding.attn_bwd(Q, K, V, dO, lq, lk, cfg.Cq, cfg.Ck, workspace=ws_b)
+
+        ms_b, _ = timed(bwd_step, steps, warmup)
+        binding.prof_reset()
+        binding.prof_enable(True)
+        bwd_step()
+        torch.cuda.synchronize()
+        prof_b = binding.prof_collect()
+        binding.prof_enable(False)
+        extra["backward"] = {
+            "ms_per_step": ms_b, "value": cfg.B * cfg.N / (ms_b / 1e3), "unit": "tokens/s",
+            "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in sorted(prof_b.items(), key=lambda kv: -kv[1][0])}}
+        print(f"# backward: {ms_b:.3f} ms/step, {extra['backward']['kernels_us']}", file=sys.stderr, flush=True)
+        del ws_b
     if ctx is not None:
         extra["retrieved_keys"] = ctx
     return {"cfg": cfg, "ms": ms, "wall": wall, "value": value, "kernels": kernels, "roofline": roofline,

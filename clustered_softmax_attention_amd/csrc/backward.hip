@@ -39,34 +39,36 @@ constexpr int kBwQT = 16;   // queries per tile of the stage-2 backward
 constexpr int kBwGST = kBwD + 8;  // LDS row stride (bf16) of the staged G_Dip tiles
 
 // dL/dlog Z, dL/dK, dL/dV, dL/dD of one query cluster and the residual part of dq.
-// LDS: K_i. and V_i. rows (fp32, padded), D_i, the tile's residuals and upstream
-// gradients, and the tile's weights p and dl = dL/dlogit.
+// LDS: K_i. and V_i. rows and D_i (fp32, rows padded to 68 floats: 16-byte reads by 16
+// lanes hit distinct banks), the tile's residuals and upstream gradients, and the tile's
+// weights p and dl = dL/dlogit; every product reads its operands 4 at a time.
 template <typename T>
 __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
-  constexpr int D = kBwD, DP = D + 1, CP = kMaxClusters + 1, QT = kBwQT;
-  __shared__ float sK[kMaxClusters * DP];
-  __shared__ float sV[kMaxClusters * DP];
-  __shared__ float sDip[D * DP];
-  __shared__ float sQt[QT * DP];
-  __shared__ float sG[QT * DP];
-  __shared__ float sL[QT * CP];
-  __shared__ float sDl[QT * CP];
+  constexpr int D = kBwD, DP = D + 4, CP = kMaxClusters + 4, QT = kBwQT;
+  __shared__ __align__(16) float sK[kMaxClusters * DP];
+  __shared__ __align__(16) float sV[kMaxClusters * DP];
+  __shared__ __align__(16) float sDip[D * DP];
+  __shared__ __align__(16) float sQt[QT * DP];
+  __shared__ __align__(16) float sG[QT * DP];
+  __shared__ __align__(16) float sL[QT * CP];
+  __shared__ __align__(16) float sDl[QT * CP];
   __shared__ float sLz[kMaxClusters];
   __shared__ float sQbar[D];
   __shared__ int sRow[QT];
-  __shared__ float sRed[4][D];
+  __shared__ __align__(16) float sRed[QT][D];
   const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Cq = a.Cq, Ck = a.Ck, N = a.N;
+  const int Cq = a.Cq, Ck = a.Ck, N = a.N, Ck4 = (Ck + 3) & ~3;
   const float s = a.scale;
   const bool dip = a.dipole != 0;
   const size_t ti = static_cast<size_t>(bh) * Cq + i;
-  for (int e = tid; e < Ck * D; e += 256) {
+  // tables; rows Ck .. Ck4 - 1 of K and columns Ck .. Ck4 - 1 of dl stay zero
+  for (int e = tid; e < Ck4 * D; e += 256) {
     const int j = e / D, d = e % D;
-    sK[j * DP + d] = a.tk[ti * Ck * D + e];
-    sV[j * DP + d] = a.tv[ti * Ck * D + e];
+    sK[j * DP + d] = j < Ck ? a.tk[ti * Ck * D + e] : 0.f;
+    sV[j * DP + d] = j < Ck ? a.tv[ti * Ck * D + e] : 0.f;
   }
-  if (dip)
-    for (int e = tid; e < D * D; e += 256) sDip[(e / D) * DP + e % D] = a.dip[ti * D * D + e];
+  for (int e = tid; e < D * D; e += 256) sDip[(e / D) * DP + e % D] = dip ? a.dip[ti * D * D + e] : 0.f;
+  for (int e = tid; e < QT * CP; e += 256) sDl[e] = 0.f;
   for (int j = tid; j < Ck; j += 256) sLz[j] = a.logz[ti * Ck + j];
   if (tid < D) sQbar[tid] = a.qbar[ti * D + tid];
   const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (Cq + 1);
@@ -77,33 +79,47 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
   float* dq = a.dq + static_cast<size_t>(bh) * N * D;
   // summary-gradient accumulators: dL/dK, dL/dV of cluster aj, dims ad0 .. ad0 + 31
   const int aj = tid >> 1, ad0 = (tid & 1) * 32;
-  float gk[32], gv[32];
+  f32x4_t gk[8], gv[8];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) gk[r] = gv[r] = 0.f;
+  for (int r = 0; r < 8; ++r) gk[r] = gv[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // dL/dD_i: row pv (value index), columns pd0 .. pd0 + 15
   const int pv = tid >> 2, pd0 = (tid & 3) * 16;
-  float gdp[16];
+  f32x4_t gdp[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) gdp[r] = 0.f;
-  float glz = 0.f;                         // dL/dlog Z_ij for j = tid
-  const int ed = tid & 63, eg = tid >> 6;  // dq rows: dimension ed of queries 4 eg .. 4 eg + 3
-  float qbs = 0.f;                         // - sum of this thread's dq values
+  for (int r = 0; r < 4; ++r) gdp[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float glz = 0.f;                                  // dL/dlog Z_ij for j = tid
+  const int eq = tid >> 4, ed0 = (tid & 15) * 4;    // dq: query eq of the tile, dims ed0 .. ed0 + 3
+  f32x4_t qbs = {0.f, 0.f, 0.f, 0.f};               // - sum of this thread's dq values
+  // this thread's elements of a query tile: rows wave + 4 r (r < 4), dimension lane; the
+  // next tile's rows travel in registers while the current tile is processed
+  constexpr int RPT = QT * D / 256;
+  int pn[RPT];
+  float pq[RPT], pg[RPT];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int qq = wave + 4 * r;
+      pn[r] = t0 + qq < o1 ? perm[t0 + qq] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      pq[r] = pn[r] >= 0 ? Elem<T>::load(Q, static_cast<size_t>(pn[r]) * D + lane) : 0.f;
+      pg[r] = pn[r] >= 0 ? Elem<T>::load(G, static_cast<size_t>(pn[r]) * D + lane) : 0.f;
+    }
+  };
+  if (o0 < o1) fetch(o0);
   __syncthreads();
   for (int t0 = o0; t0 < o1; t0 += QT) {
     const int nq = min(QT, o1 - t0);
-    for (int e = tid; e < QT * D; e += 256) {
-      const int qq = e / D, d = e % D;
-      float qt = 0.f, g = 0.f;
-      if (qq < nq) {
-        const int n = perm[t0 + qq];
-        qt = Elem<T>::load(Q, static_cast<size_t>(n) * D + d) - sQbar[d];
-        g = Elem<T>::load(G, static_cast<size_t>(n) * D + d);
-        if (d == 0) sRow[qq] = n;
-      }
-      sQt[qq * DP + d] = qt;
-      sG[qq * DP + d] = g;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int qq = wave + 4 * r;
+      sQt[qq * DP + lane] = pn[r] >= 0 ? pq[r] - sQbar[lane] : 0.f;
+      sG[qq * DP + lane] = pg[r];
+      if (lane == 0) sRow[qq] = pn[r];
     }
     __syncthreads();
+    if (t0 + QT < o1) fetch(t0 + QT);
     {
       // logits and dp_nj = g_n . V_ij: cluster j, queries q0 .. q0 + 7
       const int j = tid & 127, q0 = (tid >> 7) * 8;
@@ -111,12 +127,18 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
         float l[8], dp[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) l[r] = dp[r] = 0.f;
-        for (int d = 0; d < D; ++d) {
-          const float kj = sK[j * DP + d], vj = sV[j * DP + d];
+        for (int d = 0; d < D; d += 4) {
+          const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(&sK[j * DP + d]);
+          const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(&sV[j * DP + d]);
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
-            l[r] = fmaf(sQt[(q0 + r) * DP + d], kj, l[r]);
-            dp[r] = fmaf(sG[(q0 + r) * DP + d], vj, dp[r]);
+            const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(&sQt[(q0 + r) * DP + d]);
+            const f32x4_t g4 = *reinterpret_cast<const f32x4_t*>(&sG[(q0 + r) * DP + d]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              l[r] = fmaf(q4[c], k4[c], l[r]);
+              dp[r] = fmaf(g4[c], v4[c], dp[r]);
+            }
           }
         }
         const float lz = sLz[j];
@@ -168,9 +190,14 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
       for (int qq = 0; qq < nq; ++qq) {
         const float p = sL[qq * CP + aj], dl = sDl[qq * CP + aj];
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-          gv[r] = fmaf(p, sG[qq * DP + ad0 + r], gv[r]);
-          gk[r] = fmaf(dl, sQt[qq * DP + ad0 + r], gk[r]);
+        for (int r = 0; r < 8; ++r) {
+          const f32x4_t g4 = *reinterpret_cast<const f32x4_t*>(&sG[qq * DP + ad0 + 4 * r]);
+          const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(&sQt[qq * DP + ad0 + 4 * r]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            gv[r][c] = fmaf(p, g4[c], gv[r][c]);
+            gk[r][c] = fmaf(dl, q4[c], gk[r][c]);
+          }
         }
       }
     }
@@ -180,32 +207,41 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
       for (int qq = 0; qq < nq; ++qq) {
         const float g = sG[qq * DP + pv];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) gdp[r] = fmaf(g, sQt[qq * DP + pd0 + r], gdp[r]);
+        for (int r = 0; r < 4; ++r) {
+          const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(&sQt[qq * DP + pd0 + 4 * r]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) gdp[r][c] = fmaf(g, q4[c], gdp[r][c]);
+        }
       }
     }
     {
-      // dq_n = s sum_j dl_nj K_ij + s D_i^T g_n  (dimension ed)
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < Ck; ++j) {
-        const float kd = sK[j * DP + ed];
+      // dq_n = s sum_j dl_nj K_ij + s D_i^T g_n: query eq, dims ed0 .. ed0 + 3
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < Ck4; j += 4) {
+        const f32x4_t dl4 = *reinterpret_cast<const f32x4_t*>(&sDl[eq * CP + j]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = fmaf(sDl[(4 * eg + r) * CP + j], kd, acc[r]);
+        for (int t = 0; t < 4; ++t) {
+          const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(&sK[(j + t) * DP + ed0]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c] = fmaf(dl4[t], k4[c], acc[c]);
+        }
       }
       if (dip) {
-        for (int vv = 0; vv < D; ++vv) {
-          const float dd = sDip[vv * DP + ed];
+        for (int vv = 0; vv < D; vv += 4) {
+          const f32x4_t g4 = *reinterpret_cast<const f32x4_t*>(&sG[eq * DP + vv]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] = fmaf(sG[(4 * eg + r) * DP + vv], dd, acc[r]);
+          for (int t = 0; t < 4; ++t) {
+            const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sDip[(vv + t) * DP + ed0]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(g4[t], d4[c], acc[c]);
+          }
         }
       }
+      if (eq < nq) {
+        const f32x4_t x = {s * acc[0], s * acc[1], s * acc[2], s * acc[3]};
+        *reinterpret_cast<f32x4_t*>(dq + static_cast<size_t>(sRow[eq]) * D + ed0) = x;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qq = 4 * eg + r;
-        if (qq < nq) {
-          const float x = s * acc[r];
-          dq[static_cast<size_t>(sRow[qq]) * D + ed] = x;
-          qbs -= x;
-        }
+        for (int c = 0; c < 4; ++c) qbs[c] -= x[c];
       }
     }
     __syncthreads();  // the tile buffers are rewritten next
@@ -213,17 +249,25 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
   if (aj < Ck) {
     const size_t o = (ti * Ck + aj) * D + ad0;
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      a.g_k[o + r] = s * gk[r];
-      a.g_v[o + r] = gv[r];
+    for (int r = 0; r < 8; ++r) {
+      *reinterpret_cast<f32x4_t*>(a.g_k + o + 4 * r) = f32x4_t{s * gk[r][0], s * gk[r][1], s * gk[r][2], s * gk[r][3]};
+      *reinterpret_cast<f32x4_t*>(a.g_v + o + 4 * r) = gv[r];
     }
   }
   if (tid < Ck) a.g_logz[ti * Ck + tid] = glz;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) a.g_dip[ti * D * D + static_cast<size_t>(pv) * D + pd0 + r] = dip ? s * gdp[r] : 0.f;
-  sRed[eg][ed] = qbs;
+  for (int r = 0; r < 4; ++r) {
+    const f32x4_t x = dip ? f32x4_t{s * gdp[r][0], s * gdp[r][1], s * gdp[r][2], s * gdp[r][3]}
+                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4_t*>(a.g_dip + ti * D * D + static_cast<size_t>(pv) * D + pd0 + 4 * r) = x;
+  }
+  *reinterpret_cast<f32x4_t*>(&sRed[eq][ed0]) = qbs;
   __syncthreads();
-  if (tid < D) a.dqbar2[ti * D + tid] = (sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid]);
+  if (tid < D) {
+    float x = 0.f;
+    for (int q = 0; q < QT; ++q) x += sRed[q][tid];
+    a.dqbar2[ti * D + tid] = x;
+  }
 }
 
 // Per query cluster i: P_i., log sum_j Z_ij, the bf16 hi/lo copies of G_Dip_i (tilted), and
@@ -459,36 +503,42 @@ __global__ void __launch_bounds__(256) bw_keys_a_kernel(BwArgs a) {
     const float w = (valid && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
     const float p = valid ? __expf(av - a.lz[ti]) : 0.f;
     const uint16_t* g = sGd[buf];
-    f32x16_t u[NMT], t[NMT];
+    // u^T = G K^T, then t^T = G^T V^T, each folded into its accumulator before the next
+    // (one 32-row tile pair of registers live at a time)
+    float qp = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) u[mt] = t[mt] = zero16();
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+    for (int mt = 0; mt < NMT; ++mt) {
+      f32x16_t u = zero16();
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int o = (32 * mt + c) * GST + 16 * ks + 8 * h;
         const bf16x8_t gh = as_bf16x8(*reinterpret_cast<const u16x8_t*>(g + o));
         const bf16x8_t gl = as_bf16x8(*reinterpret_cast<const u16x8_t*>(g + D * GST + o));
-        const bf16x8_t th = as_bf16x8(*reinterpret_cast<const u16x8_t*>(g + 2 * D * GST + o));
-        const bf16x8_t tl = as_bf16x8(*reinterpret_cast<const u16x8_t*>(g + 3 * D * GST + o));
-        u[mt] = mfma32(gh, kh[ks], u[mt]);
-        u[mt] = mfma32(gl, kh[ks], u[mt]);
-        t[mt] = mfma32(th, vh[ks], t[mt]);
-        t[mt] = mfma32(tl, vh[ks], t[mt]);
-        if (F32) {
-          u[mt] = mfma32(gh, kl[ks], u[mt]);
-          t[mt] = mfma32(th, vl[ks], t[mt]);
-        }
+        u = mfma32(gh, kh[ks], u);
+        u = mfma32(gl, kh[ks], u);
+        if (F32) u = mfma32(gh, kl[ks], u);
       }
-    float qp = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        qp = fmaf(vq[16 * mt + v], u[mt][v], qp);
-        adv[mt][v] = fmaf(p, u[mt][v], adv[mt][v]);
-        adk[mt][v] = fmaf(p, t[mt][v], adk[mt][v]);
+        qp = fmaf(vq[16 * mt + v], u[v], qp);
+        adv[mt][v] = fmaf(p, u[v], adv[mt][v]);
       }
+    }
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      f32x16_t t = zero16();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int o = (32 * mt + c) * GST + 16 * ks + 8 * h;
+        const bf16x8_t th = as_bf16x8(*reinterpret_cast<const u16x8_t*>(g + 2 * D * GST + o));
+        const bf16x8_t tl = as_bf16x8(*reinterpret_cast<const u16x8_t*>(g + 3 * D * GST + o));
+        t = mfma32(th, vh[ks], t);
+        t = mfma32(tl, vh[ks], t);
+        if (F32) t = mfma32(th, vl[ks], t);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) adk[mt][v] = fmaf(p, t[v], adk[mt][v]);
+    }
     const float qv = qp + xor32(qp);
     if (valid && h == 0) {
       const size_t o = (static_cast<size_t>(bh) * Cq + i) * N + pos;
@@ -576,15 +626,23 @@ __global__ void __launch_bounds__(256) bw_dlogz_kernel(BwArgs a) {
 // on top of the tilted dipole's terms (bw_keys_a) or, untilted, plus the covariance terms
 // (sum_i P_ij G_Dip_i)^T (v_m - mean v) / n_j and (sum_i P_ij G_Dip_i)(k_m - mean k) / n_j.
 // Then the tile's s sum_m w_im dL/dw_im k_m for every i (one partial per tile).
+// Dynamic LDS (floats): qbar [Cq][D] | w dL/dw [Cq][KT + 1] | key rows [KT][D + 1] |
+// value rows [KT][D + 1] (untilted only).
+__host__ __device__ constexpr size_t bw_keys_b_lds(int Cq, int dipole) {
+  return sizeof(float) * (static_cast<size_t>(Cq) * kBwD + static_cast<size_t>(Cq) * (kBwKeyTile + 1) +
+                          (dipole == 2 ? 2 : 1) * static_cast<size_t>(kBwKeyTile) * (kBwD + 1));
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
   constexpr int D = kBwD, KT = kBwKeyTile, DQ = D / 4, RP = D + 1;
-  __shared__ float sQb[kMaxClusters * D];
-  __shared__ float sWd[kMaxClusters * (KT + 1)];
-  __shared__ float sKr[KT * RP];
-  __shared__ float sVr[KT * RP];
+  extern __shared__ __align__(16) float dyn[];
   const int bh = blockIdx.y, tid = threadIdx.x, kk = tid >> 2, d0 = (tid & 3) * DQ;
   const int N = a.N, Cq = a.Cq, Ck = a.Ck;
+  float* sQb = dyn;
+  float* sWd = sQb + Cq * D;
+  float* sKr = sWd + Cq * (KT + 1);
+  float* sVr = sKr + KT * RP;  // untilted only
   const float s = a.scale;
   for (int e = tid; e < Cq * D; e += 256) sQb[e] = a.qbar[static_cast<size_t>(bh) * Cq * D + e];
   const int pos = blockIdx.x * KT + kk;
@@ -601,12 +659,11 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
     kf[e] = valid ? Elem<T>::load(K, static_cast<size_t>(key) * D + d0 + e) : 0.f;
     vf[e] = valid ? Elem<T>::load(V, static_cast<size_t>(key) * D + d0 + e) : 0.f;
     sKr[kk * RP + d0 + e] = kf[e];
-    sVr[kk * RP + d0 + e] = vf[e];
+    if (a.dipole == 2) sVr[kk * RP + d0 + e] = vf[e];
     dk[e] = (a.dipole == 1 && valid) ? dkr[e] : 0.f;
     dv[e] = (a.dipole == 1 && valid) ? dvr[e] : 0.f;
   }
   __syncthreads();
-  const float* Arow = a.A;
   for (int i = 0; i < Cq; ++i) {
     const size_t ti = static_cast<size_t>(bh) * Cq + i;
     float x = 0.f;
@@ -645,7 +702,6 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
     }
     if ((tid & 3) == 0) sWd[i * (KT + 1) + kk] = w * y;
   }
-  (void)Arow;
   if (a.dipole == 2 && valid) {
     // covariance terms with the cluster's dL/dCov = sum_i P_ij G_Dip_i
     const size_t tj = static_cast<size_t>(bh) * Ck + j;
@@ -691,8 +747,17 @@ __global__ void __launch_bounds__(256) bw_centroid_kernel(BwArgs a) {
   const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, d = tid & 63, g = tid >> 6;
   const int Cq = a.Cq, N = a.N;
   const size_t ti = static_cast<size_t>(bh) * Cq + i;
+  // this thread's tiles g, g + 4, ... in order, eight loads in flight at a time
   float acc = 0.f;
-  for (int tb = g; tb < a.ntb; tb += 4) acc += a.dqbar_part[((static_cast<size_t>(bh) * a.ntb + tb) * Cq + i) * D + d];
+  const float* src = a.dqbar_part + (static_cast<size_t>(bh) * a.ntb * Cq + i) * D + d;
+  const size_t stride = static_cast<size_t>(Cq) * D;
+  for (int t0 = g; t0 < a.ntb; t0 += 32) {
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x[r] = t0 + 4 * r < a.ntb ? src[(t0 + 4 * r) * stride] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc += x[r];
+  }
   sRed[g][d] = acc;
   __syncthreads();
   if (tid < D) sTot[tid] = a.dqbar2[ti * D + tid] + a.dqbar1[ti * D + tid] + ((sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid]));
@@ -703,9 +768,19 @@ __global__ void __launch_bounds__(256) bw_centroid_kernel(BwArgs a) {
   const float inv = 1.f / static_cast<float>(o1 - o0);
   const int32_t* perm = a.perm_q + static_cast<size_t>(bh) * N;
   float* dq = a.dq + static_cast<size_t>(bh) * N * D;
-  for (int e = tid; e < (o1 - o0) * D; e += 256) {
-    const int n = perm[o0 + e / D], dd = e % D;
-    dq[static_cast<size_t>(n) * D + dd] += sTot[dd] * inv;
+  // four rows per pass (a wave per row), four passes' loads in flight
+  for (int r0 = 0; r0 < o1 - o0; r0 += 16) {
+    float* row[4];
+    float x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = r0 + 4 * q + g;
+      row[q] = r < o1 - o0 ? dq + static_cast<size_t>(perm[o0 + r]) * D + d : nullptr;
+      x[q] = row[q] != nullptr ? *row[q] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (row[q] != nullptr) *row[q] = x[q] + sTot[d] * inv;
   }
 }
 
@@ -737,8 +812,10 @@ static void launch_backward_t(const BwArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bw_dlogz_kernel, gi, dim3(256), 0, s, a);
   }
   {
+    const size_t lds = bw_keys_b_lds(a.Cq, a.dipole);
+    allow_lds((const void*)bw_keys_b_kernel<T>, lds);
     ProfScope ps_("bw_keys_b", s);
-    hipLaunchKernelGGL((bw_keys_b_kernel<T>), gk, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bw_keys_b_kernel<T>), gk, dim3(256), lds, s, a);
   }
   {
     ProfScope ps_("bw_centroid", s);

@@ -232,6 +232,25 @@ __global__ void __launch_bounds__(256) s1_moments_kernel(S1Args a) {
     for (int y = 0; y < TD; ++y) out[(tr * TD + x) * D + tc * TD + y] = acc[x][y];
 }
 
+// Acausal tables of the general path (a single key block, whose atoms are whole): per
+// (query centroid i, head), for every key cluster j, log Z_ij = m + log z and the tilted
+// means K_ij = (sum w k) / z, V_ij = (sum w v) / z (zero for an empty cluster).
+__global__ void __launch_bounds__(256) s1_tables_acausal_kernel(S1Args a) {
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int D = a.D, Cq = a.Cq, Ck = a.Ck;
+  const size_t base = (static_cast<size_t>(bh) * Cq + i) * Ck;
+  for (int j = tid; j < Ck; j += 256) {
+    const float z = a.at_z[base + j];
+    a.s_logz[base + j] = z > 0.f ? a.at_m[base + j] + __logf(z) : kNegInf;
+  }
+  for (int e = tid; e < Ck * D; e += 256) {
+    const float z = a.at_z[base + e / D];
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    a.s_k[base * D + e] = a.at_k[base * D + e] * inv;
+    a.s_v[base * D + e] = a.at_v[base * D + e] * inv;
+  }
+}
+
 constexpr int kHierLevels = 12;  // binary-counter depth of the hierarchical folds (nb < 2^11)
 
 // Fold atoms over blocks: one workgroup per (j, i, head), 2*D threads (K then V dims).
@@ -1006,9 +1025,12 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
     ProfScope ps_("s1_atoms", s);
     hipLaunchKernelGGL((s1_atoms_kernel<T, D>), dim3(a.Ck, a.nb, a.BH), dim3(256), lds_atoms, s, a);
   }
-  {
+  if (!a.causal) {
+    ProfScope ps_("s1_tables", s);
+    hipLaunchKernelGGL(s1_tables_acausal_kernel, dim3(a.Cq, a.BH), dim3(256), 0, s, a);
+  } else {
     ProfScope ps_("s1_prefix", s);
-    if (a.causal && a.hier) hipLaunchKernelGGL(s1_prefix_kernel<true>, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
+    if (a.hier) hipLaunchKernelGGL(s1_prefix_kernel<true>, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
     else hipLaunchKernelGGL(s1_prefix_kernel<false>, dim3(a.Ck, a.Cq, a.BH), dim3(2 * D), 0, s, a);
   }
   if (a.dipole == 2) {  // untilted (no retrieval, no hierarchy): per key cluster covariances
