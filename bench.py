@@ -158,6 +158,23 @@ def kernel_work(name: str, cfg, hier: bool = False, ctx: dict = None):
         # D_i = sum_j P_ij Cov_j (covariances and log Z read, s D_i written)
         "s1_cluster_cov": (2 * x + BH * Ck * D * D * 4, 2.0 * BH * N * D * D),
         "s1_untilted_dip": (BH * Ck * D * D * 4 + BH * Cq * Ck * 4 + BH * Cq * D * D * e, 2.0 * BH * Cq * Ck * D * D),
+        # causal untilted: bucket statistics folded into prefix counts and means; per block
+        # the running centred sums take the block's buckets and D_i = sum_j P_ij Cov_j^{<b}
+        "s1_untilted_prefix": (2 * BH * nb * Ck * (1 + 2 * D) * 4, 0.0),
+        "s1_untilted_causal": (BH * nb * Ck * (D * D + 2 + 4 * D) * 4 + BH * nb * Cq * Ck * 4 + BH * nb * Cq * D * D * e,
+                               2.0 * BH * nb * Cq * Ck * D * D + 2.0 * BH * nb * Ck * D * D),
+        # acausal general-path tables from whole atoms
+        "s1_tables": (table * (2 + 2 * D) * 4 + ftab, 0.0),
+        # backward (acausal): stage 2 per query cluster (q, dout read; dq written; tables read;
+        # summary gradients written), q.K, g.V, p g, dl q, dl K, g D, g q per query
+        "bw_refine": (2 * x + BH * N * D * 4 + 2 * (ftab + dip32), 2.0 * BH * N * (5 * Ck * D + 2 * D * D)),
+        # tilted: per (query cluster, key) G k and G^T v on the matrix cores; keys, values,
+        # a_im and G (bf16 hi/lo, both layouts) read, Q and w Q written, the dk and dv terms written
+        "bw_keys_a": (2 * x + 3 * BH * Cq * N * 4 + BH * Cq * 4 * D * D * 2 + 2 * BH * N * D * 4,
+                      4.0 * BH * Cq * N * D * D),
+        # per (query cluster, key): a_im, dL/dw, the dk and dv updates and the tile partials
+        "bw_keys_b": (2 * x + 4 * BH * N * D * 4 + 2 * table * D * 4 + 4 * table * 4 + BH * Cq * N * 4
+                      + BH * (-(-N // 64)) * Cq * D * 4, 14.0 * BH * N * Cq * D),
     }
     if cfg.topk_clusters and ctx is not None:
         k1, k2 = cfg.topk_clusters, cfg.topk_blocks
@@ -179,13 +196,22 @@ def kernel_work(name: str, cfg, hier: bool = False, ctx: dict = None):
     return w.get(name)
 
 
+# kernels whose arithmetic runs on the vector ALUs in fp32 (priced against the vector peak)
+ALU_KERNELS = ("bw_refine", "bw_keys_b")
+
+
 def roofline_entry(name: str, cfg, avg_s: float, hier: bool = False, ctx: dict = None):
     """Roofline of one kernel from its measured average launch duration: memory-bound when
-    its arithmetic intensity is below the ridge point, else matrix-core-bound."""
+    its arithmetic intensity is below the ridge point, else matrix-core-bound (vector-ALU
+    bound for the fp32 vector kernels of ALU_KERNELS above their own ridge point)."""
     wk = kernel_work(name, cfg, hier, ctx)
     if wk is None:
         return None
     nbytes, flops = wk
+    if name in ALU_KERNELS and flops / nbytes >= PEAK_FP32_VALU_TFLOPS * 1e3 / PEAK_HBM_GBS:
+        return {"bound": "alu", "achieved": flops / avg_s / 1e12, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                "frac": flops / avg_s / 1e12 / PEAK_FP32_VALU_TFLOPS, "bytes_per_launch": nbytes,
+                "flops_per_launch": flops}
     if flops / nbytes < RIDGE or flops == 0:
         return {"bound": "hbm", "achieved": nbytes / avg_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": nbytes / avg_s / 1e9 / PEAK_HBM_GBS, "bytes_per_launch": nbytes, "flops_per_launch": flops}
@@ -575,8 +601,12 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
         torch.cuda.synchronize()
         prof_b = binding.prof_collect()
         binding.prof_enable(False)
+        dom_b = next((n for n, _ in sorted(prof_b.items(), key=lambda kv: -kv[1][0])
+                      if kernel_work(n, cfg) is not None), None)
         extra["backward"] = {
             "ms_per_step": ms_b, "value": cfg.B * cfg.N / (ms_b / 1e3), "unit": "tokens/s",
+            "roofline": None if dom_b is None else {
+                "kernel": dom_b, **roofline_entry(dom_b, cfg, prof_b[dom_b][0] / prof_b[dom_b][1] / 1e3)},
             "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in sorted(prof_b.items(), key=lambda kv: -kv[1][0])}}
         print(f"# backward: {ms_b:.3f} ms/step, {extra['backward']['kernels_us']}", file=sys.stderr, flush=True)
         del ws_b

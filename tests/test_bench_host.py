@@ -116,3 +116,22 @@ def test_traffic_lookup_follows_the_source_hash(workload, kernel, monkeypatch):
     monkeypatch.setattr(bench, "csrc_sha", lambda: "0" * 16)
     assert bench.measured_traffic(workload, kernel) is None
     assert bench.measured_traffic("no_such_workload", kernel) is None
+
+
+def test_backward_accounting_by_hand():
+    # acausal_8k: 32 heads x 8192 queries, Ck 128, D 64: per query 5 Ck D + 2 D^2 fp32
+    # multiply-adds in the stage-2 backward; priced against the vector-ALU peak
+    import bench
+    from workloads import CONFIGS
+    cfg = CONFIGS["acausal_8k"]
+    nbytes, flops = bench.kernel_work("bw_refine", cfg)
+    assert flops == 2.0 * 32 * 8192 * (5 * 128 * 64 + 2 * 64 * 64)
+    x = 32 * 8192 * 64 * 2
+    ftab = 32 * 32 * 128 * (1 + 2 * 64) * 4
+    dip = 32 * 32 * 64 * 64 * 4
+    assert nbytes == 2 * x + 32 * 8192 * 64 * 4 + 2 * (ftab + dip)
+    r = bench.roofline_entry("bw_refine", cfg, 1e-3)
+    assert r["bound"] == "alu" and r["peak"] == bench.PEAK_FP32_VALU_TFLOPS
+    assert abs(r["achieved"] - flops / 1e-3 / 1e12) < 1e-9
+    # the matrix-core key pass is priced against the bf16 peak (above the ridge point)
+    assert bench.roofline_entry("bw_keys_a", cfg, 1e-3)["bound"] == "mfma"
