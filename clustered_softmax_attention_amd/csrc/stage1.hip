@@ -637,9 +637,12 @@ __device__ __forceinline__ void load8_f32<float>(const float* p, float* out) {
   }
 }
 
-template <typename T, int D>
+// KC keys staged per step: 64, or 2048 / D for the short buckets of causal calls (a
+// smaller LDS footprint, so that more workgroups share a CU).
+template <typename T, int D, int KC>
 __global__ void __launch_bounds__(256) s1_cluster_cov_kernel(S1Args a) {
-  constexpr int TD = D / 16, KC = 64, EPT = D / 4, SST = D + 4;  // EPT: staged elements per thread
+  constexpr int TD = D / 16, EPT = D * KC / 256, SST = D + 4;  // EPT: staged elements per thread
+  static_assert(EPT % 8 == 0, "whole 8-element loads per thread");
   __shared__ __align__(16) float sk[KC * SST];
   __shared__ __align__(16) float sv[KC * SST];
   __shared__ float smk[D], smv[D];
@@ -652,7 +655,7 @@ __global__ void __launch_bounds__(256) s1_cluster_cov_kernel(S1Args a) {
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
   const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * a.N * D;
-  const int sr = tid / 4, sc = (tid % 4) * EPT;  // staged row and first column of this thread
+  const int sr = tid / (D / EPT), sc = (tid % (D / EPT)) * EPT;  // staged row and first column of this thread
   auto stage = [&](int c0) {  // keys c0 .. c0 + KC - 1 of the cluster (zeros past its end)
     float kf[EPT], vf[EPT];
     const int m = c0 + sr;
@@ -942,7 +945,10 @@ static void launch_untilted(const S1Args& a, int part, hipStream_t s) {
   if (part == 0) {
     {
       ProfScope ps_("s1_cluster_cov", s);
-      hipLaunchKernelGGL((s1_cluster_cov_kernel<T, D>), dim3(a.nb * a.Ck, a.BH), dim3(256), 0, s, a);
+      if (a.causal)
+        hipLaunchKernelGGL((s1_cluster_cov_kernel<T, D, 2048 / D>), dim3(a.nb * a.Ck, a.BH), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((s1_cluster_cov_kernel<T, D, 64>), dim3(a.nb * a.Ck, a.BH), dim3(256), 0, s, a);
     }
     if (a.causal) {
       ProfScope ps_("s1_untilted_prefix", s);
