@@ -5,11 +5,16 @@
 //   L = log(e^L_loc + e^L_far),  o = e^(L_loc - L) o_loc + e^(L_far - L) o_far.
 //
 // bf16 path (flash_bf16): workgroup of 4 waves = 128 queries; key/value tiles of 64
-// keys staged row-major in LDS (the next tile in registers meanwhile); per wave
-// S^T = K Q^T on the matrix cores (32 keys x 32 queries per tile), online softmax along
-// accumulator rows (one lane and its partner), O^T += V^T P^T with P rounded to bf16 and
-// V^T read by the transpose read in the key order of the P accumulator. Workgroups are
-// renumbered so that those of one head run on one XCD and share its L2.
+// keys staged row-major in LDS, two of each (the tiles after them in registers
+// meanwhile), one barrier per tile; per wave S^T = K Q^T on the matrix cores (32 keys x
+// 32 queries per tile), online softmax along accumulator rows (one lane and its
+// partner), O^T += V^T P^T with P rounded to bf16 and V^T read by the transpose read in
+// the key order of the P accumulator. The loop is software-pipelined: the products of
+// the next tile's scores are issued between the exponentials of the current one, so
+// the matrix cores and the vector ALU work at the same time within a wave. The running
+// max is raised only when a row's products exceed it by 8 / (scale log2 e), which leaves
+// the result unchanged (it is a stabiliser) and skips most rescaling passes. Workgroups
+// are renumbered so that those of one head run on one XCD and share its L2.
 // fp32 path: one thread per query, online softmax over chunks of 32 keys; all lanes
 // of a wave visit the same key at the same time, so key and value rows are read
 // once per wave.
@@ -120,8 +125,10 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
   constexpr int NMT = D / 32;
   constexpr int CH = D / 8;    // 16-byte chunks per row
   constexpr int NP = BK * CH / 256;  // 16-byte pieces per thread and tensor
-  __shared__ __align__(16) uint16_t sK[BK * KST];
-  __shared__ __align__(16) uint16_t sV[BK * KST];
+  // two K and two V tiles: iteration j reads K of tile j + 1 and V of tile j while the
+  // K of tile j + 2 and the V of tile j + 1 are stored into the other halves
+  __shared__ __align__(16) uint16_t sK[2][BK * KST];
+  __shared__ __align__(16) uint16_t sV[2][BK * KST];
 
   const int total = nqt * a.BH;
   // workgroup id -> (query tile, head) such that each XCD takes a contiguous range: the
@@ -140,115 +147,167 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + base * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + base * D;
 
+  // queries past the end repeat the last one (their rows are not stored)
+  const int qq = qvalid ? qi : N - 1;
   bf16x8_t qf[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    u16x8_t u = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (qvalid) u = *reinterpret_cast<const u16x8_t*>(Q + static_cast<size_t>(qi) * D + 16 * ks + 8 * h);
-    qf[ks] = as_bf16x8(u);
-  }
-  const int qq = qvalid ? qi : N - 1;
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(Q + static_cast<size_t>(qq) * D + 16 * ks + 8 * h));
   const int kbeg = a.block > 0 ? (qq / a.block) * a.block : 0;
   const int kend = a.causal ? qq + 1 : N;
-  const int wkb_min = wave_min_int(kbeg), wkb_max = wave_max_int(kbeg);
-  const int wke_min = wave_min_int(kend), wke_max = wave_max_int(kend);
+  // wave-uniform bounds (scalar registers, so that the tile tests are scalar branches)
+  const int wkb_min = __builtin_amdgcn_readfirstlane(wave_min_int(kbeg));
+  const int wkb_max = __builtin_amdgcn_readfirstlane(wave_max_int(kbeg));
+  const int wke_min = __builtin_amdgcn_readfirstlane(wave_min_int(kend));
+  const int wke_max = __builtin_amdgcn_readfirstlane(wave_max_int(kend));
   const int qlast = min(q0 + BQ, N) - 1;
   const int gkb = a.block > 0 ? (q0 / a.block) * a.block : 0;
   const int gke = a.causal ? qlast + 1 : N;
+  const int T = (gke - gkb + BK - 1) / BK;  // key tiles of this workgroup
   const float sl2 = a.scale * 1.4426950408889634f;
+  const float thr = 8.f / sl2;
 
   float m = -1e30f, l = 0.f;
   f32x16_t o[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) o[mt] = zero16();
 
-  // the next tile's rows travel in registers while the current one is used
-  u16x8_t pk[NP], pv[NP];
-  auto load_tile = [&](int kt) {
+  u16x8_t rk[NP], rv[NP];
+  auto load_rows = [&](const uint16_t* X, u16x8_t* r, int j) {
+    const int kt = gkb + j * BK;
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
-      const int e = tid + 256 * q, r = e / CH, cc = e % CH, key = kt + r;
-      pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      pv[q] = pk[q];
-      if (key < N) {
-        pk[q] = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(key) * D + cc * 8);
-        pv[q] = *reinterpret_cast<const u16x8_t*>(V + static_cast<size_t>(key) * D + cc * 8);
-      }
+      // rows past the end repeat the last row: their scores are masked and their weights
+      // are zero, so they only need to be finite
+      const int e = tid + 256 * q, row = e / CH, cc = e % CH, key = min(kt + row, N - 1);
+      r[q] = *reinterpret_cast<const u16x8_t*>(X + static_cast<size_t>(key) * D + cc * 8);
     }
   };
-  if (gkb < gke) load_tile(gkb);
-  for (int kt = gkb; kt < gke; kt += BK) {
-    __syncthreads();  // the previous tile is consumed
+  auto store_rows = [&](uint16_t* S, const u16x8_t* r) {
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
-      const int e = tid + 256 * q, r = e / CH, cc = e % CH;
-      *reinterpret_cast<u16x8_t*>(sK + r * KST + cc * 8) = pk[q];
-      *reinterpret_cast<u16x8_t*>(sV + r * KST + cc * 8) = pv[q];
+      const int e = tid + 256 * q, row = e / CH, cc = e % CH;
+      *reinterpret_cast<u16x8_t*>(S + row * KST + cc * 8) = r[q];
     }
-    __syncthreads();
-    if (kt + BK < gke) load_tile(kt + BK);
-    if (kt >= wke_max || kt + BK <= wkb_min) continue;  // tile outside every row of this wave
-    const bool full = kt >= wkb_max && kt + BK <= wke_min && kt + BK <= N;
-
-    f32x16_t s[2];
+  };
+  auto scores = [&](const uint16_t* S, f32x16_t* s) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s[t] = zero16();
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8_t af = as_bf16x8(*reinterpret_cast<const u16x8_t*>(sK + (32 * t + c) * KST + 16 * ks + 8 * h));
+        const bf16x8_t af = as_bf16x8(*reinterpret_cast<const u16x8_t*>(S + (32 * t + c) * KST + 16 * ks + 8 * h));
         s[t] = mfma32(af, qf[ks], s[t]);
       }
     }
-    // running max on the raw products q.k (the scale is folded into the exponent below)
-    float mx = -1e30f;
-    if (!full) {
+  };
+  auto needed = [&](int j) {
+    const int kt = gkb + j * BK;
+    return !(kt >= wke_max || kt + BK <= wkb_min);
+  };
+
+  // prologue (a workgroup has at least one key tile): K and V of tile 0 and K of tile 1
+  // in LDS, the scores of tile 0, and K of tile 2 and V of tile 1 in registers
+  load_rows(K, rk, 0);
+  load_rows(V, rv, 0);
+  store_rows(sK[0], rk);
+  store_rows(sV[0], rv);
+  load_rows(K, rk, min(1, T - 1));
+  store_rows(sK[1], rk);
+  __syncthreads();
+  f32x16_t sA[2], sB[2];
+  scores(sK[0], sA);
+  load_rows(K, rk, min(2, T - 1));
+  load_rows(V, rv, min(1, T - 1));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+
+  auto iteration = [&](int j, f32x16_t (&scur)[2], f32x16_t (&snxt)[2]) {
+    __syncthreads();  // iteration j - 1 is done everywhere; its stores are visible
+    const int kt = gkb + j * BK;
+    if (needed(j)) {
+      const bool full = kt >= wkb_max && kt + BK <= wke_min && kt + BK <= N;
+      if (!full) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = kt + 32 * t + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (key < kbeg || key >= kend) scur[t][v] = kNegInf;
+          }
+      }
+      // running max on the raw products q.k (the scale is folded into the exponent); it
+      // is a stabiliser only, raised (with the accumulators rescaled) when a row's
+      // products exceed it by more than 8 / sl2, so the weights stay below 2^8
+      float mx = -1e30f;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kt + 32 * t + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (key < kbeg || key >= kend) s[t][v] = kNegInf;
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[t][v], s[t][v + 1]));
-    mx = fmaxf(mx, xor32(mx));
-    const float mn = fmaxf(m, mx);
-    if (__ballot(mn > m) != 0ull) {  // rescale only when a row's running max grew (else alpha = 1)
-      const float alpha = fast_exp2((m - mn) * sl2);
-      l *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
-    }
-    m = mn;
-    const float nb = -mn * sl2;
-    // p = 2^(s sl2 - mn sl2), rounded to bf16 for the product with V; the row sum is taken
-    // of the same rounded weights (packed dot products with ones), so that numerator and
-    // normaliser use identical values
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        float pv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(s[t][8 * ss + i], sl2, nb));
-        const bf16x8_t bfr = pack_bf16x8(pv);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bf16x2_t p2 = {bfr[2 * i], bfr[2 * i + 1]};
-          l = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l, false);
-        }
+        for (int v = 0; v < 16; v += 2)
+          mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, scur[t][v]), scur[t][v + 1]);
+      mx = __builtin_elementwise_maximum(mx, xor32(mx));
+      if (__ballot(mx > m + thr) != 0ull) {
+        const float mn = __builtin_elementwise_maximum(m, mx);
+        const float alpha = fast_exp2((m - mn) * sl2);
+        l *= alpha;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
-          o[mt] = mfma32(lds_operand_tr_acc(sV, KST, 32 * t + 16 * ss, 32 * mt, lane), bfr, o[mt]);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+        m = mn;
       }
+      const float nb = -m * sl2;
+      // the next tile's scores on the matrix cores while this tile's weights are formed
+      // (after the last tile they are computed from a stale half and not used): the
+      // NKS k-steps of its two 32-key halves are spread over the four weight steps
+      const uint16_t* sk = sK[(j + 1) & 1];
+      snxt[0] = zero16();
+      snxt[1] = zero16();
+      // p = 2^(s sl2 - m sl2), rounded to bf16 for the product with V; the row sum is
+      // taken of the same rounded weights (packed dot products with ones), so that
+      // numerator and normaliser use identical values
+      const uint16_t* sv = sV[j & 1];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+          for (int u = 0; u < NKS / 4; ++u) {
+            const int ks = (2 * t + ss) * (NKS / 4) + u;
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) {
+              const bf16x8_t af =
+                  as_bf16x8(*reinterpret_cast<const u16x8_t*>(sk + (32 * tn + c) * KST + 16 * ks + 8 * h));
+              snxt[tn] = mfma32(af, qf[ks], snxt[tn]);
+            }
+          }
+          float pv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(scur[t][8 * ss + i], sl2, nb));
+          const bf16x8_t bfr = pack_bf16x8(pv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16x2_t p2 = {bfr[2 * i], bfr[2 * i + 1]};
+            l = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l, false);
+          }
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt)
+            o[mt] = mfma32(lds_operand_tr_acc(sv, KST, 32 * t + 16 * ss, 32 * mt, lane), bfr, o[mt]);
+        }
+    } else {
+      scores(sK[(j + 1) & 1], snxt);
+    }
+    // stage K of tile j + 2 and V of tile j + 1 into the halves read in iteration j - 1;
+    // unconditionally, past the last tile with repeated rows that are never read, so
+    // that no branch separates a load from its wait
+    store_rows(sK[j & 1], rk);
+    store_rows(sV[(j + 1) & 1], rv);
+    load_rows(K, rk, min(j + 3, T - 1));
+    load_rows(V, rv, min(j + 2, T - 1));
+  };
+  for (int j = 0; j < T; j += 2) {
+    iteration(j, sA, sB);
+    if (j + 1 < T) iteration(j + 1, sB, sA);
   }
   const float lt = l + xor32(l);
   if (!qvalid) return;
