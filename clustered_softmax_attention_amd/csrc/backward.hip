@@ -42,7 +42,9 @@ constexpr int kBwGST = kBwD + 8;  // LDS row stride (bf16) of the staged G_Dip t
 // LDS: K_i. and V_i. rows and D_i (fp32, rows padded to 68 floats: 16-byte reads by 16
 // lanes hit distinct banks), the tile's residuals and upstream gradients, and the tile's
 // weights p and dl = dL/dlogit; every product reads its operands 4 at a time.
-template <typename T>
+// Causal calls: one workgroup per (block b, query cluster i) bucket, against table entry
+// b, with the far field's share of the upstream gradient (fp32) and of dL/dlog-normaliser.
+template <typename T, typename TG>
 __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
   constexpr int D = kBwD, DP = D + 4, CP = kMaxClusters + 4, QT = kBwQT;
   __shared__ __align__(16) float sK[kMaxClusters * DP];
@@ -55,12 +57,15 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
   __shared__ float sLz[kMaxClusters];
   __shared__ float sQbar[D];
   __shared__ int sRow[QT];
+  __shared__ float sDL[QT];    // dL/d(log normaliser) of the tile's queries (causal far field)
   __shared__ __align__(16) float sRed[QT][D];
-  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Cq = a.Cq, Ck = a.Ck, N = a.N, Ck4 = (Ck + 3) & ~3;
+  const int nbS = a.causal ? a.nb : 1;
+  const int i = e % Cq;
   const float s = a.scale;
   const bool dip = a.dipole != 0;
-  const size_t ti = static_cast<size_t>(bh) * Cq + i;
+  const size_t ti = static_cast<size_t>(bh) * nbS * Cq + e;  // table entry e / Cq, cluster i
   // tables; rows Ck .. Ck4 - 1 of K and columns Ck .. Ck4 - 1 of dl stay zero
   for (int e = tid; e < Ck4 * D; e += 256) {
     const int j = e / D, d = e % D;
@@ -70,12 +75,13 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
   for (int e = tid; e < D * D; e += 256) sDip[(e / D) * DP + e % D] = dip ? a.dip[ti * D * D + e] : 0.f;
   for (int e = tid; e < QT * CP; e += 256) sDl[e] = 0.f;
   for (int j = tid; j < Ck; j += 256) sLz[j] = a.logz[ti * Ck + j];
-  if (tid < D) sQbar[tid] = a.qbar[ti * D + tid];
-  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (Cq + 1);
-  const int o0 = offq[i], o1 = offq[i + 1];
+  if (tid < D) sQbar[tid] = a.qbar[(static_cast<size_t>(bh) * Cq + i) * D + tid];
+  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (nbS * Cq + 1);
+  const int o0 = offq[e], o1 = offq[e + 1];
   const int32_t* perm = a.perm_q + static_cast<size_t>(bh) * N;
   const T* Q = static_cast<const T*>(a.q) + static_cast<size_t>(bh) * N * D;
-  const T* G = static_cast<const T*>(a.dout) + static_cast<size_t>(bh) * N * D;
+  const TG* G = static_cast<const TG*>(a.causal ? static_cast<const void*>(a.o_far) : a.dout) + static_cast<size_t>(bh) * N * D;
+  const float* dLn = a.causal ? a.l_far + static_cast<size_t>(bh) * N : nullptr;
   float* dq = a.dq + static_cast<size_t>(bh) * N * D;
   // summary-gradient accumulators: dL/dK, dL/dV of cluster aj, dims ad0 .. ad0 + 31
   const int aj = tid >> 1, ad0 = (tid & 1) * 32;
@@ -94,7 +100,7 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
   // next tile's rows travel in registers while the current tile is processed
   constexpr int RPT = QT * D / 256;
   int pn[RPT];
-  float pq[RPT], pg[RPT];
+  float pq[RPT], pg[RPT], pdl[RPT];
   auto fetch = [&](int t0) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
@@ -104,7 +110,8 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       pq[r] = pn[r] >= 0 ? Elem<T>::load(Q, static_cast<size_t>(pn[r]) * D + lane) : 0.f;
-      pg[r] = pn[r] >= 0 ? Elem<T>::load(G, static_cast<size_t>(pn[r]) * D + lane) : 0.f;
+      pg[r] = pn[r] >= 0 ? Elem<TG>::load(G, static_cast<size_t>(pn[r]) * D + lane) : 0.f;
+      pdl[r] = (dLn != nullptr && pn[r] >= 0) ? dLn[pn[r]] : 0.f;
     }
   };
   if (o0 < o1) fetch(o0);
@@ -116,7 +123,10 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
       const int qq = wave + 4 * r;
       sQt[qq * DP + lane] = pn[r] >= 0 ? pq[r] - sQbar[lane] : 0.f;
       sG[qq * DP + lane] = pg[r];
-      if (lane == 0) sRow[qq] = pn[r];
+      if (lane == 0) {
+        sRow[qq] = pn[r];
+        sDL[qq] = pdl[r];
+      }
     }
     __syncthreads();
     if (t0 + QT < o1) fetch(t0 + QT);
@@ -175,7 +185,7 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
         e2[t] *= inv;
         rs = fmaf(e2[t], dv2[t], rs);
       }
-      rs = wave_sum(rs);
+      rs = wave_sum(rs) - sDL[qq];  // the log normaliser's gradient adds p dL/dL_far
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int j = lane + 64 * t;
@@ -270,17 +280,19 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
   }
 }
 
-// Per query cluster i: P_i., log sum_j Z_ij, the bf16 hi/lo copies of G_Dip_i (tilted), and
-// for every key cluster j: dK'_ij, dV'_ij and V_ij^T G_Dip_i K_ij. Two clusters at a time
-// (threads 0-127: j, 128-255: j + 1; of each half, 64 threads per output dimension).
+// Per query cluster i: P_i., log sum_j Z_ij, the bf16 hi/lo copies of G_Dip_i (tilted,
+// acausal), and for every key cluster j: dK'_ij, dV'_ij and V_ij^T G_Dip_i K_ij. Two
+// clusters at a time (threads 0-127: j, 128-255: j + 1; of each half, 64 threads per
+// output dimension). Causal calls: one workgroup per (table entry, query cluster); an
+// entry whose row has no keys (entry 0) gets P = 0 and log sum = -inf.
 __global__ void __launch_bounds__(256) bw_prep_i_kernel(BwArgs a) {
   constexpr int D = kBwD, DP = D + 1;
   __shared__ float sGd[D * DP];
   __shared__ float sP[kMaxClusters];
   __shared__ float sKr[2][D], sVr[2][D], sY[2][D];
-  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Cq = a.Cq, Ck = a.Ck;
-  const size_t ti = static_cast<size_t>(bh) * Cq + i;
+  const size_t ti = static_cast<size_t>(bh) * (a.causal ? a.nb : 1) * Cq + blockIdx.x;
   const bool tilted = a.dipole == 1;
   if (wave == 0) {
     float l[2], mx = kNegInf;
@@ -302,16 +314,17 @@ __global__ void __launch_bounds__(256) bw_prep_i_kernel(BwArgs a) {
     for (int t = 0; t < 2; ++t) {
       const int j = lane + 64 * t;
       if (j < Ck) {
-        sP[j] = e2[t] / z;
-        a.P[ti * Ck + j] = e2[t] / z;
+        const float pj = z > 0.f ? e2[t] / z : 0.f;
+        sP[j] = pj;
+        a.P[ti * Ck + j] = pj;
       }
     }
-    if (lane == 0) a.lz[ti] = mx + __logf(z);
+    if (lane == 0) a.lz[ti] = z > 0.f ? mx + __logf(z) : kNegInf;
   }
   if (tilted)
     for (int e = tid; e < D * D; e += 256) sGd[(e / D) * DP + e % D] = a.g_dip[ti * D * D + e];
   __syncthreads();
-  if (tilted) {
+  if (tilted && !a.causal) {
     uint16_t* gd = a.gd + ti * 4 * D * D;
     for (int e = tid; e < D * D; e += 256) {
       const int r = e / D, c = e % D;
@@ -405,6 +418,144 @@ __global__ void __launch_bounds__(256) bw_prep_j_kernel(BwArgs a) {
   }
 }
 
+// Causal calls: backward of the log-sum-exp merge of the exact in-block part (o_loc,
+// L_loc) and the far field (o_far, L_far):  o = e^(L_far - L) o_far + e^(L_loc - L) o_loc
+// with L = log(e^L_far + e^L_loc). With g = dL/do and the weights af, al:
+//   dL/do_far = af g,  dL/dL_far = af g . (o_far - o),  dL/do_loc = al g,
+// and for the in-block backward delta = dL/do_loc . o_loc - dL/dL_loc = al g . o.
+// One wave per query row; the far-field arrays and o_loc are overwritten in place.
+template <typename T>
+__global__ void __launch_bounds__(256) bw_merge_kernel(BwArgs a) {
+  constexpr int D = kBwD;
+  const size_t row = static_cast<size_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= static_cast<size_t>(a.BH) * a.N) return;
+  const float lf = a.l_far[row], ll = a.l_loc[row];
+  float af = 0.f, al = 1.f;
+  if (lf != kNegInf) {
+    const float L = fmaxf(lf, ll) + __logf(1.f + __expf(-fabsf(lf - ll)));
+    af = __expf(lf - L);
+    al = __expf(ll - L);
+  }
+  const float g = Elem<T>::load(static_cast<const T*>(a.dout), row * D + lane);
+  const float of = a.o_far[row * D + lane], ol = a.o_loc[row * D + lane];
+  const float o = af * of + al * ol;
+  const float go = wave_sum(g * o), gf = wave_sum(g * of);
+  a.o_far[row * D + lane] = af * g;
+  a.o_loc[row * D + lane] = al * g;
+  if (lane == 0) {
+    a.l_far[row] = af * (gf - go);
+    a.delta_loc[row] = al * go;
+  }
+}
+
+// Causal calls, per (table entry b, query cluster i): with the dipole differentiated
+// through D_i = E_i - sum_j P_ij V_ij K_ij^T, E_i = sum_m p_im v_m k_m^T (p_im = w_im
+// P_ij = exp(a_im - lz_i)), which equals the per-cluster form sum_j P_ij C_ij, the total
+//   dL/dlog Z_ij - S_ij = G_logZ_ij - P_ij (V_ij^T G K_ij + <G, D_i>) - (dK'.K + dV'.V)
+// (S_ij = sum_{m in j} w dL/dw over the K and V paths; the E path's per-key term is
+// p_im v_m^T G k_m). Written to dlogz.
+__global__ void __launch_bounds__(256) bw_entry_kernel(BwArgs a) {
+  constexpr int D = kBwD;
+  __shared__ float sRed[4];
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Cq = a.Cq, Ck = a.Ck;
+  const size_t ti = static_cast<size_t>(bh) * a.nb * Cq + blockIdx.x;
+  const bool tilted = a.dipole == 1;
+  float ge = 0.f;
+  if (tilted) {
+    float x = 0.f;
+    for (int e = tid; e < D * D; e += 256) x = fmaf(a.g_dip[ti * D * D + e], a.dip[ti * D * D + e], x);
+    x = wave_sum(x);
+    if (lane == 0) sRed[wave] = x;
+    __syncthreads();
+    ge = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+  }
+  for (int j = wave; j < Ck; j += 4) {
+    const size_t tj = (ti * Ck + j) * D;
+    float x = 0.f;
+    if (a.logz[ti * Ck + j] != kNegInf) {
+      x = a.g_logz[ti * Ck + j] - wave_sum(fmaf(a.dKp[tj + lane], a.tk[tj + lane], a.dVp[tj + lane] * a.tv[tj + lane]));
+      if (tilted) x -= a.P[ti * Ck + j] * (a.vgk[ti * Ck + j] + ge);
+    }
+    if (lane == 0) a.dlogz[ti * Ck + j] = x;
+  }
+}
+
+// Causal calls: a key m of block b' enters table entries b' + 1 .. nb - 1, with weights
+// w^b_im = exp(a_im - log Z^b_ij) = w^{b'+1}_im exp(log Z^{b'+1}_ij - log Z^b_ij) and
+// p^b_im = p^{b'+1}_im exp(lz^{b'+1}_i - lz^b_i); both factors are at most 1 (the sums
+// only grow with b). So its gradient needs, per (b', i, j), the suffix sums
+//   sdk = sum_{b > b'} exp(log Z^{b'+1} - log Z^b) dK'^b  (and sdv, st of dL/dlog Z - S)
+// and per (b', i) sh = sum_{b > b'} exp(lz^{b'+1} - lz^b) G_Dip^b, each by one backward
+// recurrence X^{b'} = Y^{b'+1} + r X^{b'+1} over the blocks (zero at b' = nb - 1).
+// Part one: 64 threads (one per dimension) per (i, j) pair, four pairs per workgroup.
+__global__ void __launch_bounds__(256) bw_suffix_kernel(BwArgs a) {
+  constexpr int D = kBwD;
+  const int bh = blockIdx.y, tid = threadIdx.x, d = tid & 63;
+  const int Cq = a.Cq, Ck = a.Ck, nb = a.nb;
+  const int ij = blockIdx.x * 4 + (tid >> 6);
+  if (ij >= Cq * Ck) return;
+  const size_t CC = static_cast<size_t>(Cq) * Ck;
+  const size_t e0 = static_cast<size_t>(bh) * nb * CC + ij;  // (entry 0, i, j)
+  float xk = 0.f, xv = 0.f, xt = 0.f;
+  a.sdk[(e0 + (nb - 1) * CC) * D + d] = 0.f;
+  a.sdv[(e0 + (nb - 1) * CC) * D + d] = 0.f;
+  if (d == 0) a.st[e0 + (nb - 1) * CC] = 0.f;
+  for (int bp = nb - 2; bp >= 0; --bp) {
+    const size_t e1 = e0 + (bp + 1) * CC;
+    const float l1 = a.logz[e1];
+    const float l2 = bp + 2 < nb ? a.logz[e1 + CC] : kNegInf;
+    const float r = (l1 == kNegInf || l2 == kNegInf) ? 0.f : __expf(l1 - l2);
+    xk = fmaf(r, xk, a.dKp[e1 * D + d]);
+    xv = fmaf(r, xv, a.dVp[e1 * D + d]);
+    xt = fmaf(r, xt, a.dlogz[e1]);
+    a.sdk[(e0 + bp * CC) * D + d] = xk;
+    a.sdv[(e0 + bp * CC) * D + d] = xv;
+    if (d == 0) a.st[e0 + bp * CC] = xt;
+  }
+}
+
+// Part two (tilted): per (i, head), sh for every b', written as the bf16 hi + lo copies the
+// per-key matrix-core pass reads (rows v, then the transpose with rows d).
+__global__ void __launch_bounds__(256) bw_suffix_dip_kernel(BwArgs a) {
+  constexpr int D = kBwD, DP = D + 1, EPT = D * D / 256;
+  __shared__ float sX[D * DP];
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int Cq = a.Cq, nb = a.nb;
+  float x[EPT];
+#pragma unroll
+  for (int r = 0; r < EPT; ++r) x[r] = 0.f;
+  for (int bp = nb - 1; bp >= 0; --bp) {
+    if (bp + 1 < nb) {
+      const size_t e1 = (static_cast<size_t>(bh) * nb + bp + 1) * Cq + i;
+      const float l1 = a.lz[e1];
+      const float l2 = bp + 2 < nb ? a.lz[e1 + Cq] : kNegInf;
+      const float r = (l1 == kNegInf || l2 == kNegInf) ? 0.f : __expf(l1 - l2);
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) x[q] = fmaf(r, x[q], a.g_dip[e1 * D * D + tid + 256 * q]);
+    }
+    __syncthreads();  // the previous entry's transpose reads are done
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = tid + 256 * q;
+      sX[(e / D) * DP + e % D] = x[q];
+    }
+    __syncthreads();
+    uint16_t* gd = a.gd + ((static_cast<size_t>(bh) * nb + bp) * Cq + i) * 4 * D * D;
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = tid + 256 * q, r = e / D, c = e % D;
+      const float y = sX[c * DP + r];  // transpose: row d = r, column v = c
+      const uint16_t xh = f32_to_bf16_bits(x[q]), yh = f32_to_bf16_bits(y);
+      gd[e] = xh;
+      gd[D * D + e] = f32_to_bf16_bits(x[q] - bf16_to_f32(xh));
+      gd[2 * D * D + e] = yh;
+      gd[3 * D * D + e] = f32_to_bf16_bits(y - bf16_to_f32(yh));
+    }
+  }
+}
+
 // a_im = s qbar_i . k_m at every key position (bucket order): four threads per key
 // (16 dimensions each, summed over the quad).
 template <typename T>
@@ -438,6 +589,9 @@ __global__ void __launch_bounds__(256) bw_scores_kernel(BwArgs a) {
 // buffered: on the matrix cores u^T = G_Dip_i K^T (rows v, column = key) and
 // t^T = G_Dip_i^T V^T (rows d); then Q_im = v_m . u_m, and the accumulators
 // dv_m += p_im u_m, dk_m += p_im t_m, written as the dipole terms of dk and dv.
+// Causal calls: the workgroups tile each key block separately (positions in bucket order
+// are grouped by block), and a key of block b' takes the suffix sum sh of block b' in
+// place of G_Dip_i and p^{b'+1}_im as its weight; keys of the last block enter no table.
 template <typename T>
 __global__ void __launch_bounds__(256) bw_keys_a_kernel(BwArgs a) {
   constexpr int D = kBwD, GST = kBwGST, NKS = D / 16, NMT = D / 32;
@@ -447,8 +601,15 @@ __global__ void __launch_bounds__(256) bw_keys_a_kernel(BwArgs a) {
   const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int wave = tid >> 6;
   const int N = a.N, Cq = a.Cq, Ck = a.Ck;
-  const int pos = blockIdx.x * 128 + wave * 32 + c;
-  const bool valid = pos < N;
+  const int blk = a.causal ? a.block : N, tpb = (blk + 127) / 128;
+  const int bp = blockIdx.x / tpb;           // key block (0 when acausal)
+  const int pend = min(N, (bp + 1) * blk);
+  const int pos = bp * blk + (blockIdx.x % tpb) * 128 + wave * 32 + c;
+  const bool valid = pos < pend;
+  const bool last = a.causal && bp == a.nb - 1;  // uniform: no table entry after this block
+  const int nbW = a.causal ? a.nb : 1;
+  const size_t ew = static_cast<size_t>(bh) * nbW + (a.causal ? bp + 1 : 0);  // weights' entry
+  const size_t eg = static_cast<size_t>(bh) * nbW + (a.causal ? bp : 0);      // G tiles' entry
   const int key = valid ? a.perm_k[static_cast<size_t>(bh) * N + pos] : 0;
   const int j = valid ? min(max(a.labels_k[static_cast<size_t>(bh) * N + key], 0), Ck - 1) : 0;
   const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * N * D;
@@ -476,7 +637,7 @@ __global__ void __launch_bounds__(256) bw_keys_a_kernel(BwArgs a) {
       vq[16 * mt + v] = valid ? Elem<T>::load(V, static_cast<size_t>(key) * D + 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3)) : 0.f;
   u16x8_t pf[NPF];
   auto fetch = [&](int i) {
-    const uint16_t* src = a.gd + (static_cast<size_t>(bh) * Cq + i) * 4 * D * D;
+    const uint16_t* src = a.gd + (eg * Cq + i) * 4 * D * D;
 #pragma unroll
     for (int q = 0; q < NPF; ++q) pf[q] = *reinterpret_cast<const u16x8_t*>(src + 8 * (tid + 256 * q));
   };
@@ -490,18 +651,22 @@ __global__ void __launch_bounds__(256) bw_keys_a_kernel(BwArgs a) {
   f32x16_t adk[NMT], adv[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) adk[mt] = adv[mt] = zero16();
-  fetch(0);
-  stage(0);
+  const int nci = last ? 0 : Cq;  // query clusters visited
+  if (nci > 0) {
+    fetch(0);
+    stage(0);
+  }
   __syncthreads();
   const float* Arow = a.A + static_cast<size_t>(bh) * Cq * N;
-  for (int i = 0; i < Cq; ++i) {
+  for (int i = 0; i < nci; ++i) {
     const int buf = i & 1;
     if (i + 1 < Cq) fetch(i + 1);  // the next tiles travel during this cluster's products
-    const size_t ti = static_cast<size_t>(bh) * Cq + i;
+    const size_t ti = ew * Cq + i;
     const float av = valid ? Arow[static_cast<size_t>(i) * N + pos] : 0.f;
     const float lzij = a.logz[ti * Ck + j];
     const float w = (valid && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
-    const float p = valid ? __expf(av - a.lz[ti]) : 0.f;
+    const float lzi = a.lz[ti];
+    const float p = (valid && lzi != kNegInf) ? __expf(av - lzi) : 0.f;
     const uint16_t* g = sGd[buf];
     // u^T = G K^T, then t^T = G^T V^T, each folded into its accumulator before the next
     // (one 32-row tile pair of registers live at a time)
@@ -543,11 +708,13 @@ __global__ void __launch_bounds__(256) bw_keys_a_kernel(BwArgs a) {
     if (valid && h == 0) {
       const size_t o = (static_cast<size_t>(bh) * Cq + i) * N + pos;
       a.Q[o] = qv;
-      a.WQ[o] = w * qv;
+      if (!a.causal) a.WQ[o] = w * qv;
     }
     if (i + 1 < Cq) stage(buf ^ 1);
     __syncthreads();
   }
+  if (last && valid && h == 0)
+    for (int i = 0; i < Cq; ++i) a.Q[(static_cast<size_t>(bh) * Cq + i) * N + pos] = 0.f;
   if (valid) {
     float* dk = a.dk + (static_cast<size_t>(bh) * N + key) * D;
     float* dv = a.dv + (static_cast<size_t>(bh) * N + key) * D;
@@ -633,12 +800,21 @@ __host__ __device__ constexpr size_t bw_keys_b_lds(int Cq, int dipole) {
                           (dipole == 2 ? 2 : 1) * static_cast<size_t>(kBwKeyTile) * (kBwD + 1));
 }
 
+// Causal calls (a tile lies in one key block b', the block being a multiple of the tile):
+// with the suffix sums of block b' and the weights of entry b' + 1,
+//   da_im = w (sdk . k_m + sdv . v_m + st) + p v_m^T sh k_m,
+//   dk_m += sum_i (w sdk + s da_im qbar_i),  dv_m += sum_i w sdv,
+// and the tile partial is s sum_m da_im k_m (all of dL/dqbar's stage-1 part).
 template <typename T>
 __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
   constexpr int D = kBwD, KT = kBwKeyTile, DQ = D / 4, RP = D + 1;
   extern __shared__ __align__(16) float dyn[];
   const int bh = blockIdx.y, tid = threadIdx.x, kk = tid >> 2, d0 = (tid & 3) * DQ;
   const int N = a.N, Cq = a.Cq, Ck = a.Ck;
+  const int bp = a.causal ? (blockIdx.x * KT) / a.block : 0;  // key block of the tile
+  const bool last = a.causal && bp == a.nb - 1;               // enters no table entry
+  const size_t ew = static_cast<size_t>(bh) * (a.causal ? a.nb : 1) + (a.causal ? bp + 1 : 0);
+  const size_t es = static_cast<size_t>(bh) * (a.causal ? a.nb : 1) + bp;  // suffix entry (causal)
   float* sQb = dyn;
   float* sWd = sQb + Cq * D;
   float* sKr = sWd + Cq * (KT + 1);
@@ -664,8 +840,8 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
     dv[e] = (a.dipole == 1 && valid) ? dvr[e] : 0.f;
   }
   __syncthreads();
-  for (int i = 0; i < Cq; ++i) {
-    const size_t ti = static_cast<size_t>(bh) * Cq + i;
+  for (int i = 0; i < (last ? 0 : Cq); ++i) {
+    const size_t ti = ew * Cq + i;
     float x = 0.f;
 #pragma unroll
     for (int e = 0; e < DQ; ++e) x = fmaf(sQb[i * D + d0 + e], kf[e], x);
@@ -673,10 +849,11 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
     x += dpp_f32<0x4E>(x);
     const float av = s * x;
     const size_t tij = ti * Ck + j;
+    const size_t sij_ = (es * Cq + i) * Ck + j;  // suffix tables (causal)
     const float lzij = a.logz[tij];
     const float w = (valid && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
-    const float* kp = a.dKp + tij * D + d0;
-    const float* vp = a.dVp + tij * D + d0;
+    const float* kp = a.causal ? a.sdk + sij_ * D + d0 : a.dKp + tij * D + d0;
+    const float* vp = a.causal ? a.sdv + sij_ * D + d0 : a.dVp + tij * D + d0;
     float kpv[DQ], vpv[DQ];
 #pragma unroll
     for (int e = 0; e < DQ; e += 4) {
@@ -693,15 +870,25 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
     for (int e = 0; e < DQ; ++e) y = fmaf(kpv[e], kf[e], fmaf(vpv[e], vf[e], y));
     y += dpp_f32<0xB1>(y);
     y += dpp_f32<0x4E>(y);
-    if (a.dipole == 1 && valid) y += a.P[tij] * a.Q[ti * N + pos];
-    const float da = w * (y - a.sij[tij] + a.dlogz[tij]);
+    float da;
+    if (a.causal) {
+      const float lzi = a.lz[ti];
+      const float p = (a.dipole == 1 && valid && lzi != kNegInf) ? __expf(av - lzi) : 0.f;
+      const float qi = a.dipole == 1 ? a.Q[(static_cast<size_t>(bh) * Cq + i) * N + pos] : 0.f;
+      da = fmaf(w, y + a.st[sij_], p * qi);
+    } else {
+      if (a.dipole == 1 && valid) y += a.P[tij] * a.Q[(static_cast<size_t>(bh) * Cq + i) * N + pos];
+      da = w * (y - a.sij[tij] + a.dlogz[tij]);
+    }
 #pragma unroll
     for (int e = 0; e < DQ; ++e) {
       dk[e] = fmaf(w, kpv[e], fmaf(s * da, sQb[i * D + d0 + e], dk[e]));
       dv[e] = fmaf(w, vpv[e], dv[e]);
     }
-    if ((tid & 3) == 0) sWd[i * (KT + 1) + kk] = w * y;
+    if ((tid & 3) == 0) sWd[i * (KT + 1) + kk] = a.causal ? da : w * y;
   }
+  if (last)
+    for (int e = tid; e < Cq * (KT + 1); e += 256) sWd[e] = 0.f;
   if (a.dipole == 2 && valid) {
     // covariance terms with the cluster's dL/dCov = sum_i P_ij G_Dip_i
     const size_t tj = static_cast<size_t>(bh) * Ck + j;
@@ -760,54 +947,272 @@ __global__ void __launch_bounds__(256) bw_centroid_kernel(BwArgs a) {
   }
   sRed[g][d] = acc;
   __syncthreads();
-  if (tid < D) sTot[tid] = a.dqbar2[ti * D + tid] + a.dqbar1[ti * D + tid] + ((sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid]));
+  // causal calls: the stage-2 parts of every table entry (in entry order); the stage-1
+  // part is all in the key tiles' partials
+  const int nbS = a.causal ? a.nb : 1;
+  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (nbS * Cq + 1);
+  if (tid < D) {
+    float x = a.causal ? 0.f : a.dqbar1[ti * D + tid];
+    for (int b = 0; b < nbS; ++b) x += a.dqbar2[((static_cast<size_t>(bh) * nbS + b) * Cq + i) * D + tid];
+    sTot[tid] = x + ((sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid]));
+  }
   __syncthreads();
-  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (Cq + 1);
-  const int o0 = offq[i], o1 = offq[i + 1];
-  if (o1 <= o0) return;
-  const float inv = 1.f / static_cast<float>(o1 - o0);
+  int n_i = 0;
+  for (int b = 0; b < nbS; ++b) n_i += offq[b * Cq + i + 1] - offq[b * Cq + i];
+  if (n_i == 0) return;
+  const float inv = 1.f / static_cast<float>(n_i);
   const int32_t* perm = a.perm_q + static_cast<size_t>(bh) * N;
   float* dq = a.dq + static_cast<size_t>(bh) * N * D;
-  // four rows per pass (a wave per row), four passes' loads in flight
-  for (int r0 = 0; r0 < o1 - o0; r0 += 16) {
-    float* row[4];
-    float x[4];
+  for (int b = 0; b < nbS; ++b) {
+    const int o0 = offq[b * Cq + i], o1 = offq[b * Cq + i + 1];
+    // four rows per pass (a wave per row), four passes' loads in flight
+    for (int r0 = 0; r0 < o1 - o0; r0 += 16) {
+      float* row[4];
+      float x[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = r0 + 4 * q + g;
-      row[q] = r < o1 - o0 ? dq + static_cast<size_t>(perm[o0 + r]) * D + d : nullptr;
-      x[q] = row[q] != nullptr ? *row[q] : 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + 4 * q + g;
+        row[q] = r < o1 - o0 ? dq + static_cast<size_t>(perm[o0 + r]) * D + d : nullptr;
+        x[q] = row[q] != nullptr ? *row[q] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (row[q] != nullptr) *row[q] = x[q] + sTot[d] * inv;
+    }
+  }
+}
+
+// Causal calls: backward of the exact attention inside each block (queries n and keys
+// m <= n of one block), P_nm = exp(s q_n . k_m - L_loc_n), with g_n = dL/do_loc:
+//   dV_m = sum_n P_nm g_n,  dS_nm = P_nm (g_n . v_m - delta_n),
+//   dK_m = s sum_n dS_nm q_n,  dQ_n = s sum_m dS_nm k_m,
+// delta_n = g_n . o_loc_n - dL/dL_loc_n. fp32 arithmetic on 64 x 64 tiles staged in LDS
+// (rows padded to 68 floats), each thread holding a 4 x 4 block of every product; the
+// results are added to the far-field gradients already in dk, dv (bw_local_kv: one
+// workgroup per key tile, over the query tiles of its block from the diagonal on) and
+// dq (bw_local_q: one per query tile, over the key tiles up to the diagonal).
+constexpr int kLocT = 64, kLocRS = kLocT + 4;
+
+template <typename T>
+__device__ __forceinline__ void loc_stage_rows(float* dst, const T* src, int row0, int tid) {
+  constexpr int D = kBwD;
+#pragma unroll
+  for (int q = 0; q < kLocT * D / 256; ++q) {
+    const int e = tid + 256 * q, r = e / D, d = e % D;
+    dst[r * kLocRS + d] = Elem<T>::load(src, static_cast<size_t>(row0 + r) * D + d);
+  }
+}
+
+// S = Q K^T and dP = G V^T for queries 4 ty + r and keys 4 tx + c of the staged tiles,
+// then P and dS with the causal mask (key position <= query position).
+__device__ __forceinline__ void loc_scores(const float* sQ, const float* sG, const float* sK, const float* sV,
+                                           const float* sL, const float* sDel, int ty, int tx, int n0, int m0,
+                                           float scale, float (&P)[4][4], float (&dS)[4][4]) {
+  constexpr int D = kBwD;
+  float sc[4][4], dp[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sc[r][c] = dp[r][c] = 0.f;
+  for (int d = 0; d < D; d += 4) {
+    f32x4_t q4[4], g4[4], k4[4], v4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      q4[r] = *reinterpret_cast<const f32x4_t*>(&sQ[(4 * ty + r) * kLocRS + d]);
+      g4[r] = *reinterpret_cast<const f32x4_t*>(&sG[(4 * ty + r) * kLocRS + d]);
+      k4[r] = *reinterpret_cast<const f32x4_t*>(&sK[(4 * tx + r) * kLocRS + d]);
+      v4[r] = *reinterpret_cast<const f32x4_t*>(&sV[(4 * tx + r) * kLocRS + d]);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (row[q] != nullptr) *row[q] = x[q] + sTot[d] * inv;
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          sc[r][c] = fmaf(q4[r][u], k4[c][u], sc[r][c]);
+          dp[r][c] = fmaf(g4[r][u], v4[c][u], dp[r][c]);
+        }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int n = 4 * ty + r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int m = 4 * tx + c;
+      const float p = (m0 + m <= n0 + n) ? __expf(scale * sc[r][c] - sL[n]) : 0.f;
+      P[r][c] = p;
+      dS[r][c] = p * (dp[r][c] - sDel[n]);
+    }
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) bw_local_kv_kernel(BwArgs a) {
+  constexpr int D = kBwD, TT = kLocT, RS = kLocRS;
+  __shared__ __align__(16) float sK[TT * RS], sV[TT * RS], sQ[TT * RS], sG[TT * RS], sP[TT * RS], sS[TT * RS];
+  __shared__ float sL[TT], sDel[TT];
+  const int bh = blockIdx.y, tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int N = a.N, m0 = blockIdx.x * TT, bend = (m0 / a.block + 1) * a.block;
+  const size_t base = static_cast<size_t>(bh) * N;
+  const T* Q = static_cast<const T*>(a.q) + base * D;
+  const T* K = static_cast<const T*>(a.k) + base * D;
+  const T* V = static_cast<const T*>(a.v) + base * D;
+  const float* G = a.o_loc + base * D;  // dL/do_loc
+  loc_stage_rows<T>(sK, K, m0, tid);
+  loc_stage_rows<T>(sV, V, m0, tid);
+  float accV[4][4], accK[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) accV[r][c] = accK[r][c] = 0.f;
+  for (int n0 = m0; n0 < bend; n0 += TT) {
+    __syncthreads();  // the previous query tile is consumed
+    loc_stage_rows<T>(sQ, Q, n0, tid);
+    loc_stage_rows<float>(sG, G, n0, tid);
+    if (tid < TT) {
+      sL[tid] = a.l_loc[base + n0 + tid];
+      sDel[tid] = a.delta_loc[base + n0 + tid];
+    }
+    __syncthreads();
+    float P[4][4], dS[4][4];
+    loc_scores(sQ, sG, sK, sV, sL, sDel, ty, tx, n0, m0, a.scale, P, dS);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<f32x4_t*>(&sP[(4 * ty + r) * RS + 4 * tx]) = f32x4_t{P[r][0], P[r][1], P[r][2], P[r][3]};
+      *reinterpret_cast<f32x4_t*>(&sS[(4 * ty + r) * RS + 4 * tx]) = f32x4_t{dS[r][0], dS[r][1], dS[r][2], dS[r][3]};
+    }
+    __syncthreads();
+    // keys 4 ty + r, dimensions 4 tx + c
+    for (int n = 0; n < TT; ++n) {
+      const f32x4_t p4 = *reinterpret_cast<const f32x4_t*>(&sP[n * RS + 4 * ty]);
+      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(&sS[n * RS + 4 * ty]);
+      const f32x4_t g4 = *reinterpret_cast<const f32x4_t*>(&sG[n * RS + 4 * tx]);
+      const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(&sQ[n * RS + 4 * tx]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          accV[r][c] = fmaf(p4[r], g4[c], accV[r][c]);
+          accK[r][c] = fmaf(s4[r], q4[c], accK[r][c]);
+        }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const size_t o = (base + m0 + 4 * ty + r) * D + 4 * tx;
+    f32x4_t dk4 = *reinterpret_cast<const f32x4_t*>(a.dk + o);
+    f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(a.dv + o);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      dk4[c] = fmaf(a.scale, accK[r][c], dk4[c]);
+      dv4[c] += accV[r][c];
+    }
+    *reinterpret_cast<f32x4_t*>(a.dk + o) = dk4;
+    *reinterpret_cast<f32x4_t*>(a.dv + o) = dv4;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) bw_local_q_kernel(BwArgs a) {
+  constexpr int D = kBwD, TT = kLocT, RS = kLocRS;
+  __shared__ __align__(16) float sK[TT * RS], sV[TT * RS], sQ[TT * RS], sG[TT * RS], sSt[TT * RS];
+  __shared__ float sL[TT], sDel[TT];
+  const int bh = blockIdx.y, tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int N = a.N, n0 = blockIdx.x * TT, bbeg = (n0 / a.block) * a.block;
+  const size_t base = static_cast<size_t>(bh) * N;
+  const T* Q = static_cast<const T*>(a.q) + base * D;
+  const T* K = static_cast<const T*>(a.k) + base * D;
+  const T* V = static_cast<const T*>(a.v) + base * D;
+  const float* G = a.o_loc + base * D;
+  loc_stage_rows<T>(sQ, Q, n0, tid);
+  loc_stage_rows<float>(sG, G, n0, tid);
+  if (tid < TT) {
+    sL[tid] = a.l_loc[base + n0 + tid];
+    sDel[tid] = a.delta_loc[base + n0 + tid];
+  }
+  float acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+  for (int m0 = bbeg; m0 <= n0; m0 += TT) {
+    __syncthreads();  // the previous key tile is consumed
+    loc_stage_rows<T>(sK, K, m0, tid);
+    loc_stage_rows<T>(sV, V, m0, tid);
+    __syncthreads();
+    float P[4][4], dS[4][4];
+    loc_scores(sQ, sG, sK, sV, sL, sDel, ty, tx, n0, m0, a.scale, P, dS);
+    // dS transposed: row = key, column = query
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<f32x4_t*>(&sSt[(4 * tx + c) * RS + 4 * ty]) = f32x4_t{dS[0][c], dS[1][c], dS[2][c], dS[3][c]};
+    __syncthreads();
+    // queries 4 ty + r, dimensions 4 tx + c
+    for (int m = 0; m < TT; ++m) {
+      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(&sSt[m * RS + 4 * ty]);
+      const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(&sK[m * RS + 4 * tx]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(s4[r], k4[c], acc[r][c]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const size_t o = (base + n0 + 4 * ty + r) * D + 4 * tx;
+    f32x4_t dq4 = *reinterpret_cast<const f32x4_t*>(a.dq + o);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dq4[c] = fmaf(a.scale, acc[r][c], dq4[c]);
+    *reinterpret_cast<f32x4_t*>(a.dq + o) = dq4;
   }
 }
 
 template <typename T>
 static void launch_backward_t(const BwArgs& a, hipStream_t s) {
-  const dim3 gi(a.Cq, a.BH), gj(a.Ck, a.BH), gk((a.N + kBwKeyTile - 1) / kBwKeyTile, a.BH);
+  const int nbS = a.causal ? a.nb : 1;
+  const dim3 gi(a.Cq, a.BH), ge(nbS * a.Cq, a.BH), gk((a.N + kBwKeyTile - 1) / kBwKeyTile, a.BH);
+  if (a.causal) {
+    ProfScope ps_("bw_merge", s);
+    hipLaunchKernelGGL((bw_merge_kernel<T>), dim3((a.BH * a.N + 3) / 4), dim3(256), 0, s, a);
+  }
   {
     ProfScope ps_("bw_refine", s);
-    hipLaunchKernelGGL((bw_refine_kernel<T>), gi, dim3(256), 0, s, a);
+    if (a.causal) hipLaunchKernelGGL((bw_refine_kernel<T, float>), ge, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((bw_refine_kernel<T, T>), ge, dim3(256), 0, s, a);
   }
   {
     ProfScope ps_("bw_prep_i", s);
-    hipLaunchKernelGGL(bw_prep_i_kernel, gi, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bw_prep_i_kernel, ge, dim3(256), 0, s, a);
+  }
+  if (a.causal) {
+    {
+      ProfScope ps_("bw_entry", s);
+      hipLaunchKernelGGL(bw_entry_kernel, ge, dim3(256), 0, s, a);
+    }
+    {
+      ProfScope ps_("bw_suffix", s);
+      hipLaunchKernelGGL(bw_suffix_kernel, dim3((a.Cq * a.Ck + 3) / 4, a.BH), dim3(256), 0, s, a);
+    }
+    if (a.dipole == 1) {
+      ProfScope ps_("bw_suffix_dip", s);
+      hipLaunchKernelGGL(bw_suffix_dip_kernel, gi, dim3(256), 0, s, a);
+    }
   }
   if (a.dipole == 2) {
     ProfScope ps_("bw_prep_j", s);
-    hipLaunchKernelGGL((bw_prep_j_kernel<T>), gj, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bw_prep_j_kernel<T>), dim3(a.Ck, a.BH), dim3(256), 0, s, a);
   }
   if (a.dipole == 1) {
     {
       ProfScope ps_("bw_scores", s);
       hipLaunchKernelGGL((bw_scores_kernel<T>), gk, dim3(256), 0, s, a);
     }
+    const int blk = a.causal ? a.block : a.N;
+    const int nwg = nbS * ((blk + 127) / 128);
     ProfScope ps_("bw_keys_a", s);
-    hipLaunchKernelGGL((bw_keys_a_kernel<T>), dim3((a.N + 127) / 128, a.BH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bw_keys_a_kernel<T>), dim3(nwg, a.BH), dim3(256), 0, s, a);
   }
-  {
+  if (!a.causal) {
     ProfScope ps_("bw_dlogz", s);
     hipLaunchKernelGGL(bw_dlogz_kernel, gi, dim3(256), 0, s, a);
   }
@@ -820,6 +1225,15 @@ static void launch_backward_t(const BwArgs& a, hipStream_t s) {
   {
     ProfScope ps_("bw_centroid", s);
     hipLaunchKernelGGL(bw_centroid_kernel, gi, dim3(256), 0, s, a);
+  }
+  if (a.causal) {
+    const dim3 gl(a.N / kLocT, a.BH);
+    {
+      ProfScope ps_("bw_local_kv", s);
+      hipLaunchKernelGGL((bw_local_kv_kernel<T>), gl, dim3(256), 0, s, a);
+    }
+    ProfScope ps_("bw_local_q", s);
+    hipLaunchKernelGGL((bw_local_q_kernel<T>), gl, dim3(256), 0, s, a);
   }
 }
 

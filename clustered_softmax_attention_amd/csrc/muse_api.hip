@@ -561,8 +561,9 @@ int run_muse(const void* q, const void* k, const void* v, void* out, const Shape
 int validate_bwd(Shape& s, const muse_fwd_params* p) {
   const int r = validate_muse(s, p);
   if (r != MUSE_OK) return r;
-  if (s.causal) return fail(MUSE_ERR_UNSUPPORTED, "the backward pass is implemented for acausal calls");
   if (s.D != muse::kBwD) return fail(MUSE_ERR_UNSUPPORTED, "the backward pass is implemented for D=%d", muse::kBwD);
+  if (s.causal && p != nullptr && p->dipole == MUSE_DIPOLE_UNTILTED)
+    return fail(MUSE_ERR_UNSUPPORTED, "the causal backward pass takes the tilted dipole or none");
   if (p != nullptr) {
     if (p->topk_clusters > 0 || p->hierarchy || p->cap_ratio > 0.0)
       return fail(MUSE_ERR_UNSUPPORTED, "the backward pass takes no retrieval, hierarchy or cluster size cap");
@@ -576,9 +577,10 @@ int validate_bwd(Shape& s, const muse_fwd_params* p) {
 }
 
 struct BwPlan {
-  Plan f;  // the forward's regions (clustering with the fixed labels and the stage-1 tables)
+  Plan f;  // the forward's regions (clustering with the fixed labels, stage-1 tables, far field)
   size_t g_logz, g_k, g_v, g_dip, P, lz, gd, dKp, dVp, vgk, dP, dlogz, sij, A, Q, WQ, dcov, kmean, vmean;
   size_t dqbar1, dqbar2, dqbar_part;
+  size_t o_loc, l_loc, delta_loc, sdk, sdv, st;  // causal
   int ntb;
   size_t total;
 };
@@ -589,25 +591,35 @@ BwPlan make_bwd_plan(const Shape& s, const muse_fwd_params* p) {
   Layout L;
   L.bytes = B.f.total;
   const size_t BH = s.BH, N = s.N, D = s.D, Cq = s.Cq, Ck = s.Ck, f = sizeof(float);
+  const size_t E = s.causal ? s.nb : 1;  // table entries
   const int dipole = p ? p->dipole : MUSE_DIPOLE_TILTED;
   B.ntb = (s.N + muse::kBwKeyTile - 1) / muse::kBwKeyTile;
-  B.g_logz = L.take(BH * Cq * Ck * f);
-  B.g_k = L.take(BH * Cq * Ck * D * f);
-  B.g_v = L.take(BH * Cq * Ck * D * f);
-  B.g_dip = L.take(BH * Cq * D * D * f);
-  B.P = L.take(BH * Cq * Ck * f);
-  B.lz = L.take(BH * Cq * f);
-  B.dKp = L.take(BH * Cq * Ck * D * f);
-  B.dVp = L.take(BH * Cq * Ck * D * f);
-  B.dP = L.take(BH * Cq * Ck * f);
-  B.dlogz = L.take(BH * Cq * Ck * f);
-  B.sij = L.take(BH * Cq * Ck * f);
+  B.g_logz = L.take(BH * E * Cq * Ck * f);
+  B.g_k = L.take(BH * E * Cq * Ck * D * f);
+  B.g_v = L.take(BH * E * Cq * Ck * D * f);
+  B.g_dip = L.take(BH * E * Cq * D * D * f);
+  B.P = L.take(BH * E * Cq * Ck * f);
+  B.lz = L.take(BH * E * Cq * f);
+  B.dKp = L.take(BH * E * Cq * Ck * D * f);
+  B.dVp = L.take(BH * E * Cq * Ck * D * f);
+  B.dlogz = L.take(BH * E * Cq * Ck * f);
+  if (!s.causal) {
+    B.dP = L.take(BH * Cq * Ck * f);
+    B.sij = L.take(BH * Cq * Ck * f);
+  } else {
+    B.sdk = L.take(BH * E * Cq * Ck * D * f);
+    B.sdv = L.take(BH * E * Cq * Ck * D * f);
+    B.st = L.take(BH * E * Cq * Ck * f);
+    B.o_loc = L.take(BH * N * D * f);
+    B.l_loc = L.take(BH * N * f);
+    B.delta_loc = L.take(BH * N * f);
+  }
   if (dipole == MUSE_DIPOLE_TILTED) {
-    B.gd = L.take(BH * Cq * 4 * D * D * sizeof(uint16_t));
-    B.vgk = L.take(BH * Cq * Ck * f);
+    B.gd = L.take(BH * E * Cq * 4 * D * D * sizeof(uint16_t));
+    B.vgk = L.take(BH * E * Cq * Ck * f);
     B.A = L.take(BH * Cq * N * f);
     B.Q = L.take(BH * Cq * N * f);
-    B.WQ = L.take(BH * Cq * N * f);
+    if (!s.causal) B.WQ = L.take(BH * Cq * N * f);
   }
   if (dipole == MUSE_DIPOLE_UNTILTED) {
     B.dcov = L.take(BH * Ck * D * D * f);
@@ -615,7 +627,7 @@ BwPlan make_bwd_plan(const Shape& s, const muse_fwd_params* p) {
     B.vmean = L.take(BH * Ck * D * f);
   }
   B.dqbar1 = L.take(BH * Cq * D * f);
-  B.dqbar2 = L.take(BH * Cq * D * f);
+  B.dqbar2 = L.take(BH * E * Cq * D * f);
   B.dqbar_part = L.take(BH * static_cast<size_t>(B.ntb) * Cq * D * f);
   B.total = L.bytes;
   return B;
@@ -644,6 +656,51 @@ int run_muse_bwd(const void* q, const void* k, const void* v, const void* dout, 
   a1.t_khi = a1.t_klo = a1.t_vhi = a1.t_vlo = a1.t_dip = nullptr;
   e = launch_stage1(a1, s.dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
+  // causal calls: the forward's far field and in-block exact part, in fp32 arithmetic (the
+  // vector-ALU paths, which take the fp32 tables), kept apart for the merge's backward
+  const int valu_dtype = s.dtype == MUSE_BF16 ? 2 : 0;
+  if (s.causal) {
+    S2Args a2{};
+    a2.q = q;
+    a2.BH = s.BH;
+    a2.N = s.N;
+    a2.D = s.D;
+    a2.Cq = s.Cq;
+    a2.Ck = s.Ck;
+    a2.causal = 1;
+    a2.block = s.block;
+    a2.nbS = s.nbS;
+    a2.scale = scale;
+    a2.dipole = dipole;
+    a2.labels_q = km.t[0].labels;
+    a2.qbar = km.t[0].cent;
+    a2.s_logz = a1.s_logz;
+    a2.s_k = a1.s_k;
+    a2.s_v = a1.s_v;
+    a2.s_dip = a1.s_dip;
+    a2.perm_q = km.t[0].perm;
+    a2.offs_q = km.t[0].offs;
+    a2.nb = s.nb;
+    a2.o_far = at<float>(ws, P.o_far);
+    a2.l_far = at<float>(ws, P.l_far);
+    e = launch_stage2(a2, valu_dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "stage-2 launch");
+    ExactArgs ax{};
+    ax.q = q;
+    ax.k = k;
+    ax.v = v;
+    ax.out = at<float>(ws, B.o_loc);
+    ax.lse_out = at<float>(ws, B.l_loc);
+    ax.BH = s.BH;
+    ax.N = s.N;
+    ax.D = s.D;
+    ax.causal = 1;
+    ax.block = s.block;
+    ax.scale = scale;
+    ax.out_bf16 = 0;
+    e = launch_exact(ax, valu_dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "local block launch");
+  }
   BwArgs b{};
   b.q = q;
   b.k = k;
@@ -678,15 +735,29 @@ int run_muse_bwd(const void* q, const void* k, const void* v, const void* dout, 
   b.lz = at<float>(ws, B.lz);
   b.dKp = at<float>(ws, B.dKp);
   b.dVp = at<float>(ws, B.dVp);
-  b.dP = at<float>(ws, B.dP);
   b.dlogz = at<float>(ws, B.dlogz);
-  b.sij = at<float>(ws, B.sij);
+  if (!s.causal) {
+    b.dP = at<float>(ws, B.dP);
+    b.sij = at<float>(ws, B.sij);
+  } else {
+    b.causal = 1;
+    b.nb = s.nb;
+    b.block = s.block;
+    b.o_loc = at<float>(ws, B.o_loc);
+    b.l_loc = at<float>(ws, B.l_loc);
+    b.delta_loc = at<float>(ws, B.delta_loc);
+    b.o_far = at<float>(ws, P.o_far);
+    b.l_far = at<float>(ws, P.l_far);
+    b.sdk = at<float>(ws, B.sdk);
+    b.sdv = at<float>(ws, B.sdv);
+    b.st = at<float>(ws, B.st);
+  }
   if (dipole == MUSE_DIPOLE_TILTED) {
     b.gd = at<uint16_t>(ws, B.gd);
     b.vgk = at<float>(ws, B.vgk);
     b.A = at<float>(ws, B.A);
     b.Q = at<float>(ws, B.Q);
-    b.WQ = at<float>(ws, B.WQ);
+    if (!s.causal) b.WQ = at<float>(ws, B.WQ);
   }
   if (dipole == MUSE_DIPOLE_UNTILTED) {
     b.dcov = at<float>(ws, B.dcov);

@@ -233,7 +233,7 @@ struct ExactArgs {
 
 hipError_t launch_exact(const ExactArgs& a, int dtype, hipStream_t s);
 
-// ------------------------------------------------------------------ backward (acausal)
+// ------------------------------------------------------------------ backward
 
 constexpr int kBwD = 64;       // head dimension of the backward kernels
 constexpr int kBwKeyTile = 64; // keys per tile of the per-key backward pass
@@ -285,6 +285,21 @@ struct BwArgs {
   float* dqbar2;               // [BH, Cq, D] stage-2 part
   float* dqbar_part;           // [BH, ntb, Cq, D] per key tile: s sum_m w dL/dw k_m
   int ntb;                     // key tiles of kBwKeyTile positions
+  // causal calls: table entry b (b >= 1) covers the key blocks before b; the summary
+  // arrays above then hold one entry per block ([BH, nb, Cq, ...]); the far field is
+  // merged with the exact attention inside each block by log-sum-exp
+  int causal, nb, block;
+  float* o_loc;                // [BH, N, D] exact in-block output (fp32), then dL/d(it) in place
+  float* l_loc;                // [BH, N] its log normaliser
+  float* delta_loc;            // [BH, N] dL/do_loc . o_loc - dL/dl_loc
+  float* o_far;                // [BH, N, D] far-field output (fp32), then dL/d(it) in place
+  float* l_far;                // [BH, N] its log normaliser, then dL/d(it) in place
+  // suffix tables over the entries after block b' (scaled relative to entry b' + 1)
+  float* sdk;                  // [BH, nb, Cq, Ck, D] sum_{b > b'} exp(logZ^{b'+1} - logZ^b) dK'^b
+  float* sdv;                  // [BH, nb, Cq, Ck, D]
+  float* st;                   // [BH, nb, Cq, Ck] the same of dL/dlog Z^b - S^b
+  // (tilted) gd then holds, per (b', i), sh = sum_{b > b'} exp(lz^{b'+1} - lz^b) G_Dip^b
+  // in the same four bf16 layouts ([BH, nb, Cq, 4, D, D])
 };
 
 hipError_t launch_backward(const BwArgs& a, int dtype, hipStream_t s);

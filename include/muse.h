@@ -215,7 +215,7 @@ int muse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out
                           int dtype, void* hip_stream, const muse_fwd_params* p);
 
 /*
- * Backward pass of the acausal MuSe forward: the vector-Jacobian products dq, dk, dv of
+ * Backward pass of the MuSe forward: the vector-Jacobian products dq, dk, dv of
  * muse_attn_fwd_ex's output o(q, k, v) for an upstream gradient dout = dLoss/do. The
  * reviews note that the method's backward pass uses the same approximations as its
  * forward and that its gradient error was never measured (pith.science review, "Reading
@@ -224,7 +224,12 @@ int muse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out
  * has no gradient). The query centroids are the member means of labels_q and pass their
  * gradient to every member; stage 1 (log Z_ij, the tilted means K_ij and V_ij, P_ij and
  * the dipole D_i, tilted or untilted as p->dipole says) and stage 2 (the refinement) are
- * differentiated exactly; the no-dipole mode drops D_i from both.
+ * differentiated exactly; the no-dipole mode drops D_i from both. Causal calls (the
+ * prefix form: block b's far field summarises the keys of blocks < b, merged by
+ * log-sum-exp with exact attention inside the block; gist.science summary,
+ * Kernmechanismen 3; pith.science review, caption of Figure 2) differentiate the merge,
+ * the exact in-block attention, and every block's table entry, whose gradients reach the
+ * keys of the earlier blocks.
  *   q, k, v, dout   device [B,H,N,D] in dtype (MUSE_F32 or MUSE_BF16), as in the forward
  *   labels_q/_k     device int32 [B,H,N]: the forward call's final labels (the last row
  *                   of labels_*_trace, or the labels_*_in it was given); values outside
@@ -235,8 +240,10 @@ int muse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out
  *                   and workspace_bytes as in muse_attn_fwd_ex, sized by
  *                   muse_attn_bwd_workspace_bytes. Every other field keeps its default
  *                   (MUSE_ERR_INVALID_ARG for the forward's output pointers).
- * Implemented for causal = 0 and D = 64; causal calls, other head sizes, retrieval, the
- * hierarchy and the cluster size cap return MUSE_ERR_UNSUPPORTED before any launch. All
+ * Implemented for D = 64, acausal (every dipole mode) and causal (tilted dipole or none)
+ * with the forward's block rules; other head sizes, the untilted dipole with causal = 1,
+ * retrieval, the hierarchy and the cluster size cap return MUSE_ERR_UNSUPPORTED before
+ * any launch. All
  * arithmetic in fp32 (bf16 inputs are exact in it); results are deterministic (fixed
  * summation orders, no floating-point atomics). Work is queued on hip_stream.
  */

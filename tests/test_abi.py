@@ -242,8 +242,15 @@ def test_backward_entry_rejects_before_launch(lib):
                                  None if pp is None else ctypes.byref(pp))
 
     assert lib.muse_attn_bwd_workspace_bytes(4, 8, 8192, 64, 32, 128, 0, 0, 1, None) > 0
-    assert call(causal=1, block=256) == -2 and "acausal" in lib.muse_last_error().decode()
-    assert lib.muse_attn_bwd_workspace_bytes(1, 1, 1024, 64, 8, 32, 1, 256, 1, None) == 0
+    # causal calls: the tilted dipole or none, with the forward's block rules
+    causal_ws = lib.muse_attn_bwd_workspace_bytes(1, 1, 1024, 64, 8, 32, 1, 256, 1, None)
+    assert causal_ws > lib.muse_attn_bwd_workspace_bytes(1, 1, 1024, 64, 8, 32, 0, 0, 1, None)
+    assert call(causal=1, block=100) == -1                      # block must divide N
+    assert call(causal=1, block=32) == -2                       # blocks below 64 keys
+    p.dipole = 2
+    assert call(causal=1, block=256, pp=p) == -2 and "causal" in lib.muse_last_error().decode()
+    assert lib.muse_attn_bwd_workspace_bytes(1, 1, 1024, 64, 8, 32, 1, 256, 1, ctypes.byref(p)) == 0
+    p.dipole = 1
     assert call(D=128) == -2
     assert call(ins=ins[:4] + (None, vp(6))) == -1  # labels are required
     assert call(outs=(vp(7), vp(7), vp(9))) == -1   # distinct outputs
