@@ -165,16 +165,31 @@ def kernel_work(name: str, cfg, hier: bool = False, ctx: dict = None):
                                2.0 * BH * nb * Cq * Ck * D * D + 2.0 * BH * nb * Ck * D * D),
         # acausal general-path tables from whole atoms
         "s1_tables": (table * (2 + 2 * D) * 4 + ftab, 0.0),
-        # backward (acausal): stage 2 per query cluster (q, dout read; dq written; tables read;
-        # summary gradients written), q.K, g.V, p g, dl q, dl K, g D, g q per query
-        "bw_refine": (2 * x + BH * N * D * 4 + 2 * (ftab + dip32), 2.0 * BH * N * (5 * Ck * D + 2 * D * D)),
+        # backward: stage 2 per query cluster (q and dout read, causal: the far field's fp32
+        # share of dout; dq written; tables read; summary gradients written), q.K, g.V, p g,
+        # dl q, dl K, g D, g q per query
+        "bw_refine": (x + (BH * N * (D + 1) * 4 if cfg.causal else x) + BH * N * D * 4 + 2 * (ftab + dip32),
+                      2.0 * BH * N * (5 * Ck * D + 2 * D * D)),
         # tilted: per (query cluster, key) G k and G^T v on the matrix cores; keys, values,
         # a_im and G (bf16 hi/lo, both layouts) read, Q and w Q written, the dk and dv terms written
-        "bw_keys_a": (2 * x + 3 * BH * Cq * N * 4 + BH * Cq * 4 * D * D * 2 + 2 * BH * N * D * 4,
-                      4.0 * BH * Cq * N * D * D),
+        "bw_keys_a": (2 * x + (2 if cfg.causal else 3) * BH * Cq * N * 4 + BH * nb * Cq * 4 * D * D * 2
+                      + 2 * BH * N * D * 4, 4.0 * BH * Cq * (N - blk if cfg.causal else N) * D * D),
         # per (query cluster, key): a_im, dL/dw, the dk and dv updates and the tile partials
         "bw_keys_b": (2 * x + 4 * BH * N * D * 4 + 2 * table * D * 4 + 4 * table * 4 + BH * Cq * N * 4
                       + BH * (-(-N // 64)) * Cq * D * 4, 14.0 * BH * N * Cq * D),
+        # causal backward: the merge (both partial outputs and the upstream gradient read,
+        # their gradients written in place), the suffix sums (dK', dV' of every entry read,
+        # sdk, sdv written; G_Dip of every entry read, its four bf16 copies written)
+        "bw_merge": (x + 4 * BH * N * D * 4 + 4 * BH * N * 4, 0.0),
+        "bw_suffix": (4 * table * D * 4 + 3 * table * 4, 0.0),
+        "bw_suffix_dip": (BH * nb * Cq * D * D * (4 + 8), 0.0),
+        # exact in-block backward over the 64 x 64 tile pairs on or below the diagonal:
+        # q.k, g.v, p g, dS q per pair (keys' pass) and q.k, g.v, dS k (queries' pass); inputs,
+        # dL/do_loc and the gradients read once, dk, dv (dq) updated
+        "bw_local_kv": (3 * x + BH * N * D * 4 + 4 * BH * N * D * 4 + 2 * BH * N * 4,
+                        8.0 * 64 ** 3 * BH * nb * (blk // 64) * (blk // 64 + 1) // 2),
+        "bw_local_q": (3 * x + BH * N * D * 4 + 2 * BH * N * D * 4 + 2 * BH * N * 4,
+                       6.0 * 64 ** 3 * BH * nb * (blk // 64) * (blk // 64 + 1) // 2),
     }
     if cfg.topk_clusters and ctx is not None:
         k1, k2 = cfg.topk_clusters, cfg.topk_blocks
@@ -197,7 +212,7 @@ def kernel_work(name: str, cfg, hier: bool = False, ctx: dict = None):
 
 
 # kernels whose arithmetic runs on the vector ALUs in fp32 (priced against the vector peak)
-ALU_KERNELS = ("bw_refine", "bw_keys_b")
+ALU_KERNELS = ("bw_refine", "bw_keys_b", "bw_local_kv", "bw_local_q")
 
 
 def roofline_entry(name: str, cfg, avg_s: float, hier: bool = False, ctx: dict = None):
@@ -578,21 +593,22 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
             # the hierarchical block decomposition (one two-stage approximation per square
             # below the diagonal, log-sum-exp merged)
             variant("hierarchy", cfg.iters, lambda n: True, hierarchy=True)
-    if not cfg.causal and cfg.D == 64:
+    if cfg.D == 64 and cfg.topk_clusters == 0 and not hierarchy:
         # the backward pass (dq, dk, dv for an upstream gradient, labels of one forward call
         # held fixed), timed like the forward step
-        _, ex_b = binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, return_trace=True)
+        _, ex_b = binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=cfg.causal, block=cfg.block,
+                                   return_trace=True)
         lq = ex_b["labels_q_trace"][-1].contiguous()
         lk = ex_b["labels_k_trace"][-1].contiguous()
         del ex_b
         gen = torch.Generator(device="cuda").manual_seed(11)
         dO = torch.randn(Q.shape, generator=gen, device="cuda", dtype=torch.float32).to(Q.dtype)
-        ws_b = torch.empty(binding.bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, False, 0,
-                                                       1 if cfg.dtype == "bf16" else 0),
+        ws_b = torch.empty(binding.bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.D, cfg.Cq, cfg.Ck, cfg.causal,
+                                                       cfg.block, 1 if cfg.dtype == "bf16" else 0),
                            dtype=torch.uint8, device="cuda")
 
         def bwd_step():
-            binding.attn_bwd(Q, K, V, dO, lq, lk, cfg.Cq, cfg.Ck, workspace=ws_b)
+            binding.attn_bwd(Q, K, V, dO, lq, lk, cfg.Cq, cfg.Ck, causal=cfg.causal, block=cfg.block, workspace=ws_b)
 
         ms_b, _ = timed(bwd_step, steps, warmup)
         binding.prof_reset()

@@ -117,7 +117,10 @@ __global__ void __launch_bounds__(kExThreads) exact_valu_kernel(ExactArgs a) {
   }
 }
 
-template <int D>
+// EXACT_P: the weights enter the product with V as bf16 hi + lo and the normaliser as
+// their fp32 sum (output accurate to fp32 rounding; one more product per step), for the
+// backward pass's recomputation of the forward.
+template <int D, bool EXACT_P>
 __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt) {
   constexpr int BQ = 128, BK = 64;
   constexpr int KST = D + 16;  // bf16 elements per K and V row in LDS (padded)
@@ -284,15 +287,29 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
           float pv[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(scur[t][8 * ss + i], sl2, nb));
-          const bf16x8_t bfr = pack_bf16x8(pv);
+          if constexpr (EXACT_P) {
+            // the weights as bf16 hi + lo (fp32-accurate products with V) and their fp32 sum
+            bf16x8_t ph, pl;
+            split_bf16x8(pv, ph, pl);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bf16x2_t p2 = {bfr[2 * i], bfr[2 * i + 1]};
-            l = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l, false);
+            for (int i = 0; i < 8; ++i) l += pv[i];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+              const bf16x8_t vt = lds_operand_tr_acc(sv, KST, 32 * t + 16 * ss, 32 * mt, lane);
+              o[mt] = mfma32(vt, ph, o[mt]);
+              o[mt] = mfma32(vt, pl, o[mt]);
+            }
+          } else {
+            const bf16x8_t bfr = pack_bf16x8(pv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bf16x2_t p2 = {bfr[2 * i], bfr[2 * i + 1]};
+              l = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l, false);
+            }
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+              o[mt] = mfma32(lds_operand_tr_acc(sv, KST, 32 * t + 16 * ss, 32 * mt, lane), bfr, o[mt]);
           }
-#pragma unroll
-          for (int mt = 0; mt < NMT; ++mt)
-            o[mt] = mfma32(lds_operand_tr_acc(sv, KST, 32 * t + 16 * ss, 32 * mt, lane), bfr, o[mt]);
         }
     } else {
       scores(sK[(j + 1) & 1], snxt);
@@ -356,8 +373,14 @@ hipError_t launch_exact(const ExactArgs& a, int dtype, hipStream_t s) {
   if (dtype == 1) {
     const int nqt = (a.N + 127) / 128;
     ProfScope ps_(a.block > 0 ? "local_block_mfma" : "exact_mfma", s);
-    if (a.D == 64) hipLaunchKernelGGL((flash_bf16_kernel<64>), dim3(nqt * a.BH), dim3(256), 0, s, a, nqt);
-    else hipLaunchKernelGGL((flash_bf16_kernel<128>), dim3(nqt * a.BH), dim3(256), 0, s, a, nqt);
+    const dim3 g(nqt * a.BH);
+    if (a.exact_p) {
+      if (a.D == 64) hipLaunchKernelGGL((flash_bf16_kernel<64, true>), g, dim3(256), 0, s, a, nqt);
+      else hipLaunchKernelGGL((flash_bf16_kernel<128, true>), g, dim3(256), 0, s, a, nqt);
+    } else {
+      if (a.D == 64) hipLaunchKernelGGL((flash_bf16_kernel<64, false>), g, dim3(256), 0, s, a, nqt);
+      else hipLaunchKernelGGL((flash_bf16_kernel<128, false>), g, dim3(256), 0, s, a, nqt);
+    }
     return hipGetLastError();
   }
   ProfScope ps_(a.block > 0 ? "local_block_exact" : "exact_valu", s);

@@ -656,9 +656,19 @@ int run_muse_bwd(const void* q, const void* k, const void* v, const void* dout, 
   a1.t_khi = a1.t_klo = a1.t_vhi = a1.t_vlo = a1.t_dip = nullptr;
   e = launch_stage1(a1, s.dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
-  // causal calls: the forward's far field and in-block exact part, in fp32 arithmetic (the
-  // vector-ALU paths, which take the fp32 tables), kept apart for the merge's backward
-  const int valu_dtype = s.dtype == MUSE_BF16 ? 2 : 0;
+  // causal calls: the forward's far field and in-block exact part, kept apart for the
+  // merge's backward; bf16 inputs take the forward's own matrix-core kernels (the far field
+  // from bf16 hi/lo copies of the fp32 tables), fp32 inputs the vector-ALU ones
+  const bool mf = s.dtype == MUSE_BF16;
+  if (s.causal && mf) {
+    a1.t_khi = at<uint16_t>(ws, P.t_khi);
+    a1.t_klo = at<uint16_t>(ws, P.t_klo);
+    a1.t_vhi = at<uint16_t>(ws, P.t_vhi);
+    a1.t_vlo = at<uint16_t>(ws, P.t_vlo);
+    a1.t_dip = at<uint16_t>(ws, P.t_dip);
+    e = launch_stage1_pack(a1, stream);
+    if (e != hipSuccess) return hip_fail(e, "table packing launch");
+  }
   if (s.causal) {
     S2Args a2{};
     a2.q = q;
@@ -678,12 +688,22 @@ int run_muse_bwd(const void* q, const void* k, const void* v, const void* dout, 
     a2.s_k = a1.s_k;
     a2.s_v = a1.s_v;
     a2.s_dip = a1.s_dip;
+    a2.t_khi = a1.t_khi;
+    a2.t_klo = a1.t_klo;
+    a2.t_vhi = a1.t_vhi;
+    a2.t_vlo = a1.t_vlo;
+    a2.t_dip = a1.t_dip;
     a2.perm_q = km.t[0].perm;
     a2.offs_q = km.t[0].offs;
     a2.nb = s.nb;
+    if (mf) {
+      a2.tiles = at<int2>(ws, P.tiles);
+      a2.ntiles = at<int32_t>(ws, P.ntiles);
+      a2.max_tiles = P.max_tiles;
+    }
     a2.o_far = at<float>(ws, P.o_far);
     a2.l_far = at<float>(ws, P.l_far);
-    e = launch_stage2(a2, valu_dtype, stream);
+    e = launch_stage2(a2, s.dtype, stream);
     if (e != hipSuccess) return hip_fail(e, "stage-2 launch");
     ExactArgs ax{};
     ax.q = q;
@@ -698,7 +718,8 @@ int run_muse_bwd(const void* q, const void* k, const void* v, const void* dout, 
     ax.block = s.block;
     ax.scale = scale;
     ax.out_bf16 = 0;
-    e = launch_exact(ax, valu_dtype, stream);
+    ax.exact_p = 1;
+    e = launch_exact(ax, s.dtype, stream);
     if (e != hipSuccess) return hip_fail(e, "local block launch");
   }
   BwArgs b{};

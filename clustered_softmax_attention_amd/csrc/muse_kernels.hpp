@@ -175,6 +175,8 @@ struct S1Args {
 };
 
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s);
+// bf16 hi/lo copies (t_*) of fp32 tables already built (s_logz, s_k, s_v, s_dip)
+hipError_t launch_stage1_pack(const S1Args& a, hipStream_t s);
 void launch_stage1_mfma(const S1Args& a, int which, hipStream_t s);  // 0 scores, 1 atoms (+ merge), 2 moments, 3 finalise, 4 scan, 5 general-path dipole
 
 // ------------------------------------------------------------------ stage 2
@@ -229,6 +231,7 @@ struct ExactArgs {
   int block;                   // > 0: keys restricted to the query's own block (local)
   float scale;
   int out_bf16;
+  int exact_p;                 // bf16 path: weights as bf16 hi + lo in the product with V
 };
 
 hipError_t launch_exact(const ExactArgs& a, int dtype, hipStream_t s);

@@ -1082,6 +1082,12 @@ static void launch_stage1_t(const S1Args& a, hipStream_t s) {
   }
 }
 
+hipError_t launch_stage1_pack(const S1Args& a, hipStream_t s) {
+  ProfScope ps_("s1_pack", s);
+  hipLaunchKernelGGL(s1_pack_kernel, dim3(a.Cq, a.nbS, a.BH), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_stage1(const S1Args& a, int dtype, hipStream_t s) {
   if (dtype == 0) {
     if (a.D == 64) launch_stage1_t<float, 64>(a, s);
