@@ -1167,6 +1167,213 @@ __global__ void __launch_bounds__(256) bw_local_q_kernel(BwArgs a) {
   }
 }
 
+// The same on the matrix cores (bf16 inputs): 32 x 32 x 16 bf16 products with fp32
+// accumulation; the fp32 operands (dL/do_loc, P, dS) enter as bf16 hi + lo, so every
+// product is fp32-accurate (hi hi + hi lo + lo hi where both operands are fp32). A
+// workgroup of two waves takes 64 positions, a wave 32 of them.
+// bw_local_kv_mfma: a wave's 32 keys m (K and V rows in registers) over the query tiles of
+// the block from the diagonal on (Q rows, dL/do_loc as hi and lo, L_loc, delta staged in
+// LDS). Per 32-query chunk: S = Q K^T and dP = G V^T with queries as rows (a lane holds
+// its key's column), P and dS elementwise, then dV^T += G^T P and dK^T += Q^T dS with the
+// accumulators as B operands and G^T, Q^T read by the LDS transpose read.
+constexpr int kLocST = kBwD + 8;  // bf16 row stride of the staged tiles (16-byte aligned rows)
+
+__global__ void __launch_bounds__(128) bw_local_kv_mfma_kernel(BwArgs a) {
+  constexpr int D = kBwD, ST = kLocST, NKS = D / 16, NMT = D / 32, TT = 64;
+  __shared__ __align__(16) uint16_t sQ[TT * ST], sGh[TT * ST], sGl[TT * ST];
+  __shared__ float sL[TT], sDel[TT];
+  const int bh = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int N = a.N, m0 = blockIdx.x * TT, bend = (m0 / a.block + 1) * a.block;
+  const int mk = m0 + 32 * wave + c;  // this lane's key
+  const size_t base = static_cast<size_t>(bh) * N;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + base * D;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + base * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + base * D;
+  const float* G = a.o_loc + base * D;  // dL/do_loc
+  const float sl2 = a.scale * 1.4426950408889634f;
+  bf16x8_t kb[NKS], vb[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    kb[ks] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(mk) * D + 16 * ks + 8 * h));
+    vb[ks] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(V + static_cast<size_t>(mk) * D + 16 * ks + 8 * h));
+  }
+  f32x16_t dvt[NMT], dkt[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) dvt[mt] = dkt[mt] = zero16();
+  for (int n0 = m0; n0 < bend; n0 += TT) {
+    __syncthreads();  // the previous query tile is consumed
+    // Q rows (bf16) and G rows (fp32 -> hi, lo): 16-byte pieces, 8 bf16 / 4 floats each
+#pragma unroll
+    for (int q = 0; q < TT * D / 8 / 128; ++q) {
+      const int e = tid + 128 * q, r = e / (D / 8), cc = e % (D / 8);
+      *reinterpret_cast<u16x8_t*>(&sQ[r * ST + 8 * cc]) =
+          *reinterpret_cast<const u16x8_t*>(Q + static_cast<size_t>(n0 + r) * D + 8 * cc);
+    }
+#pragma unroll
+    for (int q = 0; q < TT * D / 4 / 128; ++q) {
+      const int e = tid + 128 * q, r = e / (D / 4), cc = e % (D / 4);
+      const f32x4_t g4 = *reinterpret_cast<const f32x4_t*>(G + static_cast<size_t>(n0 + r) * D + 4 * cc);
+      u16x4_t hi, lo;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        hi[u] = f32_to_bf16_bits(g4[u]);
+        lo[u] = f32_to_bf16_bits(g4[u] - bf16_to_f32(hi[u]));
+      }
+      *reinterpret_cast<u16x4_t*>(&sGh[r * ST + 4 * cc]) = hi;
+      *reinterpret_cast<u16x4_t*>(&sGl[r * ST + 4 * cc]) = lo;
+    }
+    if (tid < TT) {
+      sL[tid] = a.l_loc[base + n0 + tid];
+      sDel[tid] = a.delta_loc[base + n0 + tid];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+      if (n0 + 32 * qc + 31 < m0 + 32 * wave) continue;  // every query of the chunk precedes the wave's keys
+      f32x16_t sc = zero16(), dp = zero16();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int o = (32 * qc + c) * ST + 16 * ks + 8 * h;
+        sc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8_t*>(&sQ[o])), kb[ks], sc);
+        dp = mfma32(as_bf16x8(*reinterpret_cast<const u16x8_t*>(&sGh[o])), vb[ks], dp);
+        dp = mfma32(as_bf16x8(*reinterpret_cast<const u16x8_t*>(&sGl[o])), vb[ks], dp);
+      }
+      // P and dS: element v is query row 8 (v / 4) + 4 h + v % 4 of the chunk, key mk
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 32 * qc + 8 * (v >> 2) + 4 * h + (v & 3);
+        const float p = (mk <= n0 + r) ? fast_exp2(fmaf(sc[v], sl2, -sL[r] * 1.4426950408889634f)) : 0.f;
+        pv[v] = p;
+        dsv[v] = p * (dp[v] - sDel[r]);
+      }
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        bf16x8_t ph, pl, dh, dl;
+        split_bf16x8(pv + 8 * ss, ph, pl);
+        split_bf16x8(dsv + 8 * ss, dh, dl);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          const bf16x8_t gth = lds_operand_tr_acc(sGh, ST, 32 * qc + 16 * ss, 32 * mt, lane);
+          const bf16x8_t gtl = lds_operand_tr_acc(sGl, ST, 32 * qc + 16 * ss, 32 * mt, lane);
+          const bf16x8_t qt = lds_operand_tr_acc(sQ, ST, 32 * qc + 16 * ss, 32 * mt, lane);
+          dvt[mt] = mfma32(gth, ph, dvt[mt]);
+          dvt[mt] = mfma32(gth, pl, dvt[mt]);
+          dvt[mt] = mfma32(gtl, ph, dvt[mt]);
+          dkt[mt] = mfma32(qt, dh, dkt[mt]);
+          dkt[mt] = mfma32(qt, dl, dkt[mt]);
+        }
+      }
+    }
+  }
+  // dV^T and dK^T: this lane's key mk, dimensions 32 mt + 8 g + 4 h + 0..3
+  float* dkr = a.dk + (base + mk) * D;
+  float* dvr = a.dv + (base + mk) * D;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * mt + 8 * g + 4 * h;
+      f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(dkr + d0);
+      f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(dvr + d0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        k4[u] = fmaf(a.scale, dkt[mt][4 * g + u], k4[u]);
+        v4[u] += dvt[mt][4 * g + u];
+      }
+      *reinterpret_cast<f32x4_t*>(dkr + d0) = k4;
+      *reinterpret_cast<f32x4_t*>(dvr + d0) = v4;
+    }
+}
+
+// bw_local_q_mfma: a wave's 32 queries n (Q rows and dL/do_loc as hi and lo in registers,
+// L_loc and delta of the lane's query) over the key tiles of the block up to the diagonal
+// (K and V rows staged in LDS). Per 32-key chunk: S^T = K Q^T and dP^T = V G^T with keys
+// as rows (a lane holds its query's column), P^T and dS^T elementwise, then
+// dQ^T += K^T dS^T with dS^T as the B operand and K^T read by the LDS transpose read.
+__global__ void __launch_bounds__(128) bw_local_q_mfma_kernel(BwArgs a) {
+  constexpr int D = kBwD, ST = kLocST, NKS = D / 16, NMT = D / 32, TT = 64;
+  __shared__ __align__(16) uint16_t sK[TT * ST], sV[TT * ST];
+  const int bh = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int N = a.N, n0 = blockIdx.x * TT, bbeg = (n0 / a.block) * a.block;
+  const int nq = n0 + 32 * wave + c;  // this lane's query
+  const size_t base = static_cast<size_t>(bh) * N;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + base * D;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + base * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + base * D;
+  const float* G = a.o_loc + base * D;
+  const float sl2 = a.scale * 1.4426950408889634f;
+  bf16x8_t qb[NKS], gh[NKS], gl[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qb[ks] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(Q + static_cast<size_t>(nq) * D + 16 * ks + 8 * h));
+    float g8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) g8[u] = G[static_cast<size_t>(nq) * D + 16 * ks + 8 * h + u];
+    split_bf16x8(g8, gh[ks], gl[ks]);
+  }
+  const float lq = a.l_loc[base + nq] * 1.4426950408889634f, dq_del = a.delta_loc[base + nq];
+  f32x16_t acc[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) acc[mt] = zero16();
+  for (int m0 = bbeg; m0 <= n0; m0 += TT) {
+    __syncthreads();  // the previous key tile is consumed
+#pragma unroll
+    for (int q = 0; q < TT * D / 8 / 128; ++q) {
+      const int e = tid + 128 * q, r = e / (D / 8), cc = e % (D / 8);
+      *reinterpret_cast<u16x8_t*>(&sK[r * ST + 8 * cc]) =
+          *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(m0 + r) * D + 8 * cc);
+      *reinterpret_cast<u16x8_t*>(&sV[r * ST + 8 * cc]) =
+          *reinterpret_cast<const u16x8_t*>(V + static_cast<size_t>(m0 + r) * D + 8 * cc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      if (m0 + 32 * kc > n0 + 32 * wave + 31) continue;  // every key of the chunk follows the wave's queries
+      f32x16_t st = zero16(), dpt = zero16();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int o = (32 * kc + c) * ST + 16 * ks + 8 * h;
+        const bf16x8_t kr = as_bf16x8(*reinterpret_cast<const u16x8_t*>(&sK[o]));
+        const bf16x8_t vr = as_bf16x8(*reinterpret_cast<const u16x8_t*>(&sV[o]));
+        st = mfma32(kr, qb[ks], st);
+        dpt = mfma32(vr, gh[ks], dpt);
+        dpt = mfma32(vr, gl[ks], dpt);
+      }
+      // P^T and dS^T: element v is key row 8 (v / 4) + 4 h + v % 4 of the chunk, query nq
+      float dsv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int mkey = m0 + 32 * kc + 8 * (v >> 2) + 4 * h + (v & 3);
+        const float p = (mkey <= nq) ? fast_exp2(fmaf(st[v], sl2, -lq)) : 0.f;
+        dsv[v] = p * (dpt[v] - dq_del);
+      }
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        bf16x8_t dh, dl;
+        split_bf16x8(dsv + 8 * ss, dh, dl);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          const bf16x8_t kt = lds_operand_tr_acc(sK, ST, 32 * kc + 16 * ss, 32 * mt, lane);
+          acc[mt] = mfma32(kt, dh, acc[mt]);
+          acc[mt] = mfma32(kt, dl, acc[mt]);
+        }
+      }
+    }
+  }
+  float* dqr = a.dq + (base + nq) * D;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * mt + 8 * g + 4 * h;
+      f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(dqr + d0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q4[u] = fmaf(a.scale, acc[mt][4 * g + u], q4[u]);
+      *reinterpret_cast<f32x4_t*>(dqr + d0) = q4;
+    }
+}
+
 template <typename T>
 static void launch_backward_t(const BwArgs& a, hipStream_t s) {
   const int nbS = a.causal ? a.nb : 1;
@@ -1228,12 +1435,15 @@ static void launch_backward_t(const BwArgs& a, hipStream_t s) {
   }
   if (a.causal) {
     const dim3 gl(a.N / kLocT, a.BH);
+    constexpr bool MF = sizeof(T) == 2;
     {
-      ProfScope ps_("bw_local_kv", s);
-      hipLaunchKernelGGL((bw_local_kv_kernel<T>), gl, dim3(256), 0, s, a);
+      ProfScope ps_(MF ? "bw_local_kv_mfma" : "bw_local_kv", s);
+      if (MF) hipLaunchKernelGGL(bw_local_kv_mfma_kernel, gl, dim3(128), 0, s, a);
+      else hipLaunchKernelGGL((bw_local_kv_kernel<T>), gl, dim3(256), 0, s, a);
     }
-    ProfScope ps_("bw_local_q", s);
-    hipLaunchKernelGGL((bw_local_q_kernel<T>), gl, dim3(256), 0, s, a);
+    ProfScope ps_(MF ? "bw_local_q_mfma" : "bw_local_q", s);
+    if (MF) hipLaunchKernelGGL(bw_local_q_mfma_kernel, gl, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((bw_local_q_kernel<T>), gl, dim3(256), 0, s, a);
   }
 }
 
