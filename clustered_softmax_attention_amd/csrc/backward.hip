@@ -1,4 +1,4 @@
-// Backward pass of the acausal MuSe forward (gfx950).
+// Backward pass of the MuSe forward (gfx950), acausal and causal (prefix form).
 //
 // The reviews note that the method's backward pass uses the same approximations as its
 // forward and that its error was never measured (pith.science review, "Reading between
@@ -28,6 +28,16 @@
 //   bw_keys_b    per 64 keys: dL/dw_im, da_im = w_im (dL/dw_im - sum_j + dL/dlog Z_ij), the
 //                rest of dk_m and dv_m, and per tile s sum_m w dL/dw k_m for dL/dqbar.
 //   bw_centroid  per i: dL/dqbar_i, spread over the members (qbar is their mean).
+// Causal calls (block b's far field summarises the keys of blocks < b and is merged with
+// exact attention inside the block by log-sum-exp; gist.science summary, Kernmechanismen
+// 3; pith.science review, caption of Figure 2) add:
+//   bw_merge     the merge's backward: the far field's and the in-block part's shares of
+//                dL/do and dL/d(log normaliser).
+//   (per entry)  bw_refine, bw_prep_i for every (block, query cluster) against table entry
+//                b; bw_entry: dL/dlog Z - S through the dipole's aggregated form.
+//   bw_suffix    the suffix sums over the later entries that a key's gradient needs.
+//   bw_keys_a/b  against the suffix tables of the key's block.
+//   bw_local_*   the exact in-block attention's backward.
 // All arithmetic in fp32 (bf16 inputs are exact in it); the matrix-core products split
 // G_Dip (and fp32 keys and values) into bf16 hi + lo. Every sum runs in a fixed order.
 #include "mfma.hpp"
