@@ -170,6 +170,9 @@ def kernel_work(name: str, cfg, hier: bool = False, ctx: dict = None):
         # dl q, dl K, g D, g q per query
         "bw_refine": (x + (BH * N * (D + 1) * 4 if cfg.causal else x) + BH * N * D * 4 + 2 * (ftab + dip32),
                       2.0 * BH * N * (5 * Ck * D + 2 * D * D)),
+        # the same on the matrix cores (bf16 inputs)
+        "bw_refine_mfma": (x + (BH * N * (D + 1) * 4 if cfg.causal else x) + BH * N * D * 4 + 2 * (ftab + dip32),
+                           2.0 * BH * N * (5 * Ck * D + 2 * D * D)),
         # tilted: per (query cluster, key) G k and G^T v on the matrix cores; keys, values,
         # a_im and G (bf16 hi/lo, both layouts) read, Q and w Q written, the dk and dv terms written
         "bw_keys_a": (2 * x + (2 if cfg.causal else 3) * BH * Cq * N * 4 + BH * nb * Cq * 4 * D * D * 2
@@ -191,6 +194,9 @@ def kernel_work(name: str, cfg, hier: bool = False, ctx: dict = None):
         "bw_local_q": (3 * x + BH * N * D * 4 + 2 * BH * N * D * 4 + 2 * BH * N * 4,
                        6.0 * 64 ** 3 * BH * nb * (blk // 64) * (blk // 64 + 1) // 2),
     }
+    # the matrix-core versions of the in-block backward (bf16 inputs) do the same work
+    w["bw_local_kv_mfma"] = w["bw_local_kv"]
+    w["bw_local_q_mfma"] = w["bw_local_q"]
     if cfg.topk_clusters and ctx is not None:
         k1, k2 = cfg.topk_clusters, cfg.topk_blocks
         cells = BH * (nb - 1) * Cq                   # (head, i, b >= 1)

@@ -290,6 +290,305 @@ __global__ void __launch_bounds__(256) bw_refine_kernel(BwArgs a) {
   }
 }
 
+// The stage-2 backward on the matrix cores (bf16 inputs): one workgroup per bucket as
+// above, 32 queries per tile. The fp32 operands (K_i., V_i., D_i, the residuals qt, an
+// fp32 upstream gradient, p and dl) enter as bf16 hi + lo (three products where both
+// sides are fp32, so every product is fp32-accurate up to about 2^-16). Per tile:
+//   wave w (key clusters 32 w .. 32 w + 31): L^T = K qt^T and dP^T = V g^T, then the
+//     softmax over all clusters (cross-wave max and sums through LDS), p and
+//     dl = p (dp - sum_j p dp + dL) stored transposed (cluster rows) as bf16 hi, lo;
+//     dL/dV^T += g^T P and dL/dK^T += qt^T dl for its clusters (accumulators over the
+//     bucket), and dL/dlog Z partials;
+//   waves 0, 1 (dimensions 32 w ..): dq^T = K^T dl^T + D_i^T g^T;
+//   waves 2, 3: dL/dD_i += g^T qt (two 32 x 32 tiles each).
+// Operands that run along the LDS rows are read by the transpose read.
+constexpr int kRfQT = 32, kRfST = kBwD + 8, kRfPT = kRfQT + 8;
+
+__host__ __device__ constexpr size_t bw_refine_mfma_lds(int Ck) {
+  const size_t ckp = 32 * static_cast<size_t>((Ck + 31) / 32);
+  return sizeof(uint16_t) * (4 * ckp * kRfST + 2 * kBwD * kRfST + 4 * kRfQT * kRfST + 4 * ckp * kRfPT) +
+         sizeof(float) * (3 * 4 * kRfQT + ckp + kBwD + kRfQT) + sizeof(int) * kRfQT;
+}
+
+template <typename TG>
+__global__ void __launch_bounds__(256) bw_refine_mfma_kernel(BwArgs a) {
+  constexpr int D = kBwD, ST = kRfST, PT = kRfPT, QT = kRfQT, NKS = D / 16;
+  constexpr bool GF = sizeof(TG) == 4;  // fp32 upstream gradient: hi + lo
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  const int e = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Cq = a.Cq, Ck = a.Ck, N = a.N, njt = (Ck + 31) / 32, Ckp = 32 * njt;
+  const int nbS = a.causal ? a.nb : 1;
+  const int i = e % Cq;
+  const float s = a.scale;
+  const bool dip = a.dipole != 0;
+  const size_t ti = static_cast<size_t>(bh) * nbS * Cq + e;
+  uint16_t* sKh = reinterpret_cast<uint16_t*>(lds_raw);
+  uint16_t* sKl = sKh + Ckp * ST;
+  uint16_t* sVh = sKl + Ckp * ST;
+  uint16_t* sVl = sVh + Ckp * ST;
+  uint16_t* sDh = sVl + Ckp * ST;   // D_i rows v
+  uint16_t* sDl = sDh + D * ST;
+  uint16_t* sQh = sDl + D * ST;     // tile residual rows
+  uint16_t* sQl = sQh + QT * ST;
+  uint16_t* sGh = sQl + QT * ST;    // tile upstream-gradient rows
+  uint16_t* sGl = sGh + QT * ST;
+  uint16_t* sPh = sGl + QT * ST;    // P^T: cluster rows, query columns
+  uint16_t* sPl = sPh + Ckp * PT;
+  uint16_t* sLh = sPl + Ckp * PT;   // dl^T
+  uint16_t* sLl = sLh + Ckp * PT;
+  float* sRed = reinterpret_cast<float*>(sLl + Ckp * PT);  // [3][4][QT]: max, sum, sum e dp
+  float* sLz = sRed + 3 * 4 * QT;
+  float* sQbar = sLz + Ckp;
+  float* sDL = sQbar + D;
+  int* sRow = reinterpret_cast<int*>(sDL + QT);
+  auto split_store = [&](uint16_t* hi, uint16_t* lo, int o, float x) {
+    const uint16_t xh = f32_to_bf16_bits(x);
+    hi[o] = xh;
+    lo[o] = f32_to_bf16_bits(x - bf16_to_f32(xh));
+  };
+  // the bucket's tables (rows Ck .. Ckp - 1 zero, their log Z -inf)
+  for (int x = tid; x < Ckp * D; x += 256) {
+    const int j = x / D, d = x % D;
+    const float kv = j < Ck ? a.tk[(ti * Ck + j) * D + d] : 0.f;
+    const float vv = j < Ck ? a.tv[(ti * Ck + j) * D + d] : 0.f;
+    split_store(sKh, sKl, j * ST + d, kv);
+    split_store(sVh, sVl, j * ST + d, vv);
+  }
+  for (int x = tid; x < D * D; x += 256) split_store(sDh, sDl, (x / D) * ST + x % D, dip ? a.dip[ti * D * D + x] : 0.f);
+  for (int j = tid; j < Ckp; j += 256) sLz[j] = j < Ck ? a.logz[ti * Ck + j] : kNegInf;
+  if (tid < D) sQbar[tid] = a.qbar[(static_cast<size_t>(bh) * Cq + i) * D + tid];
+  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (nbS * Cq + 1);
+  const int o0 = offq[e], o1 = offq[e + 1];
+  const int32_t* perm = a.perm_q + static_cast<size_t>(bh) * N;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + static_cast<size_t>(bh) * N * D;
+  const TG* G = static_cast<const TG*>(a.causal ? static_cast<const void*>(a.o_far) : a.dout) + static_cast<size_t>(bh) * N * D;
+  const float* dLn = a.causal ? a.l_far + static_cast<size_t>(bh) * N : nullptr;
+  float* dq = a.dq + static_cast<size_t>(bh) * N * D;
+  const bool ownj = 32 * wave < Ck;  // this wave's clusters exist
+  f32x16_t gvt[2], gkt[2], dqa, gdp[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) gvt[q] = gkt[q] = gdp[q] = zero16();
+  float glz[16], qbs[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) glz[v] = qbs[v] = 0.f;
+  __syncthreads();
+  for (int t0 = o0; t0 < o1; t0 += QT) {
+    // stage the tile: thread -> query row tid / 8, dimensions 8 (tid % 8) .. + 7
+    {
+      const int r = tid >> 3, d0 = (tid & 7) * 8;
+      const int n = t0 + r < o1 ? perm[t0 + r] : -1;
+      float qv[8], gv[8];
+      if (n >= 0) {
+        const u16x8_t q8 = *reinterpret_cast<const u16x8_t*>(Q + static_cast<size_t>(n) * D + d0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          qv[u] = bf16_to_f32(q8[u]) - sQbar[d0 + u];
+          gv[u] = Elem<TG>::load(G, static_cast<size_t>(n) * D + d0 + u);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) qv[u] = gv[u] = 0.f;
+      }
+      bf16x8_t qh, ql, gh, gl;
+      split_bf16x8(qv, qh, ql);
+      split_bf16x8(gv, gh, gl);
+      *reinterpret_cast<bf16x8_t*>(&sQh[r * ST + d0]) = qh;
+      *reinterpret_cast<bf16x8_t*>(&sQl[r * ST + d0]) = ql;
+      *reinterpret_cast<bf16x8_t*>(&sGh[r * ST + d0]) = gh;
+      *reinterpret_cast<bf16x8_t*>(&sGl[r * ST + d0]) = gl;
+      if ((tid & 7) == 0) {
+        sRow[r] = n;
+        sDL[r] = (dLn != nullptr && n >= 0) ? dLn[n] : 0.f;
+      }
+    }
+    __syncthreads();
+    // logits and dp for this wave's clusters (rows 32 w + 8 (v / 4) + 4 h + v % 4, query c)
+    f32x16_t lt = zero16(), dpt = zero16();
+    if (ownj) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int ok = (32 * wave + c) * ST + 16 * ks + 8 * h, oq = c * ST + 16 * ks + 8 * h;
+        const bf16x8_t kh = *reinterpret_cast<const bf16x8_t*>(&sKh[ok]), kl = *reinterpret_cast<const bf16x8_t*>(&sKl[ok]);
+        const bf16x8_t vh = *reinterpret_cast<const bf16x8_t*>(&sVh[ok]), vl = *reinterpret_cast<const bf16x8_t*>(&sVl[ok]);
+        const bf16x8_t qh = *reinterpret_cast<const bf16x8_t*>(&sQh[oq]), ql = *reinterpret_cast<const bf16x8_t*>(&sQl[oq]);
+        const bf16x8_t gh = *reinterpret_cast<const bf16x8_t*>(&sGh[oq]);
+        lt = mfma32(kh, qh, lt);
+        lt = mfma32(kh, ql, lt);
+        lt = mfma32(kl, qh, lt);
+        dpt = mfma32(vh, gh, dpt);
+        dpt = mfma32(vl, gh, dpt);
+        if (GF) dpt = mfma32(vh, *reinterpret_cast<const bf16x8_t*>(&sGl[oq]), dpt);
+      }
+    }
+    float lg[16], mx = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float lz = ownj ? sLz[32 * wave + 8 * (v >> 2) + 4 * h + (v & 3)] : kNegInf;
+      lg[v] = lz == kNegInf ? kNegInf : lz + s * lt[v];
+      mx = fmaxf(mx, lg[v]);
+    }
+    mx = fmaxf(mx, xor32(mx));
+    if (h == 0) sRed[wave * QT + c] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(sRed[c], sRed[QT + c]), fmaxf(sRed[2 * QT + c], sRed[3 * QT + c]));
+    float ev[16], z = 0.f, zd = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      ev[v] = lg[v] == kNegInf ? 0.f : __expf(lg[v] - mx);
+      z += ev[v];
+      zd = fmaf(ev[v], dpt[v], zd);
+    }
+    z += xor32(z);
+    zd += xor32(zd);
+    if (h == 0) {
+      sRed[4 * QT + wave * QT + c] = z;
+      sRed[8 * QT + wave * QT + c] = zd;
+    }
+    __syncthreads();
+    const float zt = (sRed[4 * QT + c] + sRed[5 * QT + c]) + (sRed[6 * QT + c] + sRed[7 * QT + c]);
+    const float zdt = (sRed[8 * QT + c] + sRed[9 * QT + c]) + (sRed[10 * QT + c] + sRed[11 * QT + c]);
+    const bool qok = sRow[c] >= 0;
+    const float inv = (zt > 0.f && qok) ? 1.f / zt : 0.f;
+    const float rs = zdt * inv - sDL[c];  // sum_j p dp - dL/dL_far
+    if (ownj) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = ev[v] * inv;
+        const float dl = p * (dpt[v] - rs);
+        glz[v] += dl;
+        const int o = (32 * wave + 8 * (v >> 2) + 4 * h + (v & 3)) * PT + c;
+        split_store(sPh, sPl, o, p);
+        split_store(sLh, sLl, o, dl);
+      }
+    }
+    __syncthreads();
+    if (ownj) {
+      // dL/dV^T += g^T P, dL/dK^T += qt^T dl (dimension rows, this wave's cluster columns)
+#pragma unroll
+      for (int ks = 0; ks < QT / 16; ++ks) {
+        const int ob = (32 * wave + c) * PT + 16 * ks + 8 * h;
+        const bf16x8_t ph = *reinterpret_cast<const bf16x8_t*>(&sPh[ob]), pl = *reinterpret_cast<const bf16x8_t*>(&sPl[ob]);
+        const bf16x8_t lh = *reinterpret_cast<const bf16x8_t*>(&sLh[ob]), ll = *reinterpret_cast<const bf16x8_t*>(&sLl[ob]);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const bf16x8_t gth = lds_operand_tr(sGh, ST, 16 * ks, 32 * dt, lane);
+          const bf16x8_t qth = lds_operand_tr(sQh, ST, 16 * ks, 32 * dt, lane);
+          const bf16x8_t qtl = lds_operand_tr(sQl, ST, 16 * ks, 32 * dt, lane);
+          gvt[dt] = mfma32(gth, ph, gvt[dt]);
+          gvt[dt] = mfma32(gth, pl, gvt[dt]);
+          if (GF) gvt[dt] = mfma32(lds_operand_tr(sGl, ST, 16 * ks, 32 * dt, lane), ph, gvt[dt]);
+          gkt[dt] = mfma32(qth, lh, gkt[dt]);
+          gkt[dt] = mfma32(qth, ll, gkt[dt]);
+          gkt[dt] = mfma32(qtl, lh, gkt[dt]);
+        }
+      }
+    }
+    if (wave < 2) {
+      // dq^T = K^T dl^T + D^T g^T for dimensions 32 wave .. + 31, query columns
+      dqa = zero16();
+      for (int js = 0; js < Ckp / 16; ++js) {
+        const bf16x8_t kth = lds_operand_tr(sKh, ST, 16 * js, 32 * wave, lane);
+        const bf16x8_t ktl = lds_operand_tr(sKl, ST, 16 * js, 32 * wave, lane);
+        const bf16x8_t lth = lds_operand_tr(sLh, PT, 16 * js, 0, lane);
+        const bf16x8_t ltl = lds_operand_tr(sLl, PT, 16 * js, 0, lane);
+        dqa = mfma32(kth, lth, dqa);
+        dqa = mfma32(kth, ltl, dqa);
+        dqa = mfma32(ktl, lth, dqa);
+      }
+      if (dip) {
+#pragma unroll
+        for (int vs = 0; vs < NKS; ++vs) {
+          const bf16x8_t dth = lds_operand_tr(sDh, ST, 16 * vs, 32 * wave, lane);
+          const bf16x8_t dtl = lds_operand_tr(sDl, ST, 16 * vs, 32 * wave, lane);
+          const int og = c * ST + 16 * vs + 8 * h;
+          const bf16x8_t gh = *reinterpret_cast<const bf16x8_t*>(&sGh[og]);
+          dqa = mfma32(dth, gh, dqa);
+          dqa = mfma32(dtl, gh, dqa);
+          if (GF) dqa = mfma32(dth, *reinterpret_cast<const bf16x8_t*>(&sGl[og]), dqa);
+        }
+      }
+      const int n = sRow[c];
+      if (n >= 0) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * wave + 8 * g4 + 4 * h;
+          const f32x4_t x = {s * dqa[4 * g4], s * dqa[4 * g4 + 1], s * dqa[4 * g4 + 2], s * dqa[4 * g4 + 3]};
+          *reinterpret_cast<f32x4_t*>(dq + static_cast<size_t>(n) * D + d0) = x;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) qbs[4 * g4 + u] -= x[u];
+        }
+      }
+    } else if (dip) {
+      // dL/dD_i (rows v, columns d) += g^T qt: tiles (vt, dt) = (wave - 2, 0 and 1)
+      const int vt = wave - 2;
+#pragma unroll
+      for (int ks = 0; ks < QT / 16; ++ks) {
+        const bf16x8_t gth = lds_operand_tr(sGh, ST, 16 * ks, 32 * vt, lane);
+        const bf16x8_t gtl = GF ? lds_operand_tr(sGl, ST, 16 * ks, 32 * vt, lane) : gth;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const bf16x8_t qh = lds_operand_tr(sQh, ST, 16 * ks, 32 * dt, lane);
+          const bf16x8_t ql = lds_operand_tr(sQl, ST, 16 * ks, 32 * dt, lane);
+          gdp[dt] = mfma32(gth, qh, gdp[dt]);
+          gdp[dt] = mfma32(gth, ql, gdp[dt]);
+          if (GF) gdp[dt] = mfma32(gtl, qh, gdp[dt]);
+        }
+      }
+    }
+    __syncthreads();  // the tile buffers are rewritten next
+  }
+  // summary gradients of this wave's clusters: lane column j = 32 wave + c, rows d
+  const int j = 32 * wave + c;
+  if (ownj && j < Ck) {
+    const size_t o = (ti * Ck + j) * D;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * h;
+        *reinterpret_cast<f32x4_t*>(a.g_v + o + d0) =
+            f32x4_t{gvt[dt][4 * g4], gvt[dt][4 * g4 + 1], gvt[dt][4 * g4 + 2], gvt[dt][4 * g4 + 3]};
+        *reinterpret_cast<f32x4_t*>(a.g_k + o + d0) =
+            f32x4_t{s * gkt[dt][4 * g4], s * gkt[dt][4 * g4 + 1], s * gkt[dt][4 * g4 + 2], s * gkt[dt][4 * g4 + 3]};
+      }
+  }
+  if (wave >= 2) {
+    const int vt = wave - 2;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        // element v: row v_idx = 32 vt + 8 (v / 4) + 4 h + v % 4, column d = 32 dt + c
+        const int vi = 32 * vt + 8 * (v >> 2) + 4 * h + (v & 3);
+        a.g_dip[ti * D * D + static_cast<size_t>(vi) * D + 32 * dt + c] = dip ? s * gdp[dt][v] : 0.f;
+      }
+  }
+  // dL/dlog Z (sum over the queries: lanes c) and the stage-2 part of dL/dqbar (waves 0, 1:
+  // sum over the query columns), through LDS in a fixed order
+  float* red = reinterpret_cast<float*>(sPh);  // free now: [Ckp][33] then [D][33]
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = 32 * wave + 8 * (v >> 2) + 4 * h + (v & 3);
+    if (ownj) red[r * 33 + c] = glz[v];
+  }
+  float* red2 = red + Ckp * 33;
+  if (wave < 2)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red2[(32 * wave + 8 * (v >> 2) + 4 * h + (v & 3)) * 33 + c] = qbs[v];
+  __syncthreads();
+  if (tid < Ck) {
+    float x = 0.f;
+    for (int q = 0; q < 32; ++q) x += red[tid * 33 + q];
+    a.g_logz[ti * Ck + tid] = x;
+  }
+  if (tid < D) {
+    float x = 0.f;
+    for (int q = 0; q < 32; ++q) x += red2[tid * 33 + q];
+    a.dqbar2[ti * D + tid] = x;
+  }
+}
+
 // Per query cluster i: P_i., log sum_j Z_ij, the bf16 hi/lo copies of G_Dip_i (tilted,
 // acausal), and for every key cluster j: dK'_ij, dV'_ij and V_ij^T G_Dip_i K_ij. Two
 // clusters at a time (threads 0-127: j, 128-255: j + 1; of each half, 64 threads per
@@ -1392,7 +1691,17 @@ static void launch_backward_t(const BwArgs& a, hipStream_t s) {
     ProfScope ps_("bw_merge", s);
     hipLaunchKernelGGL((bw_merge_kernel<T>), dim3((a.BH * a.N + 3) / 4), dim3(256), 0, s, a);
   }
-  {
+  if (sizeof(T) == 2) {
+    const size_t lds = bw_refine_mfma_lds(a.Ck);
+    ProfScope ps_("bw_refine_mfma", s);
+    if (a.causal) {
+      allow_lds((const void*)bw_refine_mfma_kernel<float>, lds);
+      hipLaunchKernelGGL(bw_refine_mfma_kernel<float>, ge, dim3(256), lds, s, a);
+    } else {
+      allow_lds((const void*)bw_refine_mfma_kernel<bf16>, lds);
+      hipLaunchKernelGGL(bw_refine_mfma_kernel<bf16>, ge, dim3(256), lds, s, a);
+    }
+  } else {
     ProfScope ps_("bw_refine", s);
     if (a.causal) hipLaunchKernelGGL((bw_refine_kernel<T, float>), ge, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((bw_refine_kernel<T, T>), ge, dim3(256), 0, s, a);
