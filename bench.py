@@ -1,7 +1,8 @@
 """Throughput of the MuSe forward pass on one MI355X, with roofline and CPU-oracle baseline.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload acausal_8k] [--no-cpu]
-                [--no-exact] [--no-secondary] [--no-peaks] [--hierarchy] [--single-stream]
+                [--no-exact] [--no-secondary] [--no-peaks] [--no-backward] [--hierarchy]
+                [--single-stream]
 
 A step is one muse_attn_fwd call over the whole workload batch (K-means, stage 1,
 stage 2 and, when causal, the exact diagonal blocks), with inputs resident in HBM and
@@ -11,8 +12,9 @@ on the same shape (speedup), the relative squared error of MuSe against it, per-
 average durations measured with HIP events on the stream the kernels run on, the
 untilted-dipole run and the paper's speed setting (key clusters capped at 1.5 N / Ck
 members, one Lloyd iteration) of a workload without retrieval, the hierarchical-decomposition
-run of a causal one without retrieval, the backward pass of an acausal one (`backward`:
-dq, dk, dv for an upstream gradient with the forward's labels fixed), `measured_peaks` (a
+run of a causal one without retrieval, the backward pass of a D = 64 one without
+retrieval (`backward`: dq, dk, dv for an upstream gradient with the forward's labels
+fixed), `measured_peaks` (a
 device copy and a bf16
 GEMM on this GPU, beside the published peaks the roofline uses) and, with the default
 workload, `secondary`: the same figures for the 64k causal configuration.
@@ -255,12 +257,12 @@ def csrc_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def profile_record(workload: str, kernel: str):
-    """The per-launch figures of `kernel` in the rocprofv3 summary profiles/muse_fwd_<workload>.md
-    (bytes read and written at the L2-to-memory interface from the raw EA request counters,
-    matrix-core busy fraction, counted matrix-core flops), or None when absent or taken on
-    other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"muse_fwd_{workload}.md")
+def profile_record(workload: str, kernel: str, kind: str = "fwd"):
+    """The per-launch figures of `kernel` in the rocprofv3 summary profiles/muse_<kind>_<workload>.md
+    (kind fwd: the forward step; bwd: the run with the backward pass), i.e. bytes read and
+    written at the L2-to-memory interface from the raw EA request counters, matrix-core busy
+    fraction, counted matrix-core flops; None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"muse_{kind}_{workload}.md")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -273,9 +275,9 @@ def profile_record(workload: str, kernel: str):
     return None
 
 
-def measured_traffic(workload: str, kernel: str):
+def measured_traffic(workload: str, kernel: str, kind: str = "fwd"):
     """HBM bytes per launch (read + written) from the profile summary, or None."""
-    k = profile_record(workload, kernel)
+    k = profile_record(workload, kernel, kind)
     return None if k is None else k["fetch_bytes"] + k["write_bytes"]
 
 
@@ -362,6 +364,7 @@ def main():
                     help="with the default workload, skip the 64k causal configuration reported beside it")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-peaks", action="store_true", help="skip the copy and GEMM reference measurements")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass record")
     ap.add_argument("--single-stream", action="store_true",
                     help="run every library kernel on one stream (no side stream), e.g. to profile each alone")
     ap.add_argument("--hierarchy", action="store_true",
@@ -390,7 +393,8 @@ def main():
     from clustered_softmax_attention_amd import binding
 
     binding.load()
-    res = measure(args.workload, args.steps, args.warmup, not args.no_exact, args.hierarchy, args.single_stream)
+    res = measure(args.workload, args.steps, args.warmup, not args.no_exact, args.hierarchy, args.single_stream,
+                  backward=not args.no_backward)
     cfg = res["cfg"]
     cpu = None
     if not args.no_cpu:
@@ -474,7 +478,7 @@ def measured_peaks() -> dict:
 
 
 def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = False,
-            single_stream: bool = False) -> dict:
+            single_stream: bool = False, backward: bool = True) -> dict:
     """Time `steps` MuSe forward calls of workload `name` after `warmup` (whole step on
     the GPU, inputs resident), then the per-kernel HIP-event durations over a second pass,
     the roofline of the dominant kernel and, with `exact`, the in-library exact attention."""
@@ -599,7 +603,7 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
             # the hierarchical block decomposition (one two-stage approximation per square
             # below the diagonal, log-sum-exp merged)
             variant("hierarchy", cfg.iters, lambda n: True, hierarchy=True)
-    if cfg.D == 64 and cfg.topk_clusters == 0 and not hierarchy:
+    if backward and cfg.D == 64 and cfg.topk_clusters == 0 and not hierarchy:
         # the backward pass (dq, dk, dv for an upstream gradient, labels of one forward call
         # held fixed), timed like the forward step
         _, ex_b = binding.attn_fwd(Q, K, V, cfg.Cq, cfg.Ck, cfg.iters, causal=cfg.causal, block=cfg.block,
@@ -625,10 +629,13 @@ def measure(name: str, steps: int, warmup: int, exact: bool, hierarchy: bool = F
         binding.prof_enable(False)
         dom_b = next((n for n, _ in sorted(prof_b.items(), key=lambda kv: -kv[1][0])
                       if kernel_work(n, cfg) is not None), None)
+        rec_b = None if dom_b is None else profile_record(name, dom_b, "bwd")
         extra["backward"] = {
             "ms_per_step": ms_b, "value": cfg.B * cfg.N / (ms_b / 1e3), "unit": "tokens/s",
             "roofline": None if dom_b is None else {
-                "kernel": dom_b, **roofline_entry(dom_b, cfg, prof_b[dom_b][0] / prof_b[dom_b][1] / 1e3)},
+                "kernel": dom_b, **roofline_entry(dom_b, cfg, prof_b[dom_b][0] / prof_b[dom_b][1] / 1e3),
+                "traffic": measured_traffic(name, dom_b, "bwd"),
+                "mfma_busy_counter": None if rec_b is None else rec_b.get("mfma_busy")},
             "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in sorted(prof_b.items(), key=lambda kv: -kv[1][0])}}
         print(f"# backward: {ms_b:.3f} ms/step, {extra['backward']['kernels_us']}", file=sys.stderr, flush=True)
         del ws_b
