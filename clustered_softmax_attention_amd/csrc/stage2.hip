@@ -11,9 +11,9 @@
 //   l^T = K_i qt^T (Ck x 32), P = softmax over the Ck rows, O^T = V_i^T P^T + (s D_i) qt^T,
 // with K_i, qt, V_i and P split into bf16 hi + lo parts (three products hi*hi, hi*lo,
 // lo*hi; error ~2^-16 relative) and the dipole product in plain bf16 (a small term).
-// fp32 inputs (s2_refine): one thread per query; the residual is kept in registers for
-// the logits and in LDS (lane-major) for the dipole product, whose table is stored key
-// index first so that a row of D_i^T is contiguous.
+// fp32 inputs (s2_refine): one wave per query; the logits with the lanes over key
+// clusters (the residual broadcast from LDS), the weighted values with the lanes over
+// dimensions, and the dipole row by row (lanes over the key dimension, a wave sum each).
 // With the hierarchical decomposition (pith.science review, Figure 2 caption) a query of
 // block b sees the entries e = b, b & (b - 1), ... > 0, one per square below the
 // diagonal; their (o, L) are merged by log-sum-exp, L = log(e^L1 + e^L2),
@@ -23,99 +23,113 @@
 
 namespace muse {
 
-constexpr int kS2Threads = 128;
-
 template <typename T, int D>
-__global__ void __launch_bounds__(kS2Threads) s2_refine_kernel(S2Args a) {
-  __shared__ float s_q[D][kS2Threads];
-  const int bh = blockIdx.y, tid = threadIdx.x;
-  const long n = static_cast<long>(blockIdx.x) * kS2Threads + tid;
-  const bool valid = n < a.N;
-  const long nn = valid ? n : a.N - 1;
-  const int b = a.causal ? static_cast<int>(nn / a.block) : 0;
-  const size_t row = static_cast<size_t>(bh) * a.N + nn;
-  const bool far_empty = a.causal && b == 0;
-  if (far_empty) {
-    if (valid) {
-      a.l_far[row] = kNegInf;
-      for (int d = 0; d < D; ++d) a.o_far[row * D + d] = 0.f;
-    }
+__global__ void __launch_bounds__(256) s2_refine_kernel(S2Args a) {
+  constexpr int NP = D / 64;  // dimensions per lane
+  __shared__ float s_qt[4][D];
+  __shared__ float s_p[4][kMaxClusters];
+  const int bh = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long n = static_cast<long>(blockIdx.x) * 4 + wave;
+  if (n >= a.N) return;  // the whole wave
+  const int b = a.causal ? static_cast<int>(n / a.block) : 0;
+  const size_t row = static_cast<size_t>(bh) * a.N + n;
+  if (a.causal && b == 0) {  // no earlier block: empty far field
+    if (lane == 0) a.l_far[row] = kNegInf;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) a.o_far[row * D + lane + 64 * q] = 0.f;
     return;
   }
   const int i = a.labels_q[row];
   const T* Q = static_cast<const T*>(a.q);
   const float* qb = a.qbar + (static_cast<size_t>(bh) * a.Cq + i) * D;
-  float qt[D];
+  float qt[NP];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    qt[d] = Elem<T>::load(Q, row * D + d) - qb[d];
-    s_q[d][tid] = qt[d];
+  for (int q = 0; q < NP; ++q) {
+    const int d = lane + 64 * q;
+    qt[q] = Elem<T>::load(Q, row * D + d) - qb[d];
+    s_qt[wave][d] = qt[q];
   }
+  const int Ck = a.Ck;
   int e = a.causal ? b : 0;
   for (bool first = true;; first = false) {
     const size_t sidx = (static_cast<size_t>(bh) * a.nbS + e) * a.Cq + i;
-    const float* lz = a.s_logz + sidx * a.Ck;
-    const float* Kt = a.s_k + sidx * a.Ck * D;
-    const float* Vt = a.s_v + sidx * a.Ck * D;
-
-    float mx = kNegInf;
-    for (int j = 0; j < a.Ck; ++j) {
-      const float l0 = lz[j];
-      if (l0 == kNegInf) continue;
-      float dot = 0.f;
-  #pragma unroll
-      for (int d = 0; d < D; ++d) dot = fmaf(qt[d], Kt[j * D + d], dot);
-      mx = fmaxf(mx, l0 + a.scale * dot);
+    const float* lz = a.s_logz + sidx * Ck;
+    const float* Kt = a.s_k + sidx * Ck * D;
+    const float* Vt = a.s_v + sidx * Ck * D;
+    // logits: lanes over key clusters (row j of K_i read 16 bytes at a time)
+    float l[2], mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = lane + 64 * t;
+      l[t] = kNegInf;
+      if (j < Ck && lz[j] != kNegInf) {
+        float dot = 0.f;
+        for (int d = 0; d < D; d += 4) {
+          const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(Kt + static_cast<size_t>(j) * D + d);
+          const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(&s_qt[wave][d]);
+          dot = fmaf(q4[0], k4[0], fmaf(q4[1], k4[1], fmaf(q4[2], k4[2], fmaf(q4[3], k4[3], dot))));
+        }
+        l[t] = lz[j] + a.scale * dot;
+      }
+      mx = fmaxf(mx, l[t]);
     }
-    float acc[D];
-  #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] = 0.f;
+    mx = wave_max(mx);
     float z = 0.f;
-    for (int j = 0; j < a.Ck; ++j) {
-      const float l0 = lz[j];
-      if (l0 == kNegInf) continue;
-      float dot = 0.f;
-  #pragma unroll
-      for (int d = 0; d < D; ++d) dot = fmaf(qt[d], Kt[j * D + d], dot);
-      const float p = __expf(l0 + a.scale * dot - mx);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = lane + 64 * t;
+      const float p = l[t] == kNegInf ? 0.f : __expf(l[t] - mx);
       z += p;
-  #pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, Vt[j * D + d], acc[d]);
+      if (j < Ck) s_p[wave][j] = p;
     }
+    z = wave_sum(z);
     const bool empty = !(z > 0.f);  // no far-field key at all
     const float inv = empty ? 0.f : 1.f / z;
-  #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] *= inv;
+    // o = sum_j p_j V_ij: lanes over dimensions, clusters in order
+    float acc[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) acc[q] = 0.f;
+    for (int j = 0; j < Ck; ++j) {
+      const float p = s_p[wave][j];
+#pragma unroll
+      for (int q = 0; q < NP; ++q) acc[q] = fmaf(p, Vt[static_cast<size_t>(j) * D + lane + 64 * q], acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < NP; ++q) acc[q] *= inv;
     if (a.dipole && !empty) {
+      // s D_i qt: rows dv of D_i read whole (lanes over dk), one wave sum per row
       const float* dip = a.s_dip + sidx * D * D;  // [dv][dk]
-      for (int dk = 0; dk < D; ++dk) {
-        const float x = a.scale * s_q[dk][tid];
-  #pragma unroll
-        for (int dv = 0; dv < D; ++dv) acc[dv] = fmaf(dip[dv * D + dk], x, acc[dv]);
+      for (int dv = 0; dv < D; ++dv) {
+        float part = 0.f;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) part = fmaf(dip[static_cast<size_t>(dv) * D + lane + 64 * q], qt[q], part);
+        part = wave_sum(part);
+        if ((dv & 63) == lane) acc[dv >> 6] = fmaf(a.scale, part, acc[dv >> 6]);
       }
     }
     const float L = empty ? kNegInf : mx + __logf(z);
-    if (!valid) return;
     if (a.causal && !first) {
-      // a further square: merge into the far field written so far (this thread's row)
+      // a further square: merge into the far field written so far (this row)
       const float L0 = a.l_far[row];
       const float Ln = L0 == kNegInf ? L : (L == kNegInf ? L0 : fmaxf(L0, L) + log1pf(__expf(-fabsf(L0 - L))));
       const float w0 = L0 == kNegInf ? 0.f : __expf(L0 - Ln), w1 = L == kNegInf ? 0.f : __expf(L - Ln);
-      a.l_far[row] = Ln;
-  #pragma unroll
-      for (int d = 0; d < D; ++d) a.o_far[row * D + d] = w0 * a.o_far[row * D + d] + w1 * acc[d];
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        float* o = a.o_far + row * D + lane + 64 * q;
+        *o = w0 * *o + w1 * acc[q];
+      }
+      if (lane == 0) a.l_far[row] = Ln;
     } else if (a.causal) {
-      a.l_far[row] = L;
-  #pragma unroll
-      for (int d = 0; d < D; ++d) a.o_far[row * D + d] = acc[d];
+      if (lane == 0) a.l_far[row] = L;
+#pragma unroll
+      for (int q = 0; q < NP; ++q) a.o_far[row * D + lane + 64 * q] = acc[q];
     } else {
-      if (a.lse_out) a.lse_out[row] = L;
-      if (a.out_bf16) {
-  #pragma unroll
-        for (int d = 0; d < D; ++d) static_cast<bf16*>(a.out)[row * D + d].bits = f32_to_bf16_bits(acc[d]);
-      } else {
-  #pragma unroll
-        for (int d = 0; d < D; ++d) static_cast<float*>(a.out)[row * D + d] = acc[d];
+      if (a.lse_out && lane == 0) a.lse_out[row] = L;
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        const size_t o = row * D + lane + 64 * q;
+        if (a.out_bf16) static_cast<bf16*>(a.out)[o].bits = f32_to_bf16_bits(acc[q]);
+        else static_cast<float*>(a.out)[o] = acc[q];
       }
     }
     e = a.hier ? (e & (e - 1)) : 0;
@@ -430,14 +444,14 @@ hipError_t launch_stage2(const S2Args& a, int dtype, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  const dim3 g((a.N + kS2Threads - 1) / kS2Threads, a.BH);
+  const dim3 g((a.N + 3) / 4, a.BH);  // a wave per query
   ProfScope ps_("s2_refine", s);
   if (dtype == 0) {
-    if (a.D == 64) hipLaunchKernelGGL((s2_refine_kernel<float, 64>), g, dim3(kS2Threads), 0, s, a);
-    else hipLaunchKernelGGL((s2_refine_kernel<float, 128>), g, dim3(kS2Threads), 0, s, a);
+    if (a.D == 64) hipLaunchKernelGGL((s2_refine_kernel<float, 64>), g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((s2_refine_kernel<float, 128>), g, dim3(256), 0, s, a);
   } else {
-    if (a.D == 64) hipLaunchKernelGGL((s2_refine_kernel<bf16, 64>), g, dim3(kS2Threads), 0, s, a);
-    else hipLaunchKernelGGL((s2_refine_kernel<bf16, 128>), g, dim3(kS2Threads), 0, s, a);
+    if (a.D == 64) hipLaunchKernelGGL((s2_refine_kernel<bf16, 64>), g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((s2_refine_kernel<bf16, 128>), g, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
