@@ -347,15 +347,31 @@ __global__ void __launch_bounds__(256) bw_refine_mfma_kernel(BwArgs a) {
     hi[o] = xh;
     lo[o] = f32_to_bf16_bits(x - bf16_to_f32(xh));
   };
-  // the bucket's tables (rows Ck .. Ckp - 1 zero, their log Z -inf)
-  for (int x = tid; x < Ckp * D; x += 256) {
-    const int j = x / D, d = x % D;
-    const float kv = j < Ck ? a.tk[(ti * Ck + j) * D + d] : 0.f;
-    const float vv = j < Ck ? a.tv[(ti * Ck + j) * D + d] : 0.f;
-    split_store(sKh, sKl, j * ST + d, kv);
-    split_store(sVh, sVl, j * ST + d, vv);
+  // the bucket's tables (rows Ck .. Ckp - 1 zero, their log Z -inf), four values per
+  // thread and step: 16-byte loads, hi and lo written 8 bytes at a time
+  auto split4 = [&](uint16_t* hi, uint16_t* lo, int o, const f32x4_t& x) {
+    u16x4_t h4, l4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      h4[u] = f32_to_bf16_bits(x[u]);
+      l4[u] = f32_to_bf16_bits(x[u] - bf16_to_f32(h4[u]));
+    }
+    *reinterpret_cast<u16x4_t*>(hi + o) = h4;
+    *reinterpret_cast<u16x4_t*>(lo + o) = l4;
+  };
+  for (int x = tid; x < Ckp * D / 4; x += 256) {
+    const int j = x / (D / 4), d = 4 * (x % (D / 4));
+    const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+    const f32x4_t kv = j < Ck ? *reinterpret_cast<const f32x4_t*>(a.tk + (ti * Ck + j) * D + d) : z4;
+    const f32x4_t vv = j < Ck ? *reinterpret_cast<const f32x4_t*>(a.tv + (ti * Ck + j) * D + d) : z4;
+    split4(sKh, sKl, j * ST + d, kv);
+    split4(sVh, sVl, j * ST + d, vv);
   }
-  for (int x = tid; x < D * D; x += 256) split_store(sDh, sDl, (x / D) * ST + x % D, dip ? a.dip[ti * D * D + x] : 0.f);
+  for (int x = tid; x < D * D / 4; x += 256) {
+    const int r = x / (D / 4), d = 4 * (x % (D / 4));
+    const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+    split4(sDh, sDl, r * ST + d, dip ? *reinterpret_cast<const f32x4_t*>(a.dip + ti * D * D + r * D + d) : z4);
+  }
   for (int j = tid; j < Ckp; j += 256) sLz[j] = j < Ck ? a.logz[ti * Ck + j] : kNegInf;
   if (tid < D) sQbar[tid] = a.qbar[(static_cast<size_t>(bh) * Cq + i) * D + tid];
   const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (nbS * Cq + 1);
@@ -901,19 +917,21 @@ __global__ void __launch_bounds__(256) bw_scores_kernel(BwArgs a) {
 // Causal calls: the workgroups tile each key block separately (positions in bucket order
 // are grouped by block), and a key of block b' takes the suffix sum sh of block b' in
 // place of G_Dip_i and p^{b'+1}_im as its weight; keys of the last block enter no table.
-template <typename T>
-__global__ void __launch_bounds__(256) bw_keys_a_kernel(BwArgs a) {
-  constexpr int D = kBwD, GST = kBwGST, NKS = D / 16, NMT = D / 32;
-  constexpr int NPF = 4 * D * D / 8 / 256;  // 16-byte pieces of the four tiles per thread
+// NW waves per workgroup (32 keys each): 8 when the key blocks are multiples of 256 keys,
+// so that every staged G tile serves 256 keys.
+template <typename T, int NW>
+__global__ void __launch_bounds__(64 * NW) bw_keys_a_kernel(BwArgs a) {
+  constexpr int D = kBwD, GST = kBwGST, NKS = D / 16, NMT = D / 32, NT = 64 * NW, KPW = 32 * NW;
+  constexpr int NPF = 4 * D * D / 8 / NT;  // 16-byte pieces of the four tiles per thread
   constexpr bool F32 = sizeof(T) == 4;
   __shared__ __align__(16) uint16_t sGd[2][4 * D * GST];
   const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int wave = tid >> 6;
   const int N = a.N, Cq = a.Cq, Ck = a.Ck;
-  const int blk = a.causal ? a.block : N, tpb = (blk + 127) / 128;
+  const int blk = a.causal ? a.block : N, tpb = (blk + KPW - 1) / KPW;
   const int bp = blockIdx.x / tpb;           // key block (0 when acausal)
   const int pend = min(N, (bp + 1) * blk);
-  const int pos = bp * blk + (blockIdx.x % tpb) * 128 + wave * 32 + c;
+  const int pos = bp * blk + (blockIdx.x % tpb) * KPW + wave * 32 + c;
   const bool valid = pos < pend;
   const bool last = a.causal && bp == a.nb - 1;  // uniform: no table entry after this block
   const int nbW = a.causal ? a.nb : 1;
@@ -948,12 +966,12 @@ __global__ void __launch_bounds__(256) bw_keys_a_kernel(BwArgs a) {
   auto fetch = [&](int i) {
     const uint16_t* src = a.gd + (eg * Cq + i) * 4 * D * D;
 #pragma unroll
-    for (int q = 0; q < NPF; ++q) pf[q] = *reinterpret_cast<const u16x8_t*>(src + 8 * (tid + 256 * q));
+    for (int q = 0; q < NPF; ++q) pf[q] = *reinterpret_cast<const u16x8_t*>(src + 8 * (tid + NT * q));
   };
   auto stage = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < NPF; ++q) {
-      const int e = 8 * (tid + 256 * q), arr = e / (D * D), rem = e % (D * D);
+      const int e = 8 * (tid + NT * q), arr = e / (D * D), rem = e % (D * D);
       *reinterpret_cast<u16x8_t*>(&sGd[buf][arr * D * GST + (rem / D) * GST + rem % D]) = pf[q];
     }
   };
@@ -1487,12 +1505,15 @@ __global__ void __launch_bounds__(256) bw_local_q_kernel(BwArgs a) {
 // accumulators as B operands and G^T, Q^T read by the LDS transpose read.
 constexpr int kLocST = kBwD + 8;  // bf16 row stride of the staged tiles (16-byte aligned rows)
 
-__global__ void __launch_bounds__(128) bw_local_kv_mfma_kernel(BwArgs a) {
-  constexpr int D = kBwD, ST = kLocST, NKS = D / 16, NMT = D / 32, TT = 64;
+// NWK waves per workgroup (32 keys each; 4 when the block is a multiple of 128 keys), so
+// that every staged query tile serves 32 NWK keys.
+template <int NWK>
+__global__ void __launch_bounds__(64 * NWK) bw_local_kv_mfma_kernel(BwArgs a) {
+  constexpr int D = kBwD, ST = kLocST, NKS = D / 16, NMT = D / 32, TT = 64, NT = 64 * NWK;
   __shared__ __align__(16) uint16_t sQ[TT * ST], sGh[TT * ST], sGl[TT * ST];
   __shared__ float sL[TT], sDel[TT];
   const int bh = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
-  const int N = a.N, m0 = blockIdx.x * TT, bend = (m0 / a.block + 1) * a.block;
+  const int N = a.N, m0 = blockIdx.x * 32 * NWK, bend = (m0 / a.block + 1) * a.block;
   const int mk = m0 + 32 * wave + c;  // this lane's key
   const size_t base = static_cast<size_t>(bh) * N;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q) + base * D;
@@ -1513,14 +1534,14 @@ __global__ void __launch_bounds__(128) bw_local_kv_mfma_kernel(BwArgs a) {
     __syncthreads();  // the previous query tile is consumed
     // Q rows (bf16) and G rows (fp32 -> hi, lo): 16-byte pieces, 8 bf16 / 4 floats each
 #pragma unroll
-    for (int q = 0; q < TT * D / 8 / 128; ++q) {
-      const int e = tid + 128 * q, r = e / (D / 8), cc = e % (D / 8);
+    for (int q = 0; q < TT * D / 8 / NT; ++q) {
+      const int e = tid + NT * q, r = e / (D / 8), cc = e % (D / 8);
       *reinterpret_cast<u16x8_t*>(&sQ[r * ST + 8 * cc]) =
           *reinterpret_cast<const u16x8_t*>(Q + static_cast<size_t>(n0 + r) * D + 8 * cc);
     }
 #pragma unroll
-    for (int q = 0; q < TT * D / 4 / 128; ++q) {
-      const int e = tid + 128 * q, r = e / (D / 4), cc = e % (D / 4);
+    for (int q = 0; q < TT * D / 4 / NT; ++q) {
+      const int e = tid + NT * q, r = e / (D / 4), cc = e % (D / 4);
       const f32x4_t g4 = *reinterpret_cast<const f32x4_t*>(G + static_cast<size_t>(n0 + r) * D + 4 * cc);
       u16x4_t hi, lo;
 #pragma unroll
@@ -1734,9 +1755,11 @@ static void launch_backward_t(const BwArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((bw_scores_kernel<T>), gk, dim3(256), 0, s, a);
     }
     const int blk = a.causal ? a.block : a.N;
-    const int nwg = nbS * ((blk + 127) / 128);
     ProfScope ps_("bw_keys_a", s);
-    hipLaunchKernelGGL((bw_keys_a_kernel<T>), dim3(nwg, a.BH), dim3(256), 0, s, a);
+    if (sizeof(T) == 2 && blk % 256 == 0)  // (fp32 inputs: their hi/lo operands need the registers of 4 waves)
+      hipLaunchKernelGGL((bw_keys_a_kernel<T, 8>), dim3(nbS * (blk / 256), a.BH), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((bw_keys_a_kernel<T, 4>), dim3(nbS * ((blk + 127) / 128), a.BH), dim3(256), 0, s, a);
   }
   if (!a.causal) {
     ProfScope ps_("bw_dlogz", s);
@@ -1757,7 +1780,10 @@ static void launch_backward_t(const BwArgs& a, hipStream_t s) {
     constexpr bool MF = sizeof(T) == 2;
     {
       ProfScope ps_(MF ? "bw_local_kv_mfma" : "bw_local_kv", s);
-      if (MF) hipLaunchKernelGGL(bw_local_kv_mfma_kernel, gl, dim3(128), 0, s, a);
+      if (MF && a.block % 128 == 0)
+        hipLaunchKernelGGL(bw_local_kv_mfma_kernel<4>, dim3(a.N / 128, a.BH), dim3(256), 0, s, a);
+      else if (MF)
+        hipLaunchKernelGGL(bw_local_kv_mfma_kernel<2>, gl, dim3(128), 0, s, a);
       else hipLaunchKernelGGL((bw_local_kv_kernel<T>), gl, dim3(256), 0, s, a);
     }
     ProfScope ps_(MF ? "bw_local_q_mfma" : "bw_local_q", s);
