@@ -35,8 +35,8 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from .muse_ref import (NEG_INF, Summaries, _attend, _cluster, default_scale, hierarchy_squares, lse_merge,
-                       refine, tilted_summaries)
+from .muse_ref import (NEG_INF, Summaries, _attend, _cluster, cap_key_labels, default_scale, hierarchy_squares,
+                       lse_merge, refine, tilted_summaries)
 
 
 # --------------------------------------------------------------------------------------
@@ -244,14 +244,17 @@ def _centroid_bwd(dq, dqbar, labels, Cq: int):
 # --------------------------------------------------------------------------------------
 
 def muse_acausal_bwd(q, k, v, Cq: int, Ck: int, labels_q, labels_k, dO, scale: Optional[float] = None,
-                     dipole: str = "tilted"):
-    """dq, dk, dv of muse_ref.muse_acausal's output with the labels fixed."""
+                     dipole: str = "tilted", cap_ratio: Optional[float] = None):
+    """dq, dk, dv of muse_ref.muse_acausal's output with the labels fixed. cap_ratio: key
+    clusters capped as in the forward (cap_key_labels): the keys left out of the summaries
+    get no gradient through them."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     s = default_scale(q.shape[1]) if scale is None else scale
     _, lq, qbar = _cluster(q, Cq, 1, labels_q, None, 0.0)
     _, lk, _ = _cluster(k, Ck, 1, labels_k, None, 0.0)
+    lk = cap_key_labels(lk, Ck, cap_ratio)
     S = tilted_summaries(qbar, k, v, lk, Ck, s, dipole)
     dq, dqbar, G = refine_bwd(q, lq, qbar, S, s, dipole != "none", dO)
     gqbar, dk, dv = tilted_summaries_bwd(qbar, k, v, lk, Ck, s, dipole, G)
@@ -259,10 +262,13 @@ def muse_acausal_bwd(q, k, v, Cq: int, Ck: int, labels_q, labels_k, dO, scale: O
 
 
 def muse_causal_bwd(q, k, v, Cq: int, Ck: int, block: int, labels_q, labels_k, dO,
-                    scale: Optional[float] = None, dipole: str = "tilted", hierarchical: bool = False):
+                    scale: Optional[float] = None, dipole: str = "tilted", hierarchical: bool = False,
+                    cap_ratio: Optional[float] = None):
     """dq, dk, dv of muse_ref.muse_causal's output (no retrieval) with the labels fixed:
     per block, the log-sum-exp merge of the exact local part and the far part (one
-    two-stage approximation over all earlier keys, or one per square of the hierarchy)."""
+    two-stage approximation over all earlier keys, or one per square of the hierarchy).
+    cap_ratio: key clusters capped over the whole sequence as in the forward; a key left
+    out of the summaries still takes part in its own block's exact attention."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -272,6 +278,7 @@ def muse_causal_bwd(q, k, v, Cq: int, Ck: int, block: int, labels_q, labels_k, d
     nb = N // block
     _, lq, qbar = _cluster(q, Cq, 1, labels_q, None, 0.0)
     _, lk, _ = _cluster(k, Ck, 1, labels_k, None, 0.0)
+    lk = cap_key_labels(lk, Ck, cap_ratio)   # labels seen by the summaries
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)

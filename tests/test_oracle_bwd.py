@@ -2,7 +2,8 @@
 
 * central finite differences of the forward oracle (muse_acausal / muse_causal with the
   labels fixed), over every input element, for the tilted, untilted and no-dipole modes,
-  the prefix and hierarchical causal forms, s = 1/sqrt(D) and s = 1;
+  the prefix and hierarchical causal forms, s = 1/sqrt(D) and s = 1, and capped key
+  clusters;
 * exact attention's backward against torch autograd of scaled dot-product attention in
   float64 (an independent implementation);
 * reductions that fix the answer without finite differences: singleton clusters give
@@ -80,6 +81,31 @@ def test_causal_finite_differences(dipole, hier):
                                   hierarchical=hier).o * dO).sum())
 
     dq, dk, dv = muse_causal_bwd(q, k, v, Cq, Ck, block, lq, lk, dO, dipole=dipole, hierarchical=hier)
+    _check(dq, _fd(f, q))
+    _check(dk, _fd(f, k))
+    _check(dv, _fd(f, v))
+
+
+@pytest.mark.parametrize("causal,dipole", [(False, "tilted"), (False, "untilted"), (True, "tilted"),
+                                           (True, "none")])
+def test_cap_finite_differences(causal, dipole):
+    # a cap of 1.0: clusters of more than N / Ck members lose their later keys from the
+    # summaries (40 keys, 5 clusters: at most 8 kept each)
+    q, k, v, lq, lk, dO = _problem(4, N=40, empty_k=False)
+    Cq, Ck, block, cap = 3, 5, 10, 1.0
+    assert max(np.bincount(lk, minlength=Ck)) > 8  # some key is left out
+
+    def f():
+        if causal:
+            r = muse_causal(q, k, v, Cq, Ck, 1, block, dipole=dipole, labels_q=lq, labels_k=lk, cap_ratio=cap)
+        else:
+            r = muse_acausal(q, k, v, Cq, Ck, 1, dipole=dipole, labels_q=lq, labels_k=lk, cap_ratio=cap)
+        return float((r.o * dO).sum())
+
+    if causal:
+        dq, dk, dv = muse_causal_bwd(q, k, v, Cq, Ck, block, lq, lk, dO, dipole=dipole, cap_ratio=cap)
+    else:
+        dq, dk, dv = muse_acausal_bwd(q, k, v, Cq, Ck, lq, lk, dO, dipole=dipole, cap_ratio=cap)
     _check(dq, _fd(f, q))
     _check(dk, _fd(f, k))
     _check(dv, _fd(f, v))
