@@ -236,7 +236,7 @@ def attn_fwd(q, k, v, Cq: int, Ck: int, kmeans_iters: int, causal: bool = False,
 
 
 def attn_bwd(q, k, v, dout, labels_q, labels_k, Cq: int, Ck: int, causal: bool = False, block: int = 0, *,
-             scale: float = 0.0, dipole=True, workspace: Optional[torch.Tensor] = None):
+             scale: float = 0.0, dipole=True, cap_ratio: float = 0.0, workspace: Optional[torch.Tensor] = None):
     """muse_attn_bwd: (dq, dk, dv) float32 [B,H,N,D] of the forward output for the upstream
     gradient dout (the inputs' dtype), with the forward's final labels [B,H,N] held fixed."""
     lib = load()
@@ -253,6 +253,7 @@ def attn_bwd(q, k, v, dout, labels_q, labels_k, Cq: int, Ck: int, causal: bool =
     lib.muse_fwd_params_init(ctypes.byref(p))
     p.scale = float(scale)
     p.dipole = dipole_code(dipole)
+    p.cap_ratio = float(cap_ratio)
     if workspace is not None:
         p.workspace = workspace.data_ptr()
         p.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -262,11 +263,13 @@ def attn_bwd(q, k, v, dout, labels_q, labels_k, Cq: int, Ck: int, causal: bool =
     return dq, dk, dv
 
 
-def bwd_workspace_bytes(B, H, N, D, Cq, Ck, causal=False, block=0, dtype=MUSE_BF16, dipole=True) -> int:
+def bwd_workspace_bytes(B, H, N, D, Cq, Ck, causal=False, block=0, dtype=MUSE_BF16, dipole=True,
+                        cap_ratio: float = 0.0) -> int:
     lib = load()
     p = FwdParams()
     lib.muse_fwd_params_init(ctypes.byref(p))
     p.dipole = dipole_code(dipole)
+    p.cap_ratio = float(cap_ratio)
     n = lib.muse_attn_bwd_workspace_bytes(B, H, N, D, Cq, Ck, int(causal), int(block), dtype, ctypes.byref(p))
     if n == 0:
         raise MuseError(-1, lib.muse_last_error().decode())

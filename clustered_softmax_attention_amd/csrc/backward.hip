@@ -731,7 +731,8 @@ __global__ void __launch_bounds__(256) bw_prep_j_kernel(BwArgs a) {
 #pragma unroll
   for (int r = 0; r < EPT; ++r) a.dcov[tj * D * D + tid + 256 * r] = dc[r];
   const int32_t* offk = a.offs_k + static_cast<size_t>(bh) * (Ck + 1);
-  const int m0 = offk[j], m1 = offk[j + 1];
+  const int m0 = offk[j];
+  const int m1 = a.klen != nullptr ? m0 + a.klen[tj] : offk[j + 1];  // the kept prefix under a cap
   if (tid < 2 * D) {
     const T* X = static_cast<const T*>(tid < D ? a.k : a.v) + static_cast<size_t>(bh) * N * D;
     const int d = tid % D;
@@ -939,6 +940,8 @@ __global__ void __launch_bounds__(64 * NW) bw_keys_a_kernel(BwArgs a) {
   const size_t eg = static_cast<size_t>(bh) * nbW + (a.causal ? bp : 0);      // G tiles' entry
   const int key = valid ? a.perm_k[static_cast<size_t>(bh) * N + pos] : 0;
   const int j = valid ? min(max(a.labels_k[static_cast<size_t>(bh) * N + key], 0), Ck - 1) : 0;
+  // a key left out by the cluster size cap is in no summary: weights zero
+  const bool kept = valid && (a.kdrop == nullptr || a.kdrop[static_cast<size_t>(bh) * N + key] == 0);
   const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * N * D;
   const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * N * D;
   // B operands: key c, dimensions 16 ks + 8 h .. + 7 (bf16 hi, and lo for fp32 inputs)
@@ -991,9 +994,9 @@ __global__ void __launch_bounds__(64 * NW) bw_keys_a_kernel(BwArgs a) {
     const size_t ti = ew * Cq + i;
     const float av = valid ? Arow[static_cast<size_t>(i) * N + pos] : 0.f;
     const float lzij = a.logz[ti * Ck + j];
-    const float w = (valid && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
+    const float w = (kept && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
     const float lzi = a.lz[ti];
-    const float p = (valid && lzi != kNegInf) ? __expf(av - lzi) : 0.f;
+    const float p = (kept && lzi != kNegInf) ? __expf(av - lzi) : 0.f;
     const uint16_t* g = sGd[buf];
     // u^T = G K^T, then t^T = G^T V^T, each folded into its accumulator before the next
     // (one 32-row tile pair of registers live at a time)
@@ -1152,6 +1155,8 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
   const bool valid = pos < N;
   const int key = valid ? a.perm_k[static_cast<size_t>(bh) * N + pos] : 0;
   const int j = valid ? min(max(a.labels_k[static_cast<size_t>(bh) * N + key], 0), Ck - 1) : 0;
+  // a key left out by the cluster size cap is in no summary: weights zero
+  const bool kept = valid && (a.kdrop == nullptr || a.kdrop[static_cast<size_t>(bh) * N + key] == 0);
   const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * N * D;
   const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * N * D;
   float kf[DQ], vf[DQ], dk[DQ], dv[DQ];
@@ -1178,7 +1183,7 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
     const size_t tij = ti * Ck + j;
     const size_t sij_ = (es * Cq + i) * Ck + j;  // suffix tables (causal)
     const float lzij = a.logz[tij];
-    const float w = (valid && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
+    const float w = (kept && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
     const float* kp = a.causal ? a.sdk + sij_ * D + d0 : a.dKp + tij * D + d0;
     const float* vp = a.causal ? a.sdv + sij_ * D + d0 : a.dVp + tij * D + d0;
     float kpv[DQ], vpv[DQ];
@@ -1200,11 +1205,11 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
     float da;
     if (a.causal) {
       const float lzi = a.lz[ti];
-      const float p = (a.dipole == 1 && valid && lzi != kNegInf) ? __expf(av - lzi) : 0.f;
+      const float p = (a.dipole == 1 && kept && lzi != kNegInf) ? __expf(av - lzi) : 0.f;
       const float qi = a.dipole == 1 ? a.Q[(static_cast<size_t>(bh) * Cq + i) * N + pos] : 0.f;
       da = fmaf(w, y + a.st[sij_], p * qi);
     } else {
-      if (a.dipole == 1 && valid) y += a.P[tij] * a.Q[(static_cast<size_t>(bh) * Cq + i) * N + pos];
+      if (a.dipole == 1 && kept) y += a.P[tij] * a.Q[(static_cast<size_t>(bh) * Cq + i) * N + pos];
       da = w * (y - a.sij[tij] + a.dlogz[tij]);
     }
 #pragma unroll
@@ -1216,14 +1221,15 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
   }
   if (last)
     for (int e = tid; e < Cq * (KT + 1); e += 256) sWd[e] = 0.f;
-  if (a.dipole == 2 && valid) {
-    // covariance terms with the cluster's dL/dCov = sum_i P_ij G_Dip_i
+  if (a.dipole == 2 && kept) {
+    // covariance terms with the cluster's dL/dCov = sum_i P_ij G_Dip_i (over its kept keys)
     const size_t tj = static_cast<size_t>(bh) * Ck + j;
     const float* dc = a.dcov + tj * D * D;
     const float* km = a.kmean + tj * D;
     const float* vm = a.vmean + tj * D;
     const int32_t* offk = a.offs_k + static_cast<size_t>(bh) * (Ck + 1);
-    const float inv_n = 1.f / static_cast<float>(max(1, offk[j + 1] - offk[j]));
+    const int nj = a.klen != nullptr ? a.klen[tj] : offk[j + 1] - offk[j];
+    const float inv_n = 1.f / static_cast<float>(max(1, nj));
     for (int d = 0; d < D; ++d) {
       const float kc = sKr[kk * RP + d] - km[d];  // k_m - mean k, dimension d
       const float vc = sVr[kk * RP + d] - vm[d];  // v_m - mean v, dimension (value) d

@@ -565,8 +565,8 @@ int validate_bwd(Shape& s, const muse_fwd_params* p) {
   if (s.causal && p != nullptr && p->dipole == MUSE_DIPOLE_UNTILTED)
     return fail(MUSE_ERR_UNSUPPORTED, "the causal backward pass takes the tilted dipole or none");
   if (p != nullptr) {
-    if (p->topk_clusters > 0 || p->hierarchy || p->cap_ratio > 0.0)
-      return fail(MUSE_ERR_UNSUPPORTED, "the backward pass takes no retrieval, hierarchy or cluster size cap");
+    if (p->topk_clusters > 0 || p->hierarchy)
+      return fail(MUSE_ERR_UNSUPPORTED, "the backward pass takes no retrieval or hierarchy");
     if (p->labels_q_in != nullptr || p->labels_k_in != nullptr || p->labels_q_trace != nullptr ||
         p->labels_k_trace != nullptr || p->centroids_q_out != nullptr || p->centroids_k_out != nullptr ||
         p->lse_out != nullptr || p->retrieval_trace != nullptr || p->perm_q_out != nullptr ||
@@ -647,6 +647,10 @@ int run_muse_bwd(const void* q, const void* k, const void* v, const void* dout, 
   km.t[1].labels_in = labels_k;
   km.t[0].perm = at<int32_t>(ws, P.perm_q);
   km.t[0].offs = at<int32_t>(ws, P.offs_q);
+  // the cluster size cap, as in the forward: kept lengths and flags of the key buckets
+  km.t[1].cap = cap_members(s, p);
+  km.t[1].klen = km.t[1].cap > 0 ? at<int32_t>(ws, P.klen) : nullptr;
+  km.t[1].kdrop = km.t[1].cap > 0 ? at<uint8_t>(ws, P.kdrop) : nullptr;
   hipError_t e = launch_kmeans(km, 1, s.dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "K-means launch");
   // the forward's stage-1 summaries as fp32 tables
@@ -738,6 +742,8 @@ int run_muse_bwd(const void* q, const void* k, const void* v, const void* dout, 
   b.scale = scale;
   b.dipole = dipole;
   b.labels_k = labels_k;
+  b.kdrop = km.t[1].kdrop;
+  b.klen = km.t[1].klen;
   b.qbar = km.t[0].cent;
   b.perm_q = km.t[0].perm;
   b.offs_q = km.t[0].offs;

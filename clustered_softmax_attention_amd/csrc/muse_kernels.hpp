@@ -303,6 +303,10 @@ struct BwArgs {
   float* st;                   // [BH, nb, Cq, Ck] the same of dL/dlog Z^b - S^b
   // (tilted) gd then holds, per (b', i), sh = sum_{b > b'} exp(lz^{b'+1} - lz^b) G_Dip^b
   // in the same four bf16 layouts ([BH, nb, Cq, 4, D, D])
+  // cluster size cap (null: none): keys left out of the summaries take no gradient
+  // through them; per bucket the kept members are a prefix of its positions
+  const uint8_t* kdrop;        // [BH, N] by input position
+  const int32_t* klen;         // [BH, nb*Ck] kept members per bucket
 };
 
 hipError_t launch_backward(const BwArgs& a, int dtype, hipStream_t s);

@@ -255,9 +255,17 @@ def test_backward_entry_rejects_before_launch(lib):
     assert call(ins=ins[:4] + (None, vp(6))) == -1  # labels are required
     assert call(outs=(vp(7), vp(7), vp(9))) == -1   # distinct outputs
     assert call(outs=(vp(1), vp(8), vp(9))) == -1   # no output aliases an input
+    # the cap is accepted (its workspace holds the kept lengths and flags); retrieval and
+    # the hierarchy are not
     p.cap_ratio = 1.5
-    assert call(pp=p) == -2
+    assert lib.muse_attn_bwd_workspace_bytes(1, 1, 1024, 64, 8, 32, 0, 0, 1, ctypes.byref(p)) > 0
     p.cap_ratio = 0.0
+    p.hierarchy = 1
+    assert call(causal=1, block=256, pp=p) == -2 and "hierarchy" in lib.muse_last_error().decode()
+    p.hierarchy = 0
+    p.topk_clusters, p.topk_blocks = 2, 1
+    assert call(causal=1, block=256, pp=p) == -2
+    p.topk_clusters, p.topk_blocks = 0, 0
     p.lse_out = 0x1000                              # no forward outputs
     assert call(pp=p) == -1
     p.lse_out = None

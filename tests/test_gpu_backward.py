@@ -41,14 +41,14 @@ def _dout(cfg, seed=7):
     return g
 
 
-def _gpu_grads(cfg, q, k, v, dO, dipole, scale=0.0):
+def _gpu_grads(cfg, q, k, v, dO, dipole, scale=0.0, cap_ratio=0.0):
     from clustered_softmax_attention_amd import attn_bwd
-    _, ex = run_gpu(cfg, q, k, v, dipole=dipole, scale=scale)
+    _, ex = run_gpu(cfg, q, k, v, dipole=dipole, scale=scale, cap_ratio=cap_ratio)
     lq = ex["labels_q_trace"][-1].contiguous()
     lk = ex["labels_k_trace"][-1].contiguous()
     Q, K, V, G = (to_device(t, cfg.dtype) for t in (q, k, v, dO))
     dq, dk, dv = attn_bwd(Q, K, V, G, lq, lk, cfg.Cq, cfg.Ck, causal=cfg.causal, block=cfg.block, scale=scale,
-                          dipole=dipole)
+                          dipole=dipole, cap_ratio=cap_ratio)
     torch.cuda.synchronize()
     return (dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()), lq.cpu().numpy(), lk.cpu().numpy()
 
@@ -57,18 +57,19 @@ def _oracle_dipole(dipole):
     return {True: "tilted", False: "none"}.get(dipole, dipole)
 
 
-def check_bwd(cfg, heads, dipole=True, scale=None):
+def check_bwd(cfg, heads, dipole=True, scale=None, cap_ratio=None):
     q, k, v = make_inputs(cfg)
     dO = _dout(cfg)
-    grads, lq, lk = _gpu_grads(cfg, q, k, v, dO, dipole, 0.0 if scale is None else scale)
+    grads, lq, lk = _gpu_grads(cfg, q, k, v, dO, dipole, 0.0 if scale is None else scale,
+                               0.0 if cap_ratio is None else cap_ratio)
     tol = BWD_TOL[cfg.dtype]
     for b, h in heads:
         if cfg.causal:
             ref = muse_causal_bwd(q[b, h], k[b, h], v[b, h], cfg.Cq, cfg.Ck, cfg.block, lq[b, h], lk[b, h],
-                                  dO[b, h], scale=scale, dipole=_oracle_dipole(dipole))
+                                  dO[b, h], scale=scale, dipole=_oracle_dipole(dipole), cap_ratio=cap_ratio)
         else:
             ref = muse_acausal_bwd(q[b, h], k[b, h], v[b, h], cfg.Cq, cfg.Ck, lq[b, h], lk[b, h], dO[b, h],
-                                   scale=scale, dipole=_oracle_dipole(dipole))
+                                   scale=scale, dipole=_oracle_dipole(dipole), cap_ratio=cap_ratio)
         for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
             rel = rel_l2(g[b, h], r)
             log(f"[{cfg.name} bwd {_oracle_dipole(dipole)}] head ({b},{h}) {name}: rel-L2 {rel:.3e} (tol {tol:.0e})")
@@ -169,6 +170,21 @@ def test_causal_bf16(muse_lib, dipole):
 def test_causal_shapes(muse_lib, name, over):
     cfg = scaled_config(name, **over)
     check_bwd(cfg, _heads(cfg))
+
+
+@pytest.mark.parametrize("name,over,dipole", [
+    ("acausal_8k", {"B": 1, "H": 2, "N": 2048, "iters": 1}, True),
+    ("acausal_8k", {"B": 1, "H": 1, "N": 2048, "iters": 1}, "untilted"),
+    ("acausal_1k_f32", {"iters": 1}, True),
+    ("causal_16k", {"B": 1, "H": 2, "N": 2048, "block": 512, "iters": 1}, True),
+    ("causal_16k", {"B": 1, "H": 1, "N": 2048, "block": 256, "iters": 1}, False),
+])
+def test_cap_one_iteration(muse_lib, name, over, dipole):
+    # the paper's speed setting: key clusters capped at 1.5 N / Ck members, one Lloyd
+    # iteration; the keys left out of the summaries get gradients only through their own
+    # block's exact attention (causal) or none (acausal)
+    cfg = scaled_config(name, **over)
+    check_bwd(cfg, _heads(cfg), dipole, cap_ratio=1.5)
 
 
 def test_causal_scale_one(muse_lib):
