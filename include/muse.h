@@ -236,14 +236,15 @@ int muse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out
  *                   [0, C) are clamped like labels_*_in
  *   dq, dk, dv      device float32 [B,H,N,D], written (not accumulated); distinct from
  *                   each other and from every input
- *   p               scale and dipole as in the forward call (NULL: defaults); workspace
+ *   p               scale, dipole and cap_ratio as in the forward call (NULL: defaults); workspace
  *                   and workspace_bytes as in muse_attn_fwd_ex, sized by
  *                   muse_attn_bwd_workspace_bytes. Every other field keeps its default
  *                   (MUSE_ERR_INVALID_ARG for the forward's output pointers).
  * Implemented for D = 64, acausal (every dipole mode) and causal (tilted dipole or none)
- * with the forward's block rules; other head sizes, the untilted dipole with causal = 1,
- * retrieval, the hierarchy and the cluster size cap return MUSE_ERR_UNSUPPORTED before
- * any launch. All
+ * with the forward's block rules, with or without the cluster size cap (p->cap_ratio as
+ * in the forward: keys left out of the summaries take no gradient through them); other
+ * head sizes, the untilted dipole with causal = 1, retrieval and the hierarchy return
+ * MUSE_ERR_UNSUPPORTED before any launch. All
  * arithmetic in fp32 (bf16 inputs are exact in it); results are deterministic (fixed
  * summation orders, no floating-point atomics). Work is queued on hip_stream.
  */
