@@ -120,7 +120,10 @@ __global__ void __launch_bounds__(kExThreads) exact_valu_kernel(ExactArgs a) {
 // EXACT_P: the weights enter the product with V as bf16 hi + lo and the normaliser as
 // their fp32 sum (output accurate to fp32 rounding; one more product per step), for the
 // backward pass's recomputation of the forward.
-template <int D, bool EXACT_P>
+// LSE32 (with EXACT_P false, when the log-sum-exp is an output): the log-sum-exp from a
+// second, fp32 sum of the weights (one more add per weight), while the output keeps the
+// sum of the bf16-rounded weights that enter its product with V.
+template <int D, bool EXACT_P, bool LSE32>
 __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt) {
   constexpr int BQ = 128, BK = 64;
   constexpr int KST = D + 16;  // bf16 elements per K and V row in LDS (padded)
@@ -170,7 +173,10 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
   const float sl2 = a.scale * 1.4426950408889634f;
   const float thr = 8.f / sl2;
 
-  float m = -1e30f, l = 0.f;
+  // l: the row sum of the weights as they enter the product with V (the output's
+  // normaliser); l32 (LSE32): their fp32 sum, for the log-sum-exp output (the bf16
+  // rounding of a dominant weight would otherwise shift it by up to 2^-8)
+  float m = -1e30f, l = 0.f, l32 = 0.f;
   f32x16_t o[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) o[mt] = zero16();
@@ -253,6 +259,7 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
         const float mn = __builtin_elementwise_maximum(m, mx);
         const float alpha = fast_exp2((m - mn) * sl2);
         l *= alpha;
+        if constexpr (LSE32) l32 *= alpha;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -301,6 +308,7 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
             }
           } else {
             const bf16x8_t bfr = pack_bf16x8(pv);
+            if constexpr (LSE32) l32 += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const bf16x2_t p2 = {bfr[2 * i], bfr[2 * i + 1]};
@@ -327,9 +335,10 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
     if (j + 1 < T) iteration(j + 1, sB, sA);
   }
   const float lt = l + xor32(l);
+  const float lt32 = LSE32 ? l32 + xor32(l32) : lt;
   if (!qvalid) return;
   const float inv = 1.f / lt;
-  float L = (m * sl2 + __log2f(lt)) * 0.6931471805599453f;
+  float L = (m * sl2 + __log2f(lt32)) * 0.6931471805599453f;
   const size_t row = base + qi;
   float w0 = inv, w1 = 0.f;
   bool merge = false;
@@ -375,11 +384,14 @@ hipError_t launch_exact(const ExactArgs& a, int dtype, hipStream_t s) {
     ProfScope ps_(a.block > 0 ? "local_block_mfma" : "exact_mfma", s);
     const dim3 g(nqt * a.BH);
     if (a.exact_p) {
-      if (a.D == 64) hipLaunchKernelGGL((flash_bf16_kernel<64, true>), g, dim3(256), 0, s, a, nqt);
-      else hipLaunchKernelGGL((flash_bf16_kernel<128, true>), g, dim3(256), 0, s, a, nqt);
+      if (a.D == 64) hipLaunchKernelGGL((flash_bf16_kernel<64, true, false>), g, dim3(256), 0, s, a, nqt);
+      else hipLaunchKernelGGL((flash_bf16_kernel<128, true, false>), g, dim3(256), 0, s, a, nqt);
+    } else if (a.lse_out != nullptr) {
+      if (a.D == 64) hipLaunchKernelGGL((flash_bf16_kernel<64, false, true>), g, dim3(256), 0, s, a, nqt);
+      else hipLaunchKernelGGL((flash_bf16_kernel<128, false, true>), g, dim3(256), 0, s, a, nqt);
     } else {
-      if (a.D == 64) hipLaunchKernelGGL((flash_bf16_kernel<64, false>), g, dim3(256), 0, s, a, nqt);
-      else hipLaunchKernelGGL((flash_bf16_kernel<128, false>), g, dim3(256), 0, s, a, nqt);
+      if (a.D == 64) hipLaunchKernelGGL((flash_bf16_kernel<64, false, false>), g, dim3(256), 0, s, a, nqt);
+      else hipLaunchKernelGGL((flash_bf16_kernel<128, false, false>), g, dim3(256), 0, s, a, nqt);
     }
     return hipGetLastError();
   }

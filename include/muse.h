@@ -124,7 +124,10 @@ typedef struct muse_fwd_params {
   int32_t* labels_k_trace;     /* device [iters,B,H,N]                                   */
   float* centroids_q_out;      /* device [B,H,Cq,D]: final query centroids               */
   float* centroids_k_out;      /* device [B,H,Ck,D]: final key centroids                 */
-  float* lse_out;              /* device [B,H,N]: log of each row's softmax normaliser   */
+  float* lse_out;              /* device [B,H,N]: log of each row's softmax normaliser
+                                  (bf16 inputs: requesting it adds an fp32 sum of the
+                                  in-block weights beside the sum of their bf16-rounded
+                                  values that normalises the output)                      */
   void* workspace;             /* device scratch; NULL = stream-ordered allocation       */
   size_t workspace_bytes;      /* size of `workspace`                                     */
   int32_t* retrieval_trace;    /* device [B,H,N/block,Cq,k1*(1+k2)]: per (block, query
