@@ -392,20 +392,44 @@ __global__ void __launch_bounds__(256) retr_exact_kernel(RetrArgs a) {
   }
 }
 
-// Matrix-core exact part for bf16 inputs: one workgroup of 4 waves per chunk of up to 128
-// queries of bucket (b, i) (wave w: queries 32 w .. 32 w + 31). The retrieved keys are the
-// concatenation of the chosen atoms' ranges of the key permutation; they stream through
-// LDS 32 at a time (K and V rows, bf16, gathered by 16-byte loads), and on the matrix
-// cores
+// Position pos of the concatenated retrieved ranges -> key row (head-local index).
+__device__ __forceinline__ int retr_key_row(const int* s_start, const int* s_cum, int nr, const int32_t* permk,
+                                            int pos) {
+  int lo = 0, hi = nr - 1;  // last range with s_cum <= pos
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_cum[mid] <= pos) lo = mid;
+    else hi = mid - 1;
+  }
+  return permk[s_start[lo] + pos - s_cum[lo]];
+}
+
+// Matrix-core exact part for bf16 inputs. One workgroup of 4 waves per stage-2 chunk (up
+// to 128 queries of bucket (b, i)). With more than 64 queries, wave w takes queries
+// 32 w .. + 31 and all keys; with at most 64 (the usual case), wave w takes queries
+// 32 (w & 1) .. + 31 and, of every 64 staged keys, keys 32 (w >> 1) .. + 31, so that all
+// four waves work. The retrieved keys are the concatenation of the
+// chosen atoms' ranges of the key permutation; 64 at a time are gathered (16-byte row
+// pieces) into one of two LDS buffers while the other is in use, one barrier per step.
+// On the matrix cores
 //   l^T = K q^T (32 keys x 32 queries; bf16 operands are exact, fp32 accumulation),
 //   online softmax over the keys, O^T += V^T P^T (P split into bf16 hi + lo),
-// as in the stage-2 kernel; the result is merged into the far field by log-sum-exp.
+// and at the end the two key halves of each query group (when split) are merged by
+// log-sum-exp and the result merged into the far field of the query.
 template <int D>
-__global__ void __launch_bounds__(256, 2) retr_exact_mfma_kernel(RetrArgs a) {
-  constexpr int NKS = D / 16, NMT = D / 32, JC = 32, KST = D + 16;
-  constexpr int NK = JC * D / 8 / 256;  // 16-byte row pieces per thread and tensor
-  __shared__ __align__(16) uint16_t sK[JC * KST];
-  __shared__ __align__(16) uint16_t sV[JC * KST];
+struct RetrExactCfg {
+  static constexpr int JC = 64, KST = D + 8, NKS = D / 16, NMT = D / 32;
+  static constexpr int NK = JC * D / 8 / 256;  // 16-byte row pieces per thread and tensor
+  static constexpr size_t lds_bytes = 2 * 2 * JC * KST * sizeof(uint16_t);
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, D == 64 ? 3 : 2) retr_exact_mfma_kernel(RetrArgs a) {
+  using Cfg = RetrExactCfg<D>;
+  constexpr int NKS = Cfg::NKS, NMT = Cfg::NMT, JC = Cfg::JC, KST = Cfg::KST, NK = Cfg::NK;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* sK = reinterpret_cast<uint16_t*>(smem);  // [2][JC * KST]
+  uint16_t* sV = sK + 2 * JC * KST;                   // [2][JC * KST]
   __shared__ int s_start[kMaxRetrRow];    // first permutation position of each range
   __shared__ int s_cum[kMaxRetrRow + 1];  // exclusive prefix of the range lengths
   __shared__ int s_nr;
@@ -415,6 +439,10 @@ __global__ void __launch_bounds__(256, 2) retr_exact_mfma_kernel(RetrArgs a) {
   const int2 tile = a.tiles[static_cast<size_t>(bh) * a.max_tiles + tix];
   const int u = tile.x, b = u / a.Cq, i = u % a.Cq;
   if (b == 0) return;  // the first block retrieves nothing
+  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (a.nb * a.Cq + 1);
+  const int qend = min(offq[u + 1], tile.y + kS2Chunk);  // this chunk's queries end here
+  const bool split = qend - tile.y <= 64;                // uniform
+  const int g = split ? wave & 1 : wave, kp = split ? wave >> 1 : 0;
   const int Ck = a.Ck, k1 = a.k1, k2 = a.k2, row = k1 * (1 + k2);
   if (wave == 0) {
     const int32_t* sel = a.sel + ((static_cast<size_t>(bh) * a.nb + b) * a.Cq + i) * row;
@@ -422,127 +450,169 @@ __global__ void __launch_bounds__(256, 2) retr_exact_mfma_kernel(RetrArgs a) {
     const int n = retr_ranges(sel, offk, Ck, k1, k2, s_start, s_cum);
     if (lane == 0) s_nr = n;
   }
-  __syncthreads();
-  const int nr = s_nr, nR = s_cum[nr];
-  if (nR == 0) return;  // nothing retrieved (uniform: read from LDS by every thread)
-  const int32_t* offq = a.offs_q + static_cast<size_t>(bh) * (a.nb * a.Cq + 1);
-  const int st = tile.y + 32 * wave;
-  const int qn = a.perm_q[static_cast<size_t>(bh) * a.N + min(st + c, a.N - 1)];
-  const int nw = max(0, min(32, offq[u + 1] - st));  // queries of this wave
+  const int st = tile.y + 32 * g;
+  const int nw = max(0, min(32, qend - st));  // queries of this wave
   const bool valid = c < nw;
+  const int qn = a.perm_q[static_cast<size_t>(bh) * a.N + min(st + c, a.N - 1)];
   const size_t rowq = static_cast<size_t>(bh) * a.N + qn;
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
-  const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
-  const int32_t* permk = a.perm_k + static_cast<size_t>(bh) * a.N;
   // query fragments (B operand: column = query c, k = d); exact in bf16
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   bf16x8_t qf[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(Q + rowq * D + 16 * ks + 8 * h));
-  // rows of chunk ch into registers: position pos of the concatenated ranges
+  __syncthreads();
+  const int nr = s_nr, nR = s_cum[nr];
+  if (nR == 0) return;  // nothing retrieved (uniform: read from LDS by every thread)
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
+  const int32_t* permk = a.perm_k + static_cast<size_t>(bh) * a.N;
+  // the gather runs two steps ahead in two stages: the key rows of step ch + 2 (loads of
+  // the permutation) and the K, V rows of step ch + 1 are requested together, so that no
+  // load waits on another inside a step
+  int prow[NK];
   u16x8_t pk[NK], pv[NK];
-  auto load_chunk = [&](int ch) {
+  auto resolve = [&](int ch) {
 #pragma unroll
     for (int q = 0; q < NK; ++q) {
-      const int x = tid + 256 * q, r = x / (D / 8), d8 = (x % (D / 8)) * 8;
-      const int pos = ch * JC + r;
+      const int pos = ch * JC + (tid + 256 * q) / (D / 8);
+      prow[q] = pos < nR ? retr_key_row(s_start, s_cum, nr, permk, pos) : -1;
+    }
+  };
+  auto fetch = [&]() {
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+      const int d8 = ((tid + 256 * q) % (D / 8)) * 8;
       pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       pv[q] = pk[q];
-      if (pos < nR) {
-        int lo = 0, hi = nr - 1;  // last range with s_cum <= pos
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_cum[mid] <= pos) lo = mid;
-          else hi = mid - 1;
-        }
-        const size_t kr = static_cast<size_t>(permk[s_start[lo] + pos - s_cum[lo]]) * D + d8;
+      if (prow[q] >= 0) {
+        const size_t kr = static_cast<size_t>(prow[q]) * D + d8;
         pk[q] = *reinterpret_cast<const u16x8_t*>(K + kr);
         pv[q] = *reinterpret_cast<const u16x8_t*>(V + kr);
       }
     }
   };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+      const int x = tid + 256 * q, r = x / (D / 8), d8 = (x % (D / 8)) * 8;
+      *reinterpret_cast<u16x8_t*>(sK + buf * JC * KST + r * KST + d8) = pk[q];
+      *reinterpret_cast<u16x8_t*>(sV + buf * JC * KST + r * KST + d8) = pv[q];
+    }
+  };
   const int nch = (nR + JC - 1) / JC;
-  load_chunk(0);
+  resolve(0);
+  fetch();
+  store_chunk(0);
+  if (nch > 1) resolve(1);
+  __syncthreads();
   const float sl2 = a.scale * 1.4426950408889634f;
   float mx = kNegInf, z = 0.f;  // running max (log2 units) and sum of this lane pair's query
   f32x16_t o[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) o[mt] = zero16();
   for (int ch = 0; ch < nch; ++ch) {
-    __syncthreads();  // previous chunk consumed
-#pragma unroll
-    for (int q = 0; q < NK; ++q) {
-      const int x = tid + 256 * q, r = x / (D / 8), d8 = (x % (D / 8)) * 8;
-      *reinterpret_cast<u16x8_t*>(sK + r * KST + d8) = pk[q];
-      *reinterpret_cast<u16x8_t*>(sV + r * KST + d8) = pv[q];
+    if (ch + 1 < nch) {  // in flight during this step
+      fetch();
+      if (ch + 2 < nch) resolve(ch + 2);
     }
-    __syncthreads();
-    if (ch + 1 < nch) load_chunk(ch + 1);
-    if (nw == 0) continue;
-    // logits^T of the chunk (rows = keys, column = query), log2 units
-    f32x16_t lg = zero16();
+    for (int sub = kp; sub < 2; sub += split ? 2 : 1) {
+      const int k0 = ch * JC + 32 * sub;  // first of these 32 keys
+      if (nw == 0 || k0 >= nR) break;
+      const uint16_t* kt = sK + (ch & 1) * JC * KST + 32 * sub * KST;
+      const uint16_t* vt = sV + (ch & 1) * JC * KST + 32 * sub * KST;
+      // logits^T of the 32 keys (rows = keys, column = query), log2 units
+      f32x16_t lg = zero16();
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      lg = mfma32(as_bf16x8(*reinterpret_cast<const u16x8_t*>(sK + c * KST + 16 * ks + 8 * h)), qf[ks], lg);
-    float cm = kNegInf;
+      for (int ks = 0; ks < NKS; ++ks)
+        lg = mfma32(as_bf16x8(*reinterpret_cast<const u16x8_t*>(kt + c * KST + 16 * ks + 8 * h)), qf[ks], lg);
+      float cm = kNegInf;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = ch * JC + 8 * (v >> 2) + 4 * h + (v & 3);
-      const float x = key < nR ? sl2 * lg[v] : kNegInf;
-      lg[v] = x;
-      cm = fmaxf(cm, x);
-    }
-    cm = fmaxf(cm, xor32(cm));
-    const float mn = fmaxf(mx, cm);  // finite: every chunk holds at least one key
-    const float alpha = mx == kNegInf ? 0.f : fast_exp2(mx - mn);
-    const bool grow = mn > mx && mx != kNegInf;
-    mx = mn;
-    float zs = 0.f;
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + 8 * (v >> 2) + 4 * h + (v & 3);
+        const float x = key < nR ? sl2 * lg[v] : kNegInf;
+        lg[v] = x;
+        cm = fmaxf(cm, x);
+      }
+      cm = fmaxf(cm, xor32(cm));
+      const float mn = fmaxf(mx, cm);  // finite: key k0 < nR is among the 32
+      const float alpha = mx == kNegInf ? 0.f : fast_exp2(mx - mn);
+      const bool grow = mn > mx && mx != kNegInf;
+      mx = mn;
+      float zs = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = fast_exp2(lg[v] - mn);
-      lg[v] = p;
-      zs += p;
-    }
-    z = z * alpha + zs + xor32(zs);
-    if (__ballot(grow) != 0ull) {
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(lg[v] - mn);
+        lg[v] = p;
+        zs += p;
+      }
+      z = z * alpha + zs + xor32(zs);
+      if (__ballot(grow) != 0ull) {
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
+        for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
-    }
-    // O^T += V^T P^T: k-slots of step ss are rows 16 ss + 4 h + 0..3 and 16 ss + 8 + 4 h + 0..3
+          for (int v = 0; v < 16; ++v) o[mt][v] *= alpha;
+      }
+      // O^T += V^T P^T: k-slots of step ss are rows 16 ss + 4 h + 0..3 and 16 ss + 8 + 4 h + 0..3
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      float pv8[8];
+      for (int ss = 0; ss < 2; ++ss) {
+        float pv8[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) pv8[r] = lg[8 * ss + r];
-      bf16x8_t phi, plo;
-      split_bf16x8(pv8, phi, plo);
+        for (int r = 0; r < 8; ++r) pv8[r] = lg[8 * ss + r];
+        bf16x8_t phi, plo;
+        split_bf16x8(pv8, phi, plo);
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        const bf16x8_t hv = lds_operand_tr_acc(sV, KST, 16 * ss, 32 * mt, lane);
-        o[mt] = mfma32(hv, phi, o[mt]);
-        o[mt] = mfma32(hv, plo, o[mt]);
+        for (int mt = 0; mt < NMT; ++mt) {
+          const bf16x8_t hv = lds_operand_tr_acc(vt, KST, 16 * ss, 32 * mt, lane);
+          o[mt] = mfma32(hv, phi, o[mt]);
+          o[mt] = mfma32(hv, plo, o[mt]);
+        }
       }
     }
+    if (ch + 1 < nch) store_chunk((ch + 1) & 1);  // the buffer of step ch - 1, free since its barrier
+    __syncthreads();
   }
-  if (!valid) return;
+  // split workgroups: merge the key halves of each query group, waves kp = 1 hand (max,
+  // sum, O) over in LDS
+  // (lane-major, so that the partner lane reads the same index)
+  float* xo = reinterpret_cast<float*>(smem);  // [2][NMT][16][64]
+  float* xm = xo + 2 * NMT * 16 * 64;         // [2][64]
+  float* xz = xm + 2 * 64;                    // [2][64]
+  if (split && kp == 1) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) xo[((g * NMT + mt) * 16 + v) * 64 + lane] = o[mt][v];
+    xm[g * 64 + lane] = mx;
+    xz[g * 64 + lane] = z;
+  }
+  __syncthreads();
+  if (kp == 1 || !valid) return;
+  if (split) {
+    const float m1 = xm[g * 64 + lane], z1 = xz[g * 64 + lane];
+    const float M = fmaxf(mx, m1);  // finite: this wave saw key 0
+    const float f0 = fast_exp2(mx - M), f1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - M);
+    z = z * f0 + z1 * f1;
+    mx = M;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[mt][v] = o[mt][v] * f0 + xo[((g * NMT + mt) * 16 + v) * 64 + lane] * f1;
+  }
   // merge with the far field of the query: L = log(e^LR + e^Lf), o = e^(LR-L) o_R + e^(Lf-L) o_f
   const float LR = (mx + __log2f(z)) * 0.6931471805599453f;
   const float lf = a.l_far[rowq];
   const float Lt = lf == kNegInf ? LR : fmaxf(LR, lf) + log1pf(__expf(-fabsf(LR - lf)));
   const float w0 = __expf(LR - Lt) / z, w1 = lf == kNegInf ? 0.f : __expf(lf - Lt);
-  // lanes (c, h) hold rows d = 32 mt + 8 g + 4 h + r of query c
+  // lanes (c, h) hold rows d = 32 mt + 8 gg + 4 h + r of query c
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float* dst = a.o_far + rowq * D + 32 * mt + 8 * g + 4 * h;
+    for (int gg = 0; gg < 4; ++gg) {
+      float* dst = a.o_far + rowq * D + 32 * mt + 8 * gg + 4 * h;
       const f32x4_t f = *reinterpret_cast<const f32x4_t*>(dst);
       f32x4_t r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = w0 * o[mt][4 * g + e] + w1 * f[e];
+      for (int e = 0; e < 4; ++e) r[e] = w0 * o[mt][4 * gg + e] + w1 * f[e];
       *reinterpret_cast<f32x4_t*>(dst) = r;
     }
   if (h == 0) a.l_far[rowq] = Lt;
@@ -550,27 +620,35 @@ __global__ void __launch_bounds__(256, 2) retr_exact_mfma_kernel(RetrArgs a) {
 
 // Second moment without the retrieved keys for bf16 inputs, one workgroup of 4 waves per
 // (i, b): E_i[v k^T] of the entry becomes (E - sum_R w v k^T) / (1 - sum_R w), with
-// w_m = exp(s qbar_i . k_m - R) relative to the prefix log mass R. The retrieved keys
-// stream through LDS 32 at a time (K and V rows, exact in bf16); the weights in fp32, one
-// thread per key; sum_R (w v) k^T on the matrix cores with w v split into bf16 hi + lo.
+// w_m = exp(s qbar_i . k_m - R) relative to the prefix log mass R. The retrieved keys are
+// gathered 64 at a time into one of two LDS buffers (K and V rows, exact in bf16) while
+// the other is in use, one barrier per step; each key's weight comes from the D / 8
+// threads that load its row (fp32 partial dots, summed across those lanes) and is staged
+// beside the rows; sum_R (w v) k^T on the matrix cores with w v split into bf16 hi + lo.
+template <int D>
+struct RetrMomCfg {
+  static constexpr int JC = 64, ST = D + 8, NDT = D / 32, TPW = NDT * NDT / 4, NP = JC * D / 8 / 256, TPR = D / 8;
+  static constexpr size_t lds_bytes = 2 * 2 * JC * ST * sizeof(uint16_t) + 2 * JC * sizeof(float);
+};
+
 template <int D>
 __global__ void __launch_bounds__(256) retr_moment_mfma_kernel(RetrArgs a) {
-  constexpr int JC = 32, ST = D + 8, NDT = D / 32, TPW = NDT * NDT / 4, NP = JC * D / 8 / 256;
-  __shared__ __align__(16) uint16_t sK[JC * ST];
-  __shared__ __align__(16) uint16_t sV[JC * ST];
-  __shared__ float s_q[D];
-  __shared__ float sW[JC];
-  __shared__ float s_red[2];
+  using Cfg = RetrMomCfg<D>;
+  constexpr int JC = Cfg::JC, ST = Cfg::ST, NDT = Cfg::NDT, TPW = Cfg::TPW, NP = Cfg::NP, TPR = Cfg::TPR;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* sK = reinterpret_cast<uint16_t*>(smem);       // [2][JC * ST]
+  uint16_t* sV = sK + 2 * JC * ST;                         // [2][JC * ST]
+  float* sW = reinterpret_cast<float*>(sV + 2 * JC * ST);  // [2][JC]
+  __shared__ float s_red[1 + 4];
   __shared__ int s_start[kMaxRetrRow];
   __shared__ int s_cum[kMaxRetrRow + 1];
   __shared__ int s_nr;
   const int i = blockIdx.x, b = blockIdx.y, bh = blockIdx.z;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int h = lane >> 5, c = lane & 31;
+  const int h = lane >> 5;
   if (b == 0) return;
   const int Ck = a.Ck, k1 = a.k1, k2 = a.k2, row = k1 * (1 + k2);
   const size_t sidx = (static_cast<size_t>(bh) * a.nb + b) * a.Cq + i;
-  for (int d = tid; d < D; d += 256) s_q[d] = a.qbar[(static_cast<size_t>(bh) * a.Cq + i) * D + d];
   if (wave == 0) {
     // prefix log mass of the entry
     float mx = kNegInf;
@@ -589,6 +667,14 @@ __global__ void __launch_bounds__(256) retr_moment_mfma_kernel(RetrArgs a) {
     const int n = retr_ranges(sel, offk, Ck, k1, k2, s_start, s_cum);
     if (lane == 0) s_nr = n;
   }
+  // this thread's 8 features of s qbar_i (every row piece it loads starts at feature d8)
+  const int d8 = (tid % TPR) * 8;
+  float qs[8];
+  {
+    const float* qb = a.qbar + (static_cast<size_t>(bh) * a.Cq + i) * D + d8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qs[e] = a.scale * qb[e];
+  }
   __syncthreads();
   const float Rpre = s_red[0];
   const int nr = s_nr, nR = s_cum[nr];
@@ -596,71 +682,98 @@ __global__ void __launch_bounds__(256) retr_moment_mfma_kernel(RetrArgs a) {
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(bh) * a.N * D;
   const int32_t* permk = a.perm_k + static_cast<size_t>(bh) * a.N;
+  // the gather runs two steps ahead in two stages (key rows of step ch + 2, K and V rows
+  // of step ch + 1, requested together)
+  int prow[NP];
+  u16x8_t pk[NP], pv[NP];
+  auto resolve = [&](int ch) {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int pos = ch * JC + (tid + 256 * q) / TPR;
+      prow[q] = pos < nR ? retr_key_row(s_start, s_cum, nr, permk, pos) : -1;
+    }
+  };
+  auto fetch = [&]() {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      pk[q] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      pv[q] = pk[q];
+      if (prow[q] >= 0) {
+        const size_t kr = static_cast<size_t>(prow[q]) * D + d8;
+        pk[q] = *reinterpret_cast<const u16x8_t*>(K + kr);
+        pv[q] = *reinterpret_cast<const u16x8_t*>(V + kr);
+      }
+    }
+  };
+  float wsum = 0.f;  // lanes with tid % TPR == 0: their rows' weights
+  auto store_chunk = [&](int ch) {
+    const int buf = ch & 1;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int r = (tid + 256 * q) / TPR;
+      *reinterpret_cast<u16x8_t*>(sK + buf * JC * ST + r * ST + d8) = pk[q];
+      *reinterpret_cast<u16x8_t*>(sV + buf * JC * ST + r * ST + d8) = pv[q];
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf(qs[e], bf16_to_f32(pk[q][e]), dot);
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) dot += __shfl_xor(dot, o, 64);
+      if (tid % TPR == 0) {
+        const float w = ch * JC + r < nR ? __expf(dot - Rpre) : 0.f;
+        sW[buf * JC + r] = w;
+        wsum += w;
+      }
+    }
+  };
   f32x16_t acc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) acc[t] = zero16();
-  float wsum = 0.f;  // threads 0..31: their keys' weights
-  for (int c0 = 0; c0 < nR; c0 += JC) {
-    __syncthreads();  // previous chunk consumed
-#pragma unroll
-    for (int q = 0; q < NP; ++q) {
-      const int x = tid + 256 * q, r = x / (D / 8), d8 = (x % (D / 8)) * 8, pos = c0 + r;
-      u16x8_t k8 = {0, 0, 0, 0, 0, 0, 0, 0}, v8 = k8;
-      if (pos < nR) {
-        int lo = 0, hi = nr - 1;  // last range with s_cum <= pos
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_cum[mid] <= pos) lo = mid;
-          else hi = mid - 1;
-        }
-        const size_t kr = static_cast<size_t>(permk[s_start[lo] + pos - s_cum[lo]]) * D + d8;
-        k8 = *reinterpret_cast<const u16x8_t*>(K + kr);
-        v8 = *reinterpret_cast<const u16x8_t*>(V + kr);
-      }
-      *reinterpret_cast<u16x8_t*>(sK + r * ST + d8) = k8;
-      *reinterpret_cast<u16x8_t*>(sV + r * ST + d8) = v8;
+  const int nch = (nR + JC - 1) / JC;
+  resolve(0);
+  fetch();
+  store_chunk(0);
+  if (nch > 1) resolve(1);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    if (ch + 1 < nch) {  // in flight during this step
+      fetch();
+      if (ch + 2 < nch) resolve(ch + 2);
     }
-    __syncthreads();
-    if (tid < JC) {
-      float w = 0.f;
-      if (c0 + tid < nR) {
-        float dot = 0.f;
-        for (int d = 0; d < D; ++d) dot = fmaf(s_q[d], bf16_to_f32(sK[tid * ST + d]), dot);
-        w = __expf(a.scale * dot - Rpre);
-      }
-      sW[tid] = w;
-      wsum += w;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < JC / 16; ++ks) {
+    const int buf = ch & 1;
+    const uint16_t* kt = sK + buf * JC * ST;
+    const uint16_t* vt = sV + buf * JC * ST;
+    const int nks = min(JC, nR - ch * JC + 15) / 16;  // 16-key steps holding retrieved keys
+    for (int ks = 0; ks < nks; ++ks) {
       float pw[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) pw[q] = sW[16 * ks + 8 * h + q];
+      for (int q = 0; q < 8; ++q) pw[q] = sW[buf * JC + 16 * ks + 8 * h + q];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
-        const u16x8_t vb = __builtin_bit_cast(u16x8_t, lds_operand_tr(sV, ST, 16 * ks, 32 * dvt, lane));
+        const u16x8_t vb = __builtin_bit_cast(u16x8_t, lds_operand_tr(vt, ST, 16 * ks, 32 * dvt, lane));
         float av[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) av[q] = bf16_to_f32(vb[q]) * pw[q];
         bf16x8_t ah, al;
         split_bf16x8(av, ah, al);
-        const bf16x8_t kb = lds_operand_tr(sK, ST, 16 * ks, 32 * dkt, lane);
+        const bf16x8_t kb = lds_operand_tr(kt, ST, 16 * ks, 32 * dkt, lane);
         acc[t] = mfma32(ah, kb, acc[t]);
         acc[t] = mfma32(al, kb, acc[t]);
       }
     }
+    if (ch + 1 < nch) store_chunk(ch + 1);  // the buffer of step ch - 1, free since its barrier
+    __syncthreads();
   }
-  if (wave == 0) {
+  {
     const float ws = wave_sum(wsum);
-    if (lane == 0) s_red[1] = ws;
+    if (lane == 0) s_red[1 + wave] = ws;
   }
   __syncthreads();
-  const float rest = 1.f - s_red[1];
+  const float rest = 1.f - ((s_red[1] + s_red[2]) + (s_red[3] + s_red[4]));
   const float inv = rest > 1e-30f ? 1.f / rest : 0.f;
   float* dip = a.s_dip + sidx * D * D;  // [dv][dk], holds the prefix E[v k^T]
   // lanes (c, h) hold rows dv = 32 dvt + 8 (v / 4) + 4 h + v % 4 of column dk = 32 dkt + c
+  const int c = lane & 31;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int ot = wave * TPW + t, dvt = ot / NDT, dkt = ot % NDT;
@@ -681,8 +794,13 @@ hipError_t launch_retrieval(const RetrArgs& a, int phase, int dtype, hipStream_t
     }
     if (dtype == 1 && a.dipole) {
       ProfScope ps_("retr_moment_mfma", s);
-      if (a.D == 64) hipLaunchKernelGGL((retr_moment_mfma_kernel<64>), g, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((retr_moment_mfma_kernel<128>), g, dim3(256), 0, s, a);
+      if (a.D == 64) {
+        allow_lds((const void*)retr_moment_mfma_kernel<64>, RetrMomCfg<64>::lds_bytes);
+        hipLaunchKernelGGL((retr_moment_mfma_kernel<64>), g, dim3(256), RetrMomCfg<64>::lds_bytes, s, a);
+      } else {
+        allow_lds((const void*)retr_moment_mfma_kernel<128>, RetrMomCfg<128>::lds_bytes);
+        hipLaunchKernelGGL((retr_moment_mfma_kernel<128>), g, dim3(256), RetrMomCfg<128>::lds_bytes, s, a);
+      }
     }
     ProfScope ps_("retr_tables", s);
     if (dtype == 0) {
@@ -696,8 +814,13 @@ hipError_t launch_retrieval(const RetrArgs& a, int phase, int dtype, hipStream_t
     ProfScope ps_("retr_exact", s);
     if (dtype == 1 && a.tiles != nullptr) {
       const dim3 gm(a.max_tiles, a.BH);
-      if (a.D == 64) hipLaunchKernelGGL((retr_exact_mfma_kernel<64>), gm, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((retr_exact_mfma_kernel<128>), gm, dim3(256), 0, s, a);
+      if (a.D == 64) {
+        allow_lds((const void*)retr_exact_mfma_kernel<64>, RetrExactCfg<64>::lds_bytes);
+        hipLaunchKernelGGL((retr_exact_mfma_kernel<64>), gm, dim3(256), RetrExactCfg<64>::lds_bytes, s, a);
+      } else {
+        allow_lds((const void*)retr_exact_mfma_kernel<128>, RetrExactCfg<128>::lds_bytes);
+        hipLaunchKernelGGL((retr_exact_mfma_kernel<128>), gm, dim3(256), RetrExactCfg<128>::lds_bytes, s, a);
+      }
     } else if (dtype == 0) {
       if (a.D == 64) hipLaunchKernelGGL((retr_exact_kernel<float, 64>), g, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((retr_exact_kernel<float, 128>), g, dim3(256), 0, s, a);
