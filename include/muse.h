@@ -41,8 +41,10 @@
  *     implement returns MUSE_ERR_UNSUPPORTED: D not in {64, 128}, Cq or Ck above
  *     128, a causal block below 64 or not a multiple of 64.
  *   - Value range (bf16 inputs): the block second moments take keys and values as
- *     fp16 operands (bf16 converts exactly), so every |k| and |v| element must stay
- *     below 65504; larger elements give infinite or NaN outputs.
+ *     fp16 operands, so every |k| and |v| element must stay below 65504 (larger ones
+ *     give infinite or NaN outputs). bf16 converts to fp16 exactly for magnitudes from
+ *     2^-14 up; smaller ones keep fewer bits (fp16 subnormals) or become zero below
+ *     2^-25, a change far below the stated tolerances.
  */
 #ifndef MUSE_H_
 #define MUSE_H_
