@@ -220,6 +220,33 @@ def test_retrieval_bf16_d128(muse_lib):
     check_config(cfg, [(0, 0), (0, 1)])
 
 
+def _bucket_sizes(cfg, q, k, v):
+    """Queries per (block, query cluster) bucket of blocks b >= 1 (head (0, 0))."""
+    _, ex = run_gpu(cfg, q, k, v, extra_returns=True)
+    offs = ex["offs_q"][0, 0].cpu().numpy().astype(np.int64)
+    return np.diff(offs)[cfg.Cq:]
+
+
+def test_retrieval_wide_and_narrow_buckets(muse_lib):
+    # four query clusters per block of 512: buckets of more than 64 queries (each of the
+    # exact part's waves takes its own 32 queries and every retrieved key) beside chunk
+    # remainders of at most 64 (wave pairs split the keys and merge their halves); about
+    # 128 retrieved keys per entry: two 64-key staging steps
+    cfg = scaled_config("retrieval_16k", B=1, H=1, N=2048, block=512, Cq=4, Ck=16, topk_clusters=2, topk_blocks=2)
+    q, k, v = make_inputs(cfg)
+    sizes = _bucket_sizes(cfg, q, k, v)
+    chunks = np.concatenate([np.minimum(128, np.maximum(0, sizes - 128 * c)) for c in range(4)])
+    assert (chunks > 64).any() and ((chunks > 0) & (chunks <= 64)).any(), sizes
+    check_config(cfg, [(0, 0)], inputs=(q, k, v))
+
+
+def test_retrieval_few_keys(muse_lib):
+    # one cluster and one block retrieved out of 64 clusters: about eight keys per entry,
+    # so the second key half of every staging step is empty
+    cfg = scaled_config("retrieval_16k", B=1, H=1, N=2048, block=512, Cq=16, Ck=64, topk_clusters=1, topk_blocks=1)
+    check_config(cfg, [(0, 0)])
+
+
 def test_retrieval_of_everything_is_exact_d128(muse_lib):
     cfg = scaled_config("causal_64k_d128", B=1, H=1, N=2048, block=256, Cq=8, Ck=16, topk_clusters=16,
                         topk_blocks=8)
