@@ -1000,7 +1000,33 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
         }
       }
     };
-    if (Cfg::PREF && fold) load_atoms();  // lands while entry b is written
+    // this lane's elements of the block's first moment range (D = 64: requested now, they
+    // land while entry b is written; D = 128: requested together at the fold)
+    float mpre[TPW][16];
+    auto load_moment = [&](int sub) {
+      const float* M = a.blk_mom + ((static_cast<size_t>(bh) * a.nmb + b * per + sub) * Cq + i) * D * D;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        int dvt, dkt;
+        if (!tile_of(t, dvt, dkt)) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          mpre[t][v] = M[static_cast<size_t>(32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3)) * D + 32 * dkt + c];
+      }
+    };
+    if (Cfg::PREF && fold) {
+      load_atoms();
+      if (a.dipole) load_moment(0);
+    }
+    // the block's atom masses and first moment range's log mass, requested now
+    float pam = kNegInf, paz = 0.f, pR = kNegInf;
+    if (fold) {
+      if (tid < Ck) {
+        pam = a.at_m[abase + tid];
+        paz = a.at_z[abase + tid];
+      }
+      if (a.dipole) pR = a.blk_lmass[(static_cast<size_t>(bh) * a.nmb + b * per) * Cq + i];
+    }
     __syncthreads();  // sm, sz of the prefix are final
     if (b > 0) {
       // ---- entry b: log Z, P, normalised tables ----
@@ -1122,7 +1148,7 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
     if (!fold) break;
     // ---- fold block b ----
     if (tid < Ck) {
-      const float am = a.at_m[abase + tid], az = a.at_z[abase + tid];
+      const float am = pam, az = paz;
       const float m0 = sm[tid], z0 = sz[tid];
       float fo = 1.f, fn = 0.f;
       if (az > 0.f) {
@@ -1138,9 +1164,11 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
     if (a.dipole) {
       for (int sub = 0; sub < per; ++sub) {
         const size_t bidx = (static_cast<size_t>(bh) * a.nmb + b * per + sub) * Cq + i;
-        const float R = a.blk_lmass[bidx];
+        // every element of the range in flight at once (the moments are written for every
+        // range, also one of zero mass)
+        if (!(Cfg::PREF && sub == 0)) load_moment(sub);
+        const float R = sub == 0 ? pR : a.blk_lmass[bidx];
         if (R == kNegInf) continue;
-        const float* M = a.blk_mom + bidx * D * D;
         const float Rn = fmaxf(Rm, R);
         const float fo = Rm == kNegInf ? 0.f : __expf(Rm - Rn), fn = __expf(R - Rn);
 #pragma unroll
@@ -1151,7 +1179,7 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
           for (int v = 0; v < 16; ++v) {
             const int row = 32 * dvt + 8 * (v >> 2) + 4 * h + (v & 3);
             float* pe = sE + row * D + 32 * dkt + c;  // this lane's element
-            *pe = *pe * fo + M[static_cast<size_t>(row) * D + 32 * dkt + c] * fn;
+            *pe = *pe * fo + mpre[t][v] * fn;
           }
         }
         W = W * fo + fn;
@@ -1172,14 +1200,19 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
         }
       }
     } else {
-      // one tensor at a time (registers)
-      auto fold_tensor = [&](const float* src, f32x4_t (&st)[NE4]) {
-        f32x4_t pr[NE4];
+      {
+        // the block's atoms (both tensors' rows requested together: one wait, and fewer
+        // registers spilled than with one tensor at a time)
+        f32x4_t prk[NE4], prv[NE4];
 #pragma unroll
         for (int r = 0; r < NE4; ++r) {
           const int e4 = tid + T * r;
-          pr[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if (e4 < Ck * D / 4) pr[r] = *reinterpret_cast<const f32x4_t*>(src + abase * D + 4 * static_cast<size_t>(e4));
+          prk[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          prv[r] = prk[r];
+          if (e4 < Ck * D / 4) {
+            prk[r] = *reinterpret_cast<const f32x4_t*>(a.at_k + abase * D + 4 * static_cast<size_t>(e4));
+            prv[r] = *reinterpret_cast<const f32x4_t*>(a.at_v + abase * D + 4 * static_cast<size_t>(e4));
+          }
         }
 #pragma unroll
         for (int r = 0; r < NE4; ++r) {
@@ -1187,11 +1220,12 @@ __global__ void __launch_bounds__(ScanCfg<D>::T) s1_causal_scan_kernel(S1Args a)
           if (j >= Ck) continue;
           const float fo = sfo[j], fn = sfn[j];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) st[r][q] = st[r][q] * fo + pr[r][q] * fn;
+          for (int q = 0; q < 4; ++q) {
+            ks[r][q] = ks[r][q] * fo + prk[r][q] * fn;
+            vs[r][q] = vs[r][q] * fo + prv[r][q] * fn;
+          }
         }
-      };
-      fold_tensor(a.at_k, ks);
-      fold_tensor(a.at_v, vs);
+      }
     }
   }
 }
