@@ -988,14 +988,21 @@ __global__ void __launch_bounds__(64 * NW) bw_keys_a_kernel(BwArgs a) {
   }
   __syncthreads();
   const float* Arow = a.A + static_cast<size_t>(bh) * Cq * N;
+  // this key's score and the entry's log masses for cluster i, requested one cluster ahead
+  auto fetch_s = [&](int i, float& av, float& lzij, float& lzi) {
+    const size_t ti = ew * Cq + i;
+    av = valid ? Arow[static_cast<size_t>(i) * N + pos] : 0.f;
+    lzij = a.logz[ti * Ck + j];
+    lzi = a.lz[ti];
+  };
+  float cav = 0.f, clzij = kNegInf, clzi = kNegInf, nav = 0.f, nlzij = kNegInf, nlzi = kNegInf;
+  if (nci > 0) fetch_s(0, cav, clzij, clzi);
   for (int i = 0; i < nci; ++i) {
     const int buf = i & 1;
     if (i + 1 < Cq) fetch(i + 1);  // the next tiles travel during this cluster's products
-    const size_t ti = ew * Cq + i;
-    const float av = valid ? Arow[static_cast<size_t>(i) * N + pos] : 0.f;
-    const float lzij = a.logz[ti * Ck + j];
+    if (i + 1 < nci) fetch_s(i + 1, nav, nlzij, nlzi);
+    const float av = cav, lzij = clzij, lzi = clzi;
     const float w = (kept && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
-    const float lzi = a.lz[ti];
     const float p = (kept && lzi != kNegInf) ? __expf(av - lzi) : 0.f;
     const uint16_t* g = sGd[buf];
     // u^T = G K^T, then t^T = G^T V^T, each folded into its accumulator before the next
@@ -1041,6 +1048,9 @@ __global__ void __launch_bounds__(64 * NW) bw_keys_a_kernel(BwArgs a) {
       if (!a.causal) a.WQ[o] = w * qv;
     }
     if (i + 1 < Cq) stage(buf ^ 1);
+    cav = nav;
+    clzij = nlzij;
+    clzi = nlzi;
     __syncthreads();
   }
   if (last && valid && h == 0)
@@ -1172,31 +1182,56 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
     dv[e] = (a.dipole == 1 && valid) ? dvr[e] : 0.f;
   }
   __syncthreads();
-  for (int i = 0; i < (last ? 0 : Cq); ++i) {
+  // the table rows of query cluster i + 1 are requested while cluster i is used (they do
+  // not depend on the computation): one memory round trip per cluster is hidden
+  struct Rows {
+    float lzij, kpv[DQ], vpv[DQ], x0, x1, x2, x3;
+  };
+  auto fetch = [&](int i, Rows& r) {
     const size_t ti = ew * Cq + i;
+    const size_t tij = ti * Ck + j;
+    const size_t sij_ = (es * Cq + i) * Ck + j;  // suffix tables (causal)
+    r.lzij = a.logz[tij];
+    const float* kp = a.causal ? a.sdk + sij_ * D + d0 : a.dKp + tij * D + d0;
+    const float* vp = a.causal ? a.sdv + sij_ * D + d0 : a.dVp + tij * D + d0;
+#pragma unroll
+    for (int e = 0; e < DQ; e += 4) {
+      const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(kp + e);
+      const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(vp + e);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        r.kpv[e + q] = k4[q];
+        r.vpv[e + q] = v4[q];
+      }
+    }
+    const float qi = a.dipole == 1 ? a.Q[(static_cast<size_t>(bh) * Cq + i) * N + pos] : 0.f;
+    if (a.causal) {
+      r.x0 = a.lz[ti];
+      r.x1 = qi;
+      r.x2 = a.st[sij_];
+      r.x3 = 0.f;
+    } else {
+      r.x0 = a.dipole == 1 ? a.P[tij] : 0.f;
+      r.x1 = qi;
+      r.x2 = a.sij[tij];
+      r.x3 = a.dlogz[tij];
+    }
+  };
+  Rows cur, nxt;
+  const int nci = last ? 0 : Cq;
+  if (nci > 0) fetch(0, cur);
+  for (int i = 0; i < nci; ++i) {
+    if (i + 1 < nci) fetch(i + 1, nxt);
     float x = 0.f;
 #pragma unroll
     for (int e = 0; e < DQ; ++e) x = fmaf(sQb[i * D + d0 + e], kf[e], x);
     x += dpp_f32<0xB1>(x);
     x += dpp_f32<0x4E>(x);
     const float av = s * x;
-    const size_t tij = ti * Ck + j;
-    const size_t sij_ = (es * Cq + i) * Ck + j;  // suffix tables (causal)
-    const float lzij = a.logz[tij];
+    const float lzij = cur.lzij;
     const float w = (kept && lzij != kNegInf) ? __expf(av - lzij) : 0.f;
-    const float* kp = a.causal ? a.sdk + sij_ * D + d0 : a.dKp + tij * D + d0;
-    const float* vp = a.causal ? a.sdv + sij_ * D + d0 : a.dVp + tij * D + d0;
-    float kpv[DQ], vpv[DQ];
-#pragma unroll
-    for (int e = 0; e < DQ; e += 4) {
-      const f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(kp + e);
-      const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(vp + e);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        kpv[e + r] = k4[r];
-        vpv[e + r] = v4[r];
-      }
-    }
+    const float* kpv = cur.kpv;
+    const float* vpv = cur.vpv;
     float y = 0.f;
 #pragma unroll
     for (int e = 0; e < DQ; ++e) y = fmaf(kpv[e], kf[e], fmaf(vpv[e], vf[e], y));
@@ -1204,13 +1239,12 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
     y += dpp_f32<0x4E>(y);
     float da;
     if (a.causal) {
-      const float lzi = a.lz[ti];
+      const float lzi = cur.x0;
       const float p = (a.dipole == 1 && kept && lzi != kNegInf) ? __expf(av - lzi) : 0.f;
-      const float qi = a.dipole == 1 ? a.Q[(static_cast<size_t>(bh) * Cq + i) * N + pos] : 0.f;
-      da = fmaf(w, y + a.st[sij_], p * qi);
+      da = fmaf(w, y + cur.x2, p * cur.x1);
     } else {
-      if (a.dipole == 1 && kept) y += a.P[tij] * a.Q[(static_cast<size_t>(bh) * Cq + i) * N + pos];
-      da = w * (y - a.sij[tij] + a.dlogz[tij]);
+      if (a.dipole == 1 && kept) y += cur.x0 * cur.x1;
+      da = w * (y - cur.x2 + cur.x3);
     }
 #pragma unroll
     for (int e = 0; e < DQ; ++e) {
@@ -1218,6 +1252,7 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
       dv[e] = fmaf(w, vpv[e], dv[e]);
     }
     if ((tid & 3) == 0) sWd[i * (KT + 1) + kk] = a.causal ? da : w * y;
+    cur = nxt;
   }
   if (last)
     for (int e = tid; e < Cq * (KT + 1); e += 256) sWd[e] = 0.f;
