@@ -48,6 +48,28 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
   const int Cq = a.Cq, Cqp = (Cq + 31) & ~31, nt_n = Cqp / 32;
   uint16_t* qhi = sq;
   uint16_t* qlo = sq + Cqp * QST;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
+  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
+  float* S = a.scores + static_cast<size_t>(bh) * Cq * a.N;
+  // the key rows of this wave's two 32-position tiles are requested before the centroids
+  // are staged (permutation entries of both tiles, then their rows), one round trip each
+  int keys[2];
+  bf16x8_t ak2[2][NKS];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int pos = blockIdx.x * 256 + wave * 64 + tt * 32 + c;
+    keys[tt] = pos < a.N ? perm[pos] : 0;
+  }
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int pos = blockIdx.x * 256 + wave * 64 + tt * 32 + c;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u16x8_t u = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (pos < a.N) u = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(keys[tt]) * D + 16 * ks + 8 * h);
+      ak2[tt][ks] = as_bf16x8(u);
+    }
+  }
   for (int x = tid; x < Cqp * D; x += 256) {
     const int i = x / D, d = x % D;
     const float v = i < Cq ? a.qbar[(static_cast<size_t>(bh) * Cq + i) * D + d] : 0.f;
@@ -56,24 +78,16 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
     qlo[i * QST + d] = f32_to_bf16_bits(v - bf16_to_f32(hv));
   }
   __syncthreads();
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
-  const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N;
-  float* S = a.scores + static_cast<size_t>(bh) * Cq * a.N;
+#pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int kb = blockIdx.x * 256 + wave * 64 + tt * 32;  // first position of the tile
     if (kb >= a.N) break;
     const int pos = kb + c;
-    const int key = pos < a.N ? perm[pos] : 0;
+    const int key = keys[tt];
     // bit p of dmask: position kb + p is left out by a cluster size cap (score -inf)
     const bool drop = a.kdrop != nullptr && pos < a.N && a.kdrop[static_cast<size_t>(bh) * a.N + key] != 0;
     const uint32_t dmask = static_cast<uint32_t>(__ballot(drop));
-    bf16x8_t ak[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u16x8_t u = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (pos < a.N) u = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(key) * D + 16 * ks + 8 * h);
-      ak[ks] = as_bf16x8(u);
-    }
+    const bf16x8_t* ak = ak2[tt];
     for (int nt = 0; nt < nt_n; ++nt) {
       f32x16_t acc = zero16();
 #pragma unroll
