@@ -38,6 +38,31 @@ __device__ __forceinline__ f32x16_t mfma32_f16(const f16x8_t& a, const f16x8_t& 
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// sc * qbar of the head split into bf16 hi + lo rows of stride QST, padded with zero rows
+// to Cqp; every thread's elements are requested before any is stored (eight at a time,
+// clamped indices), so that the staging costs one memory round trip, not one per element.
+template <int D, int NT>
+__device__ __forceinline__ void stage_qbar_split(const float* qb, int Cq, int Cqp, float sc, uint16_t* qhi,
+                                                 uint16_t* qlo, int QST, int tid) {
+  const int n = Cqp * D, nv = Cq * D;
+  for (int x0 = tid; x0 < n; x0 += 8 * NT) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = qb[min(x0 + NT * q, nv - 1)];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int x = x0 + NT * q;
+      if (x < n) {
+        const int i = x / D, d = x % D;
+        const float y = i < Cq ? sc * v[q] : 0.f;
+        const uint16_t hv = f32_to_bf16_bits(y);
+        qhi[i * QST + d] = hv;
+        qlo[i * QST + d] = f32_to_bf16_bits(y - bf16_to_f32(hv));
+      }
+    }
+  }
+}
+
 // Workgroup = 256 keys (4 waves x 2 tiles of 32); dynamic LDS: qbar hi/lo [Cqp][D+8].
 template <int D>
 __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
@@ -55,28 +80,16 @@ __global__ void __launch_bounds__(256) s1_scores_kernel(S1Args a) {
   // are staged (permutation entries of both tiles, then their rows), one round trip each
   int keys[2];
   bf16x8_t ak2[2][NKS];
+  // (unconditional loads with clamped positions, so that they issue back to back; the
+  // rows past the end are masked below)
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int pos = blockIdx.x * 256 + wave * 64 + tt * 32 + c;
-    keys[tt] = pos < a.N ? perm[pos] : 0;
-  }
+  for (int tt = 0; tt < 2; ++tt) keys[tt] = perm[min(static_cast<int>(blockIdx.x) * 256 + wave * 64 + tt * 32 + c, a.N - 1)];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int pos = blockIdx.x * 256 + wave * 64 + tt * 32 + c;
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u16x8_t u = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (pos < a.N) u = *reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(keys[tt]) * D + 16 * ks + 8 * h);
-      ak2[tt][ks] = as_bf16x8(u);
-    }
-  }
-  for (int x = tid; x < Cqp * D; x += 256) {
-    const int i = x / D, d = x % D;
-    const float v = i < Cq ? a.qbar[(static_cast<size_t>(bh) * Cq + i) * D + d] : 0.f;
-    const uint16_t hv = f32_to_bf16_bits(v);
-    qhi[i * QST + d] = hv;
-    qlo[i * QST + d] = f32_to_bf16_bits(v - bf16_to_f32(hv));
-  }
+    for (int ks = 0; ks < NKS; ++ks)
+      ak2[tt][ks] = as_bf16x8(*reinterpret_cast<const u16x8_t*>(K + static_cast<size_t>(keys[tt]) * D + 16 * ks + 8 * h));
+  stage_qbar_split<D, 256>(a.qbar + static_cast<size_t>(bh) * Cq * D, Cq, Cqp, 1.f, qhi, qlo, QST, tid);
   __syncthreads();
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
@@ -173,13 +186,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 1) s1_atoms_mfma_kernel(S1A
   int pl = gather(hd), pl_nx = gather(hd_nx);
   uint16_t* qhi = sq;
   uint16_t* qlo = sq + Cqp * QST;
-  for (int x = tid; x < Cqp * D; x += 256) {
-    const int i = x / D, d = x % D;
-    const float v = i < Cq ? a.scale * a.qbar[(static_cast<size_t>(bh) * Cq + i) * D + d] : 0.f;
-    const uint16_t hv = f32_to_bf16_bits(v);
-    qhi[i * QST + d] = hv;
-    qlo[i * QST + d] = f32_to_bf16_bits(v - bf16_to_f32(hv));
-  }
+  stage_qbar_split<D, 256>(a.qbar + static_cast<size_t>(bh) * Cq * D, Cq, Cqp, a.scale, qhi, qlo, QST, tid);
   __syncthreads();
   if (hd.y < 0) return;  // no item (padding); no workgroup barrier below
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(bh) * a.N * D;
@@ -437,7 +444,15 @@ __global__ void __launch_bounds__(512) s1_moments_f16_kernel(S1Args a) {
   const int key0 = mb * a.mbk, key1 = min(a.N, key0 + a.mbk), nkeys = key1 - key0;
   const float* S = a.scores + (static_cast<size_t>(bh) * Cq + i0) * a.N + key0;
   const int32_t* perm = a.perm_k + static_cast<size_t>(bh) * a.N + key0;
-  for (int k = tid; k < nkeys; k += 512) s_perm[k] = perm[k];
+  // the range's permutation entries, eight per thread requested at a time (clamped)
+  for (int k0 = tid; k0 < nkeys; k0 += 512 * 8) {
+    int pv8[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) pv8[q] = perm[min(k0 + 512 * q, nkeys - 1)];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (k0 + 512 * q < nkeys) s_perm[k0 + 512 * q] = pv8[q];
+  }
 
   // max of the scores over the range, per centroid, from the maxima of its 32-position
   // tiles (the range starts on a tile): 32 lanes (a half-wave) per centroid
