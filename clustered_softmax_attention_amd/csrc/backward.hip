@@ -890,14 +890,23 @@ __global__ void __launch_bounds__(256) bw_scores_kernel(BwArgs a) {
   __shared__ float sQb[kMaxClusters * D];
   const int bh = blockIdx.y, tid = threadIdx.x, kk = tid >> 2, d0 = (tid & 3) * DQ;
   const int N = a.N, Cq = a.Cq;
-  for (int e = tid; e < Cq * D; e += 256) sQb[e] = a.qbar[static_cast<size_t>(bh) * Cq * D + e];
+  for (int e0 = tid; e0 < Cq * D; e0 += 256 * 8) {  // eight loads in flight per thread
+    float qv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) qv[q] = a.qbar[static_cast<size_t>(bh) * Cq * D + min(e0 + 256 * q, Cq * D - 1)];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (e0 + 256 * q < Cq * D) sQb[e0 + 256 * q] = qv[q];
+  }
   const int pos = blockIdx.x * KT + kk;
   const bool valid = pos < N;
   const int key = valid ? a.perm_k[static_cast<size_t>(bh) * N + pos] : 0;
   const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * N * D;
   float kf[DQ];
 #pragma unroll
-  for (int e = 0; e < DQ; ++e) kf[e] = valid ? Elem<T>::load(K, static_cast<size_t>(key) * D + d0 + e) : 0.f;
+  for (int e = 0; e < DQ; ++e) kf[e] = Elem<T>::load(K, static_cast<size_t>(key) * D + d0 + e);  // key 0 if invalid
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) kf[e] = valid ? kf[e] : 0.f;
   __syncthreads();
   float* A = a.A + static_cast<size_t>(bh) * Cq * N;
   for (int i = 0; i < Cq; ++i) {
@@ -945,6 +954,8 @@ __global__ void __launch_bounds__(64 * NW) bw_keys_a_kernel(BwArgs a) {
   const T* K = static_cast<const T*>(a.k) + static_cast<size_t>(bh) * N * D;
   const T* V = static_cast<const T*>(a.v) + static_cast<size_t>(bh) * N * D;
   // B operands: key c, dimensions 16 ks + 8 h .. + 7 (bf16 hi, and lo for fp32 inputs)
+  // (the row of key `key`, 0 for an invalid lane, is loaded unconditionally and zeroed
+  // after: loads under the lane's validity are issued and waited for one at a time)
   bf16x8_t kh[NKS], kl[NKS], vh[NKS], vl[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
@@ -952,8 +963,13 @@ __global__ void __launch_bounds__(64 * NW) bw_keys_a_kernel(BwArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const size_t o = static_cast<size_t>(key) * D + 16 * ks + 8 * h + e;
-      x[e] = valid ? Elem<T>::load(K, o) : 0.f;
-      y[e] = valid ? Elem<T>::load(V, o) : 0.f;
+      x[e] = Elem<T>::load(K, o);
+      y[e] = Elem<T>::load(V, o);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = valid ? x[e] : 0.f;
+      y[e] = valid ? y[e] : 0.f;
     }
     split_bf16x8(x, kh[ks], kl[ks]);
     split_bf16x8(y, vh[ks], vl[ks]);
@@ -964,7 +980,9 @@ __global__ void __launch_bounds__(64 * NW) bw_keys_a_kernel(BwArgs a) {
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int v = 0; v < 16; ++v)
-      vq[16 * mt + v] = valid ? Elem<T>::load(V, static_cast<size_t>(key) * D + 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3)) : 0.f;
+      vq[16 * mt + v] = Elem<T>::load(V, static_cast<size_t>(key) * D + 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3));
+#pragma unroll
+  for (int v = 0; v < NMT * 16; ++v) vq[v] = valid ? vq[v] : 0.f;
   u16x8_t pf[NPF];
   auto fetch = [&](int i) {
     const uint16_t* src = a.gd + (eg * Cq + i) * 4 * D * D;
@@ -991,7 +1009,8 @@ __global__ void __launch_bounds__(64 * NW) bw_keys_a_kernel(BwArgs a) {
   // this key's score and the entry's log masses for cluster i, requested one cluster ahead
   auto fetch_s = [&](int i, float& av, float& lzij, float& lzi) {
     const size_t ti = ew * Cq + i;
-    av = valid ? Arow[static_cast<size_t>(i) * N + pos] : 0.f;
+    av = Arow[static_cast<size_t>(i) * N + min(pos, N - 1)];  // unconditional (zeroed below)
+    av = valid ? av : 0.f;
     lzij = a.logz[ti * Ck + j];
     lzi = a.lz[ti];
   };
@@ -1160,7 +1179,14 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
   float* sKr = sWd + Cq * (KT + 1);
   float* sVr = sKr + KT * RP;  // untilted only
   const float s = a.scale;
-  for (int e = tid; e < Cq * D; e += 256) sQb[e] = a.qbar[static_cast<size_t>(bh) * Cq * D + e];
+  for (int e0 = tid; e0 < Cq * D; e0 += 256 * 8) {  // eight loads in flight per thread
+    float qv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) qv[q] = a.qbar[static_cast<size_t>(bh) * Cq * D + min(e0 + 256 * q, Cq * D - 1)];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (e0 + 256 * q < Cq * D) sQb[e0 + 256 * q] = qv[q];
+  }
   const int pos = blockIdx.x * KT + kk;
   const bool valid = pos < N;
   const int key = valid ? a.perm_k[static_cast<size_t>(bh) * N + pos] : 0;
@@ -1172,14 +1198,23 @@ __global__ void __launch_bounds__(256) bw_keys_b_kernel(BwArgs a) {
   float kf[DQ], vf[DQ], dk[DQ], dv[DQ];
   float* dkr = a.dk + (static_cast<size_t>(bh) * N + key) * D + d0;
   float* dvr = a.dv + (static_cast<size_t>(bh) * N + key) * D + d0;
+  // the rows of key `key` (0 for an invalid lane) loaded unconditionally and zeroed after:
+  // loads under the lane's validity are issued and waited for one at a time
 #pragma unroll
   for (int e = 0; e < DQ; ++e) {
-    kf[e] = valid ? Elem<T>::load(K, static_cast<size_t>(key) * D + d0 + e) : 0.f;
-    vf[e] = valid ? Elem<T>::load(V, static_cast<size_t>(key) * D + d0 + e) : 0.f;
+    kf[e] = Elem<T>::load(K, static_cast<size_t>(key) * D + d0 + e);
+    vf[e] = Elem<T>::load(V, static_cast<size_t>(key) * D + d0 + e);
+    dk[e] = dkr[e];
+    dv[e] = dvr[e];
+  }
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) {
+    kf[e] = valid ? kf[e] : 0.f;
+    vf[e] = valid ? vf[e] : 0.f;
     sKr[kk * RP + d0 + e] = kf[e];
     if (a.dipole == 2) sVr[kk * RP + d0 + e] = vf[e];
-    dk[e] = (a.dipole == 1 && valid) ? dkr[e] : 0.f;
-    dv[e] = (a.dipole == 1 && valid) ? dvr[e] : 0.f;
+    dk[e] = (a.dipole == 1 && valid) ? dk[e] : 0.f;
+    dv[e] = (a.dipole == 1 && valid) ? dv[e] : 0.f;
   }
   __syncthreads();
   // the table rows of query cluster i + 1 are requested while cluster i is used (they do

@@ -268,13 +268,18 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) s2_mfma_kernel(S2Args a)
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) qr[ks] = *reinterpret_cast<const u16x8_t*>(Q + row * D + 16 * ks + 8 * h);
   store_dip();
+  // (the centroid's elements are loaded unconditionally, as whole vectors: a load under
+  // the lane's validity would be issued and waited for one element at a time)
   bf16x8_t qhi[NKS], qlo[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int d0 = 16 * ks + 8 * h;
+    const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(qb + d0);
+    const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(qb + d0 + 4);
+    const float cb[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
     float x[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) x[r] = valid ? bf16_to_f32(qr[ks][r]) - qb[d0 + r] : 0.f;
+    for (int r = 0; r < 8; ++r) x[r] = valid ? bf16_to_f32(qr[ks][r]) - cb[r] : 0.f;
     split_bf16x8(x, qhi[ks], qlo[ks]);
   }
 
