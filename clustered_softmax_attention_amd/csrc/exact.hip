@@ -342,7 +342,15 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
   const size_t row = base + qi;
   float w0 = inv, w1 = 0.f;
   bool merge = false;
+  // the far-field row requested together with its log-sum-exp (a load under `merge`
+  // would be issued and waited for one 16-byte piece at a time)
+  f32x4_t ofar[NMT][4];
   if (a.l_far != nullptr) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        ofar[mt][g] = *reinterpret_cast<const f32x4_t*>(a.o_far + row * D + 32 * mt + 8 * g + 4 * h);
     const float lf = a.l_far[row];
     if (lf != kNegInf) {
       const float Lt = fmaxf(L, lf) + __logf(1.f + __expf(-fabsf(L - lf)));
@@ -362,9 +370,8 @@ __global__ void __launch_bounds__(256, 2) flash_bf16_kernel(ExactArgs a, int nqt
 #pragma unroll
       for (int r = 0; r < 4; ++r) r4[r] = o[mt][4 * g + r] * w0;
       if (merge) {
-        const f32x4_t f = *reinterpret_cast<const f32x4_t*>(a.o_far + row * D + d0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) r4[r] += w1 * f[r];
+        for (int r = 0; r < 4; ++r) r4[r] += w1 * ofar[mt][g][r];
       }
       if (a.out_bf16) {
         const u16x4_t u = {f32_to_bf16_bits(r4[0]), f32_to_bf16_bits(r4[1]), f32_to_bf16_bits(r4[2]),
