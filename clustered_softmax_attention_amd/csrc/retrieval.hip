@@ -40,10 +40,14 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx) {
   }
 }
 
+// One wave per (i, b): the k1 clusters first (LDS only), then per chosen cluster its
+// block scores, loaded once for all k2 picks (each lane's rows requested together,
+// unconditionally at a clamped block index), a chosen entry marked by a score of -inf.
+// Dynamic LDS: nb floats (the block scores of one cluster).
 __global__ void __launch_bounds__(64) retr_select_kernel(RetrArgs a) {
+  extern __shared__ float s_bs[];
   __shared__ float s_sj[kMaxClusters];
-  __shared__ unsigned char s_used[kMaxClusters];
-  __shared__ unsigned char s_bused[kMaxRetrBlocks];
+  __shared__ int s_out[kMaxRetrRow];  // the selection row, written out at the end
   const int i = blockIdx.x, b = blockIdx.y, bh = blockIdx.z;
   const int lane = threadIdx.x;
   const int Ck = a.Ck, k1 = a.k1, k2 = a.k2, row = k1 * (1 + k2);
@@ -53,53 +57,71 @@ __global__ void __launch_bounds__(64) retr_select_kernel(RetrArgs a) {
     return;
   }
   const size_t sidx = (static_cast<size_t>(bh) * a.nb + b) * a.Cq + i;
-  for (int j = lane; j < Ck; j += 64) {
-    s_sj[j] = a.s_logz[sidx * Ck + j];
-    s_used[j] = 0;
+  {
+    float l[kMaxClusters / 64];
+#pragma unroll
+    for (int q = 0; q < kMaxClusters / 64; ++q) l[q] = a.s_logz[sidx * Ck + min(lane + 64 * q, Ck - 1)];
+#pragma unroll
+    for (int q = 0; q < kMaxClusters / 64; ++q)
+      if (lane + 64 * q < Ck) s_sj[lane + 64 * q] = l[q];
   }
   __syncthreads();
+  // clusters: highest prefix log mass first, ties to the lower index; -inf ends the list
   for (int t = 0; t < k1; ++t) {
     float v = kNegInf;
     int idx = 1 << 30;
     for (int j = lane; j < Ck; j += 64)
-      if (!s_used[j] && s_sj[j] != kNegInf && (s_sj[j] > v || (s_sj[j] == v && j < idx))) {
+      if (s_sj[j] != kNegInf && (s_sj[j] > v || (s_sj[j] == v && j < idx))) {
         v = s_sj[j];
         idx = j;
       }
     wave_argmax(v, idx);
-    int32_t* o = out + t * (1 + k2);
-    if (v == kNegInf) {
-      for (int x = lane; x < 1 + k2; x += 64) o[x] = -1;
+    const int j = v == kNegInf ? -1 : idx;
+    if (lane == 0) {
+      if (j >= 0) s_sj[j] = kNegInf;
+      s_out[t * (1 + k2)] = j;
+    }
+    __syncthreads();
+  }
+  // blocks of each chosen cluster: highest atom log mass among blocks < b, ties to the
+  // earlier block; empty atoms never chosen
+  for (int t = 0; t < k1; ++t) {
+    const int j = s_out[t * (1 + k2)];
+    int* o = s_out + t * (1 + k2);
+    if (j < 0) {
+      for (int x = lane; x < k2; x += 64) o[1 + x] = -1;
       continue;
     }
-    const int j = idx;
-    if (lane == 0) {
-      s_used[j] = 1;
-      o[0] = j;
+    for (int bb0 = 0; bb0 < b; bb0 += 64) {
+      const int bb = bb0 + lane;
+      const size_t aidx = ((static_cast<size_t>(bh) * a.nb + min(bb, b - 1)) * a.Cq + i) * Ck + j;
+      const float z = a.at_z[aidx], m = a.at_m[aidx];
+      if (bb < b) s_bs[bb] = z > 0.f ? m + __logf(z) : kNegInf;
     }
-    for (int bb = lane; bb < b; bb += 64) s_bused[bb] = 0;
     __syncthreads();
     for (int u = 0; u < k2; ++u) {
       float bv = kNegInf;
       int bi = 1 << 30;
       for (int bb = lane; bb < b; bb += 64) {
-        const size_t aidx = ((static_cast<size_t>(bh) * a.nb + bb) * a.Cq + i) * Ck + j;
-        const float z = a.at_z[aidx];
-        if (s_bused[bb] || !(z > 0.f)) continue;
-        const float sv = a.at_m[aidx] + __logf(z);
-        if (sv > bv || (sv == bv && bb < bi)) {
+        const float sv = s_bs[bb];
+        if (sv != kNegInf && (sv > bv || (sv == bv && bb < bi))) {
           bv = sv;
           bi = bb;
         }
       }
       wave_argmax(bv, bi);
-      if (lane == 0) o[1 + u] = bv == kNegInf ? -1 : bi;
-      if (bv != kNegInf && lane == 0) s_bused[bi] = 1;
+      if (lane == 0) {
+        o[1 + u] = bv == kNegInf ? -1 : bi;
+        if (bv != kNegInf) s_bs[bi] = kNegInf;
+      }
       __syncthreads();
     }
   }
-  if (a.trace != nullptr)
-    for (int x = lane; x < row; x += 64) a.trace[((static_cast<size_t>(bh) * a.nb + b) * a.Cq + i) * row + x] = out[x];
+  __syncthreads();
+  for (int x = lane; x < row; x += 64) {
+    out[x] = s_out[x];
+    if (a.trace != nullptr) a.trace[((static_cast<size_t>(bh) * a.nb + b) * a.Cq + i) * row + x] = s_out[x];
+  }
 }
 
 __device__ __forceinline__ bool atom_selected(const int32_t* selrow, int k2, int bb) {
@@ -170,11 +192,19 @@ __global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
   if (b == 0) return;
   const int Ck = a.Ck, k1 = a.k1, k2 = a.k2, row = k1 * (1 + k2);
   const int32_t* sel = a.sel + ((static_cast<size_t>(bh) * a.nb + b) * a.Cq + i) * row;
-  for (int x = tid; x < row; x += 256) s_sel[x] = sel[x];
-  for (int d = tid; d < D; d += 256) s_q[d] = a.qbar[(static_cast<size_t>(bh) * a.Cq + i) * D + d];
+  static_assert(kMaxRetrRow <= 256 && D <= 256, "one element per thread");
+  {
+    // both requested before either is stored (a load under the thread's bound would wait
+    // for itself)
+    const int32_t sv = sel[min(tid, row - 1)];
+    const float qv = a.qbar[(static_cast<size_t>(bh) * a.Cq + i) * D + min(tid, D - 1)];
+    if (tid < row) s_sel[tid] = sv;
+    if (tid < D) s_q[tid] = qv;
+  }
   const size_t sidx = (static_cast<size_t>(bh) * a.nb + b) * a.Cq + i;
-  // prefix log mass (before any entry is rewritten)
-  if (tid < 64) {
+  // prefix log mass (before any entry is rewritten), for the fp32 second moment
+  const bool mom32 = a.dipole && sizeof(T) == 4;
+  if (mom32 && tid < 64) {
     float mx = kNegInf;
     for (int j = tid; j < Ck; j += 64) mx = fmaxf(mx, a.s_logz[sidx * Ck + j]);
     mx = wave_max(mx);
@@ -187,7 +217,7 @@ __global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
     if (tid == 0) s_red[0] = mx == kNegInf ? kNegInf : mx + __logf(sm);
   }
   __syncthreads();
-  const float Rpre = s_red[0];
+  const float Rpre = mom32 ? s_red[0] : kNegInf;
 
   // 1. remainder summaries of the chosen clusters (re-merged from unselected atoms): the
   // k1 x 2D (cluster, feature) folds spread over all threads
@@ -233,7 +263,7 @@ __global__ void __launch_bounds__(256) retr_tables_kernel(RetrArgs a) {
     }
   }
   // bf16 inputs: the second moment was handled by retr_moment_mfma
-  if (!a.dipole || Rpre == kNegInf || sizeof(T) == 2) return;
+  if (!mom32 || Rpre == kNegInf) return;
 
   // 2. second moment without the retrieved keys
   const int tr = tid / 16, tc = tid % 16;
@@ -790,7 +820,7 @@ hipError_t launch_retrieval(const RetrArgs& a, int phase, int dtype, hipStream_t
   if (phase == 0) {
     {
       ProfScope ps_("retr_select", s);
-      hipLaunchKernelGGL(retr_select_kernel, g, dim3(64), 0, s, a);
+      hipLaunchKernelGGL(retr_select_kernel, g, dim3(64), sizeof(float) * a.nb, s, a);
     }
     if (dtype == 1 && a.dipole) {
       ProfScope ps_("retr_moment_mfma", s);
