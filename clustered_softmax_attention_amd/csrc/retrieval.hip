@@ -453,8 +453,11 @@ struct RetrExactCfg {
   static constexpr size_t lds_bytes = 2 * 2 * JC * KST * sizeof(uint16_t);
 };
 
+// D = 64: four workgroups per compute unit (128 registers, three of them spilled); the
+// kernel waits on its gathers, so the extra workgroup in flight pays (6 % at 16k tokens
+// against three workgroups without spills).
 template <int D>
-__global__ void __launch_bounds__(256, D == 64 ? 3 : 2) retr_exact_mfma_kernel(RetrArgs a) {
+__global__ void __launch_bounds__(256, D == 64 ? 4 : 2) retr_exact_mfma_kernel(RetrArgs a) {
   using Cfg = RetrExactCfg<D>;
   constexpr int NKS = Cfg::NKS, NMT = Cfg::NMT, JC = Cfg::JC, KST = Cfg::KST, NK = Cfg::NK;
   extern __shared__ __align__(16) unsigned char smem[];
